@@ -1,0 +1,177 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) token-choice top-k Mixture-of-Experts
+ * FFN layer: routing, token permutation, grouped SwiGLU expert GEMMs, weighted
+ * combine, and the backward pass.
+ *
+ * What the layer computes (sources are the pages this library follows):
+ *   - "Beam" blog (hncyxsy.com), sections 2.2 and 5.3: the MoE layer replaces a
+ *     transformer FFN; a router (d_model x N matrix, nn.Linear without bias)
+ *     scores every expert, the top-k experts of each token run, and the output
+ *     is the gate-weighted sum of their outputs; the gates are a softmax over
+ *     the k selected logits.
+ *   - "Trinity Large" commentary (ai-stack.site), code examples 1-3: top-k then
+ *     softmax; per-expert counts; dispatch to per-expert buffers and combine.
+ *   - Olmo-core 3 article (pwwt.cn), "three splits" section: tokens are written
+ *     straight into contiguous per-expert input buffers, routing stays resident
+ *     on the GPU (the host never waits for routing metadata), the expert GEMMs
+ *     are grouped, and MXFP8 is a precision switch for them.
+ *   - SonicMoE article (techwalker.com), section 1: the router-score gradient is
+ *     dS = <dA', A> (not <dO, Y>), so expert outputs Y are never stored;
+ *     section 3: token rounding of per-expert counts to the GEMM tile.
+ *
+ * Expert e is a SwiGLU FFN without biases: h = W1_e x (W1_e = [W_gate; W_up],
+ * [2f, d], gate rows first), a = silu(h_gate) * h_up, y = W2_e a (W2_e [d, f]).
+ *
+ * Conventions (all entry points):
+ *   - Every data pointer is a DEVICE pointer owned by the caller, row-major,
+ *     16-byte aligned.  The library never allocates or frees device memory and
+ *     keeps no global mutable state.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls only enqueue work on it and return; there is no device-to-host copy
+ *     or synchronisation anywhere.  Routing-dependent sizes stay in device
+ *     memory (plan.offsets etc.); kernels read them there.
+ *   - Validation happens on the host before anything is enqueued: on any error
+ *     nothing is launched.  MOE_EHIP reports a failed kernel launch; faults that
+ *     happen asynchronously on the device surface at the caller's next sync.
+ *   - Results are bitwise reproducible run to run (no floating-point atomics).
+ *   - Concurrent calls on different streams need separate plan and workspace
+ *     buffers.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,     /* null/misaligned pointer, non-positive size, k > E, bad dtype mix */
+  MOE_ENOTSUP = 2,    /* shape outside what the kernels support (see moe_shape) */
+  MOE_EWORKSPACE = 3, /* workspace or plan blob smaller than the *_bytes() query */
+  MOE_EHIP = 4        /* a kernel launch failed */
+} moe_status;
+
+typedef enum {
+  MOE_F32 = 0,   /* IEEE float32 */
+  MOE_BF16 = 1,  /* bfloat16, round-to-nearest-even on every store */
+  MOE_MXFP8 = 2  /* expert-GEMM operands only: FP8 E4M3 + one E8M0 scale per 32 along K */
+} moe_dtype;
+
+/* Problem shape.
+ *   T tokens, d = d_model, E experts, k experts per token, d_ff = f (SwiGLU
+ *   hidden size per expert).
+ *   act:  storage type of x, weights, dout and the outputs (MOE_F32 or MOE_BF16).
+ *   gemm: expert-GEMM operand format: MOE_F32 (requires act == MOE_F32),
+ *         MOE_BF16 or MOE_MXFP8 (both require act == MOE_BF16).
+ *   round_tile: 0 = no token rounding; otherwise the tile multiple (128) that
+ *         moe_round_tokens rounds per-expert counts to.
+ * Supported: 1 <= k <= min(E, 8), 1 <= E <= 256, d % 64 == 0, d_ff % 64 == 0,
+ * d, d_ff <= 16384, T <= 2^24, T*k + E*round_tile/2 < 2^31. */
+typedef struct moe_shape {
+  int32_t T, d, E, k, d_ff;
+  int32_t act;
+  int32_t gemm;
+  int32_t round_tile;
+} moe_shape;
+
+/* The routing plan: device arrays carved from one caller-allocated blob by
+ * moe_plan_init.  N = plan rows = offsets[E] (device-resident; N <= N_max =
+ * T*k + E*round_tile/2).  Rows are token-expert pairs grouped by expert, and
+ * inside one expert ordered by ascending token. */
+typedef struct moe_plan {
+  float   *logits;       /* [T,E]  router logits, bias included                      */
+  float   *probs_t;      /* [E,T]  full softmax, expert-major (token rounding only)  */
+  int32_t *topk_idx;     /* [T,k]  selected experts, descending logit, ties -> lower index */
+  float   *topk_gate;    /* [T,k]  softmax over the k selected logits                */
+  int32_t *counts_raw;   /* [E]    rows per expert before rounding                   */
+  int32_t *counts;       /* [E]    rows per expert (after rounding when enabled)     */
+  int32_t *offsets;      /* [E+1]  exclusive scan of counts; offsets[E] = N          */
+  int32_t *token_of_row; /* [N_max] token of row r                                   */
+  int32_t *expert_of_row;/* [N_max] expert of row r                                  */
+  float   *gate_of_row;  /* [N_max] gate of row r                                    */
+  int32_t *row_of_slot;  /* [T,k]  row of slot j of token t, -1 if rounding dropped it */
+  int32_t *tok_ptr;      /* [T+1]  CSR token -> rows                                 */
+  int32_t *tok_rows;     /* [N_max] rows of each token, ascending                    */
+  uint32_t *keep_bits;   /* [T, ceil(E/32)] bit (t,e) set when token t has a row at e */
+  int32_t *sched;        /* internal: per-expert tile prefixes for the grouped GEMMs  */
+} moe_plan;
+
+/* Sizes.  All are pure host arithmetic. */
+int64_t    moe_max_rows(const moe_shape *s);            /* N_max */
+size_t     moe_plan_bytes(const moe_shape *s);
+/* Fill `plan` with pointers into `blob` (device memory of >= moe_plan_bytes). */
+moe_status moe_plan_init(const moe_shape *s, void *blob, size_t blob_bytes, moe_plan *plan);
+
+/* Workspace queries, one per entry point that takes a workspace. */
+enum { MOE_WS_ROUTE = 0, MOE_WS_ROUND = 1, MOE_WS_EXPERTS = 2, MOE_WS_BACKWARD = 3 };
+size_t     moe_workspace_bytes(const moe_shape *s, int which);
+
+/* Router GEMM, top-k softmax and the plan (histogram, prefix scan, stable
+ * scatter by token).  x [T,d] (act), w_gate [E,d] (act), bias [E] float32 or
+ * NULL (added to the logits before top-k and softmax; receives no gradient).
+ * With round_tile == 0 the plan is final; otherwise call moe_round_tokens. */
+moe_status moe_route(const moe_shape *s, const void *x, const void *w_gate, const float *bias,
+                     moe_plan *plan, void *ws, size_t ws_bytes, void *stream);
+
+/* Token rounding (SonicMoE article, section 3): every expert's row count moves
+ * to the nearest multiple of round_tile (half rounds up; if that exceeds T it
+ * rounds down).  Fewer rows: the selected pairs with the smallest full-softmax
+ * probability are dropped (ties: larger token first).  More rows: the
+ * unselected tokens with the largest probability are added (ties: smaller token
+ * first) with gate P_te / sum over the token's top-k of P.  Rebuilds the plan. */
+moe_status moe_round_tokens(const moe_shape *s, moe_plan *plan, void *ws, size_t ws_bytes,
+                            void *stream);
+
+/* Permute (gather): dst[r] = src[token_of_row[r]] for r < N.  src [T,d],
+ * dst [N_max,d], both act dtype.  Also used for dout in the backward. */
+moe_status moe_permute(const moe_shape *s, const void *src, const moe_plan *plan, void *dst,
+                       void *stream);
+
+/* Grouped expert FFN on the permuted rows.
+ *   x_perm [N_max,d], w1 [E,2f,d] (gate rows first), w2 [E,d,f], all act dtype.
+ *   h_saved [N_max,2f] (act): H = x_perm W1_e^T, kept for the backward.
+ *   y [N_max,d] (act): Y = A W2_e^T with A = silu(H_gate) * H_up (A is rounded
+ *   to the act dtype and computed from the stored H).
+ * With gemm == MOE_MXFP8 every GEMM operand is quantised to MXFP8 along K
+ * inside this call (workspace). */
+moe_status moe_grouped_gemm_swiglu(const moe_shape *s, const void *x_perm, const void *w1,
+                                   const void *w2, const moe_plan *plan, void *h_saved, void *y,
+                                   void *ws, size_t ws_bytes, void *stream);
+
+/* Weighted combine: out[t] = sum over the rows of t (ascending) of
+ * gate_of_row[r] * y[r], accumulated in float32.  y [N_max,d], out [T,d]. */
+moe_status moe_unpermute_combine(const moe_shape *s, const void *y, const moe_plan *plan,
+                                 void *out, void *stream);
+
+/* Backward for the loss sum_t <out_t, dout_t>.
+ *   Inputs: x [T,d], w_gate [E,d], w1, w2, the plan, h_saved, dout [T,d].
+ *   Outputs: dx [T,d] (act), dw_gate [E,d] f32, dw1 [E,2f,d] f32, dw2 [E,d,f] f32;
+ *   optional dlogits [T,E] f32 and ds [N_max] f32 (per-row gate gradient) when
+ *   not NULL.
+ * dS_r = <dA'_r, A_r> with dA' = dO_perm W2_e and A recomputed from h_saved
+ * (SonicMoE article, section 1); the chain rule gives the rest. */
+moe_status moe_backward(const moe_shape *s, const void *x, const void *w_gate, const void *w1,
+                        const void *w2, const moe_plan *plan, const void *h_saved,
+                        const void *dout, void *dx, float *dw_gate, float *dw1, float *dw2,
+                        float *dlogits, float *ds, void *ws, size_t ws_bytes, void *stream);
+
+/* MXFP8 quantiser (OCP Microscaling v1.0; the pages only name the format):
+ * blocks of 32 consecutive values along a row; shared exponent
+ * X = floor(log2(max|v|)) - 8 clamped to [-127,127] (-127 for an all-zero
+ * block); scale byte = X + 127; element = v / 2^X rounded to nearest-even
+ * E4M3 (bias 7, max 448), saturating, sign bit kept.
+ *   src [rows, cols] bf16 with cols % 32 == 0; codes [rows, cols] u8;
+ *   scales [rows, cols/32] u8. */
+moe_status moe_quantize_mx(const void *src_bf16, int64_t rows, int64_t cols, uint8_t *codes,
+                           uint8_t *scales, void *stream);
+
+const char *moe_status_str(moe_status st);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

@@ -5,11 +5,12 @@ The compute path is a C-ABI HIP library (``libmoe_mi355x.so``) built for gfx950;
 binding is imported lazily so that the input generator and the config table can
 be used without a built library.
 """
+import importlib
+
 __all__ = ["configs", "synth", "binding"]
 
 
 def __getattr__(name):
     if name == "binding":
-        from . import binding
-        return binding
+        return importlib.import_module(".binding", __name__)
     raise AttributeError(name)

@@ -1,0 +1,293 @@
+// C ABI of the MoE layer: validation, plan/workspace carving and launch order.
+// Every call only enqueues on the caller's stream; nothing is launched when a
+// check fails; no device-to-host copy or synchronisation happens anywhere.
+#include <string.h>
+
+#include "moe_internal.h"
+
+namespace moe {
+
+hipError_t launch_quantize_rows(const void* src, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                                hipStream_t st);
+
+int64_t max_rows(const moe_shape& s) {
+  return (int64_t)s.T * s.k + (s.round_tile ? (int64_t)s.E * (s.round_tile / 2) : 0);
+}
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t al(size_t b) { return (b + kAlign - 1) / kAlign * kAlign; }
+
+int words_of(const moe_shape& s) { return (s.E + 31) / 32; }
+int nblk_of(const moe_shape& s) { return (s.T + kPlanBlock - 1) / kPlanBlock; }
+int ldz_of(const moe_shape& s) { return (s.E + 7) / 8 * 8; }
+size_t esz(const moe_shape& s) { return s.act == MOE_BF16 ? 2 : 4; }
+
+// Carves the plan blob in a fixed order; with base == nullptr it only measures.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  template <typename P>
+  P* take(size_t bytes) {
+    P* p = base ? reinterpret_cast<P*>(base + off) : nullptr;
+    off += al(bytes);
+    return p;
+  }
+};
+
+void carve_plan(const moe_shape& s, char* base, moe_plan* p, size_t* total) {
+  Carver c{base};
+  const int64_t T = s.T, E = s.E, k = s.k, N = max_rows(s);
+  moe_plan q{};
+  q.logits = c.take<float>(T * E * 4);
+  q.probs_t = s.round_tile ? c.take<float>(E * T * 4) : nullptr;
+  q.topk_idx = c.take<int32_t>(T * k * 4);
+  q.topk_gate = c.take<float>(T * k * 4);
+  q.counts_raw = c.take<int32_t>(E * 4);
+  q.counts = c.take<int32_t>(E * 4);
+  q.offsets = c.take<int32_t>((E + 1) * 4);
+  q.token_of_row = c.take<int32_t>(N * 4);
+  q.expert_of_row = c.take<int32_t>(N * 4);
+  q.gate_of_row = c.take<float>(N * 4);
+  q.row_of_slot = c.take<int32_t>(T * k * 4);
+  q.tok_ptr = c.take<int32_t>((T + 1) * 4);
+  q.tok_rows = c.take<int32_t>(N * 4);
+  q.keep_bits = c.take<uint32_t>(T * words_of(s) * 4);
+  // internal region
+  q.sched = c.take<int32_t>(2 * (E + 1) * 4);
+  c.take<int32_t>(E * nblk_of(s) * 4);
+  c.take<int32_t>((nblk_of(s) + 1) * 4);
+  if (s.round_tile) c.take<uint32_t>(E * ((T + 31) / 32) * 4);
+  if (p) *p = q;
+  if (total) *total = c.off;
+}
+
+moe_status check_shape(const moe_shape* s) {
+  if (!s) return MOE_EINVAL;
+  if (s->T <= 0 || s->d <= 0 || s->E <= 0 || s->k <= 0 || s->d_ff <= 0) return MOE_EINVAL;
+  if (s->k > s->E) return MOE_EINVAL;
+  if (s->act != MOE_F32 && s->act != MOE_BF16) return MOE_EINVAL;
+  if (s->gemm == MOE_F32 && s->act != MOE_F32) return MOE_EINVAL;
+  if ((s->gemm == MOE_BF16 || s->gemm == MOE_MXFP8) && s->act != MOE_BF16) return MOE_EINVAL;
+  if (s->gemm != MOE_F32 && s->gemm != MOE_BF16 && s->gemm != MOE_MXFP8) return MOE_EINVAL;
+  if (s->round_tile < 0 || (s->round_tile & 1)) return MOE_EINVAL;
+  if (s->k > 8 || s->E > 256) return MOE_ENOTSUP;
+  if (s->d % 64 || s->d_ff % 64) return MOE_ENOTSUP;
+  if (s->act == MOE_BF16 && s->d_ff % 128) return MOE_ENOTSUP;
+  if (s->d > 16384 || s->d_ff > 16384) return MOE_ENOTSUP;
+  if (s->T > (1 << 20)) return MOE_ENOTSUP;
+  if (s->round_tile > 4096) return MOE_ENOTSUP;
+  if (max_rows(*s) >= ((int64_t)1 << 31)) return MOE_ENOTSUP;
+  if (s->gemm == MOE_MXFP8) return MOE_ENOTSUP;   // MX expert GEMMs: see moe_quantize_mx for the quantiser
+  return MOE_OK;
+}
+
+bool aligned(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+bool aligned_or_null(const void* p) { return !p || (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+moe_status check_plan(const moe_shape& s, const moe_plan* p) {
+  if (!p) return MOE_EINVAL;
+  const void* ptrs[] = {p->logits, p->topk_idx, p->topk_gate, p->counts_raw, p->counts, p->offsets,
+                        p->token_of_row, p->expert_of_row, p->gate_of_row, p->row_of_slot, p->tok_ptr,
+                        p->tok_rows, p->keep_bits, p->sched};
+  for (const void* q : ptrs)
+    if (!aligned(q)) return MOE_EINVAL;
+  if (s.round_tile && !aligned(p->probs_t)) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+struct BwdWs {
+  void *do_perm, *dh, *ga, *xbuf, *dzq;
+  float *ds_part, *dlogits, *dwg_part;
+};
+
+size_t carve_bwd(const moe_shape& s, char* base, BwdWs* w) {
+  Carver c{base};
+  const int64_t N = max_rows(s);
+  BwdWs q{};
+  q.do_perm = c.take<char>(N * s.d * esz(s));
+  q.dh = c.take<char>(N * 2 * s.d_ff * esz(s));
+  q.ga = c.take<char>(N * s.d_ff * esz(s));
+  q.xbuf = c.take<char>(N * s.d * esz(s));
+  q.ds_part = c.take<float>((size_t)gemm_dact_parts(s) * N * 4);
+  q.dlogits = c.take<float>((size_t)s.T * s.E * 4);
+  q.dzq = c.take<char>((size_t)s.T * ldz_of(s) * esz(s));
+  q.dwg_part = c.take<float>((size_t)gemm_router_dwg_splits(s) * s.E * s.d * 4);
+  if (w) *w = q;
+  return c.off;
+}
+
+size_t experts_ws(const moe_shape& s) { return al((size_t)max_rows(s) * s.d_ff * esz(s)); }
+
+}  // namespace
+
+PlanInternal plan_internal(const moe_shape& s, const moe_plan& p) {
+  PlanInternal pi{};
+  pi.nblk = nblk_of(s);
+  pi.words = words_of(s);
+  char* b = reinterpret_cast<char*>(p.sched);
+  pi.prefix128 = reinterpret_cast<int32_t*>(b);
+  pi.prefix256 = pi.prefix128 + (s.E + 1);
+  b += al(2 * (size_t)(s.E + 1) * 4);
+  pi.hist = reinterpret_cast<int32_t*>(b);
+  b += al((size_t)s.E * pi.nblk * 4);
+  pi.blk_tok = reinterpret_cast<int32_t*>(b);
+  b += al((size_t)(pi.nblk + 1) * 4);
+  pi.sel_t = s.round_tile ? reinterpret_cast<uint32_t*>(b) : nullptr;
+  return pi;
+}
+
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" {
+
+int64_t moe_max_rows(const moe_shape* s) { return (check_shape(s) == MOE_OK) ? max_rows(*s) : -1; }
+
+size_t moe_plan_bytes(const moe_shape* s) {
+  if (check_shape(s) != MOE_OK) return 0;
+  size_t total = 0;
+  carve_plan(*s, nullptr, nullptr, &total);
+  return total;
+}
+
+moe_status moe_plan_init(const moe_shape* s, void* blob, size_t blob_bytes, moe_plan* plan) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!aligned(blob) || !plan) return MOE_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(blob) & (kAlign - 1)) != 0) return MOE_EINVAL;
+  size_t total = 0;
+  carve_plan(*s, nullptr, nullptr, &total);
+  if (blob_bytes < total) return MOE_EWORKSPACE;
+  carve_plan(*s, reinterpret_cast<char*>(blob), plan, nullptr);
+  return MOE_OK;
+}
+
+size_t moe_workspace_bytes(const moe_shape* s, int which) {
+  if (check_shape(s) != MOE_OK) return 0;
+  switch (which) {
+    case MOE_WS_ROUTE: return 0;
+    case MOE_WS_ROUND: return 0;
+    case MOE_WS_EXPERTS: return experts_ws(*s);
+    case MOE_WS_BACKWARD: return carve_bwd(*s, nullptr, nullptr);
+    default: return 0;
+  }
+}
+
+moe_status moe_route(const moe_shape* s, const void* x, const void* w_gate, const float* bias, moe_plan* plan,
+                     void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!aligned(x) || !aligned(w_gate) || (bias && (reinterpret_cast<uintptr_t>(bias) & 3))) return MOE_EINVAL;
+  if ((st = check_plan(*s, plan)) != MOE_OK) return st;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  PlanInternal pi = plan_internal(*s, *plan);
+  hipError_t e = gemm_router_logits(*s, x, w_gate, bias, plan->logits, hs);
+  if (e == hipSuccess) e = launch_topk(*s, *plan, pi, s->round_tile != 0, hs);
+  if (e == hipSuccess) e = launch_plan_build(*s, *plan, pi, true, false, hs);
+  return hip_status(e);
+}
+
+moe_status moe_round_tokens(const moe_shape* s, moe_plan* plan, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (s->round_tile == 0) return MOE_EINVAL;
+  if ((st = check_plan(*s, plan)) != MOE_OK) return st;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  PlanInternal pi = plan_internal(*s, *plan);
+  hipError_t e = launch_round_select(*s, *plan, pi, hs);
+  if (e == hipSuccess) e = launch_plan_build(*s, *plan, pi, false, true, hs);
+  return hip_status(e);
+}
+
+moe_status moe_permute(const moe_shape* s, const void* src, const moe_plan* plan, void* dst, void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!aligned(src) || !aligned(dst)) return MOE_EINVAL;
+  if ((st = check_plan(*s, plan)) != MOE_OK) return st;
+  return hip_status(launch_gather_rows(*s, src, plan->token_of_row, plan->offsets, dst,
+                                       reinterpret_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_grouped_gemm_swiglu(const moe_shape* s, const void* x_perm, const void* w1, const void* w2,
+                                   const moe_plan* plan, void* h_saved, void* y, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!aligned(x_perm) || !aligned(w1) || !aligned(w2) || !aligned(h_saved) || !aligned(y)) return MOE_EINVAL;
+  if ((st = check_plan(*s, plan)) != MOE_OK) return st;
+  if (!aligned(ws) || ws_bytes < experts_ws(*s)) return MOE_EWORKSPACE;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  PlanInternal pi = plan_internal(*s, *plan);
+  hipError_t e = gemm_up_swiglu(*s, *plan, pi, x_perm, w1, h_saved, ws, hs);
+  if (e == hipSuccess) e = gemm_down(*s, *plan, pi, ws, w2, y, hs);
+  return hip_status(e);
+}
+
+moe_status moe_unpermute_combine(const moe_shape* s, const void* y, const moe_plan* plan, void* out, void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!aligned(y) || !aligned(out)) return MOE_EINVAL;
+  if ((st = check_plan(*s, plan)) != MOE_OK) return st;
+  return hip_status(launch_combine(*s, y, *plan, out, reinterpret_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_backward(const moe_shape* s, const void* x, const void* w_gate, const void* w1, const void* w2,
+                        const moe_plan* plan, const void* h_saved, const void* dout, void* dx, float* dw_gate,
+                        float* dw1, float* dw2, float* dlogits, float* ds, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!aligned(x) || !aligned(w_gate) || !aligned(w1) || !aligned(w2) || !aligned(h_saved) || !aligned(dout) ||
+      !aligned(dx) || !aligned(dw_gate) || !aligned(dw1) || !aligned(dw2) || !aligned_or_null(dlogits) ||
+      (ds && (reinterpret_cast<uintptr_t>(ds) & 3)))
+    return MOE_EINVAL;
+  if ((st = check_plan(*s, plan)) != MOE_OK) return st;
+  if (!aligned(ws) || ws_bytes < carve_bwd(*s, nullptr, nullptr)) return MOE_EWORKSPACE;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  PlanInternal pi = plan_internal(*s, *plan);
+  BwdWs w;
+  carve_bwd(*s, reinterpret_cast<char*>(ws), &w);
+  float* dz = dlogits ? dlogits : w.dlogits;
+  const int ldz = ldz_of(*s);
+  hipError_t e = launch_gather_rows(*s, dout, plan->token_of_row, plan->offsets, w.do_perm, hs);
+  if (e == hipSuccess) e = gemm_dact(*s, *plan, pi, w.do_perm, w2, h_saved, w.dh, w.ga, w.ds_part, hs);
+  if (e == hipSuccess) e = launch_gather_rows(*s, x, plan->token_of_row, plan->offsets, w.xbuf, hs);
+  if (e == hipSuccess) e = gemm_dw1(*s, *plan, w.dh, w.xbuf, dw1, hs);
+  if (e == hipSuccess) e = gemm_dw2(*s, *plan, w.do_perm, w.ga, dw2, hs);
+  if (e == hipSuccess) e = gemm_dx_perm(*s, *plan, pi, w.dh, w1, w.xbuf, hs);   // x_perm no longer needed
+  if (e == hipSuccess)
+    e = launch_router_bwd(*s, *plan, w.ds_part, gemm_dact_parts(*s), ds, dz, w.dzq, ldz, hs);
+  if (e == hipSuccess) e = gemm_router_dx(*s, *plan, w.dzq, ldz, w_gate, w.xbuf, dx, hs);
+  if (e == hipSuccess) e = gemm_router_dwg(*s, w.dzq, ldz, x, w.dwg_part, hs);
+  if (e == hipSuccess)
+    e = launch_splitk_reduce(w.dwg_part, gemm_router_dwg_splits(*s), (int64_t)s->E * s->d, dw_gate, hs);
+  return hip_status(e);
+}
+
+moe_status moe_quantize_mx(const void* src_bf16, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                           void* stream) {
+  if (!aligned(src_bf16) || !aligned(codes) || !scales) return MOE_EINVAL;
+  if (rows <= 0 || cols <= 0 || cols % 32) return MOE_EINVAL;
+  return hip_status(launch_quantize_rows(src_bf16, rows, cols, codes, scales, reinterpret_cast<hipStream_t>(stream)));
+}
+
+const char* moe_status_str(moe_status st) {
+  switch (st) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_ENOTSUP: return "shape not supported";
+    case MOE_EWORKSPACE: return "workspace or plan blob too small";
+    case MOE_EHIP: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,185 @@
+// HBM-bound kernels of the layer: the permutation gather (tokens into contiguous
+// per-expert rows, the "row-wise" expert buffers of the Olmo-core 3 article,
+// "three splits" section), the gate-weighted combine ("Beam" blog section 2.2:
+// the output is the gate-weighted sum of the chosen experts' outputs), the
+// router backward, and the split-K reduction.
+//
+// Rows are moved as 16-byte vectors; consecutive threads take consecutive
+// vectors of one row, so every wave reads and writes whole 1 KiB spans.
+#include "moe_common.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+// dst[r] = src[map[r]] for r < offsets[E]; vec = 16-byte vectors per row.
+__global__ __launch_bounds__(256) void gather_rows_kernel(const char* __restrict__ src, const int32_t* __restrict__ map,
+                                                         const int32_t* __restrict__ nrows_ptr, int vec,
+                                                         char* __restrict__ dst, int64_t rows_cap) {
+  const int64_t nrows = *nrows_ptr;
+  const int64_t total = nrows * vec;
+  const int64_t stride = (int64_t)gridDim.x * 256 * 4;
+  for (int64_t base = (int64_t)blockIdx.x * 256 * 4 + threadIdx.x; base < total; base += stride) {
+    u32x4 v[4];
+    int64_t idx[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      idx[u] = base + u * 256;
+      if (idx[u] < total) {
+        int64_t r = idx[u] / vec, c = idx[u] - r * vec;
+        v[u] = ldg16(src + ((int64_t)map[r] * vec + c) * 16);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (idx[u] < total) stg16(dst + idx[u] * 16, v[u]);
+  }
+}
+
+// out[t] = sum over the rows of t (ascending) of gate[r] * y[r], fp32 accumulation.
+template <typename T>
+__global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, const int32_t* __restrict__ tok_ptr,
+                                                     const int32_t* __restrict__ tok_rows,
+                                                     const float* __restrict__ gate, int T_, int d,
+                                                     T* __restrict__ out) {
+  constexpr int EV = 16 / sizeof(T);   // elements per vector
+  const int vec = d / EV;
+  const int64_t total = (int64_t)T_ * vec;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int t = (int)(i / vec), c = (int)(i - (int64_t)t * vec);
+    float acc[EV];
+#pragma unroll
+    for (int q = 0; q < EV; ++q) acc[q] = 0.0f;
+    const int p0 = tok_ptr[t], p1 = tok_ptr[t + 1];
+    for (int p = p0; p < p1; ++p) {
+      const int r = tok_rows[p];
+      const float g = gate[r];
+      u32x4 v = ldg16(y + (int64_t)r * d + c * EV);
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc[2 * q] += g * __uint_as_float(v[q] << 16);
+          acc[2 * q + 1] += g * __uint_as_float(v[q] & 0xffff0000u);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[q] += g * __uint_as_float(v[q]);
+      }
+    }
+    u32x4 o;
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[q] = pack_bf2(acc[2 * q], acc[2 * q + 1]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[q] = __float_as_uint(acc[q]);
+    }
+    stg16(out + (int64_t)t * d + c * EV, o);
+  }
+}
+
+// Router backward, one wave per token.  dS of every row is the fixed-order sum of
+// the per-column-tile partials.  For token t with top-k set K (gates S) and rows
+// A (gates g):  dz_e = [e in A] g_e dS_e - [e in K] S_e * sum_{A} g dS.
+// Writes dlogits (fp32) and the GEMM operand dzq (act dtype, ld = ldz, zero padded).
+template <typename T>
+__global__ __launch_bounds__(256) void router_bwd_kernel(const int32_t* __restrict__ tok_ptr,
+                                                        const int32_t* __restrict__ tok_rows,
+                                                        const int32_t* __restrict__ expert_of_row,
+                                                        const float* __restrict__ gate_of_row,
+                                                        const int32_t* __restrict__ topk_idx,
+                                                        const float* __restrict__ topk_gate,
+                                                        const float* __restrict__ ds_part, int nparts,
+                                                        int64_t part_stride, int T_, int E, int k,
+                                                        float* __restrict__ ds_out, float* __restrict__ dlogits,
+                                                        T* __restrict__ dzq, int ldz) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T_) return;
+  const int p0 = tok_ptr[t], p1 = tok_ptr[t + 1];
+  float vals[4] = {0.f, 0.f, 0.f, 0.f};   // experts lane, lane+64, lane+128, lane+192
+  float acc = 0.0f;
+  for (int p = p0; p < p1; ++p) {
+    const int r = tok_rows[p];
+    float ds = 0.0f;
+    for (int q = 0; q < nparts; ++q) ds += ds_part[q * part_stride + r];
+    if (ds_out && lane == 0) ds_out[r] = ds;
+    const float gds = gate_of_row[r] * ds;
+    acc += gds;
+    const int e = expert_of_row[r];
+    if ((e & 63) == lane) vals[e >> 6] += gds;
+  }
+  for (int j = 0; j < k; ++j) {
+    const int e = topk_idx[(int64_t)t * k + j];
+    if ((e & 63) == lane) vals[e >> 6] -= topk_gate[(int64_t)t * k + j] * acc;
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int e = lane + 64 * v;
+    if (e < E) dlogits[(int64_t)t * E + e] = vals[v];
+    if (e < ldz) Elem<T>::store(dzq + (int64_t)t * ldz + e, e < E ? vals[v] : 0.0f);
+  }
+}
+
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, int nsplit, int64_t n,
+                                                           float* __restrict__ out) {
+  for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; i < n; i += (int64_t)gridDim.x * 256 * 4) {
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < nsplit; ++q) s += *reinterpret_cast<const f32x4*>(part + q * n + i);
+    *reinterpret_cast<f32x4*>(out + i) = s;
+  }
+}
+
+int grid_for(int64_t work, int per_block) {
+  int64_t g = (work + per_block - 1) / per_block;
+  if (g > 256 * 32) g = 256 * 32;
+  if (g < 1) g = 1;
+  return (int)g;
+}
+
+}  // namespace
+
+hipError_t launch_gather_rows(const moe_shape& s, const void* src, const int32_t* rows_map, const int32_t* offsets,
+                              void* dst, hipStream_t st) {
+  const int esz = s.act == MOE_BF16 ? 2 : 4;
+  const int vec = s.d * esz / 16;
+  const int64_t work = max_rows(s) * vec;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(grid_for(work, 1024)), dim3(256), 0, st, (const char*)src, rows_map,
+                     offsets + s.E, vec, (char*)dst, max_rows(s));
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const moe_shape& s, const void* y, const moe_plan& p, void* out, hipStream_t st) {
+  if (s.act == MOE_BF16) {
+    const int64_t work = (int64_t)s.T * (s.d / 8);
+    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(grid_for(work, 256)), dim3(256), 0, st, (const bf16_t*)y,
+                       p.tok_ptr, p.tok_rows, p.gate_of_row, s.T, s.d, (bf16_t*)out);
+  } else {
+    const int64_t work = (int64_t)s.T * (s.d / 4);
+    hipLaunchKernelGGL(combine_kernel<float>, dim3(grid_for(work, 256)), dim3(256), 0, st, (const float*)y,
+                       p.tok_ptr, p.tok_rows, p.gate_of_row, s.T, s.d, (float*)out);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_router_bwd(const moe_shape& s, const moe_plan& p, const float* ds_part, int nparts,
+                             float* ds_out, float* dlogits, void* dzq, int ldz, hipStream_t st) {
+  const int grid = ceil_div(s.T, 4);
+  const int64_t pstride = max_rows(s);
+  if (s.act == MOE_BF16)
+    hipLaunchKernelGGL(router_bwd_kernel<bf16_t>, dim3(grid), dim3(256), 0, st, p.tok_ptr, p.tok_rows,
+                       p.expert_of_row, p.gate_of_row, p.topk_idx, p.topk_gate, ds_part, nparts, pstride, s.T, s.E,
+                       s.k, ds_out, dlogits, (bf16_t*)dzq, ldz);
+  else
+    hipLaunchKernelGGL(router_bwd_kernel<float>, dim3(grid), dim3(256), 0, st, p.tok_ptr, p.tok_rows,
+                       p.expert_of_row, p.gate_of_row, p.topk_idx, p.topk_gate, ds_part, nparts, pstride, s.T, s.E,
+                       s.k, ds_out, dlogits, (float*)dzq, ldz);
+  return hipGetLastError();
+}
+
+hipError_t launch_splitk_reduce(const float* part, int nsplit, int64_t n, float* out, hipStream_t st) {
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(grid_for(n / 4, 256)), dim3(256), 0, st, part, nsplit, n, out);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,207 @@
+// Launchers of the grouped GEMMs of the MoE layer (forward, backward, router).
+//
+// Expert FFN = SwiGLU without biases (h = W1_e x with W1_e = [W_gate; W_up],
+// a = silu(h_gate) * h_up, y = W2_e a).  The per-expert loop of the "Beam"
+// blog's MoELayer (section 5.3) becomes one grouped launch per GEMM ("grouped
+// GEMM" of the Olmo-core 3 article, "three splits" section): tiles are
+// scheduled per expert segment from device-resident offsets, so no routing
+// metadata ever returns to the host.
+//
+// Backward (SonicMoE article, section 1): dA' = dO_perm W2_e is never stored;
+// its epilogue recomputes A from the saved H, reduces dS = <dA', A> per row,
+// and emits dH (SwiGLU backward) and gA = g * A for the W2 gradient.
+#include "gemm_engine.h"
+#include "moe_internal.h"
+
+namespace moe {
+using namespace moe_gemm;
+
+namespace {
+
+template <typename T, int BM, int BN, int WM, int WN, bool AKC, bool BKC, int GROUP, int EPI>
+hipError_t run(const Args& a, int64_t logical_tiles, hipStream_t st) {
+  auto kern = grouped_gemm<T, BM, BN, WM, WN, AKC, BKC, GROUP, EPI>;
+  constexpr size_t lds = (size_t)2 * (BM + BN) * 128;
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  const int64_t grid = 8 * ((logical_tiles + 7) / 8);
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(WM * WN * 64), lds, st, a);
+  return hipGetLastError();
+}
+
+Args base_args() {
+  Args a{};
+  a.ksplit = 1;
+  return a;
+}
+
+int64_t grouped_m_tiles(const moe_shape& s, int bm) { return (max_rows(s) + bm - 1) / bm + s.E; }
+
+}  // namespace
+
+// ---------------------------------------------------------------- forward
+
+hipError_t gemm_up_swiglu(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const void* x_perm,
+                          const void* w1, void* h, void* act, hipStream_t st) {
+  Args a = base_args();
+  a.A = x_perm; a.lda = s.d;
+  a.B = w1; a.ldb = s.d; a.b_estride = (int64_t)2 * s.d_ff * s.d;
+  a.C = h; a.ldc = 2 * s.d_ff;
+  a.C2 = act; a.ldc2 = s.d_ff;
+  a.offsets = p.offsets;
+  a.N = 2 * s.d_ff; a.K = s.d; a.E = s.E; a.f = s.d_ff;
+  if (s.act == MOE_BF16) {
+    a.tile_prefix = pi.prefix256; a.tilesN = a.N / 256;
+    return run<bf16_t, 256, 256, 2, 4, true, true, GROUP_M, EPI_SWIGLU>(a, grouped_m_tiles(s, 256) * a.tilesN, st);
+  }
+  a.tile_prefix = pi.prefix128; a.tilesN = a.N / 128;
+  return run<float, 128, 128, 2, 2, true, true, GROUP_M, EPI_SWIGLU>(a, grouped_m_tiles(s, 128) * a.tilesN, st);
+}
+
+hipError_t gemm_down(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const void* act,
+                     const void* w2, void* y, hipStream_t st) {
+  Args a = base_args();
+  a.A = act; a.lda = s.d_ff;
+  a.B = w2; a.ldb = s.d_ff; a.b_estride = (int64_t)s.d * s.d_ff;
+  a.C = y; a.ldc = s.d;
+  a.offsets = p.offsets;
+  a.N = s.d; a.K = s.d_ff; a.E = s.E; a.f = s.d_ff;
+  if (s.act == MOE_BF16) {
+    a.tile_prefix = pi.prefix256; a.tilesN = ceil_div(a.N, 256);
+    return run<bf16_t, 256, 256, 2, 4, true, true, GROUP_M, EPI_ACT>(a, grouped_m_tiles(s, 256) * a.tilesN, st);
+  }
+  a.tile_prefix = pi.prefix128; a.tilesN = ceil_div(a.N, 128);
+  return run<float, 128, 128, 2, 2, true, true, GROUP_M, EPI_ACT>(a, grouped_m_tiles(s, 128) * a.tilesN, st);
+}
+
+// ---------------------------------------------------------------- backward
+
+int gemm_dact_parts(const moe_shape& s) { return ceil_div(s.d_ff, s.act == MOE_BF16 ? 256 : 128); }
+
+hipError_t gemm_dact(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const void* do_perm,
+                     const void* w2, const void* h, void* dh, void* ga, float* ds_part, hipStream_t st) {
+  Args a = base_args();
+  a.A = do_perm; a.lda = s.d;
+  a.B = w2; a.ldb = s.d_ff; a.b_estride = (int64_t)s.d * s.d_ff;   // W2_e read as [K = d, N = f]
+  a.C = dh; a.ldc = 2 * s.d_ff;
+  a.C2 = ga; a.ldc2 = s.d_ff;
+  a.C3 = ds_part; a.ldc3 = max_rows(s);
+  a.aux = h; a.ld_aux = 2 * s.d_ff;
+  a.row_gate = p.gate_of_row;
+  a.offsets = p.offsets;
+  a.N = s.d_ff; a.K = s.d; a.E = s.E; a.f = s.d_ff;
+  if (s.act == MOE_BF16) {
+    a.tile_prefix = pi.prefix256; a.tilesN = ceil_div(a.N, 256);
+    return run<bf16_t, 256, 256, 2, 4, true, false, GROUP_M, EPI_DSWIGLU>(a, grouped_m_tiles(s, 256) * a.tilesN, st);
+  }
+  a.tile_prefix = pi.prefix128; a.tilesN = ceil_div(a.N, 128);
+  return run<float, 128, 128, 2, 2, true, false, GROUP_M, EPI_DSWIGLU>(a, grouped_m_tiles(s, 128) * a.tilesN, st);
+}
+
+hipError_t gemm_dx_perm(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const void* dh,
+                        const void* w1, void* dx_perm, hipStream_t st) {
+  Args a = base_args();
+  a.A = dh; a.lda = 2 * s.d_ff;
+  a.B = w1; a.ldb = s.d; a.b_estride = (int64_t)2 * s.d_ff * s.d;    // W1_e read as [K = 2f, N = d]
+  a.C = dx_perm; a.ldc = s.d;
+  a.offsets = p.offsets;
+  a.N = s.d; a.K = 2 * s.d_ff; a.E = s.E; a.f = s.d_ff;
+  if (s.act == MOE_BF16) {
+    a.tile_prefix = pi.prefix256; a.tilesN = ceil_div(a.N, 256);
+    return run<bf16_t, 256, 256, 2, 4, true, false, GROUP_M, EPI_ACT>(a, grouped_m_tiles(s, 256) * a.tilesN, st);
+  }
+  a.tile_prefix = pi.prefix128; a.tilesN = ceil_div(a.N, 128);
+  return run<float, 128, 128, 2, 2, true, false, GROUP_M, EPI_ACT>(a, grouped_m_tiles(s, 128) * a.tilesN, st);
+}
+
+// dW1_e [2f, d] = dH_e^T X_perm_e and dW2_e [d, f] = dO_perm_e^T gA_e: the
+// reduction runs over the expert's rows (variable K), fp32 outputs.
+hipError_t gemm_dw1(const moe_shape& s, const moe_plan& p, const void* dh, const void* x_perm, float* dw1,
+                    hipStream_t st) {
+  Args a = base_args();
+  a.A = dh; a.lda = 2 * s.d_ff;          // [K = rows, M = 2f]
+  a.B = x_perm; a.ldb = s.d;             // [K = rows, N = d]
+  a.C = dw1; a.ldc = s.d; a.c_estride = (int64_t)2 * s.d_ff * s.d;
+  a.offsets = p.offsets;
+  a.M = 2 * s.d_ff; a.N = s.d; a.E = s.E;
+  const int bm = s.act == MOE_BF16 ? 256 : 128;
+  a.tilesM = ceil_div(a.M, bm); a.tilesN = ceil_div(a.N, bm);
+  a.total_static = s.E * a.tilesM * a.tilesN;
+  if (s.act == MOE_BF16) return run<bf16_t, 256, 256, 2, 4, false, false, GROUP_K, EPI_F32>(a, a.total_static, st);
+  return run<float, 128, 128, 2, 2, false, false, GROUP_K, EPI_F32>(a, a.total_static, st);
+}
+
+hipError_t gemm_dw2(const moe_shape& s, const moe_plan& p, const void* do_perm, const void* ga, float* dw2,
+                    hipStream_t st) {
+  Args a = base_args();
+  a.A = do_perm; a.lda = s.d;            // [K = rows, M = d]
+  a.B = ga; a.ldb = s.d_ff;              // [K = rows, N = f]
+  a.C = dw2; a.ldc = s.d_ff; a.c_estride = (int64_t)s.d * s.d_ff;
+  a.offsets = p.offsets;
+  a.M = s.d; a.N = s.d_ff; a.E = s.E;
+  const int bm = s.act == MOE_BF16 ? 256 : 128;
+  a.tilesM = ceil_div(a.M, bm); a.tilesN = ceil_div(a.N, bm);
+  a.total_static = s.E * a.tilesM * a.tilesN;
+  if (s.act == MOE_BF16) return run<bf16_t, 256, 256, 2, 4, false, false, GROUP_K, EPI_F32>(a, a.total_static, st);
+  return run<float, 128, 128, 2, 2, false, false, GROUP_K, EPI_F32>(a, a.total_static, st);
+}
+
+// ---------------------------------------------------------------- router
+
+hipError_t gemm_router_logits(const moe_shape& s, const void* x, const void* wg, const float* bias,
+                              float* logits, hipStream_t st) {
+  Args a = base_args();
+  a.A = x; a.lda = s.d;
+  a.B = wg; a.ldb = s.d;
+  a.C = logits; a.ldc = s.E;
+  a.bias = bias;
+  a.M = s.T; a.N = s.E; a.K = s.d;
+  a.tilesM = ceil_div(s.T, 128); a.tilesN = ceil_div(s.E, 64);
+  a.total_static = a.tilesM * a.tilesN;
+  if (s.act == MOE_BF16) return run<bf16_t, 128, 64, 4, 1, true, true, GROUP_NONE, EPI_LOGITS>(a, a.total_static, st);
+  return run<float, 128, 64, 4, 1, true, true, GROUP_NONE, EPI_LOGITS>(a, a.total_static, st);
+}
+
+// dx[t] = dzq[t] W_g + sum over the rows of t of dx_perm[row]   (router term + unpermute-sum)
+hipError_t gemm_router_dx(const moe_shape& s, const moe_plan& p, const void* dzq, int ldz, const void* wg,
+                          const void* dx_perm, void* dx, hipStream_t st) {
+  Args a = base_args();
+  a.A = dzq; a.lda = ldz;                // [T, K = E]
+  a.B = wg; a.ldb = s.d;                 // W_g [E, d] read as [K = E, N = d]
+  a.C = dx; a.ldc = s.d;
+  a.csr_ptr = p.tok_ptr; a.csr_rows = p.tok_rows; a.gsrc = dx_perm; a.ld_gsrc = s.d;
+  a.M = s.T; a.N = s.d; a.K = s.E;
+  a.tilesM = ceil_div(s.T, 128); a.tilesN = ceil_div(s.d, 128);
+  a.total_static = a.tilesM * a.tilesN;
+  if (s.act == MOE_BF16) return run<bf16_t, 128, 128, 2, 2, true, false, GROUP_NONE, EPI_DX>(a, a.total_static, st);
+  return run<float, 128, 128, 2, 2, true, false, GROUP_NONE, EPI_DX>(a, a.total_static, st);
+}
+
+int gemm_router_dwg_splits(const moe_shape& s) {
+  const int tiles = ceil_div(s.E, 128) * ceil_div(s.d, 128);
+  int sp = ceil_div(512, tiles);
+  const int maxsp = ceil_div(s.T, 256);
+  if (sp > maxsp) sp = maxsp;
+  if (sp < 1) sp = 1;
+  return sp;
+}
+
+// dW_g partials: part[split] [E, d] = dzq[K-slice]^T x[K-slice]
+hipError_t gemm_router_dwg(const moe_shape& s, const void* dzq, int ldz, const void* x, float* part,
+                           hipStream_t st) {
+  Args a = base_args();
+  a.A = dzq; a.lda = ldz;                // [K = T, M = E]
+  a.B = x; a.ldb = s.d;                  // [K = T, N = d]
+  a.C = part; a.ldc = s.d; a.c_kstride = (int64_t)s.E * s.d;
+  a.M = s.E; a.N = s.d; a.K = s.T;
+  a.ksplit = gemm_router_dwg_splits(s);
+  a.tilesM = ceil_div(s.E, 128); a.tilesN = ceil_div(s.d, 128);
+  a.total_static = a.tilesM * a.tilesN * a.ksplit;
+  if (s.act == MOE_BF16) return run<bf16_t, 128, 128, 2, 2, false, false, GROUP_NONE, EPI_F32>(a, a.total_static, st);
+  return run<float, 128, 128, 2, 2, false, false, GROUP_NONE, EPI_F32>(a, a.total_static, st);
+}
+
+}  // namespace moe

@@ -1,0 +1,475 @@
+// Grouped GEMM engine for gfx950 (CDNA4): one template covers every expert GEMM
+// of the MoE layer and the two router GEMMs.
+//
+//   D[m, n] = sum_k A[m, k] * B[n, k]        (B given as [N,K] or as [K,N])
+//
+// * Element type: bf16 (v_mfma_f32_32x32x16_bf16) or fp32 (v_mfma_f32_32x32x2_f32);
+//   fp32 accumulation either way.
+// * Operand layouts: "KC" = K contiguous ([rows, K] row-major), or "MN" = M/N
+//   contiguous ([K, rows]); MN operands are transposed in registers while they
+//   are staged into LDS, so the LDS tile is always [rows][K] and the MFMA loop
+//   is the same for every variant.
+// * Grouping: GROUP_M -- rows of A are split into per-expert segments given by
+//   device offsets (forward GEMMs, dA', dX); GROUP_K -- the reduction runs over
+//   one expert's segment of rows (weight gradients, variable K); GROUP_NONE --
+//   one plain problem (router GEMMs), optionally split along K.
+// * Tiles: BM x BN block tile, BK = 128 bytes of K per stage, WM x WN waves,
+//   each wave owns (BM/WM) x (BN/WN) as 32x32 MFMA sub-tiles.  Two LDS stages,
+//   register-staged global loads for stage k+1 overlap the MFMAs of stage k.
+//   LDS rows are 128 B; 16-byte chunks are XOR-swizzled by (row ^ row>>3) & 7 so
+//   the MFMA fragment reads (32 consecutive rows, one chunk) and the transposed
+//   stores (rows 8 apart) are both free of bank conflicts.
+// * Block -> tile order is XCD-aware: hardware block b runs on XCD b % 8, so
+//   consecutive logical tiles (same expert and weight tile) go to one XCD and
+//   share its L2.
+#pragma once
+#include <type_traits>
+#include "moe_common.h"
+
+namespace moe_gemm {
+
+enum { GROUP_M = 0, GROUP_K = 1, GROUP_NONE = 2 };
+enum { EPI_ACT = 0, EPI_F32 = 1, EPI_SWIGLU = 2, EPI_DSWIGLU = 3, EPI_LOGITS = 4, EPI_DX = 5 };
+
+struct Args {
+  const void* A; int64_t lda; int64_t a_estride; const int32_t* a_gather;
+  const void* B; int64_t ldb; int64_t b_estride;
+  void* C; int64_t ldc; int64_t c_estride;
+  void* C2; int64_t ldc2;
+  float* C3; int64_t ldc3;
+  const void* aux; int64_t ld_aux;
+  const float* row_gate;
+  const float* bias;
+  const int32_t* offsets;       // [E+1] segment offsets (GROUP_M rows, GROUP_K reduction rows)
+  const int32_t* tile_prefix;   // [E+1] prefix of per-expert m-tile counts (GROUP_M)
+  const int32_t* csr_ptr; const int32_t* csr_rows; const void* gsrc; int64_t ld_gsrc;
+  int M, N, K, E, f;
+  int tilesM, tilesN;
+  int total_static;             // GROUP_K / GROUP_NONE: number of logical tiles
+  int ksplit;                   // GROUP_NONE: number of K slices (1 = none)
+  int64_t c_kstride;            // GROUP_NONE split-K: stride between partial outputs
+};
+
+MOE_DEV int swz(int row) { return (row ^ (row >> 3)) & 7; }
+MOE_DEV int lds_off(int row, int byte) {  // byte offset inside a 128 B row
+  return row * 128 + ((((byte >> 4) ^ swz(row)) << 4) | (byte & 15));
+}
+
+// ---------------------------------------------------------------- staging
+// One operand tile: ROWS rows x 128 bytes of K.
+
+template <typename T, int ROWS, int NT>
+struct KcStage {  // K-contiguous source
+  static constexpr int CHUNKS = ROWS * 8;
+  static constexpr int PER = CHUNKS / NT;
+  static constexpr int EPC = 16 / sizeof(T);
+  static_assert(CHUNKS % NT == 0, "K-contiguous tile must split evenly");
+  const T* rowp[PER];
+  u32x4 v[PER];
+  // rowfn(row) -> pointer to element (row, 0) of this tile's source row
+  template <class RowFn>
+  MOE_DEV void init(RowFn rowfn) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      int c = threadIdx.x + i * NT;
+      rowp[i] = rowfn(c >> 3) + (c & 7) * EPC;
+    }
+  }
+  // k0: first K element of the stage; kvalid: valid K elements from k0 (per-chunk mask)
+  MOE_DEV void load(int k0, int kvalid) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      int ch = (threadIdx.x + i * NT) & 7;
+      if (ch * EPC < kvalid) v[i] = ldg16(rowp[i] + k0);
+      else v[i] = u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  MOE_DEV void store(char* lds) const {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      int c = threadIdx.x + i * NT;
+      *reinterpret_cast<u32x4*>(lds + lds_off(c >> 3, (c & 7) << 4)) = v[i];
+    }
+  }
+};
+
+template <typename T, int ROWS, int NT>
+struct MnStage {  // M/N-contiguous source: element (k, row) at base + k*ld + row
+  static constexpr int V = 16 / sizeof(T);            // rows per 16 B vector
+  static constexpr int BK = 128 / sizeof(T);
+  static constexpr int EPT = ROWS * BK / NT;          // elements per thread
+  static constexpr int R0 = EPT / V;                  // k values per thread
+  static constexpr int R = R0 > 8 ? 8 : R0;           // k per unit
+  static constexpr int UPT = R0 / R;                  // units per thread
+  static_assert(EPT % V == 0 && R0 % R == 0 && R >= 2, "transposed tile must split evenly");
+  static constexpr int RB = ROWS / V;                 // row blocks
+  u32x4 v[UPT][R];
+  // base points at (k0, row0); kvalid = valid k rows from k0; rvalid = valid rows
+  MOE_DEV void load(const T* base, int64_t ld, int kvalid, int rvalid) {
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      int unit = threadIdx.x + u * NT;
+      int rb = unit % RB, kb = unit / RB;
+#pragma unroll
+      for (int r = 0; r < R; ++r) {
+        int k = kb * R + r;
+        int row = rb * V;
+        if (k < kvalid && row < rvalid) v[u][r] = ldg16(base + (int64_t)k * ld + row);
+        else v[u][r] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+  MOE_DEV void store(char* lds) const {
+#pragma unroll
+    for (int u = 0; u < UPT; ++u) {
+      int unit = threadIdx.x + u * NT;
+      int rb = unit % RB, kb = unit / RB;
+      int kbyte = kb * R * (int)sizeof(T);
+      if constexpr (sizeof(T) == 2) {
+        // 8 rows x R k values of bf16: output row j collects element j of each k vector
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          uint32_t w[4];
+#pragma unroll
+          for (int p = 0; p < R / 2; ++p) {
+            uint32_t a = v[u][2 * p][j >> 1], b = v[u][2 * p + 1][j >> 1];
+            uint32_t lo = (j & 1) ? (a >> 16) : (a & 0xffffu);
+            uint32_t hi = (j & 1) ? (b & 0xffff0000u) : (b << 16);
+            w[p] = lo | hi;
+          }
+          char* dst = lds + lds_off(rb * 8 + j, kbyte);
+          if constexpr (R == 8) *reinterpret_cast<u32x4*>(dst) = u32x4{w[0], w[1], w[2], w[3]};
+          else if constexpr (R == 4) *reinterpret_cast<uint2*>(dst) = make_uint2(w[0], w[1]);
+          else *reinterpret_cast<uint32_t*>(dst) = w[0];
+        }
+      } else {
+        // 4 rows x R k values of fp32
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint32_t w[8];
+#pragma unroll
+          for (int r = 0; r < R; ++r) w[r] = v[u][r][j];
+          if constexpr (R >= 4) {
+#pragma unroll
+            for (int q = 0; q < R / 4; ++q)  // each 16 B chunk has its own swizzled slot
+              *reinterpret_cast<u32x4*>(lds + lds_off(rb * 4 + j, kbyte + 16 * q)) =
+                  u32x4{w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]};
+          } else {
+            *reinterpret_cast<uint2*>(lds + lds_off(rb * 4 + j, kbyte)) = make_uint2(w[0], w[1]);
+          }
+        }
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------- MFMA step
+
+template <typename T> struct Mma;
+template <> struct Mma<bf16_t> {
+  // one 16-byte fragment per lane = 8 k values -> one 32x32x16 MFMA
+  static MOE_DEV void run(f32x16& acc, u32x4 a, u32x4 b) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), acc, 0, 0, 0);
+  }
+};
+template <> struct Mma<float> {
+  // one 16-byte fragment per lane = 4 k values -> four 32x32x2 MFMAs; lanes 0-31
+  // and 32-63 hold different k, identically for A and B, so every product pairs up
+  static MOE_DEV void run(f32x16& acc, u32x4 a, u32x4 b) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[j]), __uint_as_float(b[j]), acc, 0, 0, 0);
+  }
+};
+
+// ---------------------------------------------------------------- kernel
+
+template <typename T, int BM, int BN, int WM, int WN, bool AKC, bool BKC, int GROUP, int EPI>
+__global__ __launch_bounds__(WM* WN * 64) void grouped_gemm(Args args) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int BK = 128 / sizeof(T);
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  static_assert(TM >= 1 && TN >= 1, "wave tile must hold a 32x32 MFMA tile");
+  static_assert(EPI != EPI_SWIGLU || TN % 2 == 0, "SwiGLU needs gate and up tiles per wave");
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  // stage s: A tile at s*(BM+BN)*128, B tile right after it
+  auto a_stage = [&](int st) -> char* { return smem + st * (BM + BN) * 128; };
+  auto b_stage = [&](int st) -> char* { return smem + st * (BM + BN) * 128 + BM * 128; };
+
+  // ---- logical tile (XCD-aware order)
+  int total;
+  if constexpr (GROUP == GROUP_M) total = args.tile_prefix[args.E] * args.tilesN;
+  else total = args.total_static;
+  const int per = (total + 7) >> 3;
+  const int b = blockIdx.x;
+  if ((b >> 3) >= per) return;
+  const int L = (b & 7) * per + (b >> 3);
+  if (L >= total) return;
+
+  int e = 0, mt = 0, nt = 0, split = 0;
+  int row_begin = 0, row_end = 0;     // GROUP_M: rows of A / D;  others: unused
+  int k_begin = 0, k_end = args.K;    // reduction range (rows of MN operands for GROUP_K)
+  if constexpr (GROUP == GROUP_M) {
+    int lo = 0, hi = args.E;          // find e: prefix[e]*tilesN <= L < prefix[e+1]*tilesN
+    while (hi - lo > 1) {
+      int mid = (lo + hi) >> 1;
+      if (args.tile_prefix[mid] * args.tilesN <= L) lo = mid; else hi = mid;
+    }
+    e = lo;
+    int p0 = args.tile_prefix[e], cnt = args.tile_prefix[e + 1] - p0;
+    int r = L - p0 * args.tilesN;
+    nt = r / cnt;
+    mt = r - nt * cnt;
+    row_begin = args.offsets[e] + mt * BM;
+    row_end = args.offsets[e + 1];
+  } else if constexpr (GROUP == GROUP_K) {
+    int pe = args.tilesM * args.tilesN;
+    e = L / pe;
+    int r = L - e * pe;
+    nt = r / args.tilesM;
+    mt = r - nt * args.tilesM;
+    k_begin = args.offsets[e];
+    k_end = args.offsets[e + 1];
+  } else {
+    int pe = args.tilesM * args.tilesN;
+    split = L / pe;
+    int r = L - split * pe;
+    nt = r / args.tilesM;
+    mt = r - nt * args.tilesM;
+    int kc = (((args.K + args.ksplit - 1) / args.ksplit) + BK - 1) / BK * BK;
+    k_begin = split * kc;
+    k_end = min(args.K, k_begin + kc);
+  }
+  const int m0 = mt * BM, n0 = nt * BN;
+  const T* Ab = reinterpret_cast<const T*>(args.A) + (int64_t)e * args.a_estride;
+  const T* Bb = reinterpret_cast<const T*>(args.B) + (int64_t)e * args.b_estride;
+
+  // ---- operand row pointers (K-contiguous operands)
+  auto a_row = [&](int row) -> const T* {
+    if constexpr (GROUP == GROUP_M) {
+      int g = row_begin + row;
+      if (g >= row_end) g = row_end - 1;       // rows past the segment only feed unstored outputs
+      int src = args.a_gather ? args.a_gather[g] : g;
+      return Ab + (int64_t)src * args.lda;
+    } else {
+      int g = m0 + row;
+      if (g >= args.M) g = args.M - 1;
+      return Ab + (int64_t)g * args.lda;
+    }
+  };
+  auto b_row = [&](int row) -> const T* {
+    int j = n0 + row;
+    if constexpr (EPI == EPI_SWIGLU) {
+      // wave wn's columns: first half gate rows, second half the matching up rows
+      int wn = row / WTN, jj = row % WTN;
+      int g = nt * (BN / 2) + wn * (WTN / 2) + (jj % (WTN / 2));
+      j = (jj < WTN / 2) ? g : (args.f + g);
+    }
+    if (j >= args.N && EPI != EPI_SWIGLU) j = args.N - 1;
+    return Bb + (int64_t)j * args.ldb;
+  };
+
+  using AStage = typename std::conditional<AKC, KcStage<T, BM, NT>, MnStage<T, BM, NT>>::type;
+  using BStage = typename std::conditional<BKC, KcStage<T, BN, NT>, MnStage<T, BN, NT>>::type;
+  AStage sa;
+  BStage sb;
+  if constexpr (AKC) sa.init(a_row);
+  if constexpr (BKC) sb.init(b_row);
+
+  auto load_tiles = [&](int k0) {
+    int kvalid = k_end - k0;
+    if constexpr (AKC) {
+      sa.load(k0, kvalid);
+    } else {
+      // A stored [K, M]: rows of the tile are M positions
+      sa.load(Ab + (int64_t)k0 * args.lda + m0, args.lda, kvalid, args.M - m0);
+    }
+    if constexpr (BKC) {
+      sb.load(k0, kvalid);
+    } else {
+      sb.load(Bb + (int64_t)k0 * args.ldb + n0, args.ldb, kvalid, args.N - n0);
+    }
+  };
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+
+  const int nk = (k_end > k_begin) ? (k_end - k_begin + BK - 1) / BK : 0;
+  if (nk > 0) {
+    load_tiles(k_begin);
+    sa.store(a_stage(0));
+    sb.store(b_stage(0));
+    __syncthreads();
+  }
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    const bool more = kt + 1 < nk;
+    if (more) load_tiles(k_begin + (kt + 1) * BK);
+    const char* as = a_stage(cur);
+    const char* bs = b_stage(cur);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int kbyte = (ks * 2 + (lane >> 5)) << 4;
+      u32x4 af[TM], bfr[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        af[i] = *reinterpret_cast<const u32x4*>(as + lds_off(wm * WTM + i * 32 + (lane & 31), kbyte));
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        bfr[j] = *reinterpret_cast<const u32x4*>(bs + lds_off(wn * WTN + j * 32 + (lane & 31), kbyte));
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) Mma<T>::run(acc[i][j], af[i], bfr[j]);
+    }
+    if (more) {
+      sa.store(a_stage(cur ^ 1));
+      sb.store(b_stage(cur ^ 1));
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogues.  Sub-tile (i, j), register q holds
+  //      row = wm*WTM + i*32 + 8*(q/4) + 4*(lane/32) + q%4,  col = wn*WTN + j*32 + lane%32
+  const int rbase = wm * WTM + 4 * (lane >> 5);
+  const int cbase = wn * WTN + (lane & 31);
+
+  if constexpr (EPI == EPI_ACT || EPI == EPI_F32 || EPI == EPI_LOGITS) {
+    using OT = typename std::conditional<EPI == EPI_ACT, T, float>::type;
+    OT* C = reinterpret_cast<OT*>(args.C);
+    if constexpr (GROUP == GROUP_K) C += (int64_t)e * args.c_estride;
+    if constexpr (GROUP == GROUP_NONE) C += (int64_t)split * args.c_kstride;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        int r = rbase + i * 32 + 8 * (q >> 2) + (q & 3);
+        int grow;
+        bool ok;
+        if constexpr (GROUP == GROUP_M) { grow = row_begin + r; ok = grow < row_end; }
+        else { grow = m0 + r; ok = grow < args.M; }
+        if (!ok) continue;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          int col = n0 + cbase + j * 32;
+          if (col >= args.N) continue;
+          float v = acc[i][j][q];
+          if constexpr (EPI == EPI_LOGITS) { if (args.bias) v += args.bias[col]; }
+          Elem<OT>::store(C + (int64_t)grow * args.ldc + col, v);
+        }
+      }
+  } else if constexpr (EPI == EPI_SWIGLU) {
+    // H (C, ld 2f) gets both halves; A (C2, ld f) = silu(H_gate) * H_up from the stored H
+    T* H = reinterpret_cast<T*>(args.C);
+    T* Aout = reinterpret_cast<T*>(args.C2);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        int r = rbase + i * 32 + 8 * (q >> 2) + (q & 3);
+        int grow = row_begin + r;
+        if (grow >= row_end) continue;
+#pragma unroll
+        for (int j = 0; j < TN / 2; ++j) {
+          int gcol = nt * (BN / 2) + wn * (WTN / 2) + j * 32 + (lane & 31);
+          T* hrow = H + (int64_t)grow * args.ldc;
+          float hg = acc[i][j][q], hu = acc[i][j + TN / 2][q];
+          if constexpr (sizeof(T) == 2) {  // A is computed from H as stored
+            hg = bf2f(f2bf(hg));
+            hu = bf2f(f2bf(hu));
+          }
+          Elem<T>::store(hrow + gcol, hg);
+          Elem<T>::store(hrow + args.f + gcol, hu);
+          float a = hg / (1.0f + expf(-hg)) * hu;
+          Elem<T>::store(Aout + (int64_t)grow * args.ldc2 + gcol, a);
+        }
+      }
+  } else if constexpr (EPI == EPI_DSWIGLU) {
+    // acc = dA' (columns n0.. of f).  aux = H [rows, 2f]; C = dH [rows, 2f];
+    // C2 = gA [rows, f]; C3 = dS partial for this column tile: C3[nt * ldc3 + row]
+    const T* H = reinterpret_cast<const T*>(args.aux);
+    T* dH = reinterpret_cast<T*>(args.C);
+    T* gA = reinterpret_cast<T*>(args.C2);
+    float* red = reinterpret_cast<float*>(smem);   // LDS is free after the main loop
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        int r = rbase + i * 32 + 8 * (q >> 2) + (q & 3);
+        int grow = row_begin + r;
+        bool ok = grow < row_end;
+        float part = 0.0f;
+        if (ok) {
+          float g = args.row_gate[grow];
+          const T* hrow = H + (int64_t)grow * args.ld_aux;
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            int col = n0 + cbase + j * 32;
+            if (col >= args.N) continue;
+            float dap = acc[i][j][q];
+            float hg = Elem<T>::load(hrow + col);
+            float hu = Elem<T>::load(hrow + args.f + col);
+            float sg = 1.0f / (1.0f + expf(-hg));
+            float sl = hg * sg;
+            float a = sl * hu;
+            if constexpr (sizeof(T) == 2) a = bf2f(f2bf(a));   // A as stored in the forward
+            part += dap * a;
+            float da = g * dap;
+            float dsl = sg * (1.0f + hg * (1.0f - sg));
+            T* drow = dH + (int64_t)grow * args.ldc;
+            Elem<T>::store(drow + col, da * hu * dsl);
+            Elem<T>::store(drow + args.f + col, da * sl);
+            Elem<T>::store(gA + (int64_t)grow * args.ldc2 + col, g * a);
+          }
+        }
+        // sum over the 32 columns held by lanes with the same lane/32
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) part += __shfl_xor(part, o, 64);
+        if ((lane & 31) == 0) red[wn * BM + r] = part;
+      }
+    __syncthreads();
+    for (int r = threadIdx.x; r < BM; r += NT) {
+      int grow = row_begin + r;
+      if (grow < row_end) {
+        float s = 0.0f;
+#pragma unroll
+        for (int w = 0; w < WN; ++w) s += red[w * BM + r];
+        args.C3[(int64_t)nt * args.ldc3 + grow] = s;
+      }
+    }
+  } else if constexpr (EPI == EPI_DX) {
+    // dx[t, c] = acc + sum over the rows of t of gsrc[row, c]  (router term + unpermute-sum)
+    T* C = reinterpret_cast<T*>(args.C);
+    const T* G = reinterpret_cast<const T*>(args.gsrc);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        int t = m0 + rbase + i * 32 + 8 * (q >> 2) + (q & 3);
+        if (t >= args.M) continue;
+        int p0 = args.csr_ptr[t], p1 = args.csr_ptr[t + 1];
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          int col = n0 + cbase + j * 32;
+          if (col >= args.N) continue;
+          float v = acc[i][j][q];
+          for (int p = p0; p < p1; ++p) v += Elem<T>::load(G + (int64_t)args.csr_rows[p] * args.ld_gsrc + col);
+          Elem<T>::store(C + (int64_t)t * args.ldc + col, v);
+        }
+      }
+  }
+}
+
+template <typename T, int BM, int BN, int WM, int WN>
+constexpr size_t lds_bytes() { return (size_t)2 * (BM + BN) * 128; }
+
+}  // namespace moe_gemm

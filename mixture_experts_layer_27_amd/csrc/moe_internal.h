@@ -1,0 +1,77 @@
+// Internal declarations shared by the host-side translation units.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+constexpr int kPlanBlock = 256;     // tokens per block in the plan kernels
+constexpr int kBmSmall = 128;       // m-tile of the fp32 grouped GEMMs
+constexpr int kBmLarge = 256;       // m-tile of the bf16 grouped GEMMs
+
+// Internal region of the plan blob (plan.sched points at its start):
+//   [0, E+1)            m-tile prefix for BM = 128
+//   [E+1, 2E+2)         m-tile prefix for BM = 256
+//   hist [E * nblk]     per-(expert, token block) counts, then bases after the scan
+//   blk_tok [nblk + 1]  rows per token block, then its exclusive scan
+//   sel_t [E * ceil(T/32)] (rounding only) bit t of row e: token t selected expert e
+struct PlanInternal {
+  int32_t* prefix128;
+  int32_t* prefix256;
+  int32_t* hist;
+  int32_t* blk_tok;
+  uint32_t* sel_t;
+  int nblk;
+  int words;   // ceil(E/32)
+};
+PlanInternal plan_internal(const moe_shape& s, const moe_plan& p);
+int64_t max_rows(const moe_shape& s);
+inline int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+// ---- routing (route.hip)
+hipError_t launch_topk(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, bool rounding,
+                       hipStream_t st);
+hipError_t launch_plan_build(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, bool raw,
+                             bool with_prob_gates, hipStream_t st);
+hipError_t launch_round_select(const moe_shape& s, const moe_plan& p, const PlanInternal& pi,
+                               hipStream_t st);
+
+// ---- elementwise (elementwise.hip)
+hipError_t launch_gather_rows(const moe_shape& s, const void* src, const int32_t* rows_map,
+                              const int32_t* offsets, void* dst, hipStream_t st);
+hipError_t launch_combine(const moe_shape& s, const void* y, const moe_plan& p, void* out,
+                          hipStream_t st);
+hipError_t launch_router_bwd(const moe_shape& s, const moe_plan& p, const float* ds_part, int nparts,
+                             float* ds_out, float* dlogits, void* dzq, int ldz, hipStream_t st);
+hipError_t launch_splitk_reduce(const float* part, int nsplit, int64_t n, float* out, hipStream_t st);
+
+// ---- grouped GEMMs (gemm.hip)
+struct GemmPlanView {
+  const int32_t* offsets;
+  const int32_t* prefix;   // m-tile prefix matching the kernel's BM
+  int64_t n_max;
+};
+hipError_t gemm_up_swiglu(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const void* x_perm,
+                          const void* w1, void* h, void* a, hipStream_t st);
+hipError_t gemm_down(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const void* a,
+                     const void* w2, void* y, hipStream_t st);
+hipError_t gemm_dact(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const void* do_perm,
+                     const void* w2, const void* h, void* dh, void* ga, float* ds_part, hipStream_t st);
+int gemm_dact_parts(const moe_shape& s);
+hipError_t gemm_dx_perm(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const void* dh,
+                        const void* w1, void* dx_perm, hipStream_t st);
+hipError_t gemm_dw1(const moe_shape& s, const moe_plan& p, const void* dh, const void* x_perm, float* dw1,
+                    hipStream_t st);
+hipError_t gemm_dw2(const moe_shape& s, const moe_plan& p, const void* do_perm, const void* ga, float* dw2,
+                    hipStream_t st);
+hipError_t gemm_router_logits(const moe_shape& s, const void* x, const void* wg, const float* bias,
+                              float* logits, hipStream_t st);
+hipError_t gemm_router_dx(const moe_shape& s, const moe_plan& p, const void* dzq, int ldz, const void* wg,
+                          const void* dx_perm, void* dx, hipStream_t st);
+int gemm_router_dwg_splits(const moe_shape& s);
+hipError_t gemm_router_dwg(const moe_shape& s, const void* dzq, int ldz, const void* x, float* part,
+                           hipStream_t st);
+
+}  // namespace moe

@@ -1,0 +1,436 @@
+// Routing kernels: wave64 top-k with softmax over the selected logits, the
+// deterministic plan build (histogram -> prefix scan -> stable scatter by token)
+// and token rounding.
+//
+// Top-k follows the "Beam" blog (section 5.3) and the "Trinity Large" commentary
+// (code example 1): experts are ranked by logit, the k best are kept and their
+// gates are a softmax over those k logits.  Ties go to the lower expert index.
+// The plan lays the token-expert pairs out as contiguous per-expert row
+// segments ("row-wise" expert buffers of the Olmo-core 3 article, "three splits"
+// section), tokens ascending inside a segment; everything stays on the device.
+// Token rounding follows the SonicMoE article, section 3.
+#include "moe_common.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+MOE_DEV bool better(float av, int ae, float bv, int be) { return av > bv || (av == bv && ae < be); }
+
+// One wave per token, 16 tokens per wave, 64 tokens per block.  Lane l holds
+// experts l, l+64, ...  With ROUND the block also writes the full softmax
+// expert-major (probs_t) and the selection bitmap expert-major (sel_t).
+template <int V, bool ROUND>
+__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E, int k,
+                                                  int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate,
+                                                  uint32_t* __restrict__ keep_bits, int words,
+                                                  float* __restrict__ probs_t, uint32_t* __restrict__ sel_t,
+                                                  int wordsT) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  float* pt = reinterpret_cast<float*>(smem);                       // [E][64]
+  uint32_t* sel = reinterpret_cast<uint32_t*>(smem + (size_t)E * 64 * 4);  // [E][2]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * 64;
+  if constexpr (ROUND) {
+    for (int i = threadIdx.x; i < E * 2; i += 256) sel[i] = 0u;
+    __syncthreads();
+  }
+  for (int it = 0; it < 16; ++it) {
+    const int tl = wave * 16 + it;
+    const int t = t0 + tl;
+    if (t >= T) break;
+    float z[V];
+    bool taken[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      int e = lane + 64 * v;
+      z[v] = (e < E) ? logits[(int64_t)t * E + e] : -INFINITY;
+      taken[v] = !(e < E);
+    }
+    int sel_e[8];
+    float sel_z[8];
+    for (int j = 0; j < k; ++j) {
+      float bv = -INFINITY;
+      int be = 0x7fffffff;
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        int e = lane + 64 * v;
+        if (!taken[v] && better(z[v], e, bv, be)) { bv = z[v]; be = e; }
+      }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) {
+        float ov = __shfl_xor(bv, o, 64);
+        int oe = __shfl_xor(be, o, 64);
+        if (better(ov, oe, bv, be)) { bv = ov; be = oe; }
+      }
+      sel_e[j] = be;
+      sel_z[j] = bv;
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+        if (lane + 64 * v == be) taken[v] = true;
+    }
+    // softmax over the k selected logits (the first is the largest)
+    float den = 0.0f;
+    for (int j = 0; j < k; ++j) den += expf(sel_z[j] - sel_z[0]);
+    if (lane < k) {
+      float zj = sel_z[0];
+      int ej = sel_e[0];
+      for (int j = 1; j < k; ++j)
+        if (lane == j) { zj = sel_z[j]; ej = sel_e[j]; }
+      topk_idx[(int64_t)t * k + lane] = ej;
+      topk_gate[(int64_t)t * k + lane] = expf(zj - sel_z[0]) / den;
+    }
+    if (lane < words) {
+      uint32_t w = 0;
+      for (int j = 0; j < k; ++j)
+        if ((sel_e[j] >> 5) == lane) w |= 1u << (sel_e[j] & 31);
+      keep_bits[(int64_t)t * words + lane] = w;
+    }
+    if constexpr (ROUND) {
+      float s = 0.0f;
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+        if (lane + 64 * v < E) s += expf(z[v] - sel_z[0]);
+      s = wave_sum(s);
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        int e = lane + 64 * v;
+        if (e < E) pt[e * 64 + tl] = expf(z[v] - sel_z[0]) / s;
+      }
+      if (lane < k) {
+        int ej = sel_e[0];
+        for (int j = 1; j < k; ++j)
+          if (lane == j) ej = sel_e[j];
+        atomicOr(&sel[ej * 2 + (tl >> 5)], 1u << (tl & 31));
+      }
+    }
+  }
+  if constexpr (ROUND) {
+    __syncthreads();
+    for (int i = threadIdx.x; i < E * 64; i += 256) {
+      int e = i >> 6, tl = i & 63;
+      if (t0 + tl < T) probs_t[(int64_t)e * T + t0 + tl] = pt[e * 64 + tl];
+    }
+    for (int i = threadIdx.x; i < E * 2; i += 256) {
+      int e = i >> 1, h = i & 1;
+      int wi = blockIdx.x * 2 + h;
+      if (wi < wordsT) sel_t[(int64_t)e * wordsT + wi] = sel[i];
+    }
+  }
+}
+
+// Per-(wave, expert) 64-bit masks of the tokens of a 256-token block that keep
+// the expert: bit l of mask[w][e] = token (block, w, l) has a row at e.
+struct BlockMasks {
+  uint32_t* m;  // [4][E][2]
+  int E;
+  MOE_DEV uint32_t& at(int w, int e, int h) { return m[(w * E + e) * 2 + h]; }
+};
+
+MOE_DEV void build_masks(BlockMasks bm, const uint32_t* keep_bits, int words, int t, bool valid,
+                         int* tok_count) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < 4 * bm.E * 2; i += 256) bm.m[i] = 0u;
+  __syncthreads();
+  int cnt = 0;
+  if (valid) {
+    for (int w = 0; w < words; ++w) {
+      uint32_t bits = keep_bits[(int64_t)t * words + w];
+      cnt += __popc(bits);
+      while (bits) {
+        int b = __ffs(bits) - 1;
+        bits &= bits - 1;
+        atomicOr(&bm.at(wave, w * 32 + b, lane >> 5), 1u << (lane & 31));
+      }
+    }
+  }
+  *tok_count = cnt;
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(256) void plan_count_kernel(const uint32_t* __restrict__ keep_bits, int T, int E,
+                                                        int words, int nblk, int32_t* __restrict__ hist,
+                                                        int32_t* __restrict__ blk_tok) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  BlockMasks bm{reinterpret_cast<uint32_t*>(smem), E};
+  __shared__ int red[256];
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  int cnt;
+  build_masks(bm, keep_bits, words, t, t < T, &cnt);
+  for (int e = threadIdx.x; e < E; e += 256) {
+    int h = 0;
+    for (int w = 0; w < 4; ++w) h += __popc(bm.at(w, e, 0)) + __popc(bm.at(w, e, 1));
+    hist[(int64_t)e * nblk + blockIdx.x] = h;
+  }
+  red[threadIdx.x] = cnt;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (threadIdx.x < o) red[threadIdx.x] += red[threadIdx.x + o];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) blk_tok[blockIdx.x] = red[0];
+}
+
+// Exclusive scan of n ints in place by one 1024-thread block; returns the total.
+MOE_DEV int block_scan_inplace(int32_t* a, int64_t n, int* sh) {
+  const int tid = threadIdx.x;
+  const int64_t per = (n + 1023) / 1024;
+  const int64_t lo = min((int64_t)tid * per, n), hi = min(lo + per, n);
+  int s = 0;
+  for (int64_t i = lo; i < hi; ++i) s += a[i];
+  sh[tid] = s;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {     // inclusive Hillis-Steele
+    int v = (tid >= o) ? sh[tid - o] : 0;
+    __syncthreads();
+    sh[tid] += v;
+    __syncthreads();
+  }
+  int run = sh[tid] - s;
+  int total = sh[1023];
+  for (int64_t i = lo; i < hi; ++i) {
+    int v = a[i];
+    a[i] = run;
+    run += v;
+  }
+  __syncthreads();
+  return total;
+}
+
+__global__ __launch_bounds__(1024) void plan_scan_kernel(int E, int nblk, int32_t* __restrict__ hist,
+                                                        int32_t* __restrict__ blk_tok, int32_t* __restrict__ counts,
+                                                        int32_t* __restrict__ counts_raw, int32_t* __restrict__ offsets,
+                                                        int32_t* __restrict__ pre128, int32_t* __restrict__ pre256) {
+  __shared__ int sh[1024];
+  const int total = block_scan_inplace(hist, (int64_t)E * nblk, sh);
+  const int toks = block_scan_inplace(blk_tok, nblk, sh);
+  if (threadIdx.x == 0) blk_tok[nblk] = toks;
+  for (int e = threadIdx.x; e < E; e += 1024) {
+    int o = hist[(int64_t)e * nblk];
+    int o1 = (e + 1 < E) ? hist[(int64_t)(e + 1) * nblk] : total;
+    offsets[e] = o;
+    counts[e] = o1 - o;
+    if (counts_raw) counts_raw[e] = o1 - o;
+  }
+  if (threadIdx.x == 0) offsets[E] = total;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int a = 0, b = 0;
+    for (int e = 0; e < E; ++e) {
+      pre128[e] = a;
+      pre256[e] = b;
+      int c = counts[e];
+      a += (c + 127) / 128;
+      b += (c + 255) / 256;
+    }
+    pre128[E] = a;
+    pre256[E] = b;
+  }
+}
+
+__global__ __launch_bounds__(256) void plan_scatter_kernel(
+    const uint32_t* __restrict__ keep_bits, int T, int E, int k, int words, int nblk,
+    const int32_t* __restrict__ hist, const int32_t* __restrict__ blk_tok, const int32_t* __restrict__ topk_idx,
+    const float* __restrict__ topk_gate, const float* __restrict__ probs_t, bool prob_gates,
+    int32_t* __restrict__ token_of_row, int32_t* __restrict__ expert_of_row, float* __restrict__ gate_of_row,
+    int32_t* __restrict__ row_of_slot, int32_t* __restrict__ tok_ptr, int32_t* __restrict__ tok_rows) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  BlockMasks bm{reinterpret_cast<uint32_t*>(smem), E};
+  __shared__ int sc[256];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  const bool valid = t < T;
+  int cnt;
+  build_masks(bm, keep_bits, words, t, valid, &cnt);
+  // token -> first row slot in tok_rows (block base + exclusive scan of counts)
+  sc[threadIdx.x] = cnt;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    int v = (threadIdx.x >= o) ? sc[threadIdx.x - o] : 0;
+    __syncthreads();
+    sc[threadIdx.x] += v;
+    __syncthreads();
+  }
+  const int tbase = blk_tok[blockIdx.x] + sc[threadIdx.x] - cnt;
+  if (blockIdx.x == 0 && threadIdx.x == 0) tok_ptr[T] = blk_tok[nblk];
+  if (!valid) return;
+  tok_ptr[t] = tbase;
+  const uint32_t ltmask = (1u << (lane & 31)) - 1u;
+  auto row_of = [&](int e) -> int {
+    int r = hist[(int64_t)e * nblk + blockIdx.x];
+    for (int w = 0; w < wave; ++w) r += __popc(bm.at(w, e, 0)) + __popc(bm.at(w, e, 1));
+    if (lane >= 32) r += __popc(bm.at(wave, e, 0));
+    r += __popc(bm.at(wave, e, lane >> 5) & ltmask);
+    return r;
+  };
+  float ptop = 0.0f;
+  if (prob_gates)
+    for (int j = 0; j < k; ++j) ptop += probs_t[(int64_t)topk_idx[(int64_t)t * k + j] * T + t];
+  for (int j = 0; j < k; ++j) row_of_slot[(int64_t)t * k + j] = -1;
+  int n = 0;
+  for (int w = 0; w < words; ++w) {
+    uint32_t bits = keep_bits[(int64_t)t * words + w];
+    while (bits) {
+      int b = __ffs(bits) - 1;
+      bits &= bits - 1;
+      int e = w * 32 + b;
+      int r = row_of(e);
+      int slot = -1;
+      for (int j = 0; j < k; ++j)
+        if (topk_idx[(int64_t)t * k + j] == e) slot = j;
+      float g;
+      if (slot >= 0) {
+        g = topk_gate[(int64_t)t * k + slot];
+        row_of_slot[(int64_t)t * k + slot] = r;
+      } else {
+        g = probs_t[(int64_t)e * T + t] / ptop;   // pair added by token rounding
+      }
+      token_of_row[r] = t;
+      expert_of_row[r] = e;
+      gate_of_row[r] = g;
+      tok_rows[tbase + n] = r;
+      ++n;
+    }
+  }
+}
+
+// Token rounding, one 1024-thread block per expert: radix-select the cut among
+// the candidates (selected pairs when dropping, unselected tokens when adding)
+// and flip their keep bits.
+__global__ __launch_bounds__(1024) void round_select_kernel(const float* __restrict__ probs_t,
+                                                           const uint32_t* __restrict__ sel_t, int wordsT,
+                                                           const int32_t* __restrict__ counts_raw, int T, int tile,
+                                                           uint32_t* __restrict__ keep_bits, int words,
+                                                           bool col_in_lds) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  __shared__ int hist[256];
+  __shared__ int sh[1024];
+  __shared__ int bc[2];
+  const int e = blockIdx.x, tid = threadIdx.x;
+  const int n = counts_raw[e];
+  int target = ((n + tile / 2) / tile) * tile;
+  if (target > T) target = (n / tile) * tile;
+  if (target == n) return;
+  const bool drop = target < n;
+  int c = drop ? n - target : target - n;
+  const uint32_t* selrow = sel_t + (int64_t)e * wordsT;
+  const float* col = probs_t + (int64_t)e * T;
+  if (col_in_lds) {
+    float* lc = reinterpret_cast<float*>(smem);
+    for (int i = tid; i < T; i += 1024) lc[i] = col[i];
+    col = lc;
+    __syncthreads();
+  }
+  auto is_cand = [&](int t) -> bool {
+    bool s = (selrow[t >> 5] >> (t & 31)) & 1u;
+    return drop ? s : !s;
+  };
+  auto key_of = [&](int t) -> uint32_t {
+    uint32_t b = __float_as_uint(col[t]);   // P >= 0: bit order = value order
+    return drop ? b : ~b;                   // ascending key = order of removal / addition
+  };
+  const int per = (T + 1023) / 1024;
+  const int lo = min(tid * per, T), hi = min(lo + per, T);
+  uint32_t prefix = 0u, mask = 0u;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = tid; i < 256; i += 1024) hist[i] = 0;
+    __syncthreads();
+    for (int t = lo; t < hi; ++t) {
+      if (!is_cand(t)) continue;
+      uint32_t kk = key_of(t);
+      if ((kk & mask) == prefix) atomicAdd(&hist[(kk >> shift) & 255], 1);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int cum = 0, dg = 255;
+      for (int d = 0; d < 256; ++d) {
+        if (cum + hist[d] >= c) { dg = d; break; }
+        cum += hist[d];
+      }
+      bc[0] = dg;
+      bc[1] = c - cum;
+    }
+    __syncthreads();
+    prefix |= (uint32_t)bc[0] << shift;
+    mask |= 255u << shift;
+    c = bc[1];
+    __syncthreads();
+  }
+  // c = number of candidates with key == prefix to take; ties go by token
+  int ties = 0;
+  for (int t = lo; t < hi; ++t)
+    if (is_cand(t) && key_of(t) == prefix) ++ties;
+  sh[tid] = ties;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {
+    int v = (tid >= o) ? sh[tid - o] : 0;
+    __syncthreads();
+    sh[tid] += v;
+    __syncthreads();
+  }
+  const int total_ties = sh[1023];
+  int rank = sh[tid] - ties;
+  const uint32_t bit = 1u << (e & 31);
+  for (int t = lo; t < hi; ++t) {
+    if (!is_cand(t)) continue;
+    uint32_t kk = key_of(t);
+    bool take = kk < prefix;
+    if (kk == prefix) {
+      // dropping removes the larger tokens first, adding takes the smaller first
+      take = drop ? (rank >= total_ties - c) : (rank < c);
+      ++rank;
+    }
+    if (!take) continue;
+    uint32_t* w = keep_bits + (int64_t)t * words + (e >> 5);
+    if (drop) atomicAnd(w, ~bit);
+    else atomicOr(w, bit);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_topk(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, bool rounding,
+                       hipStream_t st) {
+  const int grid = ceil_div(s.T, 64);
+  const int wordsT = ceil_div(s.T, 32);
+  size_t lds = rounding ? (size_t)s.E * 64 * 4 + (size_t)s.E * 8 : 0;
+#define MOE_TOPK(V, R)                                                                                  \
+  do {                                                                                                 \
+    auto kern = topk_kernel<V, R>;                                                                     \
+    if (lds > 65536) hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, st, p.logits, s.T, s.E, s.k, p.topk_idx,      \
+                       p.topk_gate, p.keep_bits, pi.words, p.probs_t, pi.sel_t, wordsT);               \
+  } while (0)
+  if (s.E <= 64) { if (rounding) MOE_TOPK(1, true); else MOE_TOPK(1, false); }
+  else if (s.E <= 128) { if (rounding) MOE_TOPK(2, true); else MOE_TOPK(2, false); }
+  else { if (rounding) MOE_TOPK(4, true); else MOE_TOPK(4, false); }
+#undef MOE_TOPK
+  return hipGetLastError();
+}
+
+hipError_t launch_plan_build(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, bool raw,
+                             bool with_prob_gates, hipStream_t st) {
+  const size_t lds = (size_t)4 * s.E * 2 * 4;
+  hipLaunchKernelGGL(plan_count_kernel, dim3(pi.nblk), dim3(256), lds, st, p.keep_bits, s.T, s.E, pi.words,
+                     pi.nblk, pi.hist, pi.blk_tok);
+  hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, st, s.E, pi.nblk, pi.hist, pi.blk_tok, p.counts,
+                     raw ? p.counts_raw : nullptr, p.offsets, pi.prefix128, pi.prefix256);
+  hipLaunchKernelGGL(plan_scatter_kernel, dim3(pi.nblk), dim3(256), lds, st, p.keep_bits, s.T, s.E, s.k,
+                     pi.words, pi.nblk, pi.hist, pi.blk_tok, p.topk_idx, p.topk_gate, p.probs_t,
+                     with_prob_gates, p.token_of_row, p.expert_of_row, p.gate_of_row, p.row_of_slot, p.tok_ptr,
+                     p.tok_rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_round_select(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, hipStream_t st) {
+  const size_t col = (size_t)s.T * 4;
+  const bool in_lds = col <= 128 * 1024;
+  const size_t lds = in_lds ? col : 0;
+  if (lds > 65536)
+    hipFuncSetAttribute((const void*)round_select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipLaunchKernelGGL(round_select_kernel, dim3(s.E), dim3(1024), lds, st, p.probs_t, pi.sel_t,
+                     ceil_div(s.T, 32), p.counts_raw, s.T, s.round_tile, p.keep_bits, pi.words, in_lds);
+  return hipGetLastError();
+}
+
+}  // namespace moe

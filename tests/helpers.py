@@ -1,0 +1,62 @@
+"""Shared pieces of the GPU parity tests: inputs (seeded, clear of routing ties),
+the oracle run on the same inputs, and the tolerance check."""
+import numpy as np
+import torch
+
+from mixture_experts_layer_27_amd import configs, synth
+from oracle import moe_oracle as mo
+from oracle.tie_clearance import clear_ties
+
+# Parity cases at sizes the oracle finishes in seconds: several tiles per GEMM,
+# ragged per-expert segments and ragged token counts.
+CASES = {
+    "tiny_fp32": configs.TINY,
+    "coarse_small": configs.COARSE.scaled("coarse_small", T=1000, d=256, f=512, backward=True),
+    "fine_small": configs.FINE.scaled("fine_small", T=1500, d=256, E=32, f=256),
+    "fine_zipf_small": configs.FINE_ZIPF.scaled("fine_zipf_small", T=1500, d=256, E=32, f=256),
+    "sparse_small": configs.SPARSE.scaled("sparse_small", T=1200, d=512, E=64, f=128),
+    "sparse_round_small": configs.SPARSE_ROUND.scaled("sparse_round_small", T=1200, d=512, E=64, f=128),
+    "single_expert": configs.FINE.scaled("single_expert", T=300, d=128, E=1, k=1, f=128),
+    "k_equals_E": configs.FINE.scaled("k_equals_E", T=200, d=192, E=4, k=4, f=128),
+    "one_token": configs.FINE.scaled("one_token", T=1, d=128, E=8, k=2, f=128),
+}
+
+
+def make_inputs(cfg):
+    g = synth.generate(cfg)
+
+    def redraw(x, rows, attempt):
+        return synth.redraw_rows(cfg, x, rows, attempt)
+
+    g["x"], _ = clear_ties(g["x"], g["w_gate"], g.get("bias"), cfg.k, redraw, round_tile=cfg.round_tile)
+    return g
+
+
+def precision(cfg):
+    return mo.CONTRACT if cfg.act == "bf16" else mo.TRUTH
+
+
+def oracle_run(cfg, g):
+    f = lambda t: None if t is None else t.double().numpy()
+    return mo.layer(f(g["x"]), f(g["w_gate"]), f(g.get("bias")), f(g["w1"]), f(g["w2"]), cfg.k,
+                    dout=f(g.get("dout")), round_tile=cfg.round_tile, prec=precision(cfg))
+
+
+def close(got, ref, atol=2e-2, rfrob=1e-2):
+    """(ok, max-abs in units of max(1, rms(ref)), relative Frobenius error)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    if ref.size == 0:
+        return True, 0.0, 0.0
+    scale = max(1.0, float(np.sqrt(np.mean(ref ** 2))))
+    err = got - ref
+    mabs = float(np.abs(err).max()) / scale
+    nref = float(np.linalg.norm(ref))
+    rf = float(np.linalg.norm(err)) / nref if nref > 0 else float(np.linalg.norm(err))
+    return (mabs <= atol and rf <= rfrob), mabs, rf
+
+
+def assert_close(name, got, ref, atol=2e-2, rfrob=1e-2):
+    ok, mabs, rf = close(got, ref, atol, rfrob)
+    assert ok, f"{name}: max-abs/scale {mabs:.3e} (tol {atol}), rel-Frobenius {rf:.3e} (tol {rfrob})"
+    return mabs, rf

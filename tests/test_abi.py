@@ -1,0 +1,81 @@
+"""The C-ABI library: it loads, exports every entry point the header declares,
+and its host-side validation answers without touching a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+LIB = os.path.join(ROOT, "mixture_experts_layer_27_amd", "libmoe_mi355x.so")
+
+
+def declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def b():
+    if not os.path.exists(LIB):
+        pytest.fail("library not built: run __graft_entry__.build()")
+    from mixture_experts_layer_27_amd import binding
+    return binding
+
+
+def test_exports_every_declared_symbol(b):
+    names = declared()
+    assert len(names) >= 12
+    lib = ctypes.CDLL(LIB)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(b.EXPORTS) == set(names)
+
+
+def test_sizes_and_status_strings(b):
+    s = b.make_shape(256, 128, 8, 2, 256, b.MOE_F32)
+    assert b.max_rows(s) == 512
+    assert b.plan_bytes(s) > 0
+    assert b.workspace_bytes(s, b.MOE_WS_EXPERTS) >= 512 * 256 * 4
+    assert b.workspace_bytes(s, b.MOE_WS_BACKWARD) > b.workspace_bytes(s, b.MOE_WS_EXPERTS)
+    r = b.make_shape(1000, 256, 64, 8, 128, b.MOE_BF16, round_tile=128)
+    assert b.max_rows(r) == 1000 * 8 + 64 * 64
+    for code in range(5):
+        assert b._lib.moe_status_str(code)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=0), 1), (dict(k=9, E=16), 2), (dict(k=5, E=4), 1), (dict(E=300), 2), (dict(d=100), 2),
+    (dict(d_ff=96), 2), (dict(act=7), 1), (dict(round_tile=3), 1), (dict(T=(1 << 20) + 1), 2),
+])
+def test_shape_validation(b, kw, code):
+    base = dict(T=64, d=128, E=8, k=2, d_ff=128, act=b.MOE_BF16, gemm=None, round_tile=0)
+    base.update(kw)
+    s = b.make_shape(**base)
+    assert b.plan_bytes(s) == 0 and b.max_rows(s) == -1
+    plan = b.MoePlan()
+    blob = ctypes.c_void_p(1 << 20)   # host address: never dereferenced on the error path
+    got = b._lib.moe_plan_init(ctypes.byref(s), blob, 1 << 30, ctypes.byref(plan))
+    assert got == code
+
+
+def test_argument_errors_return_before_launch(b):
+    s = b.make_shape(64, 128, 8, 2, 128, b.MOE_BF16)
+    plan = b.MoePlan()
+    fake = ctypes.c_void_p(1 << 20)
+    assert b._lib.moe_plan_init(ctypes.byref(s), fake, 16, ctypes.byref(plan)) == 3      # blob too small
+    assert b._lib.moe_plan_init(ctypes.byref(s), ctypes.c_void_p((1 << 20) + 8), 1 << 30, ctypes.byref(plan)) == 1
+    assert b._lib.moe_plan_init(ctypes.byref(s), fake, 1 << 30, ctypes.byref(plan)) == 0
+    # null inputs, misaligned pointers, missing workspace: rejected on the host
+    assert b._lib.moe_route(ctypes.byref(s), None, fake, None, ctypes.byref(plan), None, 0, None) == 1
+    assert b._lib.moe_permute(ctypes.byref(s), ctypes.c_void_p((1 << 20) + 4), ctypes.byref(plan), fake, None) == 1
+    assert b._lib.moe_grouped_gemm_swiglu(ctypes.byref(s), fake, fake, fake, ctypes.byref(plan), fake, fake,
+                                          fake, 0, None) == 3
+    assert b._lib.moe_backward(ctypes.byref(s), fake, fake, fake, fake, ctypes.byref(plan), fake, fake, fake,
+                               fake, fake, fake, None, None, fake, 0, None) == 3
+    assert b._lib.moe_round_tokens(ctypes.byref(s), ctypes.byref(plan), None, 0, None) == 1   # rounding off
+    assert b._lib.moe_quantize_mx(fake, 4, 48, fake, fake, None) == 1                         # cols % 32
+    empty = b.MoePlan()
+    assert b._lib.moe_unpermute_combine(ctypes.byref(s), fake, ctypes.byref(empty), fake, None) == 1
