@@ -1,0 +1,168 @@
+"""Benchmark of the MoE layer's hot path on one MI355X.
+
+One step = the whole layer on one batch: route (router GEMM, top-k softmax,
+plan) [+ token rounding], permute, grouped SwiGLU expert GEMMs, combine, and
+the full backward.  Inputs are synthetic (seeded), already resident in HBM when
+the timed region starts.  Prints ONE JSON line.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config fine_e128]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer tokens/s fwd+bwd at 1 GPU; grouped-GEMM % MFMA peak; permute GB/s"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="fine_e128")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0 = automatic)")
+    ap.add_argument("--out", default=None, help="also append the JSON line to this file")
+    return ap.parse_args()
+
+
+def cpu_baseline(cfg, g, tokens):
+    """The CPU oracle (float64 numpy, contract precision) on the first `tokens`
+    tokens of the same workload: forward + backward, timed on the host cores."""
+    import numpy as np
+    import threadpoolctl
+    from oracle import moe_oracle as mo
+
+    f = lambda t: None if t is None else t.double().numpy()
+    x = f(g["x"][:tokens])
+    dout = f(g["dout"][:tokens]) if "dout" in g else None
+    wg, b, w1, w2 = f(g["w_gate"]), f(g.get("bias")), f(g["w1"]), f(g["w2"])
+    info = threadpoolctl.threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] or [1])
+    t0 = time.perf_counter()
+    mo.layer(x, wg, b, w1, w2, cfg.k, dout=dout, round_tile=cfg.round_tile,
+             prec=mo.CONTRACT if cfg.act == "bf16" else mo.TRUTH)
+    dt = time.perf_counter() - t0
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {tokens} of {cfg.T} tokens of {cfg.name} (same weights), fwd+bwd, "
+                      f"float64 numpy, {dt:.1f} s"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {a.gpus}); this build has no multi-GPU path.",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from mixture_experts_layer_27_amd import binding, configs, synth
+
+    cfg = configs.get(a.config)
+    print(f"[bench] generating {cfg.name} inputs", file=sys.stderr, flush=True)
+    g = synth.generate(cfg)
+    run = binding.LayerRun(cfg, g)
+    s = run.s
+    stream = torch.cuda.current_stream()
+
+    phases = ["route", "permute", "experts", "combine", "backward"]
+
+    def step(ev=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        run.route()
+        mark(1)
+        binding.permute(s, run.inp["x"], run.plan, run.x_perm)
+        mark(2)
+        binding.grouped_gemm_swiglu(s, run.x_perm, run.inp["w1"], run.inp["w2"], run.plan, run.h, run.y, run.ws_fwd)
+        mark(3)
+        binding.unpermute_combine(s, run.y, run.plan, run.out)
+        mark(4)
+        if run.has_bwd:
+            run.backward(with_optional=False)
+        mark(5)
+
+    print(f"[bench] warmup {a.warmup}", file=sys.stderr, flush=True)
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(a.steps)]
+    print(f"[bench] timing {a.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = {p: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(a.steps)) / a.steps
+          for j, p in enumerate(phases)}
+    step_ms = sum(evs[i][0].elapsed_time(evs[i][5]) for i in range(a.steps)) / a.steps
+    ms_per_step = wall * 1000.0 / a.steps
+
+    N = cfg.N  # rows without rounding (algorithmic work)
+    counts = run.plan.arrays()["counts"].cpu()
+    rows = int(counts.sum())
+    esz = 2 if cfg.act == "bf16" else 4
+    fwd_gemm_flops = 2.0 * rows * cfg.d * 2 * cfg.f + 2.0 * rows * cfg.f * cfg.d
+    peak = PEAK_BF16_TFLOPS if cfg.act == "bf16" else PEAK_F32_TFLOPS
+    achieved = fwd_gemm_flops / (ms["experts"] * 1e-3) / 1e12
+    permute_bytes = cfg.T * cfg.d * esz + rows * cfg.d * esz + 4 * rows
+    combine_bytes = rows * cfg.d * esz + cfg.T * cfg.d * esz + 8 * rows
+    bwd_flops = 2 * fwd_gemm_flops
+    out = {
+        "metric": METRIC,
+        "value": cfg.T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.act == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: T={cfg.T} d_model={cfg.d} E={cfg.E} top-k={cfg.k} "
+                               f"d_ff={cfg.f} SwiGLU, {'fwd+bwd' if run.has_bwd else 'fwd'}"
+                               f"{', token rounding ' + str(cfg.round_tile) if cfg.round_tile else ''}",
+                   "global_batch": cfg.T, "seq_len": 1, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "kernel": "forward expert GEMMs (up+SwiGLU, down) in one call",
+                     "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
+                     "traffic": None},
+        "phases_ms": ms,
+        "events_ms_per_step": step_ms,
+        "grouped_gemm_mfma_frac": {"forward": achieved / peak,
+                                   "backward_call": bwd_flops / (ms["backward"] * 1e-3) / 1e12 / peak
+                                   if run.has_bwd else None},
+        "permute_GBps": permute_bytes / (ms["permute"] * 1e-3) / 1e9,
+        "combine_GBps": combine_bytes / (ms["combine"] * 1e-3) / 1e9,
+        "hbm_peak_GBps": PEAK_HBM_GBS,
+        "rows": rows,
+        "max_expert_rows": int(counts.max()),
+    }
+    if not a.no_cpu_baseline:
+        del run
+        torch.cuda.empty_cache()
+        tokens = a.cpu_tokens or max(1, min(cfg.T, 16384))
+        print(f"[bench] cpu oracle on {tokens} tokens", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(cfg, g, tokens)
+    line = json.dumps(out)
+    print(line, flush=True)
+    if a.out:
+        with open(a.out, "a") as fh:
+            fh.write(line + "\n")
+
+
+if __name__ == "__main__":
+    main()

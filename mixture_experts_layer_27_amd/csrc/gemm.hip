@@ -10,6 +10,7 @@
 // Backward (SonicMoE article, section 1): dA' = dO_perm W2_e is never stored;
 // its epilogue recomputes A from the saved H, reduces dS = <dA', A> per row,
 // and emits dH (SwiGLU backward) and gA = g * A for the W2 gradient.
+#include "gemm_dma.h"
 #include "gemm_engine.h"
 #include "moe_internal.h"
 
@@ -21,7 +22,21 @@ namespace {
 template <typename T, int BM, int BN, int WM, int WN, bool AKC, bool BKC, int GROUP, int EPI>
 hipError_t run(const Args& a, int64_t logical_tiles, hipStream_t st) {
   auto kern = grouped_gemm<T, BM, BN, WM, WN, AKC, BKC, GROUP, EPI>;
-  constexpr size_t lds = (size_t)2 * (BM + BN) * 128;
+  constexpr size_t lds = lds_bytes<T, BM, BN, WM, WN>();
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  const int64_t grid = 8 * ((logical_tiles + 7) / 8);
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(WM * WN * 64), lds, st, a);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN, bool AKC, bool BKC, int GROUP, int EPI, int S = 4>
+hipError_t run_dma(const Args& a, int64_t logical_tiles, hipStream_t st) {
+  auto kern = grouped_gemm_dma<BM, BN, WM, WN, AKC, BKC, GROUP, EPI, S>;
+  constexpr size_t lds = dma_lds_bytes<BM, BN, WM, WN, S>();
   if (lds > 65536) {
     hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -54,8 +69,8 @@ hipError_t gemm_up_swiglu(const moe_shape& s, const moe_plan& p, const PlanInter
   a.offsets = p.offsets;
   a.N = 2 * s.d_ff; a.K = s.d; a.E = s.E; a.f = s.d_ff;
   if (s.act == MOE_BF16) {
-    a.tile_prefix = pi.prefix256; a.tilesN = a.N / 256;
-    return run<bf16_t, 256, 256, 2, 4, true, true, GROUP_M, EPI_SWIGLU>(a, grouped_m_tiles(s, 256) * a.tilesN, st);
+    a.tile_prefix = pi.prefix128; a.tilesN = a.N / 256;
+    return run_dma<128, 256, 2, 4, true, true, GROUP_M, EPI_SWIGLU, 3>(a, grouped_m_tiles(s, 128) * a.tilesN, st);
   }
   a.tile_prefix = pi.prefix128; a.tilesN = a.N / 128;
   return run<float, 128, 128, 2, 2, true, true, GROUP_M, EPI_SWIGLU>(a, grouped_m_tiles(s, 128) * a.tilesN, st);
@@ -70,8 +85,8 @@ hipError_t gemm_down(const moe_shape& s, const moe_plan& p, const PlanInternal& 
   a.offsets = p.offsets;
   a.N = s.d; a.K = s.d_ff; a.E = s.E; a.f = s.d_ff;
   if (s.act == MOE_BF16) {
-    a.tile_prefix = pi.prefix256; a.tilesN = ceil_div(a.N, 256);
-    return run<bf16_t, 256, 256, 2, 4, true, true, GROUP_M, EPI_ACT>(a, grouped_m_tiles(s, 256) * a.tilesN, st);
+    a.tile_prefix = pi.prefix128; a.tilesN = ceil_div(a.N, 256);
+    return run_dma<128, 256, 2, 4, true, true, GROUP_M, EPI_ACT, 3>(a, grouped_m_tiles(s, 128) * a.tilesN, st);
   }
   a.tile_prefix = pi.prefix128; a.tilesN = ceil_div(a.N, 128);
   return run<float, 128, 128, 2, 2, true, true, GROUP_M, EPI_ACT>(a, grouped_m_tiles(s, 128) * a.tilesN, st);
@@ -79,7 +94,9 @@ hipError_t gemm_down(const moe_shape& s, const moe_plan& p, const PlanInternal& 
 
 // ---------------------------------------------------------------- backward
 
-int gemm_dact_parts(const moe_shape& s) { return ceil_div(s.d_ff, s.act == MOE_BF16 ? 256 : 128); }
+// dS partial sums per row: one per (column tile, wave column) on the bf16 path,
+// one per column tile on the fp32 path
+int gemm_dact_parts(const moe_shape& s) { return s.act == MOE_BF16 ? ceil_div(s.d_ff, 256) * 4 : ceil_div(s.d_ff, 128); }
 
 hipError_t gemm_dact(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const void* do_perm,
                      const void* w2, const void* h, void* dh, void* ga, float* ds_part, hipStream_t st) {
@@ -94,8 +111,8 @@ hipError_t gemm_dact(const moe_shape& s, const moe_plan& p, const PlanInternal& 
   a.offsets = p.offsets;
   a.N = s.d_ff; a.K = s.d; a.E = s.E; a.f = s.d_ff;
   if (s.act == MOE_BF16) {
-    a.tile_prefix = pi.prefix256; a.tilesN = ceil_div(a.N, 256);
-    return run<bf16_t, 256, 256, 2, 4, true, false, GROUP_M, EPI_DSWIGLU>(a, grouped_m_tiles(s, 256) * a.tilesN, st);
+    a.tile_prefix = pi.prefix128; a.tilesN = ceil_div(a.N, 256);
+    return run_dma<128, 256, 2, 4, true, false, GROUP_M, EPI_DSWIGLU, 3>(a, grouped_m_tiles(s, 128) * a.tilesN, st);
   }
   a.tile_prefix = pi.prefix128; a.tilesN = ceil_div(a.N, 128);
   return run<float, 128, 128, 2, 2, true, false, GROUP_M, EPI_DSWIGLU>(a, grouped_m_tiles(s, 128) * a.tilesN, st);
@@ -110,8 +127,8 @@ hipError_t gemm_dx_perm(const moe_shape& s, const moe_plan& p, const PlanInterna
   a.offsets = p.offsets;
   a.N = s.d; a.K = 2 * s.d_ff; a.E = s.E; a.f = s.d_ff;
   if (s.act == MOE_BF16) {
-    a.tile_prefix = pi.prefix256; a.tilesN = ceil_div(a.N, 256);
-    return run<bf16_t, 256, 256, 2, 4, true, false, GROUP_M, EPI_ACT>(a, grouped_m_tiles(s, 256) * a.tilesN, st);
+    a.tile_prefix = pi.prefix128; a.tilesN = ceil_div(a.N, 256);
+    return run_dma<128, 256, 2, 4, true, false, GROUP_M, EPI_ACT, 3>(a, grouped_m_tiles(s, 128) * a.tilesN, st);
   }
   a.tile_prefix = pi.prefix128; a.tilesN = ceil_div(a.N, 128);
   return run<float, 128, 128, 2, 2, true, false, GROUP_M, EPI_ACT>(a, grouped_m_tiles(s, 128) * a.tilesN, st);
@@ -127,10 +144,10 @@ hipError_t gemm_dw1(const moe_shape& s, const moe_plan& p, const void* dh, const
   a.C = dw1; a.ldc = s.d; a.c_estride = (int64_t)2 * s.d_ff * s.d;
   a.offsets = p.offsets;
   a.M = 2 * s.d_ff; a.N = s.d; a.E = s.E;
-  const int bm = s.act == MOE_BF16 ? 256 : 128;
-  a.tilesM = ceil_div(a.M, bm); a.tilesN = ceil_div(a.N, bm);
+  const int bn = s.act == MOE_BF16 ? 256 : 128;
+  a.tilesM = ceil_div(a.M, 128); a.tilesN = ceil_div(a.N, bn);
   a.total_static = s.E * a.tilesM * a.tilesN;
-  if (s.act == MOE_BF16) return run<bf16_t, 256, 256, 2, 4, false, false, GROUP_K, EPI_F32>(a, a.total_static, st);
+  if (s.act == MOE_BF16) return run_dma<128, 256, 2, 4, false, false, GROUP_K, EPI_F32, 3>(a, a.total_static, st);
   return run<float, 128, 128, 2, 2, false, false, GROUP_K, EPI_F32>(a, a.total_static, st);
 }
 
@@ -142,10 +159,10 @@ hipError_t gemm_dw2(const moe_shape& s, const moe_plan& p, const void* do_perm, 
   a.C = dw2; a.ldc = s.d_ff; a.c_estride = (int64_t)s.d * s.d_ff;
   a.offsets = p.offsets;
   a.M = s.d; a.N = s.d_ff; a.E = s.E;
-  const int bm = s.act == MOE_BF16 ? 256 : 128;
-  a.tilesM = ceil_div(a.M, bm); a.tilesN = ceil_div(a.N, bm);
+  const int bn = s.act == MOE_BF16 ? 256 : 128;
+  a.tilesM = ceil_div(a.M, 128); a.tilesN = ceil_div(a.N, bn);
   a.total_static = s.E * a.tilesM * a.tilesN;
-  if (s.act == MOE_BF16) return run<bf16_t, 256, 256, 2, 4, false, false, GROUP_K, EPI_F32>(a, a.total_static, st);
+  if (s.act == MOE_BF16) return run_dma<128, 256, 2, 4, false, false, GROUP_K, EPI_F32, 3>(a, a.total_static, st);
   return run<float, 128, 128, 2, 2, false, false, GROUP_K, EPI_F32>(a, a.total_static, st);
 }
 

@@ -1,0 +1,369 @@
+// Pipelined bf16 main loop for the grouped expert GEMMs on gfx950.
+//
+// Operand tiles go global -> LDS with global_load_lds_dwordx4 (no VGPR staging)
+// into a ring of S stages of BK = 32; the loads for stage k+S-1 are issued while
+// stage k is multiplied, so up to S-1 stages of memory latency are covered.  One
+// barrier per stage; each wave waits only for its own loads of the stage it is
+// about to read (s_waitcnt vmcnt(n)) before the barrier.
+//
+// LDS layouts (both 64 B of K per tile row, i.e. 32 bf16).  The gfx950 LDS has
+// 64 banks: a 16-byte read serves 16 lanes (256 B) per cycle, so 16 consecutive
+// fragment rows must land in 16 different 16 B bank groups.
+//  * K-contiguous operand: [rows][32] bf16, 16 B chunk c of row r stored at slot
+//    c ^ h(r), h(r) = ((r >> 1) ^ (r >> 3)) & 1 | ((r >> 2) & 1) << 1: rows r..r+15
+//    of one chunk (an MFMA fragment read) then cover all 64 banks, and any 8
+//    consecutive rows cover 32.
+//  * M/N-contiguous operand: [32 k][rows] bf16, 32 B slot s of k-row k stored at
+//    s ^ ((k & 3) << 1).  Fragments are read with ds_read_b64_tr_b16: within each group
+//    of 16 lanes, lane i receives element i % 4 of the 8-byte words read by lanes
+//    4j + i/4 (j = 0..3).  Lanes reading k-rows kb..kb+3 at columns n0 + 4*(i%4)
+//    therefore hand lane i the four k values of column n0 + i -- two such reads
+//    build the 8-k MFMA operand from a tile stored in its natural layout.
+// The DMA write of one wave instruction covers 1 KiB of LDS contiguously
+// (lane i -> byte 16 i), so each lane fetches the global chunk that the layout
+// places there; masked lanes (rows past a segment) fetch a zero block.
+#pragma once
+#include "gemm_engine.h"
+
+namespace moe_gemm {
+
+__device__ __attribute__((aligned(16))) uint32_t g_dma_zero[4];
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+MOE_DEV void dma16(const void* g, char* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds_wave_base, 16, 0, 0);
+}
+
+MOE_DEV u32x4 lds_tr_frag(const char* p0, const char* p1) {
+  s16x4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p0);
+  s16x4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p1);
+  uint2 x = __builtin_bit_cast(uint2, a), y = __builtin_bit_cast(uint2, b);
+  return u32x4{x.x, x.y, y.x, y.y};
+}
+
+// barrier without the compiler's implicit wait on every outstanding memory op;
+// the asm fences keep the compiler from moving LDS accesses across it
+MOE_DEV void cta_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// s_waitcnt vmcnt(n) lgkmcnt(0) (gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt_hi[15:14])
+template <int N>
+MOE_DEV void wait_vm_lgkm0() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (0 << 8) | (((N >> 4) & 3) << 14));
+}
+
+MOE_DEV int kc_h(int row) { return (((row >> 1) ^ (row >> 3)) & 1) | (((row >> 2) & 1) << 1); }
+MOE_DEV int kc_off(int row, int chunk) { return row * 64 + ((chunk ^ kc_h(row)) << 4); }
+MOE_DEV int mn_x(int k) { return (k & 3) << 1; }
+template <int ROWS>
+MOE_DEV int mn_off(int k, int byte) {
+  static_assert(ROWS >= 128, "the k-row swizzle needs 8 slots of 32 B");
+  return k * (ROWS * 2) + ((((byte >> 5) ^ mn_x(k)) << 5) | (byte & 31));
+}
+
+// DMA sources of one operand tile (ROWS rows x 32 k) for the lanes of this wave.
+template <int ROWS, int NW, bool KC>
+struct DmaOperand {
+  static constexpr int Q = ROWS / 16 / NW;   // 1 KiB instructions per wave per stage
+  static_assert(Q >= 1 && (ROWS / 16) % NW == 0, "tile rows must split over the waves");
+  const bf16_t* src[Q];   // KC: element pointer of (row, chunk) at k = 0; MN: unused
+  int kl[Q], mn[Q];       // MN: local k row and column of the lane's 16 bytes
+  int q0;
+
+  template <class RowFn>
+  MOE_DEV void init_kc(RowFn rowfn, int wave, int lane) {
+    q0 = wave * Q;
+#pragma unroll
+    for (int u = 0; u < Q; ++u) {
+      const int row = (q0 + u) * 16 + (lane >> 2);
+      const int c = (lane & 3) ^ kc_h(row);
+      src[u] = rowfn(row) + c * 8;
+    }
+  }
+  MOE_DEV void init_mn(int wave, int lane) {
+    q0 = wave * Q;
+#pragma unroll
+    for (int u = 0; u < Q; ++u) {
+      const int b = (q0 + u) * 1024 + lane * 16;
+      const int k = b / (ROWS * 2), within = b % (ROWS * 2);
+      const int s = (within >> 5) ^ mn_x(k);
+      kl[u] = k;
+      mn[u] = s * 16 + ((within >> 4) & 1) * 8;
+    }
+  }
+  // KC: k0 = first K element of the stage (no K tail on these operands)
+  MOE_DEV void issue_kc(char* tile, int k0) const {
+#pragma unroll
+    for (int u = 0; u < Q; ++u) dma16(src[u] + k0, tile + (q0 + u) * 1024);
+  }
+  // MN: base = element (k = 0, row = 0) of the operand; rows [k0, k_end) valid,
+  // columns [0, rvalid) valid relative to base's column
+  MOE_DEV void issue_mn(char* tile, const bf16_t* base, int64_t ld, int k0, int k_end, int rvalid) const {
+#pragma unroll
+    for (int u = 0; u < Q; ++u) {
+      const int k = k0 + kl[u];
+      const void* g = (k < k_end && mn[u] < rvalid) ? (const void*)(base + (int64_t)k * ld + mn[u])
+                                                    : (const void*)g_dma_zero;
+      dma16(g, tile + (q0 + u) * 1024);
+    }
+  }
+};
+
+MOE_DEV float fast_sigmoid(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
+
+// Wave-private epilogue: each wave stages its (BM/WM) x (BN/WN) accumulators in
+// its own LDS slab, 32 rows at a time, and reads them back as 8-column vectors --
+// no block-wide barrier.  Slab row stride WTN + 8 floats keeps the two 32-lane
+// halves of each staging store in different bank halves.
+// SwiGLU: the wave's columns [0, WTN/2) are gate columns, [WTN/2, WTN) the
+// matching up columns.  dS partials go to C3[(nt * WN + wn) * ldc3 + row].
+template <int BM, int BN, int WM, int WN, int GROUP, int EPI>
+MOE_DEV void wave_epilogue(const Args& args, const TileCtx& ctx, f32x16 (&acc)[BM / WM / 32][BN / WN / 32],
+                           char* smem) {
+  using T = bf16_t;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  constexpr int SS = WTN + 8;              // slab row stride (floats)
+  constexpr int CPR = WTN / 8;             // 8-column chunks per wave row
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  float* slab = reinterpret_cast<float*>(smem) + wave * 32 * SS;
+  const int rbase = ctx.row_begin + wm * WTM;     // GROUP_M: first row of this wave's tile
+  const int mbase = ctx.m0 + wm * WTM;            // GROUP_K: first output row
+  const int cbase = ctx.n0 + wn * WTN;            // first output column
+#pragma unroll
+  for (int i = 0; i < TM; ++i) {
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q)
+        slab[(8 * (q >> 2) + 4 * (lane >> 5) + (q & 3)) * SS + j * 32 + (lane & 31)] = acc[i][j][q];
+    __builtin_amdgcn_s_waitcnt(0xc07f);          // lgkmcnt(0): the slab is written (one wave, in order)
+    if constexpr (EPI == EPI_SWIGLU) {
+      constexpr int HC = CPR / 2;
+      T* H = reinterpret_cast<T*>(args.C);
+      T* Aout = reinterpret_cast<T*>(args.C2);
+#pragma unroll
+      for (int it = 0; it < 32 * HC / 64; ++it) {
+        const int u = lane + 64 * it;
+        const int rr = u / HC, ch = u % HC;
+        const int grow = rbase + i * 32 + rr;
+        if (grow >= ctx.row_end) continue;
+        const float* src = slab + rr * SS + ch * 8;
+        float hg[8], hu[8], a[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          hg[c] = Vec8<T>::rnd(src[c]);
+          hu[c] = Vec8<T>::rnd(src[WTN / 2 + c]);
+          a[c] = hg[c] * fast_sigmoid(hg[c]) * hu[c];
+        }
+        const int gcol = ctx.nt * (BN / 2) + wn * (WTN / 2) + ch * 8;
+        T* hrow = H + (int64_t)grow * args.ldc;
+        Vec8<T>::store(hrow + gcol, hg);
+        Vec8<T>::store(hrow + args.f + gcol, hu);
+        Vec8<T>::store(Aout + (int64_t)grow * args.ldc2 + gcol, a);
+      }
+    } else if constexpr (EPI == EPI_DSWIGLU) {
+      static_assert(CPR <= 64 && (32 * CPR) % 64 == 0, "row reduction inside one wave");
+      const T* Hs = reinterpret_cast<const T*>(args.aux);
+      T* dH = reinterpret_cast<T*>(args.C);
+      T* gA = reinterpret_cast<T*>(args.C2);
+#pragma unroll
+      for (int it = 0; it < 32 * CPR / 64; ++it) {
+        const int u = lane + 64 * it;
+        const int rr = u / CPR, ch = u % CPR;
+        const int grow = rbase + i * 32 + rr;
+        const int col = cbase + ch * 8;
+        float part = 0.0f;
+        if (grow < ctx.row_end && col < args.N) {
+          const float* src = slab + rr * SS + ch * 8;
+          const float g = args.row_gate[grow];
+          const T* hrow = Hs + (int64_t)grow * args.ld_aux;
+          float hg[8], hu[8], dhg[8], dhu[8], ga[8];
+          Vec8<T>::load(hrow + col, hg);
+          Vec8<T>::load(hrow + args.f + col, hu);
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            const float dap = src[c];
+            const float sg = fast_sigmoid(hg[c]);
+            const float sl = hg[c] * sg;
+            const float a = Vec8<T>::rnd(sl * hu[c]);      // A as stored in the forward
+            part += dap * a;
+            const float da = g * dap;
+            dhg[c] = da * hu[c] * (sg * (1.0f + hg[c] * (1.0f - sg)));
+            dhu[c] = da * sl;
+            ga[c] = g * a;
+          }
+          T* drow = dH + (int64_t)grow * args.ldc;
+          Vec8<T>::store(drow + col, dhg);
+          Vec8<T>::store(drow + args.f + col, dhu);
+          Vec8<T>::store(gA + (int64_t)grow * args.ldc2 + col, ga);
+        }
+#pragma unroll
+        for (int o = 1; o < CPR; o <<= 1) part += __shfl_xor(part, o, 64);
+        if (ch == 0 && grow < ctx.row_end) args.C3[(int64_t)(ctx.nt * WN + wn) * args.ldc3 + grow] = part;
+      }
+    } else {
+      using OT = typename std::conditional<EPI == EPI_ACT, T, float>::type;
+      OT* C = reinterpret_cast<OT*>(args.C);
+      if constexpr (GROUP == GROUP_K) C += (int64_t)ctx.e * args.c_estride;
+#pragma unroll
+      for (int it = 0; it < 32 * CPR / 64; ++it) {
+        const int u = lane + 64 * it;
+        const int rr = u / CPR, ch = u % CPR;
+        int grow;
+        bool ok;
+        if constexpr (GROUP == GROUP_M) { grow = rbase + i * 32 + rr; ok = grow < ctx.row_end; }
+        else { grow = mbase + i * 32 + rr; ok = grow < args.M; }
+        const int col = cbase + ch * 8;
+        if (!ok || col >= args.N) continue;
+        const float* src = slab + rr * SS + ch * 8;
+        float v[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) v[c] = src[c];
+        Vec8<OT>::store(C + (int64_t)grow * args.ldc + col, v);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);          // slab reads done before the next sub-tile overwrites it
+  }
+}
+
+template <int BM, int BN, int WM, int WN, bool AKC, bool BKC, int GROUP, int EPI, int S>
+__global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma(Args args) {
+  using T = bf16_t;
+  constexpr int NW = WM * WN;
+  constexpr int BK = 32;
+  static_assert(S >= 2 && S <= 5, "ring depth");
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  constexpr int ASZ = BM * 64, BSZ = BN * 64, STAGE = ASZ + BSZ;
+  static_assert(TM >= 1 && TN >= 1, "wave tile must hold a 32x32 MFMA tile");
+  static_assert(GROUP != GROUP_NONE, "router GEMMs use the register-staged kernel");
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+
+  TileCtx ctx;
+  if (!decode_tile<BM, BN, BK, GROUP>(args, ctx)) return;
+  const int e = ctx.e, nt = ctx.nt;
+  const int row_begin = ctx.row_begin, row_end = ctx.row_end;
+  const int k_begin = ctx.k_begin, k_end = ctx.k_end;
+  const int m0 = ctx.m0, n0 = ctx.n0;
+  const T* Ab = reinterpret_cast<const T*>(args.A) + (int64_t)e * args.a_estride;
+  const T* Bb = reinterpret_cast<const T*>(args.B) + (int64_t)e * args.b_estride;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+
+  DmaOperand<BM, NW, AKC> da;
+  DmaOperand<BN, NW, BKC> db;
+  if constexpr (AKC) {
+    da.init_kc([&](int row) -> const T* {
+      int g = row_begin + row;
+      if (g >= row_end) g = row_end - 1;     // rows past the segment only feed unstored outputs
+      const int src = args.a_gather ? args.a_gather[g] : g;
+      return Ab + (int64_t)src * args.lda;
+    }, wave, lane);
+  } else {
+    da.init_mn(wave, lane);
+  }
+  if constexpr (BKC) {
+    db.init_kc([&](int row) -> const T* {
+      int j = n0 + row;
+      if constexpr (EPI == EPI_SWIGLU) {
+        // wave wn's columns: first half gate rows, second half the matching up rows
+        const int w = row / WTN, jj = row % WTN;
+        const int g = nt * (BN / 2) + w * (WTN / 2) + (jj % (WTN / 2));
+        j = (jj < WTN / 2) ? g : (args.f + g);
+      } else {
+        if (j >= args.N) j = args.N - 1;
+      }
+      return Bb + (int64_t)j * args.ldb;
+    }, wave, lane);
+  } else {
+    db.init_mn(wave, lane);
+  }
+
+  auto issue = [&](int kt) {
+    char* st = smem + (kt % S) * STAGE;
+    const int k0 = k_begin + kt * BK;
+    if constexpr (AKC) da.issue_kc(st, k0);
+    else da.issue_mn(st, Ab + m0, args.lda, k0, k_end, args.M - m0);
+    if constexpr (BKC) db.issue_kc(st + ASZ, k0);
+    else db.issue_mn(st + ASZ, Bb + n0, args.ldb, k0, k_end, args.N - n0);
+  };
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+
+  constexpr int LPS = DmaOperand<BM, NW, AKC>::Q + DmaOperand<BN, NW, BKC>::Q;   // loads per stage
+  const int nk = (k_end > k_begin) ? (k_end - k_begin + BK - 1) / BK : 0;
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s)
+    if (s < nk) issue(s);
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int ahead = min(S - 2, nk - 1 - kt);   // stages already issued after this one
+    if (S >= 5 && ahead >= 3) wait_vm_lgkm0<3 * LPS>();
+    else if (S >= 4 && ahead >= 2) wait_vm_lgkm0<2 * LPS>();
+    else if (S >= 3 && ahead >= 1) wait_vm_lgkm0<LPS>();
+    else wait_vm_lgkm0<0>();
+    cta_barrier();
+    if (kt + S - 1 < nk) issue(kt + S - 1);
+    const char* as = smem + (kt % S) * STAGE;
+    const char* bs = as + ASZ;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      u32x4 af[TM], bfr[TN];
+      if constexpr (AKC) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          af[i] = *reinterpret_cast<const u32x4*>(as + kc_off(wm * WTM + i * 32 + (lane & 31), ks * 2 + (lane >> 5)));
+      } else {
+        const int kb = ks * 16 + (lane >> 5) * 8 + ((lane & 15) >> 2);
+        const int cb = (((lane >> 4) & 1) * 16 + 4 * (lane & 3)) * 2;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const int byte = (wm * WTM + i * 32) * 2 + cb;
+          af[i] = lds_tr_frag(as + mn_off<BM>(kb, byte), as + mn_off<BM>(kb + 4, byte));
+        }
+      }
+      if constexpr (BKC) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          bfr[j] = *reinterpret_cast<const u32x4*>(bs + kc_off(wn * WTN + j * 32 + (lane & 31), ks * 2 + (lane >> 5)));
+      } else {
+        const int kb = ks * 16 + (lane >> 5) * 8 + ((lane & 15) >> 2);
+        const int cb = (((lane >> 4) & 1) * 16 + 4 * (lane & 3)) * 2;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int byte = (wn * WTN + j * 32) * 2 + cb;
+          bfr[j] = lds_tr_frag(bs + mn_off<BN>(kb, byte), bs + mn_off<BN>(kb + 4, byte));
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) Mma<T>::run(acc[i][j], af[i], bfr[j]);
+    }
+  }
+  __syncthreads();
+  wave_epilogue<BM, BN, WM, WN, GROUP, EPI>(args, ctx, acc, smem);
+}
+
+template <int BM, int BN, int WM, int WN, int S>
+constexpr size_t dma_lds_bytes() {
+  constexpr size_t ring = (size_t)S * (BM + BN) * 64;
+  constexpr size_t epi = (size_t)WM * WN * 32 * (BN / WN + 8) * 4;
+  return ring > epi ? ring : epi;
+}
+
+}  // namespace moe_gemm

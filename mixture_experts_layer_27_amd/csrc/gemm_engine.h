@@ -183,34 +183,70 @@ template <> struct Mma<float> {
   }
 };
 
+// ---------------------------------------------------------------- 8-wide vectors
+
+template <typename T> struct Vec8;
+template <> struct Vec8<bf16_t> {
+  static MOE_DEV float rnd(float v) { return bf2f(f2bf(v)); }
+  static MOE_DEV void load(const bf16_t* p, float* v) {
+    u32x4 a = ldg16(p);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[2 * q] = __uint_as_float(a[q] << 16);
+      v[2 * q + 1] = __uint_as_float(a[q] & 0xffff0000u);
+    }
+  }
+  static MOE_DEV void store(bf16_t* p, const float* v) {
+    u32x4 a;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) a[q] = pack_bf2(v[2 * q], v[2 * q + 1]);
+    stg16(p, a);
+  }
+};
+template <> struct Vec8<float> {
+  static MOE_DEV float rnd(float v) { return v; }
+  static MOE_DEV void load(const float* p, float* v) {
+    u32x4 a = ldg16(p), b = ldg16(p + 4);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      v[q] = __uint_as_float(a[q]);
+      v[4 + q] = __uint_as_float(b[q]);
+    }
+  }
+  static MOE_DEV void store(float* p, const float* v) {
+    stg16(p, u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])});
+    stg16(p + 4, u32x4{__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]), __float_as_uint(v[7])});
+  }
+};
+
 // ---------------------------------------------------------------- kernel
 
-template <typename T, int BM, int BN, int WM, int WN, bool AKC, bool BKC, int GROUP, int EPI>
-__global__ __launch_bounds__(WM* WN * 64) void grouped_gemm(Args args) {
-  constexpr int NT = WM * WN * 64;
-  constexpr int BK = 128 / sizeof(T);
-  constexpr int WTM = BM / WM, WTN = BN / WN;
-  constexpr int TM = WTM / 32, TN = WTN / 32;
-  static_assert(TM >= 1 && TN >= 1, "wave tile must hold a 32x32 MFMA tile");
-  static_assert(EPI != EPI_SWIGLU || TN % 2 == 0, "SwiGLU needs gate and up tiles per wave");
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  // stage s: A tile at s*(BM+BN)*128, B tile right after it
-  auto a_stage = [&](int st) -> char* { return smem + st * (BM + BN) * 128; };
-  auto b_stage = [&](int st) -> char* { return smem + st * (BM + BN) * 128 + BM * 128; };
+// Logical tile of this block, in XCD-aware order: hardware block b runs on XCD
+// b % 8, so logical tile (b % 8) * per + b / 8 gives each XCD a contiguous run of
+// logical tiles.  Returns false when the block has no tile.
+struct TileCtx {
+  int e, mt, nt, split;
+  int row_begin, row_end;   // GROUP_M: rows of A / D of this tile's expert segment
+  int k_begin, k_end;       // reduction range (segment rows for GROUP_K, a K slice for split-K)
+  int m0, n0;
+};
 
-  // ---- logical tile (XCD-aware order)
+constexpr int kGroupM = 4;
+
+template <int BM, int BN, int BK, int GROUP>
+MOE_DEV bool decode_tile(const Args& args, TileCtx& c) {
   int total;
   if constexpr (GROUP == GROUP_M) total = args.tile_prefix[args.E] * args.tilesN;
   else total = args.total_static;
   const int per = (total + 7) >> 3;
   const int b = blockIdx.x;
-  if ((b >> 3) >= per) return;
+  if ((b >> 3) >= per) return false;
   const int L = (b & 7) * per + (b >> 3);
-  if (L >= total) return;
+  if (L >= total) return false;
 
   int e = 0, mt = 0, nt = 0, split = 0;
-  int row_begin = 0, row_end = 0;     // GROUP_M: rows of A / D;  others: unused
-  int k_begin = 0, k_end = args.K;    // reduction range (rows of MN operands for GROUP_K)
+  int row_begin = 0, row_end = 0;
+  int k_begin = 0, k_end = args.K;
   if constexpr (GROUP == GROUP_M) {
     int lo = 0, hi = args.E;          // find e: prefix[e]*tilesN <= L < prefix[e+1]*tilesN
     while (hi - lo > 1) {
@@ -220,8 +256,14 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm(Args args) {
     e = lo;
     int p0 = args.tile_prefix[e], cnt = args.tile_prefix[e + 1] - p0;
     int r = L - p0 * args.tilesN;
-    nt = r / cnt;
-    mt = r - nt * cnt;
+    // m-tiles of the expert in groups of kGroupM; inside a group the n-tile is
+    // outer and the m-tile inner, so a window of consecutive tiles covers a few
+    // m-tiles x several n-tiles and both operands are reused from L2
+    const int g = r / (kGroupM * args.tilesN);
+    const int gsize = min(kGroupM, cnt - g * kGroupM);
+    const int within = r - g * kGroupM * args.tilesN;
+    nt = within / gsize;
+    mt = g * kGroupM + (within - nt * gsize);
     row_begin = args.offsets[e] + mt * BM;
     row_end = args.offsets[e + 1];
   } else if constexpr (GROUP == GROUP_K) {
@@ -242,7 +284,183 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm(Args args) {
     k_begin = split * kc;
     k_end = min(args.K, k_begin + kc);
   }
-  const int m0 = mt * BM, n0 = nt * BN;
+  c.e = e; c.mt = mt; c.nt = nt; c.split = split;
+  c.row_begin = row_begin; c.row_end = row_end;
+  c.k_begin = k_begin; c.k_end = k_end;
+  c.m0 = mt * BM; c.n0 = nt * BN;
+  return true;
+}
+
+// Epilogue shared by both main loops.  acc holds the wave's (BM/WM) x (BN/WN)
+// tile as 32x32 MFMA sub-tiles; LDS (at least (BM/WM) * (BN+8) floats) must be
+// free.  Ends with a barrier.
+template <typename T, int BM, int BN, int WM, int WN, int GROUP, int EPI>
+MOE_DEV void gemm_epilogue(const Args& args, const TileCtx& ctx, f32x16 (&acc)[BM / WM / 32][BN / WN / 32],
+                           char* smem) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int e = ctx.e, nt = ctx.nt, split = ctx.split;
+  const int row_begin = ctx.row_begin, row_end = ctx.row_end;
+  const int m0 = ctx.m0, n0 = ctx.n0;
+  (void)e; (void)split; (void)nt;
+  // ---- epilogue.  The accumulators are staged through LDS one wave-row at a
+  // time (sub-tile (i, j), register q holds row i*32 + 8*(q/4) + 4*(lane/32) + q%4,
+  // column j*32 + lane%32 of the wave tile); then every thread works on 8
+  // consecutive columns of one row, so global loads/stores are 16-byte vectors
+  // and 32 consecutive lanes cover one 256-column row.
+  constexpr int CS = BN + 8;          // staged row stride (floats)
+  constexpr int CPR = BN / 8;         // 8-column chunks per row
+  float* cs = reinterpret_cast<float*>(smem);
+  for (int pass = 0; pass < WM; ++pass) {
+    if (wm == pass) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int q = 0; q < 16; ++q)
+            cs[(i * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3)) * CS + wn * WTN + j * 32 + (lane & 31)] =
+                acc[i][j][q];
+    }
+    __syncthreads();
+    const int r0 = pass * WTM;
+    if constexpr (EPI == EPI_SWIGLU) {
+      // tile columns [0, BN/2) are gate columns g0.., [BN/2, BN) the matching up columns
+      constexpr int HC = CPR / 2;
+      T* H = reinterpret_cast<T*>(args.C);
+      T* Aout = reinterpret_cast<T*>(args.C2);
+      for (int u = threadIdx.x; u < WTM * HC; u += NT) {
+        const int rr = u / HC, ch = u % HC;
+        const int grow = row_begin + r0 + rr;
+        if (grow >= row_end) continue;
+        const float* src = cs + rr * CS + ch * 8;
+        float hg[8], hu[8], a[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+          hg[c] = Vec8<T>::rnd(src[c]);              // H as stored
+          hu[c] = Vec8<T>::rnd(src[BN / 2 + c]);
+          a[c] = hg[c] / (1.0f + expf(-hg[c])) * hu[c];
+        }
+        const int gcol = nt * (BN / 2) + ch * 8;
+        T* hrow = H + (int64_t)grow * args.ldc;
+        Vec8<T>::store(hrow + gcol, hg);
+        Vec8<T>::store(hrow + args.f + gcol, hu);
+        Vec8<T>::store(Aout + (int64_t)grow * args.ldc2 + gcol, a);
+      }
+    } else if constexpr (EPI == EPI_DSWIGLU) {
+      // cs = dA' for columns n0.. of f.  aux = H [rows, 2f]; C = dH [rows, 2f];
+      // C2 = gA [rows, f]; C3[nt * ldc3 + row] = this tile's part of dS = <dA', A>
+      static_assert((WTM * CPR) % NT == 0 && CPR <= 64, "uniform trip count for the row reduction");
+      const T* H = reinterpret_cast<const T*>(args.aux);
+      T* dH = reinterpret_cast<T*>(args.C);
+      T* gA = reinterpret_cast<T*>(args.C2);
+      for (int u = threadIdx.x; u < WTM * CPR; u += NT) {
+        const int rr = u / CPR, ch = u % CPR;
+        const int grow = row_begin + r0 + rr;
+        const int col = n0 + ch * 8;
+        float part = 0.0f;
+        if (grow < row_end && col < args.N) {
+          const float* src = cs + rr * CS + ch * 8;
+          const float g = args.row_gate[grow];
+          const T* hrow = H + (int64_t)grow * args.ld_aux;
+          float hg[8], hu[8], dhg[8], dhu[8], ga[8];
+          Vec8<T>::load(hrow + col, hg);
+          Vec8<T>::load(hrow + args.f + col, hu);
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            const float dap = src[c];
+            const float sg = 1.0f / (1.0f + expf(-hg[c]));
+            const float sl = hg[c] * sg;
+            const float a = Vec8<T>::rnd(sl * hu[c]);      // A as stored in the forward
+            part += dap * a;
+            const float da = g * dap;
+            dhg[c] = da * hu[c] * (sg * (1.0f + hg[c] * (1.0f - sg)));
+            dhu[c] = da * sl;
+            ga[c] = g * a;
+          }
+          T* drow = dH + (int64_t)grow * args.ldc;
+          Vec8<T>::store(drow + col, dhg);
+          Vec8<T>::store(drow + args.f + col, dhu);
+          Vec8<T>::store(gA + (int64_t)grow * args.ldc2 + col, ga);
+        }
+#pragma unroll
+        for (int o = 1; o < CPR; o <<= 1) part += __shfl_xor(part, o, 64);
+        if (ch == 0 && grow < row_end) args.C3[(int64_t)nt * args.ldc3 + grow] = part;
+      }
+    } else if constexpr (EPI == EPI_DX) {
+      // dx[t, c] = acc + sum over the rows of t of gsrc[row, c]  (router term + unpermute-sum)
+      T* C = reinterpret_cast<T*>(args.C);
+      const T* G = reinterpret_cast<const T*>(args.gsrc);
+      for (int u = threadIdx.x; u < WTM * CPR; u += NT) {
+        const int rr = u / CPR, ch = u % CPR;
+        const int t = m0 + r0 + rr;
+        const int col = n0 + ch * 8;
+        if (t >= args.M || col >= args.N) continue;
+        const float* src = cs + rr * CS + ch * 8;
+        float v[8], w[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) v[c] = src[c];
+        const int p0 = args.csr_ptr[t], p1 = args.csr_ptr[t + 1];
+        for (int p = p0; p < p1; ++p) {
+          Vec8<T>::load(G + (int64_t)args.csr_rows[p] * args.ld_gsrc + col, w);
+#pragma unroll
+          for (int c = 0; c < 8; ++c) v[c] += w[c];
+        }
+        Vec8<T>::store(C + (int64_t)t * args.ldc + col, v);
+      }
+    } else {
+      // EPI_ACT (act dtype), EPI_F32 (fp32, split-K partials / per-expert slabs), EPI_LOGITS (+ bias)
+      using OT = typename std::conditional<EPI == EPI_ACT, T, float>::type;
+      OT* C = reinterpret_cast<OT*>(args.C);
+      if constexpr (GROUP == GROUP_K) C += (int64_t)e * args.c_estride;
+      if constexpr (GROUP == GROUP_NONE) C += (int64_t)split * args.c_kstride;
+      for (int u = threadIdx.x; u < WTM * CPR; u += NT) {
+        const int rr = u / CPR, ch = u % CPR;
+        int grow;
+        bool ok;
+        if constexpr (GROUP == GROUP_M) { grow = row_begin + r0 + rr; ok = grow < row_end; }
+        else { grow = m0 + r0 + rr; ok = grow < args.M; }
+        const int col = n0 + ch * 8;
+        if (!ok || col >= args.N) continue;
+        const float* src = cs + rr * CS + ch * 8;
+        float v[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) v[c] = src[c];
+        OT* dst = C + (int64_t)grow * args.ldc + col;
+        if constexpr (EPI == EPI_LOGITS) {
+#pragma unroll
+          for (int c = 0; c < 8; ++c)
+            if (col + c < args.N) dst[c] = v[c] + (args.bias ? args.bias[col + c] : 0.0f);
+        } else {
+          Vec8<OT>::store(dst, v);
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <typename T, int BM, int BN, int WM, int WN, bool AKC, bool BKC, int GROUP, int EPI>
+__global__ __launch_bounds__(WM* WN * 64) void grouped_gemm(Args args) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int BK = 128 / sizeof(T);
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  static_assert(TM >= 1 && TN >= 1, "wave tile must hold a 32x32 MFMA tile");
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  // stage s: A tile at s*(BM+BN)*128, B tile right after it
+  auto a_stage = [&](int st) -> char* { return smem + st * (BM + BN) * 128; };
+  auto b_stage = [&](int st) -> char* { return smem + st * (BM + BN) * 128 + BM * 128; };
+
+  TileCtx ctx;
+  if (!decode_tile<BM, BN, BK, GROUP>(args, ctx)) return;
+  const int e = ctx.e, nt = ctx.nt;
+  const int row_begin = ctx.row_begin, row_end = ctx.row_end;
+  const int k_begin = ctx.k_begin, k_end = ctx.k_end;
+  const int m0 = ctx.m0, n0 = ctx.n0;
   const T* Ab = reinterpret_cast<const T*>(args.A) + (int64_t)e * args.a_estride;
   const T* Bb = reinterpret_cast<const T*>(args.B) + (int64_t)e * args.b_estride;
 
@@ -262,10 +480,9 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm(Args args) {
   auto b_row = [&](int row) -> const T* {
     int j = n0 + row;
     if constexpr (EPI == EPI_SWIGLU) {
-      // wave wn's columns: first half gate rows, second half the matching up rows
-      int wn = row / WTN, jj = row % WTN;
-      int g = nt * (BN / 2) + wn * (WTN / 2) + (jj % (WTN / 2));
-      j = (jj < WTN / 2) ? g : (args.f + g);
+      // tile rows [0, BN/2): gate rows g0..; [BN/2, BN): the matching up rows
+      const int g0 = nt * (BN / 2);
+      j = (row < BN / 2) ? (g0 + row) : (args.f + g0 + row - BN / 2);
     }
     if (j >= args.N && EPI != EPI_SWIGLU) j = args.N - 1;
     return Bb + (int64_t)j * args.ldb;
@@ -338,138 +555,16 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm(Args args) {
     __syncthreads();
   }
 
-  // ---- epilogues.  Sub-tile (i, j), register q holds
-  //      row = wm*WTM + i*32 + 8*(q/4) + 4*(lane/32) + q%4,  col = wn*WTN + j*32 + lane%32
-  const int rbase = wm * WTM + 4 * (lane >> 5);
-  const int cbase = wn * WTN + (lane & 31);
-
-  if constexpr (EPI == EPI_ACT || EPI == EPI_F32 || EPI == EPI_LOGITS) {
-    using OT = typename std::conditional<EPI == EPI_ACT, T, float>::type;
-    OT* C = reinterpret_cast<OT*>(args.C);
-    if constexpr (GROUP == GROUP_K) C += (int64_t)e * args.c_estride;
-    if constexpr (GROUP == GROUP_NONE) C += (int64_t)split * args.c_kstride;
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        int r = rbase + i * 32 + 8 * (q >> 2) + (q & 3);
-        int grow;
-        bool ok;
-        if constexpr (GROUP == GROUP_M) { grow = row_begin + r; ok = grow < row_end; }
-        else { grow = m0 + r; ok = grow < args.M; }
-        if (!ok) continue;
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          int col = n0 + cbase + j * 32;
-          if (col >= args.N) continue;
-          float v = acc[i][j][q];
-          if constexpr (EPI == EPI_LOGITS) { if (args.bias) v += args.bias[col]; }
-          Elem<OT>::store(C + (int64_t)grow * args.ldc + col, v);
-        }
-      }
-  } else if constexpr (EPI == EPI_SWIGLU) {
-    // H (C, ld 2f) gets both halves; A (C2, ld f) = silu(H_gate) * H_up from the stored H
-    T* H = reinterpret_cast<T*>(args.C);
-    T* Aout = reinterpret_cast<T*>(args.C2);
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        int r = rbase + i * 32 + 8 * (q >> 2) + (q & 3);
-        int grow = row_begin + r;
-        if (grow >= row_end) continue;
-#pragma unroll
-        for (int j = 0; j < TN / 2; ++j) {
-          int gcol = nt * (BN / 2) + wn * (WTN / 2) + j * 32 + (lane & 31);
-          T* hrow = H + (int64_t)grow * args.ldc;
-          float hg = acc[i][j][q], hu = acc[i][j + TN / 2][q];
-          if constexpr (sizeof(T) == 2) {  // A is computed from H as stored
-            hg = bf2f(f2bf(hg));
-            hu = bf2f(f2bf(hu));
-          }
-          Elem<T>::store(hrow + gcol, hg);
-          Elem<T>::store(hrow + args.f + gcol, hu);
-          float a = hg / (1.0f + expf(-hg)) * hu;
-          Elem<T>::store(Aout + (int64_t)grow * args.ldc2 + gcol, a);
-        }
-      }
-  } else if constexpr (EPI == EPI_DSWIGLU) {
-    // acc = dA' (columns n0.. of f).  aux = H [rows, 2f]; C = dH [rows, 2f];
-    // C2 = gA [rows, f]; C3 = dS partial for this column tile: C3[nt * ldc3 + row]
-    const T* H = reinterpret_cast<const T*>(args.aux);
-    T* dH = reinterpret_cast<T*>(args.C);
-    T* gA = reinterpret_cast<T*>(args.C2);
-    float* red = reinterpret_cast<float*>(smem);   // LDS is free after the main loop
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        int r = rbase + i * 32 + 8 * (q >> 2) + (q & 3);
-        int grow = row_begin + r;
-        bool ok = grow < row_end;
-        float part = 0.0f;
-        if (ok) {
-          float g = args.row_gate[grow];
-          const T* hrow = H + (int64_t)grow * args.ld_aux;
-#pragma unroll
-          for (int j = 0; j < TN; ++j) {
-            int col = n0 + cbase + j * 32;
-            if (col >= args.N) continue;
-            float dap = acc[i][j][q];
-            float hg = Elem<T>::load(hrow + col);
-            float hu = Elem<T>::load(hrow + args.f + col);
-            float sg = 1.0f / (1.0f + expf(-hg));
-            float sl = hg * sg;
-            float a = sl * hu;
-            if constexpr (sizeof(T) == 2) a = bf2f(f2bf(a));   // A as stored in the forward
-            part += dap * a;
-            float da = g * dap;
-            float dsl = sg * (1.0f + hg * (1.0f - sg));
-            T* drow = dH + (int64_t)grow * args.ldc;
-            Elem<T>::store(drow + col, da * hu * dsl);
-            Elem<T>::store(drow + args.f + col, da * sl);
-            Elem<T>::store(gA + (int64_t)grow * args.ldc2 + col, g * a);
-          }
-        }
-        // sum over the 32 columns held by lanes with the same lane/32
-#pragma unroll
-        for (int o = 1; o < 32; o <<= 1) part += __shfl_xor(part, o, 64);
-        if ((lane & 31) == 0) red[wn * BM + r] = part;
-      }
-    __syncthreads();
-    for (int r = threadIdx.x; r < BM; r += NT) {
-      int grow = row_begin + r;
-      if (grow < row_end) {
-        float s = 0.0f;
-#pragma unroll
-        for (int w = 0; w < WN; ++w) s += red[w * BM + r];
-        args.C3[(int64_t)nt * args.ldc3 + grow] = s;
-      }
-    }
-  } else if constexpr (EPI == EPI_DX) {
-    // dx[t, c] = acc + sum over the rows of t of gsrc[row, c]  (router term + unpermute-sum)
-    T* C = reinterpret_cast<T*>(args.C);
-    const T* G = reinterpret_cast<const T*>(args.gsrc);
-#pragma unroll
-    for (int i = 0; i < TM; ++i)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        int t = m0 + rbase + i * 32 + 8 * (q >> 2) + (q & 3);
-        if (t >= args.M) continue;
-        int p0 = args.csr_ptr[t], p1 = args.csr_ptr[t + 1];
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          int col = n0 + cbase + j * 32;
-          if (col >= args.N) continue;
-          float v = acc[i][j][q];
-          for (int p = p0; p < p1; ++p) v += Elem<T>::load(G + (int64_t)args.csr_rows[p] * args.ld_gsrc + col);
-          Elem<T>::store(C + (int64_t)t * args.ldc + col, v);
-        }
-      }
-  }
+  gemm_epilogue<T, BM, BN, WM, WN, GROUP, EPI>(args, ctx, acc, smem);
 }
 
+// Dynamic LDS of one block: two operand stages, or the staged accumulator rows
+// of the epilogue, whichever is larger.
 template <typename T, int BM, int BN, int WM, int WN>
-constexpr size_t lds_bytes() { return (size_t)2 * (BM + BN) * 128; }
+constexpr size_t lds_bytes() {
+  constexpr size_t main_loop = (size_t)2 * (BM + BN) * 128;
+  constexpr size_t epi = (size_t)(BM / WM) * (BN + 8) * 4;
+  return main_loop > epi ? main_loop : epi;
+}
 
 }  // namespace moe_gemm

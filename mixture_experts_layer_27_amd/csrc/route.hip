@@ -17,10 +17,11 @@ namespace {
 
 MOE_DEV bool better(float av, int ae, float bv, int be) { return av > bv || (av == bv && ae < be); }
 
-// One wave per token, 16 tokens per wave, 64 tokens per block.  Lane l holds
-// experts l, l+64, ...  With ROUND the block also writes the full softmax
-// expert-major (probs_t) and the selection bitmap expert-major (sel_t).
-template <int V, bool ROUND>
+// One wave per token; a wave takes TPW tokens in turn (4*TPW per block).  Lane l
+// holds experts l, l+64, ...  With ROUND (TPW = 16, 64 tokens per block) the
+// block also writes the full softmax expert-major (probs_t) and the selection
+// bitmap expert-major (sel_t), transposed through LDS.
+template <int V, bool ROUND, int TPW>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                   int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate,
                                                   uint32_t* __restrict__ keep_bits, int words,
@@ -30,13 +31,14 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   float* pt = reinterpret_cast<float*>(smem);                       // [E][64]
   uint32_t* sel = reinterpret_cast<uint32_t*>(smem + (size_t)E * 64 * 4);  // [E][2]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t0 = blockIdx.x * 64;
+  static_assert(!ROUND || TPW == 16, "the transposed writes assume 64 tokens per block");
+  const int t0 = blockIdx.x * 4 * TPW;
   if constexpr (ROUND) {
     for (int i = threadIdx.x; i < E * 2; i += 256) sel[i] = 0u;
     __syncthreads();
   }
-  for (int it = 0; it < 16; ++it) {
-    const int tl = wave * 16 + it;
+  for (int it = 0; it < TPW; ++it) {
+    const int tl = wave * TPW + it;
     const int t = t0 + tl;
     if (t >= T) break;
     float z[V];
@@ -391,12 +393,12 @@ __global__ __launch_bounds__(1024) void round_select_kernel(const float* __restr
 
 hipError_t launch_topk(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, bool rounding,
                        hipStream_t st) {
-  const int grid = ceil_div(s.T, 64);
+  const int grid = rounding ? ceil_div(s.T, 64) : ceil_div(s.T, 4);
   const int wordsT = ceil_div(s.T, 32);
   size_t lds = rounding ? (size_t)s.E * 64 * 4 + (size_t)s.E * 8 : 0;
 #define MOE_TOPK(V, R)                                                                                  \
   do {                                                                                                 \
-    auto kern = topk_kernel<V, R>;                                                                     \
+    auto kern = topk_kernel<V, R, R ? 16 : 1>;                                                                     \
     if (lds > 65536) hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
     hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, st, p.logits, s.T, s.E, s.k, p.topk_idx,      \
                        p.topk_gate, p.keep_bits, pi.words, p.probs_t, pi.sel_t, wordsT);               \
