@@ -270,6 +270,27 @@ def route(x, w_gate, bias, k, round_tile=0):
 # expert FFN forward: F6-F7
 
 
+def _wexp(w, e):
+    """Expert e's weight matrix in float64.  ``w`` is an array [E, ...] or any
+    object whose ``w[e]`` converts to one (lets full-size checks avoid
+    materialising every expert in float64)."""
+    return np.asarray(w[e], dtype=np.float64)
+
+
+def sub_plan(plan: Plan, tokens=None, experts=None) -> Plan:
+    """The plan restricted to the rows of the given tokens and/or experts.
+
+    Same routing decisions, fewer rows: used to evaluate the layer's outputs
+    for a sample of tokens (or all rows of a sample of experts) one by one."""
+    keep = np.ones(plan.N, bool)
+    if tokens is not None:
+        keep &= np.isin(plan.token_of_row, np.asarray(tokens))
+    if experts is not None:
+        keep &= np.isin(plan.expert_of_row, np.asarray(experts))
+    return _assemble(plan.T, plan.E, plan.k, plan.topk_idx, plan.topk_gate, plan.probs,
+                     plan.token_of_row[keep], plan.expert_of_row[keep], plan.gate_of_row[keep])
+
+
 def _segments(plan):
     for e in range(plan.E):
         a, b = int(plan.offsets[e]), int(plan.offsets[e + 1])
@@ -292,8 +313,6 @@ def forward(x, w1, w2, plan: Plan, prec: Precision = CONTRACT) -> Dict[str, np.n
     Under ``prec`` the stored H, A and Y are rounded to bf16; A is computed from
     the stored H."""
     x = np.asarray(x, np.float64)
-    w1 = np.asarray(w1, np.float64)
-    w2 = np.asarray(w2, np.float64)
     N = plan.N
     T, d = x.shape
     f = w2.shape[2]
@@ -304,7 +323,7 @@ def forward(x, w1, w2, plan: Plan, prec: Precision = CONTRACT) -> Dict[str, np.n
         if a == b:
             continue
         xe = _mxk(x_perm[a:b], prec, 1)
-        w1e = _mxk(w1[e], prec, 1)
+        w1e = _mxk(_wexp(w1, e), prec, 1)
         H[a:b] = xe @ w1e.T
     H = prec.st(H)
     A = prec.st(silu(H[:, :f]) * H[:, f:])
@@ -312,7 +331,7 @@ def forward(x, w1, w2, plan: Plan, prec: Precision = CONTRACT) -> Dict[str, np.n
         if a == b:
             continue
         ae = _mxk(A[a:b], prec, 1)
-        w2e = _mxk(w2[e], prec, 1)
+        w2e = _mxk(_wexp(w2, e), prec, 1)
         Y[a:b] = ae @ w2e.T
     Y = prec.st(Y)
     O = np.zeros((T, d))
@@ -352,7 +371,8 @@ def router_backward(plan: Plan, dS):
     return dz
 
 
-def backward(x, w_gate, w1, w2, plan: Plan, H, dout, prec: Precision = CONTRACT) -> Dict[str, np.ndarray]:
+def backward(x, w_gate, w1, w2, plan: Plan, H, dout, prec: Precision = CONTRACT,
+             weight_grads=True) -> Dict[str, np.ndarray]:
     """Backward of the layer for the loss sum_t <O_t, dout_t>.
 
     SonicMoE article section 1: the router-score gradient of row r is
@@ -362,8 +382,6 @@ def backward(x, w_gate, w1, w2, plan: Plan, H, dout, prec: Precision = CONTRACT)
     the router softmax (``router_backward``) and the router GEMM."""
     x = np.asarray(x, np.float64)
     w_gate = np.asarray(w_gate, np.float64)
-    w1 = np.asarray(w1, np.float64)
-    w2 = np.asarray(w2, np.float64)
     H = np.asarray(H, np.float64)
     dout = np.asarray(dout, np.float64)
     N = plan.N
@@ -379,20 +397,32 @@ def backward(x, w_gate, w1, w2, plan: Plan, H, dout, prec: Precision = CONTRACT)
     for e, a, b in _segments(plan):
         if a == b:
             continue
-        dAp[a:b] = _mxk(do_perm[a:b], prec, 1) @ _mxk(w2[e], prec, 0)
+        dAp[a:b] = _mxk(do_perm[a:b], prec, 1) @ _mxk(_wexp(w2, e), prec, 0)
     dS = np.einsum("rj,rj->r", dAp, A)
     dA = g[:, None] * dAp
     dH = prec.st(np.concatenate([dA * hu * dsilu(hg), dA * silu(hg)], axis=1))
     gA = prec.st(g[:, None] * A)
     dx_perm = np.zeros((N, d))
-    dw1 = np.zeros_like(w1)
-    dw2 = np.zeros_like(w2)
+    # weight gradients: True -> full [E, ...] arrays; a collection of experts ->
+    # dicts for those experts only; False -> not computed
+    if weight_grads is True:
+        dw1 = np.zeros((E, 2 * f, d))
+        dw2 = np.zeros((E, d, f))
+        wanted = range(E)
+    elif weight_grads is False:
+        dw1 = dw2 = None
+        wanted = ()
+    else:
+        wanted = list(weight_grads)
+        dw1 = {e: np.zeros((2 * f, d)) for e in wanted}
+        dw2 = {e: np.zeros((d, f)) for e in wanted}
     for e, a, b in _segments(plan):
         if a == b:
             continue
-        dx_perm[a:b] = _mxk(dH[a:b], prec, 1) @ _mxk(w1[e], prec, 0)
-        dw1[e] = _mxk(dH[a:b], prec, 0).T @ _mxk(x_perm[a:b], prec, 0)
-        dw2[e] = _mxk(do_perm[a:b], prec, 0).T @ _mxk(gA[a:b], prec, 0)
+        dx_perm[a:b] = _mxk(dH[a:b], prec, 1) @ _mxk(_wexp(w1, e), prec, 0)
+        if e in wanted:
+            dw1[e] = _mxk(dH[a:b], prec, 0).T @ _mxk(x_perm[a:b], prec, 0)
+            dw2[e] = _mxk(do_perm[a:b], prec, 0).T @ _mxk(gA[a:b], prec, 0)
     dx_perm = prec.st(dx_perm)
     dz = router_backward(plan, dS)
     dzq = prec.st(dz)                                # GEMM operand of the router terms

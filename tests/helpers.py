@@ -60,3 +60,15 @@ def assert_close(name, got, ref, atol=2e-2, rfrob=1e-2):
     ok, mabs, rf = close(got, ref, atol, rfrob)
     assert ok, f"{name}: max-abs/scale {mabs:.3e} (tol {atol}), rel-Frobenius {rf:.3e} (tol {rfrob})"
     return mabs, rf
+
+
+class LazyExperts:
+    """Per-expert float64 view of a [E, ...] torch weight tensor (the oracle reads
+    one expert at a time, so full-size checks never hold all experts in float64)."""
+
+    def __init__(self, w):
+        self.w = w
+        self.shape = tuple(w.shape)
+
+    def __getitem__(self, e):
+        return self.w[e].double().numpy()
