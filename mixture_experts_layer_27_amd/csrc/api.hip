@@ -7,9 +7,6 @@
 
 namespace moe {
 
-hipError_t launch_quantize_rows(const void* src, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
-                                hipStream_t st);
-
 int64_t max_rows(const moe_shape& s) {
   return (int64_t)s.T * s.k + (s.round_tile ? (int64_t)s.E * (s.round_tile / 2) : 0);
 }
@@ -79,7 +76,6 @@ moe_status check_shape(const moe_shape* s) {
   if (s->T > (1 << 20)) return MOE_ENOTSUP;
   if (s->round_tile > 4096) return MOE_ENOTSUP;
   if (max_rows(*s) >= ((int64_t)1 << 31)) return MOE_ENOTSUP;
-  if (s->gemm == MOE_MXFP8) return MOE_ENOTSUP;   // MX expert GEMMs: see moe_quantize_mx for the quantiser
   return MOE_OK;
 }
 
@@ -99,9 +95,24 @@ moe_status check_plan(const moe_shape& s, const moe_plan* p) {
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
 
+// token capacity of the expert-padded layout of the MX weight-gradient operands
+int64_t tok_cap(const moe_shape& s) { return (max_rows(s) + 64 * (int64_t)s.E + 63) / 64 * 64; }
+
+MxOperand take_mx(Carver& c, int64_t rows, int64_t K, int64_t srows, const int32_t* pad = nullptr) {
+  MxOperand o;
+  o.codes = c.take<uint8_t>((size_t)rows * K);
+  o.scales = c.take<uint8_t>((size_t)(K / 64) * srows * 2);
+  o.srows = srows;
+  o.pad = pad;
+  return o;
+}
+
 struct BwdWs {
   void *do_perm, *dh, *ga, *xbuf, *dzq;
   float *ds_part, *dlogits, *dwg_part;
+  // MXFP8 only
+  MxOperand doq, w2t, dhq, w1t, dh_t, x_t, do_t, ga_t;
+  int32_t* pad_off;
 };
 
 size_t carve_bwd(const moe_shape& s, char* base, BwdWs* w) {
@@ -116,11 +127,46 @@ size_t carve_bwd(const moe_shape& s, char* base, BwdWs* w) {
   q.dlogits = c.take<float>((size_t)s.T * s.E * 4);
   q.dzq = c.take<char>((size_t)s.T * ldz_of(s) * esz(s));
   q.dwg_part = c.take<float>((size_t)gemm_router_dwg_splits(s) * s.E * s.d * 4);
+  if (s.gemm == MOE_MXFP8) {
+    const int64_t E = s.E, d = s.d, f = s.d_ff, P = tok_cap(s);
+    q.pad_off = c.take<int32_t>((E + 1) * 4);
+    q.doq = take_mx(c, P, d, P, q.pad_off);
+    q.w2t = take_mx(c, E * f, d, E * f);
+    q.dhq = take_mx(c, P, 2 * f, P, q.pad_off);
+    q.w1t = take_mx(c, E * d, 2 * f, E * d);
+    q.dh_t = take_mx(c, 2 * f, P, 2 * f);
+    q.x_t = take_mx(c, d, P, d);
+    q.do_t = take_mx(c, d, P, d);
+    q.ga_t = take_mx(c, f, P, f);
+  }
   if (w) *w = q;
   return c.off;
 }
 
-size_t experts_ws(const moe_shape& s) { return al((size_t)max_rows(s) * s.d_ff * esz(s)); }
+struct FwdWs {
+  void* act;              // A [N_max, f]
+  int32_t* pad_off;       // MXFP8 only: expert-padded row offsets, quantised operands
+  MxOperand x, w1, a, w2;
+};
+
+size_t carve_fwd(const moe_shape& s, char* base, FwdWs* w) {
+  Carver c{base};
+  const int64_t N = max_rows(s);
+  FwdWs q{};
+  q.act = c.take<char>((size_t)N * s.d_ff * esz(s));
+  if (s.gemm == MOE_MXFP8) {
+    const int64_t E = s.E, d = s.d, f = s.d_ff, P = tok_cap(s);
+    q.pad_off = c.take<int32_t>((E + 1) * 4);
+    q.x = take_mx(c, P, d, P, q.pad_off);
+    q.w1 = take_mx(c, E * 2 * f, d, E * 2 * f);
+    q.a = take_mx(c, P, f, P, q.pad_off);
+    q.w2 = take_mx(c, E * d, f, E * d);
+  }
+  if (w) *w = q;
+  return c.off;
+}
+
+size_t experts_ws(const moe_shape& s) { return carve_fwd(s, nullptr, nullptr); }
 
 }  // namespace
 
@@ -227,8 +273,26 @@ moe_status moe_grouped_gemm_swiglu(const moe_shape* s, const void* x_perm, const
   if (!aligned(ws) || ws_bytes < experts_ws(*s)) return MOE_EWORKSPACE;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   PlanInternal pi = plan_internal(*s, *plan);
-  hipError_t e = gemm_up_swiglu(*s, *plan, pi, x_perm, w1, h_saved, ws, hs);
-  if (e == hipSuccess) e = gemm_down(*s, *plan, pi, ws, w2, y, hs);
+  FwdWs w;
+  carve_fwd(*s, reinterpret_cast<char*>(ws), &w);
+  hipError_t e;
+  if (s->gemm == MOE_MXFP8) {
+    const int64_t N = max_rows(*s);
+    const int E = s->E, d = s->d, f = s->d_ff;
+    const int32_t *off = plan->offsets, *eor = plan->expert_of_row;
+    e = mx_pad_offsets(off, E, w.pad_off, hs);
+    if (e == hipSuccess)
+      e = mx_quantize_rows_padded(x_perm, N, d, off, eor, w.pad_off, E, w.x.codes, w.x.scales, w.x.srows, hs);
+    if (e == hipSuccess) e = mx_quantize_rows_staged(w1, (int64_t)E * 2 * f, d, w.w1.codes, w.w1.scales, w.w1.srows, hs);
+    if (e == hipSuccess) e = gemm_mx_up_swiglu(*s, *plan, pi, w.x, w.w1, h_saved, w.act, hs);
+    if (e == hipSuccess)
+      e = mx_quantize_rows_padded(w.act, N, f, off, eor, w.pad_off, E, w.a.codes, w.a.scales, w.a.srows, hs);
+    if (e == hipSuccess) e = mx_quantize_rows_staged(w2, (int64_t)E * d, f, w.w2.codes, w.w2.scales, w.w2.srows, hs);
+    if (e == hipSuccess) e = gemm_mx_down(*s, *plan, pi, w.a, w.w2, y, hs);
+    return hip_status(e);
+  }
+  e = gemm_up_swiglu(*s, *plan, pi, x_perm, w1, h_saved, w.act, hs);
+  if (e == hipSuccess) e = gemm_down(*s, *plan, pi, w.act, w2, y, hs);
   return hip_status(e);
 }
 
@@ -258,11 +322,33 @@ moe_status moe_backward(const moe_shape* s, const void* x, const void* w_gate, c
   float* dz = dlogits ? dlogits : w.dlogits;
   const int ldz = ldz_of(*s);
   hipError_t e = launch_gather_rows(*s, dout, plan->token_of_row, plan->offsets, w.do_perm, hs);
-  if (e == hipSuccess) e = gemm_dact(*s, *plan, pi, w.do_perm, w2, h_saved, w.dh, w.ga, w.ds_part, hs);
-  if (e == hipSuccess) e = launch_gather_rows(*s, x, plan->token_of_row, plan->offsets, w.xbuf, hs);
-  if (e == hipSuccess) e = gemm_dw1(*s, *plan, w.dh, w.xbuf, dw1, hs);
-  if (e == hipSuccess) e = gemm_dw2(*s, *plan, w.do_perm, w.ga, dw2, hs);
-  if (e == hipSuccess) e = gemm_dx_perm(*s, *plan, pi, w.dh, w1, w.xbuf, hs);   // x_perm no longer needed
+  if (s->gemm == MOE_MXFP8) {
+    const int64_t N = max_rows(*s), P = tok_cap(*s);
+    const int E = s->E, d = s->d, f = s->d_ff;
+    const int32_t *off = plan->offsets, *eor = plan->expert_of_row;
+    if (e == hipSuccess) e = mx_pad_offsets(off, E, w.pad_off, hs);
+    if (e == hipSuccess)
+      e = mx_quantize_rows_padded(w.do_perm, N, d, off, eor, w.pad_off, E, w.doq.codes, w.doq.scales, w.doq.srows, hs);
+    if (e == hipSuccess) e = mx_quantize_cols(w2, E, d, f, w.w2t.codes, w.w2t.scales, hs);
+    if (e == hipSuccess) e = gemm_mx_dact(*s, *plan, pi, w.doq, w.w2t, h_saved, w.dh, w.ga, w.ds_part, hs);
+    if (e == hipSuccess)
+      e = mx_quantize_rows_padded(w.dh, N, 2 * f, off, eor, w.pad_off, E, w.dhq.codes, w.dhq.scales, w.dhq.srows, hs);
+    if (e == hipSuccess) e = mx_quantize_cols(w1, E, 2 * f, d, w.w1t.codes, w.w1t.scales, hs);
+    if (e == hipSuccess) e = launch_gather_rows(*s, x, plan->token_of_row, plan->offsets, w.xbuf, hs);
+    if (e == hipSuccess) e = mx_quantize_tokens(w.dh, 2 * f, plan->offsets, w.pad_off, E, P, w.dh_t.codes, w.dh_t.scales, hs);
+    if (e == hipSuccess) e = mx_quantize_tokens(w.xbuf, d, plan->offsets, w.pad_off, E, P, w.x_t.codes, w.x_t.scales, hs);
+    if (e == hipSuccess) e = mx_quantize_tokens(w.do_perm, d, plan->offsets, w.pad_off, E, P, w.do_t.codes, w.do_t.scales, hs);
+    if (e == hipSuccess) e = mx_quantize_tokens(w.ga, f, plan->offsets, w.pad_off, E, P, w.ga_t.codes, w.ga_t.scales, hs);
+    if (e == hipSuccess) e = gemm_mx_wgrad(*s, w.pad_off, P, w.dh_t, 2 * f, w.x_t, d, dw1, hs);
+    if (e == hipSuccess) e = gemm_mx_wgrad(*s, w.pad_off, P, w.do_t, d, w.ga_t, f, dw2, hs);
+    if (e == hipSuccess) e = gemm_mx_dx_perm(*s, *plan, pi, w.dhq, w.w1t, w.xbuf, hs);   // x_perm no longer needed
+  } else {
+    if (e == hipSuccess) e = gemm_dact(*s, *plan, pi, w.do_perm, w2, h_saved, w.dh, w.ga, w.ds_part, hs);
+    if (e == hipSuccess) e = launch_gather_rows(*s, x, plan->token_of_row, plan->offsets, w.xbuf, hs);
+    if (e == hipSuccess) e = gemm_dw1(*s, *plan, w.dh, w.xbuf, dw1, hs);
+    if (e == hipSuccess) e = gemm_dw2(*s, *plan, w.do_perm, w.ga, dw2, hs);
+    if (e == hipSuccess) e = gemm_dx_perm(*s, *plan, pi, w.dh, w1, w.xbuf, hs);   // x_perm no longer needed
+  }
   if (e == hipSuccess)
     e = launch_router_bwd(*s, *plan, w.ds_part, gemm_dact_parts(*s), ds, dz, w.dzq, ldz, hs);
   if (e == hipSuccess) e = gemm_router_dx(*s, *plan, w.dzq, ldz, w_gate, w.xbuf, dx, hs);

@@ -27,7 +27,7 @@
 
 namespace moe_gemm {
 
-__device__ __attribute__((aligned(16))) uint32_t g_dma_zero[4];
+static __device__ __attribute__((aligned(16))) uint32_t g_dma_zero[4];   // source of masked DMA lanes
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;

@@ -1,0 +1,119 @@
+// Launchers of the MXFP8 expert GEMMs (the three splits of the Olmo-core 3
+// article, "three splits" section, with their operands in MXFP8).
+//
+// Every operand is quantised along the reduction axis of its GEMM (mx.hip):
+//   forward   H  = X_perm W1_e^T   : X_perm rows along d,   W1_e rows along d
+//             Y  = A W2_e^T        : A rows along f,        W2_e rows along f
+//   backward  dA'= dO_perm W2_e    : dO_perm rows along d,  W2_e columns along d
+//             dX_perm = dH W1_e    : dH rows along 2f,      W1_e columns along 2f
+//             dW1_e = dH^T X_perm  : both along the expert's tokens
+//             dW2_e = dO^T gA      : both along the expert's tokens
+// The epilogues (SwiGLU, its backward with dS, plain stores) are the bf16 ones.
+#include "gemm_mx.h"
+#include "moe_internal.h"
+
+namespace moe {
+using namespace moe_gemm;
+
+namespace {
+
+template <int GROUP, int EPI, int S = 3>
+hipError_t run_mx(const Args& a, const MxArgs& m, int64_t logical_tiles, hipStream_t st) {
+  auto kern = grouped_gemm_mx<128, 256, 2, 4, GROUP, EPI, S>;
+  constexpr size_t lds = mx_lds_bytes<128, 256, 2, 4, S>();
+  if (lds > 65536) {
+    hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  const int64_t grid = 8 * ((logical_tiles + 7) / 8);
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(512), lds, st, a, m);
+  return hipGetLastError();
+}
+
+Args base_args() {
+  Args a{};
+  a.ksplit = 1;
+  return a;
+}
+
+int64_t m_tiles(const moe_shape& s) { return (max_rows(s) + 127) / 128 + s.E; }
+
+}  // namespace
+
+hipError_t gemm_mx_up_swiglu(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const MxOperand& x,
+                             const MxOperand& w1, void* h, void* act, hipStream_t st) {
+  Args a = base_args();
+  a.A = x.codes; a.lda = s.d;
+  a.B = w1.codes; a.ldb = s.d; a.b_estride = (int64_t)2 * s.d_ff * s.d;
+  a.C = h; a.ldc = 2 * s.d_ff;
+  a.C2 = act; a.ldc2 = s.d_ff;
+  a.offsets = p.offsets;
+  a.N = 2 * s.d_ff; a.K = s.d; a.E = s.E; a.f = s.d_ff;
+  a.tile_prefix = pi.prefix128; a.tilesN = a.N / 256;
+  MxArgs m{x.scales, x.srows, x.pad, w1.scales, w1.srows, 2 * (int64_t)s.d_ff};
+  return run_mx<GROUP_M, EPI_SWIGLU>(a, m, m_tiles(s) * a.tilesN, st);
+}
+
+hipError_t gemm_mx_down(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const MxOperand& act,
+                        const MxOperand& w2, void* y, hipStream_t st) {
+  Args a = base_args();
+  a.A = act.codes; a.lda = s.d_ff;
+  a.B = w2.codes; a.ldb = s.d_ff; a.b_estride = (int64_t)s.d * s.d_ff;
+  a.C = y; a.ldc = s.d;
+  a.offsets = p.offsets;
+  a.N = s.d; a.K = s.d_ff; a.E = s.E; a.f = s.d_ff;
+  a.tile_prefix = pi.prefix128; a.tilesN = ceil_div(a.N, 256);
+  MxArgs m{act.scales, act.srows, act.pad, w2.scales, w2.srows, (int64_t)s.d};
+  return run_mx<GROUP_M, EPI_ACT>(a, m, m_tiles(s) * a.tilesN, st);
+}
+
+// w2t: W2 quantised along d, stored [E][f][d]
+hipError_t gemm_mx_dact(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const MxOperand& dout,
+                        const MxOperand& w2t, const void* h, void* dh, void* ga, float* ds_part, hipStream_t st) {
+  Args a = base_args();
+  a.A = dout.codes; a.lda = s.d;
+  a.B = w2t.codes; a.ldb = s.d; a.b_estride = (int64_t)s.d_ff * s.d;
+  a.C = dh; a.ldc = 2 * s.d_ff;
+  a.C2 = ga; a.ldc2 = s.d_ff;
+  a.C3 = ds_part; a.ldc3 = max_rows(s);
+  a.aux = h; a.ld_aux = 2 * s.d_ff;
+  a.row_gate = p.gate_of_row;
+  a.offsets = p.offsets;
+  a.N = s.d_ff; a.K = s.d; a.E = s.E; a.f = s.d_ff;
+  a.tile_prefix = pi.prefix128; a.tilesN = ceil_div(a.N, 256);
+  MxArgs m{dout.scales, dout.srows, dout.pad, w2t.scales, w2t.srows, (int64_t)s.d_ff};
+  return run_mx<GROUP_M, EPI_DSWIGLU>(a, m, m_tiles(s) * a.tilesN, st);
+}
+
+// w1t: W1 quantised along 2f, stored [E][d][2f]
+hipError_t gemm_mx_dx_perm(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const MxOperand& dh,
+                           const MxOperand& w1t, void* dx_perm, hipStream_t st) {
+  Args a = base_args();
+  a.A = dh.codes; a.lda = 2 * s.d_ff;
+  a.B = w1t.codes; a.ldb = 2 * s.d_ff; a.b_estride = (int64_t)s.d * 2 * s.d_ff;
+  a.C = dx_perm; a.ldc = s.d;
+  a.offsets = p.offsets;
+  a.N = s.d; a.K = 2 * s.d_ff; a.E = s.E; a.f = s.d_ff;
+  a.tile_prefix = pi.prefix128; a.tilesN = ceil_div(a.N, 256);
+  MxArgs m{dh.scales, dh.srows, dh.pad, w1t.scales, w1t.srows, (int64_t)s.d};
+  return run_mx<GROUP_M, EPI_ACT>(a, m, m_tiles(s) * a.tilesN, st);
+}
+
+// dW_e [M, N] = sum over the expert's (64-padded) token positions of lhs x rhs;
+// lhs codes [M][P], rhs codes [N][P], both quantised along the token axis.
+hipError_t gemm_mx_wgrad(const moe_shape& s, const int32_t* pad_off, int64_t P, const MxOperand& lhs, int M,
+                         const MxOperand& rhs, int N, float* dw, hipStream_t st) {
+  Args a = base_args();
+  a.A = lhs.codes; a.lda = P;
+  a.B = rhs.codes; a.ldb = P;
+  a.C = dw; a.ldc = N; a.c_estride = (int64_t)M * N;
+  a.offsets = pad_off;
+  a.M = M; a.N = N; a.E = s.E;
+  a.tilesM = ceil_div(M, 128); a.tilesN = ceil_div(N, 256);
+  a.total_static = s.E * a.tilesM * a.tilesN;
+  MxArgs m{lhs.scales, lhs.srows, nullptr, rhs.scales, rhs.srows, 0};
+  return run_mx<GROUP_K, EPI_F32>(a, m, a.total_static, st);
+}
+
+}  // namespace moe

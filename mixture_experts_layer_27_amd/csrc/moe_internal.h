@@ -74,4 +74,38 @@ int gemm_router_dwg_splits(const moe_shape& s);
 hipError_t gemm_router_dwg(const moe_shape& s, const void* dzq, int ldz, const void* x, float* part,
                            hipStream_t st);
 
+// ---- MXFP8 (mx.hip, gemm_mx.hip)
+// A quantised GEMM operand: codes [rows][K] (E4M3 bytes, K-contiguous) and
+// stage-major scales [K/64][srows][2] (E8M0 bytes).
+// Row-quantised activations of the grouped-M GEMMs are stored expert-padded:
+// the segment of expert e starts at row pad[e] (a multiple of 64).
+struct MxOperand {
+  uint8_t* codes;
+  uint8_t* scales;
+  int64_t srows;
+  const int32_t* pad;   // expert-padded row layout, or nullptr
+};
+hipError_t launch_quantize_rows(const void* src, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
+                                hipStream_t st);
+hipError_t mx_quantize_rows_staged(const void* src, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales,
+                                   int64_t srows, hipStream_t st);
+// rows of a permuted activation [offsets[E], K] into the expert-padded layout
+hipError_t mx_quantize_rows_padded(const void* src, int64_t rows, int64_t K, const int32_t* offsets,
+                                   const int32_t* expert_of_row, const int32_t* pad_off, int E, uint8_t* codes,
+                                   uint8_t* scales, int64_t srows, hipStream_t st);
+hipError_t mx_quantize_cols(const void* src, int G, int R, int C, uint8_t* codes, uint8_t* scales, hipStream_t st);
+hipError_t mx_quantize_tokens(const void* src, int C, const int32_t* seg_off, const int32_t* pad_off, int E,
+                              int64_t P, uint8_t* codes, uint8_t* scales, hipStream_t st);
+hipError_t mx_pad_offsets(const int32_t* offsets, int E, int32_t* pad_off, hipStream_t st);
+hipError_t gemm_mx_up_swiglu(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const MxOperand& x,
+                             const MxOperand& w1, void* h, void* act, hipStream_t st);
+hipError_t gemm_mx_down(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const MxOperand& act,
+                        const MxOperand& w2, void* y, hipStream_t st);
+hipError_t gemm_mx_dact(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const MxOperand& dout,
+                        const MxOperand& w2t, const void* h, void* dh, void* ga, float* ds_part, hipStream_t st);
+hipError_t gemm_mx_dx_perm(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const MxOperand& dh,
+                           const MxOperand& w1t, void* dx_perm, hipStream_t st);
+hipError_t gemm_mx_wgrad(const moe_shape& s, const int32_t* pad_off, int64_t P, const MxOperand& lhs, int M,
+                         const MxOperand& rhs, int N, float* dw, hipStream_t st);
+
 }  // namespace moe

@@ -103,3 +103,22 @@ def quantize(v, axis=-1):
 def mx_roundtrip(v, axis=-1):
     """Dequantised MXFP8 values of ``v`` (blocks along ``axis``)."""
     return quantize(v, axis)[2]
+
+
+def block_exponent(amax):
+    """Shared exponent the amax rule picks for a block whose largest magnitude is ``amax``."""
+    if not amax > 0:
+        return -127
+    return int(np.clip(_floor_log2(np.float64(amax)) - EMAX_ELEM, -127, 127))
+
+
+def roundtrip_at(block, X):
+    """Dequantised values of ``block`` quantised with the shared exponent ``X``
+    given by the caller instead of the one the amax rule picks (elements still
+    rounded to nearest-even E4M3 and saturated at 448).  With X one above or
+    below the rule's choice this is the other outcome of a scale decision taken
+    on an amax that sits at a power of two."""
+    b = np.asarray(block, np.float64)
+    scale = np.ldexp(1.0, int(X))
+    mag = e4m3_round(np.abs(b) / scale)
+    return np.where(np.signbit(b), -mag, mag) * scale

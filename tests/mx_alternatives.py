@@ -1,0 +1,143 @@
+"""Both outcomes of MXFP8 quantisation decisions taken on values at a boundary.
+
+An MX operand is decided twice: the block's shared exponent floor(log2 amax) - 8,
+then each element's nearest-even E4M3 code.  When the operand is a value the
+layer computes (A from the saved H, dH, gA), the GPU's fp32 accumulation and the
+oracle's fp64 one can store it in bf16 one or two ulps apart; a decision whose
+input sits that close to its boundary (amax at a power of two, an element at the
+midpoint of two E4M3 values) then goes either way, and both outcomes are correct
+results of the MX contract.  They are visibly different: the amax element may
+saturate at 448 on one side only, and the E4M3 step is 1/8 of the value at the
+top of a binade.
+
+Each decision is therefore re-taken with its input moved by +-WINDOW (relative).
+Where the outcome changes, the changed dequantised values minus the oracle's
+give a delta that enters the GEMM output linearly.  The reference a GPU output
+vector is compared with is the oracle's vector plus those deltas that bring it
+closer to the GPU's (one pass: delta d is taken when 2 <r, d> > |d|^2 for the
+residual r = GPU - oracle).  Every delta is computed by the oracle from the
+oracle's own values; the GPU output only selects among them.  Inputs of the layer
+(x, dout, the weights) are never decided this way: both sides quantise the same
+bf16 values.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from oracle import mx
+
+BLOCK = 32
+# bf16 ulps are 2^-8..2^-7 of a value; computed values differ by at most about
+# two ulps between the two sides
+WINDOW = 2.0 ** -6
+
+
+def _exponents(amax):
+    return np.array([mx.block_exponent(a) for a in np.ravel(amax)], np.int64).reshape(np.shape(amax))
+
+
+def block_candidates(blk):
+    """Deltas (each the size of ``blk`` [b, M], blocks along axis 0 -- one block
+    per column) of every decision of the block that may go either way.  Returns a
+    list of (column j, delta vector of length b)."""
+    blk = np.asarray(blk, np.float64)
+    amax = np.abs(blk).max(axis=0)
+    X = _exponents(amax)
+    q = mx.mx_roundtrip(blk, axis=0)
+    out = []
+    for f in (1.0 + WINDOW, 1.0 - WINDOW):
+        Xa = _exponents(amax * f)
+        for j in np.nonzero((Xa != X) & (amax > 0))[0]:
+            out.append((int(j), mx.roundtrip_at(blk[:, j], Xa[j]) - q[:, j]))
+    scale = np.ldexp(1.0, X)[None, :]
+    s = np.abs(blk) / scale
+    base = mx.e4m3_round(s)
+    sign = np.where(np.signbit(blk), -1.0, 1.0)
+    for f in (1.0 + WINDOW, 1.0 - WINDOW):
+        alt = mx.e4m3_round(s * f)
+        ii, jj = np.nonzero(alt != base)
+        for i, j in zip(ii, jj):
+            d = np.zeros(blk.shape[0])
+            d[i] = sign[i, j] * (alt[i, j] - base[i, j]) * scale[0, j]
+            out.append((int(j), d))
+    return out
+
+
+def _select(got, ref, D):
+    """ref + the deltas (rows of D) that each bring ref closer to got."""
+    if len(D) == 0:
+        return ref
+    D = np.asarray(D)
+    r = got - ref
+    take = 2.0 * (D @ r) > np.einsum("ij,ij->i", D, D)
+    return ref + D[take].sum(axis=0)
+
+
+def operand_deltas(v, axis, other):
+    """{index along the non-block axis: [output deltas]} for the computed operand
+    ``v`` (2-D) quantised in blocks of 32 along ``axis`` (starting at 0), whose
+    quantised block (length b, rows sl of ``other``) multiplies ``other[sl, :]``."""
+    v = np.asarray(v, np.float64)
+    vt = v if axis == 0 else v.T
+    out = {}
+    for lo in range(0, vt.shape[0], BLOCK):
+        sl = slice(lo, min(lo + BLOCK, vt.shape[0]))
+        for j, d in block_candidates(vt[sl, :]):
+            out.setdefault(j, []).append(d @ other[sl, :])
+    return out
+
+
+# ---------------------------------------------------------------- per output
+
+
+def adjust_forward(plan, y_gpu, o_gpu, Y, O, A, w2_mx):
+    """Y rows = A rows (quantised along f) times W2_e^T (w2_mx(e): oracle MX round
+    trip of W2_e [d, f]); O sums the gated rows of each token."""
+    Yadj = np.array(Y, np.float64, copy=True)
+    for e in range(plan.E):
+        a, b = int(plan.offsets[e]), int(plan.offsets[e + 1])
+        if a == b:
+            continue
+        for r, dl in operand_deltas(A[a:b], 1, w2_mx(e).T).items():
+            Yadj[a + r] = _select(np.asarray(y_gpu[a + r], np.float64), Yadj[a + r], dl)
+    Oadj = np.array(O, np.float64, copy=True)
+    g = plan.gate_of_row
+    for t in range(plan.T):
+        for r in plan.tok_rows[plan.tok_ptr[t]:plan.tok_ptr[t + 1]]:
+            Oadj[t] += g[r] * (Yadj[r] - Y[r])
+    return Yadj, Oadj
+
+
+def adjust_dx(plan, dx_gpu, dx_ref, dH, w1_mx_k):
+    """dx_perm rows = dH rows (quantised along 2f) times W1_e (w1_mx_k(e): oracle
+    MX round trip of W1_e [2f, d] along 2f); dx sums the rows of each token."""
+    per_row = {}
+    for e in range(plan.E):
+        a, b = int(plan.offsets[e]), int(plan.offsets[e + 1])
+        if a == b:
+            continue
+        for r, dl in operand_deltas(dH[a:b], 1, w1_mx_k(e)).items():
+            per_row[a + r] = dl
+    adj = np.array(dx_ref, np.float64, copy=True)
+    for t in range(plan.T):
+        dl = []
+        for r in plan.tok_rows[plan.tok_ptr[t]:plan.tok_ptr[t + 1]]:
+            dl.extend(per_row.get(int(r), []))
+        adj[t] = _select(np.asarray(dx_gpu[t], np.float64), adj[t], dl)
+    return adj
+
+
+def adjust_wgrad(computed, other, got, ref, rows):
+    """Weight gradient of one expert, both operands quantised along its tokens.
+
+    dW1_e = dH_e^T X_e: computed = dH_e [n, 2f], other = X_e [n, d]; column c of
+    dH_e moves row c of dW1_e (rows=True).  dW2_e = dO_e^T gA_e: computed = gA_e
+    [n, f], other = dO_e [n, d]; column j of gA_e moves column j of dW2_e."""
+    oq = mx.mx_roundtrip(other, axis=0)
+    adj = np.array(ref, np.float64, copy=True)
+    for j, dl in operand_deltas(computed, 0, oq).items():
+        if rows:
+            adj[j] = _select(np.asarray(got[j], np.float64), adj[j], dl)
+        else:
+            adj[:, j] = _select(np.asarray(got[:, j], np.float64), adj[:, j], dl)
+    return adj

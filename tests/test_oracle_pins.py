@@ -427,6 +427,26 @@ def test_mx_special_cases():
     assert (np.abs(deq - v)[unclipped] <= np.abs(v)[unclipped] * 2.0 ** -4 + 2.0 ** -9 * blkmax[unclipped] / 256).all()
 
 
+def test_mx_forced_exponent():
+    # hand example: amax 3.984375 (just below 4) -> rule exponent -7, scaled 510,
+    # saturated to 448 -> 3.5; with the exponent one higher the value is
+    # 255 * 2^-6 -> nearest E4M3 is 256 -> 4.0
+    b = np.zeros(32); b[0] = 3.984375; b[1] = -1.0; b[2] = 0.3
+    assert mx.block_exponent(3.984375) == -7 and mx.block_exponent(4.0) == -6
+    assert mx.block_exponent(0.0) == -127
+    np.testing.assert_array_equal(mx.roundtrip_at(b, -7)[:2], [3.5, -1.0])
+    np.testing.assert_array_equal(mx.roundtrip_at(b, -6)[:2], [4.0, -1.0])
+    # 0.3 * 2^6 = 19.2 -> E4M3 step 2 in [16, 32) -> 20 -> 0.3125; at 2^7: 38.4 -> step 4 -> 40 -> 0.3125
+    assert mx.roundtrip_at(b, -6)[2] == 0.3125 and mx.roundtrip_at(b, -7)[2] == 0.3125
+    # at the rule's exponent it is the quantiser's round trip; scaling by 2 commutes
+    r = _rng(23)
+    for _ in range(20):
+        blk = r.standard_normal(32) * np.exp(r.uniform(-8, 8))
+        X = mx.block_exponent(np.abs(blk).max())
+        np.testing.assert_array_equal(mx.roundtrip_at(blk, X), mx.mx_roundtrip(blk))
+        np.testing.assert_array_equal(mx.roundtrip_at(2 * blk, X + 1), 2 * mx.roundtrip_at(blk, X))
+
+
 def _worst_rel(got, ref):
     """Largest relative Frobenius error over the rows and over the columns."""
     err = got - ref
