@@ -20,6 +20,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE layer tokens/s fwd+bwd at 1 GPU; grouped-GEMM % MFMA peak; permute GB/s"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 (MXFP8) MFMA
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
@@ -51,11 +52,11 @@ def cpu_baseline(cfg, g, tokens):
     threads = max([i.get("num_threads", 1) for i in info] or [1])
     t0 = time.perf_counter()
     mo.layer(x, wg, b, w1, w2, cfg.k, dout=dout, round_tile=cfg.round_tile,
-             prec=mo.CONTRACT if cfg.act == "bf16" else mo.TRUTH)
+             prec=mo.MX_CONTRACT if cfg.gemm == "mxfp8" else (mo.CONTRACT if cfg.act == "bf16" else mo.TRUTH))
     dt = time.perf_counter() - t0
     return {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"first {tokens} of {cfg.T} tokens of {cfg.name} (same weights), fwd+bwd, "
-                      f"float64 numpy, {dt:.1f} s"}
+                      f"float64 numpy{', MXFP8 operands' if cfg.gemm == 'mxfp8' else ''}, {dt:.1f} s"}
 
 
 def main():
@@ -115,7 +116,7 @@ def main():
     rows = int(counts.sum())
     esz = 2 if cfg.act == "bf16" else 4
     fwd_gemm_flops = 2.0 * rows * cfg.d * 2 * cfg.f + 2.0 * rows * cfg.f * cfg.d
-    peak = PEAK_BF16_TFLOPS if cfg.act == "bf16" else PEAK_F32_TFLOPS
+    peak = {"mxfp8": PEAK_FP8_TFLOPS, "bf16": PEAK_BF16_TFLOPS}.get(cfg.gemm, PEAK_F32_TFLOPS)
     achieved = fwd_gemm_flops / (ms["experts"] * 1e-3) / 1e12
     permute_bytes = cfg.T * cfg.d * esz + rows * cfg.d * esz + 4 * rows
     combine_bytes = rows * cfg.d * esz + cfg.T * cfg.d * esz + 8 * rows
@@ -131,7 +132,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if cfg.act == "bf16" else "f32",
+        "dtype": {"mxfp8": "mxfp8", "bf16": "bf16"}.get(cfg.gemm, "f32"),
         "data": "synthetic",
         "config": {"workload": f"{cfg.name}: T={cfg.T} d_model={cfg.d} E={cfg.E} top-k={cfg.k} "
                                f"d_ff={cfg.f} SwiGLU, {'fwd+bwd' if run.has_bwd else 'fwd'}"

@@ -106,10 +106,13 @@ def mx_roundtrip(v, axis=-1):
 
 
 def block_exponent(amax):
-    """Shared exponent the amax rule picks for a block whose largest magnitude is ``amax``."""
-    if not amax > 0:
-        return -127
-    return int(np.clip(_floor_log2(np.float64(amax)) - EMAX_ELEM, -127, 127))
+    """Shared exponent the amax rule picks for blocks whose largest magnitude is
+    ``amax`` (a scalar, or an array of them)."""
+    a = np.asarray(amax, np.float64)
+    X = np.full(a.shape, -127, np.int64)
+    pos = a > 0
+    X[pos] = np.clip(_floor_log2(a[pos]) - EMAX_ELEM, -127, 127)
+    return int(X) if X.ndim == 0 else X
 
 
 def roundtrip_at(block, X):

@@ -32,23 +32,22 @@ BLOCK = 32
 WINDOW = 2.0 ** -6
 
 
-def _exponents(amax):
-    return np.array([mx.block_exponent(a) for a in np.ravel(amax)], np.int64).reshape(np.shape(amax))
-
-
 def block_candidates(blk):
-    """Deltas (each the size of ``blk`` [b, M], blocks along axis 0 -- one block
-    per column) of every decision of the block that may go either way.  Returns a
-    list of (column j, delta vector of length b)."""
+    """Decisions of the blocks in ``blk`` [b, M] (one block per column, along
+    axis 0) that may go either way, as records (column j, i, delta): i = -1 for
+    the block exponent (delta: the block's value change, length b), else the
+    element at position i (delta: its value change, a scalar)."""
     blk = np.asarray(blk, np.float64)
     amax = np.abs(blk).max(axis=0)
-    X = _exponents(amax)
-    q = mx.mx_roundtrip(blk, axis=0)
+    X = mx.block_exponent(amax)
     out = []
+    q = None
     for f in (1.0 + WINDOW, 1.0 - WINDOW):
-        Xa = _exponents(amax * f)
+        Xa = mx.block_exponent(amax * f)
         for j in np.nonzero((Xa != X) & (amax > 0))[0]:
-            out.append((int(j), mx.roundtrip_at(blk[:, j], Xa[j]) - q[:, j]))
+            if q is None:
+                q = mx.mx_roundtrip(blk, axis=0)
+            out.append((int(j), -1, mx.roundtrip_at(blk[:, j], Xa[j]) - q[:, j]))
     scale = np.ldexp(1.0, X)[None, :]
     s = np.abs(blk) / scale
     base = mx.e4m3_round(s)
@@ -56,10 +55,8 @@ def block_candidates(blk):
     for f in (1.0 + WINDOW, 1.0 - WINDOW):
         alt = mx.e4m3_round(s * f)
         ii, jj = np.nonzero(alt != base)
-        for i, j in zip(ii, jj):
-            d = np.zeros(blk.shape[0])
-            d[i] = sign[i, j] * (alt[i, j] - base[i, j]) * scale[0, j]
-            out.append((int(j), d))
+        vals = sign[ii, jj] * (alt[ii, jj] - base[ii, jj]) * scale[0, jj]
+        out.extend(zip(jj.tolist(), ii.tolist(), vals.tolist()))
     return out
 
 
@@ -74,17 +71,24 @@ def _select(got, ref, D):
 
 
 def operand_deltas(v, axis, other):
-    """{index along the non-block axis: [output deltas]} for the computed operand
-    ``v`` (2-D) quantised in blocks of 32 along ``axis`` (starting at 0), whose
-    quantised block (length b, rows sl of ``other``) multiplies ``other[sl, :]``."""
+    """Yields (index j along the non-block axis, output deltas [m, width]) for the
+    computed operand ``v`` (2-D) quantised in blocks of 32 along ``axis`` (from
+    0): its block at positions sl multiplies ``other[sl, :]``."""
     v = np.asarray(v, np.float64)
     vt = v if axis == 0 else v.T
-    out = {}
+    by = {}
     for lo in range(0, vt.shape[0], BLOCK):
         sl = slice(lo, min(lo + BLOCK, vt.shape[0]))
-        for j, d in block_candidates(vt[sl, :]):
-            out.setdefault(j, []).append(d @ other[sl, :])
-    return out
+        for j, i, d in block_candidates(vt[sl, :]):
+            by.setdefault(j, []).append((lo, i, d))
+    for j, recs in by.items():
+        D = np.empty((len(recs), other.shape[1]))
+        for n, (lo, i, d) in enumerate(recs):
+            if i < 0:
+                D[n] = d @ other[lo:lo + len(d), :]
+            else:
+                D[n] = d * other[lo + i, :]
+        yield j, D
 
 
 # ---------------------------------------------------------------- per output
@@ -98,8 +102,8 @@ def adjust_forward(plan, y_gpu, o_gpu, Y, O, A, w2_mx):
         a, b = int(plan.offsets[e]), int(plan.offsets[e + 1])
         if a == b:
             continue
-        for r, dl in operand_deltas(A[a:b], 1, w2_mx(e).T).items():
-            Yadj[a + r] = _select(np.asarray(y_gpu[a + r], np.float64), Yadj[a + r], dl)
+        for r, D in operand_deltas(A[a:b], 1, w2_mx(e).T):
+            Yadj[a + r] = _select(np.asarray(y_gpu[a + r], np.float64), Yadj[a + r], D)
     Oadj = np.array(O, np.float64, copy=True)
     g = plan.gate_of_row
     for t in range(plan.T):
@@ -116,14 +120,13 @@ def adjust_dx(plan, dx_gpu, dx_ref, dH, w1_mx_k):
         a, b = int(plan.offsets[e]), int(plan.offsets[e + 1])
         if a == b:
             continue
-        for r, dl in operand_deltas(dH[a:b], 1, w1_mx_k(e)).items():
-            per_row[a + r] = dl
+        for r, D in operand_deltas(dH[a:b], 1, w1_mx_k(e)):
+            per_row[a + r] = D
     adj = np.array(dx_ref, np.float64, copy=True)
     for t in range(plan.T):
-        dl = []
-        for r in plan.tok_rows[plan.tok_ptr[t]:plan.tok_ptr[t + 1]]:
-            dl.extend(per_row.get(int(r), []))
-        adj[t] = _select(np.asarray(dx_gpu[t], np.float64), adj[t], dl)
+        D = [per_row[int(r)] for r in plan.tok_rows[plan.tok_ptr[t]:plan.tok_ptr[t + 1]] if int(r) in per_row]
+        if D:
+            adj[t] = _select(np.asarray(dx_gpu[t], np.float64), adj[t], np.concatenate(D))
     return adj
 
 
@@ -135,9 +138,9 @@ def adjust_wgrad(computed, other, got, ref, rows):
     [n, f], other = dO_e [n, d]; column j of gA_e moves column j of dW2_e."""
     oq = mx.mx_roundtrip(other, axis=0)
     adj = np.array(ref, np.float64, copy=True)
-    for j, dl in operand_deltas(computed, 0, oq).items():
+    for j, D in operand_deltas(computed, 0, oq):
         if rows:
-            adj[j] = _select(np.asarray(got[j], np.float64), adj[j], dl)
+            adj[j] = _select(np.asarray(got[j], np.float64), adj[j], D)
         else:
-            adj[:, j] = _select(np.asarray(got[:, j], np.float64), adj[:, j], dl)
+            adj[:, j] = _select(np.asarray(got[:, j], np.float64), adj[:, j], D)
     return adj

@@ -5,18 +5,23 @@ routing integer (top-k, counts, offsets, all plan maps, token rounding) is
 compared bit for bit over all tokens; outputs and gradients are compared on a
 seeded sample of tokens (all of their rows) and on every element of the
 weight gradients of a sample of experts, each computed by the oracle one by
-one; dW_g is checked through the identity dW_g = bf16(dlogits)^T X on all tokens."""
+one; dW_g is checked through the identity dW_g = bf16(dlogits)^T X on all tokens.
+With MXFP8 expert GEMMs the references of Y, O, dx and dW take the other outcome
+of quantisation decisions that sit on a boundary where the GPU's does
+(mx_alternatives)."""
 import numpy as np
 import pytest
 import torch
 
-from helpers import LazyExperts, assert_close, make_inputs, precision
+import mx_alternatives as mxa
+from helpers import LazyExperts, assert_close, make_inputs, precision, tol
 from mixture_experts_layer_27_amd import configs
 from oracle import moe_oracle as mo
+from oracle import mx
 
 pytestmark = pytest.mark.gpu
 
-FULL = ["fine_e128", "sparse_e256_round", "coarse_e8", "fine_e128_zipf"]
+FULL = ["fine_e128", "sparse_e256_round", "coarse_e8", "fine_e128_zipf", "fine_e128_mxfp8"]
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -47,30 +52,51 @@ def test_full_size_sampled(name):
     prec = precision(cfg)
     W1, W2 = LazyExperts(g["w1"]), LazyExperts(g["w2"])
     rng = np.random.default_rng(2024)
-    toks = np.sort(rng.choice(cfg.T, 32, replace=False))
+    is_mx = cfg.gemm == "mxfp8"
+    # fewer samples with MXFP8: the oracle re-quantises every touched expert's weights
+    toks = np.sort(rng.choice(cfg.T, 8 if is_mx else 32, replace=False))
     sub = mo.sub_plan(plan, tokens=toks)
     print(f"[fullsize] {name}: oracle on {len(toks)} tokens ({sub.N} rows)", flush=True)
     fw = mo.forward(x, W1, W2, sub, prec)
     row_of = {(int(t), int(e)): r for r, (t, e) in enumerate(zip(plan.token_of_row, plan.expert_of_row))}
     rows = np.array([row_of[(int(t), int(e))] for t, e in zip(sub.token_of_row, sub.expert_of_row)])
-    assert_close("O", run.out[toks].double().cpu().numpy(), fw["O"][toks])
-    assert_close("H", run.h[rows].double().cpu().numpy(), fw["H"])
+    t = tol(cfg)
+    mx_w = lambda w, axis: (lambda e: mx.mx_roundtrip(w[e], axis=axis))
+    o_gpu = run.out.double().cpu().numpy()
+    O = fw["O"]
+    if is_mx:
+        y_sub = run.y[rows].double().cpu().numpy()
+        Y, O = mxa.adjust_forward(sub, y_sub, None, fw["Y"], O, fw["A"], mx_w(W2, 1))
+        assert_close("Y", y_sub, Y, *t)
+    assert_close("O", o_gpu[toks], O[toks], *t)
+    assert_close("H", run.h[rows].double().cpu().numpy(), fw["H"], *t)
     if not run.has_bwd:
         return
     dout = f64(g["dout"])
     bw = mo.backward(x, wg, W1, W2, sub, fw["H"], dout, prec, weight_grads=False)
-    assert_close("dS", run.ds[rows].double().cpu().numpy(), bw["dS"])
-    assert_close("dlogits", run.dlogits[toks].double().cpu().numpy(), bw["dlogits"][toks])
-    assert_close("dx", run.dx[toks].double().cpu().numpy(), bw["dx"][toks])
-    # every element of the weight gradients of two experts (the busiest and a random one)
-    experts = [int(np.argmax(plan.counts)), int(rng.integers(cfg.E))]
+    dx_gpu = run.dx.double().cpu().numpy()
+    dx_ref = bw["dx"]
+    if is_mx:
+        dx_ref = mxa.adjust_dx(sub, dx_gpu, dx_ref, bw["dH"], mx_w(W1, 0))
+    assert_close("dS", run.ds[rows].double().cpu().numpy(), bw["dS"], *t)
+    assert_close("dlogits", run.dlogits[toks].double().cpu().numpy(), bw["dlogits"][toks], *t)
+    assert_close("dx", dx_gpu[toks], dx_ref[toks], *t)
+    # every element of the weight gradients of the busiest expert and (bf16) a random one
+    experts = [int(np.argmax(plan.counts))] + ([] if is_mx else [int(rng.integers(cfg.E))])
     for e in experts:
         sub_e = mo.sub_plan(plan, experts=[e])
         print(f"[fullsize] {name}: oracle weight gradients of expert {e} ({sub_e.N} rows)", flush=True)
         fw_e = mo.forward(x, W1, W2, sub_e, prec)
         bw_e = mo.backward(x, wg, W1, W2, sub_e, fw_e["H"], dout, prec, weight_grads=[e])
-        assert_close(f"dw1[{e}]", run.dw1[e].double().cpu().numpy(), bw_e["dw1"][e])
-        assert_close(f"dw2[{e}]", run.dw2[e].double().cpu().numpy(), bw_e["dw2"][e])
+        dw1 = run.dw1[e].double().cpu().numpy()
+        dw2 = run.dw2[e].double().cpu().numpy()
+        ref1, ref2 = bw_e["dw1"][e], bw_e["dw2"][e]
+        if is_mx:
+            a, b = int(sub_e.offsets[e]), int(sub_e.offsets[e + 1])
+            ref1 = mxa.adjust_wgrad(bw_e["dH"][a:b], fw_e["x_perm"][a:b], dw1, ref1, rows=True)
+            ref2 = mxa.adjust_wgrad(bw_e["gA"][a:b], dout[sub_e.token_of_row[a:b]], dw2, ref2, rows=False)
+        assert_close(f"dw1[{e}]", dw1, ref1, *t)
+        assert_close(f"dw2[{e}]", dw2, ref2, *t)
     # dW_g = bf16(dlogits)^T X over all tokens (the router-weight GEMM on the GPU's own dz)
     dzq = run.dlogits.cpu().to(torch.bfloat16).double().numpy() if cfg.act == "bf16" else f64(run.dlogits.cpu())
     assert_close("dw_gate", run.dw_gate.double().cpu().numpy(), dzq.T @ x)

@@ -445,6 +445,12 @@ def test_mx_forced_exponent():
         X = mx.block_exponent(np.abs(blk).max())
         np.testing.assert_array_equal(mx.roundtrip_at(blk, X), mx.mx_roundtrip(blk))
         np.testing.assert_array_equal(mx.roundtrip_at(2 * blk, X + 1), 2 * mx.roundtrip_at(blk, X))
+    # array form: the exponents behind the quantiser's scale bytes
+    v = r.standard_normal((40, 96)) * np.exp(r.uniform(-40, 40, (40, 1)))
+    v[3, :32] = 0.0
+    _, sc, _ = mx.quantize(v, axis=1)
+    amax = np.abs(v.reshape(40, 3, 32)).max(-1)
+    np.testing.assert_array_equal(mx.block_exponent(amax) + 127, sc.astype(np.int64))
 
 
 def _worst_rel(got, ref):
