@@ -97,7 +97,7 @@ typedef struct moe_plan {
   int32_t *tok_ptr;      /* [T+1]  CSR token -> rows                                 */
   int32_t *tok_rows;     /* [N_max] rows of each token, ascending                    */
   uint32_t *keep_bits;   /* [T, ceil(E/32)] bit (t,e) set when token t has a row at e */
-  int32_t *sched;        /* internal: per-expert tile prefixes for the grouped GEMMs  */
+  int32_t *sched;        /* internal: per-expert tile prefixes and the tile-to-expert map of the grouped GEMMs */
 } moe_plan;
 
 /* Sizes.  All are pure host arithmetic. */

@@ -52,7 +52,8 @@ void carve_plan(const moe_shape& s, char* base, moe_plan* p, size_t* total) {
   q.tok_rows = c.take<int32_t>(N * 4);
   q.keep_bits = c.take<uint32_t>(T * words_of(s) * 4);
   // internal region
-  q.sched = c.take<int32_t>(2 * (E + 1) * 4);
+  q.sched = c.take<int32_t>((E + 1) * 4);
+  c.take<int32_t>(max_mtiles128(s) * 4);
   c.take<int32_t>(E * nblk_of(s) * 4);
   c.take<int32_t>((nblk_of(s) + 1) * 4);
   if (s.round_tile) c.take<uint32_t>(E * ((T + 31) / 32) * 4);
@@ -176,8 +177,9 @@ PlanInternal plan_internal(const moe_shape& s, const moe_plan& p) {
   pi.words = words_of(s);
   char* b = reinterpret_cast<char*>(p.sched);
   pi.prefix128 = reinterpret_cast<int32_t*>(b);
-  pi.prefix256 = pi.prefix128 + (s.E + 1);
-  b += al(2 * (size_t)(s.E + 1) * 4);
+  b += al((size_t)(s.E + 1) * 4);
+  pi.tile_e128 = reinterpret_cast<int32_t*>(b);
+  b += al((size_t)max_mtiles128(s) * 4);
   pi.hist = reinterpret_cast<int32_t*>(b);
   b += al((size_t)s.E * pi.nblk * 4);
   pi.blk_tok = reinterpret_cast<int32_t*>(b);

@@ -69,10 +69,10 @@ hipError_t gemm_up_swiglu(const moe_shape& s, const moe_plan& p, const PlanInter
   a.offsets = p.offsets;
   a.N = 2 * s.d_ff; a.K = s.d; a.E = s.E; a.f = s.d_ff;
   if (s.act == MOE_BF16) {
-    a.tile_prefix = pi.prefix128; a.tilesN = a.N / 256;
+    a.tile_prefix = pi.prefix128; a.tile_expert = pi.tile_e128; a.tilesN = a.N / 256;
     return run_dma<128, 256, 2, 4, true, true, GROUP_M, EPI_SWIGLU, 3>(a, grouped_m_tiles(s, 128) * a.tilesN, st);
   }
-  a.tile_prefix = pi.prefix128; a.tilesN = a.N / 128;
+  a.tile_prefix = pi.prefix128; a.tile_expert = pi.tile_e128; a.tilesN = a.N / 128;
   return run<float, 128, 128, 2, 2, true, true, GROUP_M, EPI_SWIGLU>(a, grouped_m_tiles(s, 128) * a.tilesN, st);
 }
 
@@ -85,10 +85,10 @@ hipError_t gemm_down(const moe_shape& s, const moe_plan& p, const PlanInternal& 
   a.offsets = p.offsets;
   a.N = s.d; a.K = s.d_ff; a.E = s.E; a.f = s.d_ff;
   if (s.act == MOE_BF16) {
-    a.tile_prefix = pi.prefix128; a.tilesN = ceil_div(a.N, 256);
+    a.tile_prefix = pi.prefix128; a.tile_expert = pi.tile_e128; a.tilesN = ceil_div(a.N, 256);
     return run_dma<128, 256, 2, 4, true, true, GROUP_M, EPI_ACT, 3>(a, grouped_m_tiles(s, 128) * a.tilesN, st);
   }
-  a.tile_prefix = pi.prefix128; a.tilesN = ceil_div(a.N, 128);
+  a.tile_prefix = pi.prefix128; a.tile_expert = pi.tile_e128; a.tilesN = ceil_div(a.N, 128);
   return run<float, 128, 128, 2, 2, true, true, GROUP_M, EPI_ACT>(a, grouped_m_tiles(s, 128) * a.tilesN, st);
 }
 
@@ -111,10 +111,10 @@ hipError_t gemm_dact(const moe_shape& s, const moe_plan& p, const PlanInternal& 
   a.offsets = p.offsets;
   a.N = s.d_ff; a.K = s.d; a.E = s.E; a.f = s.d_ff;
   if (s.act == MOE_BF16) {
-    a.tile_prefix = pi.prefix128; a.tilesN = ceil_div(a.N, 256);
+    a.tile_prefix = pi.prefix128; a.tile_expert = pi.tile_e128; a.tilesN = ceil_div(a.N, 256);
     return run_dma<128, 256, 2, 4, true, false, GROUP_M, EPI_DSWIGLU, 3>(a, grouped_m_tiles(s, 128) * a.tilesN, st);
   }
-  a.tile_prefix = pi.prefix128; a.tilesN = ceil_div(a.N, 128);
+  a.tile_prefix = pi.prefix128; a.tile_expert = pi.tile_e128; a.tilesN = ceil_div(a.N, 128);
   return run<float, 128, 128, 2, 2, true, false, GROUP_M, EPI_DSWIGLU>(a, grouped_m_tiles(s, 128) * a.tilesN, st);
 }
 
@@ -127,10 +127,10 @@ hipError_t gemm_dx_perm(const moe_shape& s, const moe_plan& p, const PlanInterna
   a.offsets = p.offsets;
   a.N = s.d; a.K = 2 * s.d_ff; a.E = s.E; a.f = s.d_ff;
   if (s.act == MOE_BF16) {
-    a.tile_prefix = pi.prefix128; a.tilesN = ceil_div(a.N, 256);
+    a.tile_prefix = pi.prefix128; a.tile_expert = pi.tile_e128; a.tilesN = ceil_div(a.N, 256);
     return run_dma<128, 256, 2, 4, true, false, GROUP_M, EPI_ACT, 3>(a, grouped_m_tiles(s, 128) * a.tilesN, st);
   }
-  a.tile_prefix = pi.prefix128; a.tilesN = ceil_div(a.N, 128);
+  a.tile_prefix = pi.prefix128; a.tile_expert = pi.tile_e128; a.tilesN = ceil_div(a.N, 128);
   return run<float, 128, 128, 2, 2, true, false, GROUP_M, EPI_ACT>(a, grouped_m_tiles(s, 128) * a.tilesN, st);
 }
 

@@ -42,6 +42,7 @@ struct Args {
   const float* bias;
   const int32_t* offsets;       // [E+1] segment offsets (GROUP_M rows, GROUP_K reduction rows)
   const int32_t* tile_prefix;   // [E+1] prefix of per-expert m-tile counts (GROUP_M)
+  const int32_t* tile_expert;   // [prefix[E]] expert of each m-tile (GROUP_M)
   const int32_t* csr_ptr; const int32_t* csr_rows; const void* gsrc; int64_t ld_gsrc;
   int M, N, K, E, f;
   int tilesM, tilesN;
@@ -248,12 +249,9 @@ MOE_DEV bool decode_tile(const Args& args, TileCtx& c) {
   int row_begin = 0, row_end = 0;
   int k_begin = 0, k_end = args.K;
   if constexpr (GROUP == GROUP_M) {
-    int lo = 0, hi = args.E;          // find e: prefix[e]*tilesN <= L < prefix[e+1]*tilesN
-    while (hi - lo > 1) {
-      int mid = (lo + hi) >> 1;
-      if (args.tile_prefix[mid] * args.tilesN <= L) lo = mid; else hi = mid;
-    }
-    e = lo;
+    // expert e holds logical tiles [prefix[e]*tilesN, prefix[e+1]*tilesN), so
+    // L / tilesN is one of its m-tile indices
+    e = args.tile_expert[L / args.tilesN];
     int p0 = args.tile_prefix[e], cnt = args.tile_prefix[e + 1] - p0;
     int r = L - p0 * args.tilesN;
     // m-tiles of the expert in groups of kGroupM; inside a group the n-tile is

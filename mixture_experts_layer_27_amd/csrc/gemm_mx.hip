@@ -50,7 +50,7 @@ hipError_t gemm_mx_up_swiglu(const moe_shape& s, const moe_plan& p, const PlanIn
   a.C2 = act; a.ldc2 = s.d_ff;
   a.offsets = p.offsets;
   a.N = 2 * s.d_ff; a.K = s.d; a.E = s.E; a.f = s.d_ff;
-  a.tile_prefix = pi.prefix128; a.tilesN = a.N / 256;
+  a.tile_prefix = pi.prefix128; a.tile_expert = pi.tile_e128; a.tilesN = a.N / 256;
   MxArgs m{x.scales, x.srows, x.pad, w1.scales, w1.srows, 2 * (int64_t)s.d_ff};
   return run_mx<GROUP_M, EPI_SWIGLU>(a, m, m_tiles(s) * a.tilesN, st);
 }
@@ -63,7 +63,7 @@ hipError_t gemm_mx_down(const moe_shape& s, const moe_plan& p, const PlanInterna
   a.C = y; a.ldc = s.d;
   a.offsets = p.offsets;
   a.N = s.d; a.K = s.d_ff; a.E = s.E; a.f = s.d_ff;
-  a.tile_prefix = pi.prefix128; a.tilesN = ceil_div(a.N, 256);
+  a.tile_prefix = pi.prefix128; a.tile_expert = pi.tile_e128; a.tilesN = ceil_div(a.N, 256);
   MxArgs m{act.scales, act.srows, act.pad, w2.scales, w2.srows, (int64_t)s.d};
   return run_mx<GROUP_M, EPI_ACT>(a, m, m_tiles(s) * a.tilesN, st);
 }
@@ -81,7 +81,7 @@ hipError_t gemm_mx_dact(const moe_shape& s, const moe_plan& p, const PlanInterna
   a.row_gate = p.gate_of_row;
   a.offsets = p.offsets;
   a.N = s.d_ff; a.K = s.d; a.E = s.E; a.f = s.d_ff;
-  a.tile_prefix = pi.prefix128; a.tilesN = ceil_div(a.N, 256);
+  a.tile_prefix = pi.prefix128; a.tile_expert = pi.tile_e128; a.tilesN = ceil_div(a.N, 256);
   MxArgs m{dout.scales, dout.srows, dout.pad, w2t.scales, w2t.srows, (int64_t)s.d_ff};
   return run_mx<GROUP_M, EPI_DSWIGLU>(a, m, m_tiles(s) * a.tilesN, st);
 }
@@ -95,7 +95,7 @@ hipError_t gemm_mx_dx_perm(const moe_shape& s, const moe_plan& p, const PlanInte
   a.C = dx_perm; a.ldc = s.d;
   a.offsets = p.offsets;
   a.N = s.d; a.K = 2 * s.d_ff; a.E = s.E; a.f = s.d_ff;
-  a.tile_prefix = pi.prefix128; a.tilesN = ceil_div(a.N, 256);
+  a.tile_prefix = pi.prefix128; a.tile_expert = pi.tile_e128; a.tilesN = ceil_div(a.N, 256);
   MxArgs m{dh.scales, dh.srows, dh.pad, w1t.scales, w1t.srows, (int64_t)s.d};
   return run_mx<GROUP_M, EPI_ACT>(a, m, m_tiles(s) * a.tilesN, st);
 }

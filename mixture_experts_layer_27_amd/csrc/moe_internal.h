@@ -13,13 +13,13 @@ constexpr int kBmLarge = 256;       // m-tile of the bf16 grouped GEMMs
 
 // Internal region of the plan blob (plan.sched points at its start):
 //   [0, E+1)            m-tile prefix for BM = 128
-//   [E+1, 2E+2)         m-tile prefix for BM = 256
+//   tile_e [max_rows/128 + E]  expert of each 128-row m-tile
 //   hist [E * nblk]     per-(expert, token block) counts, then bases after the scan
 //   blk_tok [nblk + 1]  rows per token block, then its exclusive scan
 //   sel_t [E * ceil(T/32)] (rounding only) bit t of row e: token t selected expert e
 struct PlanInternal {
   int32_t* prefix128;
-  int32_t* prefix256;
+  int32_t* tile_e128;
   int32_t* hist;
   int32_t* blk_tok;
   uint32_t* sel_t;
@@ -28,6 +28,7 @@ struct PlanInternal {
 };
 PlanInternal plan_internal(const moe_shape& s, const moe_plan& p);
 int64_t max_rows(const moe_shape& s);
+inline int64_t max_mtiles128(const moe_shape& s) { return (max_rows(s) + 127) / 128 + s.E; }
 inline int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
 // ---- routing (route.hip)

@@ -202,7 +202,7 @@ MOE_DEV int block_scan_inplace(int32_t* a, int64_t n, int* sh) {
 __global__ __launch_bounds__(1024) void plan_scan_kernel(int E, int nblk, int32_t* __restrict__ hist,
                                                         int32_t* __restrict__ blk_tok, int32_t* __restrict__ counts,
                                                         int32_t* __restrict__ counts_raw, int32_t* __restrict__ offsets,
-                                                        int32_t* __restrict__ pre128, int32_t* __restrict__ pre256) {
+                                                        int32_t* __restrict__ pre128, int32_t* __restrict__ tile_e) {
   __shared__ int sh[1024];
   const int total = block_scan_inplace(hist, (int64_t)E * nblk, sh);
   const int toks = block_scan_inplace(blk_tok, nblk, sh);
@@ -217,17 +217,16 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(int E, int nblk, int32_
   if (threadIdx.x == 0) offsets[E] = total;
   __syncthreads();
   if (threadIdx.x == 0) {
-    int a = 0, b = 0;
+    int a = 0;
     for (int e = 0; e < E; ++e) {
       pre128[e] = a;
-      pre256[e] = b;
-      int c = counts[e];
-      a += (c + 127) / 128;
-      b += (c + 255) / 256;
+      a += (counts[e] + 127) / 128;
     }
     pre128[E] = a;
-    pre256[E] = b;
   }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += 1024)
+    for (int j = pre128[e]; j < pre128[e + 1]; ++j) tile_e[j] = e;
 }
 
 __global__ __launch_bounds__(256) void plan_scatter_kernel(
@@ -416,7 +415,7 @@ hipError_t launch_plan_build(const moe_shape& s, const moe_plan& p, const PlanIn
   hipLaunchKernelGGL(plan_count_kernel, dim3(pi.nblk), dim3(256), lds, st, p.keep_bits, s.T, s.E, pi.words,
                      pi.nblk, pi.hist, pi.blk_tok);
   hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, st, s.E, pi.nblk, pi.hist, pi.blk_tok, p.counts,
-                     raw ? p.counts_raw : nullptr, p.offsets, pi.prefix128, pi.prefix256);
+                     raw ? p.counts_raw : nullptr, p.offsets, pi.prefix128, pi.tile_e128);
   hipLaunchKernelGGL(plan_scatter_kernel, dim3(pi.nblk), dim3(256), lds, st, p.keep_bits, s.T, s.E, s.k,
                      pi.words, pi.nblk, pi.hist, pi.blk_tok, p.topk_idx, p.topk_gate, p.probs_t,
                      with_prob_gates, p.token_of_row, p.expert_of_row, p.gate_of_row, p.row_of_slot, p.tok_ptr,
