@@ -60,6 +60,14 @@ MOE_DEV void wait_vm_lgkm0() {
 
 MOE_DEV int kc_h(int row) { return (((row >> 1) ^ (row >> 3)) & 1) | (((row >> 2) & 1) << 1); }
 MOE_DEV int kc_off(int row, int chunk) { return row * 64 + ((chunk ^ kc_h(row)) << 4); }
+// 128-byte rows (BK = 64): chunk c of row r at slot c ^ ((r >> 1) & 7); rows r..r+15
+// of one chunk land in 16 different 16 B bank groups
+MOE_DEV int kc8_h(int row) { return (row >> 1) & 7; }
+template <int BK>
+MOE_DEV int kc_offk(int row, int chunk) {
+  if constexpr (BK == 32) return kc_off(row, chunk);
+  else return row * 128 + ((chunk ^ kc8_h(row)) << 4);
+}
 MOE_DEV int mn_x(int k) { return (k & 3) << 1; }
 template <int ROWS>
 MOE_DEV int mn_off(int k, int byte) {
@@ -67,11 +75,14 @@ MOE_DEV int mn_off(int k, int byte) {
   return k * (ROWS * 2) + ((((byte >> 5) ^ mn_x(k)) << 5) | (byte & 31));
 }
 
-// DMA sources of one operand tile (ROWS rows x 32 k) for the lanes of this wave.
-template <int ROWS, int NW, bool KC>
+// DMA sources of one operand tile (ROWS rows x BK k) for the lanes of this wave.
+template <int ROWS, int NW, bool KC, int BK = 32>
 struct DmaOperand {
-  static constexpr int Q = ROWS / 16 / NW;   // 1 KiB instructions per wave per stage
-  static_assert(Q >= 1 && (ROWS / 16) % NW == 0, "tile rows must split over the waves");
+  static_assert(BK == 32 || BK == 64, "stage depth");
+  static constexpr int RPI = 1024 / (BK * 2);   // KC: tile rows per 1 KiB instruction
+  static constexpr int LPR = BK * 2 / 16;       // KC: lanes per tile row
+  static constexpr int Q = ROWS * BK * 2 / 1024 / NW;   // 1 KiB instructions per wave per stage
+  static_assert(Q >= 1 && (ROWS * BK * 2 / 1024) % NW == 0, "tile rows must split over the waves");
   const bf16_t* src[Q];   // KC: element pointer of (row, chunk) at k = 0; MN: unused
   int kl[Q], mn[Q];       // MN: local k row and column of the lane's 16 bytes
   int q0;
@@ -81,8 +92,8 @@ struct DmaOperand {
     q0 = wave * Q;
 #pragma unroll
     for (int u = 0; u < Q; ++u) {
-      const int row = (q0 + u) * 16 + (lane >> 2);
-      const int c = (lane & 3) ^ kc_h(row);
+      const int row = (q0 + u) * RPI + lane / LPR;
+      const int c = (lane % LPR) ^ (BK == 32 ? kc_h(row) : kc8_h(row));
       src[u] = rowfn(row) + c * 8;
     }
   }
@@ -234,15 +245,14 @@ MOE_DEV void wave_epilogue(const Args& args, const TileCtx& ctx, f32x16 (&acc)[B
   }
 }
 
-template <int BM, int BN, int WM, int WN, bool AKC, bool BKC, int GROUP, int EPI, int S>
+template <int BM, int BN, int WM, int WN, bool AKC, bool BKC, int GROUP, int EPI, int S, int BK = 32>
 __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma(Args args) {
   using T = bf16_t;
   constexpr int NW = WM * WN;
-  constexpr int BK = 32;
   static_assert(S >= 2 && S <= 5, "ring depth");
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
-  constexpr int ASZ = BM * 64, BSZ = BN * 64, STAGE = ASZ + BSZ;
+  constexpr int ASZ = BM * BK * 2, BSZ = BN * BK * 2, STAGE = ASZ + BSZ;
   static_assert(TM >= 1 && TN >= 1, "wave tile must hold a 32x32 MFMA tile");
   static_assert(GROUP != GROUP_NONE, "router GEMMs use the register-staged kernel");
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -258,8 +268,8 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma(Args args) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / WN, wn = wave % WN;
 
-  DmaOperand<BM, NW, AKC> da;
-  DmaOperand<BN, NW, BKC> db;
+  DmaOperand<BM, NW, AKC, BK> da;
+  DmaOperand<BN, NW, BKC, BK> db;
   if constexpr (AKC) {
     da.init_kc([&](int row) -> const T* {
       int g = row_begin + row;
@@ -304,7 +314,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma(Args args) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
-  constexpr int LPS = DmaOperand<BM, NW, AKC>::Q + DmaOperand<BN, NW, BKC>::Q;   // loads per stage
+  constexpr int LPS = DmaOperand<BM, NW, AKC, BK>::Q + DmaOperand<BN, NW, BKC, BK>::Q;   // loads per stage
   const int nk = (k_end > k_begin) ? (k_end - k_begin + BK - 1) / BK : 0;
 #pragma unroll
   for (int s = 0; s < S - 1; ++s)
@@ -321,12 +331,12 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma(Args args) {
     const char* as = smem + (kt % S) * STAGE;
     const char* bs = as + ASZ;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int ks = 0; ks < BK / 16; ++ks) {
       u32x4 af[TM], bfr[TN];
       if constexpr (AKC) {
 #pragma unroll
         for (int i = 0; i < TM; ++i)
-          af[i] = *reinterpret_cast<const u32x4*>(as + kc_off(wm * WTM + i * 32 + (lane & 31), ks * 2 + (lane >> 5)));
+          af[i] = *reinterpret_cast<const u32x4*>(as + kc_offk<BK>(wm * WTM + i * 32 + (lane & 31), ks * 2 + (lane >> 5)));
       } else {
         const int kb = ks * 16 + (lane >> 5) * 8 + ((lane & 15) >> 2);
         const int cb = (((lane >> 4) & 1) * 16 + 4 * (lane & 3)) * 2;
@@ -339,7 +349,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma(Args args) {
       if constexpr (BKC) {
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-          bfr[j] = *reinterpret_cast<const u32x4*>(bs + kc_off(wn * WTN + j * 32 + (lane & 31), ks * 2 + (lane >> 5)));
+          bfr[j] = *reinterpret_cast<const u32x4*>(bs + kc_offk<BK>(wn * WTN + j * 32 + (lane & 31), ks * 2 + (lane >> 5)));
       } else {
         const int kb = ks * 16 + (lane >> 5) * 8 + ((lane & 15) >> 2);
         const int cb = (((lane >> 4) & 1) * 16 + 4 * (lane & 3)) * 2;
@@ -359,9 +369,9 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma(Args args) {
   wave_epilogue<BM, BN, WM, WN, GROUP, EPI>(args, ctx, acc, smem);
 }
 
-template <int BM, int BN, int WM, int WN, int S>
+template <int BM, int BN, int WM, int WN, int S, int BK = 32>
 constexpr size_t dma_lds_bytes() {
-  constexpr size_t ring = (size_t)S * (BM + BN) * 64;
+  constexpr size_t ring = (size_t)S * (BM + BN) * BK * 2;
   constexpr size_t epi = (size_t)WM * WN * 32 * (BN / WN + 8) * 4;
   return ring > epi ? ring : epi;
 }

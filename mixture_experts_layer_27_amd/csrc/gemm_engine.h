@@ -234,17 +234,16 @@ struct TileCtx {
 
 constexpr int kGroupM = 4;
 
-template <int BM, int BN, int BK, int GROUP>
-MOE_DEV bool decode_tile(const Args& args, TileCtx& c) {
-  int total;
-  if constexpr (GROUP == GROUP_M) total = args.tile_prefix[args.E] * args.tilesN;
-  else total = args.total_static;
-  const int per = (total + 7) >> 3;
-  const int b = blockIdx.x;
-  if ((b >> 3) >= per) return false;
-  const int L = (b & 7) * per + (b >> 3);
-  if (L >= total) return false;
+// Number of logical tiles of the launch (GROUP_M: read from the plan on the device).
+template <int GROUP>
+MOE_DEV int total_tiles(const Args& args) {
+  if constexpr (GROUP == GROUP_M) return args.tile_prefix[args.E] * args.tilesN;
+  else return args.total_static;
+}
 
+// Tile coordinates of logical tile L (0 <= L < total_tiles).
+template <int BM, int BN, int BK, int GROUP>
+MOE_DEV void decode_at(const Args& args, int L, TileCtx& c) {
   int e = 0, mt = 0, nt = 0, split = 0;
   int row_begin = 0, row_end = 0;
   int k_begin = 0, k_end = args.K;
@@ -286,6 +285,17 @@ MOE_DEV bool decode_tile(const Args& args, TileCtx& c) {
   c.row_begin = row_begin; c.row_end = row_end;
   c.k_begin = k_begin; c.k_end = k_end;
   c.m0 = mt * BM; c.n0 = nt * BN;
+}
+
+template <int BM, int BN, int BK, int GROUP>
+MOE_DEV bool decode_tile(const Args& args, TileCtx& c) {
+  const int total = total_tiles<GROUP>(args);
+  const int per = (total + 7) >> 3;
+  const int b = blockIdx.x;
+  if ((b >> 3) >= per) return false;
+  const int L = (b & 7) * per + (b >> 3);
+  if (L >= total) return false;
+  decode_at<BM, BN, BK, GROUP>(args, L, c);
   return true;
 }
 

@@ -9,6 +9,9 @@
 // quantum 2^-9, largest 448), saturating; the element byte keeps the sign bit of
 // v.  Every step is exact in fp32, so codes do not depend on evaluation order.
 //
+// Elements are converted with v_cvt_pk_fp8_f32 after exact scaling by 2^-X
+// (see e4m3_pair).
+//
 // Layouts produced for the MX grouped GEMMs (every operand K-contiguous):
 //  * codes [rows][K] (u8), K = the reduction axis;
 //  * "stage-major" scales [K/64][srows][2]: the two block scales of 64
@@ -24,139 +27,135 @@
 
 namespace moe {
 
-MOE_DEV uint32_t e4m3_code(float v, int X) {
-  const uint32_t sign = (__float_as_uint(v) >> 31) << 7;
-  float s = ldexpf(fabsf(v), -X);
-  float r;
-  if (s >= 0.015625f) {                       // 2^-6: normal range
-    int e = ilogbf(s);
-    float q = ldexpf(1.0f, e - 3);
-    r = rintf(s / q) * q;
-  } else {
-    r = rintf(s * 512.0f) * (1.0f / 512.0f);  // subnormal quantum 2^-9
-  }
-  r = fminf(r, 448.0f);
-  uint32_t code;
-  if (r == 0.0f) code = 0;
-  else if (r < 0.015625f) code = (uint32_t)(r * 512.0f);
-  else {
-    int e = ilogbf(r);
-    uint32_t m = (uint32_t)((ldexpf(r, -e) - 1.0f) * 8.0f);
-    code = ((uint32_t)(e + 7) << 3) | m;
-  }
-  return sign | code;
-}
-
+// Shared exponent of a block with largest magnitude amax (bits of a float).
 MOE_DEV int mx_exponent(float amax) {
   if (!(amax > 0.0f)) return -127;
   int X = ilogbf(amax) - 8;
   return X < -127 ? -127 : (X > 127 ? 127 : X);
 }
 
-// quantise 32 floats (one block) into 8 dwords of codes; returns the scale byte
-MOE_DEV uint32_t mx_block(const float* v, uint32_t* ow) {
-  float amax = 0.0f;
+// E4M3 codes of v0, v1 * 2^-X (exact scaling), packed into bytes 0-1 of the
+// result.  v_cvt_pk_fp8_f32 rounds to nearest even into the OCP E4M3 format;
+// clamping to +-448 first gives the saturating rule (values >= 464 would
+// otherwise round past the largest finite code).  Checked against the rule on
+// every finite bf16 input.
+MOE_DEV uint32_t e4m3_pair(float v0, float v1, float inv_scale) {
+  const float a = fminf(fmaxf(v0 * inv_scale, -448.0f), 448.0f);
+  const float b = fminf(fmaxf(v1 * inv_scale, -448.0f), 448.0f);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false) & 0xffffu;
+}
+MOE_DEV float pow2f(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }   // 2^e, -126 <= e <= 127
+
+// 8 values (one 16-byte bf16 chunk) -> 8 codes
+MOE_DEV uint2 e4m3_8(const float* v, float inv) {
+  return uint2{e4m3_pair(v[0], v[1], inv) | (e4m3_pair(v[2], v[3], inv) << 16),
+               e4m3_pair(v[4], v[5], inv) | (e4m3_pair(v[6], v[7], inv) << 16)};
+}
+
+MOE_DEV void unpack8(u32x4 q, float* v) {
 #pragma unroll
-  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
-  const int X = mx_exponent(amax);
-#pragma unroll
-  for (int w = 0; w < 8; ++w)
-    ow[w] = e4m3_code(v[4 * w], X) | (e4m3_code(v[4 * w + 1], X) << 8) | (e4m3_code(v[4 * w + 2], X) << 16) |
-            (e4m3_code(v[4 * w + 3], X) << 24);
-  return (uint32_t)(X + 127);
+  for (int j = 0; j < 4; ++j) {
+    v[2 * j] = __uint_as_float(q[j] << 16);
+    v[2 * j + 1] = __uint_as_float(q[j] & 0xffff0000u);
+  }
 }
 
 namespace {
 
-// (1) along rows: one thread per 32-block of a row-major [rows, K] bf16 matrix.
-// Scale layouts: plain [rows][K/32] (staged == 0, the test hook) or stage-major.
-// With `offsets` the source is a permuted activation: only its offsets[E] rows
-// in use are read, and row r of expert e lands at row r - offsets[e] + pad_off[e].
+// (1) along rows.  Lane i of a wave loads 16 bytes (8 values) at consecutive
+// addresses, so four lanes hold one 32-value block: the block maximum is
+// reduced across the quad, every lane writes its 8 codes, the first lane of the
+// quad the scale byte.  Scale layouts: plain [rows][K/32] (staged == 0, the test
+// hook) or stage-major [K/64][srows][2].  With `offsets` the source is a
+// permuted activation: only its offsets[E] rows in use are read, and row r of
+// expert e lands at row r - offsets[e] + pad_off[e].
 __global__ __launch_bounds__(256) void quantize_rows_kernel(const bf16_t* __restrict__ src, int64_t rows, int64_t K,
                                                            uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
                                                            int64_t srows, int staged,
                                                            const int32_t* __restrict__ offsets,
                                                            const int32_t* __restrict__ expert_of_row,
                                                            const int32_t* __restrict__ pad_off, int E) {
-  const int64_t nb = K / 32;
+  const int64_t chunks = K / 8;   // 16-byte chunks per row
   const int64_t nr = offsets ? (int64_t)offsets[E] : rows;
-  const int64_t total = nr * nb;
-  for (int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x; b < total; b += (int64_t)gridDim.x * 256) {
-    const int64_t r = b / nb, c = b - r * nb;
-    const bf16_t* p = src + r * K + c * 32;
-    float v[32];
+  // total is a multiple of 4 (K % 32 == 0) and so are the start and the stride:
+  // the four lanes of a quad (one block) always iterate together
+  const int64_t total = nr * chunks;
+  for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < total; q += (int64_t)gridDim.x * 256) {
+    const int64_t r = q / chunks, ch = q - r * chunks;
+    float v[8];
+    unpack8(ldg16(src + r * K + ch * 8), v);
+    float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      u32x4 q = ldg16(p + 8 * i);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v[8 * i + 2 * j] = __uint_as_float(q[j] << 16);
-        v[8 * i + 2 * j + 1] = __uint_as_float(q[j] & 0xffff0000u);
-      }
-    }
-    uint32_t ow[8];
-    const uint32_t sc = mx_block(v, ow);
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    const int X = mx_exponent(amax);
     int64_t dr = r;
     if (offsets) {
       const int e = expert_of_row[r];
       dr = r - offsets[e] + pad_off[e];
     }
-    uint8_t* cp = codes + dr * K + c * 32;
-    stg16(cp, u32x4{ow[0], ow[1], ow[2], ow[3]});
-    stg16(cp + 16, u32x4{ow[4], ow[5], ow[6], ow[7]});
-    if (staged) scales[((c >> 1) * srows + dr) * 2 + (c & 1)] = (uint8_t)sc;
-    else scales[dr * nb + c] = (uint8_t)sc;
+    *reinterpret_cast<uint2*>(codes + dr * K + ch * 8) = e4m3_8(v, pow2f(-X));
+    if ((q & 3) == 0) {
+      const int64_t c = ch >> 2;   // 32-block index along K
+      const uint8_t sb = (uint8_t)(X + 127);
+      if (staged) scales[((c >> 1) * srows + dr) * 2 + (c & 1)] = sb;
+      else scales[dr * (K / 32) + c] = sb;
+    }
   }
 }
 
-// (2)/(3) along the first axis, written transposed.  One block = 64 positions of
-// the reduction axis x 64 columns, staged through LDS.
-//   columns mode (tok_off == nullptr): src [G][R][C]; position p of group g is
+// (2)/(3) along the first axis, written transposed.  One block = 128 positions
+// of the reduction axis x 64 columns: loaded with 16-byte row reads, staged in
+// LDS, and each thread quantises one column over one 32-position block.
+//   columns mode (seg_off == nullptr): src [G][R][C]; position p of group g is
 //     row p of matrix g; out codes [G][C][R], scales [R/64][G*C][2].
 //   tokens mode: src [rows][C] (expert segments given by seg_off), positions are
 //     padded tokens: segment e occupies [pad_off[e], pad_off[e+1]) with
 //     pad_off[e] a multiple of 64; position p maps to source row
 //     seg_off[e] + (p - pad_off[e]) when that is inside the segment, else 0.
 //     out codes [C][P], scales [P/64][C][2], P = the padded capacity.
-__global__ __launch_bounds__(128) void quantize_t_kernel(const bf16_t* __restrict__ src, int G, int R, int C,
+__global__ __launch_bounds__(256) void quantize_t_kernel(const bf16_t* __restrict__ src, int G, int R, int C,
                                                         const int32_t* __restrict__ seg_off,
                                                         const int32_t* __restrict__ pad_off, int E,
                                                         uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
                                                         int64_t P) {
-  __shared__ float tile[64][65];
-  const int ct = blockIdx.x;            // column tile
-  const int pt = blockIdx.y;            // position tile (64 positions)
+  __shared__ float tile[128][65];
+  const int c0 = blockIdx.x * 64;
+  const int64_t p0 = (int64_t)blockIdx.y * 128;
   const int g = blockIdx.z;
-  const int c0 = ct * 64;
-  const int64_t p0 = (int64_t)pt * 64;
-  int e = 0;
-  int64_t src_base = 0, valid = 64;
-  if (seg_off) {
-    if (p0 >= pad_off[E]) return;
-    int lo = 0, hi = E;                 // segment holding p0
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (pad_off[mid] <= p0) lo = mid; else hi = mid;
-    }
-    e = lo;
-    const int64_t into = p0 - pad_off[e];
-    src_base = seg_off[e] + into;
-    valid = (int64_t)(seg_off[e + 1] - seg_off[e]) - into;
-  } else {
-    src_base = (int64_t)g * R + p0;
-  }
-  // load 64 rows x 64 columns (bf16) into LDS as floats
-  for (int i = threadIdx.x; i < 64 * 8; i += 128) {
-    const int rr = i >> 3, ch = i & 7;
-    float v[8];
-    if (rr < valid) {
-      u32x4 q = ldg16(src + (src_base + rr) * C + c0 + ch * 8);
+  const int64_t len = seg_off ? P : (int64_t)R;
+  if (p0 >= (seg_off ? (int64_t)pad_off[E] : (int64_t)R)) return;
+  // source row and valid count of each 64-position half
+  int64_t base[2], valid[2];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        v[2 * j] = __uint_as_float(q[j] << 16);
-        v[2 * j + 1] = __uint_as_float(q[j] & 0xffff0000u);
+  for (int hh = 0; hh < 2; ++hh) {
+    const int64_t ph = p0 + 64 * hh;
+    base[hh] = 0;
+    valid[hh] = 0;
+    if (seg_off) {
+      if (ph < pad_off[E]) {
+        int lo = 0, hi = E;   // segment holding ph: pad_off[lo] <= ph < pad_off[lo+1]
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (pad_off[mid] <= ph) lo = mid; else hi = mid;
+        }
+        const int64_t into = ph - pad_off[lo];
+        base[hh] = seg_off[lo] + into;
+        valid[hh] = (int64_t)(seg_off[lo + 1] - seg_off[lo]) - into;
       }
-    } else {
+    } else if (ph < R) {
+      base[hh] = (int64_t)g * R + ph;
+      valid[hh] = 64;
+    }
+  }
+  // 128 rows x 64 columns: 8 threads per row, 16 bytes each
+  for (int i = threadIdx.x; i < 128 * 8; i += 256) {
+    const int rr = i >> 3, ch = i & 7;
+    const int hh = rr >> 6, rl = rr & 63;
+    float v[8];
+    if (rl < valid[hh]) unpack8(ldg16(src + (base[hh] + rl) * C + c0 + ch * 8), v);
+    else {
 #pragma unroll
       for (int j = 0; j < 8; ++j) v[j] = 0.0f;
     }
@@ -164,20 +163,32 @@ __global__ __launch_bounds__(128) void quantize_t_kernel(const bf16_t* __restric
     for (int j = 0; j < 8; ++j) tile[rr][ch * 8 + j] = v[j];
   }
   __syncthreads();
-  const int c = threadIdx.x & 63, b = threadIdx.x >> 6;   // column, 32-block inside the 64 positions
+  // thread -> (column c, 32-position block b); lanes pair up blocks 2m, 2m+1 of one
+  // column so the two scale bytes of a 64-position step are written together
+  const int t = threadIdx.x;
+  const int b = ((t >> 7) << 1) | (t & 1);   // 0..3
+  const int c = (t >> 1) & 63;
   float v[32];
+  float amax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) v[i] = tile[b * 32 + i][c];
-  uint32_t ow[8];
-  const uint32_t sc = mx_block(v, ow);
+  for (int i = 0; i < 32; ++i) {
+    v[i] = tile[b * 32 + i][c];
+    amax = fmaxf(amax, fabsf(v[i]));
+  }
+  const int X = mx_exponent(amax);
+  const float inv = pow2f(-X);
   int64_t crow, srows;
   if (seg_off) { crow = c0 + c; srows = C; }
   else { crow = (int64_t)g * C + c0 + c; srows = (int64_t)G * C; }
-  const int64_t len = seg_off ? P : (int64_t)R;
-  uint8_t* cp = codes + crow * len + p0 + b * 32;
-  stg16(cp, u32x4{ow[0], ow[1], ow[2], ow[3]});
-  stg16(cp + 16, u32x4{ow[4], ow[5], ow[6], ow[7]});
-  scales[((p0 >> 6) * srows + crow) * 2 + b] = (uint8_t)sc;
+  const int64_t pb = p0 + b * 32;
+  if (pb >= len) return;
+  uint8_t* cp = codes + crow * len + pb;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint2 lo = e4m3_8(v + 16 * h, inv), hi2 = e4m3_8(v + 16 * h + 8, inv);
+    *reinterpret_cast<u32x4*>(cp + 16 * h) = u32x4{lo.x, lo.y, hi2.x, hi2.y};
+  }
+  scales[((pb >> 6) * srows + crow) * 2 + ((pb >> 5) & 1)] = (uint8_t)(X + 127);
 }
 
 // pad_off[e] = sum over experts j < e of count_j rounded up to 64 (E <= 256)
@@ -198,9 +209,9 @@ __global__ __launch_bounds__(256) void pad_offsets_kernel(const int32_t* __restr
   if (i == 0) pad_off[0] = 0;
 }
 
-int qgrid(int64_t blocks) {
-  int64_t g = (blocks + 255) / 256;
-  if (g > 8192) g = 8192;
+int qgrid(int64_t threads) {
+  int64_t g = (threads + 255) / 256;
+  if (g > 16384) g = 16384;
   if (g < 1) g = 1;
   return (int)g;
 }
@@ -209,7 +220,7 @@ int qgrid(int64_t blocks) {
 
 hipError_t launch_quantize_rows(const void* src, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
                                 hipStream_t st) {
-  hipLaunchKernelGGL(quantize_rows_kernel, dim3(qgrid(rows * (cols / 32))), dim3(256), 0, st, (const bf16_t*)src,
+  hipLaunchKernelGGL(quantize_rows_kernel, dim3(qgrid(rows * (cols / 8))), dim3(256), 0, st, (const bf16_t*)src,
                      rows, cols, codes, scales, (int64_t)0, 0, (const int32_t*)nullptr, (const int32_t*)nullptr,
                      (const int32_t*)nullptr, 0);
   return hipGetLastError();
@@ -217,7 +228,7 @@ hipError_t launch_quantize_rows(const void* src, int64_t rows, int64_t cols, uin
 
 hipError_t mx_quantize_rows_staged(const void* src, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales,
                                    int64_t srows, hipStream_t st) {
-  hipLaunchKernelGGL(quantize_rows_kernel, dim3(qgrid(rows * (K / 32))), dim3(256), 0, st, (const bf16_t*)src, rows,
+  hipLaunchKernelGGL(quantize_rows_kernel, dim3(qgrid(rows * (K / 8))), dim3(256), 0, st, (const bf16_t*)src, rows,
                      K, codes, scales, srows, 1, (const int32_t*)nullptr, (const int32_t*)nullptr,
                      (const int32_t*)nullptr, 0);
   return hipGetLastError();
@@ -226,20 +237,20 @@ hipError_t mx_quantize_rows_staged(const void* src, int64_t rows, int64_t K, uin
 hipError_t mx_quantize_rows_padded(const void* src, int64_t rows, int64_t K, const int32_t* offsets,
                                    const int32_t* expert_of_row, const int32_t* pad_off, int E, uint8_t* codes,
                                    uint8_t* scales, int64_t srows, hipStream_t st) {
-  hipLaunchKernelGGL(quantize_rows_kernel, dim3(qgrid(rows * (K / 32))), dim3(256), 0, st, (const bf16_t*)src, rows,
+  hipLaunchKernelGGL(quantize_rows_kernel, dim3(qgrid(rows * (K / 8))), dim3(256), 0, st, (const bf16_t*)src, rows,
                      K, codes, scales, srows, 1, offsets, expert_of_row, pad_off, E);
   return hipGetLastError();
 }
 
 hipError_t mx_quantize_cols(const void* src, int G, int R, int C, uint8_t* codes, uint8_t* scales, hipStream_t st) {
-  hipLaunchKernelGGL(quantize_t_kernel, dim3(C / 64, R / 64, G), dim3(128), 0, st, (const bf16_t*)src, G, R, C,
+  hipLaunchKernelGGL(quantize_t_kernel, dim3(C / 64, (R + 127) / 128, G), dim3(256), 0, st, (const bf16_t*)src, G, R, C,
                      (const int32_t*)nullptr, (const int32_t*)nullptr, 0, codes, scales, (int64_t)0);
   return hipGetLastError();
 }
 
 hipError_t mx_quantize_tokens(const void* src, int C, const int32_t* seg_off, const int32_t* pad_off, int E,
                               int64_t P, uint8_t* codes, uint8_t* scales, hipStream_t st) {
-  hipLaunchKernelGGL(quantize_t_kernel, dim3(C / 64, (unsigned)(P / 64), 1), dim3(128), 0, st, (const bf16_t*)src, 1,
+  hipLaunchKernelGGL(quantize_t_kernel, dim3(C / 64, (unsigned)((P + 127) / 128), 1), dim3(256), 0, st, (const bf16_t*)src, 1,
                      0, C, seg_off, pad_off, E, codes, scales, P);
   return hipGetLastError();
 }

@@ -130,6 +130,12 @@ def test_quantize_mx_bit_exact():
     src[3, :32] = 0.0                       # all-zero block
     src[4, 0] = 500.0                       # saturating block
     src[5, :32] = -0.0
+    # E4M3 rounding ties and the saturation band, block maximum 256 (shared exponent 0)
+    q = 2.0 ** -9
+    ties = [256.0, 17.0, 19.0, 272.0, 304.0, 1.5 * q, 2.5 * q, 0.5 * q, 0.75 * q, -17.0, -2.5 * q, 440.0 / 2]
+    src[6, :32] = 0.0
+    src[6, :len(ties)] = torch.tensor(ties)
+    src[7, :32] = torch.tensor([500.0, 460.0, 440.0, 449.0, -470.0, 3.0] + [1.0] * 26)   # exponent 0, saturating
     codes = torch.empty(src.shape, dtype=torch.uint8, device="cuda")
     scales = torch.empty((96, 8), dtype=torch.uint8, device="cuda")
     binding.quantize_mx(src.cuda(), codes, scales)
