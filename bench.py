@@ -118,7 +118,7 @@ def main():
     fwd_gemm_flops = 2.0 * rows * cfg.d * 2 * cfg.f + 2.0 * rows * cfg.f * cfg.d
     peak = {"mxfp8": PEAK_FP8_TFLOPS, "bf16": PEAK_BF16_TFLOPS}.get(cfg.gemm, PEAK_F32_TFLOPS)
     achieved = fwd_gemm_flops / (ms["experts"] * 1e-3) / 1e12
-    permute_bytes = cfg.T * cfg.d * esz + rows * cfg.d * esz + 4 * rows
+    permute_bytes = cfg.T * cfg.d * esz + rows * cfg.d * esz + 4 * (cfg.T + 1) + 4 * rows
     combine_bytes = rows * cfg.d * esz + cfg.T * cfg.d * esz + 8 * rows
     bwd_flops = 2 * fwd_gemm_flops
     out = {

@@ -261,8 +261,7 @@ moe_status moe_permute(const moe_shape* s, const void* src, const moe_plan* plan
   if (st != MOE_OK) return st;
   if (!aligned(src) || !aligned(dst)) return MOE_EINVAL;
   if ((st = check_plan(*s, plan)) != MOE_OK) return st;
-  return hip_status(launch_gather_rows(*s, src, plan->token_of_row, plan->offsets, dst,
-                                       reinterpret_cast<hipStream_t>(stream)));
+  return hip_status(launch_permute_rows(*s, src, *plan, dst, reinterpret_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_grouped_gemm_swiglu(const moe_shape* s, const void* x_perm, const void* w1, const void* w2,
@@ -323,7 +322,7 @@ moe_status moe_backward(const moe_shape* s, const void* x, const void* w_gate, c
   carve_bwd(*s, reinterpret_cast<char*>(ws), &w);
   float* dz = dlogits ? dlogits : w.dlogits;
   const int ldz = ldz_of(*s);
-  hipError_t e = launch_gather_rows(*s, dout, plan->token_of_row, plan->offsets, w.do_perm, hs);
+  hipError_t e = launch_permute_rows(*s, dout, *plan, w.do_perm, hs);
   if (s->gemm == MOE_MXFP8) {
     const int64_t N = max_rows(*s), P = tok_cap(*s);
     const int E = s->E, d = s->d, f = s->d_ff;
@@ -336,7 +335,7 @@ moe_status moe_backward(const moe_shape* s, const void* x, const void* w_gate, c
     if (e == hipSuccess)
       e = mx_quantize_rows_padded(w.dh, N, 2 * f, off, eor, w.pad_off, E, w.dhq.codes, w.dhq.scales, w.dhq.srows, hs);
     if (e == hipSuccess) e = mx_quantize_cols(w1, E, 2 * f, d, w.w1t.codes, w.w1t.scales, hs);
-    if (e == hipSuccess) e = launch_gather_rows(*s, x, plan->token_of_row, plan->offsets, w.xbuf, hs);
+    if (e == hipSuccess) e = launch_permute_rows(*s, x, *plan, w.xbuf, hs);
     if (e == hipSuccess) e = mx_quantize_tokens(w.dh, 2 * f, plan->offsets, w.pad_off, E, P, w.dh_t.codes, w.dh_t.scales, hs);
     if (e == hipSuccess) e = mx_quantize_tokens(w.xbuf, d, plan->offsets, w.pad_off, E, P, w.x_t.codes, w.x_t.scales, hs);
     if (e == hipSuccess) e = mx_quantize_tokens(w.do_perm, d, plan->offsets, w.pad_off, E, P, w.do_t.codes, w.do_t.scales, hs);
@@ -346,7 +345,7 @@ moe_status moe_backward(const moe_shape* s, const void* x, const void* w_gate, c
     if (e == hipSuccess) e = gemm_mx_dx_perm(*s, *plan, pi, w.dhq, w.w1t, w.xbuf, hs);   // x_perm no longer needed
   } else {
     if (e == hipSuccess) e = gemm_dact(*s, *plan, pi, w.do_perm, w2, h_saved, w.dh, w.ga, w.ds_part, hs);
-    if (e == hipSuccess) e = launch_gather_rows(*s, x, plan->token_of_row, plan->offsets, w.xbuf, hs);
+    if (e == hipSuccess) e = launch_permute_rows(*s, x, *plan, w.xbuf, hs);
     if (e == hipSuccess) e = gemm_dw1(*s, *plan, w.dh, w.xbuf, dw1, hs);
     if (e == hipSuccess) e = gemm_dw2(*s, *plan, w.do_perm, w.ga, dw2, hs);
     if (e == hipSuccess) e = gemm_dx_perm(*s, *plan, pi, w.dh, w1, w.xbuf, hs);   // x_perm no longer needed

@@ -5,34 +5,37 @@
 // router backward, and the split-K reduction.
 //
 // Rows are moved as 16-byte vectors; consecutive threads take consecutive
-// vectors of one row, so every wave reads and writes whole 1 KiB spans.
+// vectors of one row, so every wave reads and writes whole spans.
 #include "moe_common.h"
 #include "moe_internal.h"
 
 namespace moe {
 namespace {
 
-// dst[r] = src[map[r]] for r < offsets[E]; vec = 16-byte vectors per row.
-__global__ __launch_bounds__(256) void gather_rows_kernel(const char* __restrict__ src, const int32_t* __restrict__ map,
-                                                         const int32_t* __restrict__ nrows_ptr, int vec,
-                                                         char* __restrict__ dst, int64_t rows_cap) {
-  const int64_t nrows = *nrows_ptr;
-  const int64_t total = nrows * vec;
-  const int64_t stride = (int64_t)gridDim.x * 256 * 4;
-  for (int64_t base = (int64_t)blockIdx.x * 256 * 4 + threadIdx.x; base < total; base += stride) {
-    u32x4 v[4];
-    int64_t idx[4];
+// dst[r] = src[t] for every row r of token t (the token's rows are
+// tok_rows[tok_ptr[t] .. tok_ptr[t+1])), i.e. dst[r] = src[token_of_row[r]].
+// Written as a scatter: each source vector is read once and stored to each of
+// its rows, so the source streams from HBM once instead of once per row.
+// vec = 16-byte vectors per row; each thread moves U vectors of one token.
+template <int U>
+__global__ __launch_bounds__(256) void scatter_rows_kernel(const char* __restrict__ src,
+                                                          const int32_t* __restrict__ tok_ptr,
+                                                          const int32_t* __restrict__ tok_rows, int T_, int vec,
+                                                          char* __restrict__ dst) {
+  const int per_tok = vec / U;   // threads per token
+  const int64_t total = (int64_t)T_ * per_tok;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int t = (int)(i / per_tok);
+    const int c0 = (int)(i - (int64_t)t * per_tok);
+    u32x4 v[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      idx[u] = base + u * 256;
-      if (idx[u] < total) {
-        int64_t r = idx[u] / vec, c = idx[u] - r * vec;
-        v[u] = ldg16(src + ((int64_t)map[r] * vec + c) * 16);
-      }
+    for (int u = 0; u < U; ++u) v[u] = ldg16(src + ((int64_t)t * vec + c0 + u * per_tok) * 16);
+    const int p0 = tok_ptr[t], p1 = tok_ptr[t + 1];
+    for (int p = p0; p < p1; ++p) {
+      char* drow = dst + (int64_t)tok_rows[p] * vec * 16;
+#pragma unroll
+      for (int u = 0; u < U; ++u) stg16(drow + (int64_t)(c0 + u * per_tok) * 16, v[u]);
     }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (idx[u] < total) stg16(dst + idx[u] * 16, v[u]);
   }
 }
 
@@ -51,19 +54,31 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, c
 #pragma unroll
     for (int q = 0; q < EV; ++q) acc[q] = 0.0f;
     const int p0 = tok_ptr[t], p1 = tok_ptr[t + 1];
-    for (int p = p0; p < p1; ++p) {
-      const int r = tok_rows[p];
-      const float g = gate[r];
-      u32x4 v = ldg16(y + (int64_t)r * d + c * EV);
-      if constexpr (sizeof(T) == 2) {
+    for (int pb = p0; pb < p1; pb += 4) {
+      // up to four rows' vectors in flight, accumulated in ascending row order
+      u32x4 v[4];
+      float g[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          acc[2 * q] += g * __uint_as_float(v[q] << 16);
-          acc[2 * q + 1] += g * __uint_as_float(v[q] & 0xffff0000u);
+      for (int u = 0; u < 4; ++u) {
+        if (pb + u < p1) {
+          const int r = tok_rows[pb + u];
+          g[u] = gate[r];
+          v[u] = ldg16(y + (int64_t)r * d + c * EV);
         }
-      } else {
+      }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc[q] += g * __uint_as_float(v[q]);
+      for (int u = 0; u < 4; ++u) {
+        if (pb + u >= p1) break;
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            acc[2 * q] += g[u] * __uint_as_float(v[u][q] << 16);
+            acc[2 * q + 1] += g[u] * __uint_as_float(v[u][q] & 0xffff0000u);
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[q] += g[u] * __uint_as_float(v[u][q]);
+        }
       }
     }
     u32x4 o;
@@ -139,13 +154,18 @@ int grid_for(int64_t work, int per_block) {
 
 }  // namespace
 
-hipError_t launch_gather_rows(const moe_shape& s, const void* src, const int32_t* rows_map, const int32_t* offsets,
-                              void* dst, hipStream_t st) {
+hipError_t launch_permute_rows(const moe_shape& s, const void* src, const moe_plan& p, void* dst, hipStream_t st) {
   const int esz = s.act == MOE_BF16 ? 2 : 4;
   const int vec = s.d * esz / 16;
-  const int64_t work = max_rows(s) * vec;
-  hipLaunchKernelGGL(gather_rows_kernel, dim3(grid_for(work, 1024)), dim3(256), 0, st, (const char*)src, rows_map,
-                     offsets + s.E, vec, (char*)dst, max_rows(s));
+  if (vec % 4 == 0) {
+    const int64_t work = (int64_t)s.T * (vec / 4);
+    hipLaunchKernelGGL(scatter_rows_kernel<4>, dim3(grid_for(work, 256)), dim3(256), 0, st, (const char*)src,
+                       p.tok_ptr, p.tok_rows, s.T, vec, (char*)dst);
+  } else {
+    const int64_t work = (int64_t)s.T * vec;
+    hipLaunchKernelGGL(scatter_rows_kernel<1>, dim3(grid_for(work, 256)), dim3(256), 0, st, (const char*)src,
+                       p.tok_ptr, p.tok_rows, s.T, vec, (char*)dst);
+  }
   return hipGetLastError();
 }
 

@@ -40,8 +40,8 @@ hipError_t launch_round_select(const moe_shape& s, const moe_plan& p, const Plan
                                hipStream_t st);
 
 // ---- elementwise (elementwise.hip)
-hipError_t launch_gather_rows(const moe_shape& s, const void* src, const int32_t* rows_map,
-                              const int32_t* offsets, void* dst, hipStream_t st);
+// dst[r] = src[token_of_row[r]] for every routed row r
+hipError_t launch_permute_rows(const moe_shape& s, const void* src, const moe_plan& p, void* dst, hipStream_t st);
 hipError_t launch_combine(const moe_shape& s, const void* y, const moe_plan& p, void* out,
                           hipStream_t st);
 hipError_t launch_router_bwd(const moe_shape& s, const moe_plan& p, const float* ds_part, int nparts,
