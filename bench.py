@@ -23,6 +23,33 @@ PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 (MXFP8) MFMA
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
+COPY_BYTES = 256 << 20
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "moe_layer_fine_e128_forward_gemm_hbm_traffic.md")
+
+
+def recorded_traffic(workload):
+    """Calibrated HBM bytes per forward expert-GEMM call from the committed
+    FETCH_SIZE/WRITE_SIZE summary, or None when that summary is for another
+    workload or the kernel sources changed since the counters were taken."""
+    import hashlib
+    try:
+        kv = {}
+        for line in open(TRAFFIC_FILE):
+            if ":" in line and not line.startswith((" ", "|", "#")):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+        if kv.get("workload") != workload:
+            return None
+        h = hashlib.sha256()
+        for src in kv["kernel_sources"].split():
+            h.update(open(os.path.join(ROOT, src), "rb").read())
+        if h.hexdigest() != kv["kernel_sources_sha256"]:
+            return None
+        return float(kv["traffic_bytes_per_call"])
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def parse():
@@ -34,6 +61,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0 = automatic)")
     ap.add_argument("--out", default=None, help="also append the JSON line to this file")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device copy three times (reference for the HBM byte counters)")
     return ap.parse_args()
 
 
@@ -67,6 +96,17 @@ def main():
         sys.exit(2)
     import torch
     from mixture_experts_layer_27_amd import binding, configs, synth
+
+    if a.copy_calibration:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+        src.fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 3}), flush=True)
+        return
 
     cfg = configs.get(a.config)
     print(f"[bench] generating {cfg.name} inputs", file=sys.stderr, flush=True)
@@ -140,7 +180,7 @@ def main():
                    "global_batch": cfg.T, "seq_len": 1, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "kernel": "forward expert GEMMs (up+SwiGLU, down) in one call",
                      "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
-                     "traffic": None},
+                     "traffic": recorded_traffic(cfg.name), "traffic_unit": "HBM bytes per call"},
         "phases_ms": ms,
         "events_ms_per_step": step_ms,
         "grouped_gemm_mfma_frac": {"forward": achieved / peak,
