@@ -24,6 +24,8 @@ CASES = {
     "sparse_round_mx_small": configs.SPARSE_ROUND.scaled("sparse_round_mx_small", T=1200, d=512, E=64, f=128,
                                                          gemm="mxfp8"),
     "mx_ragged_d": configs.FINE_MX.scaled("mx_ragged_d", T=700, d=192, E=8, k=2, f=384),
+    "mx_zipf_small": configs.FINE_ZIPF.scaled("mx_zipf_small", T=1500, d=256, E=32, f=256, gemm="mxfp8"),
+    "mx_one_token": configs.FINE_MX.scaled("mx_one_token", T=1, d=128, E=8, k=2, f=128),
 }
 
 

@@ -14,8 +14,8 @@ Each decision is therefore re-taken with its input moved by +-WINDOW (relative).
 Where the outcome changes, the changed dequantised values minus the oracle's
 give a delta that enters the GEMM output linearly.  The reference a GPU output
 vector is compared with is the oracle's vector plus those deltas that bring it
-closer to the GPU's (one pass: delta d is taken when 2 <r, d> > |d|^2 for the
-residual r = GPU - oracle).  Every delta is computed by the oracle from the
+closer to the GPU's (best first, each taken delta reducing the squared
+residual by at least half its own squared norm).  Every delta is computed by the oracle from the
 oracle's own values; the GPU output only selects among them.  Inputs of the layer
 (x, dout, the weights) are never decided this way: both sides quantise the same
 bf16 values.
@@ -27,9 +27,11 @@ import numpy as np
 from oracle import mx
 
 BLOCK = 32
-# bf16 ulps are 2^-8..2^-7 of a value; computed values differ by at most about
-# two ulps between the two sides
+# bf16 ulps are 2^-8..2^-7 of a value; the computed values that decide a block
+# exponent or an element code differ by up to a few ulps between the two sides
+# (gA = g * A inherits A's difference, A inherits H's)
 WINDOW = 2.0 ** -6
+WINDOW_ELEM = 2.0 ** -6
 
 
 def block_candidates(blk):
@@ -52,7 +54,7 @@ def block_candidates(blk):
     s = np.abs(blk) / scale
     base = mx.e4m3_round(s)
     sign = np.where(np.signbit(blk), -1.0, 1.0)
-    for f in (1.0 + WINDOW, 1.0 - WINDOW):
+    for f in (1.0 + WINDOW_ELEM, 1.0 - WINDOW_ELEM):
         alt = mx.e4m3_round(s * f)
         ii, jj = np.nonzero(alt != base)
         vals = sign[ii, jj] * (alt[ii, jj] - base[ii, jj]) * scale[0, jj]
@@ -61,13 +63,27 @@ def block_candidates(blk):
 
 
 def _select(got, ref, D):
-    """ref + the deltas (rows of D) that each bring ref closer to got."""
+    """ref plus a subset of the deltas (rows of D) chosen best first: repeatedly
+    take the delta that most reduces |got - ref|^2, while the reduction is at
+    least half of that delta's own |d|^2 (a delta that only fits noise, or one
+    that overlaps deltas already taken, is left out)."""
     if len(D) == 0:
         return ref
     D = np.asarray(D)
-    r = got - ref
-    take = 2.0 * (D @ r) > np.einsum("ij,ij->i", D, D)
-    return ref + D[take].sum(axis=0)
+    r = np.asarray(got, np.float64) - ref
+    n2 = np.einsum("ij,ij->i", D, D)
+    c = D @ r
+    out = ref.copy()
+    free = n2 > 0
+    for _ in range(len(D)):
+        gain = np.where(free, 2.0 * c - n2, -np.inf)
+        i = int(np.argmax(gain))
+        if not free[i] or gain[i] < 0.5 * n2[i]:
+            break
+        out = out + D[i]
+        c = c - D @ D[i]
+        free[i] = False
+    return out
 
 
 def operand_deltas(v, axis, other):
