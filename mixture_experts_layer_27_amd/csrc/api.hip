@@ -108,9 +108,18 @@ MxOperand take_mx(Carver& c, int64_t rows, int64_t K, int64_t srows, const int32
   return o;
 }
 
+// rows per weight-gradient chunk: at most 32 chunks past the experts' first
+int wgrad_kch(int64_t ncap) {
+  int64_t k = (ncap + 31) / 32;
+  k = (k + 63) / 64 * 64;
+  return (int)(k < 1024 ? 1024 : k);
+}
+int64_t wgrad_cap(const moe_shape& s) { return s.gemm == MOE_MXFP8 ? tok_cap(s) : max_rows(s); }
+
 struct BwdWs {
   void *do_perm, *dh, *ga, *xbuf, *dzq;
   float *ds_part, *dlogits, *dwg_part;
+  WgradChunks wg;
   // MXFP8 only
   MxOperand doq, w2t, dhq, w1t, dh_t, x_t, do_t, ga_t;
   int32_t* pad_off;
@@ -128,6 +137,18 @@ size_t carve_bwd(const moe_shape& s, char* base, BwdWs* w) {
   q.dlogits = c.take<float>((size_t)s.T * s.E * 4);
   q.dzq = c.take<char>((size_t)s.T * ldz_of(s) * esz(s));
   q.dwg_part = c.take<float>((size_t)gemm_router_dwg_splits(s) * s.E * s.d * 4);
+  {
+    const int64_t ncap = wgrad_cap(s);
+    WgradChunks& g = q.wg;
+    g.kch = wgrad_kch(ncap);
+    g.max_extra = (int)(ncap / g.kch);
+    g.max_chunks = s.E + g.max_extra;
+    g.chunks = c.take<int4>((size_t)g.max_chunks * 16);
+    g.nchunks = c.take<int32_t>(4);
+    g.slot_range = c.take<int2>((size_t)s.E * 8);
+    const int64_t mn = (int64_t)2 * s.d_ff * s.d;   // the larger of dW1_e, dW2_e
+    g.part = c.take<float>((size_t)g.max_extra * mn * 4);
+  }
   if (s.gemm == MOE_MXFP8) {
     const int64_t E = s.E, d = s.d, f = s.d_ff, P = tok_cap(s);
     q.pad_off = c.take<int32_t>((E + 1) * 4);
@@ -340,14 +361,20 @@ moe_status moe_backward(const moe_shape* s, const void* x, const void* w_gate, c
     if (e == hipSuccess) e = mx_quantize_tokens(w.xbuf, d, plan->offsets, w.pad_off, E, P, w.x_t.codes, w.x_t.scales, hs);
     if (e == hipSuccess) e = mx_quantize_tokens(w.do_perm, d, plan->offsets, w.pad_off, E, P, w.do_t.codes, w.do_t.scales, hs);
     if (e == hipSuccess) e = mx_quantize_tokens(w.ga, f, plan->offsets, w.pad_off, E, P, w.ga_t.codes, w.ga_t.scales, hs);
-    if (e == hipSuccess) e = gemm_mx_wgrad(*s, w.pad_off, P, w.dh_t, 2 * f, w.x_t, d, dw1, hs);
-    if (e == hipSuccess) e = gemm_mx_wgrad(*s, w.pad_off, P, w.do_t, d, w.ga_t, f, dw2, hs);
+    if (e == hipSuccess) e = launch_wgrad_chunks(w.pad_off, E, w.wg.kch, w.wg, hs);
+    if (e == hipSuccess) e = gemm_mx_wgrad(*s, w.wg, P, w.dh_t, 2 * f, w.x_t, d, dw1, hs);
+    if (e == hipSuccess) e = launch_wgrad_reduce(w.wg, E, (int64_t)2 * f * d, dw1, hs);
+    if (e == hipSuccess) e = gemm_mx_wgrad(*s, w.wg, P, w.do_t, d, w.ga_t, f, dw2, hs);
+    if (e == hipSuccess) e = launch_wgrad_reduce(w.wg, E, (int64_t)d * f, dw2, hs);
     if (e == hipSuccess) e = gemm_mx_dx_perm(*s, *plan, pi, w.dhq, w.w1t, w.xbuf, hs);   // x_perm no longer needed
   } else {
     if (e == hipSuccess) e = gemm_dact(*s, *plan, pi, w.do_perm, w2, h_saved, w.dh, w.ga, w.ds_part, hs);
     if (e == hipSuccess) e = launch_permute_rows(*s, x, *plan, w.xbuf, hs);
-    if (e == hipSuccess) e = gemm_dw1(*s, *plan, w.dh, w.xbuf, dw1, hs);
-    if (e == hipSuccess) e = gemm_dw2(*s, *plan, w.do_perm, w.ga, dw2, hs);
+    if (e == hipSuccess) e = launch_wgrad_chunks(plan->offsets, s->E, w.wg.kch, w.wg, hs);
+    if (e == hipSuccess) e = gemm_dw1(*s, w.wg, w.dh, w.xbuf, dw1, hs);
+    if (e == hipSuccess) e = launch_wgrad_reduce(w.wg, s->E, (int64_t)2 * s->d_ff * s->d, dw1, hs);
+    if (e == hipSuccess) e = gemm_dw2(*s, w.wg, w.do_perm, w.ga, dw2, hs);
+    if (e == hipSuccess) e = launch_wgrad_reduce(w.wg, s->E, (int64_t)s->d * s->d_ff, dw2, hs);
     if (e == hipSuccess) e = gemm_dx_perm(*s, *plan, pi, w.dh, w1, w.xbuf, hs);   // x_perm no longer needed
   }
   if (e == hipSuccess)

@@ -145,6 +145,55 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   }
 }
 
+// Weight-gradient chunks: expert e's reduction rows [off[e], off[e+1]) are cut
+// into ch_e = max(1, ceil(n_e / kch)) pieces of at most kch rows.  Chunk c of
+// expert e is (e, k0, k1, slot): slot -1 for c = 0 (written to the expert's
+// own gradient), else one of the expert's consecutive partial slots
+// slot_range[e] = [first, last + 1).  One block, E <= 256.
+__global__ __launch_bounds__(256) void wgrad_chunks_kernel(const int32_t* __restrict__ off, int E, int kch,
+                                                          int4* __restrict__ chunks, int32_t* __restrict__ nchunks,
+                                                          int2* __restrict__ slot_range) {
+  __shared__ int sq[256], ss[256];
+  const int e = threadIdx.x;
+  int n = 0, ch = 0;
+  if (e < E) {
+    n = off[e + 1] - off[e];
+    ch = n > 0 ? (n + kch - 1) / kch : 1;
+  }
+  sq[e] = ch;
+  ss[e] = ch > 0 ? ch - 1 : 0;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {   // inclusive scans
+    const int a = e >= o ? sq[e - o] : 0, b = e >= o ? ss[e - o] : 0;
+    __syncthreads();
+    sq[e] += a;
+    ss[e] += b;
+    __syncthreads();
+  }
+  if (e >= E) return;
+  const int q0 = sq[e] - ch, s0 = ss[e] - (ch - 1);
+  for (int c = 0; c < ch; ++c) {
+    const int k0 = off[e] + c * kch;
+    chunks[q0 + c] = int4{e, k0, min(off[e + 1], k0 + kch), c == 0 ? -1 : s0 + c - 1};
+  }
+  slot_range[e] = int2{s0, s0 + ch - 1};
+  if (e == E - 1) *nchunks = sq[e];
+}
+
+// dW[e] += partial slots of e, in slot order (fixed order: deterministic).
+__global__ __launch_bounds__(256) void wgrad_reduce_kernel(float* __restrict__ dw, const float* __restrict__ part,
+                                                          const int2* __restrict__ slot_range, int64_t mn) {
+  const int e = blockIdx.y;
+  const int2 sr = slot_range[e];
+  if (sr.y <= sr.x) return;
+  float* out = dw + (int64_t)e * mn;
+  for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; i < mn; i += (int64_t)gridDim.x * 256 * 4) {
+    f32x4 a = *reinterpret_cast<const f32x4*>(out + i);
+    for (int s = sr.x; s < sr.y; ++s) a += *reinterpret_cast<const f32x4*>(part + (int64_t)s * mn + i);
+    *reinterpret_cast<f32x4*>(out + i) = a;
+  }
+}
+
 int grid_for(int64_t work, int per_block) {
   int64_t g = (work + per_block - 1) / per_block;
   if (g > 256 * 32) g = 256 * 32;
@@ -194,6 +243,18 @@ hipError_t launch_router_bwd(const moe_shape& s, const moe_plan& p, const float*
     hipLaunchKernelGGL(router_bwd_kernel<float>, dim3(grid), dim3(256), 0, st, p.tok_ptr, p.tok_rows,
                        p.expert_of_row, p.gate_of_row, p.topk_idx, p.topk_gate, ds_part, nparts, pstride, s.T, s.E,
                        s.k, ds_out, dlogits, (float*)dzq, ldz);
+  return hipGetLastError();
+}
+
+hipError_t launch_wgrad_chunks(const int32_t* offsets, int E, int kch, const WgradChunks& w, hipStream_t st) {
+  hipLaunchKernelGGL(wgrad_chunks_kernel, dim3(1), dim3(256), 0, st, offsets, E, kch, w.chunks, w.nchunks,
+                     w.slot_range);
+  return hipGetLastError();
+}
+
+hipError_t launch_wgrad_reduce(const WgradChunks& w, int E, int64_t mn, float* dw, hipStream_t st) {
+  if (w.max_extra == 0) return hipSuccess;
+  hipLaunchKernelGGL(wgrad_reduce_kernel, dim3(256, E), dim3(256), 0, st, dw, w.part, w.slot_range, mn);
   return hipGetLastError();
 }
 

@@ -135,35 +135,38 @@ hipError_t gemm_dx_perm(const moe_shape& s, const moe_plan& p, const PlanInterna
 }
 
 // dW1_e [2f, d] = dH_e^T X_perm_e and dW2_e [d, f] = dO_perm_e^T gA_e: the
-// reduction runs over the expert's rows (variable K), fp32 outputs.
-hipError_t gemm_dw1(const moe_shape& s, const moe_plan& p, const void* dh, const void* x_perm, float* dw1,
+// reduction runs over the expert's rows (variable K, cut into chunks of at most
+// w.kch rows), fp32 outputs; chunks past an expert's first land in partial
+// slots that launch_wgrad_reduce adds afterwards.
+namespace {
+hipError_t run_wgrad(const moe_shape& s, const WgradChunks& w, Args& a, hipStream_t st) {
+  a.chunks = w.chunks; a.nchunks = w.nchunks; a.Cpart = w.part;
+  const int bn = s.act == MOE_BF16 ? 256 : 128;
+  a.tilesM = ceil_div(a.M, 128); a.tilesN = ceil_div(a.N, bn);
+  const int64_t tiles = 8 * (int64_t)ceil_div(w.max_chunks, 8) * a.tilesM * a.tilesN;
+  if (s.act == MOE_BF16) return run_dma<128, 256, 2, 4, false, false, GROUP_K, EPI_F32, 3>(a, tiles, st);
+  return run<float, 128, 128, 2, 2, false, false, GROUP_K, EPI_F32>(a, tiles, st);
+}
+}  // namespace
+
+hipError_t gemm_dw1(const moe_shape& s, const WgradChunks& w, const void* dh, const void* x_perm, float* dw1,
                     hipStream_t st) {
   Args a = base_args();
   a.A = dh; a.lda = 2 * s.d_ff;          // [K = rows, M = 2f]
   a.B = x_perm; a.ldb = s.d;             // [K = rows, N = d]
   a.C = dw1; a.ldc = s.d; a.c_estride = (int64_t)2 * s.d_ff * s.d;
-  a.offsets = p.offsets;
   a.M = 2 * s.d_ff; a.N = s.d; a.E = s.E;
-  const int bn = s.act == MOE_BF16 ? 256 : 128;
-  a.tilesM = ceil_div(a.M, 128); a.tilesN = ceil_div(a.N, bn);
-  a.total_static = s.E * a.tilesM * a.tilesN;
-  if (s.act == MOE_BF16) return run_dma<128, 256, 2, 4, false, false, GROUP_K, EPI_F32, 3>(a, a.total_static, st);
-  return run<float, 128, 128, 2, 2, false, false, GROUP_K, EPI_F32>(a, a.total_static, st);
+  return run_wgrad(s, w, a, st);
 }
 
-hipError_t gemm_dw2(const moe_shape& s, const moe_plan& p, const void* do_perm, const void* ga, float* dw2,
+hipError_t gemm_dw2(const moe_shape& s, const WgradChunks& w, const void* do_perm, const void* ga, float* dw2,
                     hipStream_t st) {
   Args a = base_args();
   a.A = do_perm; a.lda = s.d;            // [K = rows, M = d]
   a.B = ga; a.ldb = s.d_ff;              // [K = rows, N = f]
   a.C = dw2; a.ldc = s.d_ff; a.c_estride = (int64_t)s.d * s.d_ff;
-  a.offsets = p.offsets;
   a.M = s.d; a.N = s.d_ff; a.E = s.E;
-  const int bn = s.act == MOE_BF16 ? 256 : 128;
-  a.tilesM = ceil_div(a.M, 128); a.tilesN = ceil_div(a.N, bn);
-  a.total_static = s.E * a.tilesM * a.tilesN;
-  if (s.act == MOE_BF16) return run_dma<128, 256, 2, 4, false, false, GROUP_K, EPI_F32, 3>(a, a.total_static, st);
-  return run<float, 128, 128, 2, 2, false, false, GROUP_K, EPI_F32>(a, a.total_static, st);
+  return run_wgrad(s, w, a, st);
 }
 
 // ---------------------------------------------------------------- router

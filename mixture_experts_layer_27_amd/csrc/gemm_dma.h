@@ -223,7 +223,7 @@ MOE_DEV void wave_epilogue(const Args& args, const TileCtx& ctx, f32x16 (&acc)[B
     } else {
       using OT = typename std::conditional<EPI == EPI_ACT, T, float>::type;
       OT* C = reinterpret_cast<OT*>(args.C);
-      if constexpr (GROUP == GROUP_K) C += (int64_t)ctx.e * args.c_estride;
+      if constexpr (GROUP == GROUP_K) C = wgrad_out<OT>(args, ctx);
 #pragma unroll
       for (int it = 0; it < 32 * CPR / 64; ++it) {
         const int u = lane + 64 * it;

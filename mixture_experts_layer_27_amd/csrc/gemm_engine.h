@@ -43,6 +43,9 @@ struct Args {
   const int32_t* offsets;       // [E+1] segment offsets (GROUP_M rows, GROUP_K reduction rows)
   const int32_t* tile_prefix;   // [E+1] prefix of per-expert m-tile counts (GROUP_M)
   const int32_t* tile_expert;   // [prefix[E]] expert of each m-tile (GROUP_M)
+  const int4* chunks;           // GROUP_K: (expert, k_begin, k_end, partial slot or -1) per K chunk
+  const int32_t* nchunks;       // GROUP_K: number of chunks (device)
+  void* Cpart;                  // GROUP_K: partial outputs of chunks past an expert's first, stride c_estride
   const int32_t* csr_ptr; const int32_t* csr_rows; const void* gsrc; int64_t ld_gsrc;
   int M, N, K, E, f;
   int tilesM, tilesN;
@@ -230,6 +233,7 @@ struct TileCtx {
   int row_begin, row_end;   // GROUP_M: rows of A / D of this tile's expert segment
   int k_begin, k_end;       // reduction range (segment rows for GROUP_K, a K slice for split-K)
   int m0, n0;
+  int slot;                 // GROUP_K: partial-output slot of the chunk, -1 = the expert's own output
 };
 
 constexpr int kGroupM = 4;
@@ -238,13 +242,14 @@ constexpr int kGroupM = 4;
 template <int GROUP>
 MOE_DEV int total_tiles(const Args& args) {
   if constexpr (GROUP == GROUP_M) return args.tile_prefix[args.E] * args.tilesN;
+  else if constexpr (GROUP == GROUP_K) return *args.nchunks * args.tilesM * args.tilesN;
   else return args.total_static;
 }
 
 // Tile coordinates of logical tile L (0 <= L < total_tiles).
 template <int BM, int BN, int BK, int GROUP>
 MOE_DEV void decode_at(const Args& args, int L, TileCtx& c) {
-  int e = 0, mt = 0, nt = 0, split = 0;
+  int e = 0, mt = 0, nt = 0, split = 0, slot = -1;
   int row_begin = 0, row_end = 0;
   int k_begin = 0, k_end = args.K;
   if constexpr (GROUP == GROUP_M) {
@@ -264,13 +269,19 @@ MOE_DEV void decode_at(const Args& args, int L, TileCtx& c) {
     row_begin = args.offsets[e] + mt * BM;
     row_end = args.offsets[e + 1];
   } else if constexpr (GROUP == GROUP_K) {
-    int pe = args.tilesM * args.tilesN;
-    e = L / pe;
-    int r = L - e * pe;
+    // logical tile L = chunk * tiles_per_chunk + r; a chunk is a piece of at most
+    // a fixed number of one expert's rows, so tiles stay balanced however
+    // unevenly the experts are loaded
+    const int pe = args.tilesM * args.tilesN;
+    const int q = L / pe;
+    const int r = L - q * pe;
+    const int4 ch = args.chunks[q];
+    e = ch.x;
+    k_begin = ch.y;
+    k_end = ch.z;
+    slot = ch.w;
     nt = r / args.tilesM;
     mt = r - nt * args.tilesM;
-    k_begin = args.offsets[e];
-    k_end = args.offsets[e + 1];
   } else {
     int pe = args.tilesM * args.tilesN;
     split = L / pe;
@@ -285,10 +296,28 @@ MOE_DEV void decode_at(const Args& args, int L, TileCtx& c) {
   c.row_begin = row_begin; c.row_end = row_end;
   c.k_begin = k_begin; c.k_end = k_end;
   c.m0 = mt * BM; c.n0 = nt * BN;
+  c.slot = slot;
+}
+
+// Output base of a GROUP_K tile: the expert's own slab, or a partial slot.
+template <typename OT>
+MOE_DEV OT* wgrad_out(const Args& args, const TileCtx& c) {
+  return c.slot < 0 ? reinterpret_cast<OT*>(args.C) + (int64_t)c.e * args.c_estride
+                    : reinterpret_cast<OT*>(args.Cpart) + (int64_t)c.slot * args.c_estride;
 }
 
 template <int BM, int BN, int BK, int GROUP>
 MOE_DEV bool decode_tile(const Args& args, TileCtx& c) {
+  if constexpr (GROUP == GROUP_K) {
+    // chunks go round robin over the XCDs (chunk q on XCD q % 8), all tiles of a
+    // chunk on one XCD: its rows of both operands are read into one L2
+    const int pe = args.tilesM * args.tilesN;
+    const int b = blockIdx.x, t = b >> 3;
+    const int q = (b & 7) + 8 * (t / pe);
+    if (q >= *args.nchunks) return false;
+    decode_at<BM, BN, BK, GROUP>(args, q * pe + t % pe, c);
+    return true;
+  }
   const int total = total_tiles<GROUP>(args);
   const int per = (total + 7) >> 3;
   const int b = blockIdx.x;
@@ -423,7 +452,7 @@ MOE_DEV void gemm_epilogue(const Args& args, const TileCtx& ctx, f32x16 (&acc)[B
       // EPI_ACT (act dtype), EPI_F32 (fp32, split-K partials / per-expert slabs), EPI_LOGITS (+ bias)
       using OT = typename std::conditional<EPI == EPI_ACT, T, float>::type;
       OT* C = reinterpret_cast<OT*>(args.C);
-      if constexpr (GROUP == GROUP_K) C += (int64_t)e * args.c_estride;
+      if constexpr (GROUP == GROUP_K) C = wgrad_out<OT>(args, ctx);
       if constexpr (GROUP == GROUP_NONE) C += (int64_t)split * args.c_kstride;
       for (int u = threadIdx.x; u < WTM * CPR; u += NT) {
         const int rr = u / CPR, ch = u % CPR;

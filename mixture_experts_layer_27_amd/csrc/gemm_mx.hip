@@ -101,19 +101,21 @@ hipError_t gemm_mx_dx_perm(const moe_shape& s, const moe_plan& p, const PlanInte
 }
 
 // dW_e [M, N] = sum over the expert's (64-padded) token positions of lhs x rhs;
-// lhs codes [M][P], rhs codes [N][P], both quantised along the token axis.
-hipError_t gemm_mx_wgrad(const moe_shape& s, const int32_t* pad_off, int64_t P, const MxOperand& lhs, int M,
+// lhs codes [M][P], rhs codes [N][P], both quantised along the token axis.  The
+// positions are cut into chunks (w, built from the padded offsets) as in the
+// bf16 weight gradients.
+hipError_t gemm_mx_wgrad(const moe_shape& s, const WgradChunks& w, int64_t P, const MxOperand& lhs, int M,
                          const MxOperand& rhs, int N, float* dw, hipStream_t st) {
   Args a = base_args();
   a.A = lhs.codes; a.lda = P;
   a.B = rhs.codes; a.ldb = P;
   a.C = dw; a.ldc = N; a.c_estride = (int64_t)M * N;
-  a.offsets = pad_off;
+  a.chunks = w.chunks; a.nchunks = w.nchunks; a.Cpart = w.part;
   a.M = M; a.N = N; a.E = s.E;
   a.tilesM = ceil_div(M, 128); a.tilesN = ceil_div(N, 256);
-  a.total_static = s.E * a.tilesM * a.tilesN;
+  const int64_t tiles = 8 * (int64_t)ceil_div(w.max_chunks, 8) * a.tilesM * a.tilesN;
   MxArgs m{lhs.scales, lhs.srows, nullptr, rhs.scales, rhs.srows, 0};
-  return run_mx<GROUP_K, EPI_F32>(a, m, a.total_static, st);
+  return run_mx<GROUP_K, EPI_F32>(a, m, tiles, st);
 }
 
 }  // namespace moe

@@ -39,6 +39,17 @@ hipError_t launch_plan_build(const moe_shape& s, const moe_plan& p, const PlanIn
 hipError_t launch_round_select(const moe_shape& s, const moe_plan& p, const PlanInternal& pi,
                                hipStream_t st);
 
+// Weight-gradient K chunks (see wgrad_chunks_kernel): tables in the backward
+// workspace, partial outputs for chunks past each expert's first.
+struct WgradChunks {
+  int4* chunks;          // [max_chunks]
+  int32_t* nchunks;      // [1]
+  int2* slot_range;      // [E]
+  float* part;           // [max_extra][largest weight gradient]
+  int kch;               // rows per chunk (a multiple of 64)
+  int max_chunks, max_extra;
+};
+
 // ---- elementwise (elementwise.hip)
 // dst[r] = src[token_of_row[r]] for every routed row r
 hipError_t launch_permute_rows(const moe_shape& s, const void* src, const moe_plan& p, void* dst, hipStream_t st);
@@ -47,6 +58,8 @@ hipError_t launch_combine(const moe_shape& s, const void* y, const moe_plan& p, 
 hipError_t launch_router_bwd(const moe_shape& s, const moe_plan& p, const float* ds_part, int nparts,
                              float* ds_out, float* dlogits, void* dzq, int ldz, hipStream_t st);
 hipError_t launch_splitk_reduce(const float* part, int nsplit, int64_t n, float* out, hipStream_t st);
+hipError_t launch_wgrad_chunks(const int32_t* offsets, int E, int kch, const WgradChunks& w, hipStream_t st);
+hipError_t launch_wgrad_reduce(const WgradChunks& w, int E, int64_t mn, float* dw, hipStream_t st);
 
 // ---- grouped GEMMs (gemm.hip)
 struct GemmPlanView {
@@ -63,9 +76,9 @@ hipError_t gemm_dact(const moe_shape& s, const moe_plan& p, const PlanInternal& 
 int gemm_dact_parts(const moe_shape& s);
 hipError_t gemm_dx_perm(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const void* dh,
                         const void* w1, void* dx_perm, hipStream_t st);
-hipError_t gemm_dw1(const moe_shape& s, const moe_plan& p, const void* dh, const void* x_perm, float* dw1,
+hipError_t gemm_dw1(const moe_shape& s, const WgradChunks& w, const void* dh, const void* x_perm, float* dw1,
                     hipStream_t st);
-hipError_t gemm_dw2(const moe_shape& s, const moe_plan& p, const void* do_perm, const void* ga, float* dw2,
+hipError_t gemm_dw2(const moe_shape& s, const WgradChunks& w, const void* do_perm, const void* ga, float* dw2,
                     hipStream_t st);
 hipError_t gemm_router_logits(const moe_shape& s, const void* x, const void* wg, const float* bias,
                               float* logits, hipStream_t st);
@@ -106,7 +119,7 @@ hipError_t gemm_mx_dact(const moe_shape& s, const moe_plan& p, const PlanInterna
                         const MxOperand& w2t, const void* h, void* dh, void* ga, float* ds_part, hipStream_t st);
 hipError_t gemm_mx_dx_perm(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const MxOperand& dh,
                            const MxOperand& w1t, void* dx_perm, hipStream_t st);
-hipError_t gemm_mx_wgrad(const moe_shape& s, const int32_t* pad_off, int64_t P, const MxOperand& lhs, int M,
+hipError_t gemm_mx_wgrad(const moe_shape& s, const WgradChunks& w, int64_t P, const MxOperand& lhs, int M,
                          const MxOperand& rhs, int N, float* dw, hipStream_t st);
 
 }  // namespace moe
