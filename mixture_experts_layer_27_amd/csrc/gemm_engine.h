@@ -280,8 +280,9 @@ MOE_DEV void decode_at(const Args& args, int L, TileCtx& c) {
     k_begin = ch.y;
     k_end = ch.z;
     slot = ch.w;
-    nt = r / args.tilesM;
-    mt = r - nt * args.tilesM;
+    // n-tile fastest: consecutive tiles write one contiguous band of output rows
+    mt = r / args.tilesN;
+    nt = r - mt * args.tilesN;
   } else {
     int pe = args.tilesM * args.tilesN;
     split = L / pe;
@@ -437,14 +438,22 @@ MOE_DEV void gemm_epilogue(const Args& args, const TileCtx& ctx, f32x16 (&acc)[B
         const int col = n0 + ch * 8;
         if (t >= args.M || col >= args.N) continue;
         const float* src = cs + rr * CS + ch * 8;
-        float v[8], w[8];
+        float v[8];
 #pragma unroll
         for (int c = 0; c < 8; ++c) v[c] = src[c];
         const int p0 = args.csr_ptr[t], p1 = args.csr_ptr[t + 1];
-        for (int p = p0; p < p1; ++p) {
-          Vec8<T>::load(G + (int64_t)args.csr_rows[p] * args.ld_gsrc + col, w);
+        for (int pb = p0; pb < p1; pb += 4) {
+          // up to four rows in flight, added in ascending row order
+          float w4[4][8];
 #pragma unroll
-          for (int c = 0; c < 8; ++c) v[c] += w[c];
+          for (int q = 0; q < 4; ++q)
+            if (pb + q < p1) Vec8<T>::load(G + (int64_t)args.csr_rows[pb + q] * args.ld_gsrc + col, w4[q]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (pb + q < p1) {
+#pragma unroll
+              for (int c = 0; c < 8; ++c) v[c] += w4[q][c];
+            }
         }
         Vec8<T>::store(C + (int64_t)t * args.ldc + col, v);
       }
