@@ -207,26 +207,34 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(int E, int nblk, int32_
   const int total = block_scan_inplace(hist, (int64_t)E * nblk, sh);
   const int toks = block_scan_inplace(blk_tok, nblk, sh);
   if (threadIdx.x == 0) blk_tok[nblk] = toks;
-  for (int e = threadIdx.x; e < E; e += 1024) {
-    int o = hist[(int64_t)e * nblk];
-    int o1 = (e + 1 < E) ? hist[(int64_t)(e + 1) * nblk] : total;
+  // one thread per expert (E <= 256 < 1024)
+  const int e = threadIdx.x;
+  int cnt = 0;
+  if (e < E) {
+    const int o = hist[(int64_t)e * nblk];
+    const int o1 = (e + 1 < E) ? hist[(int64_t)(e + 1) * nblk] : total;
+    cnt = o1 - o;
     offsets[e] = o;
-    counts[e] = o1 - o;
-    if (counts_raw) counts_raw[e] = o1 - o;
+    counts[e] = cnt;
+    if (counts_raw) counts_raw[e] = cnt;
   }
-  if (threadIdx.x == 0) offsets[E] = total;
+  if (e == 0) offsets[E] = total;
+  // 128-row m-tile prefix over the experts (block scan), then each expert's tiles
+  const int tiles = (cnt + 127) / 128;
+  sh[e] = tiles;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int a = 0;
-    for (int e = 0; e < E; ++e) {
-      pre128[e] = a;
-      a += (counts[e] + 127) / 128;
-    }
-    pre128[E] = a;
+  for (int o = 1; o < 1024; o <<= 1) {
+    const int v = (e >= o) ? sh[e - o] : 0;
+    __syncthreads();
+    sh[e] += v;
+    __syncthreads();
   }
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += 1024)
-    for (int j = pre128[e]; j < pre128[e + 1]; ++j) tile_e[j] = e;
+  if (e < E) {
+    const int p0 = sh[e] - tiles;
+    pre128[e] = p0;
+    if (e == E - 1) pre128[E] = sh[e];
+    for (int j = 0; j < tiles; ++j) tile_e[p0 + j] = e;
+  }
 }
 
 __global__ __launch_bounds__(256) void plan_scatter_kernel(
