@@ -175,7 +175,7 @@ size_t carve_fwd(const moe_shape& s, char* base, FwdWs* w) {
   Carver c{base};
   const int64_t N = max_rows(s);
   FwdWs q{};
-  q.act = c.take<char>((size_t)N * s.d_ff * esz(s));
+  if (s.gemm != MOE_MXFP8) q.act = c.take<char>((size_t)N * s.d_ff * esz(s));   // MXFP8: A only as codes
   if (s.gemm == MOE_MXFP8) {
     const int64_t E = s.E, d = s.d, f = s.d_ff, P = tok_cap(s);
     q.pad_off = c.take<int32_t>((E + 1) * 4);
@@ -306,9 +306,7 @@ moe_status moe_grouped_gemm_swiglu(const moe_shape* s, const void* x_perm, const
     if (e == hipSuccess)
       e = mx_quantize_rows_padded(x_perm, N, d, off, eor, w.pad_off, E, w.x.codes, w.x.scales, w.x.srows, hs);
     if (e == hipSuccess) e = mx_quantize_rows_staged(w1, (int64_t)E * 2 * f, d, w.w1.codes, w.w1.scales, w.w1.srows, hs);
-    if (e == hipSuccess) e = gemm_mx_up_swiglu(*s, *plan, pi, w.x, w.w1, h_saved, w.act, hs);
-    if (e == hipSuccess)
-      e = mx_quantize_rows_padded(w.act, N, f, off, eor, w.pad_off, E, w.a.codes, w.a.scales, w.a.srows, hs);
+    if (e == hipSuccess) e = gemm_mx_up_swiglu(*s, *plan, pi, w.x, w.w1, h_saved, w.a, hs);
     if (e == hipSuccess) e = mx_quantize_rows_staged(w2, (int64_t)E * d, f, w.w2.codes, w.w2.scales, w.w2.srows, hs);
     if (e == hipSuccess) e = gemm_mx_down(*s, *plan, pi, w.a, w.w2, y, hs);
     return hip_status(e);
@@ -352,9 +350,7 @@ moe_status moe_backward(const moe_shape* s, const void* x, const void* w_gate, c
     if (e == hipSuccess)
       e = mx_quantize_rows_padded(w.do_perm, N, d, off, eor, w.pad_off, E, w.doq.codes, w.doq.scales, w.doq.srows, hs);
     if (e == hipSuccess) e = mx_quantize_cols(w2, E, d, f, w.w2t.codes, w.w2t.scales, hs);
-    if (e == hipSuccess) e = gemm_mx_dact(*s, *plan, pi, w.doq, w.w2t, h_saved, w.dh, w.ga, w.ds_part, hs);
-    if (e == hipSuccess)
-      e = mx_quantize_rows_padded(w.dh, N, 2 * f, off, eor, w.pad_off, E, w.dhq.codes, w.dhq.scales, w.dhq.srows, hs);
+    if (e == hipSuccess) e = gemm_mx_dact(*s, *plan, pi, w.doq, w.w2t, h_saved, w.dh, w.dhq, w.ga, w.ds_part, hs);
     if (e == hipSuccess) e = mx_quantize_cols(w1, E, 2 * f, d, w.w1t.codes, w.w1t.scales, hs);
     if (e == hipSuccess) e = launch_permute_rows(*s, x, *plan, w.xbuf, hs);
     if (e == hipSuccess) e = mx_quantize_tokens(w.dh, 2 * f, plan->offsets, w.pad_off, E, P, w.dh_t.codes, w.dh_t.scales, hs);

@@ -24,6 +24,7 @@
 // places there; masked lanes (rows past a segment) fetch a zero block.
 #pragma once
 #include "gemm_engine.h"
+#include "mx_codes.h"
 
 namespace moe_gemm {
 
@@ -156,8 +157,9 @@ MOE_DEV void wave_epilogue(const Args& args, const TileCtx& ctx, f32x16 (&acc)[B
       for (int q = 0; q < 16; ++q)
         slab[(8 * (q >> 2) + 4 * (lane >> 5) + (q & 3)) * SS + j * 32 + (lane & 31)] = acc[i][j][q];
     __builtin_amdgcn_s_waitcnt(0xc07f);          // lgkmcnt(0): the slab is written (one wave, in order)
-    if constexpr (EPI == EPI_SWIGLU) {
+    if constexpr (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_MX) {
       constexpr int HC = CPR / 2;
+      static_assert(EPI != EPI_SWIGLU_MX || HC == 4, "one 32-column block of A per wave row");
       T* H = reinterpret_cast<T*>(args.C);
       T* Aout = reinterpret_cast<T*>(args.C2);
 #pragma unroll
@@ -165,7 +167,7 @@ MOE_DEV void wave_epilogue(const Args& args, const TileCtx& ctx, f32x16 (&acc)[B
         const int u = lane + 64 * it;
         const int rr = u / HC, ch = u % HC;
         const int grow = rbase + i * 32 + rr;
-        if (grow >= ctx.row_end) continue;
+        const bool ok = grow < ctx.row_end;   // uniform over the HC lanes of a row
         const float* src = slab + rr * SS + ch * 8;
         float hg[8], hu[8], a[8];
 #pragma unroll
@@ -175,13 +177,35 @@ MOE_DEV void wave_epilogue(const Args& args, const TileCtx& ctx, f32x16 (&acc)[B
           a[c] = hg[c] * fast_sigmoid(hg[c]) * hu[c];
         }
         const int gcol = ctx.nt * (BN / 2) + wn * (WTN / 2) + ch * 8;
-        T* hrow = H + (int64_t)grow * args.ldc;
-        Vec8<T>::store(hrow + gcol, hg);
-        Vec8<T>::store(hrow + args.f + gcol, hu);
-        Vec8<T>::store(Aout + (int64_t)grow * args.ldc2 + gcol, a);
+        if (ok) {
+          T* hrow = H + (int64_t)grow * args.ldc;
+          Vec8<T>::store(hrow + gcol, hg);
+          Vec8<T>::store(hrow + args.f + gcol, hu);
+        }
+        if constexpr (EPI == EPI_SWIGLU_MX) {
+          // A as the forward stores it (bf16), quantised along f: this row's 32
+          // columns of the wave are one block held by a lane quad
+          float amax = 0.0f;
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            a[c] = Vec8<T>::rnd(a[c]);
+            amax = fmaxf(amax, fabsf(a[c]));
+          }
+          amax = quad_max(amax);
+          if (ok) {
+            const int X = mx_exponent(amax);
+            const int64_t prow = grow + (int64_t)args.q_pad[ctx.e] - args.offsets[ctx.e];
+            *reinterpret_cast<uint2*>(args.q_codes + prow * args.q_ld + gcol) = e4m3_8(a, pow2f(-X));
+            if (ch == 0)
+              args.q_scales[((gcol >> 6) * args.q_srows + prow) * 2 + ((gcol >> 5) & 1)] = (uint8_t)(X + 127);
+          }
+        } else {
+          if (ok) Vec8<T>::store(Aout + (int64_t)grow * args.ldc2 + gcol, a);
+        }
       }
-    } else if constexpr (EPI == EPI_DSWIGLU) {
+    } else if constexpr (EPI == EPI_DSWIGLU || EPI == EPI_DSWIGLU_MX) {
       static_assert(CPR <= 64 && (32 * CPR) % 64 == 0, "row reduction inside one wave");
+      static_assert(EPI != EPI_DSWIGLU_MX || CPR % 4 == 0, "lane quads hold 32-column blocks");
       const T* Hs = reinterpret_cast<const T*>(args.aux);
       T* dH = reinterpret_cast<T*>(args.C);
       T* gA = reinterpret_cast<T*>(args.C2);
@@ -192,11 +216,15 @@ MOE_DEV void wave_epilogue(const Args& args, const TileCtx& ctx, f32x16 (&acc)[B
         const int grow = rbase + i * 32 + rr;
         const int col = cbase + ch * 8;
         float part = 0.0f;
-        if (grow < ctx.row_end && col < args.N) {
+        const bool ok = grow < ctx.row_end && col < args.N;   // uniform over each lane quad
+        float dhg[8], dhu[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) dhg[c] = dhu[c] = 0.0f;
+        if (ok) {
           const float* src = slab + rr * SS + ch * 8;
           const float g = args.row_gate[grow];
           const T* hrow = Hs + (int64_t)grow * args.ld_aux;
-          float hg[8], hu[8], dhg[8], dhu[8], ga[8];
+          float hg[8], hu[8], ga[8];
           Vec8<T>::load(hrow + col, hg);
           Vec8<T>::load(hrow + args.f + col, hu);
 #pragma unroll
@@ -215,6 +243,32 @@ MOE_DEV void wave_epilogue(const Args& args, const TileCtx& ctx, f32x16 (&acc)[B
           Vec8<T>::store(drow + col, dhg);
           Vec8<T>::store(drow + args.f + col, dhu);
           Vec8<T>::store(gA + (int64_t)grow * args.ldc2 + col, ga);
+        }
+        if constexpr (EPI == EPI_DSWIGLU_MX) {
+          // dH as stored (bf16), quantised along 2f: gate columns col.. and up
+          // columns f + col.., each lane quad one 32-column block of each
+          float mg = 0.0f, mu = 0.0f;
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            dhg[c] = Vec8<T>::rnd(dhg[c]);
+            dhu[c] = Vec8<T>::rnd(dhu[c]);
+            mg = fmaxf(mg, fabsf(dhg[c]));
+            mu = fmaxf(mu, fabsf(dhu[c]));
+          }
+          mg = quad_max(mg);
+          mu = quad_max(mu);
+          if (ok) {
+            const int Xg = mx_exponent(mg), Xu = mx_exponent(mu);
+            const int64_t prow = grow + (int64_t)args.q_pad[ctx.e] - args.offsets[ctx.e];
+            uint8_t* crow = args.q_codes + prow * args.q_ld;
+            *reinterpret_cast<uint2*>(crow + col) = e4m3_8(dhg, pow2f(-Xg));
+            *reinterpret_cast<uint2*>(crow + args.f + col) = e4m3_8(dhu, pow2f(-Xu));
+            if ((ch & 3) == 0) {
+              const int kg = col, ku = args.f + col;
+              args.q_scales[((kg >> 6) * args.q_srows + prow) * 2 + ((kg >> 5) & 1)] = (uint8_t)(Xg + 127);
+              args.q_scales[((ku >> 6) * args.q_srows + prow) * 2 + ((ku >> 5) & 1)] = (uint8_t)(Xu + 127);
+            }
+          }
         }
 #pragma unroll
         for (int o = 1; o < CPR; o <<= 1) part += __shfl_xor(part, o, 64);

@@ -29,7 +29,8 @@
 namespace moe_gemm {
 
 enum { GROUP_M = 0, GROUP_K = 1, GROUP_NONE = 2 };
-enum { EPI_ACT = 0, EPI_F32 = 1, EPI_SWIGLU = 2, EPI_DSWIGLU = 3, EPI_LOGITS = 4, EPI_DX = 5 };
+enum { EPI_ACT = 0, EPI_F32 = 1, EPI_SWIGLU = 2, EPI_DSWIGLU = 3, EPI_LOGITS = 4, EPI_DX = 5,
+       EPI_SWIGLU_MX = 6, EPI_DSWIGLU_MX = 7 };   // *_MX: also emit an MXFP8 copy of A / dH
 
 struct Args {
   const void* A; int64_t lda; int64_t a_estride; const int32_t* a_gather;
@@ -46,6 +47,9 @@ struct Args {
   const int4* chunks;           // GROUP_K: (expert, k_begin, k_end, partial slot or -1) per K chunk
   const int32_t* nchunks;       // GROUP_K: number of chunks (device)
   void* Cpart;                  // GROUP_K: partial outputs of chunks past an expert's first, stride c_estride
+  // *_MX epilogues: MXFP8 codes [rows][q_ld] and stage-major scales [q_ld/64][q_srows][2] of the
+  // quantised output, rows expert-padded (row r of expert e at r - offsets[e] + q_pad[e])
+  uint8_t* q_codes; uint8_t* q_scales; int64_t q_ld; int64_t q_srows; const int32_t* q_pad;
   const int32_t* csr_ptr; const int32_t* csr_rows; const void* gsrc; int64_t ld_gsrc;
   int M, N, K, E, f;
   int tilesM, tilesN;

@@ -93,7 +93,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_mx(Args args, MxArgs
     }
   };
   auto b_jrow = [&](int row) -> int64_t {   // row inside this expert's B matrix
-    if constexpr (EPI == EPI_SWIGLU) {
+    if constexpr (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_MX) {
       const int w = row / WTN, jj = row % WTN;
       const int g = nt * (BN / 2) + w * (WTN / 2) + (jj % (WTN / 2));
       return (jj < WTN / 2) ? g : (args.f + g);
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_mx(Args args, MxArgs
   } else if (lane < BM / 8 + BN / 8) {
     const int row = (lane - BM / 8) * 8;
     int64_t j;
-    if constexpr (EPI == EPI_SWIGLU) {
+    if constexpr (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_MX) {
       j = b_jrow(row);
     } else {
       j = n0 + row;

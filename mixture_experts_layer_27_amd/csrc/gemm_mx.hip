@@ -42,17 +42,18 @@ int64_t m_tiles(const moe_shape& s) { return (max_rows(s) + 127) / 128 + s.E; }
 }  // namespace
 
 hipError_t gemm_mx_up_swiglu(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const MxOperand& x,
-                             const MxOperand& w1, void* h, void* act, hipStream_t st) {
+                             const MxOperand& w1, void* h, const MxOperand& act, hipStream_t st) {
   Args a = base_args();
   a.A = x.codes; a.lda = s.d;
   a.B = w1.codes; a.ldb = s.d; a.b_estride = (int64_t)2 * s.d_ff * s.d;
   a.C = h; a.ldc = 2 * s.d_ff;
-  a.C2 = act; a.ldc2 = s.d_ff;
+  // A is only needed as the down GEMM's operand: the epilogue writes it in MXFP8
+  a.q_codes = act.codes; a.q_scales = act.scales; a.q_ld = s.d_ff; a.q_srows = act.srows; a.q_pad = act.pad;
   a.offsets = p.offsets;
   a.N = 2 * s.d_ff; a.K = s.d; a.E = s.E; a.f = s.d_ff;
   a.tile_prefix = pi.prefix128; a.tile_expert = pi.tile_e128; a.tilesN = a.N / 256;
   MxArgs m{x.scales, x.srows, x.pad, w1.scales, w1.srows, 2 * (int64_t)s.d_ff};
-  return run_mx<GROUP_M, EPI_SWIGLU>(a, m, m_tiles(s) * a.tilesN, st);
+  return run_mx<GROUP_M, EPI_SWIGLU_MX>(a, m, m_tiles(s) * a.tilesN, st);
 }
 
 hipError_t gemm_mx_down(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const MxOperand& act,
@@ -70,7 +71,8 @@ hipError_t gemm_mx_down(const moe_shape& s, const moe_plan& p, const PlanInterna
 
 // w2t: W2 quantised along d, stored [E][f][d]
 hipError_t gemm_mx_dact(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const MxOperand& dout,
-                        const MxOperand& w2t, const void* h, void* dh, void* ga, float* ds_part, hipStream_t st) {
+                        const MxOperand& w2t, const void* h, void* dh, const MxOperand& dhq, void* ga, float* ds_part,
+                        hipStream_t st) {
   Args a = base_args();
   a.A = dout.codes; a.lda = s.d;
   a.B = w2t.codes; a.ldb = s.d; a.b_estride = (int64_t)s.d_ff * s.d;
@@ -82,8 +84,10 @@ hipError_t gemm_mx_dact(const moe_shape& s, const moe_plan& p, const PlanInterna
   a.offsets = p.offsets;
   a.N = s.d_ff; a.K = s.d; a.E = s.E; a.f = s.d_ff;
   a.tile_prefix = pi.prefix128; a.tile_expert = pi.tile_e128; a.tilesN = ceil_div(a.N, 256);
+  // dH also in MXFP8 along 2f for the dX_perm GEMM
+  a.q_codes = dhq.codes; a.q_scales = dhq.scales; a.q_ld = 2 * s.d_ff; a.q_srows = dhq.srows; a.q_pad = dhq.pad;
   MxArgs m{dout.scales, dout.srows, dout.pad, w2t.scales, w2t.srows, (int64_t)s.d_ff};
-  return run_mx<GROUP_M, EPI_DSWIGLU>(a, m, m_tiles(s) * a.tilesN, st);
+  return run_mx<GROUP_M, EPI_DSWIGLU_MX>(a, m, m_tiles(s) * a.tilesN, st);
 }
 
 // w1t: W1 quantised along 2f, stored [E][d][2f]

@@ -112,11 +112,12 @@ hipError_t mx_quantize_tokens(const void* src, int C, const int32_t* seg_off, co
                               int64_t P, uint8_t* codes, uint8_t* scales, hipStream_t st);
 hipError_t mx_pad_offsets(const int32_t* offsets, int E, int32_t* pad_off, hipStream_t st);
 hipError_t gemm_mx_up_swiglu(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const MxOperand& x,
-                             const MxOperand& w1, void* h, void* act, hipStream_t st);
+                             const MxOperand& w1, void* h, const MxOperand& act, hipStream_t st);
 hipError_t gemm_mx_down(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const MxOperand& act,
                         const MxOperand& w2, void* y, hipStream_t st);
 hipError_t gemm_mx_dact(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const MxOperand& dout,
-                        const MxOperand& w2t, const void* h, void* dh, void* ga, float* ds_part, hipStream_t st);
+                        const MxOperand& w2t, const void* h, void* dh, const MxOperand& dhq, void* ga, float* ds_part,
+                        hipStream_t st);
 hipError_t gemm_mx_dx_perm(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const MxOperand& dh,
                            const MxOperand& w1t, void* dx_perm, hipStream_t st);
 hipError_t gemm_mx_wgrad(const moe_shape& s, const WgradChunks& w, int64_t P, const MxOperand& lhs, int M,
