@@ -160,13 +160,19 @@ moe_status moe_backward(const moe_shape *s, const void *x, const void *w_gate, c
                         float *dlogits, float *ds, void *ws, size_t ws_bytes, void *stream);
 
 /* MXFP8 quantiser (OCP Microscaling v1.0; the pages only name the format):
- * blocks of 32 consecutive values along a row; shared exponent
+ * blocks of 32 consecutive values along the reduction axis; shared exponent
  * X = floor(log2(max|v|)) - 8 clamped to [-127,127] (-127 for an all-zero
  * block); scale byte = X + 127; element = v / 2^X rounded to nearest-even
- * E4M3 (bias 7, max 448), saturating, sign bit kept.
- *   src [rows, cols] bf16 with cols % 32 == 0; codes [rows, cols] u8;
- *   scales [rows, cols/32] u8. */
-moe_status moe_quantize_mx(const void *src_bf16, int64_t rows, int64_t cols, uint8_t *codes,
+ * E4M3 (bias 7, max 448), saturating, sign bit kept.  This is the hook that
+ * exposes the two quantisers the MXFP8 GEMMs use:
+ *   k_axis = 1: blocks along each row.  src [rows, cols] bf16, cols % 32 == 0;
+ *     codes [rows, cols] u8; scales [rows, cols/32] u8.
+ *   k_axis = 0: blocks down each column, written transposed (K-contiguous, as
+ *     the GEMMs read a weight used along its first axis).  rows % 64 == 0 and
+ *     cols % 64 == 0; codes [cols, rows] u8; scales [cols, rows/32] u8.
+ * Errors: MOE_EINVAL for null/misaligned pointers, sizes <= 0 or not matching
+ * the rules above, or k_axis not 0/1. */
+moe_status moe_quantize_mx(const void *src_bf16, int64_t rows, int64_t cols, int k_axis, uint8_t *codes,
                            uint8_t *scales, void *stream);
 
 const char *moe_status_str(moe_status st);

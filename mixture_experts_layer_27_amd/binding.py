@@ -56,7 +56,7 @@ for name, res, args in [
     ("moe_unpermute_combine", ctypes.c_int, [_P_SHAPE, _vp, _P_PLAN, _vp, _vp]),
     ("moe_backward", ctypes.c_int, [_P_SHAPE, _vp, _vp, _vp, _vp, _P_PLAN, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                     _vp, _vp, _sz, _vp]),
-    ("moe_quantize_mx", ctypes.c_int, [_vp, _i64, _i64, _vp, _vp, _vp]),
+    ("moe_quantize_mx", ctypes.c_int, [_vp, _i64, _i64, ctypes.c_int, _vp, _vp, _vp]),
     ("moe_status_str", ctypes.c_char_p, [ctypes.c_int]),
 ]:
     fn = getattr(_lib, name)
@@ -199,9 +199,11 @@ def backward(s: MoeShape, x, w_gate, w1, w2, plan: Plan, h_saved, dout, dx, dw_g
                              _ptr(dlogits), _ptr(ds), _ptr(ws), ws.numel(), _stream(stream)))
 
 
-def quantize_mx(src, codes, scales, stream=None):
+def quantize_mx(src, codes, scales, k_axis=1, stream=None):
+    """MXFP8 codes/scales of src [rows, cols] bf16 along k_axis (1: rows, 0: columns,
+    written transposed [cols, rows])."""
     rows, cols = src.shape
-    _check("moe_quantize_mx", _lib.moe_quantize_mx(_ptr(src), rows, cols, _ptr(codes), _ptr(scales),
+    _check("moe_quantize_mx", _lib.moe_quantize_mx(_ptr(src), rows, cols, k_axis, _ptr(codes), _ptr(scales),
                                                    _stream(stream)))
 
 

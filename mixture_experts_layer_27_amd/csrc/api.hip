@@ -382,11 +382,17 @@ moe_status moe_backward(const moe_shape* s, const void* x, const void* w_gate, c
   return hip_status(e);
 }
 
-moe_status moe_quantize_mx(const void* src_bf16, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
-                           void* stream) {
+moe_status moe_quantize_mx(const void* src_bf16, int64_t rows, int64_t cols, int k_axis, uint8_t* codes,
+                           uint8_t* scales, void* stream) {
   if (!aligned(src_bf16) || !aligned(codes) || !scales) return MOE_EINVAL;
-  if (rows <= 0 || cols <= 0 || cols % 32) return MOE_EINVAL;
-  return hip_status(launch_quantize_rows(src_bf16, rows, cols, codes, scales, reinterpret_cast<hipStream_t>(stream)));
+  if (rows <= 0 || cols <= 0 || (k_axis != 0 && k_axis != 1)) return MOE_EINVAL;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (k_axis == 1) {
+    if (cols % 32) return MOE_EINVAL;
+    return hip_status(launch_quantize_rows(src_bf16, rows, cols, codes, scales, hs));
+  }
+  if (rows % 64 || cols % 64 || rows > (1 << 30) || cols > (1 << 30)) return MOE_EINVAL;
+  return hip_status(launch_quantize_cols_plain(src_bf16, (int)rows, (int)cols, codes, scales, hs));
 }
 
 const char* moe_status_str(moe_status st) {

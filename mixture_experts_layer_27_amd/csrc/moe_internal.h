@@ -108,6 +108,8 @@ hipError_t mx_quantize_rows_padded(const void* src, int64_t rows, int64_t K, con
                                    const int32_t* expert_of_row, const int32_t* pad_off, int E, uint8_t* codes,
                                    uint8_t* scales, int64_t srows, hipStream_t st);
 hipError_t mx_quantize_cols(const void* src, int G, int R, int C, uint8_t* codes, uint8_t* scales, hipStream_t st);
+// the same with plain scales [C][R/32] (test hook)
+hipError_t launch_quantize_cols_plain(const void* src, int R, int C, uint8_t* codes, uint8_t* scales, hipStream_t st);
 hipError_t mx_quantize_tokens(const void* src, int C, const int32_t* seg_off, const int32_t* pad_off, int E,
                               int64_t P, uint8_t* codes, uint8_t* scales, hipStream_t st);
 hipError_t mx_pad_offsets(const int32_t* offsets, int E, int32_t* pad_off, hipStream_t st);

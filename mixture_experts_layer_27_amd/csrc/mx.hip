@@ -91,11 +91,12 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const bf16_t* __rest
 //     pad_off[e] a multiple of 64; position p maps to source row
 //     seg_off[e] + (p - pad_off[e]) when that is inside the segment, else 0.
 //     out codes [C][P], scales [P/64][C][2], P = the padded capacity.
+// plain_scales (columns mode, test hook): scales [G*C][R/32] instead.
 __global__ __launch_bounds__(256) void quantize_t_kernel(const bf16_t* __restrict__ src, int G, int R, int C,
                                                         const int32_t* __restrict__ seg_off,
                                                         const int32_t* __restrict__ pad_off, int E,
                                                         uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                                                        int64_t P) {
+                                                        int64_t P, int plain_scales) {
   __shared__ float tile[128][65];
   const int c0 = blockIdx.x * 64;
   const int64_t p0 = (int64_t)blockIdx.y * 128;
@@ -164,7 +165,8 @@ __global__ __launch_bounds__(256) void quantize_t_kernel(const bf16_t* __restric
     const uint2 lo = e4m3_8(v + 16 * h, inv), hi2 = e4m3_8(v + 16 * h + 8, inv);
     *reinterpret_cast<u32x4*>(cp + 16 * h) = u32x4{lo.x, lo.y, hi2.x, hi2.y};
   }
-  scales[((pb >> 6) * srows + crow) * 2 + ((pb >> 5) & 1)] = (uint8_t)(X + 127);
+  if (plain_scales) scales[crow * (len / 32) + (pb >> 5)] = (uint8_t)(X + 127);
+  else scales[((pb >> 6) * srows + crow) * 2 + ((pb >> 5) & 1)] = (uint8_t)(X + 127);
 }
 
 // pad_off[e] = sum over experts j < e of count_j rounded up to 64 (E <= 256)
@@ -220,14 +222,20 @@ hipError_t mx_quantize_rows_padded(const void* src, int64_t rows, int64_t K, con
 
 hipError_t mx_quantize_cols(const void* src, int G, int R, int C, uint8_t* codes, uint8_t* scales, hipStream_t st) {
   hipLaunchKernelGGL(quantize_t_kernel, dim3(C / 64, (R + 127) / 128, G), dim3(256), 0, st, (const bf16_t*)src, G, R, C,
-                     (const int32_t*)nullptr, (const int32_t*)nullptr, 0, codes, scales, (int64_t)0);
+                     (const int32_t*)nullptr, (const int32_t*)nullptr, 0, codes, scales, (int64_t)0, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_cols_plain(const void* src, int R, int C, uint8_t* codes, uint8_t* scales, hipStream_t st) {
+  hipLaunchKernelGGL(quantize_t_kernel, dim3(C / 64, (R + 127) / 128, 1), dim3(256), 0, st, (const bf16_t*)src, 1, R,
+                     C, (const int32_t*)nullptr, (const int32_t*)nullptr, 0, codes, scales, (int64_t)0, 1);
   return hipGetLastError();
 }
 
 hipError_t mx_quantize_tokens(const void* src, int C, const int32_t* seg_off, const int32_t* pad_off, int E,
                               int64_t P, uint8_t* codes, uint8_t* scales, hipStream_t st) {
   hipLaunchKernelGGL(quantize_t_kernel, dim3(C / 64, (unsigned)((P + 127) / 128), 1), dim3(256), 0, st, (const bf16_t*)src, 1,
-                     0, C, seg_off, pad_off, E, codes, scales, P);
+                     0, C, seg_off, pad_off, E, codes, scales, P, 0);
   return hipGetLastError();
 }
 

@@ -76,6 +76,8 @@ def test_argument_errors_return_before_launch(b):
     assert b._lib.moe_backward(ctypes.byref(s), fake, fake, fake, fake, ctypes.byref(plan), fake, fake, fake,
                                fake, fake, fake, None, None, fake, 0, None) == 3
     assert b._lib.moe_round_tokens(ctypes.byref(s), ctypes.byref(plan), None, 0, None) == 1   # rounding off
-    assert b._lib.moe_quantize_mx(fake, 4, 48, fake, fake, None) == 1                         # cols % 32
+    assert b._lib.moe_quantize_mx(fake, 4, 48, 1, fake, fake, None) == 1                      # cols % 32
+    assert b._lib.moe_quantize_mx(fake, 96, 64, 0, fake, fake, None) == 1                     # rows % 64
+    assert b._lib.moe_quantize_mx(fake, 64, 64, 2, fake, fake, None) == 1                     # k_axis
     empty = b.MoePlan()
     assert b._lib.moe_unpermute_combine(ctypes.byref(s), fake, ctypes.byref(empty), fake, None) == 1

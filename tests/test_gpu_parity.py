@@ -138,8 +138,30 @@ def test_quantize_mx_bit_exact():
     src[7, :32] = torch.tensor([500.0, 460.0, 440.0, 449.0, -470.0, 3.0] + [1.0] * 26)   # exponent 0, saturating
     codes = torch.empty(src.shape, dtype=torch.uint8, device="cuda")
     scales = torch.empty((96, 8), dtype=torch.uint8, device="cuda")
-    binding.quantize_mx(src.cuda(), codes, scales)
+    binding.quantize_mx(src.cuda(), codes, scales, k_axis=1)
     torch.cuda.synchronize()
     c_ref, s_ref, _ = mx.quantize(src.double().numpy(), axis=1)
     np.testing.assert_array_equal(codes.cpu().numpy(), c_ref)
     np.testing.assert_array_equal(scales.cpu().numpy(), s_ref)
+
+
+def test_quantize_mx_columns_bit_exact():
+    """The transposed quantiser (blocks down each column, output [cols, rows]) that
+    prepares weights used along their first axis."""
+    from mixture_experts_layer_27_amd import binding
+    from oracle import mx
+    g = torch.Generator().manual_seed(1)
+    src = (torch.randn(128, 192, generator=g) * torch.logspace(-20, 20, 192).unsqueeze(0)).to(torch.bfloat16)
+    src[:32, 3] = 0.0                        # all-zero block
+    src[0, 4] = 500.0                        # saturating block
+    q = 2.0 ** -9
+    ties = [256.0, 17.0, 19.0, 272.0, 304.0, 1.5 * q, 2.5 * q, 0.5 * q, 0.75 * q, -17.0, -2.5 * q, 220.0]
+    src[32:64, 6] = 0.0
+    src[32:32 + len(ties), 6] = torch.tensor(ties)
+    codes = torch.empty((192, 128), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((192, 4), dtype=torch.uint8, device="cuda")
+    binding.quantize_mx(src.cuda(), codes, scales, k_axis=0)
+    torch.cuda.synchronize()
+    c_ref, s_ref, _ = mx.quantize(src.double().numpy(), axis=0)
+    np.testing.assert_array_equal(codes.cpu().numpy(), c_ref.T)
+    np.testing.assert_array_equal(scales.cpu().numpy(), s_ref.T)
