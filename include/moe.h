@@ -67,10 +67,12 @@ typedef enum {
  *   act:  storage type of x, weights, dout and the outputs (MOE_F32 or MOE_BF16).
  *   gemm: expert-GEMM operand format: MOE_F32 (requires act == MOE_F32),
  *         MOE_BF16 or MOE_MXFP8 (both require act == MOE_BF16).
- *   round_tile: 0 = no token rounding; otherwise the tile multiple (128) that
- *         moe_round_tokens rounds per-expert counts to.
- * Supported: 1 <= k <= min(E, 8), 1 <= E <= 256, d % 64 == 0, d_ff % 64 == 0,
- * d, d_ff <= 16384, T <= 2^24, T*k + E*round_tile/2 < 2^31. */
+ *   round_tile: 0 = no token rounding; otherwise the tile multiple (128 on the
+ *         pages; any even value up to 4096) that moe_round_tokens rounds
+ *         per-expert counts to.
+ * Supported (else MOE_ENOTSUP): 1 <= k <= min(E, 8), 1 <= E <= 256,
+ * d % 64 == 0, d_ff % 64 == 0 (d_ff % 128 == 0 with bf16/MXFP8 GEMMs),
+ * d, d_ff <= 16384, T <= 2^20, T*k + E*round_tile/2 < 2^31. */
 typedef struct moe_shape {
   int32_t T, d, E, k, d_ff;
   int32_t act;
@@ -126,8 +128,9 @@ moe_status moe_route(const moe_shape *s, const void *x, const void *w_gate, cons
 moe_status moe_round_tokens(const moe_shape *s, moe_plan *plan, void *ws, size_t ws_bytes,
                             void *stream);
 
-/* Permute (gather): dst[r] = src[token_of_row[r]] for r < N.  src [T,d],
- * dst [N_max,d], both act dtype.  Also used for dout in the backward. */
+/* Permute: dst[r] = src[token_of_row[r]] for r < N (rows past N untouched).
+ * src [T,d], dst [N_max,d], both act dtype.  Each source row is read once and
+ * written to every row of its token.  The backward does the same for dout. */
 moe_status moe_permute(const moe_shape *s, const void *src, const moe_plan *plan, void *dst,
                        void *stream);
 
@@ -136,8 +139,10 @@ moe_status moe_permute(const moe_shape *s, const void *src, const moe_plan *plan
  *   h_saved [N_max,2f] (act): H = x_perm W1_e^T, kept for the backward.
  *   y [N_max,d] (act): Y = A W2_e^T with A = silu(H_gate) * H_up (A is rounded
  *   to the act dtype and computed from the stored H).
- * With gemm == MOE_MXFP8 every GEMM operand is quantised to MXFP8 along K
- * inside this call (workspace). */
+ * With gemm == MOE_MXFP8 every GEMM operand is quantised to MXFP8 along its K
+ * inside this call: x_perm and the weights by quantiser passes, A by the
+ * SwiGLU epilogue (A then exists only as MXFP8 codes, in the workspace).
+ * ws: moe_workspace_bytes(s, MOE_WS_EXPERTS) bytes, 16-byte aligned. */
 moe_status moe_grouped_gemm_swiglu(const moe_shape *s, const void *x_perm, const void *w1,
                                    const void *w2, const moe_plan *plan, void *h_saved, void *y,
                                    void *ws, size_t ws_bytes, void *stream);
@@ -153,7 +158,11 @@ moe_status moe_unpermute_combine(const moe_shape *s, const void *y, const moe_pl
  *   optional dlogits [T,E] f32 and ds [N_max] f32 (per-row gate gradient) when
  *   not NULL.
  * dS_r = <dA'_r, A_r> with dA' = dO_perm W2_e and A recomputed from h_saved
- * (SonicMoE article, section 1); the chain rule gives the rest. */
+ * (SonicMoE article, section 1); the chain rule gives the rest.  The weight
+ * gradients reduce each expert's rows in chunks (partial results summed in a
+ * fixed order), so their cost does not depend on how unevenly experts are
+ * loaded.  ws: moe_workspace_bytes(s, MOE_WS_BACKWARD) bytes, 16-byte aligned
+ * (it includes the partial slabs and, with MXFP8, the quantised operands). */
 moe_status moe_backward(const moe_shape *s, const void *x, const void *w_gate, const void *w1,
                         const void *w2, const moe_plan *plan, const void *h_saved,
                         const void *dout, void *dx, float *dw_gate, float *dw1, float *dw2,
