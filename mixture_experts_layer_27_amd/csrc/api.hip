@@ -108,11 +108,16 @@ MxOperand take_mx(Carver& c, int64_t rows, int64_t K, int64_t srows, const int32
   return o;
 }
 
-// rows per weight-gradient chunk: at most 32 chunks past the experts' first
-int wgrad_kch(int64_t ncap) {
+// rows per weight-gradient chunk: at most 32 chunks past the experts' first, and
+// a chunk's rows of either operand span less than 2 GiB (one buffer resource
+// of the bf16 kernel addresses them)
+int wgrad_kch(const moe_shape& s, int64_t ncap) {
   int64_t k = (ncap + 31) / 32;
   k = (k + 63) / 64 * 64;
-  return (int)(k < 1024 ? 1024 : k);
+  if (k < 1024) k = 1024;
+  const int64_t row_bytes = (int64_t)2 * (2 * s.d_ff > s.d ? 2 * s.d_ff : s.d);
+  const int64_t cap = ((int64_t)1 << 31) / row_bytes / 64 * 64;
+  return (int)(k < cap ? k : cap);
 }
 int64_t wgrad_cap(const moe_shape& s) { return s.gemm == MOE_MXFP8 ? tok_cap(s) : max_rows(s); }
 
@@ -140,7 +145,7 @@ size_t carve_bwd(const moe_shape& s, char* base, BwdWs* w) {
   {
     const int64_t ncap = wgrad_cap(s);
     WgradChunks& g = q.wg;
-    g.kch = wgrad_kch(ncap);
+    g.kch = wgrad_kch(s, ncap);
     g.max_extra = (int)(ncap / g.kch);
     g.max_chunks = s.E + g.max_extra;
     g.chunks = c.take<int4>((size_t)g.max_chunks * 16);

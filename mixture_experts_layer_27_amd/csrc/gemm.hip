@@ -10,6 +10,7 @@
 // Backward (SonicMoE article, section 1): dA' = dO_perm W2_e is never stored;
 // its epilogue recomputes A from the saved H, reduces dS = <dA', A> per row,
 // and emits dH (SwiGLU backward) and gA = g * A for the W2 gradient.
+#include "gemm_big.h"
 #include "gemm_dma.h"
 #include "gemm_engine.h"
 #include "moe_internal.h"
@@ -47,6 +48,22 @@ hipError_t run_dma(const Args& a, int64_t logical_tiles, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <bool AKC, bool BKC, int GROUP, int EPI>
+hipError_t run_big(const Args& a, int64_t logical_tiles, hipStream_t st) {
+  auto kern = grouped_gemm_big<AKC, BKC, GROUP, EPI>;
+  const size_t lds = big_lds_bytes(GROUP == GROUP_M);   // GROUP_M may run 128 x 512 tiles
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const int64_t grid = 8 * ((logical_tiles + 7) / 8);
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds, st, a);
+  return hipGetLastError();
+}
+
+// The 256 x 256 register-staged kernel pays a longer unoverlapped epilogue per
+// tile (one block per CU); it wins when the reduction is deep enough.
+bool use_big(int K) { return K >= 1024; }
+
 Args base_args() {
   Args a{};
   a.ksplit = 1;
@@ -69,7 +86,10 @@ hipError_t gemm_up_swiglu(const moe_shape& s, const moe_plan& p, const PlanInter
   a.offsets = p.offsets;
   a.N = 2 * s.d_ff; a.K = s.d; a.E = s.E; a.f = s.d_ff;
   if (s.act == MOE_BF16) {
-    a.tile_prefix = pi.prefix128; a.tile_expert = pi.tile_e128; a.tilesN = a.N / 256;
+    a.tile_prefix = pi.prefix128; a.tile_expert = pi.tile_e128;
+    if (use_big(a.K))
+      return run_big<true, true, GROUP_M, EPI_SWIGLU>(a, grouped_m_tiles(s, 128) * ceil_div(a.N, 512), st);
+    a.tilesN = a.N / 256;
     return run_dma<128, 256, 2, 4, true, true, GROUP_M, EPI_SWIGLU, 3>(a, grouped_m_tiles(s, 128) * a.tilesN, st);
   }
   a.tile_prefix = pi.prefix128; a.tile_expert = pi.tile_e128; a.tilesN = a.N / 128;
@@ -85,7 +105,10 @@ hipError_t gemm_down(const moe_shape& s, const moe_plan& p, const PlanInternal& 
   a.offsets = p.offsets;
   a.N = s.d; a.K = s.d_ff; a.E = s.E; a.f = s.d_ff;
   if (s.act == MOE_BF16) {
-    a.tile_prefix = pi.prefix128; a.tile_expert = pi.tile_e128; a.tilesN = ceil_div(a.N, 256);
+    a.tile_prefix = pi.prefix128; a.tile_expert = pi.tile_e128;
+    if (use_big(a.K))
+      return run_big<true, true, GROUP_M, EPI_ACT>(a, grouped_m_tiles(s, 128) * ceil_div(a.N, 512), st);
+    a.tilesN = ceil_div(a.N, 256);
     return run_dma<128, 256, 2, 4, true, true, GROUP_M, EPI_ACT, 3>(a, grouped_m_tiles(s, 128) * a.tilesN, st);
   }
   a.tile_prefix = pi.prefix128; a.tile_expert = pi.tile_e128; a.tilesN = ceil_div(a.N, 128);
@@ -127,7 +150,10 @@ hipError_t gemm_dx_perm(const moe_shape& s, const moe_plan& p, const PlanInterna
   a.offsets = p.offsets;
   a.N = s.d; a.K = 2 * s.d_ff; a.E = s.E; a.f = s.d_ff;
   if (s.act == MOE_BF16) {
-    a.tile_prefix = pi.prefix128; a.tile_expert = pi.tile_e128; a.tilesN = ceil_div(a.N, 256);
+    a.tile_prefix = pi.prefix128; a.tile_expert = pi.tile_e128;
+    if (use_big(a.K))
+      return run_big<true, false, GROUP_M, EPI_ACT>(a, grouped_m_tiles(s, 128) * ceil_div(a.N, 512), st);
+    a.tilesN = ceil_div(a.N, 256);
     return run_dma<128, 256, 2, 4, true, false, GROUP_M, EPI_ACT, 3>(a, grouped_m_tiles(s, 128) * a.tilesN, st);
   }
   a.tile_prefix = pi.prefix128; a.tile_expert = pi.tile_e128; a.tilesN = ceil_div(a.N, 128);
@@ -141,10 +167,13 @@ hipError_t gemm_dx_perm(const moe_shape& s, const moe_plan& p, const PlanInterna
 namespace {
 hipError_t run_wgrad(const moe_shape& s, const WgradChunks& w, Args& a, hipStream_t st) {
   a.chunks = w.chunks; a.nchunks = w.nchunks; a.Cpart = w.part;
-  const int bn = s.act == MOE_BF16 ? 256 : 128;
-  a.tilesM = ceil_div(a.M, 128); a.tilesN = ceil_div(a.N, bn);
+  if (s.act == MOE_BF16) {
+    a.tilesM = ceil_div(a.M, 256); a.tilesN = ceil_div(a.N, 256);
+    const int64_t tiles = 8 * (int64_t)ceil_div(w.max_chunks, 8) * a.tilesM * a.tilesN;
+    return run_big<false, false, GROUP_K, EPI_F32>(a, tiles, st);
+  }
+  a.tilesM = ceil_div(a.M, 128); a.tilesN = ceil_div(a.N, 128);
   const int64_t tiles = 8 * (int64_t)ceil_div(w.max_chunks, 8) * a.tilesM * a.tilesN;
-  if (s.act == MOE_BF16) return run_dma<128, 256, 2, 4, false, false, GROUP_K, EPI_F32, 3>(a, tiles, st);
   return run<float, 128, 128, 2, 2, false, false, GROUP_K, EPI_F32>(a, tiles, st);
 }
 }  // namespace

@@ -1,0 +1,305 @@
+// Register-staged bf16 main loop for the grouped expert GEMMs on gfx950:
+// 4 waves per block, each wave a 128 x 128 output tile (4 x 4 MFMA 32x32x16
+// sub-tiles, 256 accumulator registers), K in stages of 64.
+//
+// Why this shape: a CU is fed about 35-40 GB/s of operand data from L2 in
+// these GEMMs, so output area per byte fetched decides the MFMA rate.  A
+// 256 x 256 block tile fetches 64 KiB per 64-deep stage for 8.4 MFLOP, half
+// again more work per byte than a 128 x 256 tile.  The price is one wave per
+// SIMD (the accumulators alone take 256 registers), so latency is hidden inside
+// the wave: global loads for stage k+2 are in flight in registers while stage k
+// is multiplied and stage k+1 is written to LDS, and every group of 16 MFMAs
+// runs with the fragments of the next group already being read.
+//
+// Stage pipeline per iteration k (LDS double buffer, one barrier):
+//   MFMA block 1 (k16 step 0)  + LDS reads of step 1
+//   MFMA block 2 (step 1)      + LDS writes of stage k+1 from registers, reads of step 2
+//   MFMA block 3 (step 2)      + buffer loads of stage k+2 into the freed registers, reads of step 3
+//   barrier
+//   MFMA block 4 (step 3)      + reads of step 0 of stage k+1
+// The body has no branches: past the last stage the LDS writes land in the idle
+// buffer and the buffer loads are out of range (they return zero, no access).
+// Scheduling-group barriers place one LDS/global instruction after each MFMA.
+//
+// Global loads are raw buffer loads: the tile's operand rows are one buffer
+// whose record count ends at the last valid row, so rows past an expert segment
+// or a K chunk read as zero without per-lane masks.
+//
+// Tile shapes.  GROUP_K (weight gradients): 256 x 256 tiles.  GROUP_M (row
+// segments of experts): segments are covered in units of 128 rows; each pair of
+// units is a 256 x 256 ("tall") tile, an odd last unit a 128 x 512 ("wide")
+// tile, so a segment's padding is at most 127 rows, as with 128-row tiles.  A
+// tall tile pair of n-tiles and a wide tile cover the same area, so logical
+// tile L = unit * ceil(N / 512) + c indexes both with the plan's 128-row unit
+// tables.
+//
+// LDS layouts are those of the DMA main loop with 128-byte K rows (BK = 64):
+// K-contiguous operands [rows][64] with chunk c of row r at slot c ^ ((r >> 1) & 7);
+// M/N-contiguous operands [64 k][rows] with 32 B slots XOR-swizzled by k.
+#pragma once
+#include "gemm_dma.h"
+
+namespace moe_gemm {
+
+constexpr int kBigBK = 64;
+constexpr uint32_t kBufferFlags = 0x00020000;   // gfx9 raw buffer: 32-bit dwords, no swizzle
+
+MOE_DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, (int)kBufferFlags);
+}
+
+// One operand tile (ROWS rows x 64 k, bf16) staged through registers by 256
+// threads, ROWS / 32 16-byte loads each.  Load i of a thread lands 4 KiB after
+// load i - 1 in LDS for both layouts (32 K-contiguous rows, or 2048 / ROWS k rows).
+template <int ROWS, bool KC>
+struct RegOperand {
+  static constexpr int L = ROWS / 32;
+  uint32_t voff[L];         // byte offset of each load from the stage's base
+  int lds0;                 // LDS byte offset of load 0
+  u32x4 v[L];
+  const char* base;         // operand bytes of stage 0
+  int64_t step;             // bytes per stage along K
+  int64_t num0;             // valid bytes from base at stage 0
+
+  // K-contiguous rows: row_off(r) = byte offset of tile row r from base; an absent
+  // row gives an offset past the valid range, so its loads return zero
+  template <class RowOff>
+  MOE_DEV void init_kc(RowOff row_off) {
+    const int t = threadIdx.x, c = t & 7, r0 = t >> 3;
+    lds0 = r0 * 128 + ((c ^ kc8_h(r0)) << 4);
+#pragma unroll
+    for (int i = 0; i < L; ++i) voff[i] = (uint32_t)(row_off(r0 + 32 * i) + c * 16);
+  }
+  // M/N-contiguous: k rows ld elements apart, the tile's columns contiguous
+  MOE_DEV void init_mn(int64_t ld) {
+    constexpr int CPK = ROWS / 8;          // 16-byte chunks per k row
+    constexpr int KPP = 256 / CPK;         // k rows per pass of the block
+    const int t = threadIdx.x, cc = t % CPK, k0 = t / CPK;
+    lds0 = mn_off<ROWS>(k0, cc * 16);
+#pragma unroll
+    for (int i = 0; i < L; ++i) voff[i] = (uint32_t)((int64_t)(k0 + KPP * i) * ld * 2 + cc * 16);
+  }
+  MOE_DEV void load(int kt) {
+    const int64_t n = num0 - kt * step;   // <= 0 past the operand: every load returns zero
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(base + kt * step, (uint32_t)(n > 0 ? n : 0));
+#pragma unroll
+    for (int i = 0; i < L; ++i)
+      v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff[i], 0, 0));
+  }
+  MOE_DEV void store(char* stage) const {
+#pragma unroll
+    for (int i = 0; i < L; ++i) *reinterpret_cast<u32x4*>(stage + lds0 + 4096 * i) = v[i];
+  }
+};
+
+template <int BM, int BN>
+constexpr size_t big_ring_bytes() { return (size_t)2 * (BM + BN) * kBigBK * 2; }
+constexpr size_t big_lds_bytes(bool wide) {
+  return wide ? big_ring_bytes<128, 512>() : big_ring_bytes<256, 256>();
+}
+
+// One output tile: BM x BN with WM x WN waves of 128 x 128.
+template <int BM, int BN, int WM, int WN, bool AKC, bool BKC, int GROUP, int EPI>
+MOE_DEV void big_tile(const Args& args, const TileCtx& ctx, char* smem) {
+  using T = bf16_t;
+  constexpr int BK = kBigBK;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  static_assert(WM * WN == 4 && WTM == 128 && WTN == 128, "four waves of 128 x 128");
+  constexpr int ASZ = BM * BK * 2, BSZ = BN * BK * 2, STAGE = ASZ + BSZ;
+  const int e = ctx.e, nt = ctx.nt;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const char* Ab = reinterpret_cast<const char*>(args.A) + (int64_t)e * args.a_estride * 2;
+  const char* Bb = reinterpret_cast<const char*>(args.B) + (int64_t)e * args.b_estride * 2;
+
+  RegOperand<BM, AKC> ra;
+  RegOperand<BN, BKC> rb;
+  if constexpr (AKC) {   // GROUP_M: rows row_begin.. of the segment, K contiguous
+    const int nrows = min(BM, ctx.row_end - ctx.row_begin);
+    const int64_t rowb = args.lda * 2;
+    ra.base = Ab + (int64_t)ctx.row_begin * rowb;
+    ra.step = BK * 2;
+    ra.num0 = (int64_t)nrows * rowb;     // rows >= nrows start past it
+    ra.init_kc([&](int r) -> int64_t { return (int64_t)r * rowb; });
+  } else {               // GROUP_K: k rows k_begin..k_end of the chunk, columns m0.. contiguous
+    ra.base = Ab + ((int64_t)ctx.k_begin * args.lda + ctx.m0) * 2;
+    ra.step = (int64_t)BK * args.lda * 2;
+    ra.num0 = (int64_t)(ctx.k_end - ctx.k_begin) * args.lda * 2 - (int64_t)ctx.m0 * 2;
+    ra.init_mn(args.lda);
+  }
+  if constexpr (BKC) {   // weights [N][K]
+    const int64_t rowb = args.ldb * 2;
+    rb.base = Bb;
+    rb.step = BK * 2;
+    rb.num0 = (int64_t)args.N * rowb;
+    rb.init_kc([&](int row) -> int64_t {
+      int j = ctx.n0 + row;
+      if constexpr (EPI == EPI_SWIGLU) {
+        // wave wn's columns: first half gate rows, second half the matching up rows
+        const int w = row / WTN, jj = row % WTN;
+        const int g = nt * (BN / 2) + w * (WTN / 2) + (jj % (WTN / 2));
+        j = g >= args.f ? args.N : (jj < WTN / 2) ? g : (args.f + g);   // past f: absent
+      }
+      return (int64_t)j * rowb;         // j >= N lies past num0
+    });
+  } else {               // [K][N]: k rows, columns n0.. contiguous
+    const int kb = (GROUP == GROUP_K) ? ctx.k_begin : 0;
+    const int kend = (GROUP == GROUP_K) ? ctx.k_end : args.K;
+    rb.base = Bb + ((int64_t)kb * args.ldb + ctx.n0) * 2;
+    rb.step = (int64_t)BK * args.ldb * 2;
+    rb.num0 = (int64_t)(kend - kb) * args.ldb * 2 - (int64_t)ctx.n0 * 2;
+    rb.init_mn(args.ldb);
+  }
+
+  f32x16 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+
+  auto frags = [&](const char* as, int ks, u32x4 (&af)[TM], u32x4 (&bfr)[TN]) {
+    const char* bs = as + ASZ;
+    const int kb = ks * 16 + (lane >> 5) * 8 + ((lane & 15) >> 2);       // MN: first k row of the lane
+    const int cb = (((lane >> 4) & 1) * 16 + 4 * (lane & 3)) * 2;       // MN: byte column of the lane
+    if constexpr (AKC) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        af[i] = *reinterpret_cast<const u32x4*>(as + kc_offk<64>(wm * WTM + i * 32 + (lane & 31), ks * 2 + (lane >> 5)));
+    } else {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int byte = (wm * WTM + i * 32) * 2 + cb;
+        af[i] = lds_tr_frag(as + mn_off<BM>(kb, byte), as + mn_off<BM>(kb + 4, byte));
+      }
+    }
+    if constexpr (BKC) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        bfr[j] = *reinterpret_cast<const u32x4*>(bs + kc_offk<64>(wn * WTN + j * 32 + (lane & 31), ks * 2 + (lane >> 5)));
+    } else {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int byte = (wn * WTN + j * 32) * 2 + cb;
+        bfr[j] = lds_tr_frag(bs + mn_off<BN>(kb, byte), bs + mn_off<BN>(kb + 4, byte));
+      }
+    }
+  };
+  auto mma = [&](const u32x4 (&af)[TM], const u32x4 (&bfr)[TN]) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) Mma<T>::run(acc[i][j], af[i], bfr[j]);
+  };
+
+  const int kext = (GROUP == GROUP_M) ? args.K : (ctx.k_end - ctx.k_begin);
+  const int nk = kext > 0 ? (kext + BK - 1) / BK : 0;
+  constexpr int NR = (AKC ? TM : 2 * TM) + (BKC ? TN : 2 * TN);   // LDS reads per k16 step
+  u32x4 a0[TM], b0[TN], a1[TM], b1[TN];
+  if (nk > 0) {
+    ra.load(0); rb.load(0);
+    ra.store(smem); rb.store(smem + ASZ);
+    ra.load(1); rb.load(1);
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+    cta_barrier();
+    frags(smem, 0, a0, b0);
+  }
+  for (int kt = 0; kt < nk; ++kt) {
+    const char* as = smem + (kt & 1) * STAGE;
+    char* an = smem + ((kt + 1) & 1) * STAGE;   // the next stage, written during this one
+    frags(as, 1, a1, b1);
+    mma(a0, b0);
+    frags(as, 2, a0, b0);
+    ra.store(an); rb.store(an + ASZ);
+    mma(a1, b1);
+    ra.load(kt + 2); rb.load(kt + 2);
+    frags(as, 3, a1, b1);
+    mma(a0, b0);
+#pragma unroll
+    for (int i = 0; i < TM * TN; ++i) {          // block 1: MFMA + fragment read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < TM * TN; ++i) {          // block 2: MFMA + LDS write (+ fragment read)
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < ra.L + rb.L) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+      if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < TM * TN; ++i) {          // block 3: MFMA + buffer load (+ fragment read)
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (i < ra.L + rb.L) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);          // this wave's fragment reads and stage writes are done
+    cta_barrier();
+    frags(an, 0, a0, b0);
+    mma(a1, b1);
+#pragma unroll
+    for (int i = 0; i < TM * TN; ++i) {          // block 4: MFMA + the next stage's first fragments
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+    }
+  }
+  wave_epilogue<BM, BN, WM, WN, GROUP, EPI>(args, ctx, acc, smem);
+}
+
+// GROUP_M decode over 128-row units (see the header comment): returns false when
+// the block has no tile; *wide tells the shape.  Inside an expert, the tall
+// tiles go in groups of kGroupM unit pairs with the n-tile outer and the pair
+// inner, so consecutive tiles (one XCD) share weight columns in L2.
+MOE_DEV bool big_decode_m(const Args& args, TileCtx& c, bool* wide) {
+  const int nW = (args.N + 511) / 512;
+  const int total = args.tile_prefix[args.E] * nW;
+  const int per = (total + 7) >> 3;
+  const int b = blockIdx.x;
+  if ((b >> 3) >= per) return false;
+  const int L = (b & 7) * per + (b >> 3);
+  if (L >= total) return false;
+  const int e = args.tile_expert[L / nW];
+  const int p0 = args.tile_prefix[e], ue = args.tile_prefix[e + 1] - p0;
+  const int q = L - p0 * nW;                 // tile index inside the expert
+  const int pairs = ue >> 1, ntall = 2 * nW;
+  c.e = e; c.split = 0; c.slot = -1;
+  c.row_end = args.offsets[e + 1];
+  c.k_begin = 0; c.k_end = args.K;
+  if (q < pairs * ntall) {      // tall: unit pair `pair`, n-tile nt
+    const int g = q / (kGroupM * ntall);
+    const int gsize = min(kGroupM, pairs - g * kGroupM);
+    const int within = q - g * kGroupM * ntall;
+    const int nt = within / gsize;
+    const int pair = g * kGroupM + (within - nt * gsize);
+    *wide = false;
+    c.mt = pair; c.nt = nt;
+    c.row_begin = args.offsets[e] + pair * 256;
+    c.m0 = pair * 256; c.n0 = nt * 256;
+  } else {                      // wide: the odd last unit
+    const int cq = q - pairs * ntall;
+    *wide = true;
+    c.mt = ue - 1; c.nt = cq;
+    c.row_begin = args.offsets[e] + (ue - 1) * 128;
+    c.m0 = (ue - 1) * 128; c.n0 = cq * 512;
+  }
+  return true;
+}
+
+template <bool AKC, bool BKC, int GROUP, int EPI>
+__global__ __launch_bounds__(256) void grouped_gemm_big(Args args) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  static_assert(GROUP == GROUP_M || GROUP == GROUP_K, "grouped GEMMs only");
+  TileCtx ctx;
+  if constexpr (GROUP == GROUP_K) {
+    if (!decode_tile<256, 256, kBigBK, GROUP_K>(args, ctx)) return;
+    big_tile<256, 256, 2, 2, AKC, BKC, GROUP, EPI>(args, ctx, smem);
+  } else {
+    bool wide = false;
+    if (!big_decode_m(args, ctx, &wide)) return;
+    if (wide) big_tile<128, 512, 1, 4, AKC, BKC, GROUP, EPI>(args, ctx, smem);
+    else big_tile<256, 256, 2, 2, AKC, BKC, GROUP, EPI>(args, ctx, smem);
+  }
+}
+
+}  // namespace moe_gemm

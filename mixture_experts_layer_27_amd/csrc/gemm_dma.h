@@ -127,6 +127,15 @@ struct DmaOperand {
   }
 };
 
+// f(integral_constant<int, 0>), ..., f(integral_constant<int, N - 1>), in order
+template <int N, class F>
+MOE_DEV void static_for(F&& f) {
+  if constexpr (N > 0) {
+    static_for<N - 1>(f);
+    f(std::integral_constant<int, N - 1>{});
+  }
+}
+
 MOE_DEV float fast_sigmoid(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 // Wave-private epilogue: each wave stages its (BM/WM) x (BN/WN) accumulators in
@@ -149,8 +158,10 @@ MOE_DEV void wave_epilogue(const Args& args, const TileCtx& ctx, f32x16 (&acc)[B
   const int rbase = ctx.row_begin + wm * WTM;     // GROUP_M: first row of this wave's tile
   const int mbase = ctx.m0 + wm * WTM;            // GROUP_K: first output row
   const int cbase = ctx.n0 + wn * WTN;            // first output column
-#pragma unroll
-  for (int i = 0; i < TM; ++i) {
+  // one 32-row sub-tile at a time; the sub-tile index is a compile-time constant
+  // so the accumulators stay in registers however large the per-row work is
+  static_for<TM>([&](auto ic) {
+    constexpr int i = decltype(ic)::value;
 #pragma unroll
     for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -167,7 +178,9 @@ MOE_DEV void wave_epilogue(const Args& args, const TileCtx& ctx, f32x16 (&acc)[B
         const int u = lane + 64 * it;
         const int rr = u / HC, ch = u % HC;
         const int grow = rbase + i * 32 + rr;
-        const bool ok = grow < ctx.row_end;   // uniform over the HC lanes of a row
+        const int gcol = ctx.nt * (BN / 2) + wn * (WTN / 2) + ch * 8;
+        // uniform over each lane quad (a 32-column block never straddles f, f % 128 == 0)
+        const bool ok = grow < ctx.row_end && gcol < args.f;
         const float* src = slab + rr * SS + ch * 8;
         float hg[8], hu[8], a[8];
 #pragma unroll
@@ -176,7 +189,6 @@ MOE_DEV void wave_epilogue(const Args& args, const TileCtx& ctx, f32x16 (&acc)[B
           hu[c] = Vec8<T>::rnd(src[WTN / 2 + c]);
           a[c] = hg[c] * fast_sigmoid(hg[c]) * hu[c];
         }
-        const int gcol = ctx.nt * (BN / 2) + wn * (WTN / 2) + ch * 8;
         if (ok) {
           T* hrow = H + (int64_t)grow * args.ldc;
           Vec8<T>::store(hrow + gcol, hg);
@@ -296,7 +308,7 @@ MOE_DEV void wave_epilogue(const Args& args, const TileCtx& ctx, f32x16 (&acc)[B
       }
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);          // slab reads done before the next sub-tile overwrites it
-  }
+  });
 }
 
 template <int BM, int BN, int WM, int WN, bool AKC, bool BKC, int GROUP, int EPI, int S, int BK = 32>
