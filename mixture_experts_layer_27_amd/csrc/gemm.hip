@@ -119,7 +119,13 @@ hipError_t gemm_down(const moe_shape& s, const moe_plan& p, const PlanInternal& 
 
 // dS partial sums per row: one per (column tile, wave column) on the bf16 path,
 // one per column tile on the fp32 path
-int gemm_dact_parts(const moe_shape& s) { return s.act == MOE_BF16 ? ceil_div(s.d_ff, 256) * 4 : ceil_div(s.d_ff, 128); }
+int gemm_dact_parts(const moe_shape& s) {
+  if (s.act != MOE_BF16) return ceil_div(s.d_ff, 128);
+  // 128-column wave tiles over ceil(f / 512) 512-column quanta (bf16, deep K), or
+  // 64-column ones over 256-column tiles (the MXFP8 kernel, and bf16 with shallow K)
+  if (s.gemm == MOE_BF16 && use_big(s.d)) return ceil_div(s.d_ff, 512) * 4;
+  return ceil_div(s.d_ff, 256) * 4;
+}
 
 hipError_t gemm_dact(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const void* do_perm,
                      const void* w2, const void* h, void* dh, void* ga, float* ds_part, hipStream_t st) {
@@ -134,7 +140,10 @@ hipError_t gemm_dact(const moe_shape& s, const moe_plan& p, const PlanInternal& 
   a.offsets = p.offsets;
   a.N = s.d_ff; a.K = s.d; a.E = s.E; a.f = s.d_ff;
   if (s.act == MOE_BF16) {
-    a.tile_prefix = pi.prefix128; a.tile_expert = pi.tile_e128; a.tilesN = ceil_div(a.N, 256);
+    a.tile_prefix = pi.prefix128; a.tile_expert = pi.tile_e128;
+    if (use_big(a.K))
+      return run_big<true, false, GROUP_M, EPI_DSWIGLU>(a, grouped_m_tiles(s, 128) * ceil_div(a.N, 512), st);
+    a.tilesN = ceil_div(a.N, 256);
     return run_dma<128, 256, 2, 4, true, false, GROUP_M, EPI_DSWIGLU, 3>(a, grouped_m_tiles(s, 128) * a.tilesN, st);
   }
   a.tile_prefix = pi.prefix128; a.tile_expert = pi.tile_e128; a.tilesN = ceil_div(a.N, 128);

@@ -144,6 +144,9 @@ MOE_DEV float fast_sigmoid(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf
 // halves of each staging store in different bank halves.
 // SwiGLU: the wave's columns [0, WTN/2) are gate columns, [WTN/2, WTN) the
 // matching up columns.  dS partials go to C3[(nt * WN + wn) * ldc3 + row].
+// Latency: every sub-tile first issues all its global loads (the saved H and the
+// gates of the SwiGLU backward) and all its slab reads, then computes and
+// stores, so a wave waits once per sub-tile rather than once per row chunk.
 template <int BM, int BN, int WM, int WN, int GROUP, int EPI>
 MOE_DEV void wave_epilogue(const Args& args, const TileCtx& ctx, f32x16 (&acc)[BM / WM / 32][BN / WN / 32],
                            char* smem) {
@@ -162,67 +165,48 @@ MOE_DEV void wave_epilogue(const Args& args, const TileCtx& ctx, f32x16 (&acc)[B
   // so the accumulators stay in registers however large the per-row work is
   static_for<TM>([&](auto ic) {
     constexpr int i = decltype(ic)::value;
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int q = 0; q < 16; ++q)
-        slab[(8 * (q >> 2) + 4 * (lane >> 5) + (q & 3)) * SS + j * 32 + (lane & 31)] = acc[i][j][q];
-    __builtin_amdgcn_s_waitcnt(0xc07f);          // lgkmcnt(0): the slab is written (one wave, in order)
-    if constexpr (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_MX) {
-      constexpr int HC = CPR / 2;
-      static_assert(EPI != EPI_SWIGLU_MX || HC == 4, "one 32-column block of A per wave row");
-      T* H = reinterpret_cast<T*>(args.C);
-      T* Aout = reinterpret_cast<T*>(args.C2);
-#pragma unroll
-      for (int it = 0; it < 32 * HC / 64; ++it) {
-        const int u = lane + 64 * it;
-        const int rr = u / HC, ch = u % HC;
-        const int grow = rbase + i * 32 + rr;
-        const int gcol = ctx.nt * (BN / 2) + wn * (WTN / 2) + ch * 8;
-        // uniform over each lane quad (a 32-column block never straddles f, f % 128 == 0)
-        const bool ok = grow < ctx.row_end && gcol < args.f;
-        const float* src = slab + rr * SS + ch * 8;
-        float hg[8], hu[8], a[8];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) {
-          hg[c] = Vec8<T>::rnd(src[c]);
-          hu[c] = Vec8<T>::rnd(src[WTN / 2 + c]);
-          a[c] = hg[c] * fast_sigmoid(hg[c]) * hu[c];
-        }
-        if (ok) {
-          T* hrow = H + (int64_t)grow * args.ldc;
-          Vec8<T>::store(hrow + gcol, hg);
-          Vec8<T>::store(hrow + args.f + gcol, hu);
-        }
-        if constexpr (EPI == EPI_SWIGLU_MX) {
-          // A as the forward stores it (bf16), quantised along f: this row's 32
-          // columns of the wave are one block held by a lane quad
-          float amax = 0.0f;
-#pragma unroll
-          for (int c = 0; c < 8; ++c) {
-            a[c] = Vec8<T>::rnd(a[c]);
-            amax = fmaxf(amax, fabsf(a[c]));
-          }
-          amax = quad_max(amax);
-          if (ok) {
-            const int X = mx_exponent(amax);
-            const int64_t prow = grow + (int64_t)args.q_pad[ctx.e] - args.offsets[ctx.e];
-            *reinterpret_cast<uint2*>(args.q_codes + prow * args.q_ld + gcol) = e4m3_8(a, pow2f(-X));
-            if (ch == 0)
-              args.q_scales[((gcol >> 6) * args.q_srows + prow) * 2 + ((gcol >> 5) & 1)] = (uint8_t)(X + 127);
-          }
-        } else {
-          if (ok) Vec8<T>::store(Aout + (int64_t)grow * args.ldc2 + gcol, a);
-        }
-      }
-    } else if constexpr (EPI == EPI_DSWIGLU || EPI == EPI_DSWIGLU_MX) {
+    if constexpr (EPI == EPI_DSWIGLU || EPI == EPI_DSWIGLU_MX) {
       static_assert(CPR <= 64 && (32 * CPR) % 64 == 0, "row reduction inside one wave");
       static_assert(EPI != EPI_DSWIGLU_MX || CPR % 4 == 0, "lane quads hold 32-column blocks");
+      constexpr int IT = 32 * CPR / 64;
       const T* Hs = reinterpret_cast<const T*>(args.aux);
+      // global loads first: they overlap the staging below
+      u32x4 hgv[IT], huv[IT];
+      float gv[IT];
+#pragma unroll
+      for (int it = 0; it < IT; ++it) {
+        const int u = lane + 64 * it;
+        const int rr = u / CPR, ch = u % CPR;
+        const int grow = rbase + i * 32 + rr;
+        const int col = cbase + ch * 8;
+        if (grow < ctx.row_end && col < args.N) {
+          const T* hrow = Hs + (int64_t)grow * args.ld_aux;
+          hgv[it] = ldg16(hrow + col);
+          huv[it] = ldg16(hrow + args.f + col);
+          gv[it] = args.row_gate[grow];
+        } else {
+          hgv[it] = huv[it] = u32x4{0u, 0u, 0u, 0u};
+          gv[it] = 0.0f;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+          slab[(8 * (q >> 2) + 4 * (lane >> 5) + (q & 3)) * SS + j * 32 + (lane & 31)] = acc[i][j][q];
+      __builtin_amdgcn_s_waitcnt(0xc07f);          // lgkmcnt(0): the slab is written (one wave, in order)
+      float dap[IT][8];
+#pragma unroll
+      for (int it = 0; it < IT; ++it) {
+        const int u = lane + 64 * it;
+        const float* src = slab + (u / CPR) * SS + (u % CPR) * 8;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) dap[it][c] = src[c];
+      }
       T* dH = reinterpret_cast<T*>(args.C);
       T* gA = reinterpret_cast<T*>(args.C2);
 #pragma unroll
-      for (int it = 0; it < 32 * CPR / 64; ++it) {
+      for (int it = 0; it < IT; ++it) {
         const int u = lane + 64 * it;
         const int rr = u / CPR, ch = u % CPR;
         const int grow = rbase + i * 32 + rr;
@@ -233,20 +217,22 @@ MOE_DEV void wave_epilogue(const Args& args, const TileCtx& ctx, f32x16 (&acc)[B
 #pragma unroll
         for (int c = 0; c < 8; ++c) dhg[c] = dhu[c] = 0.0f;
         if (ok) {
-          const float* src = slab + rr * SS + ch * 8;
-          const float g = args.row_gate[grow];
-          const T* hrow = Hs + (int64_t)grow * args.ld_aux;
+          const float g = gv[it];
           float hg[8], hu[8], ga[8];
-          Vec8<T>::load(hrow + col, hg);
-          Vec8<T>::load(hrow + args.f + col, hu);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            hg[2 * q] = __uint_as_float(hgv[it][q] << 16);
+            hg[2 * q + 1] = __uint_as_float(hgv[it][q] & 0xffff0000u);
+            hu[2 * q] = __uint_as_float(huv[it][q] << 16);
+            hu[2 * q + 1] = __uint_as_float(huv[it][q] & 0xffff0000u);
+          }
 #pragma unroll
           for (int c = 0; c < 8; ++c) {
-            const float dap = src[c];
             const float sg = fast_sigmoid(hg[c]);
             const float sl = hg[c] * sg;
             const float a = Vec8<T>::rnd(sl * hu[c]);      // A as stored in the forward
-            part += dap * a;
-            const float da = g * dap;
+            part += dap[it][c] * a;
+            const float da = g * dap[it][c];
             dhg[c] = da * hu[c] * (sg * (1.0f + hg[c] * (1.0f - sg)));
             dhu[c] = da * sl;
             ga[c] = g * a;
@@ -287,24 +273,90 @@ MOE_DEV void wave_epilogue(const Args& args, const TileCtx& ctx, f32x16 (&acc)[B
         if (ch == 0 && grow < ctx.row_end) args.C3[(int64_t)(ctx.nt * WN + wn) * args.ldc3 + grow] = part;
       }
     } else {
-      using OT = typename std::conditional<EPI == EPI_ACT, T, float>::type;
-      OT* C = reinterpret_cast<OT*>(args.C);
-      if constexpr (GROUP == GROUP_K) C = wgrad_out<OT>(args, ctx);
 #pragma unroll
-      for (int it = 0; it < 32 * CPR / 64; ++it) {
-        const int u = lane + 64 * it;
-        const int rr = u / CPR, ch = u % CPR;
-        int grow;
-        bool ok;
-        if constexpr (GROUP == GROUP_M) { grow = rbase + i * 32 + rr; ok = grow < ctx.row_end; }
-        else { grow = mbase + i * 32 + rr; ok = grow < args.M; }
-        const int col = cbase + ch * 8;
-        if (!ok || col >= args.N) continue;
-        const float* src = slab + rr * SS + ch * 8;
-        float v[8];
+      for (int j = 0; j < TN; ++j)
 #pragma unroll
-        for (int c = 0; c < 8; ++c) v[c] = src[c];
-        Vec8<OT>::store(C + (int64_t)grow * args.ldc + col, v);
+        for (int q = 0; q < 16; ++q)
+          slab[(8 * (q >> 2) + 4 * (lane >> 5) + (q & 3)) * SS + j * 32 + (lane & 31)] = acc[i][j][q];
+      __builtin_amdgcn_s_waitcnt(0xc07f);          // lgkmcnt(0): the slab is written (one wave, in order)
+      if constexpr (EPI == EPI_SWIGLU || EPI == EPI_SWIGLU_MX) {
+        constexpr int HC = CPR / 2;
+        constexpr int IT = 32 * HC / 64;
+        static_assert(EPI != EPI_SWIGLU_MX || HC == 4, "one 32-column block of A per wave row");
+        T* H = reinterpret_cast<T*>(args.C);
+        T* Aout = reinterpret_cast<T*>(args.C2);
+        float hg[IT][8], hu[IT][8];
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+          const int u = lane + 64 * it;
+          const float* src = slab + (u / HC) * SS + (u % HC) * 8;
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            hg[it][c] = Vec8<T>::rnd(src[c]);
+            hu[it][c] = Vec8<T>::rnd(src[WTN / 2 + c]);
+          }
+        }
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+          const int u = lane + 64 * it;
+          const int rr = u / HC, ch = u % HC;
+          const int grow = rbase + i * 32 + rr;
+          const int gcol = ctx.nt * (BN / 2) + wn * (WTN / 2) + ch * 8;
+          // uniform over each lane quad (a 32-column block never straddles f, f % 128 == 0)
+          const bool ok = grow < ctx.row_end && gcol < args.f;
+          float a[8];
+#pragma unroll
+          for (int c = 0; c < 8; ++c) a[c] = hg[it][c] * fast_sigmoid(hg[it][c]) * hu[it][c];
+          if (ok) {
+            T* hrow = H + (int64_t)grow * args.ldc;
+            Vec8<T>::store(hrow + gcol, hg[it]);
+            Vec8<T>::store(hrow + args.f + gcol, hu[it]);
+          }
+          if constexpr (EPI == EPI_SWIGLU_MX) {
+            // A as the forward stores it (bf16), quantised along f: this row's 32
+            // columns of the wave are one block held by a lane quad
+            float amax = 0.0f;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+              a[c] = Vec8<T>::rnd(a[c]);
+              amax = fmaxf(amax, fabsf(a[c]));
+            }
+            amax = quad_max(amax);
+            if (ok) {
+              const int X = mx_exponent(amax);
+              const int64_t prow = grow + (int64_t)args.q_pad[ctx.e] - args.offsets[ctx.e];
+              *reinterpret_cast<uint2*>(args.q_codes + prow * args.q_ld + gcol) = e4m3_8(a, pow2f(-X));
+              if (ch == 0)
+                args.q_scales[((gcol >> 6) * args.q_srows + prow) * 2 + ((gcol >> 5) & 1)] = (uint8_t)(X + 127);
+            }
+          } else {
+            if (ok) Vec8<T>::store(Aout + (int64_t)grow * args.ldc2 + gcol, a);
+          }
+        }
+      } else {
+        using OT = typename std::conditional<EPI == EPI_ACT, T, float>::type;
+        constexpr int IT = 32 * CPR / 64;
+        OT* C = reinterpret_cast<OT*>(args.C);
+        if constexpr (GROUP == GROUP_K) C = wgrad_out<OT>(args, ctx);
+        float v[IT][8];
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+          const int u = lane + 64 * it;
+          const float* src = slab + (u / CPR) * SS + (u % CPR) * 8;
+#pragma unroll
+          for (int c = 0; c < 8; ++c) v[it][c] = src[c];
+        }
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+          const int u = lane + 64 * it;
+          const int rr = u / CPR, ch = u % CPR;
+          int grow;
+          bool ok;
+          if constexpr (GROUP == GROUP_M) { grow = rbase + i * 32 + rr; ok = grow < ctx.row_end; }
+          else { grow = mbase + i * 32 + rr; ok = grow < args.M; }
+          const int col = cbase + ch * 8;
+          if (ok && col < args.N) Vec8<OT>::store(C + (int64_t)grow * args.ldc + col, v[it]);
+        }
       }
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);          // slab reads done before the next sub-tile overwrites it

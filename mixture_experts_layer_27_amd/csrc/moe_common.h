@@ -18,16 +18,16 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 MOE_DEV float bf2f(bf16_t h) { return __uint_as_float(((uint32_t)h) << 16); }
 
-// float -> bfloat16, round to nearest even (NaN stays a quiet NaN).
-MOE_DEV bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
-}
+// float -> bfloat16, round to nearest even; a NaN keeps its top payload bits and
+// becomes quiet.  gfx950 converts in hardware (v_cvt_pk_bf16_f32), identical
+// bit for bit to the integer rounding (u + 0x7fff + ((u >> 16) & 1)) >> 16 on
+// every non-NaN input, which is what the conversion computes.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+MOE_DEV bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 
 MOE_DEV uint32_t pack_bf2(float lo, float hi) {
-  return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // Element access for the two activation types.
