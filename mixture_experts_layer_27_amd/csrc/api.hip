@@ -380,7 +380,7 @@ moe_status moe_backward(const moe_shape* s, const void* x, const void* w_gate, c
   }
   if (e == hipSuccess)
     e = launch_router_bwd(*s, *plan, w.ds_part, gemm_dact_parts(*s), ds, dz, w.dzq, ldz, hs);
-  if (e == hipSuccess) e = gemm_router_dx(*s, *plan, w.dzq, ldz, w_gate, w.xbuf, dx, hs);
+  if (e == hipSuccess) e = launch_router_dx(*s, *plan, w.xbuf, dz, w_gate, dx, hs);
   if (e == hipSuccess) e = gemm_router_dwg(*s, w.dzq, ldz, x, w.dwg_part, hs);
   if (e == hipSuccess)
     e = launch_splitk_reduce(w.dwg_part, gemm_router_dwg_splits(*s), (int64_t)s->E * s->d, dw_gate, hs);

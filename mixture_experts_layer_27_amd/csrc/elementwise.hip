@@ -93,6 +93,80 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, c
   }
 }
 
+// Input gradient: dx[t] = sum over the rows r of t (ascending) of dx_perm[r]
+//                        + sum over the experts e of dz[t, e] * W_g[e]   (router term)
+// in fp32.  dz[t] is nonzero only at the experts of t's rows and at its top-k
+// experts (router backward below), so the router term is a gather of a few W_g
+// rows (L2-resident) rather than a GEMM; a top-k expert is visited here only when
+// t has no row at it (token rounding dropped the pair).
+template <typename T>
+__global__ __launch_bounds__(256) void router_dx_kernel(const T* __restrict__ dx_perm, const int32_t* __restrict__ tok_ptr,
+                                                       const int32_t* __restrict__ tok_rows,
+                                                       const int32_t* __restrict__ expert_of_row,
+                                                       const int32_t* __restrict__ topk_idx,
+                                                       const uint32_t* __restrict__ keep_bits, int words,
+                                                       const float* __restrict__ dz, const T* __restrict__ wg,
+                                                       int T_, int E, int d, int k, T* __restrict__ out) {
+  constexpr int EV = 16 / sizeof(T);
+  const int vec = d / EV;
+  const int64_t total = (int64_t)T_ * vec;
+  auto add = [&](float* acc, const u32x4& v, float w) {
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += w * __uint_as_float(v[q] << 16);
+        acc[2 * q + 1] += w * __uint_as_float(v[q] & 0xffff0000u);
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] += w * __uint_as_float(v[q]);
+    }
+  };
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
+    const int t = (int)(i / vec), c = (int)(i - (int64_t)t * vec);
+    const float* dzt = dz + (int64_t)t * E;
+    float acc[EV];
+#pragma unroll
+    for (int q = 0; q < EV; ++q) acc[q] = 0.0f;
+    const int p0 = tok_ptr[t], p1 = tok_ptr[t + 1];
+    for (int pb = p0; pb < p1; pb += 4) {
+      // up to four rows (and their experts' router rows) in flight
+      u32x4 v[4], w[4];
+      float z[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (pb + u < p1) {
+          const int r = tok_rows[pb + u];
+          const int e = expert_of_row[r];
+          z[u] = dzt[e];
+          v[u] = ldg16(dx_perm + (int64_t)r * d + c * EV);
+          w[u] = ldg16(wg + (int64_t)e * d + c * EV);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (pb + u >= p1) break;
+        add(acc, v[u], 1.0f);
+        add(acc, w[u], z[u]);
+      }
+    }
+    for (int j = 0; j < k; ++j) {
+      const int e = topk_idx[(int64_t)t * k + j];
+      if ((keep_bits[(int64_t)t * words + (e >> 5)] >> (e & 31)) & 1u) continue;
+      add(acc, ldg16(wg + (int64_t)e * d + c * EV), dzt[e]);
+    }
+    u32x4 o;
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[q] = pack_bf2(acc[2 * q], acc[2 * q + 1]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[q] = __float_as_uint(acc[q]);
+    }
+    stg16(out + (int64_t)t * d + c * EV, o);
+  }
+}
+
 // Router backward, one wave per token.  dS of every row is the fixed-order sum of
 // the per-column-tile partials.  For token t with top-k set K (gates S) and rows
 // A (gates g):  dz_e = [e in A] g_e dS_e - [e in K] S_e * sum_{A} g dS.
@@ -227,6 +301,23 @@ hipError_t launch_combine(const moe_shape& s, const void* y, const moe_plan& p, 
     const int64_t work = (int64_t)s.T * (s.d / 4);
     hipLaunchKernelGGL(combine_kernel<float>, dim3(grid_for(work, 256)), dim3(256), 0, st, (const float*)y,
                        p.tok_ptr, p.tok_rows, p.gate_of_row, s.T, s.d, (float*)out);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_router_dx(const moe_shape& s, const moe_plan& p, const void* dx_perm, const float* dz,
+                            const void* wg, void* dx, hipStream_t st) {
+  const int words = (s.E + 31) / 32;
+  if (s.act == MOE_BF16) {
+    const int64_t work = (int64_t)s.T * (s.d / 8);
+    hipLaunchKernelGGL(router_dx_kernel<bf16_t>, dim3(grid_for(work, 256)), dim3(256), 0, st, (const bf16_t*)dx_perm,
+                       p.tok_ptr, p.tok_rows, p.expert_of_row, p.topk_idx, p.keep_bits, words, dz,
+                       (const bf16_t*)wg, s.T, s.E, s.d, s.k, (bf16_t*)dx);
+  } else {
+    const int64_t work = (int64_t)s.T * (s.d / 4);
+    hipLaunchKernelGGL(router_dx_kernel<float>, dim3(grid_for(work, 256)), dim3(256), 0, st, (const float*)dx_perm,
+                       p.tok_ptr, p.tok_rows, p.expert_of_row, p.topk_idx, p.keep_bits, words, dz,
+                       (const float*)wg, s.T, s.E, s.d, s.k, (float*)dx);
   }
   return hipGetLastError();
 }

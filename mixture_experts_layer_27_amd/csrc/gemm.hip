@@ -223,21 +223,6 @@ hipError_t gemm_router_logits(const moe_shape& s, const void* x, const void* wg,
   return run<float, 128, 64, 4, 1, true, true, GROUP_NONE, EPI_LOGITS>(a, a.total_static, st);
 }
 
-// dx[t] = dzq[t] W_g + sum over the rows of t of dx_perm[row]   (router term + unpermute-sum)
-hipError_t gemm_router_dx(const moe_shape& s, const moe_plan& p, const void* dzq, int ldz, const void* wg,
-                          const void* dx_perm, void* dx, hipStream_t st) {
-  Args a = base_args();
-  a.A = dzq; a.lda = ldz;                // [T, K = E]
-  a.B = wg; a.ldb = s.d;                 // W_g [E, d] read as [K = E, N = d]
-  a.C = dx; a.ldc = s.d;
-  a.csr_ptr = p.tok_ptr; a.csr_rows = p.tok_rows; a.gsrc = dx_perm; a.ld_gsrc = s.d;
-  a.M = s.T; a.N = s.d; a.K = s.E;
-  a.tilesM = ceil_div(s.T, 128); a.tilesN = ceil_div(s.d, 128);
-  a.total_static = a.tilesM * a.tilesN;
-  if (s.act == MOE_BF16) return run<bf16_t, 128, 128, 2, 2, true, false, GROUP_NONE, EPI_DX>(a, a.total_static, st);
-  return run<float, 128, 128, 2, 2, true, false, GROUP_NONE, EPI_DX>(a, a.total_static, st);
-}
-
 int gemm_router_dwg_splits(const moe_shape& s) {
   const int tiles = ceil_div(s.E, 128) * ceil_div(s.d, 128);
   int sp = ceil_div(512, tiles);

@@ -13,10 +13,12 @@
 //
 // Stage pipeline per iteration k (LDS double buffer, one barrier):
 //   MFMA block 1 (k16 step 0)  + LDS reads of step 1
-//   MFMA block 2 (step 1)      + LDS writes of stage k+1 from registers, reads of step 2
-//   MFMA block 3 (step 2)      + buffer loads of stage k+2 into the freed registers, reads of step 3
+//   MFMA block 2 (step 1)      + LDS writes of stage k+1 from registers, each followed by the
+//                                buffer load of stage k+2 into the register it freed; reads of step 2
+//   MFMA block 3 (step 2)      + reads of step 3
 //   barrier
 //   MFMA block 4 (step 3)      + reads of step 0 of stage k+1
+// so a load has one full iteration to arrive.
 // The body has no branches: past the last stage the LDS writes land in the idle
 // buffer and the buffer loads are out of range (they return zero, no access).
 // Scheduling-group barriers place one LDS/global instruction after each MFMA.
@@ -213,8 +215,8 @@ MOE_DEV void big_tile(const Args& args, const TileCtx& ctx, char* smem) {
     mma(a0, b0);
     frags(as, 2, a0, b0);
     ra.store(an); rb.store(an + ASZ);
-    mma(a1, b1);
     ra.load(kt + 2); rb.load(kt + 2);
+    mma(a1, b1);
     frags(as, 3, a1, b1);
     mma(a0, b0);
 #pragma unroll
@@ -223,15 +225,15 @@ MOE_DEV void big_tile(const Args& args, const TileCtx& ctx, char* smem) {
       if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
 #pragma unroll
-    for (int i = 0; i < TM * TN; ++i) {          // block 2: MFMA + LDS write (+ fragment read)
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    for (int i = 0; i < TM * TN; ++i) {          // block 2: MFMA + LDS write + the load that refills
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // its registers (+ fragment read)
       if (i < ra.L + rb.L) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+      if (i < ra.L + rb.L) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
 #pragma unroll
-    for (int i = 0; i < TM * TN; ++i) {          // block 3: MFMA + buffer load (+ fragment read)
+    for (int i = 0; i < TM * TN; ++i) {          // block 3: MFMA + fragment read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i < ra.L + rb.L) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);          // this wave's fragment reads and stage writes are done

@@ -29,7 +29,7 @@
 namespace moe_gemm {
 
 enum { GROUP_M = 0, GROUP_K = 1, GROUP_NONE = 2 };
-enum { EPI_ACT = 0, EPI_F32 = 1, EPI_SWIGLU = 2, EPI_DSWIGLU = 3, EPI_LOGITS = 4, EPI_DX = 5,
+enum { EPI_ACT = 0, EPI_F32 = 1, EPI_SWIGLU = 2, EPI_DSWIGLU = 3, EPI_LOGITS = 4,
        EPI_SWIGLU_MX = 6, EPI_DSWIGLU_MX = 7 };   // *_MX: also emit an MXFP8 copy of A / dH
 
 struct Args {
@@ -50,7 +50,6 @@ struct Args {
   // *_MX epilogues: MXFP8 codes [rows][q_ld] and stage-major scales [q_ld/64][q_srows][2] of the
   // quantised output, rows expert-padded (row r of expert e at r - offsets[e] + q_pad[e])
   uint8_t* q_codes; uint8_t* q_scales; int64_t q_ld; int64_t q_srows; const int32_t* q_pad;
-  const int32_t* csr_ptr; const int32_t* csr_rows; const void* gsrc; int64_t ld_gsrc;
   int M, N, K, E, f;
   int tilesM, tilesN;
   int total_static;             // GROUP_K / GROUP_NONE: number of logical tiles
@@ -431,35 +430,6 @@ MOE_DEV void gemm_epilogue(const Args& args, const TileCtx& ctx, f32x16 (&acc)[B
 #pragma unroll
         for (int o = 1; o < CPR; o <<= 1) part += __shfl_xor(part, o, 64);
         if (ch == 0 && grow < row_end) args.C3[(int64_t)nt * args.ldc3 + grow] = part;
-      }
-    } else if constexpr (EPI == EPI_DX) {
-      // dx[t, c] = acc + sum over the rows of t of gsrc[row, c]  (router term + unpermute-sum)
-      T* C = reinterpret_cast<T*>(args.C);
-      const T* G = reinterpret_cast<const T*>(args.gsrc);
-      for (int u = threadIdx.x; u < WTM * CPR; u += NT) {
-        const int rr = u / CPR, ch = u % CPR;
-        const int t = m0 + r0 + rr;
-        const int col = n0 + ch * 8;
-        if (t >= args.M || col >= args.N) continue;
-        const float* src = cs + rr * CS + ch * 8;
-        float v[8];
-#pragma unroll
-        for (int c = 0; c < 8; ++c) v[c] = src[c];
-        const int p0 = args.csr_ptr[t], p1 = args.csr_ptr[t + 1];
-        for (int pb = p0; pb < p1; pb += 4) {
-          // up to four rows in flight, added in ascending row order
-          float w4[4][8];
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (pb + q < p1) Vec8<T>::load(G + (int64_t)args.csr_rows[pb + q] * args.ld_gsrc + col, w4[q]);
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (pb + q < p1) {
-#pragma unroll
-              for (int c = 0; c < 8; ++c) v[c] += w4[q][c];
-            }
-        }
-        Vec8<T>::store(C + (int64_t)t * args.ldc + col, v);
       }
     } else {
       // EPI_ACT (act dtype), EPI_F32 (fp32, split-K partials / per-expert slabs), EPI_LOGITS (+ bias)

@@ -55,6 +55,8 @@ struct WgradChunks {
 hipError_t launch_permute_rows(const moe_shape& s, const void* src, const moe_plan& p, void* dst, hipStream_t st);
 hipError_t launch_combine(const moe_shape& s, const void* y, const moe_plan& p, void* out,
                           hipStream_t st);
+hipError_t launch_router_dx(const moe_shape& s, const moe_plan& p, const void* dx_perm, const float* dz,
+                            const void* wg, void* dx, hipStream_t st);
 hipError_t launch_router_bwd(const moe_shape& s, const moe_plan& p, const float* ds_part, int nparts,
                              float* ds_out, float* dlogits, void* dzq, int ldz, hipStream_t st);
 hipError_t launch_splitk_reduce(const float* part, int nsplit, int64_t n, float* out, hipStream_t st);
@@ -82,8 +84,6 @@ hipError_t gemm_dw2(const moe_shape& s, const WgradChunks& w, const void* do_per
                     hipStream_t st);
 hipError_t gemm_router_logits(const moe_shape& s, const void* x, const void* wg, const float* bias,
                               float* logits, hipStream_t st);
-hipError_t gemm_router_dx(const moe_shape& s, const moe_plan& p, const void* dzq, int ldz, const void* wg,
-                          const void* dx_perm, void* dx, hipStream_t st);
 int gemm_router_dwg_splits(const moe_shape& s);
 hipError_t gemm_router_dwg(const moe_shape& s, const void* dzq, int ldz, const void* x, float* part,
                            hipStream_t st);
