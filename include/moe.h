@@ -153,7 +153,9 @@ moe_status moe_unpermute_combine(const moe_shape *s, const void *y, const moe_pl
                                  void *out, void *stream);
 
 /* Backward for the loss sum_t <out_t, dout_t>.
- *   Inputs: x [T,d], w_gate [E,d], w1, w2, the plan, h_saved, dout [T,d].
+ *   Inputs: x [T,d], w_gate [E,d], w1, w2, the plan, h_saved, dout [T,d];
+ *   x_perm [N_max,d] (act) = what moe_permute wrote for x with this plan, or NULL
+ *   (then x is permuted again into the workspace; the results are identical).
  *   Outputs: dx [T,d] (act), dw_gate [E,d] f32, dw1 [E,2f,d] f32, dw2 [E,d,f] f32;
  *   optional dlogits [T,E] f32 and ds [N_max] f32 (per-row gate gradient) when
  *   not NULL.
@@ -164,7 +166,7 @@ moe_status moe_unpermute_combine(const moe_shape *s, const void *y, const moe_pl
  * loaded.  ws: moe_workspace_bytes(s, MOE_WS_BACKWARD) bytes, 16-byte aligned
  * (it includes the partial slabs and, with MXFP8, the quantised operands). */
 moe_status moe_backward(const moe_shape *s, const void *x, const void *w_gate, const void *w1,
-                        const void *w2, const moe_plan *plan, const void *h_saved,
+                        const void *w2, const moe_plan *plan, const void *h_saved, const void *x_perm,
                         const void *dout, void *dx, float *dw_gate, float *dw1, float *dw2,
                         float *dlogits, float *ds, void *ws, size_t ws_bytes, void *stream);
 

@@ -330,12 +330,14 @@ moe_status moe_unpermute_combine(const moe_shape* s, const void* y, const moe_pl
 }
 
 moe_status moe_backward(const moe_shape* s, const void* x, const void* w_gate, const void* w1, const void* w2,
-                        const moe_plan* plan, const void* h_saved, const void* dout, void* dx, float* dw_gate,
+                        const moe_plan* plan, const void* h_saved, const void* x_perm, const void* dout, void* dx,
+                        float* dw_gate,
                         float* dw1, float* dw2, float* dlogits, float* ds, void* ws, size_t ws_bytes, void* stream) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
   if (!aligned(x) || !aligned(w_gate) || !aligned(w1) || !aligned(w2) || !aligned(h_saved) || !aligned(dout) ||
       !aligned(dx) || !aligned(dw_gate) || !aligned(dw1) || !aligned(dw2) || !aligned_or_null(dlogits) ||
+      !aligned_or_null(x_perm) ||
       (ds && (reinterpret_cast<uintptr_t>(ds) & 3)))
     return MOE_EINVAL;
   if ((st = check_plan(*s, plan)) != MOE_OK) return st;
@@ -357,9 +359,10 @@ moe_status moe_backward(const moe_shape* s, const void* x, const void* w_gate, c
     if (e == hipSuccess) e = mx_quantize_cols(w2, E, d, f, w.w2t.codes, w.w2t.scales, hs);
     if (e == hipSuccess) e = gemm_mx_dact(*s, *plan, pi, w.doq, w.w2t, h_saved, w.dh, w.dhq, w.ga, w.ds_part, hs);
     if (e == hipSuccess) e = mx_quantize_cols(w1, E, 2 * f, d, w.w1t.codes, w.w1t.scales, hs);
-    if (e == hipSuccess) e = launch_permute_rows(*s, x, *plan, w.xbuf, hs);
+    if (e == hipSuccess && !x_perm) e = launch_permute_rows(*s, x, *plan, w.xbuf, hs);
+    const void* xp = x_perm ? x_perm : w.xbuf;
     if (e == hipSuccess) e = mx_quantize_tokens(w.dh, 2 * f, plan->offsets, w.pad_off, E, P, w.dh_t.codes, w.dh_t.scales, hs);
-    if (e == hipSuccess) e = mx_quantize_tokens(w.xbuf, d, plan->offsets, w.pad_off, E, P, w.x_t.codes, w.x_t.scales, hs);
+    if (e == hipSuccess) e = mx_quantize_tokens(xp, d, plan->offsets, w.pad_off, E, P, w.x_t.codes, w.x_t.scales, hs);
     if (e == hipSuccess) e = mx_quantize_tokens(w.do_perm, d, plan->offsets, w.pad_off, E, P, w.do_t.codes, w.do_t.scales, hs);
     if (e == hipSuccess) e = mx_quantize_tokens(w.ga, f, plan->offsets, w.pad_off, E, P, w.ga_t.codes, w.ga_t.scales, hs);
     if (e == hipSuccess) e = launch_wgrad_chunks(w.pad_off, E, w.wg.kch, w.wg, hs);
@@ -367,16 +370,17 @@ moe_status moe_backward(const moe_shape* s, const void* x, const void* w_gate, c
     if (e == hipSuccess) e = launch_wgrad_reduce(w.wg, E, (int64_t)2 * f * d, dw1, hs);
     if (e == hipSuccess) e = gemm_mx_wgrad(*s, w.wg, P, w.do_t, d, w.ga_t, f, dw2, hs);
     if (e == hipSuccess) e = launch_wgrad_reduce(w.wg, E, (int64_t)d * f, dw2, hs);
-    if (e == hipSuccess) e = gemm_mx_dx_perm(*s, *plan, pi, w.dhq, w.w1t, w.xbuf, hs);   // x_perm no longer needed
+    if (e == hipSuccess) e = gemm_mx_dx_perm(*s, *plan, pi, w.dhq, w.w1t, w.xbuf, hs);   // dx_perm (x_perm no longer needed)
   } else {
     if (e == hipSuccess) e = gemm_dact(*s, *plan, pi, w.do_perm, w2, h_saved, w.dh, w.ga, w.ds_part, hs);
-    if (e == hipSuccess) e = launch_permute_rows(*s, x, *plan, w.xbuf, hs);
+    if (e == hipSuccess && !x_perm) e = launch_permute_rows(*s, x, *plan, w.xbuf, hs);
+    const void* xp = x_perm ? x_perm : w.xbuf;
     if (e == hipSuccess) e = launch_wgrad_chunks(plan->offsets, s->E, w.wg.kch, w.wg, hs);
-    if (e == hipSuccess) e = gemm_dw1(*s, w.wg, w.dh, w.xbuf, dw1, hs);
+    if (e == hipSuccess) e = gemm_dw1(*s, w.wg, w.dh, xp, dw1, hs);
     if (e == hipSuccess) e = launch_wgrad_reduce(w.wg, s->E, (int64_t)2 * s->d_ff * s->d, dw1, hs);
     if (e == hipSuccess) e = gemm_dw2(*s, w.wg, w.do_perm, w.ga, dw2, hs);
     if (e == hipSuccess) e = launch_wgrad_reduce(w.wg, s->E, (int64_t)s->d * s->d_ff, dw2, hs);
-    if (e == hipSuccess) e = gemm_dx_perm(*s, *plan, pi, w.dh, w1, w.xbuf, hs);   // x_perm no longer needed
+    if (e == hipSuccess) e = gemm_dx_perm(*s, *plan, pi, w.dh, w1, w.xbuf, hs);   // dx_perm (x_perm no longer needed)
   }
   if (e == hipSuccess)
     e = launch_router_bwd(*s, *plan, w.ds_part, gemm_dact_parts(*s), ds, dz, w.dzq, ldz, hs);

@@ -108,15 +108,16 @@ def test_backward(name):
 @pytest.mark.parametrize("name", ["sparse_round_small", "fine_zipf_small", "mx_zipf_small"])
 def test_bitwise_deterministic(name):
     """Two runs give identical bits (rounding; weight gradients summed over several
-    K chunks of one heavily loaded expert; the MXFP8 path)."""
+    K chunks of one heavily loaded expert; the MXFP8 path).  The first backward
+    reads the forward's permuted x, the second permutes x itself."""
     from mixture_experts_layer_27_amd import binding
     cfg = CASES[name]
     g = make_inputs(cfg)
     outs = []
-    for _ in range(2):
+    for rep in range(2):
         run = binding.LayerRun(cfg, g)
         run.forward()
-        run.backward()
+        run.backward(reuse_x_perm=(rep == 0))
         torch.cuda.synchronize()
         n = int(run.plan.arrays()["offsets"][-1].item())      # rows past N are never written
         outs.append([t.clone() for t in (run.out, run.h[:n], run.y[:n], run.ds[:n], run.dx, run.dw_gate,
