@@ -56,7 +56,7 @@ hipError_t run_big(const Args& a, int64_t logical_tiles, hipStream_t st) {
   if (e != hipSuccess) return e;
   const int64_t grid = 8 * ((logical_tiles + 7) / 8);
   if (grid <= 0) return hipSuccess;
-  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(256), lds, st, a);
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBigThreads), lds, st, a);
   return hipGetLastError();
 }
 
@@ -121,9 +121,9 @@ hipError_t gemm_down(const moe_shape& s, const moe_plan& p, const PlanInternal& 
 // one per column tile on the fp32 path
 int gemm_dact_parts(const moe_shape& s) {
   if (s.act != MOE_BF16) return ceil_div(s.d_ff, 128);
-  // 128-column wave tiles over ceil(f / 512) 512-column quanta (bf16, deep K), or
-  // 64-column ones over 256-column tiles (the MXFP8 kernel, and bf16 with shallow K)
-  if (s.gemm == MOE_BF16 && use_big(s.d)) return ceil_div(s.d_ff, 512) * 4;
+  // 64-column wave tiles: over ceil(f / 512) 512-column quanta (bf16, deep K), or
+  // over 256-column tiles (the MXFP8 kernel, and bf16 with shallow K)
+  if (s.gemm == MOE_BF16 && use_big(s.d)) return ceil_div(s.d_ff, 512) * 8;
   return ceil_div(s.d_ff, 256) * 4;
 }
 

@@ -1,15 +1,17 @@
 // Register-staged bf16 main loop for the grouped expert GEMMs on gfx950:
-// 4 waves per block, each wave a 128 x 128 output tile (4 x 4 MFMA 32x32x16
-// sub-tiles, 256 accumulator registers), K in stages of 64.
+// 8 waves per block (two per SIMD), each wave a 128 x 64 output tile (4 x 2 MFMA
+// 32x32x16 sub-tiles, 128 accumulator registers), K in stages of 64.
 //
 // Why this shape: a CU is fed about 35-40 GB/s of operand data from L2 in
 // these GEMMs, so output area per byte fetched decides the MFMA rate.  A
 // 256 x 256 block tile fetches 64 KiB per 64-deep stage for 8.4 MFLOP, half
-// again more work per byte than a 128 x 256 tile.  The price is one wave per
-// SIMD (the accumulators alone take 256 registers), so latency is hidden inside
-// the wave: global loads for stage k+2 are in flight in registers while stage k
-// is multiplied and stage k+1 is written to LDS, and every group of 16 MFMAs
-// runs with the fragments of the next group already being read.
+// again more work per byte than a 128 x 256 tile, and one such block fills a
+// CU's LDS.  Two waves per SIMD let one wave's MFMAs cover the other's waits
+// (barrier, fragment reads, load arrivals); that beats four 128 x 128 waves,
+// which read fewer fragment bytes from LDS but stall alone.  Within a wave,
+// global loads for stage k+2 are in flight in registers while stage k is
+// multiplied and stage k+1 is written to LDS, and every group of MFMAs runs
+// with the fragments of the next group already being read.
 //
 // Stage pipeline per iteration k (LDS double buffer, one barrier):
 //   MFMA block 1 (k16 step 0)  + LDS reads of step 1
@@ -29,8 +31,9 @@
 //
 // Tile shapes.  GROUP_K (weight gradients): 256 x 256 tiles.  GROUP_M (row
 // segments of experts): segments are covered in units of 128 rows; each pair of
-// units is a 256 x 256 ("tall") tile, an odd last unit a 128 x 512 ("wide")
-// tile, so a segment's padding is at most 127 rows, as with 128-row tiles.  A
+// units is a 256 x 256 ("tall", 2 x 4 waves) tile, an odd last unit a 128 x 512
+// ("wide", 1 x 8 waves) tile, so a segment's padding is at most 127 rows, as
+// with 128-row tiles.  A
 // tall tile pair of n-tiles and a wide tile cover the same area, so logical
 // tile L = unit * ceil(N / 512) + c indexes both with the plan's 128-row unit
 // tables.
@@ -44,18 +47,22 @@
 namespace moe_gemm {
 
 constexpr int kBigBK = 64;
+constexpr int kBigThreads = 512;
 constexpr uint32_t kBufferFlags = 0x00020000;   // gfx9 raw buffer: 32-bit dwords, no swizzle
 
 MOE_DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, (int)kBufferFlags);
 }
 
-// One operand tile (ROWS rows x 64 k, bf16) staged through registers by 256
-// threads, ROWS / 32 16-byte loads each.  Load i of a thread lands 4 KiB after
-// load i - 1 in LDS for both layouts (32 K-contiguous rows, or 2048 / ROWS k rows).
-template <int ROWS, bool KC>
+// One operand tile (ROWS rows x 64 k, bf16) staged through registers by NT
+// threads, ROWS * 8 / NT 16-byte loads each.  Load i of a thread lands NT * 16
+// bytes after load i - 1 in LDS for both layouts (NT / 8 K-contiguous rows, or
+// NT * 8 / ROWS k rows, a multiple of 4 so the k-row swizzle repeats).
+template <int ROWS, bool KC, int NT>
 struct RegOperand {
-  static constexpr int L = ROWS / 32;
+  static constexpr int L = ROWS * 8 / NT;
+  static constexpr int STEP = NT * 16;
+  static_assert(L >= 1 && (NT * 8 / ROWS) % 4 == 0, "block shape");
   uint32_t voff[L];         // byte offset of each load from the stage's base
   int lds0;                 // LDS byte offset of load 0
   u32x4 v[L];
@@ -70,12 +77,12 @@ struct RegOperand {
     const int t = threadIdx.x, c = t & 7, r0 = t >> 3;
     lds0 = r0 * 128 + ((c ^ kc8_h(r0)) << 4);
 #pragma unroll
-    for (int i = 0; i < L; ++i) voff[i] = (uint32_t)(row_off(r0 + 32 * i) + c * 16);
+    for (int i = 0; i < L; ++i) voff[i] = (uint32_t)(row_off(r0 + (NT / 8) * i) + c * 16);
   }
   // M/N-contiguous: k rows ld elements apart, the tile's columns contiguous
   MOE_DEV void init_mn(int64_t ld) {
     constexpr int CPK = ROWS / 8;          // 16-byte chunks per k row
-    constexpr int KPP = 256 / CPK;         // k rows per pass of the block
+    constexpr int KPP = NT / CPK;          // k rows per pass of the block
     const int t = threadIdx.x, cc = t % CPK, k0 = t / CPK;
     lds0 = mn_off<ROWS>(k0, cc * 16);
 #pragma unroll
@@ -90,7 +97,7 @@ struct RegOperand {
   }
   MOE_DEV void store(char* stage) const {
 #pragma unroll
-    for (int i = 0; i < L; ++i) *reinterpret_cast<u32x4*>(stage + lds0 + 4096 * i) = v[i];
+    for (int i = 0; i < L; ++i) *reinterpret_cast<u32x4*>(stage + lds0 + STEP * i) = v[i];
   }
 };
 
@@ -100,14 +107,15 @@ constexpr size_t big_lds_bytes(bool wide) {
   return wide ? big_ring_bytes<128, 512>() : big_ring_bytes<256, 256>();
 }
 
-// One output tile: BM x BN with WM x WN waves of 128 x 128.
+// One output tile: BM x BN with WM x WN waves of 128 x 64.
 template <int BM, int BN, int WM, int WN, bool AKC, bool BKC, int GROUP, int EPI>
 MOE_DEV void big_tile(const Args& args, const TileCtx& ctx, char* smem) {
   using T = bf16_t;
   constexpr int BK = kBigBK;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
-  static_assert(WM * WN == 4 && WTM == 128 && WTN == 128, "four waves of 128 x 128");
+  constexpr int NT = WM * WN * 64;
+  static_assert(NT == kBigThreads && WTM == 128 && WTN == 64, "eight waves of 128 x 64");
   constexpr int ASZ = BM * BK * 2, BSZ = BN * BK * 2, STAGE = ASZ + BSZ;
   const int e = ctx.e, nt = ctx.nt;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -115,8 +123,8 @@ MOE_DEV void big_tile(const Args& args, const TileCtx& ctx, char* smem) {
   const char* Ab = reinterpret_cast<const char*>(args.A) + (int64_t)e * args.a_estride * 2;
   const char* Bb = reinterpret_cast<const char*>(args.B) + (int64_t)e * args.b_estride * 2;
 
-  RegOperand<BM, AKC> ra;
-  RegOperand<BN, BKC> rb;
+  RegOperand<BM, AKC, NT> ra;
+  RegOperand<BN, BKC, NT> rb;
   if constexpr (AKC) {   // GROUP_M: rows row_begin.. of the segment, K contiguous
     const int nrows = min(BM, ctx.row_end - ctx.row_begin);
     const int64_t rowb = args.lda * 2;
@@ -289,18 +297,18 @@ MOE_DEV bool big_decode_m(const Args& args, TileCtx& c, bool* wide) {
 }
 
 template <bool AKC, bool BKC, int GROUP, int EPI>
-__global__ __launch_bounds__(256) void grouped_gemm_big(Args args) {
+__global__ __launch_bounds__(kBigThreads) void grouped_gemm_big(Args args) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   static_assert(GROUP == GROUP_M || GROUP == GROUP_K, "grouped GEMMs only");
   TileCtx ctx;
   if constexpr (GROUP == GROUP_K) {
     if (!decode_tile<256, 256, kBigBK, GROUP_K>(args, ctx)) return;
-    big_tile<256, 256, 2, 2, AKC, BKC, GROUP, EPI>(args, ctx, smem);
+    big_tile<256, 256, 2, 4, AKC, BKC, GROUP, EPI>(args, ctx, smem);
   } else {
     bool wide = false;
     if (!big_decode_m(args, ctx, &wide)) return;
-    if (wide) big_tile<128, 512, 1, 4, AKC, BKC, GROUP, EPI>(args, ctx, smem);
-    else big_tile<256, 256, 2, 2, AKC, BKC, GROUP, EPI>(args, ctx, smem);
+    if (wide) big_tile<128, 512, 1, 8, AKC, BKC, GROUP, EPI>(args, ctx, smem);
+    else big_tile<256, 256, 2, 4, AKC, BKC, GROUP, EPI>(args, ctx, smem);
   }
 }
 
