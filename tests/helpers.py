@@ -19,6 +19,9 @@ CASES = {
     "single_expert": configs.FINE.scaled("single_expert", T=300, d=128, E=1, k=1, f=128),
     "k_equals_E": configs.FINE.scaled("k_equals_E", T=200, d=192, E=4, k=4, f=128),
     "one_token": configs.FINE.scaled("one_token", T=1, d=128, E=8, k=2, f=128),
+    # every expert GEMM on the 256x256 kernel (K >= 1024): ragged segments give both
+    # tile kinds, f % 256 == 128 gives n-tiles past f (SwiGLU columns, dS partials)
+    "big_tiles_small": configs.FINE.scaled("big_tiles_small", T=800, d=1024, E=6, k=2, f=1152),
     # MXFP8 expert GEMMs
     "fine_mx_small": configs.FINE_MX.scaled("fine_mx_small", T=1500, d=256, E=32, f=256),
     "sparse_round_mx_small": configs.SPARSE_ROUND.scaled("sparse_round_mx_small", T=1200, d=512, E=64, f=128,
