@@ -167,7 +167,7 @@ __global__ __launch_bounds__(256) void router_dx_kernel(const T* __restrict__ dx
   }
 }
 
-// Router backward, one wave per token.  dS of every row is the fixed-order sum of
+// Router backward, one wave per token.  dS of every row is a fixed-order sum of
 // the per-column-tile partials.  For token t with top-k set K (gates S) and rows
 // A (gates g):  dz_e = [e in A] g_e dS_e - [e in K] S_e * sum_{A} g dS.
 // Writes dlogits (fp32) and the GEMM operand dzq (act dtype, ld = ldz, zero padded).
@@ -185,18 +185,32 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const int32_t* __restri
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T_) return;
-  const int p0 = tok_ptr[t], p1 = tok_ptr[t + 1];
+  const int p0 = tok_ptr[t], p1 = tok_ptr[t + 1], n = p1 - p0;
   float vals[4] = {0.f, 0.f, 0.f, 0.f};   // experts lane, lane+64, lane+128, lane+192
   float acc = 0.0f;
-  for (int p = p0; p < p1; ++p) {
-    const int r = tok_rows[p];
-    float ds = 0.0f;
-    for (int q = 0; q < nparts; ++q) ds += ds_part[q * part_stride + r];
-    if (ds_out && lane == 0) ds_out[r] = ds;
-    const float gds = gate_of_row[r] * ds;
-    acc += gds;
-    const int e = expert_of_row[r];
-    if ((e & 63) == lane) vals[e >> 6] += gds;
+  // the partials of a row are summed by a group of np2 lanes (all loads in flight
+  // at once, then a fixed shuffle tree); 64 / np2 rows per pass
+  int np2 = 1;
+  while (np2 < nparts && np2 < 64) np2 <<= 1;
+  const int rpp = 64 / np2;
+  for (int pb = 0; pb < n; pb += rpp) {
+    const int pi = pb + lane / np2, q0 = lane % np2;
+    float v = 0.0f;
+    int r = 0;
+    if (pi < n) {
+      r = tok_rows[p0 + pi];
+      for (int q = q0; q < nparts; q += np2) v += ds_part[q * part_stride + r];
+    }
+    for (int o = 1; o < np2; o <<= 1) v += __shfl_xor(v, o, 64);
+    for (int u = 0; u < rpp && pb + u < n; ++u) {   // rows in ascending order
+      const float ds = __shfl(v, u * np2, 64);
+      const int rr = __shfl(r, u * np2, 64);
+      if (ds_out && lane == 0) ds_out[rr] = ds;
+      const float gds = gate_of_row[rr] * ds;
+      acc += gds;
+      const int e = expert_of_row[rr];
+      if ((e & 63) == lane) vals[e >> 6] += gds;
+    }
   }
   for (int j = 0; j < k; ++j) {
     const int e = topk_idx[(int64_t)t * k + j];
@@ -255,16 +269,19 @@ __global__ __launch_bounds__(256) void wgrad_chunks_kernel(const int32_t* __rest
 }
 
 // dW[e] += partial slots of e, in slot order (fixed order: deterministic).
+// Every block walks all experts (those without partial slots are skipped at
+// once), so a heavily loaded expert's partials are spread over the whole grid.
 __global__ __launch_bounds__(256) void wgrad_reduce_kernel(float* __restrict__ dw, const float* __restrict__ part,
-                                                          const int2* __restrict__ slot_range, int64_t mn) {
-  const int e = blockIdx.y;
-  const int2 sr = slot_range[e];
-  if (sr.y <= sr.x) return;
-  float* out = dw + (int64_t)e * mn;
-  for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; i < mn; i += (int64_t)gridDim.x * 256 * 4) {
-    f32x4 a = *reinterpret_cast<const f32x4*>(out + i);
-    for (int s = sr.x; s < sr.y; ++s) a += *reinterpret_cast<const f32x4*>(part + (int64_t)s * mn + i);
-    *reinterpret_cast<f32x4*>(out + i) = a;
+                                                          const int2* __restrict__ slot_range, int E, int64_t mn) {
+  for (int e = 0; e < E; ++e) {
+    const int2 sr = slot_range[e];
+    if (sr.y <= sr.x) continue;
+    float* out = dw + (int64_t)e * mn;
+    for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; i < mn; i += (int64_t)gridDim.x * 256 * 4) {
+      f32x4 a = *reinterpret_cast<const f32x4*>(out + i);
+      for (int s = sr.x; s < sr.y; ++s) a += *reinterpret_cast<const f32x4*>(part + (int64_t)s * mn + i);
+      *reinterpret_cast<f32x4*>(out + i) = a;
+    }
   }
 }
 
@@ -345,7 +362,7 @@ hipError_t launch_wgrad_chunks(const int32_t* offsets, int E, int kch, const Wgr
 
 hipError_t launch_wgrad_reduce(const WgradChunks& w, int E, int64_t mn, float* dw, hipStream_t st) {
   if (w.max_extra == 0) return hipSuccess;
-  hipLaunchKernelGGL(wgrad_reduce_kernel, dim3(256, E), dim3(256), 0, st, dw, w.part, w.slot_range, mn);
+  hipLaunchKernelGGL(wgrad_reduce_kernel, dim3(1024), dim3(256), 0, st, dw, w.part, w.slot_range, E, mn);
   return hipGetLastError();
 }
 
