@@ -56,27 +56,41 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const bf16_t* __rest
   // total is a multiple of 4 (K % 32 == 0) and so are the start and the stride:
   // the four lanes of a quad (one block) always iterate together
   const int64_t total = nr * chunks;
-  for (int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x; q < total; q += (int64_t)gridDim.x * 256) {
-    const int64_t r = q / chunks, ch = q - r * chunks;
-    float v[8];
-    unpack8(ldg16(src + r * K + ch * 8), v);
-    float amax = 0.0f;
+  const int64_t S = (int64_t)gridDim.x * 256;
+  for (int64_t q0 = (int64_t)blockIdx.x * 256 + threadIdx.x; q0 < total; q0 += 4 * S) {
+    // four chunks per thread, all loads issued first
+    u32x4 raw[4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
-    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
-    const int X = mx_exponent(amax);
-    int64_t dr = r;
-    if (offsets) {
-      const int e = expert_of_row[r];
-      dr = r - offsets[e] + pad_off[e];
+    for (int u = 0; u < 4; ++u) {
+      const int64_t q = q0 + u * S;
+      const int64_t r = q / chunks, ch = q - r * chunks;
+      raw[u] = q < total ? ldg16(src + r * K + ch * 8) : u32x4{0u, 0u, 0u, 0u};
     }
-    *reinterpret_cast<uint2*>(codes + dr * K + ch * 8) = e4m3_8(v, pow2f(-X));
-    if ((q & 3) == 0) {
-      const int64_t c = ch >> 2;   // 32-block index along K
-      const uint8_t sb = (uint8_t)(X + 127);
-      if (staged) scales[((c >> 1) * srows + dr) * 2 + (c & 1)] = sb;
-      else scales[dr * (K / 32) + c] = sb;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t q = q0 + u * S;
+      if (q >= total) break;   // uniform over each quad (total, q0 - lane % 4 and S are multiples of 4)
+      const int64_t r = q / chunks, ch = q - r * chunks;
+      float v[8];
+      unpack8(raw[u], v);
+      float amax = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+      amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+      amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+      const int X = mx_exponent(amax);
+      int64_t dr = r;
+      if (offsets) {
+        const int e = expert_of_row[r];
+        dr = r - offsets[e] + pad_off[e];
+      }
+      *reinterpret_cast<uint2*>(codes + dr * K + ch * 8) = e4m3_8(v, pow2f(-X));
+      if ((q & 3) == 0) {
+        const int64_t c = ch >> 2;   // 32-block index along K
+        const uint8_t sb = (uint8_t)(X + 127);
+        if (staged) scales[((c >> 1) * srows + dr) * 2 + (c & 1)] = sb;
+        else scales[dr * (K / 32) + c] = sb;
+      }
     }
   }
 }
@@ -126,16 +140,22 @@ __global__ __launch_bounds__(256) void quantize_t_kernel(const bf16_t* __restric
       valid[hh] = 64;
     }
   }
-  // 128 rows x 64 columns: 8 threads per row, 16 bytes each
-  for (int i = threadIdx.x; i < 128 * 8; i += 256) {
+  // 128 rows x 64 columns: 8 threads per row, 16 bytes each; all four loads of a
+  // thread are issued before any of them is used
+  u32x4 raw[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = threadIdx.x + 256 * u;
     const int rr = i >> 3, ch = i & 7;
     const int hh = rr >> 6, rl = rr & 63;
-    float v[8];
-    if (rl < valid[hh]) unpack8(ldg16(src + (base[hh] + rl) * C + c0 + ch * 8), v);
-    else {
+    raw[u] = rl < valid[hh] ? ldg16(src + (base[hh] + rl) * C + c0 + ch * 8) : u32x4{0u, 0u, 0u, 0u};
+  }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) v[j] = 0.0f;
-    }
+  for (int u = 0; u < 4; ++u) {
+    const int i = threadIdx.x + 256 * u;
+    const int rr = i >> 3, ch = i & 7;
+    float v[8];
+    unpack8(raw[u], v);
 #pragma unroll
     for (int j = 0; j < 8; ++j) tile[rr][ch * 8 + j] = v[j];
   }
