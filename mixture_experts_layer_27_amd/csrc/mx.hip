@@ -38,39 +38,54 @@ MOE_DEV void unpack8(u32x4 q, float* v) {
 
 namespace {
 
-// (1) along rows.  Lane i of a wave loads 16 bytes (8 values) at consecutive
-// addresses, so four lanes hold one 32-value block: the block maximum is
-// reduced across the quad, every lane writes its 8 codes, the first lane of the
-// quad the scale byte.  Scale layouts: plain [rows][K/32] (staged == 0, the test
-// hook) or stage-major [K/64][srows][2].  With `offsets` the source is a
-// permuted activation: only its offsets[E] rows in use are read, and row r of
-// expert e lands at row r - offsets[e] + pad_off[e].
+// (1) along rows.  One tile = 32 rows x 128 values (four 32-blocks of each
+// row); its 512 16-byte chunks are loaded two per thread, all loads first.  Four
+// consecutive lanes hold one block: its maximum is reduced across the quad and
+// every lane writes its 8 codes.  The tile's scale bytes are gathered in LDS and
+// written per row (2 bytes per 64-value step of a row, or 4 bytes per row in the
+// plain layout), not one byte per quad.  Scale layouts: plain [rows][K/32]
+// (staged == 0, the test hook) or stage-major [K/64][srows][2].  With `offsets`
+// the source is a permuted activation: only its offsets[E] rows in use are read,
+// and row r of expert e lands at row r - offsets[e] + pad_off[e].
 __global__ __launch_bounds__(256) void quantize_rows_kernel(const bf16_t* __restrict__ src, int64_t rows, int64_t K,
                                                            uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
                                                            int64_t srows, int staged,
                                                            const int32_t* __restrict__ offsets,
                                                            const int32_t* __restrict__ expert_of_row,
                                                            const int32_t* __restrict__ pad_off, int E) {
-  const int64_t chunks = K / 8;   // 16-byte chunks per row
+  __shared__ uint8_t sc[32][4];    // [tile row][block of the tile]
+  __shared__ int64_t drow[32];     // destination row of each tile row (-1: none)
   const int64_t nr = offsets ? (int64_t)offsets[E] : rows;
-  // total is a multiple of 4 (K % 32 == 0) and so are the start and the stride:
-  // the four lanes of a quad (one block) always iterate together
-  const int64_t total = nr * chunks;
-  const int64_t S = (int64_t)gridDim.x * 256;
-  for (int64_t q0 = (int64_t)blockIdx.x * 256 + threadIdx.x; q0 < total; q0 += 4 * S) {
-    // four chunks per thread, all loads issued first
-    u32x4 raw[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t q = q0 + u * S;
-      const int64_t r = q / chunks, ch = q - r * chunks;
-      raw[u] = q < total ? ldg16(src + r * K + ch * 8) : u32x4{0u, 0u, 0u, 0u};
+  const int64_t ktiles = (K + 127) / 128;
+  const int64_t ntiles = ((nr + 31) / 32) * ktiles;
+  const int t = threadIdx.x;
+  for (int64_t tl = blockIdx.x; tl < ntiles; tl += gridDim.x) {
+    const int64_t r0 = (tl / ktiles) * 32, k0 = (tl % ktiles) * 128;
+    if (t < 32) {
+      const int64_t r = r0 + t;
+      int64_t dr = -1;
+      if (r < nr) {
+        dr = r;
+        if (offsets) {
+          const int e = expert_of_row[r];
+          dr = r - offsets[e] + pad_off[e];
+        }
+      }
+      drow[t] = dr;
     }
+    u32x4 raw[2];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t q = q0 + u * S;
-      if (q >= total) break;   // uniform over each quad (total, q0 - lane % 4 and S are multiples of 4)
-      const int64_t r = q / chunks, ch = q - r * chunks;
+    for (int u = 0; u < 2; ++u) {
+      const int i = t + 256 * u;            // row i >> 4, 8-value chunk i & 15
+      const int64_t r = r0 + (i >> 4), kk = k0 + (i & 15) * 8;
+      raw[u] = (r < nr && kk < K) ? ldg16(src + r * K + kk) : u32x4{0u, 0u, 0u, 0u};
+    }
+    __syncthreads();                          // drow visible
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int i = t + 256 * u;
+      const int rl = i >> 4, ch = i & 15;
+      const int64_t kk = k0 + ch * 8;
       float v[8];
       unpack8(raw[u], v);
       float amax = 0.0f;
@@ -79,19 +94,30 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const bf16_t* __rest
       amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
       amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
       const int X = mx_exponent(amax);
-      int64_t dr = r;
-      if (offsets) {
-        const int e = expert_of_row[r];
-        dr = r - offsets[e] + pad_off[e];
-      }
-      *reinterpret_cast<uint2*>(codes + dr * K + ch * 8) = e4m3_8(v, pow2f(-X));
-      if ((q & 3) == 0) {
-        const int64_t c = ch >> 2;   // 32-block index along K
-        const uint8_t sb = (uint8_t)(X + 127);
-        if (staged) scales[((c >> 1) * srows + dr) * 2 + (c & 1)] = sb;
-        else scales[dr * (K / 32) + c] = sb;
+      const int64_t dr = drow[rl];
+      if (dr >= 0 && kk < K) {               // uniform over the quad (K % 32 == 0)
+        *reinterpret_cast<uint2*>(codes + dr * K + kk) = e4m3_8(v, pow2f(-X));
+        if ((ch & 3) == 0) sc[rl][ch >> 2] = (uint8_t)(X + 127);
       }
     }
+    __syncthreads();                          // sc complete
+    if (t < 64) {                             // one thread per (row, 64-value step)
+      const int rl = t >> 1, s = t & 1;
+      const int64_t dr = drow[rl], kb = k0 + 64 * s;   // first value of the step
+      if (dr >= 0 && kb < K) {
+        const int nb = K - kb >= 64 ? 2 : 1;   // blocks of this step inside K
+        if (staged) {
+          uint8_t* dst = scales + ((kb >> 6) * srows + dr) * 2;
+          if (nb == 2) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)(sc[rl][2 * s] | (sc[rl][2 * s + 1] << 8));
+          else dst[0] = sc[rl][2 * s];
+        } else {
+          uint8_t* dst = scales + dr * (K / 32) + (kb >> 5);
+          dst[0] = sc[rl][2 * s];
+          if (nb == 2) dst[1] = sc[rl][2 * s + 1];
+        }
+      }
+    }
+    __syncthreads();                          // sc and drow reused by the next tile
   }
 }
 
@@ -216,9 +242,12 @@ int qgrid(int64_t threads) {
 
 }  // namespace
 
+// one block per 32-row x 128-value tile (grid-strided past 16384 tiles)
+int rows_grid(int64_t rows, int64_t K) { return qgrid(((rows + 31) / 32) * ((K + 127) / 128) * 256); }
+
 hipError_t launch_quantize_rows(const void* src, int64_t rows, int64_t cols, uint8_t* codes, uint8_t* scales,
                                 hipStream_t st) {
-  hipLaunchKernelGGL(quantize_rows_kernel, dim3(qgrid(rows * (cols / 8))), dim3(256), 0, st, (const bf16_t*)src,
+  hipLaunchKernelGGL(quantize_rows_kernel, dim3(rows_grid(rows, cols)), dim3(256), 0, st, (const bf16_t*)src,
                      rows, cols, codes, scales, (int64_t)0, 0, (const int32_t*)nullptr, (const int32_t*)nullptr,
                      (const int32_t*)nullptr, 0);
   return hipGetLastError();
@@ -226,7 +255,7 @@ hipError_t launch_quantize_rows(const void* src, int64_t rows, int64_t cols, uin
 
 hipError_t mx_quantize_rows_staged(const void* src, int64_t rows, int64_t K, uint8_t* codes, uint8_t* scales,
                                    int64_t srows, hipStream_t st) {
-  hipLaunchKernelGGL(quantize_rows_kernel, dim3(qgrid(rows * (K / 8))), dim3(256), 0, st, (const bf16_t*)src, rows,
+  hipLaunchKernelGGL(quantize_rows_kernel, dim3(rows_grid(rows, K)), dim3(256), 0, st, (const bf16_t*)src, rows,
                      K, codes, scales, srows, 1, (const int32_t*)nullptr, (const int32_t*)nullptr,
                      (const int32_t*)nullptr, 0);
   return hipGetLastError();
@@ -235,7 +264,7 @@ hipError_t mx_quantize_rows_staged(const void* src, int64_t rows, int64_t K, uin
 hipError_t mx_quantize_rows_padded(const void* src, int64_t rows, int64_t K, const int32_t* offsets,
                                    const int32_t* expert_of_row, const int32_t* pad_off, int E, uint8_t* codes,
                                    uint8_t* scales, int64_t srows, hipStream_t st) {
-  hipLaunchKernelGGL(quantize_rows_kernel, dim3(qgrid(rows * (K / 8))), dim3(256), 0, st, (const bf16_t*)src, rows,
+  hipLaunchKernelGGL(quantize_rows_kernel, dim3(rows_grid(rows, K)), dim3(256), 0, st, (const bf16_t*)src, rows,
                      K, codes, scales, srows, 1, offsets, expert_of_row, pad_off, E);
   return hipGetLastError();
 }
