@@ -22,6 +22,10 @@ CASES = {
     # every expert GEMM on the 256x256 kernel (K >= 1024): ragged segments give both
     # tile kinds, f % 256 == 128 gives n-tiles past f (SwiGLU columns, dS partials)
     "big_tiles_small": configs.FINE.scaled("big_tiles_small", T=800, d=1024, E=6, k=2, f=1152),
+    # the largest d_model and d_ff the header allows, and E = 256 with k = 8
+    "max_d": configs.FINE.scaled("max_d", T=256, d=16384, E=2, k=1, f=128),
+    "max_f": configs.FINE.scaled("max_f", T=256, d=64, E=2, k=1, f=16384),
+    "max_E_k": configs.FINE.scaled("max_E_k", T=300, d=128, E=256, k=8, f=128),
     # MXFP8 expert GEMMs
     "fine_mx_small": configs.FINE_MX.scaled("fine_mx_small", T=1500, d=256, E=32, f=256),
     "sparse_round_mx_small": configs.SPARSE_ROUND.scaled("sparse_round_mx_small", T=1200, d=512, E=64, f=128,

@@ -26,8 +26,17 @@ FULL = ["fine_e128", "sparse_e256_round", "coarse_e8", "fine_e128_zipf", "fine_e
 
 @pytest.mark.parametrize("name", FULL)
 def test_full_size_sampled(name):
+    check_sampled(configs.get(name))
+
+
+def test_max_tokens_sampled():
+    """T = 2^20 tokens, the largest the header allows (2 M plan rows)."""
+    check_sampled(configs.FINE.scaled("max_tokens", T=1 << 20, d=64, E=64, k=2, f=128))
+
+
+def check_sampled(cfg):
     from mixture_experts_layer_27_amd import binding
-    cfg = configs.get(name)
+    name = cfg.name
     print(f"[fullsize] {name}: generating inputs", flush=True)
     g = make_inputs(cfg)
     run = binding.LayerRun(cfg, g)
