@@ -121,9 +121,10 @@ hipError_t gemm_down(const moe_shape& s, const moe_plan& p, const PlanInternal& 
 // one per column tile on the fp32 path
 int gemm_dact_parts(const moe_shape& s) {
   if (s.act != MOE_BF16) return ceil_div(s.d_ff, 128);
-  // 64-column wave tiles: over ceil(f / 512) 512-column quanta (bf16, deep K), or
-  // over 256-column tiles (the MXFP8 kernel, and bf16 with shallow K)
-  if (s.gemm == MOE_BF16 && use_big(s.d)) return ceil_div(s.d_ff, 512) * 8;
+  // 64-column wave tiles: over ceil(f / 512) 512-column quanta (the 256 x 256
+  // kernels: bf16 with deep K, MXFP8 always), or over 256-column tiles (bf16
+  // with shallow K)
+  if (s.gemm == MOE_MXFP8 || use_big(s.d)) return ceil_div(s.d_ff, 512) * 8;
   return ceil_div(s.d_ff, 256) * 4;
 }
 

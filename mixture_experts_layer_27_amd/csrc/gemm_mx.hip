@@ -9,7 +9,7 @@
 //             dW1_e = dH^T X_perm  : both along the expert's tokens
 //             dW2_e = dO^T gA      : both along the expert's tokens
 // The epilogues (SwiGLU, its backward with dS, plain stores) are the bf16 ones.
-#include "gemm_mx.h"
+#include "gemm_mx_big.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -17,8 +17,24 @@ using namespace moe_gemm;
 
 namespace {
 
-template <int GROUP, int EPI, int S = 3>
+// Row-segment GEMMs: 256 x 256 register-staged tiles (128 x 512 for odd
+// segment tails), eight waves.  Weight gradients: the 128 x 256 LDS-DMA kernel,
+// whose two blocks per CU overlap one tile's fp32 stores with the other's MFMAs
+// (716 us vs 619 us for dW1 at fine_e128 on the 256 x 256 kernel).
+template <int GROUP, int EPI>
 hipError_t run_mx(const Args& a, const MxArgs& m, int64_t logical_tiles, hipStream_t st) {
+  auto kern = grouped_gemm_mx_big<GROUP, EPI>;
+  const size_t lds = big_lds_bytes(GROUP == GROUP_M);
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const int64_t grid = 8 * ((logical_tiles + 7) / 8);
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBigThreads), lds, st, a, m);
+  return hipGetLastError();
+}
+
+template <int GROUP, int EPI, int S = 3>
+hipError_t run_mx_dma(const Args& a, const MxArgs& m, int64_t logical_tiles, hipStream_t st) {
   auto kern = grouped_gemm_mx<128, 256, 2, 4, GROUP, EPI, S>;
   constexpr size_t lds = mx_lds_bytes<128, 256, 2, 4, S>();
   if (lds > 65536) {
@@ -37,7 +53,7 @@ Args base_args() {
   return a;
 }
 
-int64_t m_tiles(const moe_shape& s) { return (max_rows(s) + 127) / 128 + s.E; }
+int64_t m_tiles(const moe_shape& s) { return (max_rows(s) + 127) / 128 + s.E; }   // 128-row units
 
 }  // namespace
 
@@ -51,9 +67,9 @@ hipError_t gemm_mx_up_swiglu(const moe_shape& s, const moe_plan& p, const PlanIn
   a.q_codes = act.codes; a.q_scales = act.scales; a.q_ld = s.d_ff; a.q_srows = act.srows; a.q_pad = act.pad;
   a.offsets = p.offsets;
   a.N = 2 * s.d_ff; a.K = s.d; a.E = s.E; a.f = s.d_ff;
-  a.tile_prefix = pi.prefix128; a.tile_expert = pi.tile_e128; a.tilesN = a.N / 256;
+  a.tile_prefix = pi.prefix128; a.tile_expert = pi.tile_e128;
   MxArgs m{x.scales, x.srows, x.pad, w1.scales, w1.srows, 2 * (int64_t)s.d_ff};
-  return run_mx<GROUP_M, EPI_SWIGLU_MX>(a, m, m_tiles(s) * a.tilesN, st);
+  return run_mx<GROUP_M, EPI_SWIGLU_MX>(a, m, m_tiles(s) * ceil_div(a.N, 512), st);
 }
 
 hipError_t gemm_mx_down(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const MxOperand& act,
@@ -64,9 +80,9 @@ hipError_t gemm_mx_down(const moe_shape& s, const moe_plan& p, const PlanInterna
   a.C = y; a.ldc = s.d;
   a.offsets = p.offsets;
   a.N = s.d; a.K = s.d_ff; a.E = s.E; a.f = s.d_ff;
-  a.tile_prefix = pi.prefix128; a.tile_expert = pi.tile_e128; a.tilesN = ceil_div(a.N, 256);
+  a.tile_prefix = pi.prefix128; a.tile_expert = pi.tile_e128;
   MxArgs m{act.scales, act.srows, act.pad, w2.scales, w2.srows, (int64_t)s.d};
-  return run_mx<GROUP_M, EPI_ACT>(a, m, m_tiles(s) * a.tilesN, st);
+  return run_mx<GROUP_M, EPI_ACT>(a, m, m_tiles(s) * ceil_div(a.N, 512), st);
 }
 
 // w2t: W2 quantised along d, stored [E][f][d]
@@ -83,11 +99,11 @@ hipError_t gemm_mx_dact(const moe_shape& s, const moe_plan& p, const PlanInterna
   a.row_gate = p.gate_of_row;
   a.offsets = p.offsets;
   a.N = s.d_ff; a.K = s.d; a.E = s.E; a.f = s.d_ff;
-  a.tile_prefix = pi.prefix128; a.tile_expert = pi.tile_e128; a.tilesN = ceil_div(a.N, 256);
+  a.tile_prefix = pi.prefix128; a.tile_expert = pi.tile_e128;
   // dH also in MXFP8 along 2f for the dX_perm GEMM
   a.q_codes = dhq.codes; a.q_scales = dhq.scales; a.q_ld = 2 * s.d_ff; a.q_srows = dhq.srows; a.q_pad = dhq.pad;
   MxArgs m{dout.scales, dout.srows, dout.pad, w2t.scales, w2t.srows, (int64_t)s.d_ff};
-  return run_mx<GROUP_M, EPI_DSWIGLU_MX>(a, m, m_tiles(s) * a.tilesN, st);
+  return run_mx<GROUP_M, EPI_DSWIGLU_MX>(a, m, m_tiles(s) * ceil_div(a.N, 512), st);
 }
 
 // w1t: W1 quantised along 2f, stored [E][d][2f]
@@ -99,9 +115,9 @@ hipError_t gemm_mx_dx_perm(const moe_shape& s, const moe_plan& p, const PlanInte
   a.C = dx_perm; a.ldc = s.d;
   a.offsets = p.offsets;
   a.N = s.d; a.K = 2 * s.d_ff; a.E = s.E; a.f = s.d_ff;
-  a.tile_prefix = pi.prefix128; a.tile_expert = pi.tile_e128; a.tilesN = ceil_div(a.N, 256);
+  a.tile_prefix = pi.prefix128; a.tile_expert = pi.tile_e128;
   MxArgs m{dh.scales, dh.srows, dh.pad, w1t.scales, w1t.srows, (int64_t)s.d};
-  return run_mx<GROUP_M, EPI_ACT>(a, m, m_tiles(s) * a.tilesN, st);
+  return run_mx<GROUP_M, EPI_ACT>(a, m, m_tiles(s) * ceil_div(a.N, 512), st);
 }
 
 // dW_e [M, N] = sum over the expert's (64-padded) token positions of lhs x rhs;
@@ -119,7 +135,7 @@ hipError_t gemm_mx_wgrad(const moe_shape& s, const WgradChunks& w, int64_t P, co
   a.tilesM = ceil_div(M, 128); a.tilesN = ceil_div(N, 256);
   const int64_t tiles = 8 * (int64_t)ceil_div(w.max_chunks, 8) * a.tilesM * a.tilesN;
   MxArgs m{lhs.scales, lhs.srows, nullptr, rhs.scales, rhs.srows, 0};
-  return run_mx<GROUP_K, EPI_F32>(a, m, tiles, st);
+  return run_mx_dma<GROUP_K, EPI_F32>(a, m, tiles, st);
 }
 
 }  // namespace moe
