@@ -40,56 +40,63 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(const char* __restric
 }
 
 // out[t] = sum over the rows of t (ascending) of gate[r] * y[r], fp32 accumulation.
+// One wave per token: its rows and gates are read once (wave-uniform), each lane
+// accumulates up to four 16-byte column chunks with their loads in flight.
 template <typename T>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, const int32_t* __restrict__ tok_ptr,
                                                      const int32_t* __restrict__ tok_rows,
                                                      const float* __restrict__ gate, int T_, int d,
                                                      T* __restrict__ out) {
   constexpr int EV = 16 / sizeof(T);   // elements per vector
+  constexpr int CL = 4;                // column chunks per lane per pass
   const int vec = d / EV;
-  const int64_t total = (int64_t)T_ * vec;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
-    const int t = (int)(i / vec), c = (int)(i - (int64_t)t * vec);
-    float acc[EV];
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T_) return;
+  const int p0 = tok_ptr[t], p1 = tok_ptr[t + 1];
+  for (int cb = 0; cb < vec; cb += 64 * CL) {
+    float acc[CL][EV];
 #pragma unroll
-    for (int q = 0; q < EV; ++q) acc[q] = 0.0f;
-    const int p0 = tok_ptr[t], p1 = tok_ptr[t + 1];
-    for (int pb = p0; pb < p1; pb += 4) {
-      // up to four rows' vectors in flight, accumulated in ascending row order
-      u32x4 v[4];
-      float g[4];
+    for (int j = 0; j < CL; ++j)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (pb + u < p1) {
-          const int r = tok_rows[pb + u];
-          g[u] = gate[r];
-          v[u] = ldg16(y + (int64_t)r * d + c * EV);
-        }
+      for (int q = 0; q < EV; ++q) acc[j][q] = 0.0f;
+    for (int p = p0; p < p1; ++p) {
+      const int r = tok_rows[p];
+      const float g = gate[r];
+      u32x4 v[CL];
+#pragma unroll
+      for (int j = 0; j < CL; ++j) {
+        const int c = cb + lane + 64 * j;
+        v[j] = c < vec ? ldg16(y + (int64_t)r * d + c * EV) : u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (pb + u >= p1) break;
+      for (int j = 0; j < CL; ++j) {
         if constexpr (sizeof(T) == 2) {
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            acc[2 * q] += g[u] * __uint_as_float(v[u][q] << 16);
-            acc[2 * q + 1] += g[u] * __uint_as_float(v[u][q] & 0xffff0000u);
+            acc[j][2 * q] += g * __uint_as_float(v[j][q] << 16);
+            acc[j][2 * q + 1] += g * __uint_as_float(v[j][q] & 0xffff0000u);
           }
         } else {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) acc[q] += g[u] * __uint_as_float(v[u][q]);
+          for (int q = 0; q < 4; ++q) acc[j][q] += g * __uint_as_float(v[j][q]);
         }
       }
     }
-    u32x4 o;
-    if constexpr (sizeof(T) == 2) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) o[q] = pack_bf2(acc[2 * q], acc[2 * q + 1]);
-    } else {
+    for (int j = 0; j < CL; ++j) {
+      const int c = cb + lane + 64 * j;
+      if (c >= vec) continue;
+      u32x4 o;
+      if constexpr (sizeof(T) == 2) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) o[q] = __float_as_uint(acc[q]);
+        for (int q = 0; q < 4; ++q) o[q] = pack_bf2(acc[j][2 * q], acc[j][2 * q + 1]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = __float_as_uint(acc[j][q]);
+      }
+      stg16(out + (int64_t)t * d + c * EV, o);
     }
-    stg16(out + (int64_t)t * d + c * EV, o);
   }
 }
 
@@ -99,6 +106,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, c
 // experts (router backward below), so the router term is a gather of a few W_g
 // rows (L2-resident) rather than a GEMM; a top-k expert is visited here only when
 // t has no row at it (token rounding dropped the pair).
+// One wave per token: the token's rows, experts and dz values are read once
+// (wave-uniform), then each lane accumulates up to four 16-byte column chunks
+// with all their row loads in flight.
 template <typename T>
 __global__ __launch_bounds__(256) void router_dx_kernel(const T* __restrict__ dx_perm, const int32_t* __restrict__ tok_ptr,
                                                        const int32_t* __restrict__ tok_rows,
@@ -108,8 +118,11 @@ __global__ __launch_bounds__(256) void router_dx_kernel(const T* __restrict__ dx
                                                        const float* __restrict__ dz, const T* __restrict__ wg,
                                                        int T_, int E, int d, int k, T* __restrict__ out) {
   constexpr int EV = 16 / sizeof(T);
+  constexpr int CL = 4;                       // column chunks per lane per pass
   const int vec = d / EV;
-  const int64_t total = (int64_t)T_ * vec;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T_) return;
   auto add = [&](float* acc, const u32x4& v, float w) {
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
@@ -122,48 +135,59 @@ __global__ __launch_bounds__(256) void router_dx_kernel(const T* __restrict__ dx
       for (int q = 0; q < 4; ++q) acc[q] += w * __uint_as_float(v[q]);
     }
   };
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
-    const int t = (int)(i / vec), c = (int)(i - (int64_t)t * vec);
-    const float* dzt = dz + (int64_t)t * E;
-    float acc[EV];
+  const float* dzt = dz + (int64_t)t * E;
+  const int p0 = tok_ptr[t], p1 = tok_ptr[t + 1];
+  for (int cb = 0; cb < vec; cb += 64 * CL) {
+    float acc[CL][EV];
 #pragma unroll
-    for (int q = 0; q < EV; ++q) acc[q] = 0.0f;
-    const int p0 = tok_ptr[t], p1 = tok_ptr[t + 1];
-    for (int pb = p0; pb < p1; pb += 4) {
-      // up to four rows (and their experts' router rows) in flight
-      u32x4 v[4], w[4];
-      float z[4];
+    for (int j = 0; j < CL; ++j)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (pb + u < p1) {
-          const int r = tok_rows[pb + u];
-          const int e = expert_of_row[r];
-          z[u] = dzt[e];
-          v[u] = ldg16(dx_perm + (int64_t)r * d + c * EV);
-          w[u] = ldg16(wg + (int64_t)e * d + c * EV);
+      for (int q = 0; q < EV; ++q) acc[j][q] = 0.0f;
+    for (int p = p0; p < p1; ++p) {           // rows in ascending order
+      const int r = tok_rows[p];
+      const int e = expert_of_row[r];
+      const float z = dzt[e];
+      u32x4 v[CL], w[CL];
+#pragma unroll
+      for (int j = 0; j < CL; ++j) {
+        const int c = cb + lane + 64 * j;
+        if (c < vec) {
+          v[j] = ldg16(dx_perm + (int64_t)r * d + c * EV);
+          w[j] = ldg16(wg + (int64_t)e * d + c * EV);
+        } else {
+          v[j] = w[j] = u32x4{0u, 0u, 0u, 0u};
         }
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        if (pb + u >= p1) break;
-        add(acc, v[u], 1.0f);
-        add(acc, w[u], z[u]);
+      for (int j = 0; j < CL; ++j) {
+        add(acc[j], v[j], 1.0f);
+        add(acc[j], w[j], z);
       }
     }
-    for (int j = 0; j < k; ++j) {
-      const int e = topk_idx[(int64_t)t * k + j];
+    for (int i = 0; i < k; ++i) {
+      const int e = topk_idx[(int64_t)t * k + i];
       if ((keep_bits[(int64_t)t * words + (e >> 5)] >> (e & 31)) & 1u) continue;
-      add(acc, ldg16(wg + (int64_t)e * d + c * EV), dzt[e]);
-    }
-    u32x4 o;
-    if constexpr (sizeof(T) == 2) {
+      const float z = dzt[e];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) o[q] = pack_bf2(acc[2 * q], acc[2 * q + 1]);
-    } else {
-#pragma unroll
-      for (int q = 0; q < 4; ++q) o[q] = __float_as_uint(acc[q]);
+      for (int j = 0; j < CL; ++j) {
+        const int c = cb + lane + 64 * j;
+        if (c < vec) add(acc[j], ldg16(wg + (int64_t)e * d + c * EV), z);
+      }
     }
-    stg16(out + (int64_t)t * d + c * EV, o);
+#pragma unroll
+    for (int j = 0; j < CL; ++j) {
+      const int c = cb + lane + 64 * j;
+      if (c >= vec) continue;
+      u32x4 o;
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = pack_bf2(acc[j][2 * q], acc[j][2 * q + 1]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) o[q] = __float_as_uint(acc[j][q]);
+      }
+      stg16(out + (int64_t)t * d + c * EV, o);
+    }
   }
 }
 
@@ -310,15 +334,12 @@ hipError_t launch_permute_rows(const moe_shape& s, const void* src, const moe_pl
 }
 
 hipError_t launch_combine(const moe_shape& s, const void* y, const moe_plan& p, void* out, hipStream_t st) {
-  if (s.act == MOE_BF16) {
-    const int64_t work = (int64_t)s.T * (s.d / 8);
-    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(grid_for(work, 256)), dim3(256), 0, st, (const bf16_t*)y,
+  if (s.act == MOE_BF16)
+    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(ceil_div(s.T, 4)), dim3(256), 0, st, (const bf16_t*)y,
                        p.tok_ptr, p.tok_rows, p.gate_of_row, s.T, s.d, (bf16_t*)out);
-  } else {
-    const int64_t work = (int64_t)s.T * (s.d / 4);
-    hipLaunchKernelGGL(combine_kernel<float>, dim3(grid_for(work, 256)), dim3(256), 0, st, (const float*)y,
+  else
+    hipLaunchKernelGGL(combine_kernel<float>, dim3(ceil_div(s.T, 4)), dim3(256), 0, st, (const float*)y,
                        p.tok_ptr, p.tok_rows, p.gate_of_row, s.T, s.d, (float*)out);
-  }
   return hipGetLastError();
 }
 
@@ -326,13 +347,11 @@ hipError_t launch_router_dx(const moe_shape& s, const moe_plan& p, const void* d
                             const void* wg, void* dx, hipStream_t st) {
   const int words = (s.E + 31) / 32;
   if (s.act == MOE_BF16) {
-    const int64_t work = (int64_t)s.T * (s.d / 8);
-    hipLaunchKernelGGL(router_dx_kernel<bf16_t>, dim3(grid_for(work, 256)), dim3(256), 0, st, (const bf16_t*)dx_perm,
+    hipLaunchKernelGGL(router_dx_kernel<bf16_t>, dim3(ceil_div(s.T, 4)), dim3(256), 0, st, (const bf16_t*)dx_perm,
                        p.tok_ptr, p.tok_rows, p.expert_of_row, p.topk_idx, p.keep_bits, words, dz,
                        (const bf16_t*)wg, s.T, s.E, s.d, s.k, (bf16_t*)dx);
   } else {
-    const int64_t work = (int64_t)s.T * (s.d / 4);
-    hipLaunchKernelGGL(router_dx_kernel<float>, dim3(grid_for(work, 256)), dim3(256), 0, st, (const float*)dx_perm,
+    hipLaunchKernelGGL(router_dx_kernel<float>, dim3(ceil_div(s.T, 4)), dim3(256), 0, st, (const float*)dx_perm,
                        p.tok_ptr, p.tok_rows, p.expert_of_row, p.topk_idx, p.keep_bits, words, dz,
                        (const float*)wg, s.T, s.E, s.d, s.k, (float*)dx);
   }
