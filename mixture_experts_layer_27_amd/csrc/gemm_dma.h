@@ -334,28 +334,43 @@ MOE_DEV void wave_epilogue(const Args& args, const TileCtx& ctx, f32x16 (&acc)[B
           }
         }
       } else {
+        // act dtype (EPI_ACT) or fp32 (weight-gradient slabs, split-K partials).
+        // Every lane stores one 16-byte vector and consecutive lanes hold
+        // consecutive columns, so each store instruction writes whole 128-byte
+        // lines (fp32 rows written as two interleaved halves cost ~10% of the
+        // weight-gradient time).
         using OT = typename std::conditional<EPI == EPI_ACT, T, float>::type;
-        constexpr int IT = 32 * CPR / 64;
+        constexpr int VW = 16 / (int)sizeof(OT);   // values per 16-byte store
+        constexpr int CU = WTN / VW;               // 16-byte units per wave row
+        constexpr int IT = 32 * CU / 64;
         OT* C = reinterpret_cast<OT*>(args.C);
         if constexpr (GROUP == GROUP_K) C = wgrad_out<OT>(args, ctx);
-        float v[IT][8];
+        float v[IT][VW];
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
           const int u = lane + 64 * it;
-          const float* src = slab + (u / CPR) * SS + (u % CPR) * 8;
+          const float* src = slab + (u / CU) * SS + (u % CU) * VW;
 #pragma unroll
-          for (int c = 0; c < 8; ++c) v[it][c] = src[c];
+          for (int c = 0; c < VW; ++c) v[it][c] = src[c];
         }
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
           const int u = lane + 64 * it;
-          const int rr = u / CPR, ch = u % CPR;
+          const int rr = u / CU, ch = u % CU;
           int grow;
           bool ok;
           if constexpr (GROUP == GROUP_M) { grow = rbase + i * 32 + rr; ok = grow < ctx.row_end; }
           else { grow = mbase + i * 32 + rr; ok = grow < args.M; }
-          const int col = cbase + ch * 8;
-          if (ok && col < args.N) Vec8<OT>::store(C + (int64_t)grow * args.ldc + col, v[it]);
+          const int col = cbase + ch * VW;
+          if (ok && col < args.N) {
+            if constexpr (VW == 8) {
+              Vec8<OT>::store(C + (int64_t)grow * args.ldc + col, v[it]);
+            } else {
+              stg16(C + (int64_t)grow * args.ldc + col,
+                    u32x4{__float_as_uint(v[it][0]), __float_as_uint(v[it][1]), __float_as_uint(v[it][2]),
+                          __float_as_uint(v[it][3])});
+            }
+          }
         }
       }
     }
