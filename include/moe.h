@@ -141,7 +141,10 @@ moe_status moe_permute(const moe_shape *s, const void *src, const moe_plan *plan
  *   to the act dtype and computed from the stored H).
  * With gemm == MOE_MXFP8 every GEMM operand is quantised to MXFP8 along its K
  * inside this call: x_perm and the weights by quantiser passes, A by the
- * SwiGLU epilogue (A then exists only as MXFP8 codes, in the workspace).
+ * SwiGLU epilogue (A then exists only as MXFP8 codes, in the workspace).  The
+ * quantiser passes read x_perm, w1 and w2 once each and also write their codes
+ * along the other axis (W1, W2 along their first axes, x_perm along tokens):
+ * moe_backward can take them from ws instead of quantising again.
  * ws: moe_workspace_bytes(s, MOE_WS_EXPERTS) bytes, 16-byte aligned. */
 moe_status moe_grouped_gemm_swiglu(const moe_shape *s, const void *x_perm, const void *w1,
                                    const void *w2, const moe_plan *plan, void *h_saved, void *y,
@@ -156,6 +159,11 @@ moe_status moe_unpermute_combine(const moe_shape *s, const void *y, const moe_pl
  *   Inputs: x [T,d], w_gate [E,d], w1, w2, the plan, h_saved, dout [T,d];
  *   x_perm [N_max,d] (act) = what moe_permute wrote for x with this plan, or NULL
  *   (then x is permuted again into the workspace; the results are identical).
+ *   fwd_ws = the workspace of this step's moe_grouped_gemm_swiglu call (same
+ *   shape, plan, x_perm, w1 and w2, unchanged since), or NULL.  With MXFP8 the
+ *   backward then reads the transposed weight codes and x_perm's token-axis
+ *   codes from it instead of quantising them again (identical codes, so
+ *   identical results); ignored for the other GEMM types.  Only read.
  *   Outputs: dx [T,d] (act), dw_gate [E,d] f32, dw1 [E,2f,d] f32, dw2 [E,d,f] f32;
  *   optional dlogits [T,E] f32 and ds [N_max] f32 (per-row gate gradient) when
  *   not NULL.
@@ -167,7 +175,7 @@ moe_status moe_unpermute_combine(const moe_shape *s, const void *y, const moe_pl
  * (it includes the partial slabs and, with MXFP8, the quantised operands). */
 moe_status moe_backward(const moe_shape *s, const void *x, const void *w_gate, const void *w1,
                         const void *w2, const moe_plan *plan, const void *h_saved, const void *x_perm,
-                        const void *dout, void *dx, float *dw_gate, float *dw1, float *dw2,
+                        const void *fwd_ws, const void *dout, void *dx, float *dw_gate, float *dw1, float *dw2,
                         float *dlogits, float *ds, void *ws, size_t ws_bytes, void *stream);
 
 /* MXFP8 quantiser (OCP Microscaling v1.0; the pages only name the format):

@@ -55,7 +55,7 @@ for name, res, args in [
     ("moe_grouped_gemm_swiglu", ctypes.c_int, [_P_SHAPE, _vp, _vp, _vp, _P_PLAN, _vp, _vp, _vp, _sz, _vp]),
     ("moe_unpermute_combine", ctypes.c_int, [_P_SHAPE, _vp, _P_PLAN, _vp, _vp]),
     ("moe_backward", ctypes.c_int, [_P_SHAPE, _vp, _vp, _vp, _vp, _P_PLAN, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
-                                    _vp, _vp, _vp, _sz, _vp]),
+                                    _vp, _vp, _vp, _vp, _sz, _vp]),
     ("moe_quantize_mx", ctypes.c_int, [_vp, _i64, _i64, ctypes.c_int, _vp, _vp, _vp]),
     ("moe_status_str", ctypes.c_char_p, [ctypes.c_int]),
 ]:
@@ -192,11 +192,11 @@ def unpermute_combine(s: MoeShape, y, plan: Plan, out, stream=None):
 
 
 def backward(s: MoeShape, x, w_gate, w1, w2, plan: Plan, h_saved, dout, dx, dw_gate, dw1, dw2, ws,
-             dlogits=None, ds=None, stream=None, x_perm=None):
+             dlogits=None, ds=None, stream=None, x_perm=None, fwd_ws=None):
     _check("moe_backward",
            _lib.moe_backward(ctypes.byref(s), _ptr(x), _ptr(w_gate), _ptr(w1), _ptr(w2), ctypes.byref(plan.c),
-                             _ptr(h_saved), _ptr(x_perm), _ptr(dout), _ptr(dx), _ptr(dw_gate), _ptr(dw1), _ptr(dw2),
-                             _ptr(dlogits), _ptr(ds), _ptr(ws), ws.numel(), _stream(stream)))
+                             _ptr(h_saved), _ptr(x_perm), _ptr(fwd_ws), _ptr(dout), _ptr(dx), _ptr(dw_gate),
+                             _ptr(dw1), _ptr(dw2), _ptr(dlogits), _ptr(ds), _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def quantize_mx(src, codes, scales, k_axis=1, stream=None):
@@ -252,12 +252,14 @@ class LayerRun:
         unpermute_combine(self.s, self.y, self.plan, self.out, stream)
         return self.out
 
-    def backward(self, stream=None, with_optional=True, reuse_x_perm=True):
-        """reuse_x_perm: hand the forward's permuted x to the backward (else it permutes x again)."""
+    def backward(self, stream=None, with_optional=True, reuse_x_perm=True, reuse_fwd_ws=True):
+        """reuse_x_perm: hand the forward's permuted x to the backward (else it permutes x again);
+        reuse_fwd_ws: hand it the forward's workspace (MXFP8: the backward-orientation codes of
+        W1, W2 and x_perm), else it quantises them again."""
         backward(self.s, self.inp["x"], self.inp["w_gate"], self.inp["w1"], self.inp["w2"], self.plan, self.h,
                  self.inp["dout"], self.dx, self.dw_gate, self.dw1, self.dw2, self.ws_bwd,
                  self.dlogits if with_optional else None, self.ds if with_optional else None, stream,
-                 self.x_perm if reuse_x_perm else None)
+                 self.x_perm if reuse_x_perm else None, self.ws_fwd if reuse_fwd_ws else None)
 
     def step(self, stream=None):
         self.forward(stream)

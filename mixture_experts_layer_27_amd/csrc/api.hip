@@ -174,6 +174,7 @@ struct FwdWs {
   void* act;              // A [N_max, f]
   int32_t* pad_off;       // MXFP8 only: expert-padded row offsets, quantised operands
   MxOperand x, w1, a, w2;
+  MxOperand w1t, w2t, x_t;   // MXFP8: the backward's orientation of W1, W2 and x_perm
 };
 
 size_t carve_fwd(const moe_shape& s, char* base, FwdWs* w) {
@@ -188,6 +189,9 @@ size_t carve_fwd(const moe_shape& s, char* base, FwdWs* w) {
     q.w1 = take_mx(c, E * 2 * f, d, E * 2 * f);
     q.a = take_mx(c, P, f, P, q.pad_off);
     q.w2 = take_mx(c, E * d, f, E * d);
+    q.w1t = take_mx(c, E * d, 2 * f, E * d);
+    q.w2t = take_mx(c, E * f, d, E * f);
+    q.x_t = take_mx(c, d, P, d);
   }
   if (w) *w = q;
   return c.off;
@@ -304,15 +308,16 @@ moe_status moe_grouped_gemm_swiglu(const moe_shape* s, const void* x_perm, const
   carve_fwd(*s, reinterpret_cast<char*>(ws), &w);
   hipError_t e;
   if (s->gemm == MOE_MXFP8) {
-    const int64_t N = max_rows(*s);
+    // x_perm and the weights are quantised along both of their axes in one pass
+    // each: this call's GEMMs use the rows, the backward the other orientation
+    const int64_t P = tok_cap(*s);
     const int E = s->E, d = s->d, f = s->d_ff;
-    const int32_t *off = plan->offsets, *eor = plan->expert_of_row;
+    const int32_t* off = plan->offsets;
     e = mx_pad_offsets(off, E, w.pad_off, hs);
-    if (e == hipSuccess)
-      e = mx_quantize_rows_padded(x_perm, N, d, off, eor, w.pad_off, E, w.x.codes, w.x.scales, w.x.srows, hs);
-    if (e == hipSuccess) e = mx_quantize_rows_staged(w1, (int64_t)E * 2 * f, d, w.w1.codes, w.w1.scales, w.w1.srows, hs);
+    if (e == hipSuccess) e = mx_quantize_dual(x_perm, 1, 0, d, off, w.pad_off, E, P, w.x, w.x_t, hs);
+    if (e == hipSuccess) e = mx_quantize_dual(w1, E, 2 * f, d, nullptr, nullptr, 0, 0, w.w1, w.w1t, hs);
     if (e == hipSuccess) e = gemm_mx_up_swiglu(*s, *plan, pi, w.x, w.w1, h_saved, w.a, hs);
-    if (e == hipSuccess) e = mx_quantize_rows_staged(w2, (int64_t)E * d, f, w.w2.codes, w.w2.scales, w.w2.srows, hs);
+    if (e == hipSuccess) e = mx_quantize_dual(w2, E, d, f, nullptr, nullptr, 0, 0, w.w2, w.w2t, hs);
     if (e == hipSuccess) e = gemm_mx_down(*s, *plan, pi, w.a, w.w2, y, hs);
     return hip_status(e);
   }
@@ -330,14 +335,15 @@ moe_status moe_unpermute_combine(const moe_shape* s, const void* y, const moe_pl
 }
 
 moe_status moe_backward(const moe_shape* s, const void* x, const void* w_gate, const void* w1, const void* w2,
-                        const moe_plan* plan, const void* h_saved, const void* x_perm, const void* dout, void* dx,
+                        const moe_plan* plan, const void* h_saved, const void* x_perm, const void* fwd_ws,
+                        const void* dout, void* dx,
                         float* dw_gate,
                         float* dw1, float* dw2, float* dlogits, float* ds, void* ws, size_t ws_bytes, void* stream) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
   if (!aligned(x) || !aligned(w_gate) || !aligned(w1) || !aligned(w2) || !aligned(h_saved) || !aligned(dout) ||
       !aligned(dx) || !aligned(dw_gate) || !aligned(dw1) || !aligned(dw2) || !aligned_or_null(dlogits) ||
-      !aligned_or_null(x_perm) ||
+      !aligned_or_null(x_perm) || !aligned_or_null(fwd_ws) ||
       (ds && (reinterpret_cast<uintptr_t>(ds) & 3)))
     return MOE_EINVAL;
   if ((st = check_plan(*s, plan)) != MOE_OK) return st;
@@ -350,27 +356,33 @@ moe_status moe_backward(const moe_shape* s, const void* x, const void* w_gate, c
   const int ldz = ldz_of(*s);
   hipError_t e = launch_permute_rows(*s, dout, *plan, w.do_perm, hs);
   if (s->gemm == MOE_MXFP8) {
-    const int64_t N = max_rows(*s), P = tok_cap(*s);
+    const int64_t P = tok_cap(*s);
     const int E = s->E, d = s->d, f = s->d_ff;
-    const int32_t *off = plan->offsets, *eor = plan->expert_of_row;
+    const int32_t* off = plan->offsets;
+    // the forward's workspace already holds W1, W2 along their first axes and
+    // x_perm along tokens, quantised from the same inputs
+    FwdWs fw{};
+    if (fwd_ws) carve_fwd(*s, reinterpret_cast<char*>(const_cast<void*>(fwd_ws)), &fw);
+    const MxOperand& w1t = fwd_ws ? fw.w1t : w.w1t;
+    const MxOperand& w2t = fwd_ws ? fw.w2t : w.w2t;
+    const MxOperand& x_t = fwd_ws ? fw.x_t : w.x_t;
     if (e == hipSuccess) e = mx_pad_offsets(off, E, w.pad_off, hs);
-    if (e == hipSuccess)
-      e = mx_quantize_rows_padded(w.do_perm, N, d, off, eor, w.pad_off, E, w.doq.codes, w.doq.scales, w.doq.srows, hs);
-    if (e == hipSuccess) e = mx_quantize_cols(w2, E, d, f, w.w2t.codes, w.w2t.scales, hs);
-    if (e == hipSuccess) e = gemm_mx_dact(*s, *plan, pi, w.doq, w.w2t, h_saved, w.dh, w.dhq, w.ga, w.ds_part, hs);
-    if (e == hipSuccess) e = mx_quantize_cols(w1, E, 2 * f, d, w.w1t.codes, w.w1t.scales, hs);
-    if (e == hipSuccess && !x_perm) e = launch_permute_rows(*s, x, *plan, w.xbuf, hs);
+    if (e == hipSuccess) e = mx_quantize_dual(w.do_perm, 1, 0, d, off, w.pad_off, E, P, w.doq, w.do_t, hs);
+    if (e == hipSuccess && !fwd_ws) e = mx_quantize_cols(w2, E, d, f, w.w2t.codes, w.w2t.scales, hs);
+    if (e == hipSuccess) e = gemm_mx_dact(*s, *plan, pi, w.doq, w2t, h_saved, w.dh, w.dhq, w.ga, w.ds_part, hs);
+    if (e == hipSuccess && !fwd_ws) e = mx_quantize_cols(w1, E, 2 * f, d, w.w1t.codes, w.w1t.scales, hs);
+    if (e == hipSuccess && !x_perm && !fwd_ws) e = launch_permute_rows(*s, x, *plan, w.xbuf, hs);
     const void* xp = x_perm ? x_perm : w.xbuf;
     if (e == hipSuccess) e = mx_quantize_tokens(w.dh, 2 * f, plan->offsets, w.pad_off, E, P, w.dh_t.codes, w.dh_t.scales, hs);
-    if (e == hipSuccess) e = mx_quantize_tokens(xp, d, plan->offsets, w.pad_off, E, P, w.x_t.codes, w.x_t.scales, hs);
-    if (e == hipSuccess) e = mx_quantize_tokens(w.do_perm, d, plan->offsets, w.pad_off, E, P, w.do_t.codes, w.do_t.scales, hs);
+    if (e == hipSuccess && !fwd_ws)
+      e = mx_quantize_tokens(xp, d, plan->offsets, w.pad_off, E, P, w.x_t.codes, w.x_t.scales, hs);
     if (e == hipSuccess) e = mx_quantize_tokens(w.ga, f, plan->offsets, w.pad_off, E, P, w.ga_t.codes, w.ga_t.scales, hs);
     if (e == hipSuccess) e = launch_wgrad_chunks(w.pad_off, E, w.wg.kch, w.wg, hs);
-    if (e == hipSuccess) e = gemm_mx_wgrad(*s, w.wg, P, w.dh_t, 2 * f, w.x_t, d, dw1, hs);
+    if (e == hipSuccess) e = gemm_mx_wgrad(*s, w.wg, P, w.dh_t, 2 * f, x_t, d, dw1, hs);
     if (e == hipSuccess) e = launch_wgrad_reduce(w.wg, E, (int64_t)2 * f * d, dw1, hs);
     if (e == hipSuccess) e = gemm_mx_wgrad(*s, w.wg, P, w.do_t, d, w.ga_t, f, dw2, hs);
     if (e == hipSuccess) e = launch_wgrad_reduce(w.wg, E, (int64_t)d * f, dw2, hs);
-    if (e == hipSuccess) e = gemm_mx_dx_perm(*s, *plan, pi, w.dhq, w.w1t, w.xbuf, hs);   // dx_perm (x_perm no longer needed)
+    if (e == hipSuccess) e = gemm_mx_dx_perm(*s, *plan, pi, w.dhq, w1t, w.xbuf, hs);   // dx_perm (x_perm no longer needed)
   } else {
     if (e == hipSuccess) e = gemm_dact(*s, *plan, pi, w.do_perm, w2, h_saved, w.dh, w.ga, w.ds_part, hs);
     if (e == hipSuccess && !x_perm) e = launch_permute_rows(*s, x, *plan, w.xbuf, hs);

@@ -113,6 +113,10 @@ hipError_t launch_quantize_cols_plain(const void* src, int R, int C, uint8_t* co
 hipError_t mx_quantize_tokens(const void* src, int C, const int32_t* seg_off, const int32_t* pad_off, int E,
                               int64_t P, uint8_t* codes, uint8_t* scales, hipStream_t st);
 hipError_t mx_pad_offsets(const int32_t* offsets, int E, int32_t* pad_off, hipStream_t st);
+// rows and columns (seg_off == nullptr: G matrices [R][C]) or rows and tokens
+// (seg_off, pad_off, P as for mx_quantize_tokens) in one pass
+hipError_t mx_quantize_dual(const void* src, int G, int R, int C, const int32_t* seg_off, const int32_t* pad_off,
+                            int E, int64_t P, const MxOperand& rows, const MxOperand& pos, hipStream_t st);
 hipError_t gemm_mx_up_swiglu(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const MxOperand& x,
                              const MxOperand& w1, void* h, const MxOperand& act, hipStream_t st);
 hipError_t gemm_mx_down(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const MxOperand& act,

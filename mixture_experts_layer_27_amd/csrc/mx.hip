@@ -22,6 +22,9 @@
 // backward GEMMs), and tokens (reduction along the token axis of each expert's
 // row segment, written transposed [C][padded tokens] with every segment
 // starting at a multiple of 64 and zero-padded: the weight-gradient GEMMs).
+// A fused pass produces the row codes together with the column or token codes
+// from one read of the source (weights and permuted activations, which are
+// operands along both of their axes).
 #include "moe_common.h"
 #include "moe_internal.h"
 #include "mx_codes.h"
@@ -215,6 +218,145 @@ __global__ __launch_bounds__(256) void quantize_t_kernel(const bf16_t* __restric
   else scales[((pb >> 6) * srows + crow) * 2 + ((pb >> 5) & 1)] = (uint8_t)(X + 127);
 }
 
+// (4) both directions from one read of the source.  A tile of 128 positions x 128
+// columns is quantised along its rows (blocks of 32 columns) and along its
+// positions (blocks of 32 positions).  Positions as in quantize_t_kernel
+// (columns mode: the R rows of each of the G matrices [R][C]; tokens mode: the
+// padded tokens of the expert segments, zero past each segment's end).
+//   row codes [G*R][C] (columns mode) or [P][C] (tokens mode: row = padded
+//     position, padding rows included), stage-major scales [C/64][rsrows][2];
+//   position codes [G][C][len], len = R or P, scales [len/64][G*C][2].
+// C and the position extent (R, or pad_off[E]) are multiples of 64.  The
+// position codes are transposed through LDS so that each store instruction
+// writes whole 128-byte lines of the [C][len] layout.
+__global__ __launch_bounds__(256) void quantize_dual_kernel(const bf16_t* __restrict__ src, int G, int R, int C,
+                                                           const int32_t* __restrict__ seg_off,
+                                                           const int32_t* __restrict__ pad_off, int E, int64_t P,
+                                                           uint8_t* __restrict__ rcodes, uint8_t* __restrict__ rscales,
+                                                           int64_t rsrows, uint8_t* __restrict__ tcodes,
+                                                           uint8_t* __restrict__ tscales) {
+  constexpr int VS = 136;   // value tile row stride (bf16 elements; rows stay 16-byte aligned)
+  constexpr int CS = 144;   // code tile row stride (bytes): 16 consecutive columns hit distinct banks
+  __shared__ __attribute__((aligned(16))) uint16_t vt[128 * VS];
+  __shared__ __attribute__((aligned(16))) uint8_t ct[128 * CS];
+  __shared__ uint8_t sc[128][4];
+  const int t = threadIdx.x;
+  const int c0 = blockIdx.x * 128;
+  const int64_t p0 = (int64_t)blockIdx.y * 128;
+  const int g = blockIdx.z;
+  const int64_t len = seg_off ? P : (int64_t)R;
+  const int64_t plim = seg_off ? (int64_t)pad_off[E] : (int64_t)R;   // positions in use
+  if (p0 >= plim) return;
+  int64_t base[2], valid[2];   // source row of each 64-position half, and how many of its rows are real
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int64_t ph = p0 + 64 * hh;
+    base[hh] = 0;
+    valid[hh] = 0;
+    if (ph < plim) {
+      if (seg_off) {
+        int lo = 0, hi = E;   // segment holding ph: pad_off[lo] <= ph < pad_off[lo+1]
+        while (hi - lo > 1) {
+          const int mid = (lo + hi) >> 1;
+          if (pad_off[mid] <= ph) lo = mid; else hi = mid;
+        }
+        const int64_t into = ph - pad_off[lo];
+        base[hh] = seg_off[lo] + into;
+        valid[hh] = (int64_t)(seg_off[lo + 1] - seg_off[lo]) - into;
+      } else {
+        base[hh] = (int64_t)g * R + ph;
+        valid[hh] = 64;
+      }
+    }
+  }
+  // 128 rows x 16 chunks of 8 values, eight 16-byte loads per thread, all issued first
+  u32x4 raw[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int i = t + 256 * u;
+    const int rr = i >> 4, ch = i & 15, hh = rr >> 6, rl = rr & 63;
+    const int col = c0 + ch * 8;
+    raw[u] = (rl < valid[hh] && col < C) ? ldg16(src + (base[hh] + rl) * C + col) : u32x4{0u, 0u, 0u, 0u};
+  }
+  // along rows: four consecutive lanes hold one 32-column block
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    const int i = t + 256 * u;
+    const int rr = i >> 4, ch = i & 15;
+    const int col = c0 + ch * 8;
+    const int64_t p = p0 + rr;
+    *reinterpret_cast<u32x4*>(vt + rr * VS + ch * 8) = raw[u];
+    float v[8];
+    unpack8(raw[u], v);
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+    const int X = mx_exponent(amax);
+    if (p < plim && col < C) {               // uniform over the quad
+      const int64_t drow = seg_off ? p : (int64_t)g * R + p;
+      *reinterpret_cast<uint2*>(rcodes + drow * C + col) = e4m3_8(v, pow2f(-X));
+      if ((ch & 3) == 0) sc[rr][ch >> 2] = (uint8_t)(X + 127);
+    }
+  }
+  __syncthreads();
+  {   // row scales: one thread per (row, 64-column step)
+    const int rr = t >> 1, s = t & 1;
+    const int64_t p = p0 + rr;
+    const int kb = c0 + 64 * s;
+    if (p < plim && kb < C) {
+      const int64_t drow = seg_off ? p : (int64_t)g * R + p;
+      *reinterpret_cast<uint16_t*>(rscales + ((int64_t)(kb >> 6) * rsrows + drow) * 2) =
+          (uint16_t)(sc[rr][2 * s] | (sc[rr][2 * s + 1] << 8));
+    }
+  }
+  {   // along positions: column c, positions [64h, 64h + 64) = two blocks
+    const int c = t & 127, h = t >> 7;
+    int Xb[2];
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      float v[32];
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        v[i] = __uint_as_float((uint32_t)vt[(64 * h + 32 * b + i) * VS + c] << 16);
+        amax = fmaxf(amax, fabsf(v[i]));
+      }
+      const int X = mx_exponent(amax);
+      const float inv = pow2f(-X);
+      uint8_t* cp = ct + c * CS + 64 * h + 32 * b;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const uint2 lo = e4m3_8(v + 16 * q, inv), hi2 = e4m3_8(v + 16 * q + 8, inv);
+        *reinterpret_cast<u32x4*>(cp + 16 * q) = u32x4{lo.x, lo.y, hi2.x, hi2.y};
+      }
+      Xb[b] = X;
+    }
+    const int64_t pb = p0 + 64 * h;
+    const int col = c0 + c;
+    if (pb < plim && col < C) {
+      const int64_t crow = seg_off ? col : (int64_t)g * C + col;
+      const int64_t srows = seg_off ? C : (int64_t)G * C;
+      *reinterpret_cast<uint16_t*>(tscales + ((pb >> 6) * srows + crow) * 2) =
+          (uint16_t)((Xb[0] + 127) | ((Xb[1] + 127) << 8));
+    }
+  }
+  __syncthreads();
+  // position codes out: 8 lanes per column, 16 bytes each
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int i = t + 256 * u;
+    const int c = i >> 3, ch = i & 7;
+    const int col = c0 + c;
+    const int64_t p = p0 + ch * 16;
+    if (col < C && p < plim) {
+      const int64_t crow = seg_off ? col : (int64_t)g * C + col;
+      *reinterpret_cast<u32x4*>(tcodes + crow * len + p) = *reinterpret_cast<const u32x4*>(ct + c * CS + ch * 16);
+    }
+  }
+}
+
 // pad_off[e] = sum over experts j < e of count_j rounded up to 64 (E <= 256)
 __global__ __launch_bounds__(256) void pad_offsets_kernel(const int32_t* __restrict__ offsets, int E,
                                                          int32_t* __restrict__ pad_off) {
@@ -285,6 +427,15 @@ hipError_t mx_quantize_tokens(const void* src, int C, const int32_t* seg_off, co
                               int64_t P, uint8_t* codes, uint8_t* scales, hipStream_t st) {
   hipLaunchKernelGGL(quantize_t_kernel, dim3(C / 64, (unsigned)((P + 127) / 128), 1), dim3(256), 0, st, (const bf16_t*)src, 1,
                      0, C, seg_off, pad_off, E, codes, scales, P, 0);
+  return hipGetLastError();
+}
+
+hipError_t mx_quantize_dual(const void* src, int G, int R, int C, const int32_t* seg_off, const int32_t* pad_off,
+                            int E, int64_t P, const MxOperand& rows, const MxOperand& pos, hipStream_t st) {
+  const int64_t len = seg_off ? P : (int64_t)R;
+  hipLaunchKernelGGL(quantize_dual_kernel, dim3((C + 127) / 128, (unsigned)((len + 127) / 128), G), dim3(256), 0, st,
+                     (const bf16_t*)src, G, R, C, seg_off, pad_off, E, P, rows.codes, rows.scales, rows.srows,
+                     pos.codes, pos.scales);
   return hipGetLastError();
 }
 

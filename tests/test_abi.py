@@ -73,7 +73,7 @@ def test_argument_errors_return_before_launch(b):
     assert b._lib.moe_permute(ctypes.byref(s), ctypes.c_void_p((1 << 20) + 4), ctypes.byref(plan), fake, None) == 1
     assert b._lib.moe_grouped_gemm_swiglu(ctypes.byref(s), fake, fake, fake, ctypes.byref(plan), fake, fake,
                                           fake, 0, None) == 3
-    assert b._lib.moe_backward(ctypes.byref(s), fake, fake, fake, fake, ctypes.byref(plan), fake, None, fake, fake,
+    assert b._lib.moe_backward(ctypes.byref(s), fake, fake, fake, fake, ctypes.byref(plan), fake, None, None, fake, fake,
                                fake, fake, fake, None, None, fake, 0, None) == 3
     assert b._lib.moe_round_tokens(ctypes.byref(s), ctypes.byref(plan), None, 0, None) == 1   # rounding off
     assert b._lib.moe_quantize_mx(fake, 4, 48, 1, fake, fake, None) == 1                      # cols % 32

@@ -109,7 +109,8 @@ def test_backward(name):
 def test_bitwise_deterministic(name):
     """Two runs give identical bits (rounding; weight gradients summed over several
     K chunks of one heavily loaded expert; the MXFP8 path).  The first backward
-    reads the forward's permuted x, the second permutes x itself."""
+    reads the forward's permuted x and (MXFP8) the forward's codes of W1, W2 and
+    x_perm along their other axes; the second permutes and quantises them itself."""
     from mixture_experts_layer_27_amd import binding
     cfg = CASES[name]
     g = make_inputs(cfg)
@@ -117,7 +118,7 @@ def test_bitwise_deterministic(name):
     for rep in range(2):
         run = binding.LayerRun(cfg, g)
         run.forward()
-        run.backward(reuse_x_perm=(rep == 0))
+        run.backward(reuse_x_perm=(rep == 0), reuse_fwd_ws=(rep == 0))
         torch.cuda.synchronize()
         n = int(run.plan.arrays()["offsets"][-1].item())      # rows past N are never written
         outs.append([t.clone() for t in (run.out, run.h[:n], run.y[:n], run.ds[:n], run.dx, run.dw_gate,
