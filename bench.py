@@ -88,6 +88,26 @@ def cpu_baseline(cfg, g, tokens):
                       f"float64 numpy{', MXFP8 operands' if cfg.gemm == 'mxfp8' else ''}, {dt:.1f} s"}
 
 
+def activation_bytes(cfg, rows, plan_bytes, fwd_ws_bytes):
+    """Bytes one layer keeps alive from the forward to the backward (weights and
+    their gradients excluded).  The conventional layer keeps X_perm, H, A and the
+    expert outputs Y, because it takes the router-score gradient as <dO, Y>; this
+    one takes it as <dA', A> with A recomputed from H (SonicMoE article, section
+    1), so it needs only the layer input x, the routing plan and H.  Handing the
+    backward the forward's x_perm (and, with MXFP8, the forward workspace with
+    the backward-orientation codes) keeps those alive too, to save work."""
+    e = 2 if cfg.act == "bf16" else 4
+    x, x_perm = cfg.T * cfg.d * e, rows * cfg.d * e
+    H, A, Y = rows * 2 * cfg.f * e, rows * cfg.f * e, rows * cfg.d * e
+    minimal = x + plan_bytes + H
+    store_y = x + plan_bytes + x_perm + H + A + Y
+    return {"minimal": minimal, "with_x_perm": minimal + x_perm, "store_y_layer": store_y,
+            "saving_minimal_vs_store_y": 1.0 - minimal / store_y,
+            # MXFP8: the forward workspace handed to the backward (codes of x_perm, A and of
+            # both weights in both orientations)
+            "forward_workspace": fwd_ws_bytes if cfg.gemm == "mxfp8" else 0}
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -191,6 +211,8 @@ def main():
         "hbm_peak_GBps": PEAK_HBM_GBS,
         "rows": rows,
         "max_expert_rows": int(counts.max()),
+        "activation_memory_bytes": activation_bytes(cfg, rows, binding.plan_bytes(s), run.ws_fwd.numel())
+        if run.has_bwd else None,
     }
     if not a.no_cpu_baseline:
         del run
