@@ -44,10 +44,31 @@ the design notes):
   bf16 (round-to-nearest-even) at the same points here; everything else is fp64.
 * MXFP8 (OCP Microscaling v1.0, E4M3 elements, one E8M0 scale per 32 along K,
   shared exponent floor(log2 amax) - 8, saturating): see ``oracle/mx.py``.
+* Routing variants (``RouteOpts``; Beam blog sections 2.2, 2.3 and 3.3,
+  distributed-MoE article challenge 1, Trinity Large example 2):
+  - gate "all": the gates are the full softmax over all E experts at the
+    selected experts, not renormalised (section 2.2's formula); "topk" (the
+    default) renormalises over the k selected (section 5.3, Trinity example 1).
+    Pairs added by token rounding get P_te under "all".
+  - noisy routing: a noise array [T,E] given by the caller is added to the
+    logits before top-k and the gates (no learned noise scale: the page only
+    says noise is added to the router scores); it gets no gradient.
+  - capacity factor cf > 0: each expert keeps its first ceil(cf*T*k/E) pairs in
+    token order, the rest are dropped (their tokens skip that expert); the
+    kept gates are unchanged.  Not combined with token rounding.
+  - load-balance loss lb = lb_coef * CV(Pbar)^2, Pbar = the batch mean of the
+    per-token routing distributions P_t, CV = population standard deviation
+    over the E entries divided by their mean (distributed-MoE article,
+    challenge 1 formula); z-loss = z_coef * mean_t (log sum_e exp z_te)^2 (the
+    page only names it; this is the usual definition).  Both are added to the
+    training loss, so their gradients add to dlogits.
+  - count_mse = mean_e (c_e - mean c)^2 over the per-expert counts of the
+    selected pairs (Trinity Large example 2): a monitor, no gradient.
 """
 from __future__ import annotations
 
 import dataclasses
+import math
 from typing import Dict, Optional
 
 import numpy as np
@@ -113,6 +134,23 @@ MX_CONTRACT = Precision("bf16", True)
 
 # ----------------------------------------------------------------------------
 # routing: F1-F3
+
+
+@dataclasses.dataclass(frozen=True)
+class RouteOpts:
+    """Routing variants (see the module notes).  The defaults are the base layer."""
+    gate: str = "topk"            # "topk": softmax over the k selected; "all": full softmax, no renormalisation
+    capacity_factor: float = 0.0  # 0: no cap
+    lb_coef: float = 0.0
+    z_coef: float = 0.0
+
+    @property
+    def dense_dz(self) -> bool:
+        """True when dlogits is nonzero beyond each token's selected experts."""
+        return self.gate == "all" or self.lb_coef != 0.0 or self.z_coef != 0.0
+
+
+BASE = RouteOpts()
 
 
 def router_logits(x, w_gate, bias=None):
@@ -219,15 +257,16 @@ def plan_from_topk(topk_idx, S, P, E):
     return _assemble(T, E, k, topk_idx, S, P, pair_t, pair_e, pair_g)
 
 
-def round_tokens(topk_idx, S, P, E, tile):
+def round_tokens(topk_idx, S, P, E, tile, gate_all=False):
     """Token rounding to a multiple of the GEMM tile (SonicMoE article, section 3).
 
     For every expert e with n selected pairs, the target is the nearest multiple
     of ``tile`` (half rounds up; if that exceeds T, round down).  Fewer rows:
     drop the selected pairs with the smallest P (ties: larger token dropped
     first).  More rows: add the unselected tokens with the largest P (ties:
-    smaller token first), with gate P_te / sum_{j in topk(t)} P_tj.  Kept pairs
-    keep their top-k softmax gates."""
+    smaller token first), with gate P_te / sum_{j in topk(t)} P_tj (P_te itself
+    when the gates are not renormalised, ``gate_all``).  Kept pairs keep their
+    gates."""
     topk_idx = np.asarray(topk_idx)
     T, k = topk_idx.shape
     sel = np.zeros((T, E), bool)
@@ -252,18 +291,69 @@ def round_tokens(topk_idx, S, P, E, tile):
             order = np.lexsort((cand, -P[cand, e]))
             add = cand[order[: target - n]]
             keep[add, e] = True
-            gate[add, e] = P[add, e] / ptop[add]
+            gate[add, e] = P[add, e] if gate_all else P[add, e] / ptop[add]
     pt, pe = np.nonzero(keep)
     return _assemble(T, E, k, topk_idx, S, P, pt, pe, gate[pt, pe])
 
 
-def route(x, w_gate, bias, k, round_tile=0):
-    """F1-F5: logits, top-k softmax, optional token rounding, plan."""
+def apply_capacity(plan: Plan, capacity_factor):
+    """Capacity factor (Beam blog section 2.3; distributed-MoE article, challenge
+    1): expert e keeps its first C = ceil(cf * T * k / E) pairs in token order and
+    drops the others; kept pairs keep their gates."""
+    C = int(math.ceil(capacity_factor * plan.T * plan.k / plan.E))
+    rank = np.arange(plan.N) - plan.offsets[plan.expert_of_row]
+    keep = rank < C
+    return _assemble(plan.T, plan.E, plan.k, plan.topk_idx, plan.topk_gate, plan.probs,
+                     plan.token_of_row[keep], plan.expert_of_row[keep], plan.gate_of_row[keep])
+
+
+def route(x, w_gate, bias, k, round_tile=0, opts: RouteOpts = BASE, noise=None):
+    """F1-F5: logits (+ the caller's noise), top-k, gates, optional token rounding
+    or capacity cap, plan."""
     z = router_logits(x, w_gate, bias)
+    if noise is not None:
+        z = z + np.asarray(noise, np.float64)
     idx, S, P = topk_softmax(z, k)
+    if opts.gate == "all":
+        S = np.take_along_axis(P, idx.astype(np.int64), axis=1)
+    elif opts.gate != "topk":
+        raise ValueError(opts.gate)
     E = np.asarray(w_gate).shape[0]
-    plan = round_tokens(idx, S, P, E, round_tile) if round_tile else plan_from_topk(idx, S, P, E)
+    if round_tile and opts.capacity_factor:
+        raise ValueError("token rounding and a capacity factor are not combined")
+    if round_tile:
+        plan = round_tokens(idx, S, P, E, round_tile, gate_all=(opts.gate == "all"))
+    else:
+        plan = plan_from_topk(idx, S, P, E)
+    if opts.capacity_factor:
+        plan = apply_capacity(plan, opts.capacity_factor)
     return z, plan
+
+
+def _softmax_lse(z):
+    z = np.asarray(z, np.float64)
+    m = z.max(axis=1, keepdims=True)
+    ez = np.exp(z - m)
+    s = ez.sum(axis=1, keepdims=True)
+    return ez / s, (m + np.log(s))[:, 0]
+
+
+def router_losses(z, plan: Plan, opts: RouteOpts = BASE):
+    """Router loss terms.  lb = lb_coef * CV(Pbar)^2 with Pbar_e = mean_t P_te and
+    CV = (population std over e) / (mean over e) -- distributed-MoE article,
+    challenge 1; z = z_coef * mean_t lse_t^2; count_mse = mean_e (c_e - mean c)^2
+    of the selected-pair counts (Trinity Large example 2)."""
+    P, lse = _softmax_lse(z)
+    T, E = P.shape
+    pbar = P.sum(axis=0) / T
+    m = pbar.sum() / E
+    var = ((pbar - m) ** 2).sum() / E
+    cv2 = var / (m * m)
+    c = plan.counts_raw.astype(np.float64)
+    cm = c.sum() / E
+    return {"pbar": pbar, "cv2": cv2, "lb": opts.lb_coef * cv2,
+            "zloss": opts.z_coef * float((lse ** 2).sum()) / T,
+            "count_mse": float(((c - cm) ** 2).sum()) / E}
 
 
 # ----------------------------------------------------------------------------
@@ -346,7 +436,7 @@ def forward(x, w1, w2, plan: Plan, prec: Precision = CONTRACT) -> Dict[str, np.n
 # backward: G1-G5
 
 
-def router_backward(plan: Plan, dS):
+def router_backward(plan: Plan, dS, z=None, opts: RouteOpts = BASE):
     """Gradient of the loss w.r.t. the logits from the per-row gate gradients.
 
     Let K_t be the top-k experts of token t (softmax set, gates S) and A_t the
@@ -354,9 +444,18 @@ def router_backward(plan: Plan, dS):
     exp(z_te) / sum_{j in K_t} exp(z_tj), so
       dz_te = [e in A_t] g_te dS_te - [e in K_t] S_te * sum_{e' in A_t} g_te' dS_te'.
     Without rounding A_t = K_t and this is the softmax backward S*(dS - <S,dS>)
-    of the top-k softmax (Trinity Large example 1; Beam blog section 5.3)."""
+    of the top-k softmax (Trinity Large example 1; Beam blog section 5.3).
+
+    With gate "all" every gate is P_te = exp(z_te) / sum_{all j} exp(z_tj), so
+      dz_tj = [j in A_t] g_tj dS_tj - P_tj * sum_{e' in A_t} g_te' dS_te'.
+    The load-balance loss adds P_t * (h - <h, P_t>) with h_e = (1/T) dlb/dPbar_e,
+      dlb/dPbar_e = lb_coef * (2 (Pbar_e - m) / (E m^2) - 2 var / (E m^3)),
+    and the z-loss adds (2 z_coef / T) lse_t P_t (``router_losses`` defines both)."""
     T, E = plan.T, plan.E
     dz = np.zeros((T, E))
+    P = lse = None
+    if opts.dense_dz:
+        P, lse = _softmax_lse(z)
     for t in range(T):
         rows = plan.tok_rows[plan.tok_ptr[t]:plan.tok_ptr[t + 1]]
         acc = 0.0
@@ -365,21 +464,33 @@ def router_backward(plan: Plan, dS):
             gds = plan.gate_of_row[r] * dS[r]
             dz[t, e] += gds
             acc += gds
-        for j in range(plan.k):
-            e = plan.topk_idx[t, j]
-            dz[t, e] -= plan.topk_gate[t, j] * acc
+        if opts.gate == "all":
+            dz[t] -= P[t] * acc
+        else:
+            for j in range(plan.k):
+                e = plan.topk_idx[t, j]
+                dz[t, e] -= plan.topk_gate[t, j] * acc
+    if opts.lb_coef:
+        pbar = P.sum(axis=0) / T
+        m = pbar.sum() / E
+        var = ((pbar - m) ** 2).sum() / E
+        h = opts.lb_coef * (2.0 * (pbar - m) / (E * m * m) - 2.0 * var / (E * m ** 3)) / T
+        dz += P * (h[None, :] - (P @ h)[:, None])
+    if opts.z_coef:
+        dz += (2.0 * opts.z_coef / T) * lse[:, None] * P
     return dz
 
 
 def backward(x, w_gate, w1, w2, plan: Plan, H, dout, prec: Precision = CONTRACT,
-             weight_grads=True) -> Dict[str, np.ndarray]:
+             weight_grads=True, logits=None, opts: RouteOpts = BASE) -> Dict[str, np.ndarray]:
     """Backward of the layer for the loss sum_t <O_t, dout_t>.
 
     SonicMoE article section 1: the router-score gradient of row r is
     dS_r = <dA'_r, A_r> with dA'_r = W2_e^T dO_t, which equals <dO_t, Y_r> since
     y = W2_e a -- so Y is neither stored nor recomputed; A is recomputed from the
     saved H.  The rest is the chain rule through SwiGLU and the two expert GEMMs,
-    the router softmax (``router_backward``) and the router GEMM."""
+    the router softmax (``router_backward``; with routing variants it also takes
+    the router loss terms, which need the logits) and the router GEMM."""
     x = np.asarray(x, np.float64)
     w_gate = np.asarray(w_gate, np.float64)
     H = np.asarray(H, np.float64)
@@ -424,7 +535,7 @@ def backward(x, w_gate, w1, w2, plan: Plan, H, dout, prec: Precision = CONTRACT,
             dw1[e] = _mxk(dH[a:b], prec, 0).T @ _mxk(x_perm[a:b], prec, 0)
             dw2[e] = _mxk(do_perm[a:b], prec, 0).T @ _mxk(gA[a:b], prec, 0)
     dx_perm = prec.st(dx_perm)
-    dz = router_backward(plan, dS)
+    dz = router_backward(plan, dS, logits, opts)
     dzq = prec.st(dz)                                # GEMM operand of the router terms
     dx = np.zeros((T, d))
     for t in range(T):
@@ -436,11 +547,13 @@ def backward(x, w_gate, w1, w2, plan: Plan, H, dout, prec: Precision = CONTRACT,
             "dx": dx, "dw_gate": dw_gate, "dw1": dw1, "dw2": dw2, "A": A}
 
 
-def layer(x, w_gate, bias, w1, w2, k, dout=None, round_tile=0, prec: Precision = CONTRACT):
-    """Route, forward and (when ``dout`` is given) backward in one call."""
-    z, plan = route(x, w_gate, bias, k, round_tile)
+def layer(x, w_gate, bias, w1, w2, k, dout=None, round_tile=0, prec: Precision = CONTRACT,
+          opts: RouteOpts = BASE, noise=None):
+    """Route, forward and (when ``dout`` is given) backward in one call.  The
+    training loss is sum_t <O_t, dout_t> + lb + zloss."""
+    z, plan = route(x, w_gate, bias, k, round_tile, opts, noise)
     fw = forward(x, w1, w2, plan, prec)
-    out = {"logits": z, "plan": plan, **fw}
+    out = {"logits": z, "plan": plan, **fw, **router_losses(z, plan, opts)}
     if dout is not None:
-        out.update(backward(x, w_gate, w1, w2, plan, fw["H"], dout, prec))
+        out.update(backward(x, w_gate, w1, w2, plan, fw["H"], dout, prec, logits=z, opts=opts))
     return out

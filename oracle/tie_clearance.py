@@ -69,14 +69,18 @@ def rounding_tie_tokens(idx, P, E, tile, delta_p):
 
 
 def clear_ties(x, w_gate, bias, k, redraw, round_tile=0, delta_z=1e-3, delta_p=1e-4,
-               max_iter=200):
-    """Redraw rows of ``x`` until routing has no near-tie.  Returns (x, redraws)."""
+               max_iter=200, noise=None):
+    """Redraw rows of ``x`` until routing has no near-tie.  Returns (x, redraws).
+    ``noise`` [T,E] (noisy routing) is added to the logits the decisions use."""
     to_np = (lambda t: t.float().numpy()) if hasattr(x, "float") else (lambda t: np.asarray(t))
     wg = to_np(w_gate)
     b = None if bias is None else to_np(bias)
+    nz = None if noise is None else to_np(noise).astype(np.float64)
     redrawn = 0
     for attempt in range(max_iter):
         z = router_logits(to_np(x), wg, b)
+        if nz is not None:
+            z = z + nz
         bad = topk_tie_tokens(z, k, delta_z)
         if bad.size == 0 and round_tile:
             idx, _, P = topk_softmax(z, k)
