@@ -70,14 +70,39 @@ typedef enum {
  *   round_tile: 0 = no token rounding; otherwise the tile multiple (128 on the
  *         pages; any even value up to 4096) that moe_round_tokens rounds
  *         per-expert counts to.
+ * Routing variants ("Beam" blog sections 2.2, 2.3 and 3.3; distributed-MoE
+ * article, challenge 1; Trinity Large commentary, code example 2).  All zero
+ * is the base layer:
+ *   gate_mode: MOE_GATE_TOPK (0): gates = softmax over the k selected logits;
+ *         MOE_GATE_ALL (1): gates = the softmax over all E logits at the
+ *         selected experts, not renormalised (pairs added by token rounding
+ *         then get P_te too).
+ *   capacity_factor: 0 = none; else expert e keeps only its first
+ *         C = ceil(capacity_factor * T * k / E) rows in token order (computed
+ *         in double precision from the float value); the other pairs are
+ *         dropped (row_of_slot = -1), kept gates unchanged.  Not combined with
+ *         token rounding (MOE_ENOTSUP).
+ *   lb_coef: weight of the load-balance loss lb_coef * CV(Pbar)^2, Pbar_e =
+ *         mean over tokens of the full softmax P_te, CV = population standard
+ *         deviation over the E entries / their mean.
+ *   z_coef: weight of the z-loss z_coef * mean_t (log sum_e exp z_te)^2.
+ *   Both losses are part of the training loss: moe_route writes their values
+ *   to plan.aux and moe_backward adds their gradients to dlogits.
  * Supported (else MOE_ENOTSUP): 1 <= k <= min(E, 8), 1 <= E <= 256,
  * d % 64 == 0, d_ff % 64 == 0 (d_ff % 128 == 0 with bf16/MXFP8 GEMMs),
- * d, d_ff <= 16384, T <= 2^20, T*k + E*round_tile/2 < 2^31. */
+ * d, d_ff <= 16384, T <= 2^20, T*k + E*round_tile/2 < 2^31.  gate_mode
+ * outside {0, 1}, or a negative or non-finite capacity_factor, lb_coef or
+ * z_coef: MOE_EINVAL. */
+enum { MOE_GATE_TOPK = 0, MOE_GATE_ALL = 1 };
 typedef struct moe_shape {
   int32_t T, d, E, k, d_ff;
   int32_t act;
   int32_t gemm;
   int32_t round_tile;
+  int32_t gate_mode;
+  float   capacity_factor;
+  float   lb_coef;
+  float   z_coef;
 } moe_shape;
 
 /* The routing plan: device arrays carved from one caller-allocated blob by
@@ -85,20 +110,25 @@ typedef struct moe_shape {
  * T*k + E*round_tile/2).  Rows are token-expert pairs grouped by expert, and
  * inside one expert ordered by ascending token. */
 typedef struct moe_plan {
-  float   *logits;       /* [T,E]  router logits, bias included                      */
+  float   *logits;       /* [T,E]  router logits, bias (and routing noise) included  */
   float   *probs_t;      /* [E,T]  full softmax, expert-major (token rounding only)  */
   int32_t *topk_idx;     /* [T,k]  selected experts, descending logit, ties -> lower index */
-  float   *topk_gate;    /* [T,k]  softmax over the k selected logits                */
+  float   *topk_gate;    /* [T,k]  gates of the selected experts (see gate_mode)     */
   int32_t *counts_raw;   /* [E]    rows per expert before rounding                   */
   int32_t *counts;       /* [E]    rows per expert (after rounding when enabled)     */
   int32_t *offsets;      /* [E+1]  exclusive scan of counts; offsets[E] = N          */
   int32_t *token_of_row; /* [N_max] token of row r                                   */
   int32_t *expert_of_row;/* [N_max] expert of row r                                  */
   float   *gate_of_row;  /* [N_max] gate of row r                                    */
-  int32_t *row_of_slot;  /* [T,k]  row of slot j of token t, -1 if rounding dropped it */
+  int32_t *row_of_slot;  /* [T,k]  row of slot j of token t, -1 if rounding or the capacity dropped it */
   int32_t *tok_ptr;      /* [T+1]  CSR token -> rows                                 */
   int32_t *tok_rows;     /* [N_max] rows of each token, ascending                    */
   uint32_t *keep_bits;   /* [T, ceil(E/32)] bit (t,e) set when token t has a row at e */
+  float   *aux;          /* [4+E] router loss terms written by moe_route: [0] lb_coef*CV^2,
+                          * [1] z-loss, [2] mean_e (c_e - mean c)^2 of the per-expert counts
+                          * of selected pairs (counts_raw; a monitor, no gradient), [3] CV^2,
+                          * [4..4+E) Pbar.  [2] is always written; the others only when
+                          * lb_coef or z_coef is nonzero.                           */
   int32_t *sched;        /* internal: per-expert tile prefixes and the tile-to-expert map of the grouped GEMMs */
 } moe_plan;
 
@@ -115,9 +145,15 @@ size_t     moe_workspace_bytes(const moe_shape *s, int which);
 /* Router GEMM, top-k softmax and the plan (histogram, prefix scan, stable
  * scatter by token).  x [T,d] (act), w_gate [E,d] (act), bias [E] float32 or
  * NULL (added to the logits before top-k and softmax; receives no gradient).
- * With round_tile == 0 the plan is final; otherwise call moe_round_tokens. */
+ * noise [T,E] float32 or NULL: routing noise drawn by the caller ("Beam" blog
+ * section 3.3, noisy top-k), added to the logits after the bias; top-k, gates
+ * and the router losses use the noisy logits; no gradient flows to it.
+ * With capacity_factor > 0 the plan is built, then each expert's pairs past
+ * its capacity are dropped and the plan rebuilt.  With lb_coef or z_coef
+ * nonzero the loss values go to plan.aux.  With round_tile == 0 the plan is
+ * final; otherwise call moe_round_tokens. */
 moe_status moe_route(const moe_shape *s, const void *x, const void *w_gate, const float *bias,
-                     moe_plan *plan, void *ws, size_t ws_bytes, void *stream);
+                     const float *noise, moe_plan *plan, void *ws, size_t ws_bytes, void *stream);
 
 /* Token rounding (SonicMoE article, section 3): every expert's row count moves
  * to the nearest multiple of round_tile (half rounds up; if that exceeds T it

@@ -30,12 +30,13 @@ EXPORTS = ("moe_max_rows", "moe_plan_bytes", "moe_plan_init", "moe_workspace_byt
 class MoeShape(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("E", ctypes.c_int32), ("k", ctypes.c_int32),
                 ("d_ff", ctypes.c_int32), ("act", ctypes.c_int32), ("gemm", ctypes.c_int32),
-                ("round_tile", ctypes.c_int32)]
+                ("round_tile", ctypes.c_int32), ("gate_mode", ctypes.c_int32),
+                ("capacity_factor", ctypes.c_float), ("lb_coef", ctypes.c_float), ("z_coef", ctypes.c_float)]
 
 
 _PLAN_FIELDS = ("logits", "probs_t", "topk_idx", "topk_gate", "counts_raw", "counts", "offsets",
                 "token_of_row", "expert_of_row", "gate_of_row", "row_of_slot", "tok_ptr", "tok_rows",
-                "keep_bits", "sched")
+                "keep_bits", "aux", "sched")
 
 
 class MoePlan(ctypes.Structure):
@@ -49,7 +50,7 @@ for name, res, args in [
     ("moe_plan_bytes", _sz, [_P_SHAPE]),
     ("moe_plan_init", ctypes.c_int, [_P_SHAPE, _vp, _sz, _P_PLAN]),
     ("moe_workspace_bytes", _sz, [_P_SHAPE, ctypes.c_int]),
-    ("moe_route", ctypes.c_int, [_P_SHAPE, _vp, _vp, _vp, _P_PLAN, _vp, _sz, _vp]),
+    ("moe_route", ctypes.c_int, [_P_SHAPE, _vp, _vp, _vp, _vp, _P_PLAN, _vp, _sz, _vp]),
     ("moe_round_tokens", ctypes.c_int, [_P_SHAPE, _P_PLAN, _vp, _sz, _vp]),
     ("moe_permute", ctypes.c_int, [_P_SHAPE, _vp, _P_PLAN, _vp, _vp]),
     ("moe_grouped_gemm_swiglu", ctypes.c_int, [_P_SHAPE, _vp, _vp, _vp, _P_PLAN, _vp, _vp, _vp, _sz, _vp]),
@@ -85,16 +86,22 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def make_shape(T, d, E, k, d_ff, act=MOE_BF16, gemm=None, round_tile=0) -> MoeShape:
+MOE_GATE_TOPK, MOE_GATE_ALL = 0, 1
+
+
+def make_shape(T, d, E, k, d_ff, act=MOE_BF16, gemm=None, round_tile=0, gate_mode=MOE_GATE_TOPK,
+               capacity_factor=0.0, lb_coef=0.0, z_coef=0.0) -> MoeShape:
     if gemm is None:
         gemm = act
-    return MoeShape(T, d, E, k, d_ff, act, gemm, round_tile)
+    return MoeShape(T, d, E, k, d_ff, act, gemm, round_tile, gate_mode, capacity_factor, lb_coef, z_coef)
 
 
 def shape_of(cfg: MoEConfig) -> MoeShape:
     act = MOE_BF16 if cfg.act == "bf16" else MOE_F32
     gemm = {"bf16": MOE_BF16, "f32": MOE_F32, "mxfp8": MOE_MXFP8}[cfg.gemm]
-    return make_shape(cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, act, gemm, cfg.round_tile)
+    gate_mode = {"topk": MOE_GATE_TOPK, "all": MOE_GATE_ALL}[cfg.gate]
+    return make_shape(cfg.T, cfg.d, cfg.E, cfg.k, cfg.f, act, gemm, cfg.round_tile, gate_mode,
+                      cfg.capacity_factor, cfg.lb_coef, cfg.z_coef)
 
 
 def max_rows(s: MoeShape) -> int:
@@ -150,6 +157,7 @@ class Plan:
             "tok_ptr": self.view("tok_ptr", s.T + 1),
             "tok_rows": self.view("tok_rows", N),
             "keep_bits": self.view("keep_bits", s.T * W).view(s.T, W),
+            "aux": self.view("aux", 4 + s.E, torch.float32),
         }
         if s.round_tile:
             out["probs_t"] = self.view("probs_t", s.E * s.T, torch.float32).view(s.E, s.T)
@@ -165,9 +173,10 @@ def _aligned_ws(nbytes: int, device="cuda") -> torch.Tensor:
 # ----------------------------------------------------------------- entry points
 
 
-def route(s: MoeShape, x, w_gate, bias, plan: Plan, ws=None, stream=None):
-    _check("moe_route", _lib.moe_route(ctypes.byref(s), _ptr(x), _ptr(w_gate), _ptr(bias), ctypes.byref(plan.c),
-                                       _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
+def route(s: MoeShape, x, w_gate, bias, plan: Plan, ws=None, stream=None, noise=None):
+    _check("moe_route", _lib.moe_route(ctypes.byref(s), _ptr(x), _ptr(w_gate), _ptr(bias), _ptr(noise),
+                                       ctypes.byref(plan.c), _ptr(ws), 0 if ws is None else ws.numel(),
+                                       _stream(stream)))
 
 
 def round_tokens(s: MoeShape, plan: Plan, ws=None, stream=None):
@@ -240,7 +249,8 @@ class LayerRun:
             self.ws_bwd = _aligned_ws(workspace_bytes(s, MOE_WS_BACKWARD), device)
 
     def route(self, stream=None):
-        route(self.s, self.inp["x"], self.inp["w_gate"], self.inp.get("bias"), self.plan, stream=stream)
+        route(self.s, self.inp["x"], self.inp["w_gate"], self.inp.get("bias"), self.plan, stream=stream,
+              noise=self.inp.get("noise"))
         if self.s.round_tile:
             round_tokens(self.s, self.plan, stream=stream)
 

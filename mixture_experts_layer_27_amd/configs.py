@@ -43,6 +43,12 @@ class MoEConfig:
     round_tile: int = 0            # 0: no token rounding; else tile multiple
     backward: bool = True
     seed: int = 0
+    # routing variants (0 / "topk" = the base layer)
+    gate: str = "topk"             # "topk": softmax over the k selected; "all": full softmax, not renormalised
+    capacity_factor: float = 0.0   # 0: no cap; else each expert keeps its first ceil(cf*T*k/E) rows
+    lb_coef: float = 0.0           # load-balance loss weight (CV(Pbar)^2)
+    z_coef: float = 0.0            # z-loss weight (mean lse^2)
+    noise_std: float = 0.0         # routing noise ~ N(0, noise_std^2) [T, E] added to the logits
 
     @property
     def N(self) -> int:

@@ -51,12 +51,14 @@ void carve_plan(const moe_shape& s, char* base, moe_plan* p, size_t* total) {
   q.tok_ptr = c.take<int32_t>((T + 1) * 4);
   q.tok_rows = c.take<int32_t>(N * 4);
   q.keep_bits = c.take<uint32_t>(T * words_of(s) * 4);
+  q.aux = c.take<float>((4 + E) * 4);
   // internal region
   q.sched = c.take<int32_t>((E + 1) * 4);
   c.take<int32_t>(max_mtiles128(s) * 4);
   c.take<int32_t>(E * nblk_of(s) * 4);
   c.take<int32_t>((nblk_of(s) + 1) * 4);
   if (s.round_tile) c.take<uint32_t>(E * ((T + 31) / 32) * 4);
+  c.take<float>((size_t)nblk_of(s) * (E + 1) * 4);   // router-loss partials
   if (p) *p = q;
   if (total) *total = c.off;
 }
@@ -70,6 +72,10 @@ moe_status check_shape(const moe_shape* s) {
   if ((s->gemm == MOE_BF16 || s->gemm == MOE_MXFP8) && s->act != MOE_BF16) return MOE_EINVAL;
   if (s->gemm != MOE_F32 && s->gemm != MOE_BF16 && s->gemm != MOE_MXFP8) return MOE_EINVAL;
   if (s->round_tile < 0 || (s->round_tile & 1)) return MOE_EINVAL;
+  if (s->gate_mode != MOE_GATE_TOPK && s->gate_mode != MOE_GATE_ALL) return MOE_EINVAL;
+  for (float v : {s->capacity_factor, s->lb_coef, s->z_coef})
+    if (!(v >= 0.0f) || !(v <= 3.0e38f)) return MOE_EINVAL;   // negative, NaN or infinite
+  if (s->capacity_factor > 0.0f && s->round_tile) return MOE_ENOTSUP;
   if (s->k > 8 || s->E > 256) return MOE_ENOTSUP;
   if (s->d % 64 || s->d_ff % 64) return MOE_ENOTSUP;
   if (s->act == MOE_BF16 && s->d_ff % 128) return MOE_ENOTSUP;
@@ -124,6 +130,7 @@ int64_t wgrad_cap(const moe_shape& s) { return s.gemm == MOE_MXFP8 ? tok_cap(s) 
 struct BwdWs {
   void *do_perm, *dh, *ga, *xbuf, *dzq;
   float *ds_part, *dlogits, *dwg_part;
+  float* dxr;   // dense router term dz W_g [T, d] (routing variants only)
   WgradChunks wg;
   // MXFP8 only
   MxOperand doq, w2t, dhq, w1t, dh_t, x_t, do_t, ga_t;
@@ -142,6 +149,7 @@ size_t carve_bwd(const moe_shape& s, char* base, BwdWs* w) {
   q.dlogits = c.take<float>((size_t)s.T * s.E * 4);
   q.dzq = c.take<char>((size_t)s.T * ldz_of(s) * esz(s));
   q.dwg_part = c.take<float>((size_t)gemm_router_dwg_splits(s) * s.E * s.d * 4);
+  q.dxr = dense_router_grad(s) ? c.take<float>((size_t)s.T * s.d * 4) : nullptr;
   {
     const int64_t ncap = wgrad_cap(s);
     WgradChunks& g = q.wg;
@@ -215,6 +223,8 @@ PlanInternal plan_internal(const moe_shape& s, const moe_plan& p) {
   pi.blk_tok = reinterpret_cast<int32_t*>(b);
   b += al((size_t)(pi.nblk + 1) * 4);
   pi.sel_t = s.round_tile ? reinterpret_cast<uint32_t*>(b) : nullptr;
+  if (s.round_tile) b += al((size_t)s.E * ((s.T + 31) / 32) * 4);
+  pi.loss_part = reinterpret_cast<float*>(b);
   return pi;
 }
 
@@ -256,19 +266,26 @@ size_t moe_workspace_bytes(const moe_shape* s, int which) {
   }
 }
 
-moe_status moe_route(const moe_shape* s, const void* x, const void* w_gate, const float* bias, moe_plan* plan,
-                     void* ws, size_t ws_bytes, void* stream) {
+moe_status moe_route(const moe_shape* s, const void* x, const void* w_gate, const float* bias, const float* noise,
+                     moe_plan* plan, void* ws, size_t ws_bytes, void* stream) {
   (void)ws;
   (void)ws_bytes;
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
-  if (!aligned(x) || !aligned(w_gate) || (bias && (reinterpret_cast<uintptr_t>(bias) & 3))) return MOE_EINVAL;
+  if (!aligned(x) || !aligned(w_gate) || (bias && (reinterpret_cast<uintptr_t>(bias) & 3)) ||
+      (noise && (reinterpret_cast<uintptr_t>(noise) & 3)))
+    return MOE_EINVAL;
   if ((st = check_plan(*s, plan)) != MOE_OK) return st;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   PlanInternal pi = plan_internal(*s, *plan);
-  hipError_t e = gemm_router_logits(*s, x, w_gate, bias, plan->logits, hs);
+  hipError_t e = gemm_router_logits(*s, x, w_gate, bias, noise, plan->logits, hs);
   if (e == hipSuccess) e = launch_topk(*s, *plan, pi, s->round_tile != 0, hs);
   if (e == hipSuccess) e = launch_plan_build(*s, *plan, pi, true, false, hs);
+  if (s->capacity_factor > 0.0f) {
+    if (e == hipSuccess) e = launch_capacity_drop(*s, *plan, pi, hs);
+    if (e == hipSuccess) e = launch_plan_build(*s, *plan, pi, false, false, hs);
+  }
+  if (e == hipSuccess && (s->lb_coef != 0.0f || s->z_coef != 0.0f)) e = launch_router_losses(*s, *plan, pi, hs);
   return hip_status(e);
 }
 
@@ -396,7 +413,8 @@ moe_status moe_backward(const moe_shape* s, const void* x, const void* w_gate, c
   }
   if (e == hipSuccess)
     e = launch_router_bwd(*s, *plan, w.ds_part, gemm_dact_parts(*s), ds, dz, w.dzq, ldz, hs);
-  if (e == hipSuccess) e = launch_router_dx(*s, *plan, w.xbuf, dz, w_gate, dx, hs);
+  if (e == hipSuccess && w.dxr) e = gemm_router_dx_dense(*s, w.dzq, ldz, w_gate, w.dxr, hs);
+  if (e == hipSuccess) e = launch_router_dx(*s, *plan, w.xbuf, dz, w_gate, w.dxr, dx, hs);
   if (e == hipSuccess) e = gemm_router_dwg(*s, w.dzq, ldz, x, w.dwg_part, hs);
   if (e == hipSuccess)
     e = launch_splitk_reduce(w.dwg_part, gemm_router_dwg_splits(*s), (int64_t)s->E * s->d, dw_gate, hs);

@@ -108,7 +108,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, c
 // t has no row at it (token rounding dropped the pair).
 // One wave per token: the token's rows, experts and dz values are read once
 // (wave-uniform), then each lane accumulates up to four 16-byte column chunks
-// with all their row loads in flight.
+// with all their row loads in flight.  When dz is dense (routing variants) the
+// router term comes precomputed as dxr = dz W_g (fp32 [T, d], a GEMM) instead.
 template <typename T>
 __global__ __launch_bounds__(256) void router_dx_kernel(const T* __restrict__ dx_perm, const int32_t* __restrict__ tok_ptr,
                                                        const int32_t* __restrict__ tok_rows,
@@ -116,6 +117,7 @@ __global__ __launch_bounds__(256) void router_dx_kernel(const T* __restrict__ dx
                                                        const int32_t* __restrict__ topk_idx,
                                                        const uint32_t* __restrict__ keep_bits, int words,
                                                        const float* __restrict__ dz, const T* __restrict__ wg,
+                                                       const float* __restrict__ dxr,
                                                        int T_, int E, int d, int k, T* __restrict__ out) {
   constexpr int EV = 16 / sizeof(T);
   constexpr int CL = 4;                       // column chunks per lane per pass
@@ -146,14 +148,14 @@ __global__ __launch_bounds__(256) void router_dx_kernel(const T* __restrict__ dx
     for (int p = p0; p < p1; ++p) {           // rows in ascending order
       const int r = tok_rows[p];
       const int e = expert_of_row[r];
-      const float z = dzt[e];
+      const float z = dxr ? 0.0f : dzt[e];
       u32x4 v[CL], w[CL];
 #pragma unroll
       for (int j = 0; j < CL; ++j) {
         const int c = cb + lane + 64 * j;
         if (c < vec) {
           v[j] = ldg16(dx_perm + (int64_t)r * d + c * EV);
-          w[j] = ldg16(wg + (int64_t)e * d + c * EV);
+          w[j] = dxr ? u32x4{0u, 0u, 0u, 0u} : ldg16(wg + (int64_t)e * d + c * EV);
         } else {
           v[j] = w[j] = u32x4{0u, 0u, 0u, 0u};
         }
@@ -164,7 +166,17 @@ __global__ __launch_bounds__(256) void router_dx_kernel(const T* __restrict__ dx
         add(acc[j], w[j], z);
       }
     }
-    for (int i = 0; i < k; ++i) {
+    if (dxr) {
+#pragma unroll
+      for (int j = 0; j < CL; ++j) {
+        const int c = cb + lane + 64 * j;
+        if (c >= vec) continue;
+        const float* src = dxr + (int64_t)t * d + c * EV;
+#pragma unroll
+        for (int q = 0; q < EV; ++q) acc[j][q] += src[q];
+      }
+    }
+    for (int i = 0; i < k && !dxr; ++i) {
       const int e = topk_idx[(int64_t)t * k + i];
       if ((keep_bits[(int64_t)t * words + (e >> 5)] >> (e & 31)) & 1u) continue;
       const float z = dzt[e];
@@ -194,6 +206,13 @@ __global__ __launch_bounds__(256) void router_dx_kernel(const T* __restrict__ dx
 // Router backward, one wave per token.  dS of every row is a fixed-order sum of
 // the per-column-tile partials.  For token t with top-k set K (gates S) and rows
 // A (gates g):  dz_e = [e in A] g_e dS_e - [e in K] S_e * sum_{A} g dS.
+// Routing variants ("Beam" blog sections 2.2/2.3, distributed-MoE article,
+// challenge 1) make dz dense over all E: with full-softmax gates the second
+// term is -P_e * sum_A g dS (P = softmax of the token's logits); the
+// load-balance loss lb_coef * CV(Pbar)^2 adds P_e (h_e - <h, P>) with
+// h_e = (lb_coef / T) (2 (Pbar_e - m) / (E m^2) - 2 var / (E m^3)), m and var
+// the mean and population variance of Pbar (from the forward, aux[4..]); the
+// z-loss adds (2 z_coef / T) lse P_e.
 // Writes dlogits (fp32) and the GEMM operand dzq (act dtype, ld = ldz, zero padded).
 template <typename T>
 __global__ __launch_bounds__(256) void router_bwd_kernel(const int32_t* __restrict__ tok_ptr,
@@ -205,7 +224,9 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const int32_t* __restri
                                                         const float* __restrict__ ds_part, int nparts,
                                                         int64_t part_stride, int T_, int E, int k,
                                                         float* __restrict__ ds_out, float* __restrict__ dlogits,
-                                                        T* __restrict__ dzq, int ldz) {
+                                                        T* __restrict__ dzq, int ldz, int gate_all,
+                                                        const float* __restrict__ logits,
+                                                        const float* __restrict__ aux, float lb_coef, float z_coef) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T_) return;
@@ -236,9 +257,64 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const int32_t* __restri
       if ((e & 63) == lane) vals[e >> 6] += gds;
     }
   }
-  for (int j = 0; j < k; ++j) {
-    const int e = topk_idx[(int64_t)t * k + j];
-    if ((e & 63) == lane) vals[e >> 6] -= topk_gate[(int64_t)t * k + j] * acc;
+  const bool dense = gate_all || lb_coef != 0.0f || z_coef != 0.0f;   // uniform over the grid
+  if (!gate_all) {
+    for (int j = 0; j < k; ++j) {
+      const int e = topk_idx[(int64_t)t * k + j];
+      if ((e & 63) == lane) vals[e >> 6] -= topk_gate[(int64_t)t * k + j] * acc;
+    }
+  }
+  if (dense) {
+    // the token's full softmax P and log-sum-exp from its logits
+    float z[4], P[4];
+    float m = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int e = lane + 64 * v;
+      z[v] = e < E ? logits[(int64_t)t * E + e] : -INFINITY;
+      m = fmaxf(m, z[v]);
+    }
+    m = wave_max(m);
+    float sl = 0.0f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) sl += (lane + 64 * v < E) ? expf(z[v] - m) : 0.0f;
+    const float se = wave_sum(sl);
+#pragma unroll
+    for (int v = 0; v < 4; ++v) P[v] = (lane + 64 * v < E) ? expf(z[v] - m) / se : 0.0f;
+    if (gate_all) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) vals[v] -= P[v] * acc;
+    }
+    if (lb_coef != 0.0f) {
+      float pb[4], sp = 0.0f;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        pb[v] = (lane + 64 * v < E) ? aux[4 + lane + 64 * v] : 0.0f;
+        sp += pb[v];
+      }
+      const float mean = wave_sum(sp) / (float)E;
+      float sv = 0.0f;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sv += (lane + 64 * v < E) ? (pb[v] - mean) * (pb[v] - mean) : 0.0f;
+      const float var = wave_sum(sv) / (float)E;
+      float h[4], sh = 0.0f;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        h[v] = (lane + 64 * v < E)
+                   ? (lb_coef / (float)T_) * (2.0f * (pb[v] - mean) / ((float)E * mean * mean) -
+                                              2.0f * var / ((float)E * mean * mean * mean))
+                   : 0.0f;
+        sh += h[v] * P[v];
+      }
+      const float hp = wave_sum(sh);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) vals[v] += P[v] * (h[v] - hp);
+    }
+    if (z_coef != 0.0f) {
+      const float c = 2.0f * z_coef / (float)T_ * (m + logf(se));
+#pragma unroll
+      for (int v = 0; v < 4; ++v) vals[v] += c * P[v];
+    }
   }
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
@@ -344,16 +420,16 @@ hipError_t launch_combine(const moe_shape& s, const void* y, const moe_plan& p, 
 }
 
 hipError_t launch_router_dx(const moe_shape& s, const moe_plan& p, const void* dx_perm, const float* dz,
-                            const void* wg, void* dx, hipStream_t st) {
+                            const void* wg, const float* dxr, void* dx, hipStream_t st) {
   const int words = (s.E + 31) / 32;
   if (s.act == MOE_BF16) {
     hipLaunchKernelGGL(router_dx_kernel<bf16_t>, dim3(ceil_div(s.T, 4)), dim3(256), 0, st, (const bf16_t*)dx_perm,
                        p.tok_ptr, p.tok_rows, p.expert_of_row, p.topk_idx, p.keep_bits, words, dz,
-                       (const bf16_t*)wg, s.T, s.E, s.d, s.k, (bf16_t*)dx);
+                       (const bf16_t*)wg, dxr, s.T, s.E, s.d, s.k, (bf16_t*)dx);
   } else {
     hipLaunchKernelGGL(router_dx_kernel<float>, dim3(ceil_div(s.T, 4)), dim3(256), 0, st, (const float*)dx_perm,
                        p.tok_ptr, p.tok_rows, p.expert_of_row, p.topk_idx, p.keep_bits, words, dz,
-                       (const float*)wg, s.T, s.E, s.d, s.k, (float*)dx);
+                       (const float*)wg, dxr, s.T, s.E, s.d, s.k, (float*)dx);
   }
   return hipGetLastError();
 }
@@ -365,11 +441,13 @@ hipError_t launch_router_bwd(const moe_shape& s, const moe_plan& p, const float*
   if (s.act == MOE_BF16)
     hipLaunchKernelGGL(router_bwd_kernel<bf16_t>, dim3(grid), dim3(256), 0, st, p.tok_ptr, p.tok_rows,
                        p.expert_of_row, p.gate_of_row, p.topk_idx, p.topk_gate, ds_part, nparts, pstride, s.T, s.E,
-                       s.k, ds_out, dlogits, (bf16_t*)dzq, ldz);
+                       s.k, ds_out, dlogits, (bf16_t*)dzq, ldz, (int)(s.gate_mode == MOE_GATE_ALL), p.logits,
+                       p.aux, s.lb_coef, s.z_coef);
   else
     hipLaunchKernelGGL(router_bwd_kernel<float>, dim3(grid), dim3(256), 0, st, p.tok_ptr, p.tok_rows,
                        p.expert_of_row, p.gate_of_row, p.topk_idx, p.topk_gate, ds_part, nparts, pstride, s.T, s.E,
-                       s.k, ds_out, dlogits, (float*)dzq, ldz);
+                       s.k, ds_out, dlogits, (float*)dzq, ldz, (int)(s.gate_mode == MOE_GATE_ALL), p.logits,
+                       p.aux, s.lb_coef, s.z_coef);
   return hipGetLastError();
 }
 

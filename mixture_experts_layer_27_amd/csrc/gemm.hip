@@ -211,17 +211,32 @@ hipError_t gemm_dw2(const moe_shape& s, const WgradChunks& w, const void* do_per
 // ---------------------------------------------------------------- router
 
 hipError_t gemm_router_logits(const moe_shape& s, const void* x, const void* wg, const float* bias,
-                              float* logits, hipStream_t st) {
+                              const float* noise, float* logits, hipStream_t st) {
   Args a = base_args();
   a.A = x; a.lda = s.d;
   a.B = wg; a.ldb = s.d;
   a.C = logits; a.ldc = s.E;
   a.bias = bias;
+  a.aux = noise; a.ld_aux = s.E;         // routing noise [T, E] or nullptr
   a.M = s.T; a.N = s.E; a.K = s.d;
   a.tilesM = ceil_div(s.T, 128); a.tilesN = ceil_div(s.E, 64);
   a.total_static = a.tilesM * a.tilesN;
   if (s.act == MOE_BF16) return run<bf16_t, 128, 64, 4, 1, true, true, GROUP_NONE, EPI_LOGITS>(a, a.total_static, st);
   return run<float, 128, 64, 4, 1, true, true, GROUP_NONE, EPI_LOGITS>(a, a.total_static, st);
+}
+
+// Dense router term of the input gradient: dxr = dzq W_g, K = E.
+hipError_t gemm_router_dx_dense(const moe_shape& s, const void* dzq, int ldz, const void* wg, float* dxr,
+                                hipStream_t st) {
+  Args a = base_args();
+  a.A = dzq; a.lda = ldz;                // [T, K = E]
+  a.B = wg; a.ldb = s.d;                 // W_g [E, d] read as [K = E, N = d]
+  a.C = dxr; a.ldc = s.d;
+  a.M = s.T; a.N = s.d; a.K = s.E;
+  a.tilesM = ceil_div(s.T, 128); a.tilesN = ceil_div(s.d, 128);
+  a.total_static = a.tilesM * a.tilesN;
+  if (s.act == MOE_BF16) return run<bf16_t, 128, 128, 2, 2, true, false, GROUP_NONE, EPI_F32>(a, a.total_static, st);
+  return run<float, 128, 128, 2, 2, true, false, GROUP_NONE, EPI_F32>(a, a.total_static, st);
 }
 
 int gemm_router_dwg_splits(const moe_shape& s) {

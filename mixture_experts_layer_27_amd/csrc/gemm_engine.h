@@ -450,10 +450,11 @@ MOE_DEV void gemm_epilogue(const Args& args, const TileCtx& ctx, f32x16 (&acc)[B
 #pragma unroll
         for (int c = 0; c < 8; ++c) v[c] = src[c];
         OT* dst = C + (int64_t)grow * args.ldc + col;
-        if constexpr (EPI == EPI_LOGITS) {
+        if constexpr (EPI == EPI_LOGITS) {   // + bias [N], + noise [M, N] (args.aux, routing noise)
+          const float* nz = args.aux ? reinterpret_cast<const float*>(args.aux) + (int64_t)grow * args.ld_aux : nullptr;
 #pragma unroll
           for (int c = 0; c < 8; ++c)
-            if (col + c < args.N) dst[c] = v[c] + (args.bias ? args.bias[col + c] : 0.0f);
+            if (col + c < args.N) dst[c] = (v[c] + (args.bias ? args.bias[col + c] : 0.0f)) + (nz ? nz[col + c] : 0.0f);
         } else {
           Vec8<OT>::store(dst, v);
         }

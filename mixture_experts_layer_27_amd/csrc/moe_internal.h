@@ -23,6 +23,7 @@ struct PlanInternal {
   int32_t* hist;
   int32_t* blk_tok;
   uint32_t* sel_t;
+  float* loss_part;   // [nblk][E+1] router-loss partial sums
   int nblk;
   int words;   // ceil(E/32)
 };
@@ -38,6 +39,14 @@ hipError_t launch_plan_build(const moe_shape& s, const moe_plan& p, const PlanIn
                              bool with_prob_gates, hipStream_t st);
 hipError_t launch_round_select(const moe_shape& s, const moe_plan& p, const PlanInternal& pi,
                                hipStream_t st);
+// capacity factor: clear the keep bits of each expert's rows past its capacity
+hipError_t launch_capacity_drop(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, hipStream_t st);
+// load-balance and z-loss values into plan.aux
+hipError_t launch_router_losses(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, hipStream_t st);
+// dz is nonzero beyond each token's selected experts
+inline bool dense_router_grad(const moe_shape& s) {
+  return s.gate_mode == MOE_GATE_ALL || s.lb_coef != 0.0f || s.z_coef != 0.0f;
+}
 
 // Weight-gradient K chunks (see wgrad_chunks_kernel): tables in the backward
 // workspace, partial outputs for chunks past each expert's first.
@@ -55,8 +64,9 @@ struct WgradChunks {
 hipError_t launch_permute_rows(const moe_shape& s, const void* src, const moe_plan& p, void* dst, hipStream_t st);
 hipError_t launch_combine(const moe_shape& s, const void* y, const moe_plan& p, void* out,
                           hipStream_t st);
+// dxr: the dense router term dz W_g (fp32 [T,d]) or nullptr (then gathered from W_g)
 hipError_t launch_router_dx(const moe_shape& s, const moe_plan& p, const void* dx_perm, const float* dz,
-                            const void* wg, void* dx, hipStream_t st);
+                            const void* wg, const float* dxr, void* dx, hipStream_t st);
 hipError_t launch_router_bwd(const moe_shape& s, const moe_plan& p, const float* ds_part, int nparts,
                              float* ds_out, float* dlogits, void* dzq, int ldz, hipStream_t st);
 hipError_t launch_splitk_reduce(const float* part, int nsplit, int64_t n, float* out, hipStream_t st);
@@ -83,7 +93,10 @@ hipError_t gemm_dw1(const moe_shape& s, const WgradChunks& w, const void* dh, co
 hipError_t gemm_dw2(const moe_shape& s, const WgradChunks& w, const void* do_perm, const void* ga, float* dw2,
                     hipStream_t st);
 hipError_t gemm_router_logits(const moe_shape& s, const void* x, const void* wg, const float* bias,
-                              float* logits, hipStream_t st);
+                              const float* noise, float* logits, hipStream_t st);
+// dxr [T,d] fp32 = dzq [T, ldz] W_g (dense router gradients)
+hipError_t gemm_router_dx_dense(const moe_shape& s, const void* dzq, int ldz, const void* wg, float* dxr,
+                                hipStream_t st);
 int gemm_router_dwg_splits(const moe_shape& s);
 hipError_t gemm_router_dwg(const moe_shape& s, const void* dzq, int ldz, const void* x, float* part,
                            hipStream_t st);

@@ -5,10 +5,19 @@
 // Top-k follows the "Beam" blog (section 5.3) and the "Trinity Large" commentary
 // (code example 1): experts are ranked by logit, the k best are kept and their
 // gates are a softmax over those k logits.  Ties go to the lower expert index.
+// With MOE_GATE_ALL the gates are the full softmax at the selected experts,
+// not renormalised (the blog's section 2.2 formula; its section 3.3 names the
+// choice).  Routing variants of its section 2.3 and of the distributed-MoE
+// article (challenge 1): a per-expert capacity that drops the pairs past it in
+// token order, and the load-balance loss CV(Pbar)^2 and z-loss, reduced here
+// in a fixed order.
 // The plan lays the token-expert pairs out as contiguous per-expert row
 // segments ("row-wise" expert buffers of the Olmo-core 3 article, "three splits"
 // section), tokens ascending inside a segment; everything stays on the device.
 // Token rounding follows the SonicMoE article, section 3.
+#include <cmath>
+#include <cstdint>
+
 #include "moe_common.h"
 #include "moe_internal.h"
 
@@ -26,7 +35,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
                                                   int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate,
                                                   uint32_t* __restrict__ keep_bits, int words,
                                                   float* __restrict__ probs_t, uint32_t* __restrict__ sel_t,
-                                                  int wordsT) {
+                                                  int wordsT, int gate_all) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   float* pt = reinterpret_cast<float*>(smem);                       // [E][64]
   uint32_t* sel = reinterpret_cast<uint32_t*>(smem + (size_t)E * 64 * 4);  // [E][2]
@@ -71,9 +80,18 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
       for (int v = 0; v < V; ++v)
         if (lane + 64 * v == be) taken[v] = true;
     }
-    // softmax over the k selected logits (the first is the largest)
+    // softmax over the k selected logits (the first is the largest), or the
+    // full softmax's denominator (gate_all, uniform over the wave)
     float den = 0.0f;
-    for (int j = 0; j < k; ++j) den += expf(sel_z[j] - sel_z[0]);
+    if (gate_all) {
+      float sa = 0.0f;
+#pragma unroll
+      for (int v = 0; v < V; ++v)
+        if (lane + 64 * v < E) sa += expf(z[v] - sel_z[0]);
+      den = wave_sum(sa);
+    } else {
+      for (int j = 0; j < k; ++j) den += expf(sel_z[j] - sel_z[0]);
+    }
     if (lane < k) {
       float zj = sel_z[0];
       int ej = sel_e[0];
@@ -202,8 +220,10 @@ MOE_DEV int block_scan_inplace(int32_t* a, int64_t n, int* sh) {
 __global__ __launch_bounds__(1024) void plan_scan_kernel(int E, int nblk, int32_t* __restrict__ hist,
                                                         int32_t* __restrict__ blk_tok, int32_t* __restrict__ counts,
                                                         int32_t* __restrict__ counts_raw, int32_t* __restrict__ offsets,
-                                                        int32_t* __restrict__ pre128, int32_t* __restrict__ tile_e) {
+                                                        int32_t* __restrict__ pre128, int32_t* __restrict__ tile_e,
+                                                        float* __restrict__ aux) {
   __shared__ int sh[1024];
+  __shared__ double red[1024];
   const int total = block_scan_inplace(hist, (int64_t)E * nblk, sh);
   const int toks = block_scan_inplace(blk_tok, nblk, sh);
   if (threadIdx.x == 0) blk_tok[nblk] = toks;
@@ -219,6 +239,23 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(int E, int nblk, int32_
     if (counts_raw) counts_raw[e] = cnt;
   }
   if (e == 0) offsets[E] = total;
+  if (aux) {   // count monitor (Trinity Large example 2): mean_e (c_e - mean c)^2, fixed-order tree sums
+    red[e] = (double)cnt;
+    __syncthreads();
+    for (int o = 512; o > 0; o >>= 1) {
+      if (e < o) red[e] += red[e + o];
+      __syncthreads();
+    }
+    const double mean = red[0] / E;
+    __syncthreads();
+    red[e] = e < E ? ((double)cnt - mean) * ((double)cnt - mean) : 0.0;
+    __syncthreads();
+    for (int o = 512; o > 0; o >>= 1) {
+      if (e < o) red[e] += red[e + o];
+      __syncthreads();
+    }
+    if (e == 0) aux[2] = (float)(red[0] / E);
+  }
   // 128-row m-tile prefix over the experts (block scan), then each expert's tiles
   const int tiles = (cnt + 127) / 128;
   sh[e] = tiles;
@@ -240,7 +277,7 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(int E, int nblk, int32_
 __global__ __launch_bounds__(256) void plan_scatter_kernel(
     const uint32_t* __restrict__ keep_bits, int T, int E, int k, int words, int nblk,
     const int32_t* __restrict__ hist, const int32_t* __restrict__ blk_tok, const int32_t* __restrict__ topk_idx,
-    const float* __restrict__ topk_gate, const float* __restrict__ probs_t, bool prob_gates,
+    const float* __restrict__ topk_gate, const float* __restrict__ probs_t, bool prob_gates, bool gate_all,
     int32_t* __restrict__ token_of_row, int32_t* __restrict__ expert_of_row, float* __restrict__ gate_of_row,
     int32_t* __restrict__ row_of_slot, int32_t* __restrict__ tok_ptr, int32_t* __restrict__ tok_rows) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -273,7 +310,7 @@ __global__ __launch_bounds__(256) void plan_scatter_kernel(
     return r;
   };
   float ptop = 0.0f;
-  if (prob_gates)
+  if (prob_gates && !gate_all)
     for (int j = 0; j < k; ++j) ptop += probs_t[(int64_t)topk_idx[(int64_t)t * k + j] * T + t];
   for (int j = 0; j < k; ++j) row_of_slot[(int64_t)t * k + j] = -1;
   int n = 0;
@@ -292,7 +329,8 @@ __global__ __launch_bounds__(256) void plan_scatter_kernel(
         g = topk_gate[(int64_t)t * k + slot];
         row_of_slot[(int64_t)t * k + slot] = r;
       } else {
-        g = probs_t[(int64_t)e * T + t] / ptop;   // pair added by token rounding
+        g = probs_t[(int64_t)e * T + t];          // pair added by token rounding
+        if (!gate_all) g /= ptop;
       }
       token_of_row[r] = t;
       expert_of_row[r] = e;
@@ -396,6 +434,102 @@ __global__ __launch_bounds__(1024) void round_select_kernel(const float* __restr
   }
 }
 
+// Capacity: rows of expert e past its first C (rows are in token order) lose
+// their keep bit; the plan is rebuilt from the remaining bits.
+__global__ __launch_bounds__(256) void capacity_drop_kernel(const int32_t* __restrict__ offsets,
+                                                           const int32_t* __restrict__ token_of_row,
+                                                           const int32_t* __restrict__ expert_of_row, int E,
+                                                           int64_t nmax, int64_t C, uint32_t* __restrict__ keep_bits,
+                                                           int words) {
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (r >= nmax || r >= offsets[E]) return;
+  const int e = expert_of_row[r];
+  if (r - offsets[e] < C) return;
+  atomicAnd(keep_bits + (int64_t)token_of_row[r] * words + (e >> 5), ~(1u << (e & 31)));
+}
+
+// Router losses, pass 1: block b sums the full softmax P_t and lse_t^2 of its
+// 256 tokens (wave w: tokens 64w.., in order; then the four waves in order)
+// into part[b][0..E) and part[b][E].
+template <int V>
+__global__ __launch_bounds__(256) void router_loss_partial_kernel(const float* __restrict__ logits, int T, int E,
+                                                                 float* __restrict__ part) {
+  __shared__ float wp[4][257];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float ps[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) ps[v] = 0.0f;
+  float zs = 0.0f;
+  for (int i = 0; i < 64; ++i) {
+    const int t = blockIdx.x * 256 + wave * 64 + i;
+    if (t >= T) break;
+    float z[V];
+    float m = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int e = lane + 64 * v;
+      z[v] = e < E ? logits[(int64_t)t * E + e] : -INFINITY;
+      m = fmaxf(m, z[v]);
+    }
+    m = wave_max(m);
+    float sl = 0.0f;
+#pragma unroll
+    for (int v = 0; v < V; ++v) sl += (lane + 64 * v < E) ? expf(z[v] - m) : 0.0f;
+    const float s = wave_sum(sl);
+#pragma unroll
+    for (int v = 0; v < V; ++v)
+      if (lane + 64 * v < E) ps[v] += expf(z[v] - m) / s;
+    const float lse = m + logf(s);
+    zs += lse * lse;
+  }
+#pragma unroll
+  for (int v = 0; v < V; ++v)
+    if (lane + 64 * v < E) wp[wave][lane + 64 * v] = ps[v];
+  if (lane == 0) wp[wave][256] = zs;
+  __syncthreads();
+  const int e = threadIdx.x;
+  if (e < E) part[(int64_t)blockIdx.x * (E + 1) + e] = ((wp[0][e] + wp[1][e]) + wp[2][e]) + wp[3][e];
+  if (e == 0)
+    part[(int64_t)blockIdx.x * (E + 1) + E] = ((wp[0][256] + wp[1][256]) + wp[2][256]) + wp[3][256];
+}
+
+// Pass 2 (one block): Pbar, CV^2 = var / mean^2 (population variance over the E
+// entries), lb = lb_coef * CV^2, z-loss = z_coef * sum lse^2 / T; fixed order.
+__global__ __launch_bounds__(256) void router_loss_final_kernel(const float* __restrict__ part, int nb, int T, int E,
+                                                               float lb_coef, float z_coef,
+                                                               float* __restrict__ aux) {
+  __shared__ float red[256];
+  const int e = threadIdx.x;
+  float pb = 0.0f;
+  if (e < E) {
+    for (int b = 0; b < nb; ++b) pb += part[(int64_t)b * (E + 1) + e];
+    pb /= (float)T;
+    aux[4 + e] = pb;
+  }
+  red[e] = e < E ? pb : 0.0f;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (e < o) red[e] += red[e + o];
+    __syncthreads();
+  }
+  const float m = red[0] / (float)E;
+  __syncthreads();
+  red[e] = e < E ? (pb - m) * (pb - m) : 0.0f;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (e < o) red[e] += red[e + o];
+    __syncthreads();
+  }
+  if (e == 0) {
+    const float cv2 = (red[0] / (float)E) / (m * m);
+    float zs = 0.0f;
+    for (int b = 0; b < nb; ++b) zs += part[(int64_t)b * (E + 1) + E];
+    aux[0] = lb_coef * cv2;
+    aux[1] = z_coef * zs / (float)T;
+    aux[3] = cv2;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_topk(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, bool rounding,
@@ -408,7 +542,8 @@ hipError_t launch_topk(const moe_shape& s, const moe_plan& p, const PlanInternal
     auto kern = topk_kernel<V, R, R ? 16 : 1>;                                                                     \
     if (lds > 65536) hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
     hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, st, p.logits, s.T, s.E, s.k, p.topk_idx,      \
-                       p.topk_gate, p.keep_bits, pi.words, p.probs_t, pi.sel_t, wordsT);               \
+                       p.topk_gate, p.keep_bits, pi.words, p.probs_t, pi.sel_t, wordsT,                \
+                       (int)(s.gate_mode == MOE_GATE_ALL));                                             \
   } while (0)
   if (s.E <= 64) { if (rounding) MOE_TOPK(1, true); else MOE_TOPK(1, false); }
   else if (s.E <= 128) { if (rounding) MOE_TOPK(2, true); else MOE_TOPK(2, false); }
@@ -423,11 +558,33 @@ hipError_t launch_plan_build(const moe_shape& s, const moe_plan& p, const PlanIn
   hipLaunchKernelGGL(plan_count_kernel, dim3(pi.nblk), dim3(256), lds, st, p.keep_bits, s.T, s.E, pi.words,
                      pi.nblk, pi.hist, pi.blk_tok);
   hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, st, s.E, pi.nblk, pi.hist, pi.blk_tok, p.counts,
-                     raw ? p.counts_raw : nullptr, p.offsets, pi.prefix128, pi.tile_e128);
+                     raw ? p.counts_raw : nullptr, p.offsets, pi.prefix128, pi.tile_e128, raw ? p.aux : nullptr);
   hipLaunchKernelGGL(plan_scatter_kernel, dim3(pi.nblk), dim3(256), lds, st, p.keep_bits, s.T, s.E, s.k,
                      pi.words, pi.nblk, pi.hist, pi.blk_tok, p.topk_idx, p.topk_gate, p.probs_t,
-                     with_prob_gates, p.token_of_row, p.expert_of_row, p.gate_of_row, p.row_of_slot, p.tok_ptr,
+                     with_prob_gates, s.gate_mode == MOE_GATE_ALL, p.token_of_row, p.expert_of_row, p.gate_of_row, p.row_of_slot, p.tok_ptr,
                      p.tok_rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_capacity_drop(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, hipStream_t st) {
+  const int64_t nmax = max_rows(s);
+  const double c = std::ceil((double)s.capacity_factor * (double)s.T * (double)s.k / (double)s.E);
+  const int64_t C = c > 9.0e18 ? INT64_MAX : (int64_t)c;
+  hipLaunchKernelGGL(capacity_drop_kernel, dim3(ceil_div(nmax, 256)), dim3(256), 0, st, p.offsets, p.token_of_row,
+                     p.expert_of_row, s.E, nmax, C, p.keep_bits, pi.words);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_losses(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, hipStream_t st) {
+  const int nb = ceil_div(s.T, 256);
+  if (s.E <= 64)
+    hipLaunchKernelGGL(router_loss_partial_kernel<1>, dim3(nb), dim3(256), 0, st, p.logits, s.T, s.E, pi.loss_part);
+  else if (s.E <= 128)
+    hipLaunchKernelGGL(router_loss_partial_kernel<2>, dim3(nb), dim3(256), 0, st, p.logits, s.T, s.E, pi.loss_part);
+  else
+    hipLaunchKernelGGL(router_loss_partial_kernel<4>, dim3(nb), dim3(256), 0, st, p.logits, s.T, s.E, pi.loss_part);
+  hipLaunchKernelGGL(router_loss_final_kernel, dim3(1), dim3(256), 0, st, pi.loss_part, nb, s.T, s.E, s.lb_coef,
+                     s.z_coef, p.aux);
   return hipGetLastError();
 }
 

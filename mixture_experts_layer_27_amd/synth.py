@@ -69,6 +69,10 @@ def generate(cfg: MoEConfig, seed: int | None = None, with_dout: bool | None = N
     out["w2"] = w2
     if with_dout:
         out["dout"] = _cast(rng.standard_normal((cfg.T, cfg.d), dtype=f32), cfg.act)
+    if cfg.noise_std > 0:
+        # routing noise from a stream of its own (the other inputs do not move)
+        nrng = np.random.default_rng([seed, 2])
+        out["noise"] = torch.from_numpy(nrng.standard_normal((cfg.T, cfg.E), dtype=f32) * f32(cfg.noise_std))
     return out
 
 

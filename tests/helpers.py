@@ -33,7 +33,28 @@ CASES = {
     "mx_ragged_d": configs.FINE_MX.scaled("mx_ragged_d", T=700, d=192, E=8, k=2, f=384),
     "mx_zipf_small": configs.FINE_ZIPF.scaled("mx_zipf_small", T=1500, d=256, E=32, f=256, gemm="mxfp8"),
     "mx_one_token": configs.FINE_MX.scaled("mx_one_token", T=1, d=128, E=8, k=2, f=128),
+    # routing variants: full-softmax gates, routing noise, load-balance and z-losses
+    # (dense router gradient), capacity factor (drops past each expert's capacity)
+    "var_all_lb_z_noise": configs.FINE.scaled("var_all_lb_z_noise", T=1500, d=256, E=32, f=256, gate="all",
+                                              lb_coef=0.5, z_coef=0.01, noise_std=0.3),
+    "var_topk_lb": configs.FINE.scaled("var_topk_lb", T=1000, d=256, E=16, f=256, lb_coef=2.0),
+    "var_capacity_z": configs.FINE_ZIPF.scaled("var_capacity_z", T=1500, d=256, E=32, f=256,
+                                               capacity_factor=1.0, z_coef=0.02),
+    "var_capacity_all": configs.SPARSE.scaled("var_capacity_all", T=1200, d=512, E=64, f=128, gate="all",
+                                              capacity_factor=0.75),
+    "var_round_all": configs.SPARSE_ROUND.scaled("var_round_all", T=1200, d=512, E=64, f=128, gate="all"),
+    "var_mx_all_lb": configs.FINE_MX.scaled("var_mx_all_lb", T=1500, d=256, E=32, f=256, gate="all",
+                                            lb_coef=1.0),
+    "var_fp32_all_z_noise": configs.TINY.scaled("var_fp32_all_z_noise", gate="all", z_coef=0.05, lb_coef=0.3,
+                                                noise_std=0.5),
 }
+
+
+def route_opts(cfg):
+    """The oracle's routing options for a config (float32 values, as the C ABI holds them)."""
+    f32 = lambda v: float(np.float32(v))
+    return mo.RouteOpts(gate=cfg.gate, capacity_factor=f32(cfg.capacity_factor), lb_coef=f32(cfg.lb_coef),
+                        z_coef=f32(cfg.z_coef))
 
 
 def make_inputs(cfg):
@@ -42,7 +63,8 @@ def make_inputs(cfg):
     def redraw(x, rows, attempt):
         return synth.redraw_rows(cfg, x, rows, attempt)
 
-    g["x"], _ = clear_ties(g["x"], g["w_gate"], g.get("bias"), cfg.k, redraw, round_tile=cfg.round_tile)
+    g["x"], _ = clear_ties(g["x"], g["w_gate"], g.get("bias"), cfg.k, redraw, round_tile=cfg.round_tile,
+                           noise=g.get("noise"))
     return g
 
 
@@ -63,7 +85,8 @@ def tol(cfg):
 def oracle_run(cfg, g):
     f = lambda t: None if t is None else t.double().numpy()
     return mo.layer(f(g["x"]), f(g["w_gate"]), f(g.get("bias")), f(g["w1"]), f(g["w2"]), cfg.k,
-                    dout=f(g.get("dout")), round_tile=cfg.round_tile, prec=precision(cfg))
+                    dout=f(g.get("dout")), round_tile=cfg.round_tile, prec=precision(cfg),
+                    opts=route_opts(cfg), noise=f(g.get("noise")))
 
 
 def close(got, ref, atol=2e-2, rfrob=1e-2):

@@ -49,6 +49,8 @@ def test_sizes_and_status_strings(b):
 @pytest.mark.parametrize("kw,code", [
     (dict(T=0), 1), (dict(k=9, E=16), 2), (dict(k=5, E=4), 1), (dict(E=300), 2), (dict(d=100), 2),
     (dict(d_ff=96), 2), (dict(act=7), 1), (dict(round_tile=3), 1), (dict(T=(1 << 20) + 1), 2),
+    (dict(gate_mode=2), 1), (dict(capacity_factor=-1.0), 1), (dict(lb_coef=float("nan")), 1),
+    (dict(z_coef=float("inf")), 1), (dict(capacity_factor=1.0, round_tile=128), 2),
 ])
 def test_shape_validation(b, kw, code):
     base = dict(T=64, d=128, E=8, k=2, d_ff=128, act=b.MOE_BF16, gemm=None, round_tile=0)
@@ -69,7 +71,7 @@ def test_argument_errors_return_before_launch(b):
     assert b._lib.moe_plan_init(ctypes.byref(s), ctypes.c_void_p((1 << 20) + 8), 1 << 30, ctypes.byref(plan)) == 1
     assert b._lib.moe_plan_init(ctypes.byref(s), fake, 1 << 30, ctypes.byref(plan)) == 0
     # null inputs, misaligned pointers, missing workspace: rejected on the host
-    assert b._lib.moe_route(ctypes.byref(s), None, fake, None, ctypes.byref(plan), None, 0, None) == 1
+    assert b._lib.moe_route(ctypes.byref(s), None, fake, None, None, ctypes.byref(plan), None, 0, None) == 1
     assert b._lib.moe_permute(ctypes.byref(s), ctypes.c_void_p((1 << 20) + 4), ctypes.byref(plan), fake, None) == 1
     assert b._lib.moe_grouped_gemm_swiglu(ctypes.byref(s), fake, fake, fake, ctypes.byref(plan), fake, fake,
                                           fake, 0, None) == 3

@@ -53,6 +53,14 @@ def test_routing_bit_exact(name):
     np.testing.assert_allclose(a["topk_gate"].double().numpy(), plan.topk_gate, rtol=0, atol=2e-6)
     np.testing.assert_allclose(a["gate_of_row"][:N].double().numpy(), plan.gate_of_row, rtol=0, atol=2e-6)
     assert_close("logits", a["logits"].numpy(), ref["logits"], atol=1e-4, rfrob=1e-5)
+    # router loss terms: the count monitor always, the losses when they are on
+    aux = a["aux"].double().numpy()
+    assert abs(aux[2] - ref["count_mse"]) <= 1e-5 * max(1.0, ref["count_mse"])
+    if cfg.lb_coef or cfg.z_coef:
+        np.testing.assert_allclose(aux[4:], ref["pbar"], rtol=0, atol=1e-6)
+        assert abs(aux[3] - ref["cv2"]) <= 1e-4 * ref["cv2"] + 1e-7
+        assert abs(aux[0] - ref["lb"]) <= 1e-4 * ref["lb"] + 1e-7
+        assert abs(aux[1] - ref["zloss"]) <= 1e-5 * ref["zloss"] + 1e-7
 
 
 def _mx_w(run, key, axis):
@@ -172,3 +180,29 @@ def test_quantize_mx_columns_bit_exact():
     c_ref, s_ref, _ = mx.quantize(src.double().numpy(), axis=0)
     np.testing.assert_array_equal(codes.cpu().numpy(), c_ref.T)
     np.testing.assert_array_equal(scales.cpu().numpy(), s_ref.T)
+
+
+@pytest.mark.parametrize("name", [n for n in CASES if CASES[n].lb_coef or CASES[n].z_coef])
+def test_router_loss_gradients(name):
+    """With dout = 0 the only gradients are those of the load-balance and z-losses:
+    dlogits (the router backward's dense terms), dx (through the dense dz W_g
+    GEMM) and dW_g, checked relative to their own size (they are ~1e-5 of the
+    output-loss gradients, far below the parity bar of the other tests)."""
+    from mixture_experts_layer_27_amd import binding
+    cfg = CASES[name]
+    print(f"[parity] router losses case={name}", flush=True)
+    g = make_inputs(cfg)
+    g["dout"] = torch.zeros_like(g["dout"])
+    run = binding.LayerRun(cfg, g)
+    run.forward()
+    run.backward()
+    torch.cuda.synchronize()
+    ref = oracle_run(cfg, g)
+    for key, got, bar in (("dlogits", run.dlogits, 1e-3), ("dx", run.dx, 2e-2), ("dw_gate", run.dw_gate, 1e-2)):
+        got = got.double().cpu().numpy()
+        r = ref[key]
+        scale = float(np.abs(r).max())
+        assert scale > 0, key
+        err = float(np.abs(got - r).max()) / scale
+        rf = float(np.linalg.norm(got - r) / np.linalg.norm(r))
+        assert err < bar and rf < bar / 2, f"{key}: max-abs/max {err:.3e}, rel-Frobenius {rf:.3e} (bar {bar})"
