@@ -87,8 +87,14 @@ SPARSE = MoEConfig("sparse_e256", T=32768, d=4096, E=256, k=8, f=512,
                    wg_std=1.0 / 64.0, bias="normal", b_std=0.5)
 SPARSE_ROUND = dataclasses.replace(SPARSE, name="sparse_e256_round", round_tile=128)
 FINE_MX = dataclasses.replace(FINE, name="fine_e128_mxfp8", gemm="mxfp8")
+# routing variants at the fine_e128 shape: full-softmax gates, noisy top-k and both
+# router losses (dense router gradient); a capacity factor on the Zipf-imbalanced routing
+FINE_LOSSES = dataclasses.replace(FINE, name="fine_e128_router_losses", gate="all", lb_coef=0.01, z_coef=0.001,
+                                  noise_std=1.0)
+FINE_CAPACITY = dataclasses.replace(FINE_ZIPF, name="fine_e128_zipf_capacity", capacity_factor=1.25)
 
-CONFIGS = {c.name: c for c in (TINY, COARSE, FINE, FINE_ZIPF, SPARSE, SPARSE_ROUND, FINE_MX)}
+CONFIGS = {c.name: c for c in (TINY, COARSE, FINE, FINE_ZIPF, SPARSE, SPARSE_ROUND, FINE_MX, FINE_LOSSES,
+                               FINE_CAPACITY)}
 
 
 def get(name: str) -> MoEConfig:

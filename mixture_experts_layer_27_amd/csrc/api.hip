@@ -58,7 +58,7 @@ void carve_plan(const moe_shape& s, char* base, moe_plan* p, size_t* total) {
   c.take<int32_t>(E * nblk_of(s) * 4);
   c.take<int32_t>((nblk_of(s) + 1) * 4);
   if (s.round_tile) c.take<uint32_t>(E * ((T + 31) / 32) * 4);
-  c.take<float>((size_t)nblk_of(s) * (E + 1) * 4);   // router-loss partials
+  c.take<float>((size_t)((T + kLossTokens - 1) / kLossTokens) * (E + 1) * 4);   // router-loss partials
   if (p) *p = q;
   if (total) *total = c.off;
 }

@@ -8,6 +8,7 @@
 namespace moe {
 
 constexpr int kPlanBlock = 256;     // tokens per block in the plan kernels
+constexpr int kLossTokens = 64;     // tokens per block of the router-loss partial sums
 constexpr int kBmSmall = 128;       // m-tile of the fp32 grouped GEMMs
 constexpr int kBmLarge = 256;       // m-tile of the bf16 grouped GEMMs
 
@@ -23,7 +24,7 @@ struct PlanInternal {
   int32_t* hist;
   int32_t* blk_tok;
   uint32_t* sel_t;
-  float* loss_part;   // [nblk][E+1] router-loss partial sums
+  float* loss_part;   // [ceil(T/kLossTokens)][E+1] router-loss partial sums
   int nblk;
   int words;   // ceil(E/32)
 };

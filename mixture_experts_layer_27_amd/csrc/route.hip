@@ -449,8 +449,8 @@ __global__ __launch_bounds__(256) void capacity_drop_kernel(const int32_t* __res
 }
 
 // Router losses, pass 1: block b sums the full softmax P_t and lse_t^2 of its
-// 256 tokens (wave w: tokens 64w.., in order; then the four waves in order)
-// into part[b][0..E) and part[b][E].
+// kLossTokens tokens (wave w: 16 consecutive tokens in order; then the four
+// waves in order) into part[b][0..E) and part[b][E].
 template <int V>
 __global__ __launch_bounds__(256) void router_loss_partial_kernel(const float* __restrict__ logits, int T, int E,
                                                                  float* __restrict__ part) {
@@ -460,8 +460,8 @@ __global__ __launch_bounds__(256) void router_loss_partial_kernel(const float* _
 #pragma unroll
   for (int v = 0; v < V; ++v) ps[v] = 0.0f;
   float zs = 0.0f;
-  for (int i = 0; i < 64; ++i) {
-    const int t = blockIdx.x * 256 + wave * 64 + i;
+  for (int i = 0; i < kLossTokens / 4; ++i) {
+    const int t = blockIdx.x * kLossTokens + wave * (kLossTokens / 4) + i;
     if (t >= T) break;
     float z[V];
     float m = -INFINITY;
@@ -493,17 +493,35 @@ __global__ __launch_bounds__(256) void router_loss_partial_kernel(const float* _
     part[(int64_t)blockIdx.x * (E + 1) + E] = ((wp[0][256] + wp[1][256]) + wp[2][256]) + wp[3][256];
 }
 
-// Pass 2 (one block): Pbar, CV^2 = var / mean^2 (population variance over the E
-// entries), lb = lb_coef * CV^2, z-loss = z_coef * sum lse^2 / T; fixed order.
-__global__ __launch_bounds__(256) void router_loss_final_kernel(const float* __restrict__ part, int nb, int T, int E,
-                                                               float lb_coef, float z_coef,
-                                                               float* __restrict__ aux) {
+// Pass 2 (one block of 1024): Pbar, CV^2 = var / mean^2 (population variance
+// over the E entries), lb = lb_coef * CV^2, z-loss = z_coef * sum lse^2 / T.
+// Column e (E = the lse^2 column) is summed by four threads over the blocks
+// b = q mod 4, then the four sums in order: a fixed order.
+__global__ __launch_bounds__(1024) void router_loss_final_kernel(const float* __restrict__ part, int nb, int T, int E,
+                                                                float lb_coef, float z_coef,
+                                                                float* __restrict__ aux) {
+  __shared__ float q4[4][257];
   __shared__ float red[256];
+  {
+    const int c = threadIdx.x & 255, q = threadIdx.x >> 8;
+    float acc = 0.0f;
+    if (c <= E) {
+#pragma unroll 8
+      for (int b = q; b < nb; b += 4) acc += part[(int64_t)b * (E + 1) + c];
+    }
+    q4[q][c] = acc;
+    if (c == 255 && E == 256) {   // the lse^2 column of E = 256 sits at c = 256
+      float az = 0.0f;
+      for (int b = q; b < nb; b += 4) az += part[(int64_t)b * (E + 1) + 256];
+      q4[q][256] = az;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x >= 256) return;
   const int e = threadIdx.x;
   float pb = 0.0f;
   if (e < E) {
-    for (int b = 0; b < nb; ++b) pb += part[(int64_t)b * (E + 1) + e];
-    pb /= (float)T;
+    pb = (((q4[0][e] + q4[1][e]) + q4[2][e]) + q4[3][e]) / (float)T;
     aux[4 + e] = pb;
   }
   red[e] = e < E ? pb : 0.0f;
@@ -522,8 +540,7 @@ __global__ __launch_bounds__(256) void router_loss_final_kernel(const float* __r
   }
   if (e == 0) {
     const float cv2 = (red[0] / (float)E) / (m * m);
-    float zs = 0.0f;
-    for (int b = 0; b < nb; ++b) zs += part[(int64_t)b * (E + 1) + E];
+    const float zs = ((q4[0][E] + q4[1][E]) + q4[2][E]) + q4[3][E];
     aux[0] = lb_coef * cv2;
     aux[1] = z_coef * zs / (float)T;
     aux[3] = cv2;
@@ -576,14 +593,14 @@ hipError_t launch_capacity_drop(const moe_shape& s, const moe_plan& p, const Pla
 }
 
 hipError_t launch_router_losses(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, hipStream_t st) {
-  const int nb = ceil_div(s.T, 256);
+  const int nb = ceil_div(s.T, kLossTokens);
   if (s.E <= 64)
     hipLaunchKernelGGL(router_loss_partial_kernel<1>, dim3(nb), dim3(256), 0, st, p.logits, s.T, s.E, pi.loss_part);
   else if (s.E <= 128)
     hipLaunchKernelGGL(router_loss_partial_kernel<2>, dim3(nb), dim3(256), 0, st, p.logits, s.T, s.E, pi.loss_part);
   else
     hipLaunchKernelGGL(router_loss_partial_kernel<4>, dim3(nb), dim3(256), 0, st, p.logits, s.T, s.E, pi.loss_part);
-  hipLaunchKernelGGL(router_loss_final_kernel, dim3(1), dim3(256), 0, st, pi.loss_part, nb, s.T, s.E, s.lb_coef,
+  hipLaunchKernelGGL(router_loss_final_kernel, dim3(1), dim3(1024), 0, st, pi.loss_part, nb, s.T, s.E, s.lb_coef,
                      s.z_coef, p.aux);
   return hipGetLastError();
 }
