@@ -47,6 +47,14 @@ CASES = {
                                             lb_coef=1.0),
     "var_fp32_all_z_noise": configs.TINY.scaled("var_fp32_all_z_noise", gate="all", z_coef=0.05, lb_coef=0.3,
                                                 noise_std=0.5),
+    # degenerate cases: one token under a capacity of one pair per expert, one expert
+    # (all gates 1 under "all", CV^2 = 0), E = 256 with k = 8 and every variant
+    "var_one_token_capacity": configs.FINE.scaled("var_one_token_capacity", T=1, d=128, E=8, k=2, f=128,
+                                                  capacity_factor=0.5, z_coef=0.1),
+    "var_single_expert_all": configs.FINE.scaled("var_single_expert_all", T=300, d=128, E=1, k=1, f=128,
+                                                 gate="all", lb_coef=1.0, z_coef=0.1),
+    "var_max_E_k_all": configs.FINE.scaled("var_max_E_k_all", T=300, d=128, E=256, k=8, f=128, gate="all",
+                                           capacity_factor=1.0, lb_coef=0.5, z_coef=0.01, noise_std=0.2),
 }
 
 
