@@ -186,6 +186,18 @@ moe_status moe_grouped_gemm_swiglu(const moe_shape *s, const void *x_perm, const
                                    const void *w2, const moe_plan *plan, void *h_saved, void *y,
                                    void *ws, size_t ws_bytes, void *stream);
 
+/* The same expert FFN reading x [T,d] (act) directly: row r of every GEMM
+ * operand built from x is x[token_of_row[r]], fetched through the plan inside
+ * the GEMM's operand loads (with MXFP8: inside the quantiser pass), so no
+ * permuted copy is written or read (Olmo-core 3 article, "three splits"
+ * section: tokens go straight into the expert buffers; here the buffers are
+ * never materialised).  Results are bitwise identical to moe_permute followed
+ * by moe_grouped_gemm_swiglu.  Requires act == MOE_BF16 and T*d*2 < 2^31
+ * bytes, else MOE_ENOTSUP.  Same workspace as moe_grouped_gemm_swiglu. */
+moe_status moe_grouped_gemm_swiglu_gather(const moe_shape *s, const void *x, const void *w1,
+                                          const void *w2, const moe_plan *plan, void *h_saved, void *y,
+                                          void *ws, size_t ws_bytes, void *stream);
+
 /* Weighted combine: out[t] = sum over the rows of t (ascending) of
  * gate_of_row[r] * y[r], accumulated in float32.  y [N_max,d], out [T,d]. */
 moe_status moe_unpermute_combine(const moe_shape *s, const void *y, const moe_plan *plan,
@@ -194,7 +206,10 @@ moe_status moe_unpermute_combine(const moe_shape *s, const void *y, const moe_pl
 /* Backward for the loss sum_t <out_t, dout_t>.
  *   Inputs: x [T,d], w_gate [E,d], w1, w2, the plan, h_saved, dout [T,d];
  *   x_perm [N_max,d] (act) = what moe_permute wrote for x with this plan, or NULL
- *   (then x is permuted again into the workspace; the results are identical).
+ *   (then the GEMMs read the rows of x through plan.token_of_row, or with f32
+ *   activations or T*d*2 >= 2^31 bytes x is permuted into the workspace; the
+ *   results are identical).  dout is read the same way (bf16: through the
+ *   plan inside the GEMM loads; f32: permuted into the workspace).
  *   fwd_ws = the workspace of this step's moe_grouped_gemm_swiglu call (same
  *   shape, plan, x_perm, w1 and w2, unchanged since), or NULL.  With MXFP8 the
  *   backward then reads the transposed weight codes and x_perm's token-axis

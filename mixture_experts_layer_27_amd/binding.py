@@ -23,8 +23,8 @@ MOE_F32, MOE_BF16, MOE_MXFP8 = 0, 1, 2
 MOE_WS_ROUTE, MOE_WS_ROUND, MOE_WS_EXPERTS, MOE_WS_BACKWARD = 0, 1, 2, 3
 STATUS = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_ENOTSUP", 3: "MOE_EWORKSPACE", 4: "MOE_EHIP"}
 EXPORTS = ("moe_max_rows", "moe_plan_bytes", "moe_plan_init", "moe_workspace_bytes", "moe_route",
-           "moe_round_tokens", "moe_permute", "moe_grouped_gemm_swiglu", "moe_unpermute_combine",
-           "moe_backward", "moe_quantize_mx", "moe_status_str")
+           "moe_round_tokens", "moe_permute", "moe_grouped_gemm_swiglu", "moe_grouped_gemm_swiglu_gather",
+           "moe_unpermute_combine", "moe_backward", "moe_quantize_mx", "moe_status_str")
 
 
 class MoeShape(ctypes.Structure):
@@ -54,6 +54,7 @@ for name, res, args in [
     ("moe_round_tokens", ctypes.c_int, [_P_SHAPE, _P_PLAN, _vp, _sz, _vp]),
     ("moe_permute", ctypes.c_int, [_P_SHAPE, _vp, _P_PLAN, _vp, _vp]),
     ("moe_grouped_gemm_swiglu", ctypes.c_int, [_P_SHAPE, _vp, _vp, _vp, _P_PLAN, _vp, _vp, _vp, _sz, _vp]),
+    ("moe_grouped_gemm_swiglu_gather", ctypes.c_int, [_P_SHAPE, _vp, _vp, _vp, _P_PLAN, _vp, _vp, _vp, _sz, _vp]),
     ("moe_unpermute_combine", ctypes.c_int, [_P_SHAPE, _vp, _P_PLAN, _vp, _vp]),
     ("moe_backward", ctypes.c_int, [_P_SHAPE, _vp, _vp, _vp, _vp, _P_PLAN, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                     _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -195,6 +196,13 @@ def grouped_gemm_swiglu(s: MoeShape, x_perm, w1, w2, plan: Plan, h_saved, y, ws,
                                         _ptr(h_saved), _ptr(y), _ptr(ws), ws.numel(), _stream(stream)))
 
 
+def grouped_gemm_swiglu_gather(s: MoeShape, x, w1, w2, plan: Plan, h_saved, y, ws, stream=None):
+    """The expert FFN reading the rows of x through the plan (no permuted copy)."""
+    _check("moe_grouped_gemm_swiglu_gather",
+           _lib.moe_grouped_gemm_swiglu_gather(ctypes.byref(s), _ptr(x), _ptr(w1), _ptr(w2), ctypes.byref(plan.c),
+                                               _ptr(h_saved), _ptr(y), _ptr(ws), ws.numel(), _stream(stream)))
+
+
 def unpermute_combine(s: MoeShape, y, plan: Plan, out, stream=None):
     _check("moe_unpermute_combine", _lib.moe_unpermute_combine(ctypes.byref(s), _ptr(y), ctypes.byref(plan.c),
                                                                _ptr(out), _stream(stream)))
@@ -223,10 +231,13 @@ class LayerRun:
     """Device buffers for one layer problem and the call sequence of a training step.
 
     ``forward()`` = route [+ round] + permute + grouped GEMMs + combine;
-    ``backward()`` = the backward entry point.  Inputs must already be on the device."""
+    ``backward()`` = the backward entry point.  Inputs must already be on the device.
+    ``fused_gather``: the forward reads x through the plan inside the expert GEMMs
+    (no x_perm) and the backward gathers x and dout the same way."""
 
-    def __init__(self, cfg: MoEConfig, inputs: Dict[str, torch.Tensor], device="cuda"):
+    def __init__(self, cfg: MoEConfig, inputs: Dict[str, torch.Tensor], device="cuda", fused_gather=False):
         self.cfg = cfg
+        self.fused_gather = bool(fused_gather)
         self.s = shape_of(cfg)
         s = self.s
         dt = torch.bfloat16 if cfg.act == "bf16" else torch.float32
@@ -256,11 +267,19 @@ class LayerRun:
 
     def forward(self, stream=None):
         self.route(stream)
-        permute(self.s, self.inp["x"], self.plan, self.x_perm, stream)
-        grouped_gemm_swiglu(self.s, self.x_perm, self.inp["w1"], self.inp["w2"], self.plan, self.h, self.y,
-                            self.ws_fwd, stream)
+        self.experts(stream)
         unpermute_combine(self.s, self.y, self.plan, self.out, stream)
         return self.out
+
+    def experts(self, stream=None):
+        """Permute + expert FFN, or (fused_gather) the expert FFN reading x through the plan."""
+        if self.fused_gather:
+            grouped_gemm_swiglu_gather(self.s, self.inp["x"], self.inp["w1"], self.inp["w2"], self.plan, self.h,
+                                       self.y, self.ws_fwd, stream)
+        else:
+            permute(self.s, self.inp["x"], self.plan, self.x_perm, stream)
+            grouped_gemm_swiglu(self.s, self.x_perm, self.inp["w1"], self.inp["w2"], self.plan, self.h, self.y,
+                                self.ws_fwd, stream)
 
     def backward(self, stream=None, with_optional=True, reuse_x_perm=True, reuse_fwd_ws=True):
         """reuse_x_perm: hand the forward's permuted x to the backward (else it permutes x again);
@@ -269,7 +288,8 @@ class LayerRun:
         backward(self.s, self.inp["x"], self.inp["w_gate"], self.inp["w1"], self.inp["w2"], self.plan, self.h,
                  self.inp["dout"], self.dx, self.dw_gate, self.dw1, self.dw2, self.ws_bwd,
                  self.dlogits if with_optional else None, self.ds if with_optional else None, stream,
-                 self.x_perm if reuse_x_perm else None, self.ws_fwd if reuse_fwd_ws else None)
+                 self.x_perm if (reuse_x_perm and not self.fused_gather) else None,
+                 self.ws_fwd if reuse_fwd_ws else None)
 
     def step(self, stream=None):
         self.forward(stream)

@@ -87,6 +87,13 @@ moe_status check_shape(const moe_shape* s) {
 }
 
 bool aligned(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// Row gathers fused into the GEMM / quantiser loads: bf16 activations (the fp32
+// weight-gradient kernel has no gathered loads) whose [T, d] tensors fit the
+// 32-bit offsets of one buffer resource.
+bool gather_ok(const moe_shape& s) {
+  return s.act == MOE_BF16 && (int64_t)s.T * s.d * 2 < ((int64_t)1 << 31);
+}
 bool aligned_or_null(const void* p) { return !p || (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
 moe_status check_plan(const moe_shape& s, const moe_plan* p) {
@@ -141,7 +148,7 @@ size_t carve_bwd(const moe_shape& s, char* base, BwdWs* w) {
   Carver c{base};
   const int64_t N = max_rows(s);
   BwdWs q{};
-  q.do_perm = c.take<char>(N * s.d * esz(s));
+  q.do_perm = gather_ok(s) ? nullptr : c.take<char>(N * s.d * esz(s));   // dO is gathered inside the loads
   q.dh = c.take<char>(N * 2 * s.d_ff * esz(s));
   q.ga = c.take<char>(N * s.d_ff * esz(s));
   q.xbuf = c.take<char>(N * s.d * esz(s));
@@ -311,12 +318,15 @@ moe_status moe_permute(const moe_shape* s, const void* src, const moe_plan* plan
   return hip_status(launch_permute_rows(*s, src, *plan, dst, reinterpret_cast<hipStream_t>(stream)));
 }
 
-moe_status moe_grouped_gemm_swiglu(const moe_shape* s, const void* x_perm, const void* w1, const void* w2,
-                                   const moe_plan* plan, void* h_saved, void* y, void* ws, size_t ws_bytes,
-                                   void* stream) {
+namespace {
+// The expert FFN of the forward.  rows = x_perm (gather == nullptr) or x read
+// through gather = token_of_row (the permutation fused into the operand loads).
+moe_status experts_forward(const moe_shape* s, const void* rows, const int32_t* gather, const void* w1,
+                           const void* w2, const moe_plan* plan, void* h_saved, void* y, void* ws, size_t ws_bytes,
+                           void* stream) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
-  if (!aligned(x_perm) || !aligned(w1) || !aligned(w2) || !aligned(h_saved) || !aligned(y)) return MOE_EINVAL;
+  if (!aligned(rows) || !aligned(w1) || !aligned(w2) || !aligned(h_saved) || !aligned(y)) return MOE_EINVAL;
   if ((st = check_plan(*s, plan)) != MOE_OK) return st;
   if (!aligned(ws) || ws_bytes < experts_ws(*s)) return MOE_EWORKSPACE;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
@@ -331,16 +341,33 @@ moe_status moe_grouped_gemm_swiglu(const moe_shape* s, const void* x_perm, const
     const int E = s->E, d = s->d, f = s->d_ff;
     const int32_t* off = plan->offsets;
     e = mx_pad_offsets(off, E, w.pad_off, hs);
-    if (e == hipSuccess) e = mx_quantize_dual(x_perm, 1, 0, d, off, w.pad_off, E, P, w.x, w.x_t, hs);
+    if (e == hipSuccess) e = mx_quantize_dual(rows, 1, 0, d, off, w.pad_off, E, P, w.x, w.x_t, hs, gather);
     if (e == hipSuccess) e = mx_quantize_dual(w1, E, 2 * f, d, nullptr, nullptr, 0, 0, w.w1, w.w1t, hs);
     if (e == hipSuccess) e = gemm_mx_up_swiglu(*s, *plan, pi, w.x, w.w1, h_saved, w.a, hs);
     if (e == hipSuccess) e = mx_quantize_dual(w2, E, d, f, nullptr, nullptr, 0, 0, w.w2, w.w2t, hs);
     if (e == hipSuccess) e = gemm_mx_down(*s, *plan, pi, w.a, w.w2, y, hs);
     return hip_status(e);
   }
-  e = gemm_up_swiglu(*s, *plan, pi, x_perm, w1, h_saved, w.act, hs);
+  e = gemm_up_swiglu(*s, *plan, pi, rows, gather, w1, h_saved, w.act, hs);
   if (e == hipSuccess) e = gemm_down(*s, *plan, pi, w.act, w2, y, hs);
   return hip_status(e);
+}
+}  // namespace
+
+moe_status moe_grouped_gemm_swiglu(const moe_shape* s, const void* x_perm, const void* w1, const void* w2,
+                                   const moe_plan* plan, void* h_saved, void* y, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  return experts_forward(s, x_perm, nullptr, w1, w2, plan, h_saved, y, ws, ws_bytes, stream);
+}
+
+moe_status moe_grouped_gemm_swiglu_gather(const moe_shape* s, const void* x, const void* w1, const void* w2,
+                                          const moe_plan* plan, void* h_saved, void* y, void* ws, size_t ws_bytes,
+                                          void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!gather_ok(*s)) return MOE_ENOTSUP;
+  if ((st = check_plan(*s, plan)) != MOE_OK) return st;
+  return experts_forward(s, x, plan->token_of_row, w1, w2, plan, h_saved, y, ws, ws_bytes, stream);
 }
 
 moe_status moe_unpermute_combine(const moe_shape* s, const void* y, const moe_plan* plan, void* out, void* stream) {
@@ -371,7 +398,13 @@ moe_status moe_backward(const moe_shape* s, const void* x, const void* w_gate, c
   carve_bwd(*s, reinterpret_cast<char*>(ws), &w);
   float* dz = dlogits ? dlogits : w.dlogits;
   const int ldz = ldz_of(*s);
-  hipError_t e = launch_permute_rows(*s, dout, *plan, w.do_perm, hs);
+  // dO (and x, when x_perm is not given) reach the GEMMs through token_of_row
+  // inside their operand loads when the kernels allow it, else as permuted copies
+  const bool fused = gather_ok(*s);
+  const int32_t* tor = plan->token_of_row;
+  hipError_t e = fused ? hipSuccess : launch_permute_rows(*s, dout, *plan, w.do_perm, hs);
+  const void* dO = fused ? dout : w.do_perm;
+  const int32_t* dOg = fused ? tor : nullptr;
   if (s->gemm == MOE_MXFP8) {
     const int64_t P = tok_cap(*s);
     const int E = s->E, d = s->d, f = s->d_ff;
@@ -384,15 +417,16 @@ moe_status moe_backward(const moe_shape* s, const void* x, const void* w_gate, c
     const MxOperand& w2t = fwd_ws ? fw.w2t : w.w2t;
     const MxOperand& x_t = fwd_ws ? fw.x_t : w.x_t;
     if (e == hipSuccess) e = mx_pad_offsets(off, E, w.pad_off, hs);
-    if (e == hipSuccess) e = mx_quantize_dual(w.do_perm, 1, 0, d, off, w.pad_off, E, P, w.doq, w.do_t, hs);
+    if (e == hipSuccess) e = mx_quantize_dual(dO, 1, 0, d, off, w.pad_off, E, P, w.doq, w.do_t, hs, dOg);
     if (e == hipSuccess && !fwd_ws) e = mx_quantize_cols(w2, E, d, f, w.w2t.codes, w.w2t.scales, hs);
     if (e == hipSuccess) e = gemm_mx_dact(*s, *plan, pi, w.doq, w2t, h_saved, w.dh, w.dhq, w.ga, w.ds_part, hs);
     if (e == hipSuccess && !fwd_ws) e = mx_quantize_cols(w1, E, 2 * f, d, w.w1t.codes, w.w1t.scales, hs);
-    if (e == hipSuccess && !x_perm && !fwd_ws) e = launch_permute_rows(*s, x, *plan, w.xbuf, hs);
-    const void* xp = x_perm ? x_perm : w.xbuf;
+    if (e == hipSuccess && !x_perm && !fwd_ws && !fused) e = launch_permute_rows(*s, x, *plan, w.xbuf, hs);
+    const void* xp = x_perm ? x_perm : fused ? x : w.xbuf;
+    const int32_t* xg = (!x_perm && fused) ? tor : nullptr;
     if (e == hipSuccess) e = mx_quantize_tokens(w.dh, 2 * f, plan->offsets, w.pad_off, E, P, w.dh_t.codes, w.dh_t.scales, hs);
     if (e == hipSuccess && !fwd_ws)
-      e = mx_quantize_tokens(xp, d, plan->offsets, w.pad_off, E, P, w.x_t.codes, w.x_t.scales, hs);
+      e = mx_quantize_tokens(xp, d, plan->offsets, w.pad_off, E, P, w.x_t.codes, w.x_t.scales, hs, xg);
     if (e == hipSuccess) e = mx_quantize_tokens(w.ga, f, plan->offsets, w.pad_off, E, P, w.ga_t.codes, w.ga_t.scales, hs);
     if (e == hipSuccess) e = launch_wgrad_chunks(w.pad_off, E, w.wg.kch, w.wg, hs);
     if (e == hipSuccess) e = gemm_mx_wgrad(*s, w.wg, P, w.dh_t, 2 * f, x_t, d, dw1, hs);
@@ -401,13 +435,14 @@ moe_status moe_backward(const moe_shape* s, const void* x, const void* w_gate, c
     if (e == hipSuccess) e = launch_wgrad_reduce(w.wg, E, (int64_t)d * f, dw2, hs);
     if (e == hipSuccess) e = gemm_mx_dx_perm(*s, *plan, pi, w.dhq, w1t, w.xbuf, hs);   // dx_perm (x_perm no longer needed)
   } else {
-    if (e == hipSuccess) e = gemm_dact(*s, *plan, pi, w.do_perm, w2, h_saved, w.dh, w.ga, w.ds_part, hs);
-    if (e == hipSuccess && !x_perm) e = launch_permute_rows(*s, x, *plan, w.xbuf, hs);
-    const void* xp = x_perm ? x_perm : w.xbuf;
+    if (e == hipSuccess) e = gemm_dact(*s, *plan, pi, dO, dOg, w2, h_saved, w.dh, w.ga, w.ds_part, hs);
+    if (e == hipSuccess && !x_perm && !fused) e = launch_permute_rows(*s, x, *plan, w.xbuf, hs);
+    const void* xp = x_perm ? x_perm : fused ? x : w.xbuf;
+    const int32_t* xg = (!x_perm && fused) ? tor : nullptr;
     if (e == hipSuccess) e = launch_wgrad_chunks(plan->offsets, s->E, w.wg.kch, w.wg, hs);
-    if (e == hipSuccess) e = gemm_dw1(*s, w.wg, w.dh, xp, dw1, hs);
+    if (e == hipSuccess) e = gemm_dw1(*s, w.wg, w.dh, xp, xg, dw1, hs);
     if (e == hipSuccess) e = launch_wgrad_reduce(w.wg, s->E, (int64_t)2 * s->d_ff * s->d, dw1, hs);
-    if (e == hipSuccess) e = gemm_dw2(*s, w.wg, w.do_perm, w.ga, dw2, hs);
+    if (e == hipSuccess) e = gemm_dw2(*s, w.wg, dO, dOg, w.ga, dw2, hs);
     if (e == hipSuccess) e = launch_wgrad_reduce(w.wg, s->E, (int64_t)s->d * s->d_ff, dw2, hs);
     if (e == hipSuccess) e = gemm_dx_perm(*s, *plan, pi, w.dh, w1, w.xbuf, hs);   // dx_perm (x_perm no longer needed)
   }

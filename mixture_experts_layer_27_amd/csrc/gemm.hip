@@ -48,9 +48,9 @@ hipError_t run_dma(const Args& a, int64_t logical_tiles, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <bool AKC, bool BKC, int GROUP, int EPI>
+template <bool AKC, bool BKC, int GROUP, int EPI, int GATHER = 0>
 hipError_t run_big(const Args& a, int64_t logical_tiles, hipStream_t st) {
-  auto kern = grouped_gemm_big<AKC, BKC, GROUP, EPI>;
+  auto kern = grouped_gemm_big<AKC, BKC, GROUP, EPI, GATHER>;
   const size_t lds = big_lds_bytes(GROUP == GROUP_M);   // GROUP_M may run 128 x 512 tiles
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
@@ -76,10 +76,12 @@ int64_t grouped_m_tiles(const moe_shape& s, int bm) { return (max_rows(s) + bm -
 
 // ---------------------------------------------------------------- forward
 
-hipError_t gemm_up_swiglu(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const void* x_perm,
-                          const void* w1, void* h, void* act, hipStream_t st) {
+// x_rows = x_perm, or (gather != nullptr) x [T, d] read through gather = token_of_row
+hipError_t gemm_up_swiglu(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const void* x_rows,
+                          const int32_t* gather, const void* w1, void* h, void* act, hipStream_t st) {
   Args a = base_args();
-  a.A = x_perm; a.lda = s.d;
+  a.A = x_rows; a.lda = s.d;
+  a.a_gather = gather; a.gather_rows = s.T;
   a.B = w1; a.ldb = s.d; a.b_estride = (int64_t)2 * s.d_ff * s.d;
   a.C = h; a.ldc = 2 * s.d_ff;
   a.C2 = act; a.ldc2 = s.d_ff;
@@ -87,8 +89,11 @@ hipError_t gemm_up_swiglu(const moe_shape& s, const moe_plan& p, const PlanInter
   a.N = 2 * s.d_ff; a.K = s.d; a.E = s.E; a.f = s.d_ff;
   if (s.act == MOE_BF16) {
     a.tile_prefix = pi.prefix128; a.tile_expert = pi.tile_e128;
-    if (use_big(a.K))
-      return run_big<true, true, GROUP_M, EPI_SWIGLU>(a, grouped_m_tiles(s, 128) * ceil_div(a.N, 512), st);
+    if (use_big(a.K)) {
+      const int64_t tiles = grouped_m_tiles(s, 128) * ceil_div(a.N, 512);
+      return gather ? run_big<true, true, GROUP_M, EPI_SWIGLU, 1>(a, tiles, st)
+                    : run_big<true, true, GROUP_M, EPI_SWIGLU>(a, tiles, st);
+    }
     a.tilesN = a.N / 256;
     return run_dma<128, 256, 2, 4, true, true, GROUP_M, EPI_SWIGLU, 3>(a, grouped_m_tiles(s, 128) * a.tilesN, st);
   }
@@ -128,10 +133,12 @@ int gemm_dact_parts(const moe_shape& s) {
   return ceil_div(s.d_ff, 256) * 4;
 }
 
-hipError_t gemm_dact(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const void* do_perm,
-                     const void* w2, const void* h, void* dh, void* ga, float* ds_part, hipStream_t st) {
+hipError_t gemm_dact(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const void* do_rows,
+                     const int32_t* gather, const void* w2, const void* h, void* dh, void* ga, float* ds_part,
+                     hipStream_t st) {
   Args a = base_args();
-  a.A = do_perm; a.lda = s.d;
+  a.A = do_rows; a.lda = s.d;
+  a.a_gather = gather; a.gather_rows = s.T;
   a.B = w2; a.ldb = s.d_ff; a.b_estride = (int64_t)s.d * s.d_ff;   // W2_e read as [K = d, N = f]
   a.C = dh; a.ldc = 2 * s.d_ff;
   a.C2 = ga; a.ldc2 = s.d_ff;
@@ -142,8 +149,11 @@ hipError_t gemm_dact(const moe_shape& s, const moe_plan& p, const PlanInternal& 
   a.N = s.d_ff; a.K = s.d; a.E = s.E; a.f = s.d_ff;
   if (s.act == MOE_BF16) {
     a.tile_prefix = pi.prefix128; a.tile_expert = pi.tile_e128;
-    if (use_big(a.K))
-      return run_big<true, false, GROUP_M, EPI_DSWIGLU>(a, grouped_m_tiles(s, 128) * ceil_div(a.N, 512), st);
+    if (use_big(a.K)) {
+      const int64_t tiles = grouped_m_tiles(s, 128) * ceil_div(a.N, 512);
+      return gather ? run_big<true, false, GROUP_M, EPI_DSWIGLU, 1>(a, tiles, st)
+                    : run_big<true, false, GROUP_M, EPI_DSWIGLU>(a, tiles, st);
+    }
     a.tilesN = ceil_div(a.N, 256);
     return run_dma<128, 256, 2, 4, true, false, GROUP_M, EPI_DSWIGLU, 3>(a, grouped_m_tiles(s, 128) * a.tilesN, st);
   }
@@ -180,28 +190,33 @@ hipError_t run_wgrad(const moe_shape& s, const WgradChunks& w, Args& a, hipStrea
   if (s.act == MOE_BF16) {
     a.tilesM = ceil_div(a.M, 256); a.tilesN = ceil_div(a.N, 256);
     const int64_t tiles = 8 * (int64_t)ceil_div(w.max_chunks, 8) * a.tilesM * a.tilesN;
+    if (a.a_gather) return run_big<false, false, GROUP_K, EPI_F32, 1>(a, tiles, st);
+    if (a.b_gather) return run_big<false, false, GROUP_K, EPI_F32, 2>(a, tiles, st);
     return run_big<false, false, GROUP_K, EPI_F32>(a, tiles, st);
   }
+  if (a.a_gather || a.b_gather) return hipErrorNotSupported;   // gathered k rows: bf16 kernels only
   a.tilesM = ceil_div(a.M, 128); a.tilesN = ceil_div(a.N, 128);
   const int64_t tiles = 8 * (int64_t)ceil_div(w.max_chunks, 8) * a.tilesM * a.tilesN;
   return run<float, 128, 128, 2, 2, false, false, GROUP_K, EPI_F32>(a, tiles, st);
 }
 }  // namespace
 
-hipError_t gemm_dw1(const moe_shape& s, const WgradChunks& w, const void* dh, const void* x_perm, float* dw1,
-                    hipStream_t st) {
+hipError_t gemm_dw1(const moe_shape& s, const WgradChunks& w, const void* dh, const void* x_rows,
+                    const int32_t* gather, float* dw1, hipStream_t st) {
   Args a = base_args();
   a.A = dh; a.lda = 2 * s.d_ff;          // [K = rows, M = 2f]
-  a.B = x_perm; a.ldb = s.d;             // [K = rows, N = d]
+  a.B = x_rows; a.ldb = s.d;             // [K = rows, N = d]: x_perm, or x read through gather
+  a.b_gather = gather; a.gather_rows = s.T;
   a.C = dw1; a.ldc = s.d; a.c_estride = (int64_t)2 * s.d_ff * s.d;
   a.M = 2 * s.d_ff; a.N = s.d; a.E = s.E;
   return run_wgrad(s, w, a, st);
 }
 
-hipError_t gemm_dw2(const moe_shape& s, const WgradChunks& w, const void* do_perm, const void* ga, float* dw2,
-                    hipStream_t st) {
+hipError_t gemm_dw2(const moe_shape& s, const WgradChunks& w, const void* do_rows, const int32_t* gather,
+                    const void* ga, float* dw2, hipStream_t st) {
   Args a = base_args();
-  a.A = do_perm; a.lda = s.d;            // [K = rows, M = d]
+  a.A = do_rows; a.lda = s.d;            // [K = rows, M = d]: dO_perm, or dout read through gather
+  a.a_gather = gather; a.gather_rows = s.T;
   a.B = ga; a.ldb = s.d_ff;              // [K = rows, N = f]
   a.C = dw2; a.ldc = s.d_ff; a.c_estride = (int64_t)s.d * s.d_ff;
   a.M = s.d; a.N = s.d_ff; a.E = s.E;

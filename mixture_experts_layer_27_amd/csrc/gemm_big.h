@@ -88,6 +88,44 @@ struct RegOperand {
 #pragma unroll
     for (int i = 0; i < L; ++i) voff[i] = (uint32_t)((int64_t)(k0 + KPP * i) * ld * 2 + cc * 16);
   }
+  // M/N-contiguous with gathered k rows: k row r of the chunk [k_begin, k_end)
+  // is row gidx[r] of the source (a permutation fused into the loads).  The
+  // source rows of a stage are fetched one stage ahead (fetch_rows).
+  const int32_t* gidx;
+  int gk, gkend, kl;
+  int64_t gld;
+  uint32_t gcol;
+  int32_t nsrc[L];
+  MOE_DEV void init_mn_gather(int64_t ld, const int32_t* g, int k_begin, int k_end, int64_t col_bytes,
+                              int64_t src_rows) {
+    constexpr int CPK = ROWS / 8;
+    const int t = threadIdx.x, cc = t % CPK, k0 = t / CPK;
+    lds0 = mn_off<ROWS>(k0, cc * 16);
+    gidx = g; gk = k_begin; gkend = k_end; kl = k0;
+    gld = ld * 2;
+    gcol = (uint32_t)(col_bytes + cc * 16);
+    step = 0;
+    num0 = src_rows * gld;
+    fetch_rows();
+  }
+  MOE_DEV void fetch_rows() {
+    constexpr int KPP = NT / (ROWS / 8);
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const int k = gk + kl + KPP * i;
+      nsrc[i] = k < gkend ? gidx[k] : -1;
+    }
+    gk += KPP * L;
+  }
+  MOE_DEV void load_gather() {
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(base, (uint32_t)num0);
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const uint32_t off = nsrc[i] >= 0 ? (uint32_t)((int64_t)nsrc[i] * gld) + gcol : 0xfffffff0u;   // absent: past num0
+      v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+    }
+    fetch_rows();
+  }
   MOE_DEV void load(int kt) {
     const int64_t n = num0 - kt * step;   // <= 0 past the operand: every load returns zero
     const __amdgpu_buffer_rsrc_t r = make_rsrc(base + kt * step, (uint32_t)(n > 0 ? n : 0));
@@ -107,8 +145,12 @@ constexpr size_t big_lds_bytes(bool wide) {
   return wide ? big_ring_bytes<128, 512>() : big_ring_bytes<256, 256>();
 }
 
-// One output tile: BM x BN with WM x WN waves of 128 x 64.
-template <int BM, int BN, int WM, int WN, bool AKC, bool BKC, int GROUP, int EPI>
+// One output tile: BM x BN with WM x WN waves of 128 x 64.  GATHER bit 0: the
+// rows of A (GROUP_M) or the k rows of A (GROUP_K) are read through
+// args.a_gather from a source of args.gather_rows rows; bit 1: the k rows of B
+// (GROUP_K) through args.b_gather.  The permutation of the rows is then fused
+// into the operand loads (no permuted copy is written).
+template <int BM, int BN, int WM, int WN, bool AKC, bool BKC, int GROUP, int EPI, int GATHER = 0>
 MOE_DEV void big_tile(const Args& args, const TileCtx& ctx, char* smem) {
   using T = bf16_t;
   constexpr int BK = kBigBK;
@@ -125,13 +167,25 @@ MOE_DEV void big_tile(const Args& args, const TileCtx& ctx, char* smem) {
 
   RegOperand<BM, AKC, NT> ra;
   RegOperand<BN, BKC, NT> rb;
-  if constexpr (AKC) {   // GROUP_M: rows row_begin.. of the segment, K contiguous
+  if constexpr (AKC && (GATHER & 1)) {   // GROUP_M, rows gathered: row r of the tile is source row a_gather[..]
+    const int nrows = min(BM, ctx.row_end - ctx.row_begin);
+    const int64_t rowb = args.lda * 2;
+    ra.base = Ab;
+    ra.step = BK * 2;
+    ra.num0 = args.gather_rows * rowb;
+    ra.init_kc([&](int r) -> int64_t {
+      return (r < nrows ? (int64_t)args.a_gather[ctx.row_begin + r] : args.gather_rows) * rowb;   // absent: past num0
+    });
+  } else if constexpr (AKC) {   // GROUP_M: rows row_begin.. of the segment, K contiguous
     const int nrows = min(BM, ctx.row_end - ctx.row_begin);
     const int64_t rowb = args.lda * 2;
     ra.base = Ab + (int64_t)ctx.row_begin * rowb;
     ra.step = BK * 2;
     ra.num0 = (int64_t)nrows * rowb;     // rows >= nrows start past it
     ra.init_kc([&](int r) -> int64_t { return (int64_t)r * rowb; });
+  } else if constexpr (GATHER & 1) {    // GROUP_K, k rows gathered
+    ra.base = Ab;
+    ra.init_mn_gather(args.lda, args.a_gather, ctx.k_begin, ctx.k_end, (int64_t)ctx.m0 * 2, args.gather_rows);
   } else {               // GROUP_K: k rows k_begin..k_end of the chunk, columns m0.. contiguous
     ra.base = Ab + ((int64_t)ctx.k_begin * args.lda + ctx.m0) * 2;
     ra.step = (int64_t)BK * args.lda * 2;
@@ -153,6 +207,10 @@ MOE_DEV void big_tile(const Args& args, const TileCtx& ctx, char* smem) {
       }
       return (int64_t)j * rowb;         // j >= N lies past num0
     });
+  } else if constexpr (GATHER & 2) {    // GROUP_K, k rows of B gathered
+    static_assert(GROUP == GROUP_K, "B rows are gathered only over the reduction");
+    rb.base = Bb;
+    rb.init_mn_gather(args.ldb, args.b_gather, ctx.k_begin, ctx.k_end, (int64_t)ctx.n0 * 2, args.gather_rows);
   } else {               // [K][N]: k rows, columns n0.. contiguous
     const int kb = (GROUP == GROUP_K) ? ctx.k_begin : 0;
     const int kend = (GROUP == GROUP_K) ? ctx.k_end : args.K;
@@ -208,10 +266,17 @@ MOE_DEV void big_tile(const Args& args, const TileCtx& ctx, char* smem) {
   const int nk = kext > 0 ? (kext + BK - 1) / BK : 0;
   constexpr int NR = (AKC ? TM : 2 * TM) + (BKC ? TN : 2 * TN);   // LDS reads per k16 step
   u32x4 a0[TM], b0[TN], a1[TM], b1[TN];
+  // stage loads, in stage order (the gathered operands fetch their rows one stage ahead)
+  auto load_a = [&](int kt) {
+    if constexpr (!AKC && (GATHER & 1)) ra.load_gather(); else ra.load(kt);
+  };
+  auto load_b = [&](int kt) {
+    if constexpr (GATHER & 2) rb.load_gather(); else rb.load(kt);
+  };
   if (nk > 0) {
-    ra.load(0); rb.load(0);
+    load_a(0); load_b(0);
     ra.store(smem); rb.store(smem + ASZ);
-    ra.load(1); rb.load(1);
+    load_a(1); load_b(1);
     __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
     cta_barrier();
     frags(smem, 0, a0, b0);
@@ -223,7 +288,7 @@ MOE_DEV void big_tile(const Args& args, const TileCtx& ctx, char* smem) {
     mma(a0, b0);
     frags(as, 2, a0, b0);
     ra.store(an); rb.store(an + ASZ);
-    ra.load(kt + 2); rb.load(kt + 2);
+    load_a(kt + 2); load_b(kt + 2);
     mma(a1, b1);
     frags(as, 3, a1, b1);
     mma(a0, b0);
@@ -296,19 +361,19 @@ MOE_DEV bool big_decode_m(const Args& args, TileCtx& c, bool* wide) {
   return true;
 }
 
-template <bool AKC, bool BKC, int GROUP, int EPI>
+template <bool AKC, bool BKC, int GROUP, int EPI, int GATHER = 0>
 __global__ __launch_bounds__(kBigThreads) void grouped_gemm_big(Args args) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   static_assert(GROUP == GROUP_M || GROUP == GROUP_K, "grouped GEMMs only");
   TileCtx ctx;
   if constexpr (GROUP == GROUP_K) {
     if (!decode_tile<256, 256, kBigBK, GROUP_K>(args, ctx)) return;
-    big_tile<256, 256, 2, 4, AKC, BKC, GROUP, EPI>(args, ctx, smem);
+    big_tile<256, 256, 2, 4, AKC, BKC, GROUP, EPI, GATHER>(args, ctx, smem);
   } else {
     bool wide = false;
     if (!big_decode_m(args, ctx, &wide)) return;
-    if (wide) big_tile<128, 512, 1, 8, AKC, BKC, GROUP, EPI>(args, ctx, smem);
-    else big_tile<256, 256, 2, 4, AKC, BKC, GROUP, EPI>(args, ctx, smem);
+    if (wide) big_tile<128, 512, 1, 8, AKC, BKC, GROUP, EPI, GATHER>(args, ctx, smem);
+    else big_tile<256, 256, 2, 4, AKC, BKC, GROUP, EPI, GATHER>(args, ctx, smem);
   }
 }
 

@@ -80,19 +80,23 @@ struct GemmPlanView {
   const int32_t* prefix;   // m-tile prefix matching the kernel's BM
   int64_t n_max;
 };
-hipError_t gemm_up_swiglu(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const void* x_perm,
-                          const void* w1, void* h, void* a, hipStream_t st);
+// Row operands taken "through gather": the GEMM reads row r of the permuted
+// operand as row gather[r] of the unpermuted tensor ([T, ...]); nullptr = the
+// operand is already permuted.
+hipError_t gemm_up_swiglu(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const void* x_rows,
+                          const int32_t* gather, const void* w1, void* h, void* a, hipStream_t st);
 hipError_t gemm_down(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const void* a,
                      const void* w2, void* y, hipStream_t st);
-hipError_t gemm_dact(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const void* do_perm,
-                     const void* w2, const void* h, void* dh, void* ga, float* ds_part, hipStream_t st);
+hipError_t gemm_dact(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const void* do_rows,
+                     const int32_t* gather, const void* w2, const void* h, void* dh, void* ga, float* ds_part,
+                     hipStream_t st);
 int gemm_dact_parts(const moe_shape& s);
 hipError_t gemm_dx_perm(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const void* dh,
                         const void* w1, void* dx_perm, hipStream_t st);
-hipError_t gemm_dw1(const moe_shape& s, const WgradChunks& w, const void* dh, const void* x_perm, float* dw1,
-                    hipStream_t st);
-hipError_t gemm_dw2(const moe_shape& s, const WgradChunks& w, const void* do_perm, const void* ga, float* dw2,
-                    hipStream_t st);
+hipError_t gemm_dw1(const moe_shape& s, const WgradChunks& w, const void* dh, const void* x_rows,
+                    const int32_t* gather, float* dw1, hipStream_t st);
+hipError_t gemm_dw2(const moe_shape& s, const WgradChunks& w, const void* do_rows, const int32_t* gather,
+                    const void* ga, float* dw2, hipStream_t st);
 hipError_t gemm_router_logits(const moe_shape& s, const void* x, const void* wg, const float* bias,
                               const float* noise, float* logits, hipStream_t st);
 // dxr [T,d] fp32 = dzq [T, ldz] W_g (dense router gradients)
@@ -125,12 +129,14 @@ hipError_t mx_quantize_cols(const void* src, int G, int R, int C, uint8_t* codes
 // the same with plain scales [C][R/32] (test hook)
 hipError_t launch_quantize_cols_plain(const void* src, int R, int C, uint8_t* codes, uint8_t* scales, hipStream_t st);
 hipError_t mx_quantize_tokens(const void* src, int C, const int32_t* seg_off, const int32_t* pad_off, int E,
-                              int64_t P, uint8_t* codes, uint8_t* scales, hipStream_t st);
+                              int64_t P, uint8_t* codes, uint8_t* scales, hipStream_t st,
+                              const int32_t* gather = nullptr);
 hipError_t mx_pad_offsets(const int32_t* offsets, int E, int32_t* pad_off, hipStream_t st);
 // rows and columns (seg_off == nullptr: G matrices [R][C]) or rows and tokens
 // (seg_off, pad_off, P as for mx_quantize_tokens) in one pass
 hipError_t mx_quantize_dual(const void* src, int G, int R, int C, const int32_t* seg_off, const int32_t* pad_off,
-                            int E, int64_t P, const MxOperand& rows, const MxOperand& pos, hipStream_t st);
+                            int E, int64_t P, const MxOperand& rows, const MxOperand& pos, hipStream_t st,
+                            const int32_t* gather = nullptr);
 hipError_t gemm_mx_up_swiglu(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const MxOperand& x,
                              const MxOperand& w1, void* h, const MxOperand& act, hipStream_t st);
 hipError_t gemm_mx_down(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const MxOperand& act,

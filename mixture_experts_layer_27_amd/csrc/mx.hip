@@ -139,7 +139,8 @@ __global__ __launch_bounds__(256) void quantize_t_kernel(const bf16_t* __restric
                                                         const int32_t* __restrict__ seg_off,
                                                         const int32_t* __restrict__ pad_off, int E,
                                                         uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-                                                        int64_t P, int plain_scales) {
+                                                        int64_t P, int plain_scales,
+                                                        const int32_t* __restrict__ gather) {
   __shared__ float tile[128][65];
   const int c0 = blockIdx.x * 64;
   const int64_t p0 = (int64_t)blockIdx.y * 128;
@@ -177,7 +178,8 @@ __global__ __launch_bounds__(256) void quantize_t_kernel(const bf16_t* __restric
     const int i = threadIdx.x + 256 * u;
     const int rr = i >> 3, ch = i & 7;
     const int hh = rr >> 6, rl = rr & 63;
-    raw[u] = rl < valid[hh] ? ldg16(src + (base[hh] + rl) * C + c0 + ch * 8) : u32x4{0u, 0u, 0u, 0u};
+    const int64_t sr = gather && rl < valid[hh] ? (int64_t)gather[base[hh] + rl] : base[hh] + rl;   // tokens mode
+    raw[u] = rl < valid[hh] ? ldg16(src + sr * C + c0 + ch * 8) : u32x4{0u, 0u, 0u, 0u};
   }
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -234,7 +236,8 @@ __global__ __launch_bounds__(256) void quantize_dual_kernel(const bf16_t* __rest
                                                            const int32_t* __restrict__ pad_off, int E, int64_t P,
                                                            uint8_t* __restrict__ rcodes, uint8_t* __restrict__ rscales,
                                                            int64_t rsrows, uint8_t* __restrict__ tcodes,
-                                                           uint8_t* __restrict__ tscales) {
+                                                           uint8_t* __restrict__ tscales,
+                                                           const int32_t* __restrict__ gather) {
   constexpr int VS = 136;   // value tile row stride (bf16 elements; rows stay 16-byte aligned)
   constexpr int CS = 144;   // code tile row stride (bytes): 16 consecutive columns hit distinct banks
   __shared__ __attribute__((aligned(16))) uint16_t vt[128 * VS];
@@ -276,7 +279,9 @@ __global__ __launch_bounds__(256) void quantize_dual_kernel(const bf16_t* __rest
     const int i = t + 256 * u;
     const int rr = i >> 4, ch = i & 15, hh = rr >> 6, rl = rr & 63;
     const int col = c0 + ch * 8;
-    raw[u] = (rl < valid[hh] && col < C) ? ldg16(src + (base[hh] + rl) * C + col) : u32x4{0u, 0u, 0u, 0u};
+    const bool ok = rl < valid[hh] && col < C;
+    const int64_t sr = gather && ok ? (int64_t)gather[base[hh] + rl] : base[hh] + rl;   // tokens mode
+    raw[u] = ok ? ldg16(src + sr * C + col) : u32x4{0u, 0u, 0u, 0u};
   }
   // along rows: four consecutive lanes hold one 32-column block
 #pragma unroll
@@ -413,29 +418,32 @@ hipError_t mx_quantize_rows_padded(const void* src, int64_t rows, int64_t K, con
 
 hipError_t mx_quantize_cols(const void* src, int G, int R, int C, uint8_t* codes, uint8_t* scales, hipStream_t st) {
   hipLaunchKernelGGL(quantize_t_kernel, dim3(C / 64, (R + 127) / 128, G), dim3(256), 0, st, (const bf16_t*)src, G, R, C,
-                     (const int32_t*)nullptr, (const int32_t*)nullptr, 0, codes, scales, (int64_t)0, 0);
+                     (const int32_t*)nullptr, (const int32_t*)nullptr, 0, codes, scales, (int64_t)0, 0,
+                     (const int32_t*)nullptr);
   return hipGetLastError();
 }
 
 hipError_t launch_quantize_cols_plain(const void* src, int R, int C, uint8_t* codes, uint8_t* scales, hipStream_t st) {
   hipLaunchKernelGGL(quantize_t_kernel, dim3(C / 64, (R + 127) / 128, 1), dim3(256), 0, st, (const bf16_t*)src, 1, R,
-                     C, (const int32_t*)nullptr, (const int32_t*)nullptr, 0, codes, scales, (int64_t)0, 1);
+                     C, (const int32_t*)nullptr, (const int32_t*)nullptr, 0, codes, scales, (int64_t)0, 1,
+                     (const int32_t*)nullptr);
   return hipGetLastError();
 }
 
 hipError_t mx_quantize_tokens(const void* src, int C, const int32_t* seg_off, const int32_t* pad_off, int E,
-                              int64_t P, uint8_t* codes, uint8_t* scales, hipStream_t st) {
+                              int64_t P, uint8_t* codes, uint8_t* scales, hipStream_t st, const int32_t* gather) {
   hipLaunchKernelGGL(quantize_t_kernel, dim3(C / 64, (unsigned)((P + 127) / 128), 1), dim3(256), 0, st, (const bf16_t*)src, 1,
-                     0, C, seg_off, pad_off, E, codes, scales, P, 0);
+                     0, C, seg_off, pad_off, E, codes, scales, P, 0, gather);
   return hipGetLastError();
 }
 
 hipError_t mx_quantize_dual(const void* src, int G, int R, int C, const int32_t* seg_off, const int32_t* pad_off,
-                            int E, int64_t P, const MxOperand& rows, const MxOperand& pos, hipStream_t st) {
+                            int E, int64_t P, const MxOperand& rows, const MxOperand& pos, hipStream_t st,
+                            const int32_t* gather) {
   const int64_t len = seg_off ? P : (int64_t)R;
   hipLaunchKernelGGL(quantize_dual_kernel, dim3((C + 127) / 128, (unsigned)((len + 127) / 128), G), dim3(256), 0, st,
                      (const bf16_t*)src, G, R, C, seg_off, pad_off, E, P, rows.codes, rows.scales, rows.srows,
-                     pos.codes, pos.scales);
+                     pos.codes, pos.scales, gather);
   return hipGetLastError();
 }
 

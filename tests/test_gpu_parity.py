@@ -206,3 +206,28 @@ def test_router_loss_gradients(name):
         err = float(np.abs(got - r).max()) / scale
         rf = float(np.linalg.norm(got - r) / np.linalg.norm(r))
         assert err < bar and rf < bar / 2, f"{key}: max-abs/max {err:.3e}, rel-Frobenius {rf:.3e} (bar {bar})"
+
+
+@pytest.mark.parametrize("name", ["fine_small", "big_tiles_small", "sparse_round_small", "fine_zipf_small",
+                                  "max_E_k", "one_token", "fine_mx_small", "mx_ragged_d", "var_capacity_all",
+                                  "var_all_lb_z_noise"])
+def test_fused_gather_bitwise(name):
+    """moe_grouped_gemm_swiglu_gather (rows of x fetched through the plan inside the
+    GEMM or quantiser loads) and a backward that gathers x and dout the same way
+    give the same bits as the permute-then-GEMM path."""
+    from mixture_experts_layer_27_amd import binding
+    cfg = CASES[name]
+    print(f"[parity] fused gather case={name}", flush=True)
+    g = make_inputs(cfg)
+    outs = []
+    for fused in (False, True):
+        run = binding.LayerRun(cfg, g, fused_gather=fused)
+        run.forward()
+        run.backward()
+        torch.cuda.synchronize()
+        n = int(run.plan.arrays()["offsets"][-1].item())
+        outs.append([t.clone() for t in (run.out, run.h[:n], run.y[:n], run.ds[:n], run.dx, run.dw_gate,
+                                         run.dw1, run.dw2, run.dlogits)])
+    names = ("out", "h", "y", "ds", "dx", "dw_gate", "dw1", "dw2", "dlogits")
+    for key, a, b in zip(names, *outs):
+        assert torch.equal(a, b), key
