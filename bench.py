@@ -59,6 +59,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="fine_e128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fused-gather", action="store_true",
+                    help="forward reads x through the plan inside the expert GEMMs (no x_perm); the backward "
+                         "then permutes x itself")
     ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0 = automatic)")
     ap.add_argument("--out", default=None, help="also append the JSON line to this file")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -131,7 +134,11 @@ def main():
     cfg = configs.get(a.config)
     print(f"[bench] generating {cfg.name} inputs", file=sys.stderr, flush=True)
     g = synth.generate(cfg)
-    run = binding.LayerRun(cfg, g)
+    # default: permute x once and hand x_perm to the backward (the backward reads dout through
+    # the plan inside its GEMMs either way); --fused-gather moves the forward permutation into
+    # the expert GEMMs' loads instead
+    fused = a.fused_gather and cfg.act == "bf16" and cfg.T * cfg.d * 2 < 2 ** 31
+    run = binding.LayerRun(cfg, g, fused_gather=fused)
     s = run.s
     stream = torch.cuda.current_stream()
 
@@ -144,9 +151,15 @@ def main():
         mark(0)
         run.route()
         mark(1)
-        binding.permute(s, run.inp["x"], run.plan, run.x_perm)
+        if not fused:
+            binding.permute(s, run.inp["x"], run.plan, run.x_perm)
         mark(2)
-        binding.grouped_gemm_swiglu(s, run.x_perm, run.inp["w1"], run.inp["w2"], run.plan, run.h, run.y, run.ws_fwd)
+        if fused:
+            binding.grouped_gemm_swiglu_gather(s, run.inp["x"], run.inp["w1"], run.inp["w2"], run.plan, run.h, run.y,
+                                               run.ws_fwd)
+        else:
+            binding.grouped_gemm_swiglu(s, run.x_perm, run.inp["w1"], run.inp["w2"], run.plan, run.h, run.y,
+                                        run.ws_fwd)
         mark(3)
         binding.unpermute_combine(s, run.y, run.plan, run.out)
         mark(4)
@@ -170,6 +183,17 @@ def main():
           for j, p in enumerate(phases)}
     step_ms = sum(evs[i][0].elapsed_time(evs[i][5]) for i in range(a.steps)) / a.steps
     ms_per_step = wall * 1000.0 / a.steps
+
+    # moe_permute on its own (outside the step when it is fused into the GEMMs)
+    pev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for _ in range(3):
+        binding.permute(s, run.inp["x"], run.plan, run.x_perm)
+    pev[0].record(stream)
+    for _ in range(10):
+        binding.permute(s, run.inp["x"], run.plan, run.x_perm)
+    pev[1].record(stream)
+    torch.cuda.synchronize()
+    permute_ms = pev[0].elapsed_time(pev[1]) / 10
 
     N = cfg.N  # rows without rounding (algorithmic work)
     counts = run.plan.arrays()["counts"].cpu()
@@ -206,7 +230,8 @@ def main():
         "grouped_gemm_mfma_frac": {"forward": achieved / peak,
                                    "backward_call": bwd_flops / (ms["backward"] * 1e-3) / 1e12 / peak
                                    if run.has_bwd else None},
-        "permute_GBps": permute_bytes / (ms["permute"] * 1e-3) / 1e9,
+        "permute_GBps": permute_bytes / (permute_ms * 1e-3) / 1e9,
+        "permute_fused_into_gemms": fused,
         "combine_GBps": combine_bytes / (ms["combine"] * 1e-3) / 1e9,
         "hbm_peak_GBps": PEAK_HBM_GBS,
         "rows": rows,

@@ -398,8 +398,10 @@ moe_status moe_backward(const moe_shape* s, const void* x, const void* w_gate, c
   carve_bwd(*s, reinterpret_cast<char*>(ws), &w);
   float* dz = dlogits ? dlogits : w.dlogits;
   const int ldz = ldz_of(*s);
-  // dO (and x, when x_perm is not given) reach the GEMMs through token_of_row
-  // inside their operand loads when the kernels allow it, else as permuted copies
+  // dO reaches the GEMMs through token_of_row inside their operand loads when the
+  // kernels allow it (as fast as a permuted copy here, and no copy is stored),
+  // else as a permuted copy.  x without x_perm is permuted again: its gathered
+  // loads in the dW1 GEMM cost more than the permutation.
   const bool fused = gather_ok(*s);
   const int32_t* tor = plan->token_of_row;
   hipError_t e = fused ? hipSuccess : launch_permute_rows(*s, dout, *plan, w.do_perm, hs);
@@ -421,9 +423,10 @@ moe_status moe_backward(const moe_shape* s, const void* x, const void* w_gate, c
     if (e == hipSuccess && !fwd_ws) e = mx_quantize_cols(w2, E, d, f, w.w2t.codes, w.w2t.scales, hs);
     if (e == hipSuccess) e = gemm_mx_dact(*s, *plan, pi, w.doq, w2t, h_saved, w.dh, w.dhq, w.ga, w.ds_part, hs);
     if (e == hipSuccess && !fwd_ws) e = mx_quantize_cols(w1, E, 2 * f, d, w.w1t.codes, w.w1t.scales, hs);
-    if (e == hipSuccess && !x_perm && !fwd_ws && !fused) e = launch_permute_rows(*s, x, *plan, w.xbuf, hs);
+    // the token-axis quantiser reads x through the plan (a memory-bound pass: gathering is free)
     const void* xp = x_perm ? x_perm : fused ? x : w.xbuf;
     const int32_t* xg = (!x_perm && fused) ? tor : nullptr;
+    if (e == hipSuccess && !x_perm && !fwd_ws && !fused) e = launch_permute_rows(*s, x, *plan, w.xbuf, hs);
     if (e == hipSuccess) e = mx_quantize_tokens(w.dh, 2 * f, plan->offsets, w.pad_off, E, P, w.dh_t.codes, w.dh_t.scales, hs);
     if (e == hipSuccess && !fwd_ws)
       e = mx_quantize_tokens(xp, d, plan->offsets, w.pad_off, E, P, w.x_t.codes, w.x_t.scales, hs, xg);
@@ -436,11 +439,10 @@ moe_status moe_backward(const moe_shape* s, const void* x, const void* w_gate, c
     if (e == hipSuccess) e = gemm_mx_dx_perm(*s, *plan, pi, w.dhq, w1t, w.xbuf, hs);   // dx_perm (x_perm no longer needed)
   } else {
     if (e == hipSuccess) e = gemm_dact(*s, *plan, pi, dO, dOg, w2, h_saved, w.dh, w.ga, w.ds_part, hs);
-    if (e == hipSuccess && !x_perm && !fused) e = launch_permute_rows(*s, x, *plan, w.xbuf, hs);
-    const void* xp = x_perm ? x_perm : fused ? x : w.xbuf;
-    const int32_t* xg = (!x_perm && fused) ? tor : nullptr;
+    if (e == hipSuccess && !x_perm) e = launch_permute_rows(*s, x, *plan, w.xbuf, hs);
+    const void* xp = x_perm ? x_perm : w.xbuf;
     if (e == hipSuccess) e = launch_wgrad_chunks(plan->offsets, s->E, w.wg.kch, w.wg, hs);
-    if (e == hipSuccess) e = gemm_dw1(*s, w.wg, w.dh, xp, xg, dw1, hs);
+    if (e == hipSuccess) e = gemm_dw1(*s, w.wg, w.dh, xp, dw1, hs);
     if (e == hipSuccess) e = launch_wgrad_reduce(w.wg, s->E, (int64_t)2 * s->d_ff * s->d, dw1, hs);
     if (e == hipSuccess) e = gemm_dw2(*s, w.wg, dO, dOg, w.ga, dw2, hs);
     if (e == hipSuccess) e = launch_wgrad_reduce(w.wg, s->E, (int64_t)s->d * s->d_ff, dw2, hs);

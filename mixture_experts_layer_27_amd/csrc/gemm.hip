@@ -191,22 +191,20 @@ hipError_t run_wgrad(const moe_shape& s, const WgradChunks& w, Args& a, hipStrea
     a.tilesM = ceil_div(a.M, 256); a.tilesN = ceil_div(a.N, 256);
     const int64_t tiles = 8 * (int64_t)ceil_div(w.max_chunks, 8) * a.tilesM * a.tilesN;
     if (a.a_gather) return run_big<false, false, GROUP_K, EPI_F32, 1>(a, tiles, st);
-    if (a.b_gather) return run_big<false, false, GROUP_K, EPI_F32, 2>(a, tiles, st);
     return run_big<false, false, GROUP_K, EPI_F32>(a, tiles, st);
   }
-  if (a.a_gather || a.b_gather) return hipErrorNotSupported;   // gathered k rows: bf16 kernels only
+  if (a.a_gather) return hipErrorNotSupported;   // gathered k rows: bf16 kernels only
   a.tilesM = ceil_div(a.M, 128); a.tilesN = ceil_div(a.N, 128);
   const int64_t tiles = 8 * (int64_t)ceil_div(w.max_chunks, 8) * a.tilesM * a.tilesN;
   return run<float, 128, 128, 2, 2, false, false, GROUP_K, EPI_F32>(a, tiles, st);
 }
 }  // namespace
 
-hipError_t gemm_dw1(const moe_shape& s, const WgradChunks& w, const void* dh, const void* x_rows,
-                    const int32_t* gather, float* dw1, hipStream_t st) {
+hipError_t gemm_dw1(const moe_shape& s, const WgradChunks& w, const void* dh, const void* x_perm, float* dw1,
+                    hipStream_t st) {
   Args a = base_args();
   a.A = dh; a.lda = 2 * s.d_ff;          // [K = rows, M = 2f]
-  a.B = x_rows; a.ldb = s.d;             // [K = rows, N = d]: x_perm, or x read through gather
-  a.b_gather = gather; a.gather_rows = s.T;
+  a.B = x_perm; a.ldb = s.d;             // [K = rows, N = d]
   a.C = dw1; a.ldc = s.d; a.c_estride = (int64_t)2 * s.d_ff * s.d;
   a.M = 2 * s.d_ff; a.N = s.d; a.E = s.E;
   return run_wgrad(s, w, a, st);

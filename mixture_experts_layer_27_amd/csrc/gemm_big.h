@@ -89,12 +89,12 @@ struct RegOperand {
     for (int i = 0; i < L; ++i) voff[i] = (uint32_t)((int64_t)(k0 + KPP * i) * ld * 2 + cc * 16);
   }
   // M/N-contiguous with gathered k rows: k row r of the chunk [k_begin, k_end)
-  // is row gidx[r] of the source (a permutation fused into the loads).  The
-  // source rows of a stage are fetched one stage ahead (fetch_rows).
+  // is row gidx[r] of the source (a permutation fused into the loads).  Each
+  // lane reads the source rows of its L loads one stage ahead (fetch_rows);
+  // offsets are 32-bit (the source holds fewer than 2^31 bytes).
   const int32_t* gidx;
   int gk, gkend, kl;
-  int64_t gld;
-  uint32_t gcol;
+  uint32_t gld, gcol;
   int32_t nsrc[L];
   MOE_DEV void init_mn_gather(int64_t ld, const int32_t* g, int k_begin, int k_end, int64_t col_bytes,
                               int64_t src_rows) {
@@ -102,10 +102,10 @@ struct RegOperand {
     const int t = threadIdx.x, cc = t % CPK, k0 = t / CPK;
     lds0 = mn_off<ROWS>(k0, cc * 16);
     gidx = g; gk = k_begin; gkend = k_end; kl = k0;
-    gld = ld * 2;
+    gld = (uint32_t)(ld * 2);
     gcol = (uint32_t)(col_bytes + cc * 16);
     step = 0;
-    num0 = src_rows * gld;
+    num0 = src_rows * (int64_t)gld;
     fetch_rows();
   }
   MOE_DEV void fetch_rows() {
@@ -121,7 +121,7 @@ struct RegOperand {
     const __amdgpu_buffer_rsrc_t r = make_rsrc(base, (uint32_t)num0);
 #pragma unroll
     for (int i = 0; i < L; ++i) {
-      const uint32_t off = nsrc[i] >= 0 ? (uint32_t)((int64_t)nsrc[i] * gld) + gcol : 0xfffffff0u;   // absent: past num0
+      const uint32_t off = nsrc[i] >= 0 ? (uint32_t)nsrc[i] * gld + gcol : 0xfffffff0u;   // absent: past num0
       v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
     }
     fetch_rows();
@@ -145,11 +145,10 @@ constexpr size_t big_lds_bytes(bool wide) {
   return wide ? big_ring_bytes<128, 512>() : big_ring_bytes<256, 256>();
 }
 
-// One output tile: BM x BN with WM x WN waves of 128 x 64.  GATHER bit 0: the
+// One output tile: BM x BN with WM x WN waves of 128 x 64.  GATHER = 1: the
 // rows of A (GROUP_M) or the k rows of A (GROUP_K) are read through
-// args.a_gather from a source of args.gather_rows rows; bit 1: the k rows of B
-// (GROUP_K) through args.b_gather.  The permutation of the rows is then fused
-// into the operand loads (no permuted copy is written).
+// args.a_gather from a source of args.gather_rows rows: the permutation of the
+// rows is fused into the operand loads (no permuted copy is written).
 template <int BM, int BN, int WM, int WN, bool AKC, bool BKC, int GROUP, int EPI, int GATHER = 0>
 MOE_DEV void big_tile(const Args& args, const TileCtx& ctx, char* smem) {
   using T = bf16_t;
@@ -207,10 +206,6 @@ MOE_DEV void big_tile(const Args& args, const TileCtx& ctx, char* smem) {
       }
       return (int64_t)j * rowb;         // j >= N lies past num0
     });
-  } else if constexpr (GATHER & 2) {    // GROUP_K, k rows of B gathered
-    static_assert(GROUP == GROUP_K, "B rows are gathered only over the reduction");
-    rb.base = Bb;
-    rb.init_mn_gather(args.ldb, args.b_gather, ctx.k_begin, ctx.k_end, (int64_t)ctx.n0 * 2, args.gather_rows);
   } else {               // [K][N]: k rows, columns n0.. contiguous
     const int kb = (GROUP == GROUP_K) ? ctx.k_begin : 0;
     const int kend = (GROUP == GROUP_K) ? ctx.k_end : args.K;
@@ -270,9 +265,7 @@ MOE_DEV void big_tile(const Args& args, const TileCtx& ctx, char* smem) {
   auto load_a = [&](int kt) {
     if constexpr (!AKC && (GATHER & 1)) ra.load_gather(); else ra.load(kt);
   };
-  auto load_b = [&](int kt) {
-    if constexpr (GATHER & 2) rb.load_gather(); else rb.load(kt);
-  };
+  auto load_b = [&](int kt) { rb.load(kt); };
   if (nk > 0) {
     load_a(0); load_b(0);
     ra.store(smem); rb.store(smem + ASZ);

@@ -34,8 +34,8 @@ enum { EPI_ACT = 0, EPI_F32 = 1, EPI_SWIGLU = 2, EPI_DSWIGLU = 3, EPI_LOGITS = 4
 
 struct Args {
   const void* A; int64_t lda; int64_t a_estride; const int32_t* a_gather;
-  const void* B; int64_t ldb; int64_t b_estride; const int32_t* b_gather;
-  int64_t gather_rows;          // rows of the tensor a_gather / b_gather index (bounds of gathered loads)
+  const void* B; int64_t ldb; int64_t b_estride;
+  int64_t gather_rows;          // rows of the tensor a_gather indexes (bounds of gathered loads)
   void* C; int64_t ldc; int64_t c_estride;
   void* C2; int64_t ldc2;
   float* C3; int64_t ldc3;

@@ -93,8 +93,8 @@ hipError_t gemm_dact(const moe_shape& s, const moe_plan& p, const PlanInternal& 
 int gemm_dact_parts(const moe_shape& s);
 hipError_t gemm_dx_perm(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const void* dh,
                         const void* w1, void* dx_perm, hipStream_t st);
-hipError_t gemm_dw1(const moe_shape& s, const WgradChunks& w, const void* dh, const void* x_rows,
-                    const int32_t* gather, float* dw1, hipStream_t st);
+hipError_t gemm_dw1(const moe_shape& s, const WgradChunks& w, const void* dh, const void* x_perm, float* dw1,
+                    hipStream_t st);
 hipError_t gemm_dw2(const moe_shape& s, const WgradChunks& w, const void* do_rows, const int32_t* gather,
                     const void* ga, float* dw2, hipStream_t st);
 hipError_t gemm_router_logits(const moe_shape& s, const void* x, const void* wg, const float* bias,
