@@ -149,8 +149,9 @@ size_t carve_bwd(const moe_shape& s, char* base, BwdWs* w) {
   const int64_t N = max_rows(s);
   BwdWs q{};
   q.do_perm = gather_ok(s) ? nullptr : c.take<char>(N * s.d * esz(s));   // dO is gathered inside the loads
-  q.dh = c.take<char>(N * 2 * s.d_ff * esz(s));
-  q.ga = c.take<char>(N * s.d_ff * esz(s));
+  // MXFP8 keeps dH and gA only as codes (written by the dA' epilogue)
+  q.dh = s.gemm == MOE_MXFP8 ? nullptr : c.take<char>(N * 2 * s.d_ff * esz(s));
+  q.ga = s.gemm == MOE_MXFP8 ? nullptr : c.take<char>(N * s.d_ff * esz(s));
   q.xbuf = c.take<char>(N * s.d * esz(s));
   q.ds_part = c.take<float>((size_t)gemm_dact_parts(s) * N * 4);
   q.dlogits = c.take<float>((size_t)s.T * s.E * 4);
@@ -421,16 +422,14 @@ moe_status moe_backward(const moe_shape* s, const void* x, const void* w_gate, c
     if (e == hipSuccess) e = mx_pad_offsets(off, E, w.pad_off, hs);
     if (e == hipSuccess) e = mx_quantize_dual(dO, 1, 0, d, off, w.pad_off, E, P, w.doq, w.do_t, hs, dOg);
     if (e == hipSuccess && !fwd_ws) e = mx_quantize_cols(w2, E, d, f, w.w2t.codes, w.w2t.scales, hs);
-    if (e == hipSuccess) e = gemm_mx_dact(*s, *plan, pi, w.doq, w2t, h_saved, w.dh, w.dhq, w.ga, w.ds_part, hs);
+    if (e == hipSuccess) e = gemm_mx_dact(*s, *plan, pi, w.doq, w2t, h_saved, w.dhq, w.dh_t, w.ga_t, P, w.ds_part, hs);
     if (e == hipSuccess && !fwd_ws) e = mx_quantize_cols(w1, E, 2 * f, d, w.w1t.codes, w.w1t.scales, hs);
     // the token-axis quantiser reads x through the plan (a memory-bound pass: gathering is free)
     const void* xp = x_perm ? x_perm : fused ? x : w.xbuf;
     const int32_t* xg = (!x_perm && fused) ? tor : nullptr;
     if (e == hipSuccess && !x_perm && !fwd_ws && !fused) e = launch_permute_rows(*s, x, *plan, w.xbuf, hs);
-    if (e == hipSuccess) e = mx_quantize_tokens(w.dh, 2 * f, plan->offsets, w.pad_off, E, P, w.dh_t.codes, w.dh_t.scales, hs);
     if (e == hipSuccess && !fwd_ws)
       e = mx_quantize_tokens(xp, d, plan->offsets, w.pad_off, E, P, w.x_t.codes, w.x_t.scales, hs, xg);
-    if (e == hipSuccess) e = mx_quantize_tokens(w.ga, f, plan->offsets, w.pad_off, E, P, w.ga_t.codes, w.ga_t.scales, hs);
     if (e == hipSuccess) e = launch_wgrad_chunks(w.pad_off, E, w.wg.kch, w.wg, hs);
     if (e == hipSuccess) e = gemm_mx_wgrad(*s, w.wg, P, w.dh_t, 2 * f, x_t, d, dw1, hs);
     if (e == hipSuccess) e = launch_wgrad_reduce(w.wg, E, (int64_t)2 * f * d, dw1, hs);

@@ -45,6 +45,10 @@ MOE_DEV u32x4 lds_tr_frag(const char* p0, const char* p1) {
   return u32x4{x.x, x.y, y.x, y.y};
 }
 
+// compiler-only fence: the slab is accessed under different types (fp32 staging,
+// bf16 / packed stores); keeps the compiler from reordering those LDS accesses
+MOE_DEV void lds_fence() { asm volatile("" ::: "memory"); }
+
 // barrier without the compiler's implicit wait on every outstanding memory op;
 // the asm fences keep the compiler from moving LDS accesses across it
 MOE_DEV void cta_barrier() {
@@ -203,8 +207,14 @@ MOE_DEV void wave_epilogue(const Args& args, const TileCtx& ctx, f32x16 (&acc)[B
 #pragma unroll
         for (int c = 0; c < 8; ++c) dap[it][c] = src[c];
       }
+      lds_fence();                                 // the dA' reads above stay before the staging below
       T* dH = reinterpret_cast<T*>(args.C);
       T* gA = reinterpret_cast<T*>(args.C2);
+      // MXFP8: the sub-tile's dH (bf16, as stored) is staged in the slab (rows of
+      // 128 gate+up columns, pitch PB) for the token-axis pass below, gA kept packed
+      constexpr int PB = 2 * WTN + 8;
+      uint16_t* stage = reinterpret_cast<uint16_t*>(slab);
+      u32x4 gaq[IT];
 #pragma unroll
       for (int it = 0; it < IT; ++it) {
         const int u = lane + 64 * it;
@@ -213,12 +223,12 @@ MOE_DEV void wave_epilogue(const Args& args, const TileCtx& ctx, f32x16 (&acc)[B
         const int col = cbase + ch * 8;
         float part = 0.0f;
         const bool ok = grow < ctx.row_end && col < args.N;   // uniform over each lane quad
-        float dhg[8], dhu[8];
+        float dhg[8], dhu[8], ga[8];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) dhg[c] = dhu[c] = 0.0f;
+        for (int c = 0; c < 8; ++c) dhg[c] = dhu[c] = ga[c] = 0.0f;
         if (ok) {
           const float g = gv[it];
-          float hg[8], hu[8], ga[8];
+          float hg[8], hu[8];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             hg[2 * q] = __uint_as_float(hgv[it][q] << 16);
@@ -237,10 +247,12 @@ MOE_DEV void wave_epilogue(const Args& args, const TileCtx& ctx, f32x16 (&acc)[B
             dhu[c] = da * sl;
             ga[c] = g * a;
           }
-          T* drow = dH + (int64_t)grow * args.ldc;
-          Vec8<T>::store(drow + col, dhg);
-          Vec8<T>::store(drow + args.f + col, dhu);
-          Vec8<T>::store(gA + (int64_t)grow * args.ldc2 + col, ga);
+          if constexpr (EPI == EPI_DSWIGLU) {   // MXFP8 keeps dH and gA only as codes
+            T* drow = dH + (int64_t)grow * args.ldc;
+            Vec8<T>::store(drow + col, dhg);
+            Vec8<T>::store(drow + args.f + col, dhu);
+            Vec8<T>::store(gA + (int64_t)grow * args.ldc2 + col, ga);
+          }
         }
         if constexpr (EPI == EPI_DSWIGLU_MX) {
           // dH as stored (bf16), quantised along 2f: gate columns col.. and up
@@ -267,10 +279,71 @@ MOE_DEV void wave_epilogue(const Args& args, const TileCtx& ctx, f32x16 (&acc)[B
               args.q_scales[((ku >> 6) * args.q_srows + prow) * 2 + ((ku >> 5) & 1)] = (uint8_t)(Xu + 127);
             }
           }
+          // stage dH (bf16) for the token-axis pass (the dA' values were read from
+          // the slab before this loop; one wave, in-order LDS), keep gA (bf16)
+          u32x4 pg, pu;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            pg[q] = pack_bf2(dhg[2 * q], dhg[2 * q + 1]);
+            pu[q] = pack_bf2(dhu[2 * q], dhu[2 * q + 1]);
+            gaq[it][q] = pack_bf2(ga[2 * q], ga[2 * q + 1]);
+          }
+          *reinterpret_cast<u32x4*>(stage + rr * PB + ch * 8) = pg;
+          *reinterpret_cast<u32x4*>(stage + rr * PB + WTN + ch * 8) = pu;
         }
 #pragma unroll
         for (int o = 1; o < CPR; o <<= 1) part += __shfl_xor(part, o, 64);
         if (ch == 0 && grow < ctx.row_end) args.C3[(int64_t)(ctx.nt * WN + wn) * args.ldc3 + grow] = part;
+      }
+      if constexpr (EPI == EPI_DSWIGLU_MX) {
+        // along tokens: the sub-tile's 32 rows are one 32-position block of the
+        // expert-padded token axis (segments start at multiples of 64 and this
+        // block starts 32-aligned inside its segment); lane l quantises column l
+        // of each 64-column group from its 32 staged values.  Rows past the
+        // segment hold zeros; blocks past the padded segment are not written.
+        static_assert(WTN == 64 && CPR == 8, "one column per lane");
+        const int e = ctx.e;
+        const int rel = rbase + i * 32 - args.offsets[e];
+        const bool blk = rel < args.q_pad[e + 1] - args.q_pad[e];
+        const int64_t p0 = (int64_t)args.q_pad[e] + rel;
+        auto column = [&](const uint16_t* src, int pitch, uint8_t* codes, uint8_t* scales, int64_t srows,
+                          int64_t crow) {
+          float v[32];
+          float amax = 0.0f;
+#pragma unroll
+          for (int r = 0; r < 32; ++r) {
+            v[r] = __uint_as_float((uint32_t)src[r * pitch] << 16);
+            amax = fmaxf(amax, fabsf(v[r]));
+          }
+          const int X = mx_exponent(amax);
+          const float inv = pow2f(-X);
+          uint8_t* cp = codes + crow * args.t_len + p0;
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const uint2 lo = e4m3_8(v + 16 * q, inv), hi2 = e4m3_8(v + 16 * q + 8, inv);
+            *reinterpret_cast<u32x4*>(cp + 16 * q) = u32x4{lo.x, lo.y, hi2.x, hi2.y};
+          }
+          scales[((p0 >> 6) * srows + crow) * 2 + ((p0 >> 5) & 1)] = (uint8_t)(X + 127);
+        };
+        const int gc = cbase + lane;   // this lane's column of the gate (and gA) group
+        lds_fence();
+        __builtin_amdgcn_s_waitcnt(0xc07f);        // the staged dH is in the slab
+        if (blk && gc < args.N) {
+          column(stage + lane, PB, args.t_codes, args.t_scales, 2 * (int64_t)args.f, gc);
+          column(stage + WTN + lane, PB, args.t_codes, args.t_scales, 2 * (int64_t)args.f, args.f + gc);
+        }
+        lds_fence();
+        __builtin_amdgcn_s_waitcnt(0xc07f);        // dH read back before gA overwrites the slab
+        constexpr int PA = WTN + 8;
+#pragma unroll
+        for (int it = 0; it < IT; ++it) {
+          const int u = lane + 64 * it;
+          *reinterpret_cast<u32x4*>(stage + (u / CPR) * PA + (u % CPR) * 8) = gaq[it];
+        }
+        lds_fence();
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        if (blk && gc < args.N) column(stage + lane, PA, args.t2_codes, args.t2_scales, (int64_t)args.f, gc);
+        lds_fence();                               // read back before the next sub-tile's fp32 staging
       }
     } else {
 #pragma unroll

@@ -51,6 +51,9 @@ struct Args {
   // *_MX epilogues: MXFP8 codes [rows][q_ld] and stage-major scales [q_ld/64][q_srows][2] of the
   // quantised output, rows expert-padded (row r of expert e at r - offsets[e] + q_pad[e])
   uint8_t* q_codes; uint8_t* q_scales; int64_t q_ld; int64_t q_srows; const int32_t* q_pad;
+  // EPI_DSWIGLU_MX: dH and gA also along the token axis (the weight gradients' K): codes
+  // [2f][t_len] / [f][t_len] over expert-padded positions, scales [t_len/64][2f or f][2]
+  uint8_t* t_codes; uint8_t* t_scales; uint8_t* t2_codes; uint8_t* t2_scales; int64_t t_len;
   int M, N, K, E, f;
   int tilesM, tilesN;
   int total_static;             // GROUP_K / GROUP_NONE: number of logical tiles

@@ -87,21 +87,22 @@ hipError_t gemm_mx_down(const moe_shape& s, const moe_plan& p, const PlanInterna
 
 // w2t: W2 quantised along d, stored [E][f][d]
 hipError_t gemm_mx_dact(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const MxOperand& dout,
-                        const MxOperand& w2t, const void* h, void* dh, const MxOperand& dhq, void* ga, float* ds_part,
-                        hipStream_t st) {
+                        const MxOperand& w2t, const void* h, const MxOperand& dhq, const MxOperand& dh_t,
+                        const MxOperand& ga_t, int64_t P, float* ds_part, hipStream_t st) {
   Args a = base_args();
   a.A = dout.codes; a.lda = s.d;
   a.B = w2t.codes; a.ldb = s.d; a.b_estride = (int64_t)s.d_ff * s.d;
-  a.C = dh; a.ldc = 2 * s.d_ff;
-  a.C2 = ga; a.ldc2 = s.d_ff;
+  a.ldc = 2 * s.d_ff; a.ldc2 = s.d_ff;   // dH and gA exist only as codes (no bf16 copies)
   a.C3 = ds_part; a.ldc3 = max_rows(s);
   a.aux = h; a.ld_aux = 2 * s.d_ff;
   a.row_gate = p.gate_of_row;
   a.offsets = p.offsets;
   a.N = s.d_ff; a.K = s.d; a.E = s.E; a.f = s.d_ff;
   a.tile_prefix = pi.prefix128; a.tile_expert = pi.tile_e128;
-  // dH also in MXFP8 along 2f for the dX_perm GEMM
+  // dH in MXFP8 along 2f for the dX_perm GEMM, dH and gA along tokens for the weight gradients
   a.q_codes = dhq.codes; a.q_scales = dhq.scales; a.q_ld = 2 * s.d_ff; a.q_srows = dhq.srows; a.q_pad = dhq.pad;
+  a.t_codes = dh_t.codes; a.t_scales = dh_t.scales; a.t2_codes = ga_t.codes; a.t2_scales = ga_t.scales;
+  a.t_len = P;
   MxArgs m{dout.scales, dout.srows, dout.pad, w2t.scales, w2t.srows, (int64_t)s.d_ff};
   return run_mx<GROUP_M, EPI_DSWIGLU_MX>(a, m, m_tiles(s) * ceil_div(a.N, 512), st);
 }

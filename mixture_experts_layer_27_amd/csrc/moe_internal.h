@@ -142,8 +142,8 @@ hipError_t gemm_mx_up_swiglu(const moe_shape& s, const moe_plan& p, const PlanIn
 hipError_t gemm_mx_down(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const MxOperand& act,
                         const MxOperand& w2, void* y, hipStream_t st);
 hipError_t gemm_mx_dact(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const MxOperand& dout,
-                        const MxOperand& w2t, const void* h, void* dh, const MxOperand& dhq, void* ga, float* ds_part,
-                        hipStream_t st);
+                        const MxOperand& w2t, const void* h, const MxOperand& dhq, const MxOperand& dh_t,
+                        const MxOperand& ga_t, int64_t P, float* ds_part, hipStream_t st);
 hipError_t gemm_mx_dx_perm(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const MxOperand& dh,
                            const MxOperand& w1t, void* dx_perm, hipStream_t st);
 hipError_t gemm_mx_wgrad(const moe_shape& s, const WgradChunks& w, int64_t P, const MxOperand& lhs, int M,
