@@ -232,9 +232,21 @@ hipError_t gemm_router_logits(const moe_shape& s, const void* x, const void* wg,
   a.bias = bias;
   a.aux = noise; a.ld_aux = s.E;         // routing noise [T, E] or nullptr
   a.M = s.T; a.N = s.E; a.K = s.d;
+  // 32-row tiles: T/32 blocks keep every CU busy with two of them (the K loop is
+  // latency-bound at this width); all E columns in one tile read each x row once.
+  a.tilesM = ceil_div(s.T, 32);
+  if (s.act == MOE_BF16) {
+    if (s.E > 64) {
+      a.tilesN = ceil_div(s.E, 128);
+      a.total_static = a.tilesM * a.tilesN;
+      return run<bf16_t, 32, 128, 1, 4, true, true, GROUP_NONE, EPI_LOGITS>(a, a.total_static, st);
+    }
+    a.tilesN = 1;
+    a.total_static = a.tilesM;
+    return run<bf16_t, 32, 64, 1, 2, true, true, GROUP_NONE, EPI_LOGITS>(a, a.total_static, st);
+  }
   a.tilesM = ceil_div(s.T, 128); a.tilesN = ceil_div(s.E, 64);
   a.total_static = a.tilesM * a.tilesN;
-  if (s.act == MOE_BF16) return run<bf16_t, 128, 64, 4, 1, true, true, GROUP_NONE, EPI_LOGITS>(a, a.total_static, st);
   return run<float, 128, 64, 4, 1, true, true, GROUP_NONE, EPI_LOGITS>(a, a.total_static, st);
 }
 
