@@ -240,8 +240,11 @@ __global__ __launch_bounds__(256) void quantize_dual_kernel(const bf16_t* __rest
                                                            const int32_t* __restrict__ gather) {
   constexpr int VS = 136;   // value tile row stride (bf16 elements; rows stay 16-byte aligned)
   constexpr int CS = 144;   // code tile row stride (bytes): 16 consecutive columns hit distinct banks
+  // the code tile takes the value tile's place once every column has been read:
+  // 35 KB of LDS per block, four blocks per CU
   __shared__ __attribute__((aligned(16))) uint16_t vt[128 * VS];
-  __shared__ __attribute__((aligned(16))) uint8_t ct[128 * CS];
+  uint8_t* const ct = reinterpret_cast<uint8_t*>(vt);
+  static_assert(128 * CS <= 128 * VS * 2, "code tile fits in the value tile");
   __shared__ uint8_t sc[128][4];
   const int t = threadIdx.x;
   const int c0 = blockIdx.x * 128;
@@ -319,21 +322,23 @@ __global__ __launch_bounds__(256) void quantize_dual_kernel(const bf16_t* __rest
   {   // along positions: column c, positions [64h, 64h + 64) = two blocks
     const int c = t & 127, h = t >> 7;
     int Xb[2];
+    float v[2][32];
+#pragma unroll
+    for (int b = 0; b < 2; ++b)
+#pragma unroll
+      for (int i = 0; i < 32; ++i) v[b][i] = __uint_as_float((uint32_t)vt[(64 * h + 32 * b + i) * VS + c] << 16);
+    __syncthreads();   // all values are in registers: the code tile may overwrite them
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      float v[32];
       float amax = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 32; ++i) {
-        v[i] = __uint_as_float((uint32_t)vt[(64 * h + 32 * b + i) * VS + c] << 16);
-        amax = fmaxf(amax, fabsf(v[i]));
-      }
+      for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[b][i]));
       const int X = mx_exponent(amax);
       const float inv = pow2f(-X);
       uint8_t* cp = ct + c * CS + 64 * h + 32 * b;
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
-        const uint2 lo = e4m3_8(v + 16 * q, inv), hi2 = e4m3_8(v + 16 * q + 8, inv);
+        const uint2 lo = e4m3_8(v[b] + 16 * q, inv), hi2 = e4m3_8(v[b] + 16 * q + 8, inv);
         *reinterpret_cast<u32x4*>(cp + 16 * q) = u32x4{lo.x, lo.y, hi2.x, hi2.y};
       }
       Xb[b] = X;
