@@ -26,24 +26,25 @@ namespace {
 
 MOE_DEV bool better(float av, int ae, float bv, int be) { return av > bv || (av == bv && ae < be); }
 
-// One wave per token; a wave takes TPW tokens in turn (4*TPW per block).  Lane l
-// holds experts l, l+64, ...  With ROUND (TPW = 16, 64 tokens per block) the
-// block also writes the full softmax expert-major (probs_t) and the selection
-// bitmap expert-major (sel_t), transposed through LDS.
-template <int V, bool ROUND, int TPW>
-__global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int T, int E, int k,
+// One wave per token; a wave takes TPW tokens in turn (NT/64*TPW per block).  Lane
+// l holds experts l, l+64, ...  With ROUND (64 tokens per block: sixteen waves of
+// four) the block also writes the full softmax expert-major (probs_t) and the
+// selection bitmap expert-major (sel_t), transposed through LDS.
+template <int V, bool ROUND, int TPW, int NT>
+__global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ logits, int T, int E, int k,
                                                   int32_t* __restrict__ topk_idx, float* __restrict__ topk_gate,
                                                   uint32_t* __restrict__ keep_bits, int words,
                                                   float* __restrict__ probs_t, uint32_t* __restrict__ sel_t,
                                                   int wordsT, int gate_all) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  float* pt = reinterpret_cast<float*>(smem);                       // [E][64]
-  uint32_t* sel = reinterpret_cast<uint32_t*>(smem + (size_t)E * 64 * 4);  // [E][2]
+  float* pt = reinterpret_cast<float*>(smem);                       // [E][65]: a wave's writes (one expert
+                                                                    // per lane) fall in distinct banks
+  uint32_t* sel = reinterpret_cast<uint32_t*>(smem + (size_t)E * 65 * 4);  // [E][2]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  static_assert(!ROUND || TPW == 16, "the transposed writes assume 64 tokens per block");
-  const int t0 = blockIdx.x * 4 * TPW;
+  static_assert(!ROUND || (NT / 64) * TPW == 64, "the transposed writes assume 64 tokens per block");
+  const int t0 = blockIdx.x * (NT / 64) * TPW;
   if constexpr (ROUND) {
-    for (int i = threadIdx.x; i < E * 2; i += 256) sel[i] = 0u;
+    for (int i = threadIdx.x; i < E * 2; i += NT) sel[i] = 0u;
     __syncthreads();
   }
   for (int it = 0; it < TPW; ++it) {
@@ -115,7 +116,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
 #pragma unroll
       for (int v = 0; v < V; ++v) {
         int e = lane + 64 * v;
-        if (e < E) pt[e * 64 + tl] = expf(z[v] - sel_z[0]) / s;
+        if (e < E) pt[e * 65 + tl] = expf(z[v] - sel_z[0]) / s;
       }
       if (lane < k) {
         int ej = sel_e[0];
@@ -127,11 +128,11 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   }
   if constexpr (ROUND) {
     __syncthreads();
-    for (int i = threadIdx.x; i < E * 64; i += 256) {
+    for (int i = threadIdx.x; i < E * 64; i += NT) {
       int e = i >> 6, tl = i & 63;
-      if (t0 + tl < T) probs_t[(int64_t)e * T + t0 + tl] = pt[e * 64 + tl];
+      if (t0 + tl < T) probs_t[(int64_t)e * T + t0 + tl] = pt[e * 65 + tl];
     }
-    for (int i = threadIdx.x; i < E * 2; i += 256) {
+    for (int i = threadIdx.x; i < E * 2; i += NT) {
       int e = i >> 1, h = i & 1;
       int wi = blockIdx.x * 2 + h;
       if (wi < wordsT) sel_t[(int64_t)e * wordsT + wi] = sel[i];
@@ -191,30 +192,78 @@ __global__ __launch_bounds__(256) void plan_count_kernel(const uint32_t* __restr
   if (threadIdx.x == 0) blk_tok[blockIdx.x] = red[0];
 }
 
+// Inclusive prefix sum across the 64 lanes of a wave.
+MOE_DEV int wave_incl_scan(int x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+// Exclusive scan of one int per thread over a 1024-thread block (sh: >= 17
+// ints); returns the thread's exclusive prefix, *total the block's sum.
+MOE_DEV int block_excl_scan_1024(int x, int* sh, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int incl = wave_incl_scan(x);
+  if (lane == 63) sh[wave] = incl;
+  __syncthreads();
+  if (wave == 0) {
+    const int w = lane < 16 ? sh[lane] : 0;
+    const int wi = wave_incl_scan(w);
+    if (lane < 16) sh[lane] = wi - w;
+    if (lane == 15) sh[16] = wi;
+  }
+  __syncthreads();
+  const int r = sh[wave] + incl - x;
+  *total = sh[16];
+  __syncthreads();
+  return r;
+}
+
 // Exclusive scan of n ints in place by one 1024-thread block; returns the total.
-MOE_DEV int block_scan_inplace(int32_t* a, int64_t n, int* sh) {
-  const int tid = threadIdx.x;
-  const int64_t per = (n + 1023) / 1024;
-  const int64_t lo = min((int64_t)tid * per, n), hi = min(lo + per, n);
-  int s = 0;
-  for (int64_t i = lo; i < hi; ++i) s += a[i];
-  sh[tid] = s;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {     // inclusive Hillis-Steele
-    int v = (tid >= o) ? sh[tid - o] : 0;
+// Batches of 16 chunks of 1024 elements: each thread loads one element of every
+// chunk (coalesced, all 16 loads in flight), every chunk is scanned across the
+// waves with lane shuffles, then one pass over the 16 x 16 wave totals.
+MOE_DEV int block_scan_inplace(int32_t* a, int64_t n, int* sh /* >= 272 ints */) {
+  constexpr int B = 16;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int carry = 0;
+  for (int64_t base = 0; base < n; base += (int64_t)B * 1024) {
+    int v[B], incl[B];
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      const int64_t i = base + (int64_t)j * 1024 + tid;
+      v[j] = i < n ? a[i] : 0;
+    }
+#pragma unroll
+    for (int j = 0; j < B; ++j) incl[j] = wave_incl_scan(v[j]);
+    if (lane == 63) {
+#pragma unroll
+      for (int j = 0; j < B; ++j) sh[j * 16 + wave] = incl[j];
+    }
     __syncthreads();
-    sh[tid] += v;
+    if (wave == 0) {   // exclusive scan of the 256 wave totals in (chunk, wave) order, 4 per lane
+      int q[4], sum = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) { q[u] = sh[4 * lane + u]; sum += q[u]; }
+      int run = wave_incl_scan(sum) - sum;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) { sh[4 * lane + u] = run; run += q[u]; }
+      if (lane == 63) sh[256] = run;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      const int64_t i = base + (int64_t)j * 1024 + tid;
+      if (i < n) a[i] = carry + sh[j * 16 + wave] + incl[j] - v[j];
+    }
+    carry += sh[256];
     __syncthreads();
   }
-  int run = sh[tid] - s;
-  int total = sh[1023];
-  for (int64_t i = lo; i < hi; ++i) {
-    int v = a[i];
-    a[i] = run;
-    run += v;
-  }
-  __syncthreads();
-  return total;
+  return carry;
 }
 
 __global__ __launch_bounds__(1024) void plan_scan_kernel(int E, int nblk, int32_t* __restrict__ hist,
@@ -258,18 +307,11 @@ __global__ __launch_bounds__(1024) void plan_scan_kernel(int E, int nblk, int32_
   }
   // 128-row m-tile prefix over the experts (block scan), then each expert's tiles
   const int tiles = (cnt + 127) / 128;
-  sh[e] = tiles;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    const int v = (e >= o) ? sh[e - o] : 0;
-    __syncthreads();
-    sh[e] += v;
-    __syncthreads();
-  }
+  int all_tiles;
+  const int p0 = block_excl_scan_1024(tiles, sh, &all_tiles);
   if (e < E) {
-    const int p0 = sh[e] - tiles;
     pre128[e] = p0;
-    if (e == E - 1) pre128[E] = sh[e];
+    if (e == E - 1) pre128[E] = p0 + tiles;
     for (int j = 0; j < tiles; ++j) tile_e[p0 + j] = e;
   }
 }
@@ -282,12 +324,14 @@ __global__ __launch_bounds__(256) void plan_scatter_kernel(
     int32_t* __restrict__ row_of_slot, int32_t* __restrict__ tok_ptr, int32_t* __restrict__ tok_rows) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   BlockMasks bm{reinterpret_cast<uint32_t*>(smem), E};
+  int* hb = reinterpret_cast<int*>(smem + (size_t)4 * E * 2 * 4);   // [E] this block's first row per expert
   __shared__ int sc[256];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t = blockIdx.x * 256 + threadIdx.x;
   const bool valid = t < T;
+  for (int e = threadIdx.x; e < E; e += 256) hb[e] = hist[(int64_t)e * nblk + blockIdx.x];
   int cnt;
-  build_masks(bm, keep_bits, words, t, valid, &cnt);
+  build_masks(bm, keep_bits, words, t, valid, &cnt);   // (its barriers also publish hb)
   // token -> first row slot in tok_rows (block base + exclusive scan of counts)
   sc[threadIdx.x] = cnt;
   __syncthreads();
@@ -303,7 +347,7 @@ __global__ __launch_bounds__(256) void plan_scatter_kernel(
   tok_ptr[t] = tbase;
   const uint32_t ltmask = (1u << (lane & 31)) - 1u;
   auto row_of = [&](int e) -> int {
-    int r = hist[(int64_t)e * nblk + blockIdx.x];
+    int r = hb[e];
     for (int w = 0; w < wave; ++w) r += __popc(bm.at(w, e, 0)) + __popc(bm.at(w, e, 1));
     if (lane >= 32) r += __popc(bm.at(wave, e, 0));
     r += __popc(bm.at(wave, e, lane >> 5) & ltmask);
@@ -312,6 +356,9 @@ __global__ __launch_bounds__(256) void plan_scatter_kernel(
   float ptop = 0.0f;
   if (prob_gates && !gate_all)
     for (int j = 0; j < k; ++j) ptop += probs_t[(int64_t)topk_idx[(int64_t)t * k + j] * T + t];
+  int tk[8];   // k <= 8
+#pragma unroll
+  for (int j = 0; j < 8; ++j) tk[j] = j < k ? topk_idx[(int64_t)t * k + j] : -1;
   for (int j = 0; j < k; ++j) row_of_slot[(int64_t)t * k + j] = -1;
   int n = 0;
   for (int w = 0; w < words; ++w) {
@@ -322,8 +369,9 @@ __global__ __launch_bounds__(256) void plan_scatter_kernel(
       int e = w * 32 + b;
       int r = row_of(e);
       int slot = -1;
-      for (int j = 0; j < k; ++j)
-        if (topk_idx[(int64_t)t * k + j] == e) slot = j;
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (tk[j] == e) slot = j;
       float g;
       if (slot >= 0) {
         g = topk_gate[(int64_t)t * k + slot];
@@ -343,7 +391,11 @@ __global__ __launch_bounds__(256) void plan_scatter_kernel(
 
 // Token rounding, one 1024-thread block per expert: radix-select the cut among
 // the candidates (selected pairs when dropping, unselected tokens when adding)
-// and flip their keep bits.
+// and flip their keep bits.  Thread i owns a contiguous run of tokens (the tie
+// rule needs token order); the column sits in LDS with one pad word per 32
+// tokens, so the runs of consecutive threads fall in different banks.
+MOE_DEV int rs_pad(int t) { return t + (t >> 5); }
+
 __global__ __launch_bounds__(1024) void round_select_kernel(const float* __restrict__ probs_t,
                                                            const uint32_t* __restrict__ sel_t, int wordsT,
                                                            const int32_t* __restrict__ counts_raw, int T, int tile,
@@ -351,9 +403,9 @@ __global__ __launch_bounds__(1024) void round_select_kernel(const float* __restr
                                                            bool col_in_lds) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   __shared__ int hist[256];
-  __shared__ int sh[1024];
+  __shared__ int sh[32];
   __shared__ int bc[2];
-  const int e = blockIdx.x, tid = threadIdx.x;
+  const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = counts_raw[e];
   int target = ((n + tile / 2) / tile) * tile;
   if (target > T) target = (n / tile) * tile;
@@ -362,10 +414,9 @@ __global__ __launch_bounds__(1024) void round_select_kernel(const float* __restr
   int c = drop ? n - target : target - n;
   const uint32_t* selrow = sel_t + (int64_t)e * wordsT;
   const float* col = probs_t + (int64_t)e * T;
+  float* lc = reinterpret_cast<float*>(smem);
   if (col_in_lds) {
-    float* lc = reinterpret_cast<float*>(smem);
-    for (int i = tid; i < T; i += 1024) lc[i] = col[i];
-    col = lc;
+    for (int i = tid; i < T; i += 1024) lc[rs_pad(i)] = col[i];
     __syncthreads();
   }
   auto is_cand = [&](int t) -> bool {
@@ -373,14 +424,14 @@ __global__ __launch_bounds__(1024) void round_select_kernel(const float* __restr
     return drop ? s : !s;
   };
   auto key_of = [&](int t) -> uint32_t {
-    uint32_t b = __float_as_uint(col[t]);   // P >= 0: bit order = value order
+    uint32_t b = __float_as_uint(col_in_lds ? lc[rs_pad(t)] : col[t]);   // P >= 0: bit order = value order
     return drop ? b : ~b;                   // ascending key = order of removal / addition
   };
   const int per = (T + 1023) / 1024;
   const int lo = min(tid * per, T), hi = min(lo + per, T);
   uint32_t prefix = 0u, mask = 0u;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    for (int i = tid; i < 256; i += 1024) hist[i] = 0;
+    if (tid < 256) hist[tid] = 0;
     __syncthreads();
     for (int t = lo; t < hi; ++t) {
       if (!is_cand(t)) continue;
@@ -388,14 +439,16 @@ __global__ __launch_bounds__(1024) void round_select_kernel(const float* __restr
       if ((kk & mask) == prefix) atomicAdd(&hist[(kk >> shift) & 255], 1);
     }
     __syncthreads();
-    if (tid == 0) {
-      int cum = 0, dg = 255;
-      for (int d = 0; d < 256; ++d) {
-        if (cum + hist[d] >= c) { dg = d; break; }
-        cum += hist[d];
+    if (wave == 0) {   // the digit where the running count reaches c: four digits per lane
+      int h[4], sum = 0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) { h[u] = hist[4 * lane + u]; sum += h[u]; }
+      int cum = wave_incl_scan(sum) - sum;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (cum < c && cum + h[u] >= c) { bc[0] = 4 * lane + u; bc[1] = c - cum; }
+        cum += h[u];
       }
-      bc[0] = dg;
-      bc[1] = c - cum;
     }
     __syncthreads();
     prefix |= (uint32_t)bc[0] << shift;
@@ -407,16 +460,8 @@ __global__ __launch_bounds__(1024) void round_select_kernel(const float* __restr
   int ties = 0;
   for (int t = lo; t < hi; ++t)
     if (is_cand(t) && key_of(t) == prefix) ++ties;
-  sh[tid] = ties;
-  __syncthreads();
-  for (int o = 1; o < 1024; o <<= 1) {
-    int v = (tid >= o) ? sh[tid - o] : 0;
-    __syncthreads();
-    sh[tid] += v;
-    __syncthreads();
-  }
-  const int total_ties = sh[1023];
-  int rank = sh[tid] - ties;
+  int total_ties;
+  int rank = block_excl_scan_1024(ties, sh, &total_ties);
   const uint32_t bit = 1u << (e & 31);
   for (int t = lo; t < hi; ++t) {
     if (!is_cand(t)) continue;
@@ -553,12 +598,12 @@ hipError_t launch_topk(const moe_shape& s, const moe_plan& p, const PlanInternal
                        hipStream_t st) {
   const int grid = rounding ? ceil_div(s.T, 64) : ceil_div(s.T, 4);
   const int wordsT = ceil_div(s.T, 32);
-  size_t lds = rounding ? (size_t)s.E * 64 * 4 + (size_t)s.E * 8 : 0;
+  size_t lds = rounding ? (size_t)s.E * 65 * 4 + (size_t)s.E * 8 : 0;
 #define MOE_TOPK(V, R)                                                                                  \
   do {                                                                                                 \
-    auto kern = topk_kernel<V, R, R ? 16 : 1>;                                                                     \
+    auto kern = topk_kernel<V, R, R ? 4 : 1, R ? 1024 : 256>;                                                      \
     if (lds > 65536) hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), lds, st, p.logits, s.T, s.E, s.k, p.topk_idx,      \
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(R ? 1024 : 256), lds, st, p.logits, s.T, s.E, s.k, p.topk_idx, \
                        p.topk_gate, p.keep_bits, pi.words, p.probs_t, pi.sel_t, wordsT,                \
                        (int)(s.gate_mode == MOE_GATE_ALL));                                             \
   } while (0)
@@ -576,7 +621,7 @@ hipError_t launch_plan_build(const moe_shape& s, const moe_plan& p, const PlanIn
                      pi.nblk, pi.hist, pi.blk_tok);
   hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(1024), 0, st, s.E, pi.nblk, pi.hist, pi.blk_tok, p.counts,
                      raw ? p.counts_raw : nullptr, p.offsets, pi.prefix128, pi.tile_e128, raw ? p.aux : nullptr);
-  hipLaunchKernelGGL(plan_scatter_kernel, dim3(pi.nblk), dim3(256), lds, st, p.keep_bits, s.T, s.E, s.k,
+  hipLaunchKernelGGL(plan_scatter_kernel, dim3(pi.nblk), dim3(256), lds + (size_t)s.E * 4, st, p.keep_bits, s.T, s.E, s.k,
                      pi.words, pi.nblk, pi.hist, pi.blk_tok, p.topk_idx, p.topk_gate, p.probs_t,
                      with_prob_gates, s.gate_mode == MOE_GATE_ALL, p.token_of_row, p.expert_of_row, p.gate_of_row, p.row_of_slot, p.tok_ptr,
                      p.tok_rows);
@@ -606,8 +651,8 @@ hipError_t launch_router_losses(const moe_shape& s, const moe_plan& p, const Pla
 }
 
 hipError_t launch_round_select(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, hipStream_t st) {
-  const size_t col = (size_t)s.T * 4;
-  const bool in_lds = col <= 128 * 1024;
+  const size_t col = (size_t)(s.T + s.T / 32 + 1) * 4;   // padded column
+  const bool in_lds = col <= 144 * 1024;
   const size_t lds = in_lds ? col : 0;
   if (lds > 65536)
     hipFuncSetAttribute((const void*)round_select_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
