@@ -59,9 +59,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default="fine_e128")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--fused-gather", action="store_true",
-                    help="forward reads x through the plan inside the expert GEMMs (no x_perm); the backward "
-                         "then permutes x itself")
+    ap.add_argument("--fused-gather", choices=("auto", "on", "off"), default="auto",
+                    help="on: the forward reads x through the plan inside the expert GEMMs (bf16) or the MXFP8 "
+                         "quantiser (no x_perm); off: x is permuted once and x_perm handed to the backward; "
+                         "auto (default): on for MXFP8 expert GEMMs, off for bf16")
     ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0 = automatic)")
     ap.add_argument("--out", default=None, help="also append the JSON line to this file")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -134,10 +135,11 @@ def main():
     cfg = configs.get(a.config)
     print(f"[bench] generating {cfg.name} inputs", file=sys.stderr, flush=True)
     g = synth.generate(cfg)
-    # default: permute x once and hand x_perm to the backward (the backward reads dout through
-    # the plan inside its GEMMs either way); --fused-gather moves the forward permutation into
-    # the expert GEMMs' loads instead
-    fused = a.fused_gather and cfg.act == "bf16" and cfg.T * cfg.d * 2 < 2 ** 31
+    # bf16 default: permute x once and hand x_perm to the backward (the backward reads dout through
+    # the plan inside its GEMMs either way).  MXFP8 default: the forward quantiser reads x through
+    # the plan (it writes both code orientations the backward reuses, so x_perm is never needed)
+    want = a.fused_gather == "on" or (a.fused_gather == "auto" and cfg.gemm == "mxfp8")
+    fused = want and cfg.act == "bf16" and cfg.T * cfg.d * 2 < 2 ** 31
     run = binding.LayerRun(cfg, g, fused_gather=fused)
     s = run.s
     stream = torch.cuda.current_stream()
