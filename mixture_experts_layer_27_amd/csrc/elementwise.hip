@@ -123,7 +123,7 @@ __global__ __launch_bounds__(256) void router_dx_kernel(const T* __restrict__ dx
   constexpr int CL = 4;                       // column chunks per lane per pass
   const int vec = d / EV;
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));   // wave-uniform
   if (t >= T_) return;
   auto add = [&](float* acc, const u32x4& v, float w) {
     if constexpr (sizeof(T) == 2) {
@@ -145,25 +145,33 @@ __global__ __launch_bounds__(256) void router_dx_kernel(const T* __restrict__ dx
     for (int j = 0; j < CL; ++j)
 #pragma unroll
       for (int q = 0; q < EV; ++q) acc[j][q] = 0.0f;
-    for (int p = p0; p < p1; ++p) {           // rows in ascending order
-      const int r = tok_rows[p];
-      const int e = expert_of_row[r];
-      const float z = dxr ? 0.0f : dzt[e];
-      u32x4 v[CL], w[CL];
+    for (int p = p0; p < p1; p += 2) {        // rows in ascending order, two with their loads in flight
+      const bool two = p + 1 < p1;
+      const int r0 = tok_rows[p], r1 = two ? tok_rows[p + 1] : r0;
+      const int e0 = expert_of_row[r0], e1 = expert_of_row[r1];
+      const float z0 = dxr ? 0.0f : dzt[e0], z1 = dxr ? 0.0f : dzt[e1];
+      u32x4 v0[CL], w0[CL], v1[CL], w1[CL];
 #pragma unroll
       for (int j = 0; j < CL; ++j) {
         const int c = cb + lane + 64 * j;
+        v0[j] = w0[j] = v1[j] = w1[j] = u32x4{0u, 0u, 0u, 0u};
         if (c < vec) {
-          v[j] = ldg16(dx_perm + (int64_t)r * d + c * EV);
-          w[j] = dxr ? u32x4{0u, 0u, 0u, 0u} : ldg16(wg + (int64_t)e * d + c * EV);
-        } else {
-          v[j] = w[j] = u32x4{0u, 0u, 0u, 0u};
+          v0[j] = ldg16(dx_perm + (int64_t)r0 * d + c * EV);
+          if (!dxr) w0[j] = ldg16(wg + (int64_t)e0 * d + c * EV);
+          if (two) {
+            v1[j] = ldg16(dx_perm + (int64_t)r1 * d + c * EV);
+            if (!dxr) w1[j] = ldg16(wg + (int64_t)e1 * d + c * EV);
+          }
         }
       }
 #pragma unroll
       for (int j = 0; j < CL; ++j) {
-        add(acc[j], v[j], 1.0f);
-        add(acc[j], w[j], z);
+        add(acc[j], v0[j], 1.0f);
+        add(acc[j], w0[j], z0);
+        if (two) {
+          add(acc[j], v1[j], 1.0f);
+          add(acc[j], w1[j], z1);
+        }
       }
     }
     if (dxr) {
