@@ -223,17 +223,23 @@ MOE_DEV void big_tile(const Args& args, const TileCtx& ctx, char* smem) {
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
+  // TMV: how many of the wave's four 32-row sub-tiles hold rows of the segment.
+  // Sub-tiles wholly past the segment's last row skip their fragment reads and
+  // MFMAs (their accumulators stay zero and are never stored); the operand
+  // loads, LDS writes and barriers are the same for every wave.
+  auto run_loop = [&](auto tmv_c) {
+  constexpr int TMV = decltype(tmv_c)::value;
   auto frags = [&](const char* as, int ks, u32x4 (&af)[TM], u32x4 (&bfr)[TN]) {
     const char* bs = as + ASZ;
     const int kb = ks * 16 + (lane >> 5) * 8 + ((lane & 15) >> 2);       // MN: first k row of the lane
     const int cb = (((lane >> 4) & 1) * 16 + 4 * (lane & 3)) * 2;       // MN: byte column of the lane
     if constexpr (AKC) {
 #pragma unroll
-      for (int i = 0; i < TM; ++i)
+      for (int i = 0; i < TMV; ++i)
         af[i] = *reinterpret_cast<const u32x4*>(as + kc_offk<64>(wm * WTM + i * 32 + (lane & 31), ks * 2 + (lane >> 5)));
     } else {
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
+      for (int i = 0; i < TMV; ++i) {
         const int byte = (wm * WTM + i * 32) * 2 + cb;
         af[i] = lds_tr_frag(as + mn_off<BM>(kb, byte), as + mn_off<BM>(kb + 4, byte));
       }
@@ -252,14 +258,13 @@ MOE_DEV void big_tile(const Args& args, const TileCtx& ctx, char* smem) {
   };
   auto mma = [&](const u32x4 (&af)[TM], const u32x4 (&bfr)[TN]) {
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TMV; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) Mma<T>::run(acc[i][j], af[i], bfr[j]);
   };
-
   const int kext = (GROUP == GROUP_M) ? args.K : (ctx.k_end - ctx.k_begin);
   const int nk = kext > 0 ? (kext + BK - 1) / BK : 0;
-  constexpr int NR = (AKC ? TM : 2 * TM) + (BKC ? TN : 2 * TN);   // LDS reads per k16 step
+  constexpr int NR = (AKC ? TMV : 2 * TMV) + (BKC ? TN : 2 * TN);   // LDS reads per k16 step
   u32x4 a0[TM], b0[TN], a1[TM], b1[TN];
   // stage loads, in stage order (the gathered operands fetch their rows one stage ahead)
   auto load_a = [&](int kt) {
@@ -286,19 +291,19 @@ MOE_DEV void big_tile(const Args& args, const TileCtx& ctx, char* smem) {
     frags(as, 3, a1, b1);
     mma(a0, b0);
 #pragma unroll
-    for (int i = 0; i < TM * TN; ++i) {          // block 1: MFMA + fragment read
+    for (int i = 0; i < TMV * TN; ++i) {          // block 1: MFMA + fragment read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
 #pragma unroll
-    for (int i = 0; i < TM * TN; ++i) {          // block 2: MFMA + LDS write + the load that refills
+    for (int i = 0; i < TMV * TN; ++i) {          // block 2: MFMA + LDS write + the load that refills
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // its registers (+ fragment read)
       if (i < ra.L + rb.L) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
       if (i < ra.L + rb.L) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
       if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
 #pragma unroll
-    for (int i = 0; i < TM * TN; ++i) {          // block 3: MFMA + fragment read
+    for (int i = 0; i < TMV * TN; ++i) {          // block 3: MFMA + fragment read
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
@@ -307,10 +312,20 @@ MOE_DEV void big_tile(const Args& args, const TileCtx& ctx, char* smem) {
     frags(an, 0, a0, b0);
     mma(a1, b1);
 #pragma unroll
-    for (int i = 0; i < TM * TN; ++i) {          // block 4: MFMA + the next stage's first fragments
+    for (int i = 0; i < TMV * TN; ++i) {          // block 4: MFMA + the next stage's first fragments
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
       if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
     }
+  }
+  };
+  if constexpr (GROUP == GROUP_M) {
+    const int valid = min(BM, ctx.row_end - ctx.row_begin) - wm * WTM;   // >= 1 by the tile decode
+    if (valid > 96) run_loop(std::integral_constant<int, 4>{});
+    else if (valid > 64) run_loop(std::integral_constant<int, 3>{});
+    else if (valid > 32) run_loop(std::integral_constant<int, 2>{});
+    else run_loop(std::integral_constant<int, 1>{});
+  } else {
+    run_loop(std::integral_constant<int, TM>{});
   }
   wave_epilogue<BM, BN, WM, WN, GROUP, EPI>(args, ctx, acc, smem);
 }
