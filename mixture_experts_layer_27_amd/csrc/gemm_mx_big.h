@@ -134,15 +134,19 @@ MOE_DEV void mx_big_tile(const Args& args, const MxArgs& mx, const TileCtx& ctx,
     const u32x4 hi = *reinterpret_cast<const u32x4*>(base + kc_offk<64>(row, 4 * s + 2 + g));
     return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
   };
+  // TMV: the wave's 32-row sub-tiles that hold rows of the segment; the others
+  // skip their fragment reads and MFMAs (zero accumulators, never stored).
+  auto run_loop = [&](auto tmv_c) {
+  constexpr int TMV = decltype(tmv_c)::value;
   auto step = [&](const char* as, int s, const int (&sa)[TM], const int (&sb)[TN]) {
     const char* bs = as + ASZ;
     i32x8 af[TM], bf[TN];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) af[i] = frag(as, wm * WTM + i * 32 + (lane & 31), s);
+    for (int i = 0; i < TMV; ++i) af[i] = frag(as, wm * WTM + i * 32 + (lane & 31), s);
 #pragma unroll
     for (int j = 0; j < TN; ++j) bf[j] = frag(bs, wn * WTN + j * 32 + (lane & 31), s);
 #pragma unroll
-    for (int i = 0; i < TM; ++i)
+    for (int i = 0; i < TMV; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0, 0, sa[i], 0, sb[j]);
@@ -174,6 +178,16 @@ MOE_DEV void mx_big_tile(const Args& args, const MxArgs& mx, const TileCtx& ctx,
 #pragma unroll
       for (int j = 0; j < TN; ++j) sb[s][j] = nb[s][j];
     }
+  }
+  };
+  if constexpr (GROUP == GROUP_M && EPI != EPI_DSWIGLU_MX) {   // (the dA' epilogue leaves no registers for it)
+    const int valid = a_rows - wm * WTM;   // >= 1 by the tile decode
+    if (valid > 96) run_loop(std::integral_constant<int, 4>{});
+    else if (valid > 64) run_loop(std::integral_constant<int, 3>{});
+    else if (valid > 32) run_loop(std::integral_constant<int, 2>{});
+    else run_loop(std::integral_constant<int, 1>{});
+  } else {
+    run_loop(std::integral_constant<int, TM>{});
   }
   wave_epilogue<BM, BN, WM, WN, GROUP, EPI>(args, ctx, acc, smem);
 }
