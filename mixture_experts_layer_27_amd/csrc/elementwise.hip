@@ -379,11 +379,27 @@ __global__ __launch_bounds__(256) void wgrad_chunks_kernel(const int32_t* __rest
 // dW[e] += partial slots of e, in slot order (fixed order: deterministic).
 // Every block walks all experts (those without partial slots are skipped at
 // once), so a heavily loaded expert's partials are spread over the whole grid.
+// The experts that have partial slots are listed in LDS first (E <= 256, one
+// thread each; the list order does not matter, each expert's sum is its own).
 __global__ __launch_bounds__(256) void wgrad_reduce_kernel(float* __restrict__ dw, const float* __restrict__ part,
                                                           const int2* __restrict__ slot_range, int E, int64_t mn) {
-  for (int e = 0; e < E; ++e) {
-    const int2 sr = slot_range[e];
-    if (sr.y <= sr.x) continue;
+  __shared__ int2 srs[256];
+  __shared__ int act[256];
+  __shared__ int nact;
+  if (threadIdx.x == 0) nact = 0;
+  __syncthreads();
+  if ((int)threadIdx.x < E) {
+    const int2 sr = slot_range[threadIdx.x];
+    if (sr.y > sr.x) {
+      const int i = atomicAdd(&nact, 1);
+      act[i] = threadIdx.x;
+      srs[i] = sr;
+    }
+  }
+  __syncthreads();
+  for (int a = 0; a < nact; ++a) {
+    const int e = act[a];
+    const int2 sr = srs[a];
     float* out = dw + (int64_t)e * mn;
     for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; i < mn; i += (int64_t)gridDim.x * 256 * 4) {
       f32x4 a = *reinterpret_cast<const f32x4*>(out + i);
