@@ -201,6 +201,20 @@ def main():
     counts = run.plan.arrays()["counts"].cpu()
     rows = int(counts.sum())
     esz = 2 if cfg.act == "bf16" else 4
+    # practical HBM rate of a plain device-to-device copy of the permutation's size
+    # (reference for the data-movement kernels, not part of the layer)
+    cbytes = (cfg.T + rows) * cfg.d * esz // 2 // 16 * 16
+    csrc = torch.empty(cbytes, dtype=torch.uint8, device="cuda")
+    cdst = torch.empty_like(csrc)
+    for _ in range(3):
+        cdst.copy_(csrc)
+    pev[0].record(stream)
+    for _ in range(10):
+        cdst.copy_(csrc)
+    pev[1].record(stream)
+    torch.cuda.synchronize()
+    copy_GBps = 2 * cbytes / (pev[0].elapsed_time(pev[1]) / 10 * 1e-3) / 1e9
+    del csrc, cdst
     fwd_gemm_flops = 2.0 * rows * cfg.d * 2 * cfg.f + 2.0 * rows * cfg.f * cfg.d
     peak = {"mxfp8": PEAK_FP8_TFLOPS, "bf16": PEAK_BF16_TFLOPS}.get(cfg.gemm, PEAK_F32_TFLOPS)
     achieved = fwd_gemm_flops / (ms["experts"] * 1e-3) / 1e12
@@ -236,6 +250,7 @@ def main():
         "permute_fused_into_gemms": fused,
         "combine_GBps": combine_bytes / (ms["combine"] * 1e-3) / 1e9,
         "hbm_peak_GBps": PEAK_HBM_GBS,
+        "device_copy_GBps": copy_GBps,
         "rows": rows,
         "max_expert_rows": int(counts.max()),
         "activation_memory_bytes": activation_bytes(cfg, rows, binding.plan_bytes(s), run.ws_fwd.numel())

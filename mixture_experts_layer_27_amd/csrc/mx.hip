@@ -231,6 +231,10 @@ __global__ __launch_bounds__(256) void quantize_t_kernel(const bf16_t* __restric
 // C and the position extent (R, or pad_off[E]) are multiples of 64.  The
 // position codes are transposed through LDS so that each store instruction
 // writes whole 128-byte lines of the [C][len] layout.
+// WIDE: each lane quantises 16 columns of a row and stores their codes in one
+// 16-byte store (faster for the activation passes; the weight passes keep
+// 8 columns per lane, which measured faster for them).
+template <bool WIDE>
 __global__ __launch_bounds__(256) void quantize_dual_kernel(const bf16_t* __restrict__ src, int G, int R, int C,
                                                            const int32_t* __restrict__ seg_off,
                                                            const int32_t* __restrict__ pad_off, int E, int64_t P,
@@ -275,37 +279,81 @@ __global__ __launch_bounds__(256) void quantize_dual_kernel(const bf16_t* __rest
       }
     }
   }
-  // 128 rows x 16 chunks of 8 values, eight 16-byte loads per thread, all issued first
-  u32x4 raw[8];
+  if constexpr (WIDE) {
+    // 128 rows x 8 pairs of 8-value chunks (32 contiguous bytes per lane), eight
+    // 16-byte loads per thread, all issued first
+    u32x4 raw[8];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int i = t + 256 * u;
-    const int rr = i >> 4, ch = i & 15, hh = rr >> 6, rl = rr & 63;
-    const int col = c0 + ch * 8;
-    const bool ok = rl < valid[hh] && col < C;
-    const int64_t sr = gather && ok ? (int64_t)gather[base[hh] + rl] : base[hh] + rl;   // tokens mode
-    raw[u] = ok ? ldg16(src + sr * C + col) : u32x4{0u, 0u, 0u, 0u};
-  }
-  // along rows: four consecutive lanes hold one 32-column block
+    for (int v = 0; v < 4; ++v) {
+      const int i = t + 256 * v;
+      const int rr = i >> 3, cp = i & 7, hh = rr >> 6, rl = rr & 63;
+      const int64_t sr = gather && rl < valid[hh] ? (int64_t)gather[base[hh] + rl] : base[hh] + rl;   // tokens mode
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int i = t + 256 * u;
-    const int rr = i >> 4, ch = i & 15;
-    const int col = c0 + ch * 8;
-    const int64_t p = p0 + rr;
-    *reinterpret_cast<u32x4*>(vt + rr * VS + ch * 8) = raw[u];
-    float v[8];
-    unpack8(raw[u], v);
-    float amax = 0.0f;
+      for (int q = 0; q < 2; ++q) {
+        const int col = c0 + cp * 16 + q * 8;
+        const bool ok = rl < valid[hh] && col < C;
+        raw[2 * v + q] = ok ? ldg16(src + sr * C + col) : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+    // along rows: two consecutive lanes hold one 32-column block, each lane 16
+    // columns whose codes leave in one 16-byte store
 #pragma unroll
-    for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
-    amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
-    amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
-    const int X = mx_exponent(amax);
-    if (p < plim && col < C) {               // uniform over the quad
-      const int64_t drow = seg_off ? p : (int64_t)g * R + p;
-      *reinterpret_cast<uint2*>(rcodes + drow * C + col) = e4m3_8(v, pow2f(-X));
-      if ((ch & 3) == 0) sc[rr][ch >> 2] = (uint8_t)(X + 127);
+    for (int v = 0; v < 4; ++v) {
+      const int i = t + 256 * v;
+      const int rr = i >> 3, cp = i & 7;
+      const int col = c0 + cp * 16;
+      const int64_t p = p0 + rr;
+      *reinterpret_cast<u32x4*>(vt + rr * VS + cp * 16) = raw[2 * v];
+      *reinterpret_cast<u32x4*>(vt + rr * VS + cp * 16 + 8) = raw[2 * v + 1];
+      float x[16];
+      unpack8(raw[2 * v], x);
+      unpack8(raw[2 * v + 1], x + 8);
+      float amax = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(x[j]));
+      amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+      const int X = mx_exponent(amax);
+      if (p < plim && col < C) {               // uniform over the pair (C is a multiple of 32)
+        const int64_t drow = seg_off ? p : (int64_t)g * R + p;
+        const float inv = pow2f(-X);
+        const uint2 lo = e4m3_8(x, inv), hi = e4m3_8(x + 8, inv);
+        *reinterpret_cast<u32x4*>(rcodes + drow * C + col) = u32x4{lo.x, lo.y, hi.x, hi.y};
+        if ((cp & 1) == 0) sc[rr][cp >> 1] = (uint8_t)(X + 127);
+      }
+    }
+  } else {
+    // 128 rows x 16 chunks of 8 values, eight 16-byte loads per thread, all issued first
+    u32x4 raw[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = t + 256 * u;
+      const int rr = i >> 4, ch = i & 15, hh = rr >> 6, rl = rr & 63;
+      const int col = c0 + ch * 8;
+      const bool ok = rl < valid[hh] && col < C;
+      const int64_t sr = gather && ok ? (int64_t)gather[base[hh] + rl] : base[hh] + rl;   // tokens mode
+      raw[u] = ok ? ldg16(src + sr * C + col) : u32x4{0u, 0u, 0u, 0u};
+    }
+    // along rows: four consecutive lanes hold one 32-column block
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = t + 256 * u;
+      const int rr = i >> 4, ch = i & 15;
+      const int col = c0 + ch * 8;
+      const int64_t p = p0 + rr;
+      *reinterpret_cast<u32x4*>(vt + rr * VS + ch * 8) = raw[u];
+      float v[8];
+      unpack8(raw[u], v);
+      float amax = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) amax = fmaxf(amax, fabsf(v[j]));
+      amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+      amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+      const int X = mx_exponent(amax);
+      if (p < plim && col < C) {               // uniform over the quad
+        const int64_t drow = seg_off ? p : (int64_t)g * R + p;
+        *reinterpret_cast<uint2*>(rcodes + drow * C + col) = e4m3_8(v, pow2f(-X));
+        if ((ch & 3) == 0) sc[rr][ch >> 2] = (uint8_t)(X + 127);
+      }
     }
   }
   __syncthreads();
@@ -446,7 +494,8 @@ hipError_t mx_quantize_dual(const void* src, int G, int R, int C, const int32_t*
                             int E, int64_t P, const MxOperand& rows, const MxOperand& pos, hipStream_t st,
                             const int32_t* gather) {
   const int64_t len = seg_off ? P : (int64_t)R;
-  hipLaunchKernelGGL(quantize_dual_kernel, dim3((C + 127) / 128, (unsigned)((len + 127) / 128), G), dim3(256), 0, st,
+  auto kern = seg_off ? quantize_dual_kernel<true> : quantize_dual_kernel<false>;
+  hipLaunchKernelGGL(kern, dim3((C + 127) / 128, (unsigned)((len + 127) / 128), G), dim3(256), 0, st,
                      (const bf16_t*)src, G, R, C, seg_off, pad_off, E, P, rows.codes, rows.scales, rows.srows,
                      pos.codes, pos.scales, gather);
   return hipGetLastError();
