@@ -165,6 +165,35 @@ MOE_DEV void wave_epilogue(const Args& args, const TileCtx& ctx, f32x16 (&acc)[B
   const int rbase = ctx.row_begin + wm * WTM;     // GROUP_M: first row of this wave's tile
   const int mbase = ctx.m0 + wm * WTM;            // GROUP_K: first output row
   const int cbase = ctx.n0 + wn * WTN;            // first output column
+  // SwiGLU backward: the sub-tile's H (gate and up) and gates.  The bf16 kernel
+  // loads sub-tile i + 1's while it works on sub-tile i (two register sets, one
+  // per parity); the MXFP8 one, whose epilogue holds more registers, loads each
+  // sub-tile's at its start.
+  constexpr int IT_H = (EPI == EPI_DSWIGLU || EPI == EPI_DSWIGLU_MX) ? 32 * CPR / 64 : 1;
+  constexpr bool H_AHEAD = EPI == EPI_DSWIGLU;
+  u32x4 hgv2[H_AHEAD ? 2 : 1][IT_H], huv2[H_AHEAD ? 2 : 1][IT_H];
+  float gv2[H_AHEAD ? 2 : 1][IT_H];
+  auto load_h = [&](auto sc, auto bc) {
+    constexpr int si = decltype(sc)::value, b = decltype(bc)::value;
+    const T* Hs = reinterpret_cast<const T*>(args.aux);
+#pragma unroll
+    for (int it = 0; it < IT_H; ++it) {
+      const int u = lane + 64 * it;
+      const int rr = u / CPR, ch = u % CPR;
+      const int grow = rbase + si * 32 + rr;
+      const int col = cbase + ch * 8;
+      if (grow < ctx.row_end && col < args.N) {
+        const T* hrow = Hs + (int64_t)grow * args.ld_aux;
+        hgv2[b][it] = ldg16(hrow + col);
+        huv2[b][it] = ldg16(hrow + args.f + col);
+        gv2[b][it] = args.row_gate[grow];
+      } else {
+        hgv2[b][it] = huv2[b][it] = u32x4{0u, 0u, 0u, 0u};
+        gv2[b][it] = 0.0f;
+      }
+    }
+  };
+  if constexpr (H_AHEAD) load_h(std::integral_constant<int, 0>{}, std::integral_constant<int, 0>{});
   // one 32-row sub-tile at a time; the sub-tile index is a compile-time constant
   // so the accumulators stay in registers however large the per-row work is
   static_for<TM>([&](auto ic) {
@@ -172,27 +201,16 @@ MOE_DEV void wave_epilogue(const Args& args, const TileCtx& ctx, f32x16 (&acc)[B
     if constexpr (EPI == EPI_DSWIGLU || EPI == EPI_DSWIGLU_MX) {
       static_assert(CPR <= 64 && (32 * CPR) % 64 == 0, "row reduction inside one wave");
       static_assert(EPI != EPI_DSWIGLU_MX || CPR % 4 == 0, "lane quads hold 32-column blocks");
-      constexpr int IT = 32 * CPR / 64;
-      const T* Hs = reinterpret_cast<const T*>(args.aux);
-      // global loads first: they overlap the staging below
-      u32x4 hgv[IT], huv[IT];
-      float gv[IT];
-#pragma unroll
-      for (int it = 0; it < IT; ++it) {
-        const int u = lane + 64 * it;
-        const int rr = u / CPR, ch = u % CPR;
-        const int grow = rbase + i * 32 + rr;
-        const int col = cbase + ch * 8;
-        if (grow < ctx.row_end && col < args.N) {
-          const T* hrow = Hs + (int64_t)grow * args.ld_aux;
-          hgv[it] = ldg16(hrow + col);
-          huv[it] = ldg16(hrow + args.f + col);
-          gv[it] = args.row_gate[grow];
-        } else {
-          hgv[it] = huv[it] = u32x4{0u, 0u, 0u, 0u};
-          gv[it] = 0.0f;
-        }
+      constexpr int IT = IT_H;
+      constexpr int B = H_AHEAD ? (i & 1) : 0;
+      if constexpr (H_AHEAD) {
+        if constexpr (i + 1 < TM) load_h(std::integral_constant<int, i + 1>{}, std::integral_constant<int, B ^ 1>{});
+      } else {
+        load_h(std::integral_constant<int, i>{}, std::integral_constant<int, 0>{});   // overlaps the staging below
       }
+      auto& hgv = hgv2[B];
+      auto& huv = huv2[B];
+      auto& gv = gv2[B];
 #pragma unroll
       for (int j = 0; j < TN; ++j)
 #pragma unroll
