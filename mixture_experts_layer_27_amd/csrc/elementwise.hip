@@ -236,7 +236,7 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const int32_t* __restri
                                                         const float* __restrict__ logits,
                                                         const float* __restrict__ aux, float lb_coef, float z_coef) {
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));   // wave-uniform
   if (t >= T_) return;
   const int p0 = tok_ptr[t], p1 = tok_ptr[t + 1], n = p1 - p0;
   float vals[4] = {0.f, 0.f, 0.f, 0.f};   // experts lane, lane+64, lane+128, lane+192
@@ -248,10 +248,12 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const int32_t* __restri
   const int rpp = 64 / np2;
   for (int pb = 0; pb < n; pb += rpp) {
     const int pi = pb + lane / np2, q0 = lane % np2;
-    float v = 0.0f;
-    int r = 0;
-    if (pi < n) {
+    float v = 0.0f, gr = 0.0f;
+    int r = 0, er = 0;
+    if (pi < n) {   // the row's gate and expert load alongside its partials
       r = tok_rows[p0 + pi];
+      gr = gate_of_row[r];
+      er = expert_of_row[r];
       for (int q = q0; q < nparts; q += np2) v += ds_part[q * part_stride + r];
     }
     for (int o = 1; o < np2; o <<= 1) v += __shfl_xor(v, o, 64);
@@ -259,9 +261,9 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const int32_t* __restri
       const float ds = __shfl(v, u * np2, 64);
       const int rr = __shfl(r, u * np2, 64);
       if (ds_out && lane == 0) ds_out[rr] = ds;
-      const float gds = gate_of_row[rr] * ds;
+      const float gds = __shfl(gr, u * np2, 64) * ds;
       acc += gds;
-      const int e = expert_of_row[rr];
+      const int e = __shfl(er, u * np2, 64);
       if ((e & 63) == lane) vals[e >> 6] += gds;
     }
   }
@@ -336,7 +338,15 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
                                                            float* __restrict__ out) {
   for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; i < n; i += (int64_t)gridDim.x * 256 * 4) {
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
-    for (int q = 0; q < nsplit; ++q) s += *reinterpret_cast<const f32x4*>(part + q * n + i);
+    int q = 0;
+    for (; q + 8 <= nsplit; q += 8) {   // eight partials' loads in flight, added in split order
+      f32x4 p[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) p[u] = *reinterpret_cast<const f32x4*>(part + (q + u) * n + i);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += p[u];
+    }
+    for (; q < nsplit; ++q) s += *reinterpret_cast<const f32x4*>(part + q * n + i);
     *reinterpret_cast<f32x4*>(out + i) = s;
   }
 }
