@@ -24,7 +24,45 @@
 namespace moe {
 namespace {
 
-MOE_DEV bool better(float av, int ae, float bv, int be) { return av > bv || (av == bv && ae < be); }
+// (value desc, index asc) as one unsigned 64-bit key: larger key = better.
+// High word: the float's bits mapped to an unsigned order; low word: ~index.
+// Key 0 lies below every real value (it stands for "no candidate").
+MOE_DEV uint64_t rank_key(float v, int e) {
+  const uint32_t b = v == 0.0f ? 0u : __float_as_uint(v);   // -0 ranks as +0
+  const uint32_t u = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)u << 32) | (uint32_t)~(uint32_t)e;
+}
+MOE_DEV float key_value(uint64_t k) {
+  const uint32_t u = (uint32_t)(k >> 32);
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
+MOE_DEV int key_index(uint64_t k) { return (int)~(uint32_t)k; }
+
+// Wave-wide maximum of a 64-bit key: DPP exchanges inside each 16-lane row
+// (quad xor 1, quad xor 2, half-row mirror, row mirror), then the four row
+// results combined from lane reads.
+template <int CTRL>
+MOE_DEV uint64_t dpp_max(uint64_t k) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)k, CTRL, 0xf, 0xf, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(k >> 32), CTRL, 0xf, 0xf, false);
+  const uint64_t o = ((uint64_t)hi << 32) | lo;
+  return o > k ? o : k;
+}
+MOE_DEV uint64_t wave_max_key(uint64_t k) {
+  k = dpp_max<0xB1>(k);    // quad_perm [1,0,3,2]
+  k = dpp_max<0x4E>(k);    // quad_perm [2,3,0,1]
+  k = dpp_max<0x141>(k);   // row_half_mirror
+  k = dpp_max<0x140>(k);   // row_mirror
+  uint64_t best = 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)k, 16 * r);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), 16 * r);
+    const uint64_t o = ((uint64_t)hi << 32) | lo;
+    best = o > best ? o : best;
+  }
+  return best;
+}
 
 // One wave per token; a wave takes TPW tokens in turn (NT/64*TPW per block).  Lane
 // l holds experts l, l+64, ...  With ROUND (64 tokens per block: sixteen waves of
@@ -62,19 +100,15 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ logi
     int sel_e[8];
     float sel_z[8];
     for (int j = 0; j < k; ++j) {
-      float bv = -INFINITY;
-      int be = 0x7fffffff;
+      uint64_t kb = 0;   // this lane's best untaken expert
 #pragma unroll
       for (int v = 0; v < V; ++v) {
-        int e = lane + 64 * v;
-        if (!taken[v] && better(z[v], e, bv, be)) { bv = z[v]; be = e; }
+        const uint64_t kv = taken[v] ? 0ull : rank_key(z[v], lane + 64 * v);
+        kb = kv > kb ? kv : kb;
       }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        float ov = __shfl_xor(bv, o, 64);
-        int oe = __shfl_xor(be, o, 64);
-        if (better(ov, oe, bv, be)) { bv = ov; be = oe; }
-      }
+      kb = wave_max_key(kb);
+      const int be = key_index(kb);
+      const float bv = key_value(kb);
       sel_e[j] = be;
       sel_z[j] = bv;
 #pragma unroll
