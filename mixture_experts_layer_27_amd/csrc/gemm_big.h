@@ -89,13 +89,16 @@ struct RegOperand {
     for (int i = 0; i < L; ++i) voff[i] = (uint32_t)((int64_t)(k0 + KPP * i) * ld * 2 + cc * 16);
   }
   // M/N-contiguous with gathered k rows: k row r of the chunk [k_begin, k_end)
-  // is row gidx[r] of the source (a permutation fused into the loads).  Each
-  // lane reads the source rows of its L loads one stage ahead (fetch_rows);
-  // offsets are 32-bit (the source holds fewer than 2^31 bytes).
+  // is row gidx[r] of the source (a permutation fused into the loads).  A wave
+  // covers RPW consecutive k rows per pass, so it needs L * RPW source rows per
+  // stage: that many lanes load them one stage ahead (fetch_rows, one load
+  // instruction) and each load reads its row from them with lane reads.
+  // Offsets are 32-bit (the source holds fewer than 2^31 bytes).
+  static constexpr int RPW = 64 / (ROWS / 8);   // k rows per wave and pass
   const int32_t* gidx;
   int gk, gkend, kl;
   uint32_t gld, gcol;
-  int32_t nsrc[L];
+  int32_t idxv;
   MOE_DEV void init_mn_gather(int64_t ld, const int32_t* g, int k_begin, int k_end, int64_t col_bytes,
                               int64_t src_rows) {
     constexpr int CPK = ROWS / 8;
@@ -110,18 +113,26 @@ struct RegOperand {
   }
   MOE_DEV void fetch_rows() {
     constexpr int KPP = NT / (ROWS / 8);
-#pragma unroll
-    for (int i = 0; i < L; ++i) {
-      const int k = gk + kl + KPP * i;
-      nsrc[i] = k < gkend ? gidx[k] : -1;
+    static_assert(RPW == 1 || RPW == 2, "one or two k rows per wave and pass");
+    const int lane = threadIdx.x & 63;
+    const int kw = (int)(threadIdx.x & ~63u) / (ROWS / 8);   // the wave's first k row of a pass
+    int src = -1;
+    if (lane < L * RPW) {
+      const int k = gk + kw + lane % RPW + KPP * (lane / RPW);
+      if (k < gkend) src = gidx[k];
     }
+    idxv = src;
     gk += KPP * L;
   }
   MOE_DEV void load_gather() {
     const __amdgpu_buffer_rsrc_t r = make_rsrc(base, (uint32_t)num0);
+    const bool upper = RPW == 2 && (threadIdx.x & 63) >= 32;   // the wave's second k row
 #pragma unroll
     for (int i = 0; i < L; ++i) {
-      const uint32_t off = nsrc[i] >= 0 ? (uint32_t)nsrc[i] * gld + gcol : 0xfffffff0u;   // absent: past num0
+      const int n0 = __builtin_amdgcn_readlane(idxv, RPW * i);
+      const int n1 = RPW == 2 ? __builtin_amdgcn_readlane(idxv, RPW * i + RPW - 1) : n0;
+      const int n = upper ? n1 : n0;
+      const uint32_t off = n >= 0 ? (uint32_t)n * gld + gcol : 0xfffffff0u;   // absent: past num0
       v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
     }
     fetch_rows();
