@@ -185,6 +185,25 @@ def main():
           for j, p in enumerate(phases)}
     step_ms = sum(evs[i][0].elapsed_time(evs[i][5]) for i in range(a.steps)) / a.steps
     ms_per_step = wall * 1000.0 / a.steps
+    step_q = sorted(evs[i][0].elapsed_time(evs[i][5]) for i in range(a.steps))
+    pct = lambda q: step_q[min(len(step_q) - 1, int(round(q * (len(step_q) - 1))))]
+
+    # data-movement rates with cold caches: a 1 GiB scratch write before each
+    # timed launch evicts L2 and the 256 MB last-level cache
+    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+
+    def cold_ms(fn, n=5):
+        t = []
+        for _ in range(n):
+            flush_buf.fill_(1)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t.append(e0.elapsed_time(e1))
+        return sorted(t)[len(t) // 2]
 
     # moe_permute on its own (outside the step when it is fused into the GEMMs)
     pev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
@@ -196,6 +215,7 @@ def main():
     pev[1].record(stream)
     torch.cuda.synchronize()
     permute_ms = pev[0].elapsed_time(pev[1]) / 10
+    permute_cold_ms = cold_ms(lambda: binding.permute(s, run.inp["x"], run.plan, run.x_perm))
 
     N = cfg.N  # rows without rounding (algorithmic work)
     counts = run.plan.arrays()["counts"].cpu()
@@ -214,7 +234,8 @@ def main():
     pev[1].record(stream)
     torch.cuda.synchronize()
     copy_GBps = 2 * cbytes / (pev[0].elapsed_time(pev[1]) / 10 * 1e-3) / 1e9
-    del csrc, cdst
+    copy_cold_ms = cold_ms(lambda: cdst.copy_(csrc))
+    del csrc, cdst, flush_buf
     fwd_gemm_flops = 2.0 * rows * cfg.d * 2 * cfg.f + 2.0 * rows * cfg.f * cfg.d
     peak = {"mxfp8": PEAK_FP8_TFLOPS, "bf16": PEAK_BF16_TFLOPS}.get(cfg.gemm, PEAK_F32_TFLOPS)
     achieved = fwd_gemm_flops / (ms["experts"] * 1e-3) / 1e12
@@ -251,6 +272,10 @@ def main():
         "combine_GBps": combine_bytes / (ms["combine"] * 1e-3) / 1e9,
         "hbm_peak_GBps": PEAK_HBM_GBS,
         "device_copy_GBps": copy_GBps,
+        "cold_cache_GBps": {"permute": permute_bytes / (permute_cold_ms * 1e-3) / 1e9,
+                            "device_copy": 2 * cbytes / (copy_cold_ms * 1e-3) / 1e9,
+                            "note": "median of 5 launches, each after a 1 GiB scratch write"},
+        "step_ms_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
         "rows": rows,
         "max_expert_rows": int(counts.max()),
         "activation_memory_bytes": activation_bytes(cfg, rows, binding.plan_bytes(s), run.ws_fwd.numel())
