@@ -61,8 +61,9 @@ hipError_t run_big(const Args& a, int64_t logical_tiles, hipStream_t st) {
 }
 
 // The 256 x 256 register-staged kernel pays a longer unoverlapped epilogue per
-// tile (one block per CU); it wins when the reduction is deep enough.
-bool use_big(int K) { return K >= 1024; }
+// tile (one block per CU); it wins when the reduction is deep enough (from
+// K = 512: GEMM2 at d_ff = 512 takes 1618 instead of 1750 us).
+bool use_big(int K) { return K >= 512; }
 
 Args base_args() {
   Args a{};
