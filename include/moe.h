@@ -229,6 +229,40 @@ moe_status moe_backward(const moe_shape *s, const void *x, const void *w_gate, c
                         const void *fwd_ws, const void *dout, void *dx, float *dw_gate, float *dw1, float *dw2,
                         float *dlogits, float *ds, void *ws, size_t ws_bytes, void *stream);
 
+/* Kernel timing from the caller's side (instrumentation; the results are the
+ * same as without it).  The caller creates `capacity` hipEvent_t handles (passed
+ * as void*) and passes this struct to a *_traced entry point, which records
+ * events[0] on the stream before its first kernel and events[i + 1] after its
+ * i-th kernel, and names that kernel in names[i]; `count` is the number of
+ * events recorded (kernels + 1, at most capacity and MOE_TRACE_MAX_KERNELS + 1).
+ * hipEventElapsedTime(events[i], events[i + 1]) is then the device time of
+ * kernel names[i].  Names are static strings owned by the library, e.g. "up_swiglu",
+ * "down" (forward), "dact", "dw1", "dw2", "dx_perm", "router_bwd",
+ * "router_dx", "router_dwg" (backward), "mx_*" for the MXFP8 kernels.
+ * Errors: MOE_EINVAL for a negative capacity or a NULL event among the first
+ * `capacity`; a failed hipEventRecord stops the call with MOE_EHIP. */
+#define MOE_TRACE_MAX_KERNELS 48
+typedef struct moe_trace {
+  void **events;
+  int32_t capacity;
+  int32_t count;
+  const char *names[MOE_TRACE_MAX_KERNELS];
+} moe_trace;
+
+/* moe_grouped_gemm_swiglu, moe_grouped_gemm_swiglu_gather and moe_backward with
+ * kernel timing (above). */
+moe_status moe_grouped_gemm_swiglu_gather_traced(const moe_shape *s, const void *x, const void *w1,
+                                                 const void *w2, const moe_plan *plan, void *h_saved, void *y,
+                                                 void *ws, size_t ws_bytes, void *stream, moe_trace *trace);
+moe_status moe_grouped_gemm_swiglu_traced(const moe_shape *s, const void *x_perm, const void *w1,
+                                          const void *w2, const moe_plan *plan, void *h_saved, void *y,
+                                          void *ws, size_t ws_bytes, void *stream, moe_trace *trace);
+moe_status moe_backward_traced(const moe_shape *s, const void *x, const void *w_gate, const void *w1,
+                               const void *w2, const moe_plan *plan, const void *h_saved, const void *x_perm,
+                               const void *fwd_ws, const void *dout, void *dx, float *dw_gate, float *dw1,
+                               float *dw2, float *dlogits, float *ds, void *ws, size_t ws_bytes, void *stream,
+                               moe_trace *trace);
+
 /* MXFP8 quantiser (OCP Microscaling v1.0; the pages only name the format):
  * blocks of 32 consecutive values along the reduction axis; shared exponent
  * X = floor(log2(max|v|)) - 8 clamped to [-127,127] (-127 for an all-zero

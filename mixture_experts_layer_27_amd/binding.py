@@ -24,7 +24,9 @@ MOE_WS_ROUTE, MOE_WS_ROUND, MOE_WS_EXPERTS, MOE_WS_BACKWARD = 0, 1, 2, 3
 STATUS = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_ENOTSUP", 3: "MOE_EWORKSPACE", 4: "MOE_EHIP"}
 EXPORTS = ("moe_max_rows", "moe_plan_bytes", "moe_plan_init", "moe_workspace_bytes", "moe_route",
            "moe_round_tokens", "moe_permute", "moe_grouped_gemm_swiglu", "moe_grouped_gemm_swiglu_gather",
-           "moe_unpermute_combine", "moe_backward", "moe_quantize_mx", "moe_status_str")
+           "moe_grouped_gemm_swiglu_traced", "moe_grouped_gemm_swiglu_gather_traced", "moe_unpermute_combine", "moe_backward", "moe_backward_traced",
+           "moe_quantize_mx", "moe_status_str")
+TRACE_MAX_KERNELS = 48
 
 
 class MoeShape(ctypes.Structure):
@@ -43,8 +45,13 @@ class MoePlan(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in _PLAN_FIELDS]
 
 
+class MoeTrace(ctypes.Structure):
+    _fields_ = [("events", ctypes.POINTER(ctypes.c_void_p)), ("capacity", ctypes.c_int32),
+                ("count", ctypes.c_int32), ("names", ctypes.c_char_p * TRACE_MAX_KERNELS)]
+
+
 _vp, _sz, _i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int64
-_P_SHAPE, _P_PLAN = ctypes.POINTER(MoeShape), ctypes.POINTER(MoePlan)
+_P_SHAPE, _P_PLAN, _P_TRACE = ctypes.POINTER(MoeShape), ctypes.POINTER(MoePlan), ctypes.POINTER(MoeTrace)
 for name, res, args in [
     ("moe_max_rows", _i64, [_P_SHAPE]),
     ("moe_plan_bytes", _sz, [_P_SHAPE]),
@@ -56,8 +63,14 @@ for name, res, args in [
     ("moe_grouped_gemm_swiglu", ctypes.c_int, [_P_SHAPE, _vp, _vp, _vp, _P_PLAN, _vp, _vp, _vp, _sz, _vp]),
     ("moe_grouped_gemm_swiglu_gather", ctypes.c_int, [_P_SHAPE, _vp, _vp, _vp, _P_PLAN, _vp, _vp, _vp, _sz, _vp]),
     ("moe_unpermute_combine", ctypes.c_int, [_P_SHAPE, _vp, _P_PLAN, _vp, _vp]),
+    ("moe_grouped_gemm_swiglu_traced", ctypes.c_int,
+     [_P_SHAPE, _vp, _vp, _vp, _P_PLAN, _vp, _vp, _vp, _sz, _vp, _P_TRACE]),
+    ("moe_grouped_gemm_swiglu_gather_traced", ctypes.c_int,
+     [_P_SHAPE, _vp, _vp, _vp, _P_PLAN, _vp, _vp, _vp, _sz, _vp, _P_TRACE]),
     ("moe_backward", ctypes.c_int, [_P_SHAPE, _vp, _vp, _vp, _vp, _P_PLAN, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                     _vp, _vp, _vp, _vp, _sz, _vp]),
+    ("moe_backward_traced", ctypes.c_int, [_P_SHAPE, _vp, _vp, _vp, _vp, _P_PLAN, _vp, _vp, _vp, _vp, _vp, _vp,
+                                           _vp, _vp, _vp, _vp, _vp, _sz, _vp, _P_TRACE]),
     ("moe_quantize_mx", ctypes.c_int, [_vp, _i64, _i64, ctypes.c_int, _vp, _vp, _vp]),
     ("moe_status_str", ctypes.c_char_p, [ctypes.c_int]),
 ]:
@@ -190,14 +203,45 @@ def permute(s: MoeShape, src, plan: Plan, dst, stream=None):
                                            _stream(stream)))
 
 
-def grouped_gemm_swiglu(s: MoeShape, x_perm, w1, w2, plan: Plan, h_saved, y, ws, stream=None):
+class Trace:
+    """Timing events between the kernels of one traced call (moe_trace).  The
+    events are torch CUDA events with timing, recorded once here so their HIP
+    handles exist; after the call, ``durations_ms()`` gives (kernel name, device
+    time) in launch order (valid once the stream has passed the call)."""
+
+    def __init__(self, capacity=TRACE_MAX_KERNELS + 1, stream=None):
+        st = stream if stream is not None else torch.cuda.current_stream()
+        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(capacity)]
+        for ev in self.events:
+            ev.record(st)
+        self._handles = (ctypes.c_void_p * capacity)(*[ev.cuda_event for ev in self.events])
+        self.c = MoeTrace(ctypes.cast(self._handles, ctypes.POINTER(ctypes.c_void_p)), capacity, 0)
+
+    def durations_ms(self):
+        n = self.c.count
+        return [(self.c.names[i].decode(), self.events[i].elapsed_time(self.events[i + 1])) for i in range(n - 1)]
+
+
+def grouped_gemm_swiglu(s: MoeShape, x_perm, w1, w2, plan: Plan, h_saved, y, ws, stream=None, trace=None):
+    if trace is not None:
+        _check("moe_grouped_gemm_swiglu_traced",
+               _lib.moe_grouped_gemm_swiglu_traced(ctypes.byref(s), _ptr(x_perm), _ptr(w1), _ptr(w2),
+                                                   ctypes.byref(plan.c), _ptr(h_saved), _ptr(y), _ptr(ws), ws.numel(),
+                                                   _stream(stream), ctypes.byref(trace.c)))
+        return
     _check("moe_grouped_gemm_swiglu",
            _lib.moe_grouped_gemm_swiglu(ctypes.byref(s), _ptr(x_perm), _ptr(w1), _ptr(w2), ctypes.byref(plan.c),
                                         _ptr(h_saved), _ptr(y), _ptr(ws), ws.numel(), _stream(stream)))
 
 
-def grouped_gemm_swiglu_gather(s: MoeShape, x, w1, w2, plan: Plan, h_saved, y, ws, stream=None):
+def grouped_gemm_swiglu_gather(s: MoeShape, x, w1, w2, plan: Plan, h_saved, y, ws, stream=None, trace=None):
     """The expert FFN reading the rows of x through the plan (no permuted copy)."""
+    if trace is not None:
+        _check("moe_grouped_gemm_swiglu_gather_traced",
+               _lib.moe_grouped_gemm_swiglu_gather_traced(ctypes.byref(s), _ptr(x), _ptr(w1), _ptr(w2),
+                                                          ctypes.byref(plan.c), _ptr(h_saved), _ptr(y), _ptr(ws),
+                                                          ws.numel(), _stream(stream), ctypes.byref(trace.c)))
+        return
     _check("moe_grouped_gemm_swiglu_gather",
            _lib.moe_grouped_gemm_swiglu_gather(ctypes.byref(s), _ptr(x), _ptr(w1), _ptr(w2), ctypes.byref(plan.c),
                                                _ptr(h_saved), _ptr(y), _ptr(ws), ws.numel(), _stream(stream)))
@@ -209,11 +253,14 @@ def unpermute_combine(s: MoeShape, y, plan: Plan, out, stream=None):
 
 
 def backward(s: MoeShape, x, w_gate, w1, w2, plan: Plan, h_saved, dout, dx, dw_gate, dw1, dw2, ws,
-             dlogits=None, ds=None, stream=None, x_perm=None, fwd_ws=None):
-    _check("moe_backward",
-           _lib.moe_backward(ctypes.byref(s), _ptr(x), _ptr(w_gate), _ptr(w1), _ptr(w2), ctypes.byref(plan.c),
-                             _ptr(h_saved), _ptr(x_perm), _ptr(fwd_ws), _ptr(dout), _ptr(dx), _ptr(dw_gate),
-                             _ptr(dw1), _ptr(dw2), _ptr(dlogits), _ptr(ds), _ptr(ws), ws.numel(), _stream(stream)))
+             dlogits=None, ds=None, stream=None, x_perm=None, fwd_ws=None, trace=None):
+    args = (ctypes.byref(s), _ptr(x), _ptr(w_gate), _ptr(w1), _ptr(w2), ctypes.byref(plan.c), _ptr(h_saved),
+            _ptr(x_perm), _ptr(fwd_ws), _ptr(dout), _ptr(dx), _ptr(dw_gate), _ptr(dw1), _ptr(dw2), _ptr(dlogits),
+            _ptr(ds), _ptr(ws), ws.numel(), _stream(stream))
+    if trace is not None:
+        _check("moe_backward_traced", _lib.moe_backward_traced(*args, ctypes.byref(trace.c)))
+        return
+    _check("moe_backward", _lib.moe_backward(*args))
 
 
 def quantize_mx(src, codes, scales, k_axis=1, stream=None):
@@ -281,7 +328,7 @@ class LayerRun:
             grouped_gemm_swiglu(self.s, self.x_perm, self.inp["w1"], self.inp["w2"], self.plan, self.h, self.y,
                                 self.ws_fwd, stream)
 
-    def backward(self, stream=None, with_optional=True, reuse_x_perm=True, reuse_fwd_ws=True):
+    def backward(self, stream=None, with_optional=True, reuse_x_perm=True, reuse_fwd_ws=True, trace=None):
         """reuse_x_perm: hand the forward's permuted x to the backward (else it permutes x again);
         reuse_fwd_ws: hand it the forward's workspace (MXFP8: the backward-orientation codes of
         W1, W2 and x_perm), else it quantises them again."""
@@ -289,7 +336,7 @@ class LayerRun:
                  self.inp["dout"], self.dx, self.dw_gate, self.dw1, self.dw2, self.ws_bwd,
                  self.dlogits if with_optional else None, self.ds if with_optional else None, stream,
                  self.x_perm if (reuse_x_perm and not self.fused_gather) else None,
-                 self.ws_fwd if reuse_fwd_ws else None)
+                 self.ws_fwd if reuse_fwd_ws else None, trace)
 
     def step(self, stream=None):
         self.forward(stream)

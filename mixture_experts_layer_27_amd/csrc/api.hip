@@ -18,7 +18,6 @@ size_t al(size_t b) { return (b + kAlign - 1) / kAlign * kAlign; }
 
 int words_of(const moe_shape& s) { return (s.E + 31) / 32; }
 int nblk_of(const moe_shape& s) { return (s.T + kPlanBlock - 1) / kPlanBlock; }
-int ldz_of(const moe_shape& s) { return (s.E + 7) / 8 * 8; }
 size_t esz(const moe_shape& s) { return s.act == MOE_BF16 ? 2 : 4; }
 
 // Carves the plan blob in a fixed order; with base == nullptr it only measures.
@@ -109,6 +108,42 @@ moe_status check_plan(const moe_shape& s, const moe_plan* p) {
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
 
+// A call's launch sequence: each step runs only while every earlier one succeeded,
+// and with a trace the caller's next event is recorded after it (names[i] = the
+// kernel between events[i] and events[i + 1]).
+struct Seq {
+  hipStream_t st;
+  moe_trace* tr;
+  hipError_t e = hipSuccess;
+  Seq(hipStream_t s, moe_trace* t) : st(s), tr(t) {
+    if (tr) {
+      tr->count = 0;
+      record(nullptr);
+    }
+  }
+  void record(const char* name) {
+    if (tr->count >= tr->capacity || tr->count > MOE_TRACE_MAX_KERNELS) return;
+    if (tr->count > 0) tr->names[tr->count - 1] = name;
+    e = hipEventRecord(reinterpret_cast<hipEvent_t>(tr->events[tr->count]), st);
+    if (e == hipSuccess) tr->count++;
+  }
+  template <class F>
+  void operator()(const char* name, F&& launch) {
+    if (e != hipSuccess) return;
+    e = launch();
+    if (e == hipSuccess && tr) record(name);
+  }
+  moe_status status() const { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+};
+
+bool trace_ok(const moe_trace* t) {
+  if (!t) return true;
+  if (t->capacity < 0 || (t->capacity > 0 && !t->events)) return false;
+  for (int i = 0; i < t->capacity; ++i)
+    if (!t->events[i]) return false;
+  return true;
+}
+
 // token capacity of the expert-padded layout of the MX weight-gradient operands
 int64_t tok_cap(const moe_shape& s) { return (max_rows(s) + 64 * (int64_t)s.E + 63) / 64 * 64; }
 
@@ -135,7 +170,7 @@ int wgrad_kch(const moe_shape& s, int64_t ncap) {
 int64_t wgrad_cap(const moe_shape& s) { return s.gemm == MOE_MXFP8 ? tok_cap(s) : max_rows(s); }
 
 struct BwdWs {
-  void *do_perm, *dh, *ga, *xbuf, *dzq;
+  void *do_perm, *dh, *ga, *xbuf, *dzq, *wg2;
   float *ds_part, *dlogits, *dwg_part;
   float* dxr;   // dense router term dz W_g [T, d] (routing variants only)
   WgradChunks wg;
@@ -155,9 +190,10 @@ size_t carve_bwd(const moe_shape& s, char* base, BwdWs* w) {
   q.xbuf = c.take<char>(N * s.d * esz(s));
   q.ds_part = c.take<float>((size_t)gemm_dact_parts(s) * N * 4);
   q.dlogits = c.take<float>((size_t)s.T * s.E * 4);
-  q.dzq = c.take<char>((size_t)s.T * ldz_of(s) * esz(s));
-  q.dwg_part = c.take<float>((size_t)gemm_router_dwg_splits(s) * s.E * s.d * 4);
+  q.dzq = c.take<char>((size_t)s.T * router_dz_ld(s) * esz(s));
+  q.dwg_part = c.take<float>((size_t)gemm_router_dwg_splits(s) * router_dz_rows(s) * s.d * 4);
   q.dxr = dense_router_grad(s) ? c.take<float>((size_t)s.T * s.d * 4) : nullptr;
+  q.wg2 = dense_router_grad(s) && router_dz_split(s) ? c.take<char>((size_t)2 * router_ldz(s) * s.d * 2) : nullptr;
   {
     const int64_t ncap = wgrad_cap(s);
     WgradChunks& g = q.wg;
@@ -324,51 +360,64 @@ namespace {
 // through gather = token_of_row (the permutation fused into the operand loads).
 moe_status experts_forward(const moe_shape* s, const void* rows, const int32_t* gather, const void* w1,
                            const void* w2, const moe_plan* plan, void* h_saved, void* y, void* ws, size_t ws_bytes,
-                           void* stream) {
+                           void* stream, moe_trace* trace) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
   if (!aligned(rows) || !aligned(w1) || !aligned(w2) || !aligned(h_saved) || !aligned(y)) return MOE_EINVAL;
   if ((st = check_plan(*s, plan)) != MOE_OK) return st;
   if (!aligned(ws) || ws_bytes < experts_ws(*s)) return MOE_EWORKSPACE;
+  if (!trace_ok(trace)) return MOE_EINVAL;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   PlanInternal pi = plan_internal(*s, *plan);
   FwdWs w;
   carve_fwd(*s, reinterpret_cast<char*>(ws), &w);
-  hipError_t e;
+  Seq seq(hs, trace);
   if (s->gemm == MOE_MXFP8) {
     // x_perm and the weights are quantised along both of their axes in one pass
     // each: this call's GEMMs use the rows, the backward the other orientation
     const int64_t P = tok_cap(*s);
     const int E = s->E, d = s->d, f = s->d_ff;
     const int32_t* off = plan->offsets;
-    e = mx_pad_offsets(off, E, w.pad_off, hs);
-    if (e == hipSuccess) e = mx_quantize_dual(rows, 1, 0, d, off, w.pad_off, E, P, w.x, w.x_t, hs, gather);
-    if (e == hipSuccess) e = mx_quantize_dual(w1, E, 2 * f, d, nullptr, nullptr, 0, 0, w.w1, w.w1t, hs);
-    if (e == hipSuccess) e = gemm_mx_up_swiglu(*s, *plan, pi, w.x, w.w1, h_saved, w.a, hs);
-    if (e == hipSuccess) e = mx_quantize_dual(w2, E, d, f, nullptr, nullptr, 0, 0, w.w2, w.w2t, hs);
-    if (e == hipSuccess) e = gemm_mx_down(*s, *plan, pi, w.a, w.w2, y, hs);
-    return hip_status(e);
+    seq("mx_pad_offsets", [&] { return mx_pad_offsets(off, E, w.pad_off, hs); });
+    seq("mx_quantize_x", [&] { return mx_quantize_dual(rows, 1, 0, d, off, w.pad_off, E, P, w.x, w.x_t, hs, gather); });
+    seq("mx_quantize_w1", [&] { return mx_quantize_dual(w1, E, 2 * f, d, nullptr, nullptr, 0, 0, w.w1, w.w1t, hs); });
+    seq("mx_up_swiglu", [&] { return gemm_mx_up_swiglu(*s, *plan, pi, w.x, w.w1, h_saved, w.a, hs); });
+    seq("mx_quantize_w2", [&] { return mx_quantize_dual(w2, E, d, f, nullptr, nullptr, 0, 0, w.w2, w.w2t, hs); });
+    seq("mx_down", [&] { return gemm_mx_down(*s, *plan, pi, w.a, w.w2, y, hs); });
+    return seq.status();
   }
-  e = gemm_up_swiglu(*s, *plan, pi, rows, gather, w1, h_saved, w.act, hs);
-  if (e == hipSuccess) e = gemm_down(*s, *plan, pi, w.act, w2, y, hs);
-  return hip_status(e);
+  seq("up_swiglu", [&] { return gemm_up_swiglu(*s, *plan, pi, rows, gather, w1, h_saved, w.act, hs); });
+  seq("down", [&] { return gemm_down(*s, *plan, pi, w.act, w2, y, hs); });
+  return seq.status();
 }
 }  // namespace
 
 moe_status moe_grouped_gemm_swiglu(const moe_shape* s, const void* x_perm, const void* w1, const void* w2,
                                    const moe_plan* plan, void* h_saved, void* y, void* ws, size_t ws_bytes,
                                    void* stream) {
-  return experts_forward(s, x_perm, nullptr, w1, w2, plan, h_saved, y, ws, ws_bytes, stream);
+  return experts_forward(s, x_perm, nullptr, w1, w2, plan, h_saved, y, ws, ws_bytes, stream, nullptr);
+}
+
+moe_status moe_grouped_gemm_swiglu_traced(const moe_shape* s, const void* x_perm, const void* w1, const void* w2,
+                                          const moe_plan* plan, void* h_saved, void* y, void* ws, size_t ws_bytes,
+                                          void* stream, moe_trace* trace) {
+  return experts_forward(s, x_perm, nullptr, w1, w2, plan, h_saved, y, ws, ws_bytes, stream, trace);
+}
+
+moe_status moe_grouped_gemm_swiglu_gather_traced(const moe_shape* s, const void* x, const void* w1, const void* w2,
+                                                 const moe_plan* plan, void* h_saved, void* y, void* ws,
+                                                 size_t ws_bytes, void* stream, moe_trace* trace) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!gather_ok(*s)) return MOE_ENOTSUP;
+  if ((st = check_plan(*s, plan)) != MOE_OK) return st;
+  return experts_forward(s, x, plan->token_of_row, w1, w2, plan, h_saved, y, ws, ws_bytes, stream, trace);
 }
 
 moe_status moe_grouped_gemm_swiglu_gather(const moe_shape* s, const void* x, const void* w1, const void* w2,
                                           const moe_plan* plan, void* h_saved, void* y, void* ws, size_t ws_bytes,
                                           void* stream) {
-  moe_status st = check_shape(s);
-  if (st != MOE_OK) return st;
-  if (!gather_ok(*s)) return MOE_ENOTSUP;
-  if ((st = check_plan(*s, plan)) != MOE_OK) return st;
-  return experts_forward(s, x, plan->token_of_row, w1, w2, plan, h_saved, y, ws, ws_bytes, stream);
+  return moe_grouped_gemm_swiglu_gather_traced(s, x, w1, w2, plan, h_saved, y, ws, ws_bytes, stream, nullptr);
 }
 
 moe_status moe_unpermute_combine(const moe_shape* s, const void* y, const moe_plan* plan, void* out, void* stream) {
@@ -379,11 +428,11 @@ moe_status moe_unpermute_combine(const moe_shape* s, const void* y, const moe_pl
   return hip_status(launch_combine(*s, y, *plan, out, reinterpret_cast<hipStream_t>(stream)));
 }
 
-moe_status moe_backward(const moe_shape* s, const void* x, const void* w_gate, const void* w1, const void* w2,
-                        const moe_plan* plan, const void* h_saved, const void* x_perm, const void* fwd_ws,
-                        const void* dout, void* dx,
-                        float* dw_gate,
-                        float* dw1, float* dw2, float* dlogits, float* ds, void* ws, size_t ws_bytes, void* stream) {
+namespace {
+moe_status backward_impl(const moe_shape* s, const void* x, const void* w_gate, const void* w1, const void* w2,
+                         const moe_plan* plan, const void* h_saved, const void* x_perm, const void* fwd_ws,
+                         const void* dout, void* dx, float* dw_gate, float* dw1, float* dw2, float* dlogits, float* ds,
+                         void* ws, size_t ws_bytes, void* stream, moe_trace* trace) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
   if (!aligned(x) || !aligned(w_gate) || !aligned(w1) || !aligned(w2) || !aligned(h_saved) || !aligned(dout) ||
@@ -393,19 +442,20 @@ moe_status moe_backward(const moe_shape* s, const void* x, const void* w_gate, c
     return MOE_EINVAL;
   if ((st = check_plan(*s, plan)) != MOE_OK) return st;
   if (!aligned(ws) || ws_bytes < carve_bwd(*s, nullptr, nullptr)) return MOE_EWORKSPACE;
+  if (!trace_ok(trace)) return MOE_EINVAL;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   PlanInternal pi = plan_internal(*s, *plan);
   BwdWs w;
   carve_bwd(*s, reinterpret_cast<char*>(ws), &w);
   float* dz = dlogits ? dlogits : w.dlogits;
-  const int ldz = ldz_of(*s);
   // dO reaches the GEMMs through token_of_row inside their operand loads when the
   // kernels allow it (as fast as a permuted copy here, and no copy is stored),
   // else as a permuted copy.  x without x_perm is permuted again: its gathered
   // loads in the dW1 GEMM cost more than the permutation.
   const bool fused = gather_ok(*s);
   const int32_t* tor = plan->token_of_row;
-  hipError_t e = fused ? hipSuccess : launch_permute_rows(*s, dout, *plan, w.do_perm, hs);
+  Seq seq(hs, trace);
+  if (!fused) seq("permute_dout", [&] { return launch_permute_rows(*s, dout, *plan, w.do_perm, hs); });
   const void* dO = fused ? dout : w.do_perm;
   const int32_t* dOg = fused ? tor : nullptr;
   if (s->gemm == MOE_MXFP8) {
@@ -419,42 +469,67 @@ moe_status moe_backward(const moe_shape* s, const void* x, const void* w_gate, c
     const MxOperand& w1t = fwd_ws ? fw.w1t : w.w1t;
     const MxOperand& w2t = fwd_ws ? fw.w2t : w.w2t;
     const MxOperand& x_t = fwd_ws ? fw.x_t : w.x_t;
-    if (e == hipSuccess) e = mx_pad_offsets(off, E, w.pad_off, hs);
-    if (e == hipSuccess) e = mx_quantize_dual(dO, 1, 0, d, off, w.pad_off, E, P, w.doq, w.do_t, hs, dOg);
-    if (e == hipSuccess && !fwd_ws) e = mx_quantize_cols(w2, E, d, f, w.w2t.codes, w.w2t.scales, hs);
-    if (e == hipSuccess) e = gemm_mx_dact(*s, *plan, pi, w.doq, w2t, h_saved, w.dhq, w.dh_t, w.ga_t, P, w.ds_part, hs);
-    if (e == hipSuccess && !fwd_ws) e = mx_quantize_cols(w1, E, 2 * f, d, w.w1t.codes, w.w1t.scales, hs);
+    seq("mx_pad_offsets", [&] { return mx_pad_offsets(off, E, w.pad_off, hs); });
+    seq("mx_quantize_dout", [&] { return mx_quantize_dual(dO, 1, 0, d, off, w.pad_off, E, P, w.doq, w.do_t, hs, dOg); });
+    if (!fwd_ws) seq("mx_quantize_w2t", [&] { return mx_quantize_cols(w2, E, d, f, w.w2t.codes, w.w2t.scales, hs); });
+    seq("mx_dact", [&] {
+      return gemm_mx_dact(*s, *plan, pi, w.doq, w2t, h_saved, w.dhq, w.dh_t, w.ga_t, P, w.ds_part, hs);
+    });
+    if (!fwd_ws) seq("mx_quantize_w1t", [&] { return mx_quantize_cols(w1, E, 2 * f, d, w.w1t.codes, w.w1t.scales, hs); });
     // the token-axis quantiser reads x through the plan (a memory-bound pass: gathering is free)
     const void* xp = x_perm ? x_perm : fused ? x : w.xbuf;
     const int32_t* xg = (!x_perm && fused) ? tor : nullptr;
-    if (e == hipSuccess && !x_perm && !fwd_ws && !fused) e = launch_permute_rows(*s, x, *plan, w.xbuf, hs);
-    if (e == hipSuccess && !fwd_ws)
-      e = mx_quantize_tokens(xp, d, plan->offsets, w.pad_off, E, P, w.x_t.codes, w.x_t.scales, hs, xg);
-    if (e == hipSuccess) e = launch_wgrad_chunks(w.pad_off, E, w.wg.kch, w.wg, hs);
-    if (e == hipSuccess) e = gemm_mx_wgrad(*s, w.wg, P, w.dh_t, 2 * f, x_t, d, dw1, hs);
-    if (e == hipSuccess) e = launch_wgrad_reduce(w.wg, E, (int64_t)2 * f * d, dw1, hs);
-    if (e == hipSuccess) e = gemm_mx_wgrad(*s, w.wg, P, w.do_t, d, w.ga_t, f, dw2, hs);
-    if (e == hipSuccess) e = launch_wgrad_reduce(w.wg, E, (int64_t)d * f, dw2, hs);
-    if (e == hipSuccess) e = gemm_mx_dx_perm(*s, *plan, pi, w.dhq, w1t, w.xbuf, hs);   // dx_perm (x_perm no longer needed)
+    if (!x_perm && !fwd_ws && !fused) seq("permute_x", [&] { return launch_permute_rows(*s, x, *plan, w.xbuf, hs); });
+    if (!fwd_ws)
+      seq("mx_quantize_x_tokens", [&] {
+        return mx_quantize_tokens(xp, d, plan->offsets, w.pad_off, E, P, w.x_t.codes, w.x_t.scales, hs, xg);
+      });
+    seq("wgrad_chunks", [&] { return launch_wgrad_chunks(w.pad_off, E, w.wg.kch, w.wg, hs); });
+    seq("mx_dw1", [&] { return gemm_mx_wgrad(*s, w.wg, P, w.dh_t, 2 * f, x_t, d, dw1, hs); });
+    seq("dw1_reduce", [&] { return launch_wgrad_reduce(w.wg, E, (int64_t)2 * f * d, dw1, hs); });
+    seq("mx_dw2", [&] { return gemm_mx_wgrad(*s, w.wg, P, w.do_t, d, w.ga_t, f, dw2, hs); });
+    seq("dw2_reduce", [&] { return launch_wgrad_reduce(w.wg, E, (int64_t)d * f, dw2, hs); });
+    // dx_perm (x_perm no longer needed)
+    seq("mx_dx_perm", [&] { return gemm_mx_dx_perm(*s, *plan, pi, w.dhq, w1t, w.xbuf, hs); });
   } else {
-    if (e == hipSuccess) e = gemm_dact(*s, *plan, pi, dO, dOg, w2, h_saved, w.dh, w.ga, w.ds_part, hs);
-    if (e == hipSuccess && !x_perm) e = launch_permute_rows(*s, x, *plan, w.xbuf, hs);
+    seq("dact", [&] { return gemm_dact(*s, *plan, pi, dO, dOg, w2, h_saved, w.dh, w.ga, w.ds_part, hs); });
+    if (!x_perm) seq("permute_x", [&] { return launch_permute_rows(*s, x, *plan, w.xbuf, hs); });
     const void* xp = x_perm ? x_perm : w.xbuf;
-    if (e == hipSuccess) e = launch_wgrad_chunks(plan->offsets, s->E, w.wg.kch, w.wg, hs);
-    if (e == hipSuccess) e = gemm_dw1(*s, w.wg, w.dh, xp, dw1, hs);
-    if (e == hipSuccess) e = launch_wgrad_reduce(w.wg, s->E, (int64_t)2 * s->d_ff * s->d, dw1, hs);
-    if (e == hipSuccess) e = gemm_dw2(*s, w.wg, dO, dOg, w.ga, dw2, hs);
-    if (e == hipSuccess) e = launch_wgrad_reduce(w.wg, s->E, (int64_t)s->d * s->d_ff, dw2, hs);
-    if (e == hipSuccess) e = gemm_dx_perm(*s, *plan, pi, w.dh, w1, w.xbuf, hs);   // dx_perm (x_perm no longer needed)
+    seq("wgrad_chunks", [&] { return launch_wgrad_chunks(plan->offsets, s->E, w.wg.kch, w.wg, hs); });
+    seq("dw1", [&] { return gemm_dw1(*s, w.wg, w.dh, xp, dw1, hs); });
+    seq("dw1_reduce", [&] { return launch_wgrad_reduce(w.wg, s->E, (int64_t)2 * s->d_ff * s->d, dw1, hs); });
+    seq("dw2", [&] { return gemm_dw2(*s, w.wg, dO, dOg, w.ga, dw2, hs); });
+    seq("dw2_reduce", [&] { return launch_wgrad_reduce(w.wg, s->E, (int64_t)s->d * s->d_ff, dw2, hs); });
+    // dx_perm (x_perm no longer needed)
+    seq("dx_perm", [&] { return gemm_dx_perm(*s, *plan, pi, w.dh, w1, w.xbuf, hs); });
   }
-  if (e == hipSuccess)
-    e = launch_router_bwd(*s, *plan, w.ds_part, gemm_dact_parts(*s), ds, dz, w.dzq, ldz, hs);
-  if (e == hipSuccess && w.dxr) e = gemm_router_dx_dense(*s, w.dzq, ldz, w_gate, w.dxr, hs);
-  if (e == hipSuccess) e = launch_router_dx(*s, *plan, w.xbuf, dz, w_gate, w.dxr, dx, hs);
-  if (e == hipSuccess) e = gemm_router_dwg(*s, w.dzq, ldz, x, w.dwg_part, hs);
-  if (e == hipSuccess)
-    e = launch_splitk_reduce(w.dwg_part, gemm_router_dwg_splits(*s), (int64_t)s->E * s->d, dw_gate, hs);
-  return hip_status(e);
+  seq("router_bwd", [&] { return launch_router_bwd(*s, *plan, w.ds_part, gemm_dact_parts(*s), ds, dz, w.dzq, hs); });
+  if (w.wg2) seq("router_wg2", [&] { return launch_router_wg2(w_gate, s->E, router_ldz(*s), s->d, w.wg2, hs); });
+  if (w.dxr) seq("router_dx_dense", [&] { return gemm_router_dx_dense(*s, w.dzq, w.wg2 ? w.wg2 : w_gate, w.dxr, hs); });
+  seq("router_dx", [&] { return launch_router_dx(*s, *plan, w.xbuf, dz, w_gate, w.dxr, dx, hs); });
+  seq("router_dwg", [&] { return gemm_router_dwg(*s, w.dzq, x, w.dwg_part, hs); });
+  seq("router_dwg_reduce", [&] {
+    return launch_router_dwg_reduce(w.dwg_part, gemm_router_dwg_splits(*s), (int64_t)router_dz_rows(*s) * s->d,
+                                    s->E, s->d, router_dz_split(*s) ? router_ldz(*s) : -1, dw_gate, hs);
+  });
+  return seq.status();
+}
+}  // namespace
+
+moe_status moe_backward(const moe_shape* s, const void* x, const void* w_gate, const void* w1, const void* w2,
+                        const moe_plan* plan, const void* h_saved, const void* x_perm, const void* fwd_ws,
+                        const void* dout, void* dx, float* dw_gate, float* dw1, float* dw2, float* dlogits, float* ds,
+                        void* ws, size_t ws_bytes, void* stream) {
+  return backward_impl(s, x, w_gate, w1, w2, plan, h_saved, x_perm, fwd_ws, dout, dx, dw_gate, dw1, dw2, dlogits, ds,
+                       ws, ws_bytes, stream, nullptr);
+}
+
+moe_status moe_backward_traced(const moe_shape* s, const void* x, const void* w_gate, const void* w1, const void* w2,
+                               const moe_plan* plan, const void* h_saved, const void* x_perm, const void* fwd_ws,
+                               const void* dout, void* dx, float* dw_gate, float* dw1, float* dw2, float* dlogits,
+                               float* ds, void* ws, size_t ws_bytes, void* stream, moe_trace* trace) {
+  return backward_impl(s, x, w_gate, w1, w2, plan, h_saved, x_perm, fwd_ws, dout, dx, dw_gate, dw1, dw2, dlogits, ds,
+                       ws, ws_bytes, stream, trace);
 }
 
 moe_status moe_quantize_mx(const void* src_bf16, int64_t rows, int64_t cols, int k_axis, uint8_t* codes,

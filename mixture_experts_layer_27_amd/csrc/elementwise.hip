@@ -221,7 +221,10 @@ __global__ __launch_bounds__(256) void router_dx_kernel(const T* __restrict__ dx
 // h_e = (lb_coef / T) (2 (Pbar_e - m) / (E m^2) - 2 var / (E m^3)), m and var
 // the mean and population variance of Pbar (from the forward, aux[4..]); the
 // z-loss adds (2 z_coef / T) lse P_e.
-// Writes dlogits (fp32) and the GEMM operand dzq (act dtype, ld = ldz, zero padded).
+// Writes dlogits (fp32) and the GEMM operand dzq, row stride ld: columns [0, ldz)
+// hold dz (zero padded past E) in the act dtype; with bf16 activations columns
+// [ldz, 2 ldz) hold the rounding residual bf16(dz - bf16(dz)), so the two router
+// GEMMs see dz as the sum of two bf16 values (16 significant bits).
 template <typename T>
 __global__ __launch_bounds__(256) void router_bwd_kernel(const int32_t* __restrict__ tok_ptr,
                                                         const int32_t* __restrict__ tok_rows,
@@ -232,7 +235,7 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const int32_t* __restri
                                                         const float* __restrict__ ds_part, int nparts,
                                                         int64_t part_stride, int T_, int E, int k,
                                                         float* __restrict__ ds_out, float* __restrict__ dlogits,
-                                                        T* __restrict__ dzq, int ldz, int gate_all,
+                                                        T* __restrict__ dzq, int ldz, int ld, int gate_all,
                                                         const float* __restrict__ logits,
                                                         const float* __restrict__ aux, float lb_coef, float z_coef) {
   const int lane = threadIdx.x & 63;
@@ -330,7 +333,51 @@ __global__ __launch_bounds__(256) void router_bwd_kernel(const int32_t* __restri
   for (int v = 0; v < 4; ++v) {
     const int e = lane + 64 * v;
     if (e < E) dlogits[(int64_t)t * E + e] = vals[v];
-    if (e < ldz) Elem<T>::store(dzq + (int64_t)t * ldz + e, e < E ? vals[v] : 0.0f);
+    if (e < ldz) {
+      const float z = e < E ? vals[v] : 0.0f;
+      if constexpr (sizeof(T) == 2) {
+        const bf16_t hi = f2bf(z);
+        dzq[(int64_t)t * ld + e] = hi;
+        dzq[(int64_t)t * ld + ldz + e] = f2bf(z - bf2f(hi));   // exact difference in fp32
+      } else {
+        dzq[(int64_t)t * ld + e] = z;
+      }
+    }
+  }
+}
+
+// dW_g from the split-K partials of the router-weight GEMM: part[q] holds rows
+// [0, E) (the dz columns) and, when lo_row >= 0, rows [lo_row, lo_row + E) (their
+// bf16 residuals); out[e] = sum_q part[q][e] + sum_q part[q][lo_row + e], each sum
+// in split order.
+__global__ __launch_bounds__(256) void router_dwg_reduce_kernel(const float* __restrict__ part, int nsplit,
+                                                               int64_t pstride, int64_t n, int64_t lo_off,
+                                                               float* __restrict__ out) {
+  for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; i < n; i += (int64_t)gridDim.x * 256 * 4) {
+    f32x4 hi = {0.f, 0.f, 0.f, 0.f}, lo = {0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < nsplit; ++q) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(part + q * pstride + i);
+      f32x4 b = {0.f, 0.f, 0.f, 0.f};
+      if (lo_off >= 0) b = *reinterpret_cast<const f32x4*>(part + q * pstride + lo_off + i);
+      hi += a;
+      lo += b;
+    }
+    *reinterpret_cast<f32x4*>(out + i) = hi + lo;
+  }
+}
+
+// B operand of the dense router term with split dz: rows [0, E) and [ldz, ldz + E)
+// are W_g, the rows between and after are zero ([2 ldz, d] bf16).
+__global__ __launch_bounds__(256) void router_wg2_kernel(const bf16_t* __restrict__ wg, int E, int ldz, int d,
+                                                        bf16_t* __restrict__ wg2) {
+  const int64_t n = (int64_t)2 * ldz * d / 8;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    const int64_t el = i * 8;
+    const int r = (int)(el / d), c = (int)(el % d);
+    const int src = r < ldz ? r : r - ldz;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (src < E) v = ldg16(wg + (int64_t)src * d + c);
+    stg16(wg2 + el, v);
   }
 }
 
@@ -469,18 +516,19 @@ hipError_t launch_router_dx(const moe_shape& s, const moe_plan& p, const void* d
 }
 
 hipError_t launch_router_bwd(const moe_shape& s, const moe_plan& p, const float* ds_part, int nparts,
-                             float* ds_out, float* dlogits, void* dzq, int ldz, hipStream_t st) {
+                             float* ds_out, float* dlogits, void* dzq, hipStream_t st) {
+  const int ldz = router_ldz(s), ld = router_dz_ld(s);
   const int grid = ceil_div(s.T, 4);
   const int64_t pstride = max_rows(s);
   if (s.act == MOE_BF16)
     hipLaunchKernelGGL(router_bwd_kernel<bf16_t>, dim3(grid), dim3(256), 0, st, p.tok_ptr, p.tok_rows,
                        p.expert_of_row, p.gate_of_row, p.topk_idx, p.topk_gate, ds_part, nparts, pstride, s.T, s.E,
-                       s.k, ds_out, dlogits, (bf16_t*)dzq, ldz, (int)(s.gate_mode == MOE_GATE_ALL), p.logits,
+                       s.k, ds_out, dlogits, (bf16_t*)dzq, ldz, ld, (int)(s.gate_mode == MOE_GATE_ALL), p.logits,
                        p.aux, s.lb_coef, s.z_coef);
   else
     hipLaunchKernelGGL(router_bwd_kernel<float>, dim3(grid), dim3(256), 0, st, p.tok_ptr, p.tok_rows,
                        p.expert_of_row, p.gate_of_row, p.topk_idx, p.topk_gate, ds_part, nparts, pstride, s.T, s.E,
-                       s.k, ds_out, dlogits, (float*)dzq, ldz, (int)(s.gate_mode == MOE_GATE_ALL), p.logits,
+                       s.k, ds_out, dlogits, (float*)dzq, ldz, ld, (int)(s.gate_mode == MOE_GATE_ALL), p.logits,
                        p.aux, s.lb_coef, s.z_coef);
   return hipGetLastError();
 }
@@ -494,6 +542,20 @@ hipError_t launch_wgrad_chunks(const int32_t* offsets, int E, int kch, const Wgr
 hipError_t launch_wgrad_reduce(const WgradChunks& w, int E, int64_t mn, float* dw, hipStream_t st) {
   if (w.max_extra == 0) return hipSuccess;
   hipLaunchKernelGGL(wgrad_reduce_kernel, dim3(1024), dim3(256), 0, st, dw, w.part, w.slot_range, E, mn);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_dwg_reduce(const float* part, int nsplit, int64_t pstride, int E, int d, int lo_row,
+                                    float* out, hipStream_t st) {
+  const int64_t n = (int64_t)E * d;
+  hipLaunchKernelGGL(router_dwg_reduce_kernel, dim3(grid_for(n / 4, 256)), dim3(256), 0, st, part, nsplit, pstride,
+                     n, lo_row >= 0 ? (int64_t)lo_row * d : (int64_t)-1, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_wg2(const void* wg, int E, int ldz, int d, void* wg2, hipStream_t st) {
+  hipLaunchKernelGGL(router_wg2_kernel, dim3(grid_for((int64_t)2 * ldz * d / 8, 256)), dim3(256), 0, st,
+                     (const bf16_t*)wg, E, ldz, d, (bf16_t*)wg2);
   return hipGetLastError();
 }
 

@@ -251,14 +251,15 @@ hipError_t gemm_router_logits(const moe_shape& s, const void* x, const void* wg,
   return run<float, 128, 64, 4, 1, true, true, GROUP_NONE, EPI_LOGITS>(a, a.total_static, st);
 }
 
-// Dense router term of the input gradient: dxr = dzq W_g, K = E.
-hipError_t gemm_router_dx_dense(const moe_shape& s, const void* dzq, int ldz, const void* wg, float* dxr,
-                                hipStream_t st) {
+// Dense router term of the input gradient: dxr = dzq W, K = the dz columns (with
+// bf16 activations dz and its residual against W_g twice, so dxr = dz W_g to
+// 16 significant bits of dz).
+hipError_t gemm_router_dx_dense(const moe_shape& s, const void* dzq, const void* wg, float* dxr, hipStream_t st) {
   Args a = base_args();
-  a.A = dzq; a.lda = ldz;                // [T, K = E]
-  a.B = wg; a.ldb = s.d;                 // W_g [E, d] read as [K = E, N = d]
+  a.A = dzq; a.lda = router_dz_ld(s);    // [T, K]
+  a.B = wg; a.ldb = s.d;                 // [K, N = d]
   a.C = dxr; a.ldc = s.d;
-  a.M = s.T; a.N = s.d; a.K = s.E;
+  a.M = s.T; a.N = s.d; a.K = router_dz_rows(s);
   a.tilesM = ceil_div(s.T, 128); a.tilesN = ceil_div(s.d, 128);
   a.total_static = a.tilesM * a.tilesN;
   if (s.act == MOE_BF16) return run<bf16_t, 128, 128, 2, 2, true, false, GROUP_NONE, EPI_F32>(a, a.total_static, st);
@@ -266,7 +267,7 @@ hipError_t gemm_router_dx_dense(const moe_shape& s, const void* dzq, int ldz, co
 }
 
 int gemm_router_dwg_splits(const moe_shape& s) {
-  const int tiles = ceil_div(s.E, 128) * ceil_div(s.d, 128);
+  const int tiles = ceil_div(router_dz_rows(s), 128) * ceil_div(s.d, 128);
   int sp = ceil_div(512, tiles);
   const int maxsp = ceil_div(s.T, 256);
   if (sp > maxsp) sp = maxsp;
@@ -274,16 +275,16 @@ int gemm_router_dwg_splits(const moe_shape& s) {
   return sp;
 }
 
-// dW_g partials: part[split] [E, d] = dzq[K-slice]^T x[K-slice]
-hipError_t gemm_router_dwg(const moe_shape& s, const void* dzq, int ldz, const void* x, float* part,
-                           hipStream_t st) {
+// dW_g partials: part[split] [router_dz_rows, d] = dzq[K-slice]^T x[K-slice]; the
+// reduction adds the dz rows and (bf16) their residual rows
+hipError_t gemm_router_dwg(const moe_shape& s, const void* dzq, const void* x, float* part, hipStream_t st) {
   Args a = base_args();
-  a.A = dzq; a.lda = ldz;                // [K = T, M = E]
+  a.A = dzq; a.lda = router_dz_ld(s);    // [K = T, M]
   a.B = x; a.ldb = s.d;                  // [K = T, N = d]
-  a.C = part; a.ldc = s.d; a.c_kstride = (int64_t)s.E * s.d;
-  a.M = s.E; a.N = s.d; a.K = s.T;
+  a.M = router_dz_rows(s); a.N = s.d; a.K = s.T;
+  a.C = part; a.ldc = s.d; a.c_kstride = (int64_t)a.M * s.d;
   a.ksplit = gemm_router_dwg_splits(s);
-  a.tilesM = ceil_div(s.E, 128); a.tilesN = ceil_div(s.d, 128);
+  a.tilesM = ceil_div(a.M, 128); a.tilesN = ceil_div(s.d, 128);
   a.total_static = a.tilesM * a.tilesN * a.ksplit;
   if (s.act == MOE_BF16) return run<bf16_t, 128, 128, 2, 2, false, false, GROUP_NONE, EPI_F32>(a, a.total_static, st);
   return run<float, 128, 128, 2, 2, false, false, GROUP_NONE, EPI_F32>(a, a.total_static, st);

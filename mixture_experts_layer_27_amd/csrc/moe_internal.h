@@ -49,6 +49,15 @@ inline bool dense_router_grad(const moe_shape& s) {
   return s.gate_mode == MOE_GATE_ALL || s.lb_coef != 0.0f || s.z_coef != 0.0f;
 }
 
+// The router gradient dz as a GEMM operand dzq [T][router_dz_ld]: columns [0, ldz)
+// hold dz in the act dtype (zero past E); with bf16 activations columns
+// [ldz, 2 ldz) hold its bf16 rounding residual, and the router GEMMs treat the
+// two halves as one operand of router_dz_rows columns (W_g doubled to match).
+inline int router_ldz(const moe_shape& s) { return (s.E + 7) / 8 * 8; }
+inline bool router_dz_split(const moe_shape& s) { return s.act == MOE_BF16; }
+inline int router_dz_ld(const moe_shape& s) { return router_ldz(s) * (router_dz_split(s) ? 2 : 1); }
+inline int router_dz_rows(const moe_shape& s) { return router_dz_split(s) ? router_ldz(s) + s.E : s.E; }
+
 // Weight-gradient K chunks (see wgrad_chunks_kernel): tables in the backward
 // workspace, partial outputs for chunks past each expert's first.
 struct WgradChunks {
@@ -69,8 +78,14 @@ hipError_t launch_combine(const moe_shape& s, const void* y, const moe_plan& p, 
 hipError_t launch_router_dx(const moe_shape& s, const moe_plan& p, const void* dx_perm, const float* dz,
                             const void* wg, const float* dxr, void* dx, hipStream_t st);
 hipError_t launch_router_bwd(const moe_shape& s, const moe_plan& p, const float* ds_part, int nparts,
-                             float* ds_out, float* dlogits, void* dzq, int ldz, hipStream_t st);
+                             float* ds_out, float* dlogits, void* dzq, hipStream_t st);
 hipError_t launch_splitk_reduce(const float* part, int nsplit, int64_t n, float* out, hipStream_t st);
+// dW_g [E, d] = sum over splits of rows [0, E) (+ rows [lo_row, lo_row + E) when lo_row >= 0)
+// of the partials part[q] (stride pstride floats)
+hipError_t launch_router_dwg_reduce(const float* part, int nsplit, int64_t pstride, int E, int d, int lo_row,
+                                    float* out, hipStream_t st);
+// W_g doubled for the split dzq: [2 ldz, d] bf16, rows [0, E) and [ldz, ldz + E) = W_g, others 0
+hipError_t launch_router_wg2(const void* wg, int E, int ldz, int d, void* wg2, hipStream_t st);
 hipError_t launch_wgrad_chunks(const int32_t* offsets, int E, int kch, const WgradChunks& w, hipStream_t st);
 hipError_t launch_wgrad_reduce(const WgradChunks& w, int E, int64_t mn, float* dw, hipStream_t st);
 
@@ -99,12 +114,12 @@ hipError_t gemm_dw2(const moe_shape& s, const WgradChunks& w, const void* do_row
                     const void* ga, float* dw2, hipStream_t st);
 hipError_t gemm_router_logits(const moe_shape& s, const void* x, const void* wg, const float* bias,
                               const float* noise, float* logits, hipStream_t st);
-// dxr [T,d] fp32 = dzq [T, ldz] W_g (dense router gradients)
-hipError_t gemm_router_dx_dense(const moe_shape& s, const void* dzq, int ldz, const void* wg, float* dxr,
-                                hipStream_t st);
+// dxr [T,d] fp32 = dzq W (dense router gradients): K = router_dz_rows columns of dzq,
+// wg = W_g [E, d] (fp32) or the doubled W_g of launch_router_wg2 (bf16)
+hipError_t gemm_router_dx_dense(const moe_shape& s, const void* dzq, const void* wg, float* dxr, hipStream_t st);
 int gemm_router_dwg_splits(const moe_shape& s);
-hipError_t gemm_router_dwg(const moe_shape& s, const void* dzq, int ldz, const void* x, float* part,
-                           hipStream_t st);
+// split-K partials part[q] [router_dz_rows, d] = dzq[K-slice]^T x[K-slice]
+hipError_t gemm_router_dwg(const moe_shape& s, const void* dzq, const void* x, float* part, hipStream_t st);
 
 // ---- MXFP8 (mx.hip, gemm_mx.hip)
 // A quantised GEMM operand: codes [rows][K] (E4M3 bytes, K-contiguous) and

@@ -40,8 +40,11 @@ the design notes):
   padding adds the unselected tokens with the largest P (ties: smaller token
   first) with gate P_te / sum_{j in topk(t)} P_tj; kept pairs keep their gates.
 * Precision "contract": the values the GPU path stores in bf16 (H, A, Y, dH,
-  gA, dX_perm, and the router gradient used as a GEMM operand) are rounded to
-  bf16 (round-to-nearest-even) at the same points here; everything else is fp64.
+  gA, dX_perm) are rounded to bf16 (round-to-nearest-even) at the same points
+  here; everything else is fp64.  The router gradient dz enters the input- and
+  router-weight gradients unrounded: the GPU carries it into those GEMMs as an
+  unevaluated sum of two bf16 values (16 significant bits), whose residual is
+  far below the fp32 outputs' tolerance.
 * MXFP8 (OCP Microscaling v1.0, E4M3 elements, one E8M0 scale per 32 along K,
   shared exponent floor(log2 amax) - 8, saturating): see ``oracle/mx.py``.
 * Routing variants (``RouteOpts``; Beam blog sections 2.2, 2.3 and 3.3,
@@ -536,15 +539,14 @@ def backward(x, w_gate, w1, w2, plan: Plan, H, dout, prec: Precision = CONTRACT,
             dw2[e] = _mxk(do_perm[a:b], prec, 0).T @ _mxk(gA[a:b], prec, 0)
     dx_perm = prec.st(dx_perm)
     dz = router_backward(plan, dS, logits, opts)
-    dzq = prec.st(dz)                                # GEMM operand of the router terms
     dx = np.zeros((T, d))
     for t in range(T):
         for r in plan.tok_rows[plan.tok_ptr[t]:plan.tok_ptr[t + 1]]:
             dx[t] += dx_perm[r]
-    dx += dzq @ w_gate
-    dw_gate = dzq.T @ x
+    dx += dz @ w_gate
+    dw_gate = dz.T @ x
     return {"dS": dS, "dH": dH, "gA": gA, "dx_perm": dx_perm, "dlogits": dz,
-            "dx": dx, "dw_gate": dw_gate, "dw1": dw1, "dw2": dw2, "A": A}
+            "dx": dx, "dw_gate": dw_gate, "dw1": dw1, "dw2": dw2, "A": A, "dAp": dAp}
 
 
 def layer(x, w_gate, bias, w1, w2, k, dout=None, round_tile=0, prec: Precision = CONTRACT,

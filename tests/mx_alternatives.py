@@ -12,13 +12,17 @@ top of a binade.
 
 Each decision is therefore re-taken with its input moved by +-WINDOW (relative).
 Where the outcome changes, the changed dequantised values minus the oracle's
-give a delta that enters the GEMM output linearly.  The reference a GPU output
-vector is compared with is the oracle's vector plus those deltas that bring it
-closer to the GPU's (best first, each taken delta reducing the squared
-residual by at least half its own squared norm).  Every delta is computed by the oracle from the
-oracle's own values; the GPU output only selects among them.  Inputs of the layer
-(x, dout, the weights) are never decided this way: both sides quantise the same
-bf16 values.
+give a delta that enters the GEMM output linearly.  Only deltas that move some
+element of the output vector by at least half the max-abs tolerance are
+candidates: a smaller one cannot decide a comparison by itself, and admitting
+every small delta would let the selection fit the residual's noise (a delta
+smaller than the noise passes the test below by chance about half the time).
+The reference a GPU output vector is compared with is the oracle's vector plus
+those candidates that bring it closer to the GPU's (best first, each taken delta
+reducing the squared residual by at least half its own squared norm).  Every
+delta is computed by the oracle from the oracle's own values; the GPU output
+only selects among them.  Inputs of the layer (x, dout, the weights) are never
+decided this way: both sides quantise the same bf16 values.
 """
 from __future__ import annotations
 
@@ -62,19 +66,23 @@ def block_candidates(blk):
     return out
 
 
-def _select(got, ref, D):
+def _select(got, ref, D, atol=0.0):
     """ref plus a subset of the deltas (rows of D) chosen best first: repeatedly
     take the delta that most reduces |got - ref|^2, while the reduction is at
     least half of that delta's own |d|^2 (a delta that only fits noise, or one
-    that overlaps deltas already taken, is left out)."""
+    that overlaps deltas already taken, is left out).  Deltas whose largest
+    element is below atol / 2 are not candidates.  Returns (adjusted ref,
+    indices of the deltas taken)."""
     if len(D) == 0:
-        return ref
+        return ref, []
     D = np.asarray(D)
+    big = np.abs(D).max(axis=1) >= 0.5 * atol
     r = np.asarray(got, np.float64) - ref
     n2 = np.einsum("ij,ij->i", D, D)
     c = D @ r
     out = ref.copy()
-    free = n2 > 0
+    free = (n2 > 0) & big
+    taken = []
     for _ in range(len(D)):
         gain = np.where(free, 2.0 * c - n2, -np.inf)
         i = int(np.argmax(gain))
@@ -83,13 +91,39 @@ def _select(got, ref, D):
         out = out + D[i]
         c = c - D @ D[i]
         free[i] = False
-    return out
+        taken.append(i)
+    return out, taken
+
+
+class Tally:
+    """What the adjustment did for one output tensor: decisions that could go
+    either way (candidates), deltas taken, and the distinct 32-value blocks of the
+    computed operand those deltas lie in, out of all its blocks."""
+
+    def __init__(self, operand_elements):
+        self.candidates = 0
+        self.significant = 0
+        self.taken = 0
+        self.blocks = set()
+        self.total_blocks = -(-int(operand_elements) // BLOCK)
+
+    def add(self, ids, taken, significant=None):
+        self.candidates += len(ids)
+        self.significant += len(ids) if significant is None else int(significant)
+        self.taken += len(taken)
+        self.blocks.update(ids[i] for i in taken)
+
+    def as_dict(self):
+        return {"mx_candidates": self.candidates, "mx_significant": self.significant, "mx_deltas_taken": self.taken,
+                "mx_blocks_touched": len(self.blocks), "mx_blocks_total": self.total_blocks,
+                "mx_block_fraction": len(self.blocks) / max(1, self.total_blocks)}
 
 
 def operand_deltas(v, axis, other):
-    """Yields (index j along the non-block axis, output deltas [m, width]) for the
-    computed operand ``v`` (2-D) quantised in blocks of 32 along ``axis`` (from
-    0): its block at positions sl multiplies ``other[sl, :]``."""
+    """Yields (index j along the non-block axis, output deltas [m, width], block id
+    of each delta) for the computed operand ``v`` (2-D) quantised in blocks of 32
+    along ``axis`` (from 0): its block at positions sl multiplies ``other[sl, :]``.
+    A block id is (j, first position of the block)."""
     v = np.asarray(v, np.float64)
     vt = v if axis == 0 else v.T
     by = {}
@@ -104,59 +138,74 @@ def operand_deltas(v, axis, other):
                 D[n] = d @ other[lo:lo + len(d), :]
             else:
                 D[n] = d * other[lo + i, :]
-        yield j, D
+        yield j, D, [(j, lo) for lo, _, _ in recs]
 
 
 # ---------------------------------------------------------------- per output
 
 
-def adjust_forward(plan, y_gpu, o_gpu, Y, O, A, w2_mx):
+def _nsig(D, atol):
+    return int((np.abs(np.asarray(D)).max(axis=1) >= 0.5 * atol).sum()) if len(D) else 0
+
+
+def adjust_forward(plan, y_gpu, o_gpu, Y, O, A, w2_mx, atol=0.0):
     """Y rows = A rows (quantised along f) times W2_e^T (w2_mx(e): oracle MX round
-    trip of W2_e [d, f]); O sums the gated rows of each token."""
+    trip of W2_e [d, f]); O sums the gated rows of each token.  Returns
+    (Y reference, O reference, Tally)."""
     Yadj = np.array(Y, np.float64, copy=True)
+    tally = Tally(np.asarray(A).size)
     for e in range(plan.E):
         a, b = int(plan.offsets[e]), int(plan.offsets[e + 1])
         if a == b:
             continue
-        for r, D in operand_deltas(A[a:b], 1, w2_mx(e).T):
-            Yadj[a + r] = _select(np.asarray(y_gpu[a + r], np.float64), Yadj[a + r], D)
+        for r, D, ids in operand_deltas(A[a:b], 1, w2_mx(e).T):
+            Yadj[a + r], taken = _select(np.asarray(y_gpu[a + r], np.float64), Yadj[a + r], D, atol)
+            tally.add([(a + r, lo) for _, lo in ids], taken, _nsig(D, atol))
     Oadj = np.array(O, np.float64, copy=True)
     g = plan.gate_of_row
     for t in range(plan.T):
         for r in plan.tok_rows[plan.tok_ptr[t]:plan.tok_ptr[t + 1]]:
             Oadj[t] += g[r] * (Yadj[r] - Y[r])
-    return Yadj, Oadj
+    return Yadj, Oadj, tally
 
 
-def adjust_dx(plan, dx_gpu, dx_ref, dH, w1_mx_k):
+def adjust_dx(plan, dx_gpu, dx_ref, dH, w1_mx_k, atol=0.0):
     """dx_perm rows = dH rows (quantised along 2f) times W1_e (w1_mx_k(e): oracle
-    MX round trip of W1_e [2f, d] along 2f); dx sums the rows of each token."""
+    MX round trip of W1_e [2f, d] along 2f); dx sums the rows of each token.
+    Returns (dx reference, Tally)."""
     per_row = {}
+    tally = Tally(np.asarray(dH).size)
     for e in range(plan.E):
         a, b = int(plan.offsets[e]), int(plan.offsets[e + 1])
         if a == b:
             continue
-        for r, D in operand_deltas(dH[a:b], 1, w1_mx_k(e)):
-            per_row[a + r] = D
+        for r, D, ids in operand_deltas(dH[a:b], 1, w1_mx_k(e)):
+            per_row[a + r] = (D, [(a + r, lo) for _, lo in ids])
     adj = np.array(dx_ref, np.float64, copy=True)
     for t in range(plan.T):
-        D = [per_row[int(r)] for r in plan.tok_rows[plan.tok_ptr[t]:plan.tok_ptr[t + 1]] if int(r) in per_row]
-        if D:
-            adj[t] = _select(np.asarray(dx_gpu[t], np.float64), adj[t], np.concatenate(D))
-    return adj
+        rows = [int(r) for r in plan.tok_rows[plan.tok_ptr[t]:plan.tok_ptr[t + 1]] if int(r) in per_row]
+        if rows:
+            D = np.concatenate([per_row[r][0] for r in rows])
+            ids = [i for r in rows for i in per_row[r][1]]
+            adj[t], taken = _select(np.asarray(dx_gpu[t], np.float64), adj[t], D, atol)
+            tally.add(ids, taken, _nsig(D, atol))
+    return adj, tally
 
 
-def adjust_wgrad(computed, other, got, ref, rows):
+def adjust_wgrad(computed, other, got, ref, rows, atol=0.0):
     """Weight gradient of one expert, both operands quantised along its tokens.
 
     dW1_e = dH_e^T X_e: computed = dH_e [n, 2f], other = X_e [n, d]; column c of
     dH_e moves row c of dW1_e (rows=True).  dW2_e = dO_e^T gA_e: computed = gA_e
-    [n, f], other = dO_e [n, d]; column j of gA_e moves column j of dW2_e."""
+    [n, f], other = dO_e [n, d]; column j of gA_e moves column j of dW2_e.
+    Returns (reference, Tally)."""
     oq = mx.mx_roundtrip(other, axis=0)
     adj = np.array(ref, np.float64, copy=True)
-    for j, D in operand_deltas(computed, 0, oq):
+    tally = Tally(np.asarray(computed).size)
+    for j, D, ids in operand_deltas(computed, 0, oq):
         if rows:
-            adj[j] = _select(np.asarray(got[j], np.float64), adj[j], D)
+            adj[j], taken = _select(np.asarray(got[j], np.float64), adj[j], D, atol)
         else:
-            adj[:, j] = _select(np.asarray(got[:, j], np.float64), adj[:, j], D)
-    return adj
+            adj[:, j], taken = _select(np.asarray(got[:, j], np.float64), adj[:, j], D, atol)
+        tally.add(ids, taken, _nsig(D, atol))
+    return adj, tally

@@ -83,3 +83,23 @@ def test_argument_errors_return_before_launch(b):
     assert b._lib.moe_quantize_mx(fake, 64, 64, 2, fake, fake, None) == 1                     # k_axis
     empty = b.MoePlan()
     assert b._lib.moe_unpermute_combine(ctypes.byref(s), fake, ctypes.byref(empty), fake, None) == 1
+
+
+def test_trace_validation_returns_before_launch(b):
+    """A trace whose events are missing is rejected on the host (nothing launched)."""
+    s = b.make_shape(64, 128, 8, 2, 128, b.MOE_BF16)
+    plan = b.MoePlan()
+    fake = ctypes.c_void_p(1 << 20)
+    assert b._lib.moe_plan_init(ctypes.byref(s), fake, 1 << 30, ctypes.byref(plan)) == 0
+    handles = (ctypes.c_void_p * 4)()                      # all NULL
+    tr = b.MoeTrace(ctypes.cast(handles, ctypes.POINTER(ctypes.c_void_p)), 4, 0)
+    assert b._lib.moe_grouped_gemm_swiglu_traced(ctypes.byref(s), fake, fake, fake, ctypes.byref(plan), fake, fake,
+                                                 fake, 1 << 30, None, ctypes.byref(tr)) == 1
+    assert b._lib.moe_backward_traced(ctypes.byref(s), fake, fake, fake, fake, ctypes.byref(plan), fake, None, None,
+                                      fake, fake, fake, fake, fake, None, None, fake, 1 << 40, None,
+                                      ctypes.byref(tr)) == 1
+    neg = b.MoeTrace(ctypes.cast(handles, ctypes.POINTER(ctypes.c_void_p)), -1, 0)
+    assert b._lib.moe_grouped_gemm_swiglu_gather_traced(ctypes.byref(s), fake, fake, fake, ctypes.byref(plan), fake,
+                                                        fake, fake, 1 << 30, None, ctypes.byref(neg)) == 1
+    assert tr.count == 0
+

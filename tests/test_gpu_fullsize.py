@@ -2,26 +2,30 @@
 
 The oracle cannot run the whole layer at these sizes in seconds, so: every
 routing integer (top-k, counts, offsets, all plan maps, token rounding) is
-compared bit for bit over all tokens; outputs and gradients are compared on a
-seeded sample of tokens (all of their rows) and on every element of the
-weight gradients of a sample of experts, each computed by the oracle one by
-one; dW_g is checked through the identity dW_g = bf16(dlogits)^T X on all tokens.
+compared bit for bit over all tokens; outputs and input gradients are compared
+on every row of a sub-plan of tokens: a seeded sample plus the tokens below; every element of the weight
+gradients of the busiest and one random expert; and the router-weight gradient
+rows of those experts, which the oracle computes from exactly the tokens that
+reach them (the tokens with a row at the expert or the expert in their top-k:
+every other token's logit gradient at that expert is zero).  Each of these is
+computed by the oracle on a sub-plan (the same routing decisions, fewer rows).
 With MXFP8 expert GEMMs the references of Y, O, dx and dW take the other outcome
 of quantisation decisions that sit on a boundary where the GPU's does
-(mx_alternatives)."""
+(mx_alternatives), and the unadjusted errors are recorded beside them."""
 import numpy as np
 import pytest
 import torch
 
 import mx_alternatives as mxa
-from helpers import LazyExperts, assert_close, make_inputs, precision, tol
+from flip_envelope import Envelope
+from helpers import Checks, LazyExperts, make_inputs, precision, tokens_reaching, tol
 from mixture_experts_layer_27_amd import configs
 from oracle import moe_oracle as mo
 from oracle import mx
 
 pytestmark = pytest.mark.gpu
 
-FULL = ["fine_e128", "sparse_e256_round", "coarse_e8", "fine_e128_zipf", "fine_e128_mxfp8"]
+FULL = ["fine_e128", "sparse_e256", "sparse_e256_round", "coarse_e8", "fine_e128_zipf", "fine_e128_mxfp8"]
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -37,6 +41,7 @@ def test_max_tokens_sampled():
 def check_sampled(cfg):
     from mixture_experts_layer_27_amd import binding
     name = cfg.name
+    assert cfg.gate == "topk" and not cfg.lb_coef and not cfg.z_coef, "sampled dW_g needs a sparse dz"
     print(f"[fullsize] {name}: generating inputs", flush=True)
     g = make_inputs(cfg)
     run = binding.LayerRun(cfg, g)
@@ -62,50 +67,70 @@ def check_sampled(cfg):
     W1, W2 = LazyExperts(g["w1"]), LazyExperts(g["w2"])
     rng = np.random.default_rng(2024)
     is_mx = cfg.gemm == "mxfp8"
+    check = Checks(cfg)
     # fewer samples with MXFP8: the oracle re-quantises every touched expert's weights
-    toks = np.sort(rng.choice(cfg.T, 8 if is_mx else 32, replace=False))
-    sub = mo.sub_plan(plan, tokens=toks)
-    print(f"[fullsize] {name}: oracle on {len(toks)} tokens ({sub.N} rows)", flush=True)
+    toks = np.sort(rng.choice(cfg.T, 16 if is_mx else 128, replace=False))
+    experts = [int(np.argmax(plan.counts))] + ([] if is_mx else [int(rng.integers(cfg.E))])
+    dwg_toks = [tokens_reaching(plan, e) for e in experts] if cfg.backward else []
+    sub = mo.sub_plan(plan, tokens=np.unique(np.concatenate([toks] + dwg_toks)))
+    print(f"[fullsize] {name}: oracle on {sub.N} rows ({len(toks)} sampled tokens, "
+          f"router-weight gradients of experts {experts})", flush=True)
     fw = mo.forward(x, W1, W2, sub, prec)
     row_of = {(int(t), int(e)): r for r, (t, e) in enumerate(zip(plan.token_of_row, plan.expert_of_row))}
     rows = np.array([row_of[(int(t), int(e))] for t, e in zip(sub.token_of_row, sub.expert_of_row)])
-    t = tol(cfg)
+    stoks = np.unique(sub.token_of_row)        # every token of the sub-plan has all its rows there
     mx_w = lambda w, axis: (lambda e: mx.mx_roundtrip(w[e], axis=axis))
     o_gpu = run.out.double().cpu().numpy()
-    O = fw["O"]
+    y_sub = run.y[rows].double().cpu().numpy()
+    h_sub = run.h[rows].double().cpu().numpy()
+    Y, O = fw["Y"], fw["O"]
+    atol = tol(cfg)[0]
+    dout = f64(g["dout"]) if run.has_bwd else None
+    bw = mo.backward(x, wg, W1, W2, sub, fw["H"], dout, prec, weight_grads=False) if run.has_bwd else None
+    env = Envelope(sub, x, wg, W1, W2, fw, bw, dout)
+    T, d = cfg.T, cfg.d
+    on_toks = lambda fn, width: (lambda idx: fn(stoks[idx // width] * width + idx % width))
     if is_mx:
-        y_sub = run.y[rows].double().cpu().numpy()
-        Y, O = mxa.adjust_forward(sub, y_sub, None, fw["Y"], O, fw["A"], mx_w(W2, 1))
-        assert_close("Y", y_sub, Y, *t)
-    assert_close("O", o_gpu[toks], O[toks], *t)
-    assert_close("H", run.h[rows].double().cpu().numpy(), fw["H"], *t)
+        Ya, Oa, tally = mxa.adjust_forward(sub, y_sub, None, Y, O, fw["A"], mx_w(W2, 1), atol=atol)
+        check("Y", y_sub, Ya, Y, tally, env=env.Y)
+        check("O", o_gpu[stoks], Oa[stoks], O[stoks], env=on_toks(env.O, d))
+    else:
+        check("Y", y_sub, Y, env=env.Y)
+        check("O", o_gpu[stoks], O[stoks], env=on_toks(env.O, d))
+    check("H", h_sub, fw["H"])
     if not run.has_bwd:
+        check.done()
         return
-    dout = f64(g["dout"])
-    bw = mo.backward(x, wg, W1, W2, sub, fw["H"], dout, prec, weight_grads=False)
     dx_gpu = run.dx.double().cpu().numpy()
-    dx_ref = bw["dx"]
+    check("dS", run.ds[rows].double().cpu().numpy(), bw["dS"], env=env.dS)
+    check("dlogits", run.dlogits[stoks].double().cpu().numpy(), bw["dlogits"][stoks],
+          env=on_toks(env.dlogits, cfg.E))
     if is_mx:
-        dx_ref = mxa.adjust_dx(sub, dx_gpu, dx_ref, bw["dH"], mx_w(W1, 0))
-    assert_close("dS", run.ds[rows].double().cpu().numpy(), bw["dS"], *t)
-    assert_close("dlogits", run.dlogits[toks].double().cpu().numpy(), bw["dlogits"][toks], *t)
-    assert_close("dx", dx_gpu[toks], dx_ref[toks], *t)
+        dxa, t_dx = mxa.adjust_dx(sub, dx_gpu, bw["dx"], bw["dH"], mx_w(W1, 0), atol=atol)
+        check("dx", dx_gpu[stoks], dxa[stoks], bw["dx"][stoks], t_dx, env=on_toks(env.dx, d))
+    else:
+        check("dx", dx_gpu[stoks], bw["dx"][stoks], env=on_toks(env.dx, d))
+    # router-weight gradient rows: the sub-plan holds every token reaching these experts
+    check("dw_gate", run.dw_gate[experts].double().cpu().numpy(), bw["dw_gate"][experts],
+          env=lambda idx: env.dw_gate(idx, experts))
     # every element of the weight gradients of the busiest expert and (bf16) a random one
-    experts = [int(np.argmax(plan.counts))] + ([] if is_mx else [int(rng.integers(cfg.E))])
     for e in experts:
         sub_e = mo.sub_plan(plan, experts=[e])
         print(f"[fullsize] {name}: oracle weight gradients of expert {e} ({sub_e.N} rows)", flush=True)
         fw_e = mo.forward(x, W1, W2, sub_e, prec)
         bw_e = mo.backward(x, wg, W1, W2, sub_e, fw_e["H"], dout, prec, weight_grads=[e])
+        env_e = Envelope(sub_e, x, wg, W1, W2, fw_e, bw_e, dout)
         dw1 = run.dw1[e].double().cpu().numpy()
         dw2 = run.dw2[e].double().cpu().numpy()
         ref1, ref2 = bw_e["dw1"][e], bw_e["dw2"][e]
         if is_mx:
-            a, b = int(sub_e.offsets[e]), int(sub_e.offsets[e + 1])
-            ref1 = mxa.adjust_wgrad(bw_e["dH"][a:b], fw_e["x_perm"][a:b], dw1, ref1, rows=True)
-            ref2 = mxa.adjust_wgrad(bw_e["gA"][a:b], dout[sub_e.token_of_row[a:b]], dw2, ref2, rows=False)
-        assert_close(f"dw1[{e}]", dw1, ref1, *t)
-        assert_close(f"dw2[{e}]", dw2, ref2, *t)
-    # dW_g = bf16(dlogits)^T X over all tokens (the router-weight GEMM on the GPU's own dz)
-    dzq = run.dlogits.cpu().to(torch.bfloat16).double().numpy() if cfg.act == "bf16" else f64(run.dlogits.cpu())
-    assert_close("dw_gate", run.dw_gate.double().cpu().numpy(), dzq.T @ x)
+            lo, hi = int(sub_e.offsets[e]), int(sub_e.offsets[e + 1])
+            a1, t1 = mxa.adjust_wgrad(bw_e["dH"][lo:hi], fw_e["x_perm"][lo:hi], dw1, ref1, rows=True, atol=atol)
+            a2, t2 = mxa.adjust_wgrad(bw_e["gA"][lo:hi], dout[sub_e.token_of_row[lo:hi]], dw2, ref2, rows=False,
+                                      atol=atol)
+            check(f"dw1[{e}]", dw1, a1, ref1, t1, env=lambda idx: env_e.dw1(e, idx))
+            check(f"dw2[{e}]", dw2, a2, ref2, t2, env=lambda idx: env_e.dw2(e, idx))
+        else:
+            check(f"dw1[{e}]", dw1, ref1, env=lambda idx: env_e.dw1(e, idx))
+            check(f"dw2[{e}]", dw2, ref2, env=lambda idx: env_e.dw2(e, idx))
+    check.done()

@@ -17,6 +17,7 @@ import torch
 from oracle import moe_oracle as mo
 from oracle import mx
 from oracle.tie_clearance import clear_ties, topk_tie_tokens
+from helpers import tokens_reaching
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -519,3 +520,112 @@ def test_tie_clearance_leaves_margin():
     x2, n = clear_ties(x, wg, b, 4, redraw, delta_z=5e-2)
     assert n > 0
     assert topk_tie_tokens(mo.router_logits(x2, wg, b), 4, 5e-2).size == 0
+
+
+# ---------------------------------------------------------------- more pins
+
+
+@pytest.mark.parametrize("k", [1, 2])
+def test_rounding_rounds_down_when_nearest_multiple_exceeds_T(k):
+    """An expert chosen by every token: its nearest multiple of the tile lies past T,
+    so it takes the largest multiple that fits.  The target is checked against an
+    enumeration of every multiple of the tile in [0, T] (nearest, half up), and the
+    kept pairs against the brute-force subset search."""
+    T, E, tile = 6, 3, 4
+    r = _rng(30 + k)
+    z = r.standard_normal((T, E))
+    z[:, 0] += 20.0                                   # expert 0 first for every token
+    idx, S, P = mo.topk_softmax(z, k)
+    plan = mo.round_tokens(idx, S, P, E, tile)
+    assert plan.counts_raw[0] == T
+    for e in range(E):
+        n = int(plan.counts_raw[e])
+        fits = [m for m in range(0, T + 1, tile)]
+        # nearest multiple that fits; on a tie the larger one
+        want = min(fits, key=lambda m: (abs(m - n), -m))
+        assert plan.counts[e] == want, (e, n, plan.counts[e], want)
+    assert plan.counts[0] == 4                        # 8 would be nearest, but 8 > T = 6
+    want = _brute_round(idx, P, S, E, tile)
+    got = {(int(t), int(e)): g for t, e, g in zip(plan.token_of_row, plan.expert_of_row, plan.gate_of_row)}
+    assert got.keys() == want.keys()
+
+
+def test_sub_plan_keeps_rows_and_results():
+    """A sub-plan holds exactly the rows of the chosen tokens (or experts), in the
+    same order, and the layer evaluated on it gives those tokens' outputs and
+    gradients, and those experts' weight gradients, as on the full plan.  The
+    router-weight gradient row of an expert needs only the tokens with a row there
+    or the expert in their top-k (every other logit gradient at it is zero)."""
+    x, wg, b, w1, w2, dout, redraw = _tiny_layer(T=40, d=8, E=6, k=2, f=4, seed=31, bias=True)
+    x, _ = clear_ties(x, wg, b, 2, redraw, round_tile=4, delta_z=1e-3, delta_p=1e-3)
+    for tile in (0, 4):
+        full = mo.layer(x, wg, b, w1, w2, 2, dout=dout, round_tile=tile, prec=mo.CONTRACT)
+        plan = full["plan"]
+        toks = np.array([1, 5, 6, 17, 33])
+        sub = mo.sub_plan(plan, tokens=toks)
+        keep = np.isin(plan.token_of_row, toks)
+        np.testing.assert_array_equal(sub.token_of_row, plan.token_of_row[keep])
+        np.testing.assert_array_equal(sub.expert_of_row, plan.expert_of_row[keep])
+        np.testing.assert_array_equal(sub.gate_of_row, plan.gate_of_row[keep])
+        fw = mo.forward(x, w1, w2, sub, mo.CONTRACT)
+        bw = mo.backward(x, wg, w1, w2, sub, fw["H"], dout, mo.CONTRACT, weight_grads=False)
+        for key, a_, b_ in (("O", fw["O"], full["O"]), ("dx", bw["dx"], full["dx"]),
+                            ("dlogits", bw["dlogits"], full["dlogits"])):
+            np.testing.assert_allclose(a_[toks], b_[toks], rtol=1e-12, atol=1e-12, err_msg=key)
+        np.testing.assert_allclose(fw["H"], full["H"][keep], rtol=1e-12, atol=1e-12)
+        for e in range(plan.E):
+            sub_e = mo.sub_plan(plan, experts=[e])
+            assert (sub_e.expert_of_row == e).all() and sub_e.N == plan.counts[e]
+            fe = mo.forward(x, w1, w2, sub_e, mo.CONTRACT)
+            be = mo.backward(x, wg, w1, w2, sub_e, fe["H"], dout, mo.CONTRACT, weight_grads=[e])
+            np.testing.assert_allclose(be["dw1"][e], full["dw1"][e], rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(be["dw2"][e], full["dw2"][e], rtol=1e-12, atol=1e-12)
+            reach = tokens_reaching(plan, e)
+            sr = mo.sub_plan(plan, tokens=reach)
+            fr = mo.forward(x, w1, w2, sr, mo.CONTRACT)
+            br = mo.backward(x, wg, w1, w2, sr, fr["H"], dout, mo.CONTRACT, weight_grads=False)
+            np.testing.assert_allclose(br["dw_gate"][e], full["dw_gate"][e], rtol=1e-12, atol=1e-12)
+
+
+def test_contract_rounding_placement_torch():
+    """The contract's bf16 storage points re-derived with torch (float64 arithmetic,
+    torch's bf16 conversion, the SiLU derivative from autograd): H rounded after
+    the up GEMM; A from the rounded H, then rounded; Y rounded; dS from the
+    unrounded dA' and the rounded A; dH and gA rounded; dX_perm rounded; the router
+    gradient dz entering dx and dW_g unrounded.  Values must agree to float64
+    round-off and the rounded ones bit for bit."""
+    x, wg, b, w1, w2, dout, redraw = _tiny_layer(T=24, d=8, E=4, k=2, f=6, seed=32, bias=True)
+    x, _ = clear_ties(x, wg, b, 2, redraw)
+    out = mo.layer(x, wg, b, w1, w2, 2, dout=dout, prec=mo.CONTRACT)
+    plan = out["plan"]
+    q = lambda t: t.to(torch.bfloat16).double()
+    tor = torch.from_numpy(plan.token_of_row.astype(np.int64))
+    X, DO = torch.from_numpy(x), torch.from_numpy(dout)
+    g = torch.from_numpy(plan.gate_of_row)
+    f = w2.shape[2]
+    xp, dop = X[tor], DO[tor]
+    ex = torch.from_numpy(plan.expert_of_row.astype(np.int64))
+    W1, W2 = torch.from_numpy(w1)[ex], torch.from_numpy(w2)[ex]     # per-row expert weights
+    H = q(torch.einsum("rod,rd->ro", W1, xp))
+    hg = H[:, :f].clone().requires_grad_(True)
+    act = torch.nn.functional.silu(hg)
+    (dsilu,) = torch.autograd.grad(act.sum(), hg)
+    act = act.detach()
+    A = q(act * H[:, f:])
+    Y = q(torch.einsum("rdf,rf->rd", W2, A))
+    dAp = torch.einsum("rdf,rd->rf", W2, dop)
+    dS = (dAp * A).sum(1)
+    dA = g[:, None] * dAp
+    dH = q(torch.cat([dA * H[:, f:] * dsilu, dA * act], 1))
+    gA = q(g[:, None] * A)
+    dxp = q(torch.einsum("rod,ro->rd", W1, dH))
+    dz = torch.from_numpy(out["dlogits"])
+    dx = torch.zeros_like(X).index_add(0, tor, dxp) + dz @ torch.from_numpy(wg)
+    dwg = dz.T @ X
+    for key, ref, rounded in (("H", H, True), ("A", A, True), ("Y", Y, True), ("dS", dS, False),
+                              ("dH", dH, True), ("gA", gA, True), ("dx_perm", dxp, True), ("dx", dx, False),
+                              ("dw_gate", dwg, False)):
+        if rounded:
+            np.testing.assert_array_equal(out[key], ref.numpy(), err_msg=key)
+        else:
+            np.testing.assert_allclose(out[key], ref.numpy(), rtol=1e-12, atol=1e-12, err_msg=key)
