@@ -5,13 +5,28 @@ plan) [+ token rounding], permute, grouped SwiGLU expert GEMMs, combine, and
 the full backward.  Inputs are synthetic (seeded), already resident in HBM when
 the timed region starts.  Prints ONE JSON line.
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--config fine_e128]
+The headline workload is the largest forward+backward one that fits one GPU
+(sparse_e256: T=32768, d_model=4096, E=256, top-8, d_ff=512).  The other
+workloads (coarse_e8 forward, fine_e128, its Zipf-imbalanced variant, the
+token-rounded sparse_e256 and fine_e128 with MXFP8 expert GEMMs) are timed the
+same way and reported under "sub_results".
+
+Timing: W warm-up steps, then K timed steps bracketed by synchronisations;
+each step's device time comes from HIP events on the compute stream and the
+reported step time is the median (p10/p90 beside it).  The expert-GEMM call and
+the backward run through their *_traced entry points, which record events
+between their kernels, so every kernel's mean device time over the timed
+steps is known; the roofline entry is for the kernel with the largest mean.
+
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--config sparse_e256] [--no-sub]
 """
 from __future__ import annotations
 
 import argparse
 import json
 import os
+import statistics
+import subprocess
 import sys
 import time
 
@@ -19,45 +34,25 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MoE layer tokens/s fwd+bwd at 1 GPU; grouped-GEMM % MFMA peak; permute GB/s"
+HEADLINE = "sparse_e256"
+SUB_CONFIGS = ("coarse_e8", "fine_e128", "fine_e128_zipf", "sparse_e256_round", "fine_e128_mxfp8")
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 (MXFP8) MFMA
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 COPY_BYTES = 256 << 20
-
-
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "moe_layer_fine_e128_forward_gemm_hbm_traffic.md")
-
-
-def recorded_traffic(workload):
-    """Calibrated HBM bytes per forward expert-GEMM call from the committed
-    FETCH_SIZE/WRITE_SIZE summary, or None when that summary is for another
-    workload or the kernel sources changed since the counters were taken."""
-    import hashlib
-    try:
-        kv = {}
-        for line in open(TRAFFIC_FILE):
-            if ":" in line and not line.startswith((" ", "|", "#")):
-                k, v = line.split(":", 1)
-                kv[k.strip()] = v.strip()
-        if kv.get("workload") != workload:
-            return None
-        h = hashlib.sha256()
-        for src in kv["kernel_sources"].split():
-            h.update(open(os.path.join(ROOT, src), "rb").read())
-        if h.hexdigest() != kv["kernel_sources_sha256"]:
-            return None
-        return float(kv["traffic_bytes_per_call"])
-    except (OSError, KeyError, ValueError):
-        return None
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="fine_e128")
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default=HEADLINE)
+    ap.add_argument("--no-sub", action="store_true", help="skip the other workloads")
+    ap.add_argument("--sub-steps", type=int, default=30)
+    ap.add_argument("--sub-warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fused-gather", choices=("auto", "on", "off"), default="auto",
                     help="on: the forward reads x through the plan inside the expert GEMMs (bf16) or the MXFP8 "
@@ -70,10 +65,51 @@ def parse():
     return ap.parse_args()
 
 
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------- host facts
+
+
+def gpu_clocks():
+    """Shader/memory clocks and power from the SMI tools (whatever answers)."""
+    for cmd in (["amd-smi", "metric", "-g", "0", "-c", "-p", "--json"], ["amd-smi", "metric", "-c", "-p", "--json"],
+                ["rocm-smi", "--showclocks", "--showpower", "--json"]):
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=30)
+        except (OSError, subprocess.TimeoutExpired):
+            continue
+        if r.returncode == 0 and r.stdout.strip():
+            try:
+                return {"tool": " ".join(cmd), "reading": json.loads(r.stdout)}
+            except ValueError:
+                return {"tool": " ".join(cmd), "reading": r.stdout.strip()[:2000]}
+    return None
+
+
+def cpu_facts():
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = []
+    try:
+        import threadpoolctl
+        for i in threadpoolctl.threadpool_info():
+            blas.append({k: i.get(k) for k in ("internal_api", "version", "num_threads", "threading_layer")})
+    except Exception:
+        pass
+    return {"os_cpu_count": os.cpu_count(), "cpu_model": model, "blas": blas}
+
+
 def cpu_baseline(cfg, g, tokens):
     """The CPU oracle (float64 numpy, contract precision) on the first `tokens`
     tokens of the same workload: forward + backward, timed on the host cores."""
-    import numpy as np
     import threadpoolctl
     from oracle import moe_oracle as mo
 
@@ -88,28 +124,291 @@ def cpu_baseline(cfg, g, tokens):
              prec=mo.MX_CONTRACT if cfg.gemm == "mxfp8" else (mo.CONTRACT if cfg.act == "bf16" else mo.TRUTH))
     dt = time.perf_counter() - t0
     return {"value": tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"first {tokens} of {cfg.T} tokens of {cfg.name} (same weights), fwd+bwd, "
-                      f"float64 numpy{', MXFP8 operands' if cfg.gemm == 'mxfp8' else ''}, {dt:.1f} s"}
+            "sample": f"first {tokens} of {cfg.T} tokens of {cfg.name} (same weights, routed among themselves), "
+                      f"fwd+bwd, float64 numpy{', MXFP8 operands' if cfg.gemm == 'mxfp8' else ''}, {dt:.1f} s",
+            "seconds": dt, **cpu_facts()}
 
 
-def activation_bytes(cfg, rows, plan_bytes, fwd_ws_bytes):
-    """Bytes one layer keeps alive from the forward to the backward (weights and
-    their gradients excluded).  The conventional layer keeps X_perm, H, A and the
-    expert outputs Y, because it takes the router-score gradient as <dO, Y>; this
-    one takes it as <dA', A> with A recomputed from H (SonicMoE article, section
-    1), so it needs only the layer input x, the routing plan and H.  Handing the
-    backward the forward's x_perm (and, with MXFP8, the forward workspace with
-    the backward-orientation codes) keeps those alive too, to save work."""
-    e = 2 if cfg.act == "bf16" else 4
-    x, x_perm = cfg.T * cfg.d * e, rows * cfg.d * e
-    H, A, Y = rows * 2 * cfg.f * e, rows * cfg.f * e, rows * cfg.d * e
-    minimal = x + plan_bytes + H
-    store_y = x + plan_bytes + x_perm + H + A + Y
-    return {"minimal": minimal, "with_x_perm": minimal + x_perm, "store_y_layer": store_y,
+def recorded_traffic(workload, kernel):
+    """Calibrated HBM bytes per launch of `kernel` on `workload` from the committed
+    FETCH_SIZE/WRITE_SIZE summary, or None when there is none or the kernel
+    sources changed since the counters were taken."""
+    import hashlib
+    try:
+        kv = {}
+        for line in open(TRAFFIC_FILE):
+            if ":" in line and not line.startswith((" ", "|", "#")):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+        if kv.get("workload") != workload or kv.get("kernel") != kernel:
+            return None
+        h = hashlib.sha256()
+        for src in kv["kernel_sources"].split():
+            h.update(open(os.path.join(ROOT, src), "rb").read())
+        if h.hexdigest() != kv["kernel_sources_sha256"]:
+            return None
+        return float(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+# ----------------------------------------------------------------- work per kernel
+
+
+def kernel_work(cfg, rows):
+    """Algorithmic work of one launch of each traced GEMM kernel: (flops, peak).
+    rows = routed rows of the plan (each GEMM's M or K over all experts)."""
+    d, f = cfg.d, cfg.f
+    mx = cfg.gemm == "mxfp8"
+    peak = PEAK_FP8_TFLOPS if mx else (PEAK_BF16_TFLOPS if cfg.gemm == "bf16" else PEAK_F32_TFLOPS)
+    w = {"up_swiglu": 2.0 * rows * d * 2 * f, "down": 2.0 * rows * f * d, "dact": 2.0 * rows * d * f,
+         "dx_perm": 2.0 * rows * 2 * f * d, "dw1": 2.0 * rows * 2 * f * d, "dw2": 2.0 * rows * d * f}
+    out = {k: (v, peak) for k, v in w.items()}
+    out.update({"mx_" + k: (v, peak) for k, v in w.items()})
+    out["router_dwg"] = (2.0 * cfg.T * cfg.E * d, PEAK_BF16_TFLOPS if cfg.act == "bf16" else PEAK_F32_TFLOPS)
+    return out
+
+
+GEMM_KERNELS = ("up_swiglu", "down", "dact", "dx_perm", "dw1", "dw2")
+
+
+# ----------------------------------------------------------------- one workload
+
+
+def measure(cfg, steps, warmup, fused_gather="auto", extras=False):
+    """Time `steps` training steps of one workload; returns (metrics dict, inputs)."""
+    import torch
+    from mixture_experts_layer_27_amd import binding, synth
+
+    log(f"{cfg.name}: generating inputs")
+    g = synth.generate(cfg)
+    want = fused_gather == "on" or (fused_gather == "auto" and cfg.gemm == "mxfp8")
+    fused = want and cfg.act == "bf16" and cfg.T * cfg.d * 2 < 2 ** 31
+    torch.cuda.reset_peak_memory_stats()
+    run = binding.LayerRun(cfg, g, fused_gather=fused)
+    s = run.s
+    stream = torch.cuda.current_stream()
+    phases = ["route", "permute", "experts", "combine", "backward"]
+
+    def step(ev=None, ftr=None, btr=None):
+        def mark(i):
+            if ev is not None:
+                ev[i].record(stream)
+        mark(0)
+        run.route()
+        mark(1)
+        if not fused:
+            binding.permute(s, run.inp["x"], run.plan, run.x_perm)
+        mark(2)
+        if fused:
+            binding.grouped_gemm_swiglu_gather(s, run.inp["x"], run.inp["w1"], run.inp["w2"], run.plan, run.h, run.y,
+                                               run.ws_fwd, trace=ftr)
+        else:
+            binding.grouped_gemm_swiglu(s, run.x_perm, run.inp["w1"], run.inp["w2"], run.plan, run.h, run.y,
+                                        run.ws_fwd, trace=ftr)
+        mark(3)
+        binding.unpermute_combine(s, run.y, run.plan, run.out)
+        mark(4)
+        if run.has_bwd:
+            run.backward(with_optional=False, trace=btr)
+        mark(5)
+
+    log(f"{cfg.name}: warmup {warmup}")
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    # one trace per call and step, read after the timed region (no sync inside it)
+    ftrs = [binding.Trace(8) for _ in range(steps)]
+    btrs = [binding.Trace(binding.TRACE_MAX_KERNELS + 1) if run.has_bwd else None for _ in range(steps)]
+    log(f"{cfg.name}: timing {steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(evs[i], ftrs[i], btrs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern = {}
+    for i in range(steps):
+        for name, ms in ftrs[i].durations_ms() + (btrs[i].durations_ms() if btrs[i] else []):
+            kern.setdefault(name, []).append(ms)
+    step_ms = [evs[i][0].elapsed_time(evs[i][5]) for i in range(steps)]
+    ph = {p: statistics.median(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(steps))
+          for j, p in enumerate(phases)}
+    q = sorted(step_ms)
+    pct = lambda x: q[min(len(q) - 1, int(round(x * (len(q) - 1))))]
+    med = statistics.median(step_ms)
+    # the same steps without the trace events (their cost on the step time)
+    for _ in range(3):
+        step()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    n_plain = max(5, steps // 5)
+    for _ in range(n_plain):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    plain_ms = e0.elapsed_time(e1) / n_plain
+
+    counts = run.plan.arrays()["counts"].cpu()
+    rows = int(counts.sum())
+    work = kernel_work(cfg, rows)
+    kernels_us = {k: 1e3 * statistics.mean(v) for k, v in kern.items()}
+    dominant = max(kernels_us, key=kernels_us.get) if kernels_us else None
+    per_gemm = {}
+    gflops = gtime = 0.0
+    for k, us in kernels_us.items():
+        if k in work and k != "router_dwg":
+            fl, peak = work[k]
+            per_gemm[k] = {"us": us, "tflops": fl / (us * 1e-6) / 1e12, "frac": fl / (us * 1e-6) / 1e12 / peak}
+            gflops += fl
+            gtime += us * 1e-6
+    peak = work["up_swiglu"][1]
+    esz = 2 if cfg.act == "bf16" else 4
+    permute_bytes = cfg.T * cfg.d * esz + rows * cfg.d * esz + 4 * (cfg.T + 1) + 4 * rows
+    combine_bytes = rows * cfg.d * esz + cfg.T * cfg.d * esz + 8 * rows
+    fwd_flops = work["up_swiglu"][0] + work["down"][0]
+    out = {
+        "workload": f"{cfg.name}: T={cfg.T} d_model={cfg.d} E={cfg.E} top-k={cfg.k} d_ff={cfg.f} SwiGLU, "
+                    f"{'fwd+bwd' if run.has_bwd else 'fwd'}"
+                    f"{', token rounding ' + str(cfg.round_tile) if cfg.round_tile else ''}"
+                    f"{', MXFP8 expert GEMMs' if cfg.gemm == 'mxfp8' else ''}",
+        "tokens_per_s": cfg.T / (med * 1e-3),
+        "ms_per_step_median": med,
+        "ms_per_step_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
+        "ms_per_step_wall_mean": wall * 1e3 / steps,
+        "ms_per_step_untraced": plain_ms,
+        "phases_ms_median": ph,
+        "kernels_us_mean": kernels_us,
+        "grouped_gemm": {"per_kernel": per_gemm,
+                         "aggregate_tflops": gflops / gtime / 1e12 if gtime else None,
+                         "aggregate_frac": gflops / gtime / 1e12 / peak if gtime else None,
+                         "forward_call_frac": fwd_flops / (ph["experts"] * 1e-3) / 1e12 / peak},
+        "permute_GBps": None,
+        "combine_GBps": combine_bytes / (ph["combine"] * 1e-3) / 1e9,
+        "rows": rows,
+        "max_expert_rows": int(counts.max()),
+        "fused_gather": fused,
+    }
+    if dominant is not None:
+        fl, pk = work.get(dominant, (None, None))
+        out["dominant_kernel"] = {"name": dominant, "us": kernels_us[dominant],
+                                  "achieved_tflops": fl / (kernels_us[dominant] * 1e-6) / 1e12 if fl else None,
+                                  "peak_tflops": pk}
+    # moe_permute on its own (outside the step when it is fused into the GEMMs)
+    pev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for _ in range(3):
+        binding.permute(s, run.inp["x"], run.plan, run.x_perm)
+    pev[0].record(stream)
+    for _ in range(10):
+        binding.permute(s, run.inp["x"], run.plan, run.x_perm)
+    pev[1].record(stream)
+    torch.cuda.synchronize()
+    permute_ms = pev[0].elapsed_time(pev[1]) / 10
+    out["permute_GBps"] = permute_bytes / (permute_ms * 1e-3) / 1e9
+    if extras:
+        out.update(data_movement_extras(cfg, run, rows, permute_bytes, stream))
+        out["activation_memory"] = activation_memory(cfg, run, binding) if run.has_bwd else None
+    out["peak_allocated_bytes"] = torch.cuda.max_memory_allocated()
+    del run
+    torch.cuda.empty_cache()
+    return out, g
+
+
+def data_movement_extras(cfg, run, rows, permute_bytes, stream):
+    """Cold-cache permute and plain device-copy rates (references for the
+    data-movement kernels; not part of the layer)."""
+    import torch
+    from mixture_experts_layer_27_amd import binding
+    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+
+    def cold_ms(fn, n=5):
+        t = []
+        for _ in range(n):
+            flush_buf.fill_(1)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            t.append(e0.elapsed_time(e1))
+        return sorted(t)[len(t) // 2]
+
+    s = run.s
+    permute_cold = cold_ms(lambda: binding.permute(s, run.inp["x"], run.plan, run.x_perm))
+    esz = 2 if cfg.act == "bf16" else 4
+    cbytes = (cfg.T + rows) * cfg.d * esz // 2 // 16 * 16
+    csrc = torch.empty(cbytes, dtype=torch.uint8, device="cuda")
+    cdst = torch.empty_like(csrc)
+    pev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    for _ in range(3):
+        cdst.copy_(csrc)
+    pev[0].record(stream)
+    for _ in range(10):
+        cdst.copy_(csrc)
+    pev[1].record(stream)
+    torch.cuda.synchronize()
+    copy_GBps = 2 * cbytes / (pev[0].elapsed_time(pev[1]) / 10 * 1e-3) / 1e9
+    copy_cold = cold_ms(lambda: cdst.copy_(csrc))
+    del csrc, cdst, flush_buf
+    return {"device_copy_GBps": copy_GBps,
+            "cold_cache_GBps": {"permute": permute_bytes / (permute_cold * 1e-3) / 1e9,
+                                "device_copy": 2 * cbytes / (copy_cold * 1e-3) / 1e9,
+                                "note": "median of 5 launches, each after a 1 GiB scratch write"}}
+
+
+def activation_memory(cfg, run, binding):
+    """Bytes the allocator holds from the end of the forward to the backward, for
+    this layer (dS = <dA', A>, A recomputed from H: keeps x, the plan and H; x_perm
+    too when handed to the backward) and for a layer that keeps what the
+    conventional backward (dS = <dO, Y>) reads: x_perm, H, A and Y (SonicMoE
+    article, section 1).  Each set is allocated as the forward leaves it, the
+    forward run into it, and the allocator's count read; the layer input x is
+    included, weights and the layer output are not."""
+    import torch
+    s = run.s
+    dt = torch.bfloat16 if cfg.act == "bf16" else torch.float32
+    N = binding.max_rows(s)
+
+    def held(keep_x_perm, keep_a_y):
+        torch.cuda.synchronize()
+        base = torch.cuda.memory_allocated()
+        x = run.inp["x"].clone()
+        plan = binding.Plan(s)
+        x_perm = torch.empty((N, s.d), dtype=dt, device="cuda")
+        h = torch.empty((N, 2 * s.d_ff), dtype=dt, device="cuda")
+        y = torch.empty((N, s.d), dtype=dt, device="cuda")
+        ws = torch.empty(binding.workspace_bytes(s, binding.MOE_WS_EXPERTS), dtype=torch.uint8, device="cuda")
+        binding.route(s, x, run.inp["w_gate"], run.inp.get("bias"), plan, noise=run.inp.get("noise"))
+        if s.round_tile:
+            binding.round_tokens(s, plan)
+        binding.permute(s, x, plan, x_perm)
+        binding.grouped_gemm_swiglu(s, x_perm, run.inp["w1"], run.inp["w2"], plan, h, y, ws)
+        torch.cuda.synchronize()
+        if keep_a_y and cfg.gemm == "mxfp8":
+            # the bf16 A this layer never stores (its workspace holds the MXFP8 operand codes instead)
+            a_keep = torch.empty((N, s.d_ff), dtype=dt, device="cuda")
+        else:
+            a_keep = ws
+        keep = [x, plan, h] + ([x_perm] if keep_x_perm else []) + ([a_keep, y] if keep_a_y else [])
+        del y, ws, x_perm, a_keep
+        torch.cuda.synchronize()
+        n = torch.cuda.memory_allocated() - base
+        del keep, x, plan, h
+        torch.cuda.synchronize()
+        return n
+
+    minimal = held(False, False)
+    with_xp = held(True, False)
+    store_y = held(True, True)
+    return {"minimal": minimal, "with_x_perm": with_xp, "store_y_layer": store_y,
             "saving_minimal_vs_store_y": 1.0 - minimal / store_y,
-            # MXFP8: the forward workspace handed to the backward (codes of x_perm, A and of
-            # both weights in both orientations)
-            "forward_workspace": fwd_ws_bytes if cfg.gemm == "mxfp8" else 0}
+            "saving_with_x_perm_vs_store_y": 1.0 - with_xp / store_y,
+            "how": "torch.cuda.memory_allocated() after the forward, with only the tensors that set keeps alive "
+                   "(A lives in the expert-GEMM workspace; with MXFP8 that workspace holds the operand codes)"}
+
+
+# ----------------------------------------------------------------- main
 
 
 def main():
@@ -119,7 +418,7 @@ def main():
               file=sys.stderr)
         sys.exit(2)
     import torch
-    from mixture_experts_layer_27_amd import binding, configs, synth
+    from mixture_experts_layer_27_amd import configs
 
     if a.copy_calibration:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
@@ -133,159 +432,51 @@ def main():
         return
 
     cfg = configs.get(a.config)
-    print(f"[bench] generating {cfg.name} inputs", file=sys.stderr, flush=True)
-    g = synth.generate(cfg)
-    # bf16 default: permute x once and hand x_perm to the backward (the backward reads dout through
-    # the plan inside its GEMMs either way).  MXFP8 default: the forward quantiser reads x through
-    # the plan (it writes both code orientations the backward reuses, so x_perm is never needed)
-    want = a.fused_gather == "on" or (a.fused_gather == "auto" and cfg.gemm == "mxfp8")
-    fused = want and cfg.act == "bf16" and cfg.T * cfg.d * 2 < 2 ** 31
-    run = binding.LayerRun(cfg, g, fused_gather=fused)
-    s = run.s
-    stream = torch.cuda.current_stream()
-
-    phases = ["route", "permute", "experts", "combine", "backward"]
-
-    def step(ev=None):
-        def mark(i):
-            if ev is not None:
-                ev[i].record(stream)
-        mark(0)
-        run.route()
-        mark(1)
-        if not fused:
-            binding.permute(s, run.inp["x"], run.plan, run.x_perm)
-        mark(2)
-        if fused:
-            binding.grouped_gemm_swiglu_gather(s, run.inp["x"], run.inp["w1"], run.inp["w2"], run.plan, run.h, run.y,
-                                               run.ws_fwd)
-        else:
-            binding.grouped_gemm_swiglu(s, run.x_perm, run.inp["w1"], run.inp["w2"], run.plan, run.h, run.y,
-                                        run.ws_fwd)
-        mark(3)
-        binding.unpermute_combine(s, run.y, run.plan, run.out)
-        mark(4)
-        if run.has_bwd:
-            run.backward(with_optional=False)
-        mark(5)
-
-    print(f"[bench] warmup {a.warmup}", file=sys.stderr, flush=True)
-    for _ in range(a.warmup):
-        step()
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(a.steps)]
-    print(f"[bench] timing {a.steps} steps", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(a.steps):
-        step(evs[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = {p: sum(evs[i][j].elapsed_time(evs[i][j + 1]) for i in range(a.steps)) / a.steps
-          for j, p in enumerate(phases)}
-    step_ms = sum(evs[i][0].elapsed_time(evs[i][5]) for i in range(a.steps)) / a.steps
-    ms_per_step = wall * 1000.0 / a.steps
-    step_q = sorted(evs[i][0].elapsed_time(evs[i][5]) for i in range(a.steps))
-    pct = lambda q: step_q[min(len(step_q) - 1, int(round(q * (len(step_q) - 1))))]
-
-    # data-movement rates with cold caches: a 1 GiB scratch write before each
-    # timed launch evicts L2 and the 256 MB last-level cache
-    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-
-    def cold_ms(fn, n=5):
-        t = []
-        for _ in range(n):
-            flush_buf.fill_(1)
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            fn()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            t.append(e0.elapsed_time(e1))
-        return sorted(t)[len(t) // 2]
-
-    # moe_permute on its own (outside the step when it is fused into the GEMMs)
-    pev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-    for _ in range(3):
-        binding.permute(s, run.inp["x"], run.plan, run.x_perm)
-    pev[0].record(stream)
-    for _ in range(10):
-        binding.permute(s, run.inp["x"], run.plan, run.x_perm)
-    pev[1].record(stream)
-    torch.cuda.synchronize()
-    permute_ms = pev[0].elapsed_time(pev[1]) / 10
-    permute_cold_ms = cold_ms(lambda: binding.permute(s, run.inp["x"], run.plan, run.x_perm))
-
-    N = cfg.N  # rows without rounding (algorithmic work)
-    counts = run.plan.arrays()["counts"].cpu()
-    rows = int(counts.sum())
-    esz = 2 if cfg.act == "bf16" else 4
-    # practical HBM rate of a plain device-to-device copy of the permutation's size
-    # (reference for the data-movement kernels, not part of the layer)
-    cbytes = (cfg.T + rows) * cfg.d * esz // 2 // 16 * 16
-    csrc = torch.empty(cbytes, dtype=torch.uint8, device="cuda")
-    cdst = torch.empty_like(csrc)
-    for _ in range(3):
-        cdst.copy_(csrc)
-    pev[0].record(stream)
-    for _ in range(10):
-        cdst.copy_(csrc)
-    pev[1].record(stream)
-    torch.cuda.synchronize()
-    copy_GBps = 2 * cbytes / (pev[0].elapsed_time(pev[1]) / 10 * 1e-3) / 1e9
-    copy_cold_ms = cold_ms(lambda: cdst.copy_(csrc))
-    del csrc, cdst, flush_buf
-    fwd_gemm_flops = 2.0 * rows * cfg.d * 2 * cfg.f + 2.0 * rows * cfg.f * cfg.d
-    peak = {"mxfp8": PEAK_FP8_TFLOPS, "bf16": PEAK_BF16_TFLOPS}.get(cfg.gemm, PEAK_F32_TFLOPS)
-    achieved = fwd_gemm_flops / (ms["experts"] * 1e-3) / 1e12
-    permute_bytes = cfg.T * cfg.d * esz + rows * cfg.d * esz + 4 * (cfg.T + 1) + 4 * rows
-    combine_bytes = rows * cfg.d * esz + cfg.T * cfg.d * esz + 8 * rows
-    bwd_flops = 2 * fwd_gemm_flops
+    clocks_before = gpu_clocks()
+    head, g = measure(cfg, a.steps, a.warmup, a.fused_gather, extras=True)
+    clocks_after = gpu_clocks()
+    dom = head.get("dominant_kernel") or {}
+    fl_peak = kernel_work(cfg, head["rows"]).get(dom.get("name"), (None, None))
+    achieved = dom.get("achieved_tflops")
     out = {
         "metric": METRIC,
-        "value": cfg.T / (ms_per_step * 1e-3),
+        "value": head["tokens_per_s"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": head["ms_per_step_median"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": {"mxfp8": "mxfp8", "bf16": "bf16"}.get(cfg.gemm, "f32"),
         "data": "synthetic",
-        "config": {"workload": f"{cfg.name}: T={cfg.T} d_model={cfg.d} E={cfg.E} top-k={cfg.k} "
-                               f"d_ff={cfg.f} SwiGLU, {'fwd+bwd' if run.has_bwd else 'fwd'}"
-                               f"{', token rounding ' + str(cfg.round_tile) if cfg.round_tile else ''}",
-                   "global_batch": cfg.T, "seq_len": 1, "parallelism": "none (1 GPU)"},
-        "roofline": {"bound": "mfma", "kernel": "forward expert GEMMs (up+SwiGLU, down) in one call",
-                     "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
-                     "traffic": recorded_traffic(cfg.name), "traffic_unit": "HBM bytes per call"},
-        "phases_ms": ms,
-        "events_ms_per_step": step_ms,
-        "grouped_gemm_mfma_frac": {"forward": achieved / peak,
-                                   "backward_call": bwd_flops / (ms["backward"] * 1e-3) / 1e12 / peak
-                                   if run.has_bwd else None},
-        "permute_GBps": permute_bytes / (permute_ms * 1e-3) / 1e9,
-        "permute_fused_into_gemms": fused,
-        "combine_GBps": combine_bytes / (ms["combine"] * 1e-3) / 1e9,
+        "config": {"workload": head["workload"], "global_batch": cfg.T, "seq_len": 1,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "kernel": dom.get("name"), "achieved": achieved, "peak": fl_peak[1],
+                     "unit": "TFLOP/s", "frac": achieved / fl_peak[1] if achieved else None,
+                     "traffic": recorded_traffic(cfg.name, dom.get("name")), "traffic_unit": "HBM bytes per launch",
+                     "algorithmic_flops_per_launch": fl_peak[0], "mean_launch_us": dom.get("us")},
+        "timing": "value = T / median step device time (HIP events on the compute stream) over the timed steps",
+        **{k: v for k, v in head.items() if k not in ("workload", "tokens_per_s")},
         "hbm_peak_GBps": PEAK_HBM_GBS,
-        "device_copy_GBps": copy_GBps,
-        "cold_cache_GBps": {"permute": permute_bytes / (permute_cold_ms * 1e-3) / 1e9,
-                            "device_copy": 2 * cbytes / (copy_cold_ms * 1e-3) / 1e9,
-                            "note": "median of 5 launches, each after a 1 GiB scratch write"},
-        "step_ms_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
-        "rows": rows,
-        "max_expert_rows": int(counts.max()),
-        "activation_memory_bytes": activation_bytes(cfg, rows, binding.plan_bytes(s), run.ws_fwd.numel())
-        if run.has_bwd else None,
+        "gpu_clocks": {"before": clocks_before, "after": clocks_after},
     }
+    if not a.no_sub:
+        subs = {}
+        for name in SUB_CONFIGS:
+            if name == cfg.name:
+                continue
+            try:
+                r, _ = measure(configs.get(name), a.sub_steps, a.sub_warmup, a.fused_gather)
+            except Exception as exc:        # report, keep the headline
+                r = {"error": f"{type(exc).__name__}: {exc}"}
+            subs[name] = r
+        out["sub_results"] = subs
     if not a.no_cpu_baseline:
-        del run
         torch.cuda.empty_cache()
-        tokens = a.cpu_tokens or max(1, min(cfg.T, 16384))
-        print(f"[bench] cpu oracle on {tokens} tokens", file=sys.stderr, flush=True)
+        tokens = a.cpu_tokens or min(cfg.T, 4096 if cfg.d * cfg.f * cfg.k > 2 ** 23 else 16384)
+        log(f"cpu oracle on {tokens} tokens")
         out["cpu_baseline"] = cpu_baseline(cfg, g, tokens)
     line = json.dumps(out)
     print(line, flush=True)
