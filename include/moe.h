@@ -198,6 +198,24 @@ moe_status moe_grouped_gemm_swiglu_gather(const moe_shape *s, const void *x, con
                                           const void *w2, const moe_plan *plan, void *h_saved, void *y,
                                           void *ws, size_t ws_bytes, void *stream);
 
+/* The expert FFN of moe_grouped_gemm_swiglu (same arguments, same kernels, same
+ * bits) for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Its workspace
+ * is a device array inside the library (MOE_NOALLOC_SCRATCH_BYTES per GPU,
+ * reserved when the library's code is loaded on that GPU and held until the
+ * process ends); the call allocates nothing.  The array of the caller's
+ * current device is used, so the stream must belong to that device.  Every
+ * call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (concurrent streams, host threads) race and must be serialised by the
+ * caller; the array keeps the last call's contents.
+ * Errors: as moe_grouped_gemm_swiglu, and MOE_EWORKSPACE (nothing launched)
+ * when the problem's workspace, moe_workspace_bytes(s, MOE_WS_EXPERTS), exceeds
+ * MOE_NOALLOC_SCRATCH_BYTES. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+moe_status moe_grouped_gemm_swiglu_noalloc(const moe_shape *s, const void *x_perm, const void *w1,
+                                           const void *w2, const moe_plan *plan, void *h_saved, void *y,
+                                           void *stream);
+
 /* Weighted combine: out[t] = sum over the rows of t (ascending) of
  * gate_of_row[r] * y[r], accumulated in float32.  y [N_max,d], out [T,d]. */
 moe_status moe_unpermute_combine(const moe_shape *s, const void *y, const moe_plan *plan,

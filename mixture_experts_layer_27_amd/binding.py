@@ -24,9 +24,11 @@ MOE_WS_ROUTE, MOE_WS_ROUND, MOE_WS_EXPERTS, MOE_WS_BACKWARD = 0, 1, 2, 3
 STATUS = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_ENOTSUP", 3: "MOE_EWORKSPACE", 4: "MOE_EHIP"}
 EXPORTS = ("moe_max_rows", "moe_plan_bytes", "moe_plan_init", "moe_workspace_bytes", "moe_route",
            "moe_round_tokens", "moe_permute", "moe_grouped_gemm_swiglu", "moe_grouped_gemm_swiglu_gather",
-           "moe_grouped_gemm_swiglu_traced", "moe_grouped_gemm_swiglu_gather_traced", "moe_unpermute_combine", "moe_backward", "moe_backward_traced",
+           "moe_grouped_gemm_swiglu_traced", "moe_grouped_gemm_swiglu_gather_traced",
+           "moe_grouped_gemm_swiglu_noalloc", "moe_unpermute_combine", "moe_backward", "moe_backward_traced",
            "moe_quantize_mx", "moe_status_str")
 TRACE_MAX_KERNELS = 48
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class MoeShape(ctypes.Structure):
@@ -62,6 +64,7 @@ for name, res, args in [
     ("moe_permute", ctypes.c_int, [_P_SHAPE, _vp, _P_PLAN, _vp, _vp]),
     ("moe_grouped_gemm_swiglu", ctypes.c_int, [_P_SHAPE, _vp, _vp, _vp, _P_PLAN, _vp, _vp, _vp, _sz, _vp]),
     ("moe_grouped_gemm_swiglu_gather", ctypes.c_int, [_P_SHAPE, _vp, _vp, _vp, _P_PLAN, _vp, _vp, _vp, _sz, _vp]),
+    ("moe_grouped_gemm_swiglu_noalloc", ctypes.c_int, [_P_SHAPE, _vp, _vp, _vp, _P_PLAN, _vp, _vp, _vp]),
     ("moe_unpermute_combine", ctypes.c_int, [_P_SHAPE, _vp, _P_PLAN, _vp, _vp]),
     ("moe_grouped_gemm_swiglu_traced", ctypes.c_int,
      [_P_SHAPE, _vp, _vp, _vp, _P_PLAN, _vp, _vp, _vp, _sz, _vp, _P_TRACE]),
@@ -245,6 +248,13 @@ def grouped_gemm_swiglu_gather(s: MoeShape, x, w1, w2, plan: Plan, h_saved, y, w
     _check("moe_grouped_gemm_swiglu_gather",
            _lib.moe_grouped_gemm_swiglu_gather(ctypes.byref(s), _ptr(x), _ptr(w1), _ptr(w2), ctypes.byref(plan.c),
                                                _ptr(h_saved), _ptr(y), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def grouped_gemm_swiglu_noalloc(s: MoeShape, x_perm, w1, w2, plan: Plan, h_saved, y, stream=None):
+    """The expert FFN with the library's own device scratch (no workspace, no allocation)."""
+    _check("moe_grouped_gemm_swiglu_noalloc",
+           _lib.moe_grouped_gemm_swiglu_noalloc(ctypes.byref(s), _ptr(x_perm), _ptr(w1), _ptr(w2),
+                                                ctypes.byref(plan.c), _ptr(h_saved), _ptr(y), _stream(stream)))
 
 
 def unpermute_combine(s: MoeShape, y, plan: Plan, out, stream=None):

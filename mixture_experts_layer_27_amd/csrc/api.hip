@@ -3,6 +3,8 @@
 // check fails; no device-to-host copy or synchronisation happens anywhere.
 #include <string.h>
 
+#include <mutex>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -418,6 +420,50 @@ moe_status moe_grouped_gemm_swiglu_gather(const moe_shape* s, const void* x, con
                                           const moe_plan* plan, void* h_saved, void* y, void* ws, size_t ws_bytes,
                                           void* stream) {
   return moe_grouped_gemm_swiglu_gather_traced(s, x, w1, w2, plan, h_saved, y, ws, ws_bytes, stream, nullptr);
+}
+
+}  // extern "C"
+
+// ---- the expert FFN without any allocation: its workspace is this file's
+// device array.  Each GPU the library runs on holds its own copy of the array
+// until the process ends; host code uses only the address hipGetSymbolAddress
+// returns for the current device (the array's name is a host-side stand-in).
+namespace {
+constexpr size_t kNoAllocScratchBytes = (size_t)MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_of_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    scratch_ptr[dev] = p;
+  }
+  *out = scratch_ptr[dev];
+  return hipSuccess;
+}
+}  // namespace
+
+extern "C" {
+
+moe_status moe_grouped_gemm_swiglu_noalloc(const moe_shape* s, const void* x_perm, const void* w1, const void* w2,
+                                           const moe_plan* plan, void* h_saved, void* y, void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (!aligned(x_perm) || !aligned(w1) || !aligned(w2) || !aligned(h_saved) || !aligned(y)) return MOE_EINVAL;
+  if ((st = check_plan(*s, plan)) != MOE_OK) return st;
+  if (experts_ws(*s) > kNoAllocScratchBytes) return MOE_EWORKSPACE;
+  void* ws = nullptr;
+  if (scratch_of_current_device(&ws) != hipSuccess) return MOE_EHIP;
+  return experts_forward(s, x_perm, nullptr, w1, w2, plan, h_saved, y, ws, kNoAllocScratchBytes, stream, nullptr);
 }
 
 moe_status moe_unpermute_combine(const moe_shape* s, const void* y, const moe_plan* plan, void* out, void* stream) {

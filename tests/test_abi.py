@@ -103,3 +103,18 @@ def test_trace_validation_returns_before_launch(b):
                                                         fake, fake, 1 << 30, None, ctypes.byref(neg)) == 1
     assert tr.count == 0
 
+
+def test_noalloc_rejects_problems_past_its_scratch(b):
+    """The no-allocation expert FFN refuses, on the host, a problem whose workspace
+    exceeds the library's device scratch (nothing is launched)."""
+    fake = ctypes.c_void_p(1 << 20)
+    s = b.make_shape(16384, 2048, 128, 4, 1024, b.MOE_BF16)      # A alone is 128 MiB
+    assert b.workspace_bytes(s, b.MOE_WS_EXPERTS) > b.NOALLOC_SCRATCH_BYTES
+    plan = b.MoePlan()
+    assert b._lib.moe_plan_init(ctypes.byref(s), fake, 1 << 40, ctypes.byref(plan)) == 0
+    assert b._lib.moe_grouped_gemm_swiglu_noalloc(ctypes.byref(s), fake, fake, fake, ctypes.byref(plan), fake, fake,
+                                                  None) == 3
+    small = b.make_shape(64, 128, 8, 2, 128, b.MOE_BF16)
+    assert b.workspace_bytes(small, b.MOE_WS_EXPERTS) <= b.NOALLOC_SCRATCH_BYTES
+    assert b._lib.moe_grouped_gemm_swiglu_noalloc(ctypes.byref(small), None, fake, fake, ctypes.byref(plan), fake,
+                                                  fake, None) == 1
