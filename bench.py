@@ -350,8 +350,26 @@ def data_movement_extras(cfg, run, rows, permute_bytes, stream):
     torch.cuda.synchronize()
     copy_GBps = 2 * cbytes / (pev[0].elapsed_time(pev[1]) / 10 * 1e-3) / 1e9
     copy_cold = cold_ms(lambda: cdst.copy_(csrc))
+    # hand-written streaming kernels over the same byte count (moe_ref_stream): the
+    # practical read, write and copy rates the data-movement kernels are held to
+    ref = {}
+    for name, mode, moved in (("read_nontemporal", binding.REF_READ, cbytes),
+                              ("write", binding.REF_WRITE, cbytes),
+                              ("copy_nontemporal_loads", binding.REF_COPY_NT_LOAD, 2 * cbytes),
+                              ("copy_nontemporal_loads_stores", binding.REF_COPY_NT_BOTH, 2 * cbytes)):
+        fn = lambda: binding.ref_stream(csrc, cdst, cbytes, mode)
+        for _ in range(3):
+            fn()
+        pev[0].record(stream)
+        for _ in range(10):
+            fn()
+        pev[1].record(stream)
+        torch.cuda.synchronize()
+        ref[name] = {"warm": moved / (pev[0].elapsed_time(pev[1]) / 10 * 1e-3) / 1e9,
+                     "cold": moved / (cold_ms(fn) * 1e-3) / 1e9}
     del csrc, cdst, flush_buf
     return {"device_copy_GBps": copy_GBps,
+            "reference_stream_GBps": ref,
             "cold_cache_GBps": {"permute": permute_bytes / (permute_cold * 1e-3) / 1e9,
                                 "device_copy": 2 * cbytes / (copy_cold * 1e-3) / 1e9,
                                 "note": "median of 5 launches, each after a 1 GiB scratch write"}}

@@ -297,6 +297,16 @@ moe_status moe_backward_traced(const moe_shape *s, const void *x, const void *w_
 moe_status moe_quantize_mx(const void *src_bf16, int64_t rows, int64_t cols, int k_axis, uint8_t *codes,
                            uint8_t *scales, void *stream);
 
+/* Measurement reference, not part of the layer: streams `bytes` through HBM so
+ * the data-movement kernels above can be compared with the rates plain kernels
+ * reach on this GPU.  mode 0: read src (non-temporal loads); 1: write dst;
+ * 2: copy src to dst with non-temporal loads; 3: the same with non-temporal
+ * stores too.  src (modes 0, 2, 3) and dst device pointers, 16-byte aligned,
+ * bytes a positive multiple of 16 (mode 0 needs 16 bytes of dst, written only
+ * for a data pattern the inputs of a measurement never hold).  Errors:
+ * MOE_EINVAL for a bad pointer, size or mode. */
+moe_status moe_ref_stream(const void *src, void *dst, int64_t bytes, int mode, void *stream);
+
 const char *moe_status_str(moe_status st);
 
 #ifdef __cplusplus

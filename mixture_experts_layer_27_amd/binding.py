@@ -26,7 +26,7 @@ EXPORTS = ("moe_max_rows", "moe_plan_bytes", "moe_plan_init", "moe_workspace_byt
            "moe_round_tokens", "moe_permute", "moe_grouped_gemm_swiglu", "moe_grouped_gemm_swiglu_gather",
            "moe_grouped_gemm_swiglu_traced", "moe_grouped_gemm_swiglu_gather_traced",
            "moe_grouped_gemm_swiglu_noalloc", "moe_unpermute_combine", "moe_backward", "moe_backward_traced",
-           "moe_quantize_mx", "moe_status_str")
+           "moe_quantize_mx", "moe_ref_stream", "moe_status_str")
 TRACE_MAX_KERNELS = 48
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -75,6 +75,7 @@ for name, res, args in [
     ("moe_backward_traced", ctypes.c_int, [_P_SHAPE, _vp, _vp, _vp, _vp, _P_PLAN, _vp, _vp, _vp, _vp, _vp, _vp,
                                            _vp, _vp, _vp, _vp, _vp, _sz, _vp, _P_TRACE]),
     ("moe_quantize_mx", ctypes.c_int, [_vp, _i64, _i64, ctypes.c_int, _vp, _vp, _vp]),
+    ("moe_ref_stream", ctypes.c_int, [_vp, _vp, _i64, ctypes.c_int, _vp]),
     ("moe_status_str", ctypes.c_char_p, [ctypes.c_int]),
 ]:
     fn = getattr(_lib, name)
@@ -279,6 +280,14 @@ def quantize_mx(src, codes, scales, k_axis=1, stream=None):
     rows, cols = src.shape
     _check("moe_quantize_mx", _lib.moe_quantize_mx(_ptr(src), rows, cols, k_axis, _ptr(codes), _ptr(scales),
                                                    _stream(stream)))
+
+
+REF_READ, REF_WRITE, REF_COPY_NT_LOAD, REF_COPY_NT_BOTH = 0, 1, 2, 3
+
+
+def ref_stream(src, dst, nbytes, mode, stream=None):
+    """Reference streaming kernel (measurement only): read, write or copy nbytes."""
+    _check("moe_ref_stream", _lib.moe_ref_stream(_ptr(src), _ptr(dst), nbytes, mode, _stream(stream)))
 
 
 # ----------------------------------------------------------------- one layer

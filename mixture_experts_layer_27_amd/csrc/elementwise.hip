@@ -29,7 +29,7 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(const char* __restric
     const int c0 = (int)(i - (int64_t)t * per_tok);
     u32x4 v[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) v[u] = ldg16(src + ((int64_t)t * vec + c0 + u * per_tok) * 16);
+    for (int u = 0; u < U; ++u) v[u] = ldg16_nt(src + ((int64_t)t * vec + c0 + u * per_tok) * 16);
     const int p0 = tok_ptr[t], p1 = tok_ptr[t + 1];
     for (int p = p0; p < p1; ++p) {
       char* drow = dst + (int64_t)tok_rows[p] * vec * 16;
@@ -40,9 +40,11 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(const char* __restric
 }
 
 // out[t] = sum over the rows of t (ascending) of gate[r] * y[r], fp32 accumulation.
-// One wave per token: its rows and gates are read once (wave-uniform), each lane
-// accumulates up to four 16-byte column chunks with their loads in flight.
-template <typename T>
+// One wave per token: each lane owns CL 16-byte column chunks per pass and
+// issues the loads of up to RU rows before adding them (in ascending row order),
+// so RU * CL row vectors are in flight per lane.  The rows are read once:
+// non-temporal loads.
+template <typename T, int RU>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, const int32_t* __restrict__ tok_ptr,
                                                      const int32_t* __restrict__ tok_rows,
                                                      const float* __restrict__ gate, int T_, int d,
@@ -60,26 +62,37 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, c
     for (int j = 0; j < CL; ++j)
 #pragma unroll
       for (int q = 0; q < EV; ++q) acc[j][q] = 0.0f;
-    for (int p = p0; p < p1; ++p) {
-      const int r = tok_rows[p];
-      const float g = gate[r];
-      u32x4 v[CL];
+    for (int p = p0; p < p1; p += RU) {
+      int r[RU];
+      float g[RU];
+      u32x4 v[RU][CL];
 #pragma unroll
-      for (int j = 0; j < CL; ++j) {
-        const int c = cb + lane + 64 * j;
-        v[j] = c < vec ? ldg16(y + (int64_t)r * d + c * EV) : u32x4{0u, 0u, 0u, 0u};
+      for (int u = 0; u < RU; ++u) {
+        r[u] = p + u < p1 ? tok_rows[p + u] : -1;
+        g[u] = r[u] >= 0 ? gate[r[u]] : 0.0f;
       }
 #pragma unroll
-      for (int j = 0; j < CL; ++j) {
-        if constexpr (sizeof(T) == 2) {
+      for (int u = 0; u < RU; ++u)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            acc[j][2 * q] += g * __uint_as_float(v[j][q] << 16);
-            acc[j][2 * q + 1] += g * __uint_as_float(v[j][q] & 0xffff0000u);
+        for (int j = 0; j < CL; ++j) {
+          const int c = cb + lane + 64 * j;
+          v[u][j] = (r[u] >= 0 && c < vec) ? ldg16_nt(y + (int64_t)r[u] * d + c * EV) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+      for (int u = 0; u < RU; ++u) {
+        if (r[u] < 0) break;
+#pragma unroll
+        for (int j = 0; j < CL; ++j) {
+          if constexpr (sizeof(T) == 2) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              acc[j][2 * q] += g[u] * __uint_as_float(v[u][j][q] << 16);
+              acc[j][2 * q + 1] += g[u] * __uint_as_float(v[u][j][q] & 0xffff0000u);
+            }
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[j][q] += g[u] * __uint_as_float(v[u][j][q]);
           }
-        } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) acc[j][q] += g * __uint_as_float(v[j][q]);
         }
       }
     }
@@ -106,11 +119,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, c
 // experts (router backward below), so the router term is a gather of a few W_g
 // rows (L2-resident) rather than a GEMM; a top-k expert is visited here only when
 // t has no row at it (token rounding dropped the pair).
-// One wave per token: the token's rows, experts and dz values are read once
-// (wave-uniform), then each lane accumulates up to four 16-byte column chunks
-// with all their row loads in flight.  When dz is dense (routing variants) the
+// One wave per token: each lane owns four 16-byte column chunks per pass and
+// issues the loads of up to RU rows (and their W_g rows) before adding them in
+// ascending row order.  dX_perm rows are read once (non-temporal loads), W_g
+// rows are shared by every token (ordinary loads, L2-resident).  When dz is dense (routing variants) the
 // router term comes precomputed as dxr = dz W_g (fp32 [T, d], a GEMM) instead.
-template <typename T>
+template <typename T, int RU>
 __global__ __launch_bounds__(256) void router_dx_kernel(const T* __restrict__ dx_perm, const int32_t* __restrict__ tok_ptr,
                                                        const int32_t* __restrict__ tok_rows,
                                                        const int32_t* __restrict__ expert_of_row,
@@ -145,32 +159,32 @@ __global__ __launch_bounds__(256) void router_dx_kernel(const T* __restrict__ dx
     for (int j = 0; j < CL; ++j)
 #pragma unroll
       for (int q = 0; q < EV; ++q) acc[j][q] = 0.0f;
-    for (int p = p0; p < p1; p += 2) {        // rows in ascending order, two with their loads in flight
-      const bool two = p + 1 < p1;
-      const int r0 = tok_rows[p], r1 = two ? tok_rows[p + 1] : r0;
-      const int e0 = expert_of_row[r0], e1 = expert_of_row[r1];
-      const float z0 = dxr ? 0.0f : dzt[e0], z1 = dxr ? 0.0f : dzt[e1];
-      u32x4 v0[CL], w0[CL], v1[CL], w1[CL];
+    for (int p = p0; p < p1; p += RU) {       // rows in ascending order, RU with their loads in flight
+      int r[RU], erow[RU];
+      float z[RU];
 #pragma unroll
-      for (int j = 0; j < CL; ++j) {
-        const int c = cb + lane + 64 * j;
-        v0[j] = w0[j] = v1[j] = w1[j] = u32x4{0u, 0u, 0u, 0u};
-        if (c < vec) {
-          v0[j] = ldg16(dx_perm + (int64_t)r0 * d + c * EV);
-          if (!dxr) w0[j] = ldg16(wg + (int64_t)e0 * d + c * EV);
-          if (two) {
-            v1[j] = ldg16(dx_perm + (int64_t)r1 * d + c * EV);
-            if (!dxr) w1[j] = ldg16(wg + (int64_t)e1 * d + c * EV);
-          }
-        }
+      for (int u = 0; u < RU; ++u) {
+        r[u] = p + u < p1 ? tok_rows[p + u] : -1;
+        erow[u] = r[u] >= 0 ? expert_of_row[r[u]] : 0;
+        z[u] = (dxr || r[u] < 0) ? 0.0f : dzt[erow[u]];
       }
+      u32x4 v[RU][CL], w[RU][CL];
 #pragma unroll
-      for (int j = 0; j < CL; ++j) {
-        add(acc[j], v0[j], 1.0f);
-        add(acc[j], w0[j], z0);
-        if (two) {
-          add(acc[j], v1[j], 1.0f);
-          add(acc[j], w1[j], z1);
+      for (int u = 0; u < RU; ++u)
+#pragma unroll
+        for (int j = 0; j < CL; ++j) {
+          const int c = cb + lane + 64 * j;
+          const bool ok = r[u] >= 0 && c < vec;
+          v[u][j] = ok ? ldg16_nt(dx_perm + (int64_t)r[u] * d + c * EV) : u32x4{0u, 0u, 0u, 0u};
+          w[u][j] = (ok && !dxr) ? ldg16(wg + (int64_t)erow[u] * d + c * EV) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+      for (int u = 0; u < RU; ++u) {
+        if (r[u] < 0) break;
+#pragma unroll
+        for (int j = 0; j < CL; ++j) {
+          add(acc[j], v[u][j], 1.0f);
+          add(acc[j], w[u][j], z[u]);
         }
       }
     }
@@ -356,9 +370,9 @@ __global__ __launch_bounds__(256) void router_dwg_reduce_kernel(const float* __r
   for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; i < n; i += (int64_t)gridDim.x * 256 * 4) {
     f32x4 hi = {0.f, 0.f, 0.f, 0.f}, lo = {0.f, 0.f, 0.f, 0.f};
     for (int q = 0; q < nsplit; ++q) {
-      const f32x4 a = *reinterpret_cast<const f32x4*>(part + q * pstride + i);
+      const f32x4 a = ldf4_nt(part + q * pstride + i);
       f32x4 b = {0.f, 0.f, 0.f, 0.f};
-      if (lo_off >= 0) b = *reinterpret_cast<const f32x4*>(part + q * pstride + lo_off + i);
+      if (lo_off >= 0) b = ldf4_nt(part + q * pstride + lo_off + i);
       hi += a;
       lo += b;
     }
@@ -389,11 +403,11 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
     for (; q + 8 <= nsplit; q += 8) {   // eight partials' loads in flight, added in split order
       f32x4 p[8];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) p[u] = *reinterpret_cast<const f32x4*>(part + (q + u) * n + i);
+      for (int u = 0; u < 8; ++u) p[u] = ldf4_nt(part + (q + u) * n + i);
 #pragma unroll
       for (int u = 0; u < 8; ++u) s += p[u];
     }
-    for (; q < nsplit; ++q) s += *reinterpret_cast<const f32x4*>(part + q * n + i);
+    for (; q < nsplit; ++q) s += ldf4_nt(part + q * n + i);
     *reinterpret_cast<f32x4*>(out + i) = s;
   }
 }
@@ -460,7 +474,7 @@ __global__ __launch_bounds__(256) void wgrad_reduce_kernel(float* __restrict__ d
     float* out = dw + (int64_t)e * mn;
     for (int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; i < mn; i += (int64_t)gridDim.x * 256 * 4) {
       f32x4 a = *reinterpret_cast<const f32x4*>(out + i);
-      for (int s = sr.x; s < sr.y; ++s) a += *reinterpret_cast<const f32x4*>(part + (int64_t)s * mn + i);
+      for (int s = sr.x; s < sr.y; ++s) a += ldf4_nt(part + (int64_t)s * mn + i);
       *reinterpret_cast<f32x4*>(out + i) = a;
     }
   }
@@ -492,10 +506,10 @@ hipError_t launch_permute_rows(const moe_shape& s, const void* src, const moe_pl
 
 hipError_t launch_combine(const moe_shape& s, const void* y, const moe_plan& p, void* out, hipStream_t st) {
   if (s.act == MOE_BF16)
-    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(ceil_div(s.T, 4)), dim3(256), 0, st, (const bf16_t*)y,
+    hipLaunchKernelGGL((combine_kernel<bf16_t, 1>), dim3(ceil_div(s.T, 4)), dim3(256), 0, st, (const bf16_t*)y,
                        p.tok_ptr, p.tok_rows, p.gate_of_row, s.T, s.d, (bf16_t*)out);
   else
-    hipLaunchKernelGGL(combine_kernel<float>, dim3(ceil_div(s.T, 4)), dim3(256), 0, st, (const float*)y,
+    hipLaunchKernelGGL((combine_kernel<float, 1>), dim3(ceil_div(s.T, 4)), dim3(256), 0, st, (const float*)y,
                        p.tok_ptr, p.tok_rows, p.gate_of_row, s.T, s.d, (float*)out);
   return hipGetLastError();
 }
@@ -504,11 +518,11 @@ hipError_t launch_router_dx(const moe_shape& s, const moe_plan& p, const void* d
                             const void* wg, const float* dxr, void* dx, hipStream_t st) {
   const int words = (s.E + 31) / 32;
   if (s.act == MOE_BF16) {
-    hipLaunchKernelGGL(router_dx_kernel<bf16_t>, dim3(ceil_div(s.T, 4)), dim3(256), 0, st, (const bf16_t*)dx_perm,
+    hipLaunchKernelGGL((router_dx_kernel<bf16_t, 1>), dim3(ceil_div(s.T, 4)), dim3(256), 0, st, (const bf16_t*)dx_perm,
                        p.tok_ptr, p.tok_rows, p.expert_of_row, p.topk_idx, p.keep_bits, words, dz,
                        (const bf16_t*)wg, dxr, s.T, s.E, s.d, s.k, (bf16_t*)dx);
   } else {
-    hipLaunchKernelGGL(router_dx_kernel<float>, dim3(ceil_div(s.T, 4)), dim3(256), 0, st, (const float*)dx_perm,
+    hipLaunchKernelGGL((router_dx_kernel<float, 1>), dim3(ceil_div(s.T, 4)), dim3(256), 0, st, (const float*)dx_perm,
                        p.tok_ptr, p.tok_rows, p.expert_of_row, p.topk_idx, p.keep_bits, words, dz,
                        (const float*)wg, dxr, s.T, s.E, s.d, s.k, (float*)dx);
   }

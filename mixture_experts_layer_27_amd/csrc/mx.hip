@@ -81,7 +81,7 @@ __global__ __launch_bounds__(256) void quantize_rows_kernel(const bf16_t* __rest
     for (int u = 0; u < 2; ++u) {
       const int i = t + 256 * u;            // row i >> 4, 8-value chunk i & 15
       const int64_t r = r0 + (i >> 4), kk = k0 + (i & 15) * 8;
-      raw[u] = (r < nr && kk < K) ? ldg16(src + r * K + kk) : u32x4{0u, 0u, 0u, 0u};
+      raw[u] = (r < nr && kk < K) ? ldg16_nt(src + r * K + kk) : u32x4{0u, 0u, 0u, 0u};
     }
     __syncthreads();                          // drow visible
 #pragma unroll
@@ -179,7 +179,8 @@ __global__ __launch_bounds__(256) void quantize_t_kernel(const bf16_t* __restric
     const int rr = i >> 3, ch = i & 7;
     const int hh = rr >> 6, rl = rr & 63;
     const int64_t sr = gather && rl < valid[hh] ? (int64_t)gather[base[hh] + rl] : base[hh] + rl;   // tokens mode
-    raw[u] = rl < valid[hh] ? ldg16(src + sr * C + c0 + ch * 8) : u32x4{0u, 0u, 0u, 0u};
+    raw[u] = rl < valid[hh] ? (gather ? ldg16(src + sr * C + c0 + ch * 8) : ldg16_nt(src + sr * C + c0 + ch * 8))
+                            : u32x4{0u, 0u, 0u, 0u};
   }
 #pragma unroll
   for (int u = 0; u < 4; ++u) {
@@ -292,7 +293,7 @@ __global__ __launch_bounds__(256) void quantize_dual_kernel(const bf16_t* __rest
       for (int q = 0; q < 2; ++q) {
         const int col = c0 + cp * 16 + q * 8;
         const bool ok = rl < valid[hh] && col < C;
-        raw[2 * v + q] = ok ? ldg16(src + sr * C + col) : u32x4{0u, 0u, 0u, 0u};
+        raw[2 * v + q] = ok ? (gather ? ldg16(src + sr * C + col) : ldg16_nt(src + sr * C + col)) : u32x4{0u, 0u, 0u, 0u};
       }
     }
     // along rows: two consecutive lanes hold one 32-column block, each lane 16
@@ -331,7 +332,7 @@ __global__ __launch_bounds__(256) void quantize_dual_kernel(const bf16_t* __rest
       const int col = c0 + ch * 8;
       const bool ok = rl < valid[hh] && col < C;
       const int64_t sr = gather && ok ? (int64_t)gather[base[hh] + rl] : base[hh] + rl;   // tokens mode
-      raw[u] = ok ? ldg16(src + sr * C + col) : u32x4{0u, 0u, 0u, 0u};
+      raw[u] = ok ? (gather ? ldg16(src + sr * C + col) : ldg16_nt(src + sr * C + col)) : u32x4{0u, 0u, 0u, 0u};
     }
     // along rows: four consecutive lanes hold one 32-column block
 #pragma unroll

@@ -118,3 +118,11 @@ def test_noalloc_rejects_problems_past_its_scratch(b):
     assert b.workspace_bytes(small, b.MOE_WS_EXPERTS) <= b.NOALLOC_SCRATCH_BYTES
     assert b._lib.moe_grouped_gemm_swiglu_noalloc(ctypes.byref(small), None, fake, fake, ctypes.byref(plan), fake,
                                                   fake, None) == 1
+
+
+def test_ref_stream_validation(b):
+    fake = ctypes.c_void_p(1 << 20)
+    assert b._lib.moe_ref_stream(fake, fake, 15, 2, None) == 1                 # not a multiple of 16
+    assert b._lib.moe_ref_stream(fake, fake, 1 << 20, 4, None) == 1            # mode
+    assert b._lib.moe_ref_stream(None, fake, 1 << 20, 2, None) == 1            # copy without a source
+    assert b._lib.moe_ref_stream(fake, ctypes.c_void_p((1 << 20) + 8), 64, 1, None) == 1   # misaligned
