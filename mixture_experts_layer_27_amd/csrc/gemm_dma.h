@@ -34,8 +34,15 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4_t;
 typedef __attribute__((address_space(3))) void lds_void_t;
 
+// global_load_lds_dwordx4 written out: the compiler, which cannot tell the DMA's
+// LDS bytes from those a later ds_read_b64_tr_b16 reads, would otherwise wait for
+// every DMA in flight (vmcnt(0)) before each stage's first transposed fragment
+// read, and the ring would hide no latency.  The kernels order the DMA with
+// explicit s_waitcnt vmcnt(n) + barrier before any read of the stage.  No
+// register is written by the instruction (the data goes to LDS only).
 MOE_DEV void dma16(const void* g, char* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds(g, (lds_void_t*)lds_wave_base, 16, 0, 0);
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)lds_wave_base);
+  asm volatile("global_load_lds_dwordx4 %0, off" : : "v"(g), "{m0}"(m0) : "memory");
 }
 
 MOE_DEV u32x4 lds_tr_frag(const char* p0, const char* p1) {
@@ -539,56 +546,68 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma(Args args) {
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
   constexpr int LPS = DmaOperand<BM, NW, AKC, BK>::Q + DmaOperand<BN, NW, BKC, BK>::Q;   // loads per stage
+  constexpr int KS = BK / 16;                   // 16-deep MFMA steps per stage
+  static_assert(KS % 2 == 0, "fragment double buffer alternates over the steps of a stage");
   const int nk = (k_end > k_begin) ? (k_end - k_begin + BK - 1) / BK : 0;
 #pragma unroll
   for (int s = 0; s < S - 1; ++s)
     if (s < nk) issue(s);
 
+  auto frags = [&](const char* as, int ks, u32x4 (&af)[TM], u32x4 (&bfr)[TN]) {
+    const char* bs = as + ASZ;
+    const int kb = ks * 16 + (lane >> 5) * 8 + ((lane & 15) >> 2);   // MN: first k row of the lane
+    const int cb = (((lane >> 4) & 1) * 16 + 4 * (lane & 3)) * 2;   // MN: byte column of the lane
+    if constexpr (AKC) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+        af[i] = *reinterpret_cast<const u32x4*>(as + kc_offk<BK>(wm * WTM + i * 32 + (lane & 31), ks * 2 + (lane >> 5)));
+    } else {
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int byte = (wm * WTM + i * 32) * 2 + cb;
+        af[i] = lds_tr_frag(as + mn_off<BM>(kb, byte), as + mn_off<BM>(kb + 4, byte));
+      }
+    }
+    if constexpr (BKC) {
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        bfr[j] = *reinterpret_cast<const u32x4*>(bs + kc_offk<BK>(wn * WTN + j * 32 + (lane & 31), ks * 2 + (lane >> 5)));
+    } else {
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const int byte = (wn * WTN + j * 32) * 2 + cb;
+        bfr[j] = lds_tr_frag(bs + mn_off<BN>(kb, byte), bs + mn_off<BN>(kb + 4, byte));
+      }
+    }
+  };
+  auto mma = [&](const u32x4 (&af)[TM], const u32x4 (&bfr)[TN]) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) Mma<T>::run(acc[i][j], af[i], bfr[j]);
+  };
+  // Fragments alternate between two register sets.  The last step of stage kt
+  // is multiplied after the next barrier, so its MFMAs cover the first fragment
+  // reads of stage kt + 1 (a stage's reads can only start after its barrier).
+  u32x4 fa[2][TM], fb[2][TN];
   for (int kt = 0; kt < nk; ++kt) {
     const int ahead = min(S - 2, nk - 1 - kt);   // stages already issued after this one
     if (S >= 5 && ahead >= 3) wait_vm_lgkm0<3 * LPS>();
     else if (S >= 4 && ahead >= 2) wait_vm_lgkm0<2 * LPS>();
     else if (S >= 3 && ahead >= 1) wait_vm_lgkm0<LPS>();
     else wait_vm_lgkm0<0>();
-    cta_barrier();
+    cta_barrier();                               // stage kt landed for every wave; slot (kt - 1) % S is free
     if (kt + S - 1 < nk) issue(kt + S - 1);
     const char* as = smem + (kt % S) * STAGE;
-    const char* bs = as + ASZ;
+    frags(as, 0, fa[0], fb[0]);
+    if (kt > 0) mma(fa[1], fb[1]);               // stage kt - 1, last step
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      u32x4 af[TM], bfr[TN];
-      if constexpr (AKC) {
-#pragma unroll
-        for (int i = 0; i < TM; ++i)
-          af[i] = *reinterpret_cast<const u32x4*>(as + kc_offk<BK>(wm * WTM + i * 32 + (lane & 31), ks * 2 + (lane >> 5)));
-      } else {
-        const int kb = ks * 16 + (lane >> 5) * 8 + ((lane & 15) >> 2);
-        const int cb = (((lane >> 4) & 1) * 16 + 4 * (lane & 3)) * 2;
-#pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          const int byte = (wm * WTM + i * 32) * 2 + cb;
-          af[i] = lds_tr_frag(as + mn_off<BM>(kb, byte), as + mn_off<BM>(kb + 4, byte));
-        }
-      }
-      if constexpr (BKC) {
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          bfr[j] = *reinterpret_cast<const u32x4*>(bs + kc_offk<BK>(wn * WTN + j * 32 + (lane & 31), ks * 2 + (lane >> 5)));
-      } else {
-        const int kb = ks * 16 + (lane >> 5) * 8 + ((lane & 15) >> 2);
-        const int cb = (((lane >> 4) & 1) * 16 + 4 * (lane & 3)) * 2;
-#pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const int byte = (wn * WTN + j * 32) * 2 + cb;
-          bfr[j] = lds_tr_frag(bs + mn_off<BN>(kb, byte), bs + mn_off<BN>(kb + 4, byte));
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) Mma<T>::run(acc[i][j], af[i], bfr[j]);
+    for (int ks = 1; ks < KS; ++ks) {
+      frags(as, ks, fa[ks & 1], fb[ks & 1]);
+      mma(fa[(ks - 1) & 1], fb[(ks - 1) & 1]);
     }
   }
+  if (nk > 0) mma(fa[1], fb[1]);
   __syncthreads();
   wave_epilogue<BM, BN, WM, WN, GROUP, EPI>(args, ctx, acc, smem);
 }
