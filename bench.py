@@ -35,7 +35,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE layer tokens/s fwd+bwd at 1 GPU; grouped-GEMM % MFMA peak; permute GB/s"
 HEADLINE = "sparse_e256"
-SUB_CONFIGS = ("coarse_e8", "fine_e128", "fine_e128_zipf", "sparse_e256_round", "fine_e128_mxfp8")
+SUB_CONFIGS = ("coarse_e8", "fine_e128", "fine_e128_zipf", "sparse_e256_round", "fine_e128_mxfp8", "sparse_e256_mxfp8")
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 (MXFP8) MFMA
 PEAK_F32_TFLOPS = 157.3

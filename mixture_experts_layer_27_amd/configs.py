@@ -17,6 +17,9 @@ top-k routing.  Distributions follow the workloads the pages describe:
 * ``sparse_e256_round`` -- as above with counts rounded to multiples of 128.
 * ``fine_e128_mxfp8`` -- ``fine_e128`` with MXFP8 expert-GEMM operands (Olmo-core 3
                         article, "three splits" section: the MXFP8 switch).
+* ``sparse_e256_mxfp8`` -- ``sparse_e256`` with MXFP8 expert-GEMM operands: the
+                        switch at the wider d_model, where more tokens share
+                        each expert's weight quantisation.
 """
 from __future__ import annotations
 
@@ -87,14 +90,15 @@ SPARSE = MoEConfig("sparse_e256", T=32768, d=4096, E=256, k=8, f=512,
                    wg_std=1.0 / 64.0, bias="normal", b_std=0.5)
 SPARSE_ROUND = dataclasses.replace(SPARSE, name="sparse_e256_round", round_tile=128)
 FINE_MX = dataclasses.replace(FINE, name="fine_e128_mxfp8", gemm="mxfp8")
+SPARSE_MX = dataclasses.replace(SPARSE, name="sparse_e256_mxfp8", gemm="mxfp8")
 # routing variants at the fine_e128 shape: full-softmax gates, noisy top-k and both
 # router losses (dense router gradient); a capacity factor on the Zipf-imbalanced routing
 FINE_LOSSES = dataclasses.replace(FINE, name="fine_e128_router_losses", gate="all", lb_coef=0.01, z_coef=0.001,
                                   noise_std=1.0)
 FINE_CAPACITY = dataclasses.replace(FINE_ZIPF, name="fine_e128_zipf_capacity", capacity_factor=1.25)
 
-CONFIGS = {c.name: c for c in (TINY, COARSE, FINE, FINE_ZIPF, SPARSE, SPARSE_ROUND, FINE_MX, FINE_LOSSES,
-                               FINE_CAPACITY)}
+CONFIGS = {c.name: c for c in (TINY, COARSE, FINE, FINE_ZIPF, SPARSE, SPARSE_ROUND, FINE_MX, SPARSE_MX,
+                               FINE_LOSSES, FINE_CAPACITY)}
 
 
 def get(name: str) -> MoEConfig:

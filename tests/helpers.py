@@ -31,6 +31,7 @@ CASES = {
     "sparse_round_mx_small": configs.SPARSE_ROUND.scaled("sparse_round_mx_small", T=1200, d=512, E=64, f=128,
                                                          gemm="mxfp8"),
     "mx_ragged_d": configs.FINE_MX.scaled("mx_ragged_d", T=700, d=192, E=8, k=2, f=384),
+    "sparse_mx_small": configs.SPARSE_MX.scaled("sparse_mx_small", T=1200, d=512, E=64, f=128),
     "mx_zipf_small": configs.FINE_ZIPF.scaled("mx_zipf_small", T=1500, d=256, E=32, f=256, gemm="mxfp8"),
     "mx_one_token": configs.FINE_MX.scaled("mx_one_token", T=1, d=128, E=8, k=2, f=128),
     # routing variants: full-softmax gates, routing noise, load-balance and z-losses
@@ -175,6 +176,12 @@ def record(entry):
         os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
         with open(path, "a") as fh:
             fh.write(line + "\n")
+
+
+def progress(case, step):
+    """Record that a long reference step of a case has finished (same log as the
+    comparisons, so a run that writes only there shows where it is)."""
+    record({"case": case, "done": step})
 
 
 def assert_close(name, got, ref, atol=2e-2, rfrob=1e-2, stored="f32", case=None, extra=None, env=None):

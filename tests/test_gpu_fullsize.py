@@ -18,7 +18,7 @@ import torch
 
 import mx_alternatives as mxa
 from flip_envelope import Envelope
-from helpers import Checks, LazyExperts, make_inputs, precision, tokens_reaching, tol
+from helpers import Checks, LazyExperts, make_inputs, precision, progress, tokens_reaching, tol
 from mixture_experts_layer_27_amd import configs
 from oracle import moe_oracle as mo
 from oracle import mx
@@ -76,6 +76,7 @@ def check_sampled(cfg):
     print(f"[fullsize] {name}: oracle on {sub.N} rows ({len(toks)} sampled tokens, "
           f"router-weight gradients of experts {experts})", flush=True)
     fw = mo.forward(x, W1, W2, sub, prec)
+    progress(name, "oracle forward")
     row_of = {(int(t), int(e)): r for r, (t, e) in enumerate(zip(plan.token_of_row, plan.expert_of_row))}
     rows = np.array([row_of[(int(t), int(e))] for t, e in zip(sub.token_of_row, sub.expert_of_row)])
     stoks = np.unique(sub.token_of_row)        # every token of the sub-plan has all its rows there
@@ -87,6 +88,7 @@ def check_sampled(cfg):
     atol = tol(cfg)[0]
     dout = f64(g["dout"]) if run.has_bwd else None
     bw = mo.backward(x, wg, W1, W2, sub, fw["H"], dout, prec, weight_grads=False) if run.has_bwd else None
+    progress(name, "oracle backward")
     env = Envelope(sub, x, wg, W1, W2, fw, bw, dout)
     T, d = cfg.T, cfg.d
     on_toks = lambda fn, width: (lambda idx: fn(stoks[idx // width] * width + idx % width))
@@ -119,6 +121,7 @@ def check_sampled(cfg):
         print(f"[fullsize] {name}: oracle weight gradients of expert {e} ({sub_e.N} rows)", flush=True)
         fw_e = mo.forward(x, W1, W2, sub_e, prec)
         bw_e = mo.backward(x, wg, W1, W2, sub_e, fw_e["H"], dout, prec, weight_grads=[e])
+        progress(name, f"oracle weight gradients of expert {e}")
         env_e = Envelope(sub_e, x, wg, W1, W2, fw_e, bw_e, dout)
         dw1 = run.dw1[e].double().cpu().numpy()
         dw2 = run.dw2[e].double().cpu().numpy()
