@@ -56,8 +56,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fused-gather", choices=("auto", "on", "off"), default="auto",
                     help="on: the forward reads x through the plan inside the expert GEMMs (bf16) or the MXFP8 "
-                         "quantiser (no x_perm); off: x is permuted once and x_perm handed to the backward; "
-                         "auto (default): on for MXFP8 expert GEMMs, off for bf16")
+                         "quantiser, and the backward's dW1 reads x the same way (no x_perm); off: x is permuted "
+                         "once and x_perm handed to the backward; auto (default): on wherever the row offsets "
+                         "fit 32 bits")
     ap.add_argument("--cpu-tokens", type=int, default=0, help="oracle sample size (0 = automatic)")
     ap.add_argument("--out", default=None, help="also append the JSON line to this file")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -175,6 +176,11 @@ GEMM_KERNELS = ("up_swiglu", "down", "dact", "dx_perm", "dw1", "dw2")
 # ----------------------------------------------------------------- one workload
 
 
+def gather_possible(cfg):
+    """The expert GEMMs can read x through the plan (bf16 activations, 32-bit row offsets)."""
+    return cfg.act == "bf16" and cfg.T * cfg.d * 2 < 2 ** 31
+
+
 def measure(cfg, steps, warmup, fused_gather="auto", extras=False):
     """Time `steps` training steps of one workload; returns (metrics dict, inputs)."""
     import torch
@@ -182,8 +188,7 @@ def measure(cfg, steps, warmup, fused_gather="auto", extras=False):
 
     log(f"{cfg.name}: generating inputs")
     g = synth.generate(cfg)
-    want = fused_gather == "on" or (fused_gather == "auto" and cfg.gemm == "mxfp8")
-    fused = want and cfg.act == "bf16" and cfg.T * cfg.d * 2 < 2 ** 31
+    fused = fused_gather != "off" and gather_possible(cfg)
     torch.cuda.reset_peak_memory_stats()
     run = binding.LayerRun(cfg, g, fused_gather=fused)
     s = run.s
@@ -420,6 +425,7 @@ def activation_memory(cfg, run, binding):
     with_xp = held(True, False)
     store_y = held(True, True)
     return {"minimal": minimal, "with_x_perm": with_xp, "store_y_layer": store_y,
+            "timed_step_keeps": "with_x_perm" if run.x_perm is not None and not run.fused_gather else "minimal",
             "saving_minimal_vs_store_y": 1.0 - minimal / store_y,
             "saving_with_x_perm_vs_store_y": 1.0 - with_xp / store_y,
             "how": "torch.cuda.memory_allocated() after the forward, with only the tensors that set keeps alive "

@@ -496,8 +496,7 @@ moe_status backward_impl(const moe_shape* s, const void* x, const void* w_gate, 
   float* dz = dlogits ? dlogits : w.dlogits;
   // dO reaches the GEMMs through token_of_row inside their operand loads when the
   // kernels allow it (as fast as a permuted copy here, and no copy is stored),
-  // else as a permuted copy.  x without x_perm is permuted again: its gathered
-  // loads in the dW1 GEMM cost more than the permutation.
+  // else as a permuted copy.  x without x_perm is read the same way by dW1.
   const bool fused = gather_ok(*s);
   const int32_t* tor = plan->token_of_row;
   Seq seq(hs, trace);
@@ -539,10 +538,12 @@ moe_status backward_impl(const moe_shape* s, const void* x, const void* w_gate, 
     seq("mx_dx_perm", [&] { return gemm_mx_dx_perm(*s, *plan, pi, w.dhq, w1t, w.xbuf, hs); });
   } else {
     seq("dact", [&] { return gemm_dact(*s, *plan, pi, dO, dOg, w2, h_saved, w.dh, w.ga, w.ds_part, hs); });
-    if (!x_perm) seq("permute_x", [&] { return launch_permute_rows(*s, x, *plan, w.xbuf, hs); });
-    const void* xp = x_perm ? x_perm : w.xbuf;
+    // without x_perm, dW1 reads x through the plan (no permuted copy)
+    const bool gx = !x_perm && fused;
+    if (!x_perm && !gx) seq("permute_x", [&] { return launch_permute_rows(*s, x, *plan, w.xbuf, hs); });
+    const void* xp = x_perm ? x_perm : gx ? x : w.xbuf;
     seq("wgrad_chunks", [&] { return launch_wgrad_chunks(plan->offsets, s->E, w.wg.kch, w.wg, hs); });
-    seq("dw1", [&] { return gemm_dw1(*s, w.wg, w.dh, xp, dw1, hs); });
+    seq("dw1", [&] { return gemm_dw1(*s, w.wg, w.dh, xp, gx ? tor : nullptr, dw1, hs); });
     seq("dw1_reduce", [&] { return launch_wgrad_reduce(w.wg, s->E, (int64_t)2 * s->d_ff * s->d, dw1, hs); });
     seq("dw2", [&] { return gemm_dw2(*s, w.wg, dO, dOg, w.ga, dw2, hs); });
     seq("dw2_reduce", [&] { return launch_wgrad_reduce(w.wg, s->E, (int64_t)s->d * s->d_ff, dw2, hs); });

@@ -156,10 +156,11 @@ constexpr size_t big_lds_bytes(bool wide) {
   return wide ? big_ring_bytes<128, 512>() : big_ring_bytes<256, 256>();
 }
 
-// One output tile: BM x BN with WM x WN waves of 128 x 64.  GATHER = 1: the
+// One output tile: BM x BN with WM x WN waves of 128 x 64.  GATHER bit 1: the
 // rows of A (GROUP_M) or the k rows of A (GROUP_K) are read through
-// args.a_gather from a source of args.gather_rows rows: the permutation of the
-// rows is fused into the operand loads (no permuted copy is written).
+// args.a_gather; bit 2: the k rows of B (GROUP_K) through args.b_gather; either
+// from a source of args.gather_rows rows: the permutation of the rows is fused
+// into the operand loads (no permuted copy is written).
 template <int BM, int BN, int WM, int WN, bool AKC, bool BKC, int GROUP, int EPI, int GATHER = 0>
 MOE_DEV void big_tile(const Args& args, const TileCtx& ctx, char* smem) {
   using T = bf16_t;
@@ -217,6 +218,9 @@ MOE_DEV void big_tile(const Args& args, const TileCtx& ctx, char* smem) {
       }
       return (int64_t)j * rowb;         // j >= N lies past num0
     });
+  } else if constexpr (GATHER & 2) {    // GROUP_K, k rows of B gathered
+    rb.base = Bb;
+    rb.init_mn_gather(args.ldb, args.b_gather, ctx.k_begin, ctx.k_end, (int64_t)ctx.n0 * 2, args.gather_rows);
   } else {               // [K][N]: k rows, columns n0.. contiguous
     const int kb = (GROUP == GROUP_K) ? ctx.k_begin : 0;
     const int kend = (GROUP == GROUP_K) ? ctx.k_end : args.K;
@@ -281,7 +285,9 @@ MOE_DEV void big_tile(const Args& args, const TileCtx& ctx, char* smem) {
   auto load_a = [&](int kt) {
     if constexpr (!AKC && (GATHER & 1)) ra.load_gather(); else ra.load(kt);
   };
-  auto load_b = [&](int kt) { rb.load(kt); };
+  auto load_b = [&](int kt) {
+    if constexpr (!BKC && (GATHER & 2)) rb.load_gather(); else rb.load(kt);
+  };
   if (nk > 0) {
     load_a(0); load_b(0);
     ra.store(smem); rb.store(smem + ASZ);
