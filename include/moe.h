@@ -223,11 +223,10 @@ moe_status moe_unpermute_combine(const moe_shape *s, const void *y, const moe_pl
 
 /* Backward for the loss sum_t <out_t, dout_t>.
  *   Inputs: x [T,d], w_gate [E,d], w1, w2, the plan, h_saved, dout [T,d];
- *   x_perm [N_max,d] (act) = what moe_permute wrote for x with this plan, or NULL
- *   (then x is permuted again into the workspace; with MXFP8 its quantiser
- *   reads x through the plan instead; the results are identical).  dout is
- *   read through plan.token_of_row inside the GEMM and quantiser loads (bf16
- *   activations and T*d*2 < 2^31 bytes), else permuted into the workspace.
+ *   x_perm [N_max,d] (act) = what moe_permute wrote for x with this plan, or NULL.
+ *   Without it x and dout are read through plan.token_of_row inside the GEMM
+ *   and quantiser loads (bf16 activations and T*d*2 < 2^31 bytes), else they
+ *   are permuted into the workspace; the results are identical either way.
  *   fwd_ws = the workspace of this step's moe_grouped_gemm_swiglu call (same
  *   shape, plan, x_perm, w1 and w2, unchanged since), or NULL.  With MXFP8 the
  *   backward then reads the transposed weight codes and x_perm's token-axis

@@ -348,7 +348,8 @@ class LayerRun:
                                 self.ws_fwd, stream)
 
     def backward(self, stream=None, with_optional=True, reuse_x_perm=True, reuse_fwd_ws=True, trace=None):
-        """reuse_x_perm: hand the forward's permuted x to the backward (else it permutes x again);
+        """reuse_x_perm: hand the forward's permuted x to the backward (else its dW1 reads x
+        through the plan, or permutes x again where row gathers are not possible);
         reuse_fwd_ws: hand it the forward's workspace (MXFP8: the backward-orientation codes of
         W1, W2 and x_perm), else it quantises them again."""
         backward(self.s, self.inp["x"], self.inp["w_gate"], self.inp["w1"], self.inp["w2"], self.plan, self.h,
