@@ -35,7 +35,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "MoE layer tokens/s fwd+bwd at 1 GPU; grouped-GEMM % MFMA peak; permute GB/s"
 HEADLINE = "sparse_e256"
-SUB_CONFIGS = ("coarse_e8", "fine_e128", "fine_e128_zipf", "sparse_e256_round", "fine_e128_mxfp8", "sparse_e256_mxfp8")
+SUB_CONFIGS = ("coarse_e8", "fine_e128", "fine_e128_zipf", "sparse_e256_round", "fine_e128_mxfp8", "sparse_e256_mxfp8",
+               "fine_e128_router_losses", "fine_e128_zipf_capacity")
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 (MXFP8) MFMA
 PEAK_F32_TFLOPS = 157.3
@@ -277,7 +278,13 @@ def measure(cfg, steps, warmup, fused_gather="auto", extras=False):
         "workload": f"{cfg.name}: T={cfg.T} d_model={cfg.d} E={cfg.E} top-k={cfg.k} d_ff={cfg.f} SwiGLU, "
                     f"{'fwd+bwd' if run.has_bwd else 'fwd'}"
                     f"{', token rounding ' + str(cfg.round_tile) if cfg.round_tile else ''}"
-                    f"{', MXFP8 expert GEMMs' if cfg.gemm == 'mxfp8' else ''}",
+                    f"{', MXFP8 expert GEMMs' if cfg.gemm == 'mxfp8' else ''}"
+                    f"{', full-softmax gates' if cfg.gate == 'all' else ''}"
+                    f"{', routing noise N(0, %g)' % cfg.noise_std if cfg.noise_std else ''}"
+                    f"{', load-balance loss %g' % cfg.lb_coef if cfg.lb_coef else ''}"
+                    f"{', z-loss %g' % cfg.z_coef if cfg.z_coef else ''}"
+                    f"{', capacity factor %g' % cfg.capacity_factor if cfg.capacity_factor else ''}"
+                    f"{', Zipf routing' if cfg.bias == 'zipf' else ''}",
         "tokens_per_s": cfg.T / (med * 1e-3),
         "ms_per_step_median": med,
         "ms_per_step_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
