@@ -10,6 +10,8 @@
 // Backward (SonicMoE article, section 1): dA' = dO_perm W2_e is never stored;
 // its epilogue recomputes A from the saved H, reduces dS = <dA', A> per row,
 // and emits dH (SwiGLU backward) and gA = g * A for the W2 gradient.
+#include <atomic>
+
 #include "gemm_big.h"
 #include "gemm_dma.h"
 #include "gemm_engine.h"
@@ -55,6 +57,37 @@ hipError_t run_big(const Args& a, int64_t logical_tiles, hipStream_t st) {
   hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   const int64_t grid = 8 * ((logical_tiles + 7) / 8);
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBigThreads), lds, st, a);
+  return hipGetLastError();
+}
+
+// Compute units of the current device (cached per device).
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  if (dev >= 0 && dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// Persistent weight-gradient launch: one block per CU (its LDS admits no second),
+// a multiple of 8 so every block stays on its XCD's chunks.
+template <bool AKC, bool BKC, int EPI, int GATHER = 0>
+hipError_t run_wgrad_big(const Args& a, int64_t logical_tiles, hipStream_t st) {
+  auto kern = grouped_wgrad_big<AKC, BKC, EPI, GATHER>;
+  constexpr size_t lds = big_wgrad_lds_bytes();
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const int64_t need = 8 * ((logical_tiles + 7) / 8);
+  const int64_t cap = 8 * (int64_t)(device_cus() / 8 > 0 ? device_cus() / 8 : 1);
+  const int64_t grid = need < cap ? need : cap;
   if (grid <= 0) return hipSuccess;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBigThreads), lds, st, a);
   return hipGetLastError();
@@ -191,9 +224,9 @@ hipError_t run_wgrad(const moe_shape& s, const WgradChunks& w, Args& a, hipStrea
   if (s.act == MOE_BF16) {
     a.tilesM = ceil_div(a.M, 256); a.tilesN = ceil_div(a.N, 256);
     const int64_t tiles = 8 * (int64_t)ceil_div(w.max_chunks, 8) * a.tilesM * a.tilesN;
-    if (a.a_gather) return run_big<false, false, GROUP_K, EPI_F32, 1>(a, tiles, st);
-    if (a.b_gather) return run_big<false, false, GROUP_K, EPI_F32, 2>(a, tiles, st);
-    return run_big<false, false, GROUP_K, EPI_F32>(a, tiles, st);
+    if (a.a_gather) return run_wgrad_big<false, false, EPI_F32, 1>(a, tiles, st);
+    if (a.b_gather) return run_wgrad_big<false, false, EPI_F32, 2>(a, tiles, st);
+    return run_wgrad_big<false, false, EPI_F32>(a, tiles, st);
   }
   if (a.a_gather || a.b_gather) return hipErrorNotSupported;   // gathered k rows: bf16 kernels only
   a.tilesM = ceil_div(a.M, 128); a.tilesN = ceil_div(a.N, 128);

@@ -48,11 +48,6 @@ namespace moe_gemm {
 
 constexpr int kBigBK = 64;
 constexpr int kBigThreads = 512;
-constexpr uint32_t kBufferFlags = 0x00020000;   // gfx9 raw buffer: 32-bit dwords, no swizzle
-
-MOE_DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, (int)kBufferFlags);
-}
 
 // One operand tile (ROWS rows x 64 k, bf16) staged through registers by NT
 // threads, ROWS * 8 / NT 16-byte loads each.  Load i of a thread lands NT * 16
@@ -156,95 +151,118 @@ constexpr size_t big_lds_bytes(bool wide) {
   return wide ? big_ring_bytes<128, 512>() : big_ring_bytes<256, 256>();
 }
 
-// One output tile: BM x BN with WM x WN waves of 128 x 64.  GATHER bit 1: the
-// rows of A (GROUP_M) or the k rows of A (GROUP_K) are read through
+// The main loop of one BM x BN tile with WM x WN waves of 128 x 64.  GATHER bit
+// 1: the rows of A (GROUP_M) or the k rows of A (GROUP_K) are read through
 // args.a_gather; bit 2: the k rows of B (GROUP_K) through args.b_gather; either
 // from a source of args.gather_rows rows: the permutation of the rows is fused
 // into the operand loads (no permuted copy is written).
-template <int BM, int BN, int WM, int WN, bool AKC, bool BKC, int GROUP, int EPI, int GATHER = 0>
-MOE_DEV void big_tile(const Args& args, const TileCtx& ctx, char* smem) {
+// PERSIST: lane values come from opaque_tid (see the persistent kernel below).
+template <int BM, int BN, int WM, int WN, bool AKC, bool BKC, int GROUP, int EPI, int GATHER, bool PERSIST = false>
+struct BigPipe {
   using T = bf16_t;
-  constexpr int BK = kBigBK;
-  constexpr int WTM = BM / WM, WTN = BN / WN;
-  constexpr int TM = WTM / 32, TN = WTN / 32;
-  constexpr int NT = WM * WN * 64;
+  static constexpr int BK = kBigBK;
+  static constexpr int WTM = BM / WM, WTN = BN / WN;
+  static constexpr int TM = WTM / 32, TN = WTN / 32;
+  static constexpr int NT = WM * WN * 64;
   static_assert(NT == kBigThreads && WTM == 128 && WTN == 64, "eight waves of 128 x 64");
-  constexpr int ASZ = BM * BK * 2, BSZ = BN * BK * 2, STAGE = ASZ + BSZ;
-  const int e = ctx.e, nt = ctx.nt;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave / WN, wn = wave % WN;
-  const char* Ab = reinterpret_cast<const char*>(args.A) + (int64_t)e * args.a_estride * 2;
-  const char* Bb = reinterpret_cast<const char*>(args.B) + (int64_t)e * args.b_estride * 2;
-
+  static constexpr int ASZ = BM * BK * 2, BSZ = BN * BK * 2, STAGE = ASZ + BSZ;
   RegOperand<BM, AKC, NT> ra;
   RegOperand<BN, BKC, NT> rb;
-  if constexpr (AKC && (GATHER & 1)) {   // GROUP_M, rows gathered: row r of the tile is source row a_gather[..]
-    const int nrows = min(BM, ctx.row_end - ctx.row_begin);
-    const int64_t rowb = args.lda * 2;
-    ra.base = Ab;
-    ra.step = BK * 2;
-    ra.num0 = args.gather_rows * rowb;
-    ra.init_kc([&](int r) -> int64_t {
-      return (r < nrows ? (int64_t)args.a_gather[ctx.row_begin + r] : args.gather_rows) * rowb;   // absent: past num0
-    });
-  } else if constexpr (AKC) {   // GROUP_M: rows row_begin.. of the segment, K contiguous
-    const int nrows = min(BM, ctx.row_end - ctx.row_begin);
-    const int64_t rowb = args.lda * 2;
-    ra.base = Ab + (int64_t)ctx.row_begin * rowb;
-    ra.step = BK * 2;
-    ra.num0 = (int64_t)nrows * rowb;     // rows >= nrows start past it
-    ra.init_kc([&](int r) -> int64_t { return (int64_t)r * rowb; });
-  } else if constexpr (GATHER & 1) {    // GROUP_K, k rows gathered
-    ra.base = Ab;
-    ra.init_mn_gather(args.lda, args.a_gather, ctx.k_begin, ctx.k_end, (int64_t)ctx.m0 * 2, args.gather_rows);
-  } else {               // GROUP_K: k rows k_begin..k_end of the chunk, columns m0.. contiguous
-    ra.base = Ab + ((int64_t)ctx.k_begin * args.lda + ctx.m0) * 2;
-    ra.step = (int64_t)BK * args.lda * 2;
-    ra.num0 = (int64_t)(ctx.k_end - ctx.k_begin) * args.lda * 2 - (int64_t)ctx.m0 * 2;
-    ra.init_mn(args.lda);
-  }
-  if constexpr (BKC) {   // weights [N][K]
-    const int64_t rowb = args.ldb * 2;
-    rb.base = Bb;
-    rb.step = BK * 2;
-    rb.num0 = (int64_t)args.N * rowb;
-    rb.init_kc([&](int row) -> int64_t {
-      int j = ctx.n0 + row;
-      if constexpr (EPI == EPI_SWIGLU) {
-        // wave wn's columns: first half gate rows, second half the matching up rows
-        const int w = row / WTN, jj = row % WTN;
-        const int g = nt * (BN / 2) + w * (WTN / 2) + (jj % (WTN / 2));
-        j = g >= args.f ? args.N : (jj < WTN / 2) ? g : (args.f + g);   // past f: absent
-      }
-      return (int64_t)j * rowb;         // j >= N lies past num0
-    });
-  } else if constexpr (GATHER & 2) {    // GROUP_K, k rows of B gathered
-    rb.base = Bb;
-    rb.init_mn_gather(args.ldb, args.b_gather, ctx.k_begin, ctx.k_end, (int64_t)ctx.n0 * 2, args.gather_rows);
-  } else {               // [K][N]: k rows, columns n0.. contiguous
-    const int kb = (GROUP == GROUP_K) ? ctx.k_begin : 0;
-    const int kend = (GROUP == GROUP_K) ? ctx.k_end : args.K;
-    rb.base = Bb + ((int64_t)kb * args.ldb + ctx.n0) * 2;
-    rb.step = (int64_t)BK * args.ldb * 2;
-    rb.num0 = (int64_t)(kend - kb) * args.ldb * 2 - (int64_t)ctx.n0 * 2;
-    rb.init_mn(args.ldb);
+  int lane, wm, wn;
+
+  MOE_DEV BigPipe() { lanes(); }
+  MOE_DEV void lanes() {
+    const int tid = PERSIST ? opaque_tid() : (int)threadIdx.x;
+    const int wave = PERSIST ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
+    lane = tid & 63;
+    wm = wave / WN;
+    wn = wave % WN;
   }
 
-  f32x16 acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+  // Point the operand loads at tile ctx (a gathered operand fetches the source
+  // rows of its first stage).
+  MOE_DEV void setup(const Args& args, const TileCtx& ctx) {
+    const int e = ctx.e, nt = ctx.nt;
+    const char* Ab = reinterpret_cast<const char*>(args.A) + (int64_t)e * args.a_estride * 2;
+    const char* Bb = reinterpret_cast<const char*>(args.B) + (int64_t)e * args.b_estride * 2;
+    if constexpr (AKC && (GATHER & 1)) {   // GROUP_M, rows gathered: row r of the tile is source row a_gather[..]
+      const int nrows = min(BM, ctx.row_end - ctx.row_begin);
+      const int64_t rowb = args.lda * 2;
+      ra.base = Ab;
+      ra.step = BK * 2;
+      ra.num0 = args.gather_rows * rowb;
+      ra.init_kc([&](int r) -> int64_t {
+        return (r < nrows ? (int64_t)args.a_gather[ctx.row_begin + r] : args.gather_rows) * rowb;   // absent: past num0
+      });
+    } else if constexpr (AKC) {   // GROUP_M: rows row_begin.. of the segment, K contiguous
+      const int nrows = min(BM, ctx.row_end - ctx.row_begin);
+      const int64_t rowb = args.lda * 2;
+      ra.base = Ab + (int64_t)ctx.row_begin * rowb;
+      ra.step = BK * 2;
+      ra.num0 = (int64_t)nrows * rowb;     // rows >= nrows start past it
+      ra.init_kc([&](int r) -> int64_t { return (int64_t)r * rowb; });
+    } else if constexpr (GATHER & 1) {    // GROUP_K, k rows gathered
+      ra.base = Ab;
+      ra.init_mn_gather(args.lda, args.a_gather, ctx.k_begin, ctx.k_end, (int64_t)ctx.m0 * 2, args.gather_rows);
+    } else {               // GROUP_K: k rows k_begin..k_end of the chunk, columns m0.. contiguous
+      ra.base = Ab + ((int64_t)ctx.k_begin * args.lda + ctx.m0) * 2;
+      ra.step = (int64_t)BK * args.lda * 2;
+      ra.num0 = (int64_t)(ctx.k_end - ctx.k_begin) * args.lda * 2 - (int64_t)ctx.m0 * 2;
+      ra.init_mn(args.lda);
+    }
+    if constexpr (BKC) {   // weights [N][K]
+      const int64_t rowb = args.ldb * 2;
+      rb.base = Bb;
+      rb.step = BK * 2;
+      rb.num0 = (int64_t)args.N * rowb;
+      rb.init_kc([&](int row) -> int64_t {
+        int j = ctx.n0 + row;
+        if constexpr (EPI == EPI_SWIGLU) {
+          // wave wn's columns: first half gate rows, second half the matching up rows
+          const int w = row / WTN, jj = row % WTN;
+          const int g = nt * (BN / 2) + w * (WTN / 2) + (jj % (WTN / 2));
+          j = g >= args.f ? args.N : (jj < WTN / 2) ? g : (args.f + g);   // past f: absent
+        }
+        return (int64_t)j * rowb;         // j >= N lies past num0
+      });
+    } else if constexpr (GATHER & 2) {    // GROUP_K, k rows of B gathered
+      rb.base = Bb;
+      rb.init_mn_gather(args.ldb, args.b_gather, ctx.k_begin, ctx.k_end, (int64_t)ctx.n0 * 2, args.gather_rows);
+    } else {               // [K][N]: k rows, columns n0.. contiguous
+      const int kb = (GROUP == GROUP_K) ? ctx.k_begin : 0;
+      const int kend = (GROUP == GROUP_K) ? ctx.k_end : args.K;
+      rb.base = Bb + ((int64_t)kb * args.ldb + ctx.n0) * 2;
+      rb.step = (int64_t)BK * args.ldb * 2;
+      rb.num0 = (int64_t)(kend - kb) * args.ldb * 2 - (int64_t)ctx.n0 * 2;
+      rb.init_mn(args.ldb);
+    }
+  }
 
-  // TMV: how many of the wave's four 32-row sub-tiles hold rows of the segment.
-  // Sub-tiles wholly past the segment's last row skip their fragment reads and
-  // MFMAs (their accumulators stay zero and are never stored); the operand
-  // loads, LDS writes and barriers are the same for every wave.
-  auto run_loop = [&](auto tmv_c) {
-  constexpr int TMV = decltype(tmv_c)::value;
-  auto frags = [&](const char* as, int ks, u32x4 (&af)[TM], u32x4 (&bfr)[TN]) {
+  // stage loads, in stage order (the gathered operands fetch their rows one stage ahead)
+  MOE_DEV void load_a(int kt) {
+    if constexpr (!AKC && (GATHER & 1)) ra.load_gather(); else ra.load(kt);
+  }
+  MOE_DEV void load_b(int kt) {
+    if constexpr (!BKC && (GATHER & 2)) rb.load_gather(); else rb.load(kt);
+  }
+  // A gathered operand's loads go first: its next-stage row-index load is then
+  // followed by the other operand's loads, which the stage waits for anyway, so
+  // waiting for the index costs nothing extra (issued last, it cost dW1 5%).
+  MOE_DEV void load_ab(int kt) {
+    if constexpr (!BKC && (GATHER & 2)) { load_b(kt); load_a(kt); } else { load_a(kt); load_b(kt); }
+  }
+  MOE_DEV void store(char* stage) const { ra.store(stage); rb.store(stage + ASZ); }
+  // stage 0 written to LDS and visible to the block, stage 1 loading into registers
+  MOE_DEV void prologue(char* smem) {
+    load_ab(0);
+    store(smem);
+    load_ab(1);
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
+    cta_barrier();
+  }
+
+  template <int TMV>
+  MOE_DEV void frags(const char* as, int ks, u32x4 (&af)[TM], u32x4 (&bfr)[TN]) const {
     const char* bs = as + ASZ;
     const int kb = ks * 16 + (lane >> 5) * 8 + ((lane & 15) >> 2);       // MN: first k row of the lane
     const int cb = (((lane >> 4) & 1) * 16 + 4 * (lane & 3)) * 2;       // MN: byte column of the lane
@@ -270,87 +288,165 @@ MOE_DEV void big_tile(const Args& args, const TileCtx& ctx, char* smem) {
         bfr[j] = lds_tr_frag(bs + mn_off<BN>(kb, byte), bs + mn_off<BN>(kb + 4, byte));
       }
     }
-  };
-  auto mma = [&](const u32x4 (&af)[TM], const u32x4 (&bfr)[TN]) {
+  }
+  template <int TMV>
+  MOE_DEV static void mma(f32x16 (&acc)[TM][TN], const u32x4 (&af)[TM], const u32x4 (&bfr)[TN]) {
 #pragma unroll
     for (int i = 0; i < TMV; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) Mma<T>::run(acc[i][j], af[i], bfr[j]);
-  };
+  }
+
+  // nk stages into acc.  On entry stage 0 is in LDS (prologue) and stage 1 is
+  // loading into the registers (or PRO: the prologue is the first step).  TMV: how many of the wave's four 32-row
+  // sub-tiles hold rows of the segment; sub-tiles wholly past the segment's last
+  // row skip their fragment reads and MFMAs (their accumulators stay zero and are
+  // never stored); the operand loads, LDS writes and barriers are the same for
+  // every wave.  PEEL: the first iteration is code of its own, so its wait for
+  // stage 1 does not take in memory operations issued after those loads (they
+  // complete in issue order).
+  template <int TMV, bool PEEL, bool PRO = false>
+  MOE_DEV void run(int nk, char* smem, f32x16 (&acc)[TM][TN]) {
+    constexpr int NR = (AKC ? TMV : 2 * TMV) + (BKC ? TN : 2 * TN);   // LDS reads per k16 step
+    u32x4 a0[TM], b0[TN], a1[TM], b1[TN];
+    if constexpr (PERSIST) lanes();   // fragment offsets computed per tile (opaque_tid)
+    if (nk > 0) {
+      if constexpr (PRO) prologue(smem);   // PRO: the prologue runs here first
+      frags<TMV>(smem, 0, a0, b0);
+    }
+    auto iter = [&](int kt) __attribute__((always_inline)) {
+      const char* as = smem + (kt & 1) * STAGE;
+      char* an = smem + ((kt + 1) & 1) * STAGE;   // the next stage, written during this one
+      frags<TMV>(as, 1, a1, b1);
+      mma<TMV>(acc, a0, b0);
+      frags<TMV>(as, 2, a0, b0);
+      store(an);
+      load_ab(kt + 2);
+      mma<TMV>(acc, a1, b1);
+      frags<TMV>(as, 3, a1, b1);
+      mma<TMV>(acc, a0, b0);
+#pragma unroll
+      for (int i = 0; i < TMV * TN; ++i) {          // block 1: MFMA + fragment read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < TMV * TN; ++i) {          // block 2: MFMA + LDS write + the load that refills
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // its registers (+ fragment read)
+        if (i < ra.L + rb.L) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+        if (i < ra.L + rb.L) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < TMV * TN; ++i) {          // block 3: MFMA + fragment read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);          // this wave's fragment reads and stage writes are done
+      cta_barrier();
+      frags<TMV>(an, 0, a0, b0);
+      mma<TMV>(acc, a1, b1);
+#pragma unroll
+      for (int i = 0; i < TMV * TN; ++i) {          // block 4: MFMA + the next stage's first fragments
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+        if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+      }
+    };
+    int kt = 0;
+    if constexpr (PEEL) {
+      if (nk > 0) iter(0);
+      kt = 1;
+    }
+    for (; kt < nk; ++kt) iter(kt);
+  }
+};
+
+template <int TM, int TN>
+MOE_DEV void zero_acc(f32x16 (&acc)[TM][TN]) {
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+}
+
+// One output tile: BM x BN with WM x WN waves of 128 x 64.
+template <int BM, int BN, int WM, int WN, bool AKC, bool BKC, int GROUP, int EPI, int GATHER = 0>
+MOE_DEV void big_tile(const Args& args, const TileCtx& ctx, char* smem) {
+  using P = BigPipe<BM, BN, WM, WN, AKC, BKC, GROUP, EPI, GATHER>;
+  P p;
+  p.setup(args, ctx);
+  f32x16 acc[P::TM][P::TN];
+  zero_acc(acc);
   const int kext = (GROUP == GROUP_M) ? args.K : (ctx.k_end - ctx.k_begin);
-  const int nk = kext > 0 ? (kext + BK - 1) / BK : 0;
-  constexpr int NR = (AKC ? TMV : 2 * TMV) + (BKC ? TN : 2 * TN);   // LDS reads per k16 step
-  u32x4 a0[TM], b0[TN], a1[TM], b1[TN];
-  // stage loads, in stage order (the gathered operands fetch their rows one stage ahead)
-  auto load_a = [&](int kt) {
-    if constexpr (!AKC && (GATHER & 1)) ra.load_gather(); else ra.load(kt);
-  };
-  auto load_b = [&](int kt) {
-    if constexpr (!BKC && (GATHER & 2)) rb.load_gather(); else rb.load(kt);
-  };
-  // A gathered operand's loads go first: its next-stage row-index load is then
-  // followed by the other operand's loads, which the stage waits for anyway, so
-  // waiting for the index costs nothing extra (issued last, it cost dW1 5%).
-  auto load_ab = [&](int kt) {
-    if constexpr (!BKC && (GATHER & 2)) { load_b(kt); load_a(kt); } else { load_a(kt); load_b(kt); }
-  };
-  if (nk > 0) {
-    load_ab(0);
-    ra.store(smem); rb.store(smem + ASZ);
-    load_ab(1);
-    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0)
-    cta_barrier();
-    frags(smem, 0, a0, b0);
-  }
-  for (int kt = 0; kt < nk; ++kt) {
-    const char* as = smem + (kt & 1) * STAGE;
-    char* an = smem + ((kt + 1) & 1) * STAGE;   // the next stage, written during this one
-    frags(as, 1, a1, b1);
-    mma(a0, b0);
-    frags(as, 2, a0, b0);
-    ra.store(an); rb.store(an + ASZ);
-    load_ab(kt + 2);
-    mma(a1, b1);
-    frags(as, 3, a1, b1);
-    mma(a0, b0);
-#pragma unroll
-    for (int i = 0; i < TMV * TN; ++i) {          // block 1: MFMA + fragment read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < TMV * TN; ++i) {          // block 2: MFMA + LDS write + the load that refills
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // its registers (+ fragment read)
-      if (i < ra.L + rb.L) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-      if (i < ra.L + rb.L) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-      if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < TMV * TN; ++i) {          // block 3: MFMA + fragment read
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    }
-    __builtin_amdgcn_s_waitcnt(0xc07f);          // this wave's fragment reads and stage writes are done
-    cta_barrier();
-    frags(an, 0, a0, b0);
-    mma(a1, b1);
-#pragma unroll
-    for (int i = 0; i < TMV * TN; ++i) {          // block 4: MFMA + the next stage's first fragments
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-      if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
-    }
-  }
-  };
+  const int nk = kext > 0 ? (kext + P::BK - 1) / P::BK : 0;
   if constexpr (GROUP == GROUP_M) {
-    const int valid = min(BM, ctx.row_end - ctx.row_begin) - wm * WTM;   // >= 1 by the tile decode
-    if (valid > 96) run_loop(std::integral_constant<int, 4>{});
-    else if (valid > 64) run_loop(std::integral_constant<int, 3>{});
-    else if (valid > 32) run_loop(std::integral_constant<int, 2>{});
-    else run_loop(std::integral_constant<int, 1>{});
+    const int valid = min(BM, ctx.row_end - ctx.row_begin) - p.wm * P::WTM;   // >= 1 by the tile decode
+    if (valid > 96) p.template run<4, false, true>(nk, smem, acc);
+    else if (valid > 64) p.template run<3, false, true>(nk, smem, acc);
+    else if (valid > 32) p.template run<2, false, true>(nk, smem, acc);
+    else p.template run<1, false, true>(nk, smem, acc);
   } else {
-    run_loop(std::integral_constant<int, TM>{});
+    p.template run<P::TM, false, true>(nk, smem, acc);
   }
   wave_epilogue<BM, BN, WM, WN, GROUP, EPI>(args, ctx, acc, smem);
+}
+
+// Weight gradients (GROUP_K), persistent: a block per CU walks the logical
+// blocks b, b + gridDim.x, ... (gridDim.x a multiple of 8, so a block keeps to
+// its XCD's chunks and every CU of an XCD gets the same share of each chunk).
+// A wave that ends waits for its stores to be acknowledged, and a new block then
+// waits for its first stages; here the next tile's first stages are fetched
+// while this tile's fp32 rows are stored, in the gaps of the epilogue: the
+// gathered operand's row indices before sub-tile 0, stage 0 after it, stage 0
+// written to LDS and stage 1 fetched after sub-tile 1.  Loads complete in issue
+// order, so waiting for them does not wait for the stores issued after them, and
+// the stores drain under the next tile's first stages.  The epilogue's row slabs
+// sit above stage 0 of the ring (in stage 1, idle until the next tile's first
+// iteration, which follows a barrier).
+template <bool AKC, bool BKC, int EPI, int GATHER>
+MOE_DEV void big_wgrad_tiles(const Args& args, char* smem) {
+  using P = BigPipe<256, 256, 2, 4, AKC, BKC, GROUP_K, EPI, GATHER, true>;
+  auto stages = [](const TileCtx& c) {
+    const int kext = c.k_end - c.k_begin;
+    return kext > 0 ? (kext + P::BK - 1) / P::BK : 0;
+  };
+  P p;
+  int b = blockIdx.x;
+  TileCtx ctx;
+  if (!decode_k_block<256, 256, kBigBK>(args, b, ctx)) return;
+  f32x16 acc[P::TM][P::TN];
+  zero_acc(acc);
+  p.setup(args, ctx);
+  p.prologue(smem);
+  p.template run<P::TM, false>(stages(ctx), smem, acc);
+  for (;;) {
+    const int nb = b + (int)gridDim.x;
+    TileCtx nx;
+    const bool more = decode_k_block<256, 256, kBigBK>(args, nb, nx);
+    if (more) p.setup(args, nx);
+    // after the last stage's barrier no wave reads this tile's stages any more
+    wave_epilogue<256, 256, 2, 4, GROUP_K, EPI, true>(args, ctx, acc, smem + P::STAGE, [&](auto ic) __attribute__((always_inline)) {
+      constexpr int i = decltype(ic)::value;
+      if constexpr (i == 0) {
+        if (more) p.load_ab(0);
+      } else if constexpr (i == 1) {
+        if (more) {
+          p.store(smem);
+          p.load_ab(1);
+        }
+      }
+    });
+    if (!more) return;
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // stage 0 written, slab rows read back
+    cta_barrier();
+    ctx = nx;
+    b = nb;
+    zero_acc(acc);
+    // reached only from here: its wait for stage 1 leaves out the stores above
+    p.template run<P::TM, true>(stages(ctx), smem, acc);
+  }
 }
 
 // GROUP_M decode over 128-row units (see the header comment): returns false when
@@ -390,6 +486,19 @@ MOE_DEV bool big_decode_m(const Args& args, TileCtx& c, bool* wide) {
     c.m0 = (ue - 1) * 128; c.n0 = cq * 512;
   }
   return true;
+}
+
+// LDS of the persistent weight-gradient kernel: stage 0, then the larger of
+// stage 1 and the epilogue's row slabs (eight waves x 32 rows x 72 floats)
+constexpr size_t big_wgrad_lds_bytes() {
+  constexpr size_t stage = (size_t)(256 + 256) * kBigBK * 2, slabs = (size_t)8 * 32 * (64 + 8) * 4;
+  return stage + (slabs > stage ? slabs : stage);
+}
+
+template <bool AKC, bool BKC, int EPI, int GATHER>
+__global__ __launch_bounds__(kBigThreads) void grouped_wgrad_big(Args args) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  big_wgrad_tiles<AKC, BKC, EPI, GATHER>(args, smem);
 }
 
 template <bool AKC, bool BKC, int GROUP, int EPI, int GATHER = 0>

@@ -149,6 +149,27 @@ MOE_DEV void static_for(F&& f) {
 
 MOE_DEV float fast_sigmoid(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
+constexpr uint32_t kBufferFlags = 0x00020000;   // gfx9 raw buffer: 32-bit dwords, no swizzle
+constexpr int kCachePolicyNT = 2;                 // buffer store cache policy: non-temporal (nt)
+
+MOE_DEV __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, (int)kBufferFlags);
+}
+
+// threadIdx.x through an opaque move: values derived from it are computed where
+// they are used and not hoisted out of a persistent kernel's tile loop (where they
+// would stay live across the main loop and spill).
+MOE_DEV int opaque_tid() {
+  int t = (int)threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
+struct NoEpilogueHook {
+  template <class I>
+  MOE_DEV void operator()(I) const {}
+};
+
 // Wave-private epilogue: each wave stages its (BM/WM) x (BN/WN) accumulators in
 // its own LDS slab, 32 rows at a time, and reads them back as 8-column vectors --
 // no block-wide barrier.  Slab row stride WTN + 8 floats keeps the two 32-lane
@@ -158,15 +179,20 @@ MOE_DEV float fast_sigmoid(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf
 // Latency: every sub-tile first issues all its global loads (the saved H and the
 // gates of the SwiGLU backward) and all its slab reads, then computes and
 // stores, so a wave waits once per sub-tile rather than once per row chunk.
-template <int BM, int BN, int WM, int WN, int GROUP, int EPI>
+// PERSIST (a kernel that walks several tiles): the thread index is taken through
+// opaque_tid, the weight gradients are written with raw buffer stores (below),
+// and after(integral_constant<int, i>) runs once sub-tile i is stored and its
+// slab rows are read back (the kernel starts its next tile there).
+template <int BM, int BN, int WM, int WN, int GROUP, int EPI, bool PERSIST = false, class After = NoEpilogueHook>
 MOE_DEV void wave_epilogue(const Args& args, const TileCtx& ctx, f32x16 (&acc)[BM / WM / 32][BN / WN / 32],
-                           char* smem) {
+                           char* smem, After after = After{}) {
   using T = bf16_t;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int TM = WTM / 32, TN = WTN / 32;
   constexpr int SS = WTN + 8;              // slab row stride (floats)
   constexpr int CPR = WTN / 8;             // 8-column chunks per wave row
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = PERSIST ? opaque_tid() : (int)threadIdx.x;
+  const int lane = tid & 63, wave = PERSIST ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   float* slab = reinterpret_cast<float*>(smem) + wave * 32 * SS;
   const int rbase = ctx.row_begin + wm * WTM;     // GROUP_M: first row of this wave's tile
@@ -443,6 +469,18 @@ MOE_DEV void wave_epilogue(const Args& args, const TileCtx& ctx, f32x16 (&acc)[B
         constexpr int IT = 32 * CU / 64;
         OT* C = reinterpret_cast<OT*>(args.C);
         if constexpr (GROUP == GROUP_K) C = wgrad_out<OT>(args, ctx);
+        // Weight gradients are written once and not read again in the step: their
+        // stores carry the non-temporal hint, so gigabytes of fp32 rows stream out
+        // instead of filling the caches with dirty lines that later kernels would
+        // pay to write back (and that would push out the GEMM's operand tiles).
+        // Persistent weight gradients: raw buffer stores from the sub-tile's first
+        // row, a lane outside the output given an offset past the record count (it
+        // writes nothing), so no branch surrounds the stores and the compiler can
+        // count them (the next tile's loads, issued before them, are then waited
+        // for without waiting for the stores).  Offsets < 32 * ldc * 4 < 2^31.
+        constexpr bool BUF = PERSIST && GROUP == GROUP_K && VW == 4;
+        constexpr uint32_t kNoStore = 0x7ffffff0u;
+        const __amdgpu_buffer_rsrc_t crs = make_rsrc(BUF ? C + (int64_t)(mbase + i * 32) * args.ldc : C, kNoStore);
         float v[IT][VW];
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
@@ -460,19 +498,28 @@ MOE_DEV void wave_epilogue(const Args& args, const TileCtx& ctx, f32x16 (&acc)[B
           if constexpr (GROUP == GROUP_M) { grow = rbase + i * 32 + rr; ok = grow < ctx.row_end; }
           else { grow = mbase + i * 32 + rr; ok = grow < args.M; }
           const int col = cbase + ch * VW;
-          if (ok && col < args.N) {
+          if constexpr (BUF) {
+            const uint32_t off = (ok && col < args.N) ? (uint32_t)(rr * args.ldc + col) * 4u : kNoStore;
+            __builtin_amdgcn_raw_buffer_store_b128(
+                u32x4{__float_as_uint(v[it][0]), __float_as_uint(v[it][1]), __float_as_uint(v[it][2]),
+                      __float_as_uint(v[it][3])},
+                crs, (int)off, 0, kCachePolicyNT);
+          } else if (ok && col < args.N) {
             if constexpr (VW == 8) {
               Vec8<OT>::store(C + (int64_t)grow * args.ldc + col, v[it]);
             } else {
-              stg16(C + (int64_t)grow * args.ldc + col,
-                    u32x4{__float_as_uint(v[it][0]), __float_as_uint(v[it][1]), __float_as_uint(v[it][2]),
-                          __float_as_uint(v[it][3])});
+              const u32x4 q{__float_as_uint(v[it][0]), __float_as_uint(v[it][1]), __float_as_uint(v[it][2]),
+                            __float_as_uint(v[it][3])};
+              u32x4* dst = reinterpret_cast<u32x4*>(C + (int64_t)grow * args.ldc + col);
+              if constexpr (GROUP == GROUP_K) __builtin_nontemporal_store(q, dst);
+              else *dst = q;
             }
           }
         }
       }
     }
     __builtin_amdgcn_s_waitcnt(0xc07f);          // slab reads done before the next sub-tile overwrites it
+    after(ic);
   });
 }
 

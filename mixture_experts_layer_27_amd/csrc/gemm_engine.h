@@ -314,18 +314,31 @@ MOE_DEV OT* wgrad_out(const Args& args, const TileCtx& c) {
                     : reinterpret_cast<OT*>(args.Cpart) + (int64_t)c.slot * args.c_estride;
 }
 
+// GROUP_K tile of block index b: chunks go round robin over the XCDs (chunk q on
+// XCD q % 8, block b on XCD b % 8), all tiles of a chunk on one XCD: its rows of
+// both operands are read into one L2.  False past the last chunk (and for every
+// later b of the same XCD).
+// The chunk table is read with block-uniform addresses; a persistent kernel's
+// stores keep the compiler from using scalar loads for it, so the values are
+// moved to scalar registers explicitly (the buffer descriptors built from them
+// must be uniform).
+template <int BM, int BN, int BK>
+MOE_DEV bool decode_k_block(const Args& args, int b, TileCtx& c) {
+  const int pe = args.tilesM * args.tilesN;
+  const int t = b >> 3;
+  const int q = (b & 7) + 8 * (t / pe);
+  if (q >= __builtin_amdgcn_readfirstlane(*args.nchunks)) return false;
+  decode_at<BM, BN, BK, GROUP_K>(args, q * pe + t % pe, c);
+  c.e = __builtin_amdgcn_readfirstlane(c.e);
+  c.k_begin = __builtin_amdgcn_readfirstlane(c.k_begin);
+  c.k_end = __builtin_amdgcn_readfirstlane(c.k_end);
+  c.slot = __builtin_amdgcn_readfirstlane(c.slot);
+  return true;
+}
+
 template <int BM, int BN, int BK, int GROUP>
 MOE_DEV bool decode_tile(const Args& args, TileCtx& c) {
-  if constexpr (GROUP == GROUP_K) {
-    // chunks go round robin over the XCDs (chunk q on XCD q % 8), all tiles of a
-    // chunk on one XCD: its rows of both operands are read into one L2
-    const int pe = args.tilesM * args.tilesN;
-    const int b = blockIdx.x, t = b >> 3;
-    const int q = (b & 7) + 8 * (t / pe);
-    if (q >= *args.nchunks) return false;
-    decode_at<BM, BN, BK, GROUP>(args, q * pe + t % pe, c);
-    return true;
-  }
+  if constexpr (GROUP == GROUP_K) return decode_k_block<BM, BN, BK>(args, blockIdx.x, c);
   const int total = total_tiles<GROUP>(args);
   const int per = (total + 7) >> 3;
   const int b = blockIdx.x;
