@@ -271,6 +271,16 @@ hipError_t gemm_router_logits(const moe_shape& s, const void* x, const void* wg,
   // 32-row tiles: T/32 blocks keep every CU busy with two of them (the K loop is
   // latency-bound at this width); all E columns in one tile read each x row once.
   a.tilesM = ceil_div(s.T, 32);
+  if (s.act == MOE_BF16 && s.E % 256 == 0 && s.d % 32 == 0 &&
+      (int64_t)ceil_div(s.T, 128) * (s.E / 256) >= device_cus()) {
+    // 128 x 256 tiles on the DMA main loop: a quarter of the operand bytes per
+    // flop of 32 x 128 tiles, worth it once every CU gets a tile (sparse_e256:
+    // 104 instead of 196 us); with fewer tiles the 32-row tiles fill the chip
+    a.tilesM = ceil_div(s.T, 128);
+    a.tilesN = s.E / 256;
+    a.total_static = a.tilesM * a.tilesN;
+    return run_dma<128, 256, 2, 4, true, true, GROUP_NONE, EPI_LOGITS, 3>(a, a.total_static, st);
+  }
   if (s.act == MOE_BF16) {
     if (s.E > 64) {
       a.tilesN = ceil_div(s.E, 128);

@@ -489,6 +489,23 @@ MOE_DEV void wave_epilogue(const Args& args, const TileCtx& ctx, f32x16 (&acc)[B
 #pragma unroll
           for (int c = 0; c < VW; ++c) v[it][c] = src[c];
         }
+        if constexpr (EPI == EPI_LOGITS) {
+          // router logits: (z + bias) + noise, in that order; the launcher keeps
+          // N a multiple of the tile width (no partial column vectors)
+          static_assert(GROUP == GROUP_NONE && VW == 4, "logits: fp32 rows of x W_g^T");
+          const float* nz = reinterpret_cast<const float*>(args.aux);   // routing noise [M, N] or null
+#pragma unroll
+          for (int it = 0; it < IT; ++it) {
+            const int u = lane + 64 * it;
+            const int grow = mbase + i * 32 + u / CU, col = cbase + (u % CU) * VW;
+            if (grow < args.M && col < args.N) {
+#pragma unroll
+              for (int c = 0; c < VW; ++c)
+                v[it][c] = (v[it][c] + (args.bias ? args.bias[col + c] : 0.0f)) +
+                           (nz ? nz[(int64_t)grow * args.ld_aux + col + c] : 0.0f);
+            }
+          }
+        }
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
           const int u = lane + 64 * it;
@@ -532,7 +549,7 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma(Args args) {
   constexpr int TM = WTM / 32, TN = WTN / 32;
   constexpr int ASZ = BM * BK * 2, BSZ = BN * BK * 2, STAGE = ASZ + BSZ;
   static_assert(TM >= 1 && TN >= 1, "wave tile must hold a 32x32 MFMA tile");
-  static_assert(GROUP != GROUP_NONE, "router GEMMs use the register-staged kernel");
+  static_assert(GROUP != GROUP_NONE || (AKC && EPI == EPI_LOGITS), "GROUP_NONE: the router logits (x rows)");
   extern __shared__ __attribute__((aligned(16))) char smem[];
 
   TileCtx ctx;
@@ -550,6 +567,10 @@ __global__ __launch_bounds__(WM* WN * 64) void grouped_gemm_dma(Args args) {
   DmaOperand<BN, NW, BKC, BK> db;
   if constexpr (AKC) {
     da.init_kc([&](int row) -> const T* {
+      if constexpr (GROUP == GROUP_NONE) {   // rows m0.. of A; past M only feed unstored outputs
+        const int g = min(m0 + row, args.M - 1);
+        return Ab + (int64_t)g * args.lda;
+      }
       int g = row_begin + row;
       if (g >= row_end) g = row_end - 1;     // rows past the segment only feed unstored outputs
       const int src = args.a_gather ? args.a_gather[g] : g;

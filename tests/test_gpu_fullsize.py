@@ -38,6 +38,12 @@ def test_max_tokens_sampled():
     check_sampled(configs.FINE.scaled("max_tokens", T=1 << 20, d=64, E=64, k=2, f=128))
 
 
+def test_router_tiles_sampled():
+    """E = 256 with T = 32768 tokens: the router logits run on 128 x 256 tiles, one
+    per CU (the sparse_e256 shape with small d and d_ff)."""
+    check_sampled(configs.SPARSE.scaled("router_tiles", T=32768, d=64, E=256, k=2, f=128))
+
+
 def check_sampled(cfg):
     from mixture_experts_layer_27_amd import binding
     name = cfg.name
