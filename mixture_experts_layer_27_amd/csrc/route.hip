@@ -15,6 +15,7 @@
 // segments ("row-wise" expert buffers of the Olmo-core 3 article, "three splits"
 // section), tokens ascending inside a segment; everything stays on the device.
 // Token rounding follows the SonicMoE article, section 3.
+#include <climits>
 #include <cmath>
 #include <cstdint>
 
@@ -24,44 +25,31 @@
 namespace moe {
 namespace {
 
-// (value desc, index asc) as one unsigned 64-bit key: larger key = better.
-// High word: the float's bits mapped to an unsigned order; low word: ~index.
-// Key 0 lies below every real value (it stands for "no candidate").
-MOE_DEV uint64_t rank_key(float v, int e) {
-  const uint32_t b = v == 0.0f ? 0u : __float_as_uint(v);   // -0 ranks as +0
-  const uint32_t u = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-  return ((uint64_t)u << 32) | (uint32_t)~(uint32_t)e;
+// Logits as order-preserving integers for the selection: a larger key is a
+// larger value, -0 maps to +0 (they tie), and INT_MIN lies below every key of a
+// number (the slot of a taken or absent expert).
+MOE_DEV int order_key(float v) {
+  const int b = v == 0.0f ? 0 : __float_as_int(v);
+  return b ^ ((b >> 31) & 0x7fffffff);
 }
-MOE_DEV float key_value(uint64_t k) {
-  const uint32_t u = (uint32_t)(k >> 32);
-  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
-}
-MOE_DEV int key_index(uint64_t k) { return (int)~(uint32_t)k; }
+MOE_DEV float key_float(int k) { return __int_as_float(k ^ ((k >> 31) & 0x7fffffff)); }
 
-// Wave-wide maximum of a 64-bit key: DPP exchanges inside each 16-lane row
-// (quad xor 1, quad xor 2, half-row mirror, row mirror), then the four row
-// results combined from lane reads.
-template <int CTRL>
-MOE_DEV uint64_t dpp_max(uint64_t k) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)k, CTRL, 0xf, 0xf, false);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(k >> 32), CTRL, 0xf, 0xf, false);
-  const uint64_t o = ((uint64_t)hi << 32) | lo;
-  return o > k ? o : k;
+// Wave-wide maximum of an int (uniform result): DPP maxima inside each 16-lane
+// row, then rows 0-1 and 2-3 (row_bcast:15), then all four (row_bcast:31), which
+// leaves it in lane 63.
+template <int CTRL, int ROWS>
+MOE_DEV int dpp_imax(int v) {
+  // lanes outside ROWS read INT_MIN, the identity of max
+  return max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, CTRL, ROWS, 0xf, false));
 }
-MOE_DEV uint64_t wave_max_key(uint64_t k) {
-  k = dpp_max<0xB1>(k);    // quad_perm [1,0,3,2]
-  k = dpp_max<0x4E>(k);    // quad_perm [2,3,0,1]
-  k = dpp_max<0x141>(k);   // row_half_mirror
-  k = dpp_max<0x140>(k);   // row_mirror
-  uint64_t best = 0;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)k, 16 * r);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), 16 * r);
-    const uint64_t o = ((uint64_t)hi << 32) | lo;
-    best = o > best ? o : best;
-  }
-  return best;
+MOE_DEV int wave_max_i32(int v) {
+  v = dpp_imax<0xB1, 0xf>(v);    // quad_perm [1,0,3,2]
+  v = dpp_imax<0x4E, 0xf>(v);    // quad_perm [2,3,0,1]
+  v = dpp_imax<0x141, 0xf>(v);   // row_half_mirror
+  v = dpp_imax<0x140, 0xf>(v);   // row_mirror: every lane holds its row's maximum
+  v = dpp_imax<0x142, 0xa>(v);   // row_bcast:15 into rows 1 and 3
+  v = dpp_imax<0x143, 0xc>(v);   // row_bcast:31 into rows 2 and 3
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
 // One wave per token; a wave takes TPW tokens in turn (NT/64*TPW per block).  Lane
@@ -90,30 +78,34 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ logi
     const int t = t0 + tl;
     if (t >= T) break;
     float z[V];
-    bool taken[V];
+    int ks[V];   // selection keys of the candidates (INT_MIN once taken, or absent)
 #pragma unroll
     for (int v = 0; v < V; ++v) {
       int e = lane + 64 * v;
       z[v] = (e < E) ? logits[(int64_t)t * E + e] : -INFINITY;
-      taken[v] = !(e < E);
+      ks[v] = (e < E) ? order_key(z[v]) : INT_MIN;
     }
+    // Round j: the largest candidate key, then the lowest expert index holding
+    // it (expert lane + 64 v: the first slot v with a match, its lowest lane).
+    // k <= E leaves a candidate in every round.
     int sel_e[8];
     float sel_z[8];
     for (int j = 0; j < k; ++j) {
-      uint64_t kb = 0;   // this lane's best untaken expert
+      int m = ks[0];
 #pragma unroll
-      for (int v = 0; v < V; ++v) {
-        const uint64_t kv = taken[v] ? 0ull : rank_key(z[v], lane + 64 * v);
-        kb = kv > kb ? kv : kb;
+      for (int v = 1; v < V; ++v) m = max(m, ks[v]);
+      const int bk = wave_max_i32(m);
+      int be = -1;
+#pragma unroll
+      for (int v = V - 1; v >= 0; --v) {
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(ks[v] == bk);
+        if (hit) be = 64 * v + (int)__builtin_ctzll(hit);
       }
-      kb = wave_max_key(kb);
-      const int be = key_index(kb);
-      const float bv = key_value(kb);
       sel_e[j] = be;
-      sel_z[j] = bv;
+      sel_z[j] = key_float(bk);
 #pragma unroll
       for (int v = 0; v < V; ++v)
-        if (lane + 64 * v == be) taken[v] = true;
+        if (lane + 64 * v == be) ks[v] = INT_MIN;
     }
     // softmax over the k selected logits (the first is the largest), or the
     // full softmax's denominator (gate_all, uniform over the wave)
