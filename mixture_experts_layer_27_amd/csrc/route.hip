@@ -25,6 +25,8 @@
 namespace moe {
 namespace {
 
+constexpr int kMaxTopK = 8;   // the library's limit on k (checked on the host)
+
 // Logits as order-preserving integers for the selection: a larger key is a
 // larger value, -0 maps to +0 (they tie), and INT_MIN lies below every key of a
 // number (the slot of a taken or absent expert).
@@ -87,10 +89,14 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ logi
     }
     // Round j: the largest candidate key, then the lowest expert index holding
     // it (expert lane + 64 v: the first slot v with a match, its lowest lane).
-    // k <= E leaves a candidate in every round.
-    int sel_e[8];
-    float sel_z[8];
-    for (int j = 0; j < k; ++j) {
+    // k <= E leaves a candidate in every round.  The loops over the k selections
+    // run to kMaxTopK with a uniform j < k test, so sel_e / sel_z are indexed by
+    // constants (a runtime index costs a select chain over all 8 per access).
+    int sel_e[kMaxTopK];
+    float sel_z[kMaxTopK];
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      if (j >= k) break;
       int m = ks[0];
 #pragma unroll
       for (int v = 1; v < V; ++v) m = max(m, ks[v]);
@@ -117,20 +123,24 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ logi
         if (lane + 64 * v < E) sa += expf(z[v] - sel_z[0]);
       den = wave_sum(sa);
     } else {
-      for (int j = 0; j < k; ++j) den += expf(sel_z[j] - sel_z[0]);
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j)
+        if (j < k) den += expf(sel_z[j] - sel_z[0]);
     }
     if (lane < k) {
       float zj = sel_z[0];
       int ej = sel_e[0];
-      for (int j = 1; j < k; ++j)
-        if (lane == j) { zj = sel_z[j]; ej = sel_e[j]; }
+#pragma unroll
+      for (int j = 1; j < kMaxTopK; ++j)
+        if (j < k && lane == j) { zj = sel_z[j]; ej = sel_e[j]; }
       topk_idx[(int64_t)t * k + lane] = ej;
       topk_gate[(int64_t)t * k + lane] = expf(zj - sel_z[0]) / den;
     }
     if (lane < words) {
       uint32_t w = 0;
-      for (int j = 0; j < k; ++j)
-        if ((sel_e[j] >> 5) == lane) w |= 1u << (sel_e[j] & 31);
+#pragma unroll
+      for (int j = 0; j < kMaxTopK; ++j)
+        if (j < k && (sel_e[j] >> 5) == lane) w |= 1u << (sel_e[j] & 31);
       keep_bits[(int64_t)t * words + lane] = w;
     }
     if constexpr (ROUND) {
@@ -146,8 +156,9 @@ __global__ __launch_bounds__(NT) void topk_kernel(const float* __restrict__ logi
       }
       if (lane < k) {
         int ej = sel_e[0];
-        for (int j = 1; j < k; ++j)
-          if (lane == j) ej = sel_e[j];
+#pragma unroll
+        for (int j = 1; j < kMaxTopK; ++j)
+          if (j < k && lane == j) ej = sel_e[j];
         atomicOr(&sel[ej * 2 + (tl >> 5)], 1u << (tl & 31));
       }
     }
