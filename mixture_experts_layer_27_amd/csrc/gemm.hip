@@ -311,7 +311,24 @@ hipError_t gemm_router_dx_dense(const moe_shape& s, const void* dzq, const void*
   return run<float, 128, 128, 2, 2, true, false, GROUP_NONE, EPI_F32>(a, a.total_static, st);
 }
 
+// dW_g on the persistent 256 x 256 weight-gradient kernel: both operands are
+// token-major like the expert weight gradients.  Used when the tiles of the
+// chunks fill the 256 CUs with chunks of at least 1024 token rows
+// (sparse_e256: 2 x 16 tiles x 8 chunks of 4096 rows); otherwise 128 x 128
+// split-K tiles.
+namespace {
+int router_dwg_big_splits(const moe_shape& s) {
+  const int M = router_dz_rows(s);
+  if (s.act != MOE_BF16 || M % 256 != 0 || s.d % 256 != 0) return 0;
+  const int pe = (M / 256) * (s.d / 256);
+  const int sp = ceil_div(256, pe);
+  if ((int64_t)sp * 1024 > s.T) return 0;
+  return sp;
+}
+}  // namespace
+
 int gemm_router_dwg_splits(const moe_shape& s) {
+  if (const int big = router_dwg_big_splits(s)) return big;
   const int tiles = ceil_div(router_dz_rows(s), 128) * ceil_div(s.d, 128);
   int sp = ceil_div(512, tiles);
   const int maxsp = ceil_div(s.T, 256);
@@ -329,6 +346,11 @@ hipError_t gemm_router_dwg(const moe_shape& s, const void* dzq, const void* x, f
   a.M = router_dz_rows(s); a.N = s.d; a.K = s.T;
   a.C = part; a.ldc = s.d; a.c_kstride = (int64_t)a.M * s.d;
   a.ksplit = gemm_router_dwg_splits(s);
+  if (router_dwg_big_splits(s)) {
+    a.tilesM = a.M / 256; a.tilesN = s.d / 256;
+    a.Cpart = part + a.c_kstride; a.c_estride = a.c_kstride;   // chunk q > 0: slot q - 1 = part[q]
+    return run_wgrad_big<false, false, EPI_F32>(a, 8 * (int64_t)ceil_div(a.ksplit, 8) * a.tilesM * a.tilesN, st);
+  }
   a.tilesM = ceil_div(a.M, 128); a.tilesN = ceil_div(s.d, 128);
   a.total_static = a.tilesM * a.tilesN * a.ksplit;
   if (s.act == MOE_BF16) return run<bf16_t, 128, 128, 2, 2, false, false, GROUP_NONE, EPI_F32>(a, a.total_static, st);

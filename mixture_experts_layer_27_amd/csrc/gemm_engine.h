@@ -322,11 +322,25 @@ MOE_DEV OT* wgrad_out(const Args& args, const TileCtx& c) {
 // stores keep the compiler from using scalar loads for it, so the values are
 // moved to scalar registers explicitly (the buffer descriptors built from them
 // must be uniform).
+// Without a chunk table (args.chunks null) the launch is one reduction over K
+// rows in args.ksplit chunks of equal length (a multiple of BK; the router
+// weight gradient): chunk 0 writes C, chunk q > 0 partial slot q - 1.
 template <int BM, int BN, int BK>
 MOE_DEV bool decode_k_block(const Args& args, int b, TileCtx& c) {
   const int pe = args.tilesM * args.tilesN;
   const int t = b >> 3;
   const int q = (b & 7) + 8 * (t / pe);
+  if (args.chunks == nullptr) {
+    if (q >= args.ksplit) return false;
+    const int kc = (((args.K + args.ksplit - 1) / args.ksplit) + BK - 1) / BK * BK;
+    const int r = t % pe;
+    c.e = 0; c.split = 0; c.slot = q - 1;
+    c.k_begin = q * kc; c.k_end = min(args.K, c.k_begin + kc);
+    c.row_begin = c.row_end = 0;
+    c.mt = r / args.tilesN; c.nt = r - c.mt * args.tilesN;
+    c.m0 = c.mt * BM; c.n0 = c.nt * BN;
+    return true;
+  }
   if (q >= __builtin_amdgcn_readfirstlane(*args.nchunks)) return false;
   decode_at<BM, BN, BK, GROUP_K>(args, q * pe + t % pe, c);
   c.e = __builtin_amdgcn_readfirstlane(c.e);

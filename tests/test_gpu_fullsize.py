@@ -44,6 +44,12 @@ def test_router_tiles_sampled():
     check_sampled(configs.SPARSE.scaled("router_tiles", T=32768, d=64, E=256, k=2, f=128))
 
 
+def test_router_dwg_tiles_sampled():
+    """T = 65536, d = 512, E = 256: the router-weight gradient runs on the 256 x 256
+    weight-gradient kernel (64 chunks of 1024 token rows, 4 tiles each)."""
+    check_sampled(configs.SPARSE.scaled("router_dwg_tiles", T=65536, d=512, E=256, k=2, f=128))
+
+
 def check_sampled(cfg):
     from mixture_experts_layer_27_amd import binding
     name = cfg.name
