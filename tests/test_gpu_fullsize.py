@@ -45,9 +45,11 @@ def test_router_tiles_sampled():
 
 
 def test_router_dwg_tiles_sampled():
-    """T = 65536, d = 512, E = 256: the router-weight gradient runs on the 256 x 256
-    weight-gradient kernel (64 chunks of 1024 token rows, 4 tiles each)."""
-    check_sampled(configs.SPARSE.scaled("router_dwg_tiles", T=65536, d=512, E=256, k=2, f=128))
+    """T = 65600, d = 512, E = 256: the router-weight gradient runs on the 256 x 256
+    weight-gradient kernel in 64 chunks of 1088 token rows, 4 tiles each; the last
+    three chunks are empty (their partial slots hold zeros), and the router logits'
+    last 128-row tile is ragged."""
+    check_sampled(configs.SPARSE.scaled("router_dwg_tiles", T=65600, d=512, E=256, k=2, f=128))
 
 
 def check_sampled(cfg):
