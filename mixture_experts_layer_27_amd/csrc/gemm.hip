@@ -93,6 +93,25 @@ hipError_t run_wgrad_big(const Args& a, int64_t logical_tiles, hipStream_t st) {
   return hipGetLastError();
 }
 
+// Persistent row-segment launch (bf16 output): one block per CU, as above.  It
+// pays once a CU has many tiles to walk (sparse_e256: 72 logical tiles per CU,
+// down 1573 -> 1516 us, dX 2296 -> 2264 us); with about 10 per CU (fine_e128)
+// the static walk cannot even out tiles of unequal length and it loses 2-5%.
+bool use_rows_walk(int64_t logical_tiles) { return logical_tiles >= 32 * (int64_t)device_cus(); }
+template <bool AKC, bool BKC, int EPI, int GATHER = 0>
+hipError_t run_rows_big(const Args& a, int64_t logical_tiles, hipStream_t st) {
+  auto kern = grouped_rows_big<AKC, BKC, EPI, GATHER>;
+  constexpr size_t lds = big_rows_lds_bytes();
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  const int64_t need = 8 * ((logical_tiles + 7) / 8);
+  const int64_t cap = 8 * (int64_t)(device_cus() / 8 > 0 ? device_cus() / 8 : 1);
+  const int64_t grid = need < cap ? need : cap;
+  if (grid <= 0) return hipSuccess;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kBigThreads), lds, st, a);
+  return hipGetLastError();
+}
+
 // The 256 x 256 register-staged kernel pays a longer unoverlapped epilogue per
 // tile (one block per CU); it wins when the reduction is deep enough (from
 // K = 512: GEMM2 at d_ff = 512 takes 1618 instead of 1750 us).
@@ -145,8 +164,11 @@ hipError_t gemm_down(const moe_shape& s, const moe_plan& p, const PlanInternal& 
   a.N = s.d; a.K = s.d_ff; a.E = s.E; a.f = s.d_ff;
   if (s.act == MOE_BF16) {
     a.tile_prefix = pi.prefix128; a.tile_expert = pi.tile_e128;
-    if (use_big(a.K))
-      return run_big<true, true, GROUP_M, EPI_ACT>(a, grouped_m_tiles(s, 128) * ceil_div(a.N, 512), st);
+    if (use_big(a.K)) {
+      const int64_t tiles = grouped_m_tiles(s, 128) * ceil_div(a.N, 512);
+      return use_rows_walk(tiles) ? run_rows_big<true, true, EPI_ACT>(a, tiles, st)
+                                  : run_big<true, true, GROUP_M, EPI_ACT>(a, tiles, st);
+    }
     a.tilesN = ceil_div(a.N, 256);
     return run_dma<128, 256, 2, 4, true, true, GROUP_M, EPI_ACT, 3>(a, grouped_m_tiles(s, 128) * a.tilesN, st);
   }
@@ -205,8 +227,11 @@ hipError_t gemm_dx_perm(const moe_shape& s, const moe_plan& p, const PlanInterna
   a.N = s.d; a.K = 2 * s.d_ff; a.E = s.E; a.f = s.d_ff;
   if (s.act == MOE_BF16) {
     a.tile_prefix = pi.prefix128; a.tile_expert = pi.tile_e128;
-    if (use_big(a.K))
-      return run_big<true, false, GROUP_M, EPI_ACT>(a, grouped_m_tiles(s, 128) * ceil_div(a.N, 512), st);
+    if (use_big(a.K)) {
+      const int64_t tiles = grouped_m_tiles(s, 128) * ceil_div(a.N, 512);
+      return use_rows_walk(tiles) ? run_rows_big<true, false, EPI_ACT>(a, tiles, st)
+                                  : run_big<true, false, GROUP_M, EPI_ACT>(a, tiles, st);
+    }
     a.tilesN = ceil_div(a.N, 256);
     return run_dma<128, 256, 2, 4, true, false, GROUP_M, EPI_ACT, 3>(a, grouped_m_tiles(s, 128) * a.tilesN, st);
   }

@@ -371,10 +371,12 @@ MOE_DEV void zero_acc(f32x16 (&acc)[TM][TN]) {
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 }
 
-// One output tile: BM x BN with WM x WN waves of 128 x 64.
-template <int BM, int BN, int WM, int WN, bool AKC, bool BKC, int GROUP, int EPI, int GATHER = 0>
+// One output tile: BM x BN with WM x WN waves of 128 x 64.  PERSIST: inside a
+// persistent kernel's tile walk (lane values through opaque_tid, the epilogue's
+// branch-free stores).
+template <int BM, int BN, int WM, int WN, bool AKC, bool BKC, int GROUP, int EPI, int GATHER = 0, bool PERSIST = false>
 MOE_DEV void big_tile(const Args& args, const TileCtx& ctx, char* smem) {
-  using P = BigPipe<BM, BN, WM, WN, AKC, BKC, GROUP, EPI, GATHER>;
+  using P = BigPipe<BM, BN, WM, WN, AKC, BKC, GROUP, EPI, GATHER, PERSIST>;
   P p;
   p.setup(args, ctx);
   f32x16 acc[P::TM][P::TN];
@@ -390,7 +392,7 @@ MOE_DEV void big_tile(const Args& args, const TileCtx& ctx, char* smem) {
   } else {
     p.template run<P::TM, false, true>(nk, smem, acc);
   }
-  wave_epilogue<BM, BN, WM, WN, GROUP, EPI>(args, ctx, acc, smem);
+  wave_epilogue<BM, BN, WM, WN, GROUP, EPI, PERSIST>(args, ctx, acc, smem);
 }
 
 // Weight gradients (GROUP_K), persistent: a block per CU walks the logical
@@ -453,11 +455,10 @@ MOE_DEV void big_wgrad_tiles(const Args& args, char* smem) {
 // the block has no tile; *wide tells the shape.  Inside an expert, the tall
 // tiles go in groups of kGroupM unit pairs with the n-tile outer and the pair
 // inner, so consecutive tiles (one XCD) share weight columns in L2.
-MOE_DEV bool big_decode_m(const Args& args, TileCtx& c, bool* wide) {
+MOE_DEV bool big_decode_m(const Args& args, int b, TileCtx& c, bool* wide) {
   const int nW = (args.N + 511) / 512;
   const int total = args.tile_prefix[args.E] * nW;
   const int per = (total + 7) >> 3;
-  const int b = blockIdx.x;
   if ((b >> 3) >= per) return false;
   const int L = (b & 7) * per + (b >> 3);
   if (L >= total) return false;
@@ -488,6 +489,88 @@ MOE_DEV bool big_decode_m(const Args& args, TileCtx& c, bool* wide) {
   return true;
 }
 
+// Row-segment GEMMs with a bf16 output (GROUP_M, EPI_ACT: down, dX_perm),
+// persistent: a block per CU takes the logical blocks b, b + gridDim.x, ... of
+// big_decode_m (gridDim.x a multiple of 8: the block keeps to its XCD's range),
+// in two passes.  First its tall tiles, each started inside the previous one's
+// epilogue as the weight gradients do (big_wgrad_tiles); each wave still skips
+// the sub-tiles of its rows that lie past the segment (one main-loop copy per
+// count, chosen per tile).  Then its wide tiles (an expert's odd last unit) as
+// in the one-tile kernel: in one pass the wide tiles' code would hold the tall
+// chain's values live across it and spill.
+template <bool AKC, bool BKC, int EPI, int GATHER>
+MOE_DEV void big_rows_tiles(const Args& args, char* smem) {
+  using P = BigPipe<256, 256, 2, 4, AKC, BKC, GROUP_M, EPI, GATHER, true>;
+  const int nk = (args.K + P::BK - 1) / P::BK;
+  const int G = (int)gridDim.x;
+  // the first tall tile at block index bb or later (bb advanced to it); false past the end
+  auto next_tall = [&](int& bb, TileCtx& c) __attribute__((always_inline)) {
+    for (;; bb += G) {
+      bool w = false;
+      if (!big_decode_m(args, bb, c, &w)) return false;
+      if (!w) return true;
+    }
+  };
+  int b = blockIdx.x;
+  TileCtx ctx;
+  if (next_tall(b, ctx)) {
+    P p;
+    f32x16 acc[P::TM][P::TN];
+    // the main loop with this wave's count of sub-tiles holding rows of the
+    // segment (>= 1 by the tile decode); PEEL: reached from a prefetch, else
+    // the prologue runs first
+    auto main_loop = [&](auto peel_c) __attribute__((always_inline)) {
+      constexpr bool PEEL = decltype(peel_c)::value;
+      const int valid = min(256, ctx.row_end - ctx.row_begin) - p.wm * P::WTM;
+      if (valid > 96) p.template run<4, PEEL, !PEEL>(nk, smem, acc);
+      else if (valid > 64) p.template run<3, PEEL, !PEEL>(nk, smem, acc);
+      else if (valid > 32) p.template run<2, PEEL, !PEEL>(nk, smem, acc);
+      else p.template run<1, PEEL, !PEEL>(nk, smem, acc);
+    };
+    p.setup(args, ctx);
+    zero_acc(acc);
+    main_loop(std::false_type{});
+    for (;;) {
+      int nb = b + G;
+      TileCtx nx;
+      const bool pre = next_tall(nb, nx);
+      if (pre) p.setup(args, nx);
+      // after the last stage's barrier no wave reads this tile's stages any more
+      wave_epilogue<256, 256, 2, 4, GROUP_M, EPI, true>(args, ctx, acc, smem + P::STAGE,
+                                                        [&](auto ic) __attribute__((always_inline)) {
+        constexpr int i = decltype(ic)::value;
+        if constexpr (i == 0) {
+          if (pre) p.load_ab(0);
+        } else if constexpr (i == 1) {
+          if (pre) {
+            p.store(smem);
+            p.load_ab(1);
+          }
+        }
+      });
+      if (!pre) break;
+      __builtin_amdgcn_s_waitcnt(0xc07f);   // stage 0 written, slab rows read back
+      cta_barrier();
+      b = nb;
+      ctx = nx;
+      zero_acc(acc);
+      main_loop(std::true_type{});
+    }
+  }
+  for (int bb = blockIdx.x;; bb += G) {
+    TileCtx c;
+    bool w = false;
+    if (!big_decode_m(args, bb, c, &w)) return;
+    if (!w) continue;
+    __builtin_amdgcn_s_waitcnt(0xc07f);     // the previous tile's LDS reads done
+    cta_barrier();                          // before this tile writes its ring
+    big_tile<128, 512, 1, 8, AKC, BKC, GROUP_M, EPI, GATHER, true>(args, c, smem);
+  }
+}
+
+// LDS of the persistent row-segment kernel: the wide tiles' ring (the whole LDS)
+constexpr size_t big_rows_lds_bytes() { return big_ring_bytes<128, 512>(); }
+
 // LDS of the persistent weight-gradient kernel: stage 0, then the larger of
 // stage 1 and the epilogue's row slabs (eight waves x 32 rows x 72 floats)
 constexpr size_t big_wgrad_lds_bytes() {
@@ -501,6 +584,12 @@ __global__ __launch_bounds__(kBigThreads) void grouped_wgrad_big(Args args) {
   big_wgrad_tiles<AKC, BKC, EPI, GATHER>(args, smem);
 }
 
+template <bool AKC, bool BKC, int EPI, int GATHER>
+__global__ __launch_bounds__(kBigThreads) void grouped_rows_big(Args args) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  big_rows_tiles<AKC, BKC, EPI, GATHER>(args, smem);
+}
+
 template <bool AKC, bool BKC, int GROUP, int EPI, int GATHER = 0>
 __global__ __launch_bounds__(kBigThreads) void grouped_gemm_big(Args args) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -511,7 +600,7 @@ __global__ __launch_bounds__(kBigThreads) void grouped_gemm_big(Args args) {
     big_tile<256, 256, 2, 4, AKC, BKC, GROUP, EPI, GATHER>(args, ctx, smem);
   } else {
     bool wide = false;
-    if (!big_decode_m(args, ctx, &wide)) return;
+    if (!big_decode_m(args, blockIdx.x, ctx, &wide)) return;
     if (wide) big_tile<128, 512, 1, 8, AKC, BKC, GROUP, EPI, GATHER>(args, ctx, smem);
     else big_tile<256, 256, 2, 4, AKC, BKC, GROUP, EPI, GATHER>(args, ctx, smem);
   }

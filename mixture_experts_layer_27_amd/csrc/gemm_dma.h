@@ -478,9 +478,13 @@ MOE_DEV void wave_epilogue(const Args& args, const TileCtx& ctx, f32x16 (&acc)[B
         // writes nothing), so no branch surrounds the stores and the compiler can
         // count them (the next tile's loads, issued before them, are then waited
         // for without waiting for the stores).  Offsets < 32 * ldc * 4 < 2^31.
-        constexpr bool BUF = PERSIST && GROUP == GROUP_K && VW == 4;
+        // The same branch-free stores for a persistent kernel's bf16 rows (EPI_ACT;
+        // those are read by the next kernel and keep the default cache policy).
+        constexpr bool BUF = PERSIST && ((GROUP == GROUP_K && EPI == EPI_F32) || (GROUP == GROUP_M && EPI == EPI_ACT));
+        constexpr int BUF_POLICY = GROUP == GROUP_K ? kCachePolicyNT : 0;
         constexpr uint32_t kNoStore = 0x7ffffff0u;
-        const __amdgpu_buffer_rsrc_t crs = make_rsrc(BUF ? C + (int64_t)(mbase + i * 32) * args.ldc : C, kNoStore);
+        const int brow = (GROUP == GROUP_K ? mbase : rbase) + i * 32;
+        const __amdgpu_buffer_rsrc_t crs = make_rsrc(BUF ? C + (int64_t)brow * args.ldc : C, kNoStore);
         float v[IT][VW];
 #pragma unroll
         for (int it = 0; it < IT; ++it) {
@@ -516,11 +520,16 @@ MOE_DEV void wave_epilogue(const Args& args, const TileCtx& ctx, f32x16 (&acc)[B
           else { grow = mbase + i * 32 + rr; ok = grow < args.M; }
           const int col = cbase + ch * VW;
           if constexpr (BUF) {
-            const uint32_t off = (ok && col < args.N) ? (uint32_t)(rr * args.ldc + col) * 4u : kNoStore;
-            __builtin_amdgcn_raw_buffer_store_b128(
-                u32x4{__float_as_uint(v[it][0]), __float_as_uint(v[it][1]), __float_as_uint(v[it][2]),
-                      __float_as_uint(v[it][3])},
-                crs, (int)off, 0, kCachePolicyNT);
+            u32x4 q;
+            if constexpr (VW == 8) {
+#pragma unroll
+              for (int h = 0; h < 4; ++h) q[h] = pack_bf2(v[it][2 * h], v[it][2 * h + 1]);
+            } else {
+              q = u32x4{__float_as_uint(v[it][0]), __float_as_uint(v[it][1]), __float_as_uint(v[it][2]),
+                        __float_as_uint(v[it][3])};
+            }
+            const uint32_t off = (ok && col < args.N) ? (uint32_t)(rr * args.ldc + col) * (uint32_t)sizeof(OT) : kNoStore;
+            __builtin_amdgcn_raw_buffer_store_b128(q, crs, (int)off, 0, BUF_POLICY);
           } else if (ok && col < args.N) {
             if constexpr (VW == 8) {
               Vec8<OT>::store(C + (int64_t)grow * args.ldc + col, v[it]);

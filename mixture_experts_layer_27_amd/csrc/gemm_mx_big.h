@@ -204,7 +204,7 @@ __global__ __launch_bounds__(kBigThreads) void grouped_gemm_mx_big(Args args, Mx
     mx_big_tile<256, 256, 2, 4, GROUP, EPI>(args, mx, ctx, smem);
   } else {
     bool wide = false;
-    if (!big_decode_m(args, ctx, &wide)) return;
+    if (!big_decode_m(args, blockIdx.x, ctx, &wide)) return;
     if (wide) mx_big_tile<128, 512, 1, 8, GROUP, EPI>(args, mx, ctx, smem);
     else mx_big_tile<256, 256, 2, 4, GROUP, EPI>(args, mx, ctx, smem);
   }
