@@ -84,10 +84,26 @@ def gpu_clocks():
             continue
         if r.returncode == 0 and r.stdout.strip():
             try:
-                return {"tool": " ".join(cmd), "reading": json.loads(r.stdout)}
+                return {"tool": " ".join(cmd), **compact_clocks(json.loads(r.stdout))}
             except ValueError:
-                return {"tool": " ".join(cmd), "reading": r.stdout.strip()[:2000]}
+                return {"tool": " ".join(cmd), "reading": r.stdout.strip()[:500]}
     return None
+
+
+def compact_clocks(reading):
+    """Shader clock per XCD, memory clock and socket power out of an amd-smi
+    metric reading; anything else is kept as (shortened) text."""
+    try:
+        gpu = (reading["gpu_data"] if isinstance(reading, dict) else reading)[0]
+        clk = gpu["clock"]
+        gfx = [clk[k]["clk"]["value"] for k in sorted(clk) if k.startswith("gfx_") and isinstance(clk[k], dict)
+               and isinstance(clk[k].get("clk"), dict)]
+        mem = [clk[k]["clk"]["value"] for k in sorted(clk) if k.startswith("mem_") and isinstance(clk[k], dict)
+               and isinstance(clk[k].get("clk"), dict)]
+        return {"gfx_clk_mhz_per_xcd": gfx, "mem_clk_mhz": mem[0] if mem else None,
+                "socket_power_w": gpu["power"]["socket_power"]["value"]}
+    except (KeyError, IndexError, TypeError):
+        return {"reading": json.dumps(reading)[:500]}
 
 
 def cpu_facts():
