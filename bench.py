@@ -37,6 +37,8 @@ METRIC = "MoE layer tokens/s fwd+bwd at 1 GPU; grouped-GEMM % MFMA peak; permute
 HEADLINE = "sparse_e256"
 SUB_CONFIGS = ("coarse_e8", "fine_e128", "fine_e128_zipf", "sparse_e256_round", "fine_e128_mxfp8", "sparse_e256_mxfp8",
                "fine_e128_router_losses", "fine_e128_zipf_capacity")
+# workloads timed as one optimizer step over 4 micro-batches (bf16, MXFP8, MXFP8 with reused weight codes)
+ACCUM_CONFIGS = ("fine_e128", "sparse_e256")
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 (MXFP8) MFMA
 PEAK_F32_TFLOPS = 157.3
@@ -54,6 +56,7 @@ def parse():
     ap.add_argument("--no-sub", action="store_true", help="skip the other workloads")
     ap.add_argument("--sub-steps", type=int, default=30)
     ap.add_argument("--sub-warmup", type=int, default=5)
+    ap.add_argument("--accum-steps", type=int, default=6, help="optimizer steps timed per gradient-accumulation run")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--fused-gather", choices=("auto", "on", "off"), default="auto",
                     help="on: the forward reads x through the plan inside the expert GEMMs (bf16) or the MXFP8 "
@@ -403,6 +406,66 @@ def data_movement_extras(cfg, run, rows, permute_bytes, stream):
                                 "note": "median of 5 launches, each after a 1 GiB scratch write"}}
 
 
+def measure_accumulation(cfg, micro, steps, warmup):
+    """One optimizer step of gradient accumulation over `micro` micro-batches
+    (different x and dout, same weights), three ways in one process on the same
+    inputs: bf16 expert GEMMs; MXFP8 quantising the weights in every micro-batch
+    (the plain step); MXFP8 with the weight codes written once per optimizer step
+    (moe_quantize_weights_mx) and read by every micro-batch
+    (moe_grouped_gemm_swiglu_wcodes, moe_backward with the forward workspace).
+    Each micro-batch is a whole layer step: route, expert FFN, combine, backward.
+    Summing the weight gradients over the micro-batches is the caller's and costs
+    the same for every variant, so it is not part of the timed work."""
+    import dataclasses
+    import torch
+    from mixture_experts_layer_27_amd import binding, synth
+
+    g = synth.generate(cfg)
+    mbs = [{k: v.cuda() for k, v in synth.micro_batch(cfg, j).items()} for j in range(micro)]
+    stream = torch.cuda.current_stream()
+    res = {}
+    for variant in ("bf16", "mxfp8", "mxfp8_weight_codes_reused"):
+        c = dataclasses.replace(cfg, gemm="bf16" if variant == "bf16" else "mxfp8")
+        log(f"{cfg.name}: gradient accumulation x{micro}, {variant}")
+        run = binding.LayerRun(c, g, fused_gather=True)
+        s = run.s
+
+        def opt_step():
+            if variant == "mxfp8_weight_codes_reused":
+                binding.quantize_weights_mx(s, run.inp["w1"], run.inp["w2"], run.ws_fwd)
+            for mb in mbs:
+                run.inp["x"], run.inp["dout"] = mb["x"], mb["dout"]
+                run.route()
+                if variant == "mxfp8_weight_codes_reused":
+                    binding.grouped_gemm_swiglu_wcodes(s, run.inp["x"], run.plan, run.h, run.y, run.ws_fwd)
+                else:
+                    run.experts()
+                binding.unpermute_combine(s, run.y, run.plan, run.out)
+                run.backward(with_optional=False)
+
+        for _ in range(warmup):
+            opt_step()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for i in range(steps):
+            evs[i][0].record(stream)
+            opt_step()
+            evs[i][1].record(stream)
+        torch.cuda.synchronize()
+        med = statistics.median(e0.elapsed_time(e1) for e0, e1 in evs)
+        res[variant] = {"ms_per_optimizer_step": med, "ms_per_micro_batch": med / micro,
+                        "tokens_per_s": micro * cfg.T / (med * 1e-3)}
+        del run
+        torch.cuda.empty_cache()
+    base = res["bf16"]["ms_per_micro_batch"]
+    for v in res.values():
+        v["speedup_vs_bf16"] = base / v["ms_per_micro_batch"]
+    return {"workload": f"{cfg.name} shapes: T={cfg.T} per micro-batch, d_model={cfg.d} E={cfg.E} top-k={cfg.k} "
+                        f"d_ff={cfg.f} SwiGLU, fwd+bwd, gradient accumulation over {micro} micro-batches",
+            "micro_batches": micro, "optimizer_steps_timed": steps, "variants": res,
+            "timing": "median over the timed optimizer steps of HIP events around each; per micro-batch = / micro"}
+
+
 def activation_memory(cfg, run, binding):
     """Bytes the allocator holds from the end of the forward to the backward, for
     this layer (dS = <dA', A>, A recomputed from H: keeps x, the plan and H; x_perm
@@ -520,6 +583,13 @@ def main():
                 r = {"error": f"{type(exc).__name__}: {exc}"}
             subs[name] = r
         out["sub_results"] = subs
+        accum = {}
+        for name in ACCUM_CONFIGS:
+            try:
+                accum[name] = measure_accumulation(configs.get(name), 4, a.accum_steps, 2)
+            except Exception as exc:
+                accum[name] = {"error": f"{type(exc).__name__}: {exc}"}
+        out["gradient_accumulation"] = accum
     if not a.no_cpu_baseline:
         torch.cuda.empty_cache()
         tokens = a.cpu_tokens or min(cfg.T, 4096 if cfg.d * cfg.f * cfg.k > 2 ** 23 else 16384)

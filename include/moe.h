@@ -280,6 +280,34 @@ moe_status moe_backward_traced(const moe_shape *s, const void *x, const void *w_
                                float *dw2, float *dlogits, float *ds, void *ws, size_t ws_bytes, void *stream,
                                moe_trace *trace);
 
+/* MXFP8 weight codes kept across the micro-batches of one optimizer step
+ * (gradient accumulation: w1 and w2 do not change between them).  The
+ * Olmo-core 3 article's MXFP8 switch ("three splits" section) quantises every
+ * expert-GEMM operand; the codes of a weight depend on that weight alone, so
+ * quantising w1 and w2 once per optimizer step instead of once per micro-batch
+ * gives the same codes and bitwise the same results.
+ *
+ * moe_quantize_weights_mx writes the codes of w1 [E,2f,d] and w2 [E,d,f] (bf16)
+ * along both of their axes into ws, the expert workspace
+ * (moe_workspace_bytes(s, MOE_WS_EXPERTS) bytes), where moe_grouped_gemm_swiglu
+ * keeps them.  Where they sit depends only on E, d and d_ff, so micro-batches
+ * of different T may share one ws sized for the largest.
+ * moe_grouped_gemm_swiglu_wcodes is the expert FFN of moe_grouped_gemm_swiglu
+ * taking those codes from ws instead of quantising w1 and w2 (neither is
+ * passed): x is x_perm [N_max,d] (x_gathered = 0) or x [T,d] read through the
+ * plan (x_gathered = 1, as moe_grouped_gemm_swiglu_gather, with its
+ * requirements).  It rewrites the rest of ws, so moe_backward with fwd_ws = ws
+ * works as after moe_grouped_gemm_swiglu (and reads the transposed weight codes
+ * from there too).  trace: as the *_traced calls, or NULL.  The library cannot
+ * tell stale codes: the caller quantises again whenever w1 or w2 change.
+ * Errors: MOE_ENOTSUP unless gemm == MOE_MXFP8 (nothing launched); otherwise
+ * as moe_grouped_gemm_swiglu and moe_grouped_gemm_swiglu_gather. */
+moe_status moe_quantize_weights_mx(const moe_shape *s, const void *w1, const void *w2, void *ws,
+                                   size_t ws_bytes, void *stream);
+moe_status moe_grouped_gemm_swiglu_wcodes(const moe_shape *s, const void *x, int x_gathered,
+                                          const moe_plan *plan, void *h_saved, void *y, void *ws,
+                                          size_t ws_bytes, void *stream, moe_trace *trace);
+
 /* MXFP8 quantiser (OCP Microscaling v1.0; the pages only name the format):
  * blocks of 32 consecutive values along the reduction axis; shared exponent
  * X = floor(log2(max|v|)) - 8 clamped to [-127,127] (-127 for an all-zero

@@ -25,7 +25,8 @@ STATUS = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_ENOTSUP", 3: "MOE_EWORKSPACE", 4
 EXPORTS = ("moe_max_rows", "moe_plan_bytes", "moe_plan_init", "moe_workspace_bytes", "moe_route",
            "moe_round_tokens", "moe_permute", "moe_grouped_gemm_swiglu", "moe_grouped_gemm_swiglu_gather",
            "moe_grouped_gemm_swiglu_traced", "moe_grouped_gemm_swiglu_gather_traced",
-           "moe_grouped_gemm_swiglu_noalloc", "moe_unpermute_combine", "moe_backward", "moe_backward_traced",
+           "moe_grouped_gemm_swiglu_noalloc", "moe_quantize_weights_mx", "moe_grouped_gemm_swiglu_wcodes",
+           "moe_unpermute_combine", "moe_backward", "moe_backward_traced",
            "moe_quantize_mx", "moe_ref_stream", "moe_status_str")
 TRACE_MAX_KERNELS = 48
 NOALLOC_SCRATCH_BYTES = 64 << 20
@@ -65,6 +66,9 @@ for name, res, args in [
     ("moe_grouped_gemm_swiglu", ctypes.c_int, [_P_SHAPE, _vp, _vp, _vp, _P_PLAN, _vp, _vp, _vp, _sz, _vp]),
     ("moe_grouped_gemm_swiglu_gather", ctypes.c_int, [_P_SHAPE, _vp, _vp, _vp, _P_PLAN, _vp, _vp, _vp, _sz, _vp]),
     ("moe_grouped_gemm_swiglu_noalloc", ctypes.c_int, [_P_SHAPE, _vp, _vp, _vp, _P_PLAN, _vp, _vp, _vp]),
+    ("moe_quantize_weights_mx", ctypes.c_int, [_P_SHAPE, _vp, _vp, _vp, _sz, _vp]),
+    ("moe_grouped_gemm_swiglu_wcodes", ctypes.c_int,
+     [_P_SHAPE, _vp, ctypes.c_int, _P_PLAN, _vp, _vp, _vp, _sz, _vp, _P_TRACE]),
     ("moe_unpermute_combine", ctypes.c_int, [_P_SHAPE, _vp, _P_PLAN, _vp, _vp]),
     ("moe_grouped_gemm_swiglu_traced", ctypes.c_int,
      [_P_SHAPE, _vp, _vp, _vp, _P_PLAN, _vp, _vp, _vp, _sz, _vp, _P_TRACE]),
@@ -256,6 +260,22 @@ def grouped_gemm_swiglu_noalloc(s: MoeShape, x_perm, w1, w2, plan: Plan, h_saved
     _check("moe_grouped_gemm_swiglu_noalloc",
            _lib.moe_grouped_gemm_swiglu_noalloc(ctypes.byref(s), _ptr(x_perm), _ptr(w1), _ptr(w2),
                                                 ctypes.byref(plan.c), _ptr(h_saved), _ptr(y), _stream(stream)))
+
+
+def quantize_weights_mx(s: MoeShape, w1, w2, ws, stream=None):
+    """MXFP8 codes of w1 and w2 (both orientations) into the expert workspace ws,
+    for the micro-batches of one optimizer step (grouped_gemm_swiglu_wcodes)."""
+    _check("moe_quantize_weights_mx", _lib.moe_quantize_weights_mx(ctypes.byref(s), _ptr(w1), _ptr(w2), _ptr(ws),
+                                                                   ws.numel(), _stream(stream)))
+
+
+def grouped_gemm_swiglu_wcodes(s: MoeShape, x, plan: Plan, h_saved, y, ws, gathered=True, stream=None, trace=None):
+    """The MXFP8 expert FFN with the weight codes already in ws (quantize_weights_mx);
+    x [T, d] read through the plan (gathered) or x_perm [N_max, d]."""
+    _check("moe_grouped_gemm_swiglu_wcodes",
+           _lib.moe_grouped_gemm_swiglu_wcodes(ctypes.byref(s), _ptr(x), int(bool(gathered)), ctypes.byref(plan.c),
+                                               _ptr(h_saved), _ptr(y), _ptr(ws), ws.numel(), _stream(stream),
+                                               None if trace is None else ctypes.byref(trace.c)))
 
 
 def unpermute_combine(s: MoeShape, y, plan: Plan, out, stream=None):

@@ -231,6 +231,8 @@ struct FwdWs {
   MxOperand w1t, w2t, x_t;   // MXFP8: the backward's orientation of W1, W2 and x_perm
 };
 
+// MXFP8: the weight codes come first, so where they sit depends only on E, d
+// and d_ff (moe_quantize_weights_mx fills them once for micro-batches of any T).
 size_t carve_fwd(const moe_shape& s, char* base, FwdWs* w) {
   Carver c{base};
   const int64_t N = max_rows(s);
@@ -238,13 +240,13 @@ size_t carve_fwd(const moe_shape& s, char* base, FwdWs* w) {
   if (s.gemm != MOE_MXFP8) q.act = c.take<char>((size_t)N * s.d_ff * esz(s));   // MXFP8: A only as codes
   if (s.gemm == MOE_MXFP8) {
     const int64_t E = s.E, d = s.d, f = s.d_ff, P = tok_cap(s);
-    q.pad_off = c.take<int32_t>((E + 1) * 4);
-    q.x = take_mx(c, P, d, P, q.pad_off);
     q.w1 = take_mx(c, E * 2 * f, d, E * 2 * f);
-    q.a = take_mx(c, P, f, P, q.pad_off);
     q.w2 = take_mx(c, E * d, f, E * d);
     q.w1t = take_mx(c, E * d, 2 * f, E * d);
     q.w2t = take_mx(c, E * f, d, E * f);
+    q.pad_off = c.take<int32_t>((E + 1) * 4);
+    q.x = take_mx(c, P, d, P, q.pad_off);
+    q.a = take_mx(c, P, f, P, q.pad_off);
     q.x_t = take_mx(c, d, P, d);
   }
   if (w) *w = q;
@@ -360,12 +362,16 @@ moe_status moe_permute(const moe_shape* s, const void* src, const moe_plan* plan
 namespace {
 // The expert FFN of the forward.  rows = x_perm (gather == nullptr) or x read
 // through gather = token_of_row (the permutation fused into the operand loads).
+// wcodes (MXFP8): the weight codes are already in ws (moe_quantize_weights_mx),
+// w1 and w2 are not read.
 moe_status experts_forward(const moe_shape* s, const void* rows, const int32_t* gather, const void* w1,
                            const void* w2, const moe_plan* plan, void* h_saved, void* y, void* ws, size_t ws_bytes,
-                           void* stream, moe_trace* trace) {
+                           void* stream, moe_trace* trace, bool wcodes = false) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
-  if (!aligned(rows) || !aligned(w1) || !aligned(w2) || !aligned(h_saved) || !aligned(y)) return MOE_EINVAL;
+  if (wcodes && s->gemm != MOE_MXFP8) return MOE_ENOTSUP;
+  if (!aligned(rows) || !aligned(h_saved) || !aligned(y)) return MOE_EINVAL;
+  if (!wcodes && (!aligned(w1) || !aligned(w2))) return MOE_EINVAL;
   if ((st = check_plan(*s, plan)) != MOE_OK) return st;
   if (!aligned(ws) || ws_bytes < experts_ws(*s)) return MOE_EWORKSPACE;
   if (!trace_ok(trace)) return MOE_EINVAL;
@@ -382,9 +388,11 @@ moe_status experts_forward(const moe_shape* s, const void* rows, const int32_t* 
     const int32_t* off = plan->offsets;
     seq("mx_pad_offsets", [&] { return mx_pad_offsets(off, E, w.pad_off, hs); });
     seq("mx_quantize_x", [&] { return mx_quantize_dual(rows, 1, 0, d, off, w.pad_off, E, P, w.x, w.x_t, hs, gather); });
-    seq("mx_quantize_w1", [&] { return mx_quantize_dual(w1, E, 2 * f, d, nullptr, nullptr, 0, 0, w.w1, w.w1t, hs); });
+    if (!wcodes)
+      seq("mx_quantize_w1", [&] { return mx_quantize_dual(w1, E, 2 * f, d, nullptr, nullptr, 0, 0, w.w1, w.w1t, hs); });
     seq("mx_up_swiglu", [&] { return gemm_mx_up_swiglu(*s, *plan, pi, w.x, w.w1, h_saved, w.a, hs); });
-    seq("mx_quantize_w2", [&] { return mx_quantize_dual(w2, E, d, f, nullptr, nullptr, 0, 0, w.w2, w.w2t, hs); });
+    if (!wcodes)
+      seq("mx_quantize_w2", [&] { return mx_quantize_dual(w2, E, d, f, nullptr, nullptr, 0, 0, w.w2, w.w2t, hs); });
     seq("mx_down", [&] { return gemm_mx_down(*s, *plan, pi, w.a, w.w2, y, hs); });
     return seq.status();
   }
@@ -420,6 +428,35 @@ moe_status moe_grouped_gemm_swiglu_gather(const moe_shape* s, const void* x, con
                                           const moe_plan* plan, void* h_saved, void* y, void* ws, size_t ws_bytes,
                                           void* stream) {
   return moe_grouped_gemm_swiglu_gather_traced(s, x, w1, w2, plan, h_saved, y, ws, ws_bytes, stream, nullptr);
+}
+
+moe_status moe_quantize_weights_mx(const moe_shape* s, const void* w1, const void* w2, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (s->gemm != MOE_MXFP8) return MOE_ENOTSUP;
+  if (!aligned(w1) || !aligned(w2)) return MOE_EINVAL;
+  if (!aligned(ws) || ws_bytes < experts_ws(*s)) return MOE_EWORKSPACE;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  FwdWs w;
+  carve_fwd(*s, reinterpret_cast<char*>(ws), &w);
+  const int E = s->E, d = s->d, f = s->d_ff;
+  hipError_t e = mx_quantize_dual(w1, E, 2 * f, d, nullptr, nullptr, 0, 0, w.w1, w.w1t, hs);
+  if (e == hipSuccess) e = mx_quantize_dual(w2, E, d, f, nullptr, nullptr, 0, 0, w.w2, w.w2t, hs);
+  return hip_status(e);
+}
+
+moe_status moe_grouped_gemm_swiglu_wcodes(const moe_shape* s, const void* x, int x_gathered, const moe_plan* plan,
+                                          void* h_saved, void* y, void* ws, size_t ws_bytes, void* stream,
+                                          moe_trace* trace) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (s->gemm != MOE_MXFP8) return MOE_ENOTSUP;
+  if (x_gathered != 0 && x_gathered != 1) return MOE_EINVAL;
+  if (x_gathered && !gather_ok(*s)) return MOE_ENOTSUP;
+  if ((st = check_plan(*s, plan)) != MOE_OK) return st;
+  return experts_forward(s, x, x_gathered ? plan->token_of_row : nullptr, nullptr, nullptr, plan, h_saved, y, ws,
+                         ws_bytes, stream, trace, true);
 }
 
 }  // extern "C"

@@ -19,6 +19,10 @@ float32.  Experts are drawn one at a time, which fixes the stream order.
 ``redraw_rows`` draws replacement rows of ``x`` from a separate stream
 ``default_rng([seed, 1, attempt])``: callers that need routing decisions to be
 clear of ties use it and decide themselves which rows to replace.
+
+``micro_batch`` draws the ``x`` [T, d] and ``dout`` [T, d] of micro-batch j of a
+gradient-accumulation step (the weights stay those of ``generate``) from the
+stream ``default_rng([seed, 3, j])``, with ``generate``'s distributions.
 """
 from __future__ import annotations
 
@@ -91,3 +95,15 @@ def redraw_rows(cfg: MoEConfig, x: torch.Tensor, rows: Iterable[int], attempt: i
     fresh = rng.standard_normal((rows.size, cfg.d), dtype=np.float32) * np.float32(cfg.x_std)
     y[torch.from_numpy(rows)] = _cast(fresh, cfg.act)
     return y
+
+
+def micro_batch(cfg: MoEConfig, j: int, T: int | None = None, seed: int | None = None) -> Dict[str, torch.Tensor]:
+    """x and dout of micro-batch j (T tokens, default cfg.T).  Returns CPU tensors."""
+    seed = cfg.seed if seed is None else seed
+    T = cfg.T if T is None else T
+    rng = np.random.default_rng([seed, 3, j])
+    f32 = np.float32
+    out = {"x": _cast(rng.standard_normal((T, cfg.d), dtype=f32) * f32(cfg.x_std), cfg.act)}
+    if cfg.backward:
+        out["dout"] = _cast(rng.standard_normal((T, cfg.d), dtype=f32), cfg.act)
+    return out

@@ -120,6 +120,24 @@ def test_noalloc_rejects_problems_past_its_scratch(b):
                                                   fake, None) == 1
 
 
+def test_weight_codes_validation_returns_before_launch(b):
+    """The MXFP8 weight-code calls refuse other GEMM types, a short workspace and a
+    bad x_gathered flag on the host (nothing launched)."""
+    fake = ctypes.c_void_p(1 << 20)
+    bf = b.make_shape(64, 128, 8, 2, 128, b.MOE_BF16)
+    mx = b.make_shape(64, 128, 8, 2, 128, b.MOE_BF16, gemm=b.MOE_MXFP8)
+    plan = b.MoePlan()
+    assert b._lib.moe_plan_init(ctypes.byref(mx), fake, 1 << 30, ctypes.byref(plan)) == 0
+    assert b._lib.moe_quantize_weights_mx(ctypes.byref(bf), fake, fake, fake, 1 << 30, None) == 2
+    assert b._lib.moe_quantize_weights_mx(ctypes.byref(mx), fake, fake, fake, 16, None) == 3
+    assert b._lib.moe_quantize_weights_mx(ctypes.byref(mx), None, fake, fake, 1 << 30, None) == 1
+    wc = b._lib.moe_grouped_gemm_swiglu_wcodes
+    assert wc(ctypes.byref(bf), fake, 1, ctypes.byref(plan), fake, fake, fake, 1 << 30, None, None) == 2
+    assert wc(ctypes.byref(mx), fake, 2, ctypes.byref(plan), fake, fake, fake, 1 << 30, None, None) == 1
+    assert wc(ctypes.byref(mx), fake, 1, ctypes.byref(plan), fake, fake, fake, 16, None, None) == 3
+    assert wc(ctypes.byref(mx), None, 0, ctypes.byref(plan), fake, fake, fake, 1 << 30, None, None) == 1
+
+
 def test_ref_stream_validation(b):
     fake = ctypes.c_void_p(1 << 20)
     assert b._lib.moe_ref_stream(fake, fake, 15, 2, None) == 1                 # not a multiple of 16

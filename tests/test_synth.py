@@ -39,3 +39,15 @@ def test_redraw_rows_only_touches_given_rows():
     diff = (y != g["x"]).any(1).nonzero().flatten().tolist()
     assert diff == [1, 3]
     assert torch.equal(y, synth.redraw_rows(c, g["x"], [1, 3], attempt=0))
+
+
+def test_micro_batches_differ_and_keep_the_distribution():
+    c = configs.FINE.scaled("fm", T=512, d=256, E=16, f=128)
+    a, b = synth.micro_batch(c, 0), synth.micro_batch(c, 1)
+    assert torch.equal(a["x"], synth.micro_batch(c, 0)["x"])
+    assert not torch.equal(a["x"], b["x"]) and not torch.equal(a["dout"], b["dout"])
+    assert not torch.equal(a["x"], synth.generate(c)["x"])
+    assert a["x"].dtype == torch.bfloat16 and a["x"].shape == (c.T, c.d) and a["dout"].shape == (c.T, c.d)
+    assert synth.micro_batch(c, 2, T=100)["x"].shape == (100, c.d)
+    x = a["x"].double()
+    assert abs(x.mean()) < 0.02 and abs(x.std() - c.x_std) < 0.02
