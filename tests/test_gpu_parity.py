@@ -252,8 +252,9 @@ def test_router_loss_gradients(name):
 
 
 @pytest.mark.parametrize("name", ["fine_small", "big_tiles_small", "sparse_round_small", "fine_zipf_small",
-                                  "max_E_k", "one_token", "fine_mx_small", "mx_ragged_d", "var_capacity_all",
-                                  "var_all_lb_z_noise"])
+                                  "max_E_k", "one_token", "fine_mx_small", "mx_ragged_d", "sparse_mx_small",
+                                  "sparse_round_mx_small", "mx_zipf_small", "mx_one_token", "var_mx_all_lb",
+                                  "var_capacity_all", "var_all_lb_z_noise"])
 def test_fused_gather_bitwise(name):
     """moe_grouped_gemm_swiglu_gather (rows of x fetched through the plan inside the
     GEMM or quantiser loads) and a backward that gathers x and dout the same way
