@@ -78,7 +78,11 @@ def log(msg):
 
 
 def gpu_clocks():
-    """Shader/memory clocks and power from the SMI tools (whatever answers)."""
+    """Shader/memory clocks and power from the SMI tools (whatever answers); not
+    under a profiler, whose preloaded library would make the tools' interpreter
+    start-up an exec after GPU initialisation."""
+    if "rocprof" in os.environ.get("LD_PRELOAD", "") or any(k.startswith("ROCPROF") for k in os.environ):
+        return None
     for cmd in (["amd-smi", "metric", "-g", "0", "-c", "-p", "--json"], ["amd-smi", "metric", "-c", "-p", "--json"],
                 ["rocm-smi", "--showclocks", "--showpower", "--json"]):
         try:

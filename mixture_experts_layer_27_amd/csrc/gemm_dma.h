@@ -490,8 +490,22 @@ MOE_DEV void wave_epilogue(const Args& args, const TileCtx& ctx, f32x16 (&acc)[B
         for (int it = 0; it < IT; ++it) {
           const int u = lane + 64 * it;
           const float* src = slab + (u / CU) * SS + (u % CU) * VW;
+          if constexpr (VW == 8) {
+            // lanes of odd rows read their second 16 bytes first: with the slab's
+            // row stride (8 banks past a multiple of 64) the 16 lanes of each
+            // read then cover all 64 banks once instead of half of them twice
+            const int h = ((u / CU) & 1) * 4;
+            const f32x4 a = *reinterpret_cast<const f32x4*>(src + h);
+            const f32x4 b = *reinterpret_cast<const f32x4*>(src + (4 - h));
 #pragma unroll
-          for (int c = 0; c < VW; ++c) v[it][c] = src[c];
+            for (int c = 0; c < 4; ++c) {
+              v[it][c] = h ? b[c] : a[c];
+              v[it][4 + c] = h ? a[c] : b[c];
+            }
+          } else {
+#pragma unroll
+            for (int c = 0; c < VW; ++c) v[it][c] = src[c];
+          }
         }
         if constexpr (EPI == EPI_LOGITS) {
           // router logits: (z + bias) + noise, in that order; the launcher keeps
