@@ -470,6 +470,52 @@ def measure_accumulation(cfg, micro, steps, warmup):
             "timing": "median over the timed optimizer steps of HIP events around each; per micro-batch = / micro"}
 
 
+def measure_combine_in_gemm2(cfg, steps, warmup):
+    """The forward's expert FFN + combine two ways in one process on the same
+    routed batch: the separate calls (GEMM2 stores Y, the combine gathers each
+    token's rows and applies the gates) and moe_grouped_gemm_swiglu_combine (GEMM2's
+    epilogue applies the gate and stores each row at its token-order position, a
+    segmented sum adds each token's contiguous rows)."""
+    import torch
+    from mixture_experts_layer_27_amd import binding, synth
+
+    run = binding.LayerRun(cfg, synth.generate(cfg), fused_gather=True)
+    s = run.s
+    run.route()
+    ws = binding._aligned_ws(binding.workspace_bytes(s, binding.MOE_WS_EXPERTS_COMBINE))
+    h2, out2 = torch.empty_like(run.h), torch.empty_like(run.out)
+    ms = {"separate": [], "combine_in_gemm2": []}
+    kern = {}
+    for i in range(warmup + steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        tr = binding.Trace(8)
+        ev[0].record()
+        binding.grouped_gemm_swiglu_gather(s, run.inp["x"], run.inp["w1"], run.inp["w2"], run.plan, run.h, run.y,
+                                           run.ws_fwd)
+        binding.unpermute_combine(s, run.y, run.plan, run.out)
+        ev[1].record()
+        ev[2].record()
+        binding.grouped_gemm_swiglu_combine(s, run.inp["x"], run.inp["w1"], run.inp["w2"], run.plan, h2, out2, ws,
+                                            trace=tr)
+        ev[3].record()
+        torch.cuda.synchronize()
+        if i >= warmup:
+            ms["separate"].append(ev[0].elapsed_time(ev[1]))
+            ms["combine_in_gemm2"].append(ev[2].elapsed_time(ev[3]))
+            for name, t in tr.durations_ms():
+                kern.setdefault(name, []).append(t * 1e3)
+    diff = (out2.float() - run.out.float()).abs()
+    res = {"workload": f"{cfg.name}: T={cfg.T} d_model={cfg.d} E={cfg.E} top-k={cfg.k} d_ff={cfg.f}, forward expert "
+                       f"FFN + combine",
+           "ms_separate": statistics.median(ms["separate"]),
+           "ms_combine_in_gemm2": statistics.median(ms["combine_in_gemm2"]),
+           "kernels_us_combine_in_gemm2": {k: statistics.median(v) for k, v in kern.items()},
+           "out_max_abs_diff": diff.max().item(), "out_mean_abs_diff": diff.mean().item()}
+    del run, ws, h2, out2
+    torch.cuda.empty_cache()
+    return res
+
+
 def activation_memory(cfg, run, binding):
     """Bytes the allocator holds from the end of the forward to the backward, for
     this layer (dS = <dA', A>, A recomputed from H: keeps x, the plan and H; x_perm
@@ -594,6 +640,13 @@ def main():
             except Exception as exc:
                 accum[name] = {"error": f"{type(exc).__name__}: {exc}"}
         out["gradient_accumulation"] = accum
+        comb = {}
+        for name in ACCUM_CONFIGS:
+            try:
+                comb[name] = measure_combine_in_gemm2(configs.get(name), 20, 3)
+            except Exception as exc:
+                comb[name] = {"error": f"{type(exc).__name__}: {exc}"}
+        out["combine_in_gemm2"] = comb
     if not a.no_cpu_baseline:
         torch.cuda.empty_cache()
         tokens = a.cpu_tokens or min(cfg.T, 4096 if cfg.d * cfg.f * cfg.k > 2 ** 23 else 16384)

@@ -139,7 +139,7 @@ size_t     moe_plan_bytes(const moe_shape *s);
 moe_status moe_plan_init(const moe_shape *s, void *blob, size_t blob_bytes, moe_plan *plan);
 
 /* Workspace queries, one per entry point that takes a workspace. */
-enum { MOE_WS_ROUTE = 0, MOE_WS_ROUND = 1, MOE_WS_EXPERTS = 2, MOE_WS_BACKWARD = 3 };
+enum { MOE_WS_ROUTE = 0, MOE_WS_ROUND = 1, MOE_WS_EXPERTS = 2, MOE_WS_BACKWARD = 3, MOE_WS_EXPERTS_COMBINE = 4 };
 size_t     moe_workspace_bytes(const moe_shape *s, int which);
 
 /* Router GEMM, top-k softmax and the plan (histogram, prefix scan, stable
@@ -279,6 +279,30 @@ moe_status moe_backward_traced(const moe_shape *s, const void *x, const void *w_
                                const void *fwd_ws, const void *dout, void *dx, float *dw_gate, float *dw1,
                                float *dw2, float *dlogits, float *ds, void *ws, size_t ws_bytes, void *stream,
                                moe_trace *trace);
+
+/* The expert FFN and the weighted combine in one call, with the combine's gate
+ * and scatter in GEMM2's epilogue (Olmo-core 3 article, "three splits" section:
+ * the expert output goes straight to where its token is reduced).  GEMM1 +
+ * SwiGLU as moe_grouped_gemm_swiglu (h_saved as there; x is x_perm [N_max,d]
+ * when x_gathered = 0, x [T,d] read through the plan when x_gathered = 1, with
+ * moe_grouped_gemm_swiglu_gather's requirements); GEMM2's epilogue multiplies
+ * row r of A W2_e^T by gate_of_row[r] in fp32, rounds it to bf16 and stores it
+ * at the row's token-order position (the order of plan.tok_rows), so that each
+ * token's rows are contiguous; out[t] [T,d] is then their sum in fp32,
+ * ascending, rounded to bf16.  Y itself is never stored.  Deterministic (no
+ * atomics): the per-token sum is a separate pass over the gated rows, because
+ * a token's k rows are produced by tiles of k different experts.  Differs from
+ * moe_grouped_gemm_swiglu + moe_unpermute_combine only in where the gate meets
+ * the bf16 rounding (there the rounded Y is gated inside the fp32 sum).
+ * act = gemm = MOE_BF16 only, else MOE_ENOTSUP.
+ * ws: moe_workspace_bytes(s, MOE_WS_EXPERTS_COMBINE) bytes (the expert
+ * workspace plus N_max rows of gated output and N_max positions).
+ * trace: as the *_traced calls ("up_swiglu", "row_positions",
+ * "down_gate_scatter", "segment_sum"), or NULL. */
+moe_status moe_grouped_gemm_swiglu_combine(const moe_shape *s, const void *x, int x_gathered,
+                                           const void *w1, const void *w2, const moe_plan *plan,
+                                           void *h_saved, void *out, void *ws, size_t ws_bytes,
+                                           void *stream, moe_trace *trace);
 
 /* MXFP8 weight codes kept across the micro-batches of one optimizer step
  * (gradient accumulation: w1 and w2 do not change between them).  The

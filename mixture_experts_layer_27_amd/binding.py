@@ -20,12 +20,13 @@ if not os.path.exists(_LIB_PATH):
 _lib = ctypes.CDLL(_LIB_PATH)
 
 MOE_F32, MOE_BF16, MOE_MXFP8 = 0, 1, 2
-MOE_WS_ROUTE, MOE_WS_ROUND, MOE_WS_EXPERTS, MOE_WS_BACKWARD = 0, 1, 2, 3
+MOE_WS_ROUTE, MOE_WS_ROUND, MOE_WS_EXPERTS, MOE_WS_BACKWARD, MOE_WS_EXPERTS_COMBINE = 0, 1, 2, 3, 4
 STATUS = {0: "MOE_OK", 1: "MOE_EINVAL", 2: "MOE_ENOTSUP", 3: "MOE_EWORKSPACE", 4: "MOE_EHIP"}
 EXPORTS = ("moe_max_rows", "moe_plan_bytes", "moe_plan_init", "moe_workspace_bytes", "moe_route",
            "moe_round_tokens", "moe_permute", "moe_grouped_gemm_swiglu", "moe_grouped_gemm_swiglu_gather",
            "moe_grouped_gemm_swiglu_traced", "moe_grouped_gemm_swiglu_gather_traced",
-           "moe_grouped_gemm_swiglu_noalloc", "moe_quantize_weights_mx", "moe_grouped_gemm_swiglu_wcodes",
+           "moe_grouped_gemm_swiglu_noalloc", "moe_grouped_gemm_swiglu_combine", "moe_quantize_weights_mx",
+           "moe_grouped_gemm_swiglu_wcodes",
            "moe_unpermute_combine", "moe_backward", "moe_backward_traced",
            "moe_quantize_mx", "moe_ref_stream", "moe_status_str")
 TRACE_MAX_KERNELS = 48
@@ -66,6 +67,8 @@ for name, res, args in [
     ("moe_grouped_gemm_swiglu", ctypes.c_int, [_P_SHAPE, _vp, _vp, _vp, _P_PLAN, _vp, _vp, _vp, _sz, _vp]),
     ("moe_grouped_gemm_swiglu_gather", ctypes.c_int, [_P_SHAPE, _vp, _vp, _vp, _P_PLAN, _vp, _vp, _vp, _sz, _vp]),
     ("moe_grouped_gemm_swiglu_noalloc", ctypes.c_int, [_P_SHAPE, _vp, _vp, _vp, _P_PLAN, _vp, _vp, _vp]),
+    ("moe_grouped_gemm_swiglu_combine", ctypes.c_int,
+     [_P_SHAPE, _vp, ctypes.c_int, _vp, _vp, _P_PLAN, _vp, _vp, _vp, _sz, _vp, _P_TRACE]),
     ("moe_quantize_weights_mx", ctypes.c_int, [_P_SHAPE, _vp, _vp, _vp, _sz, _vp]),
     ("moe_grouped_gemm_swiglu_wcodes", ctypes.c_int,
      [_P_SHAPE, _vp, ctypes.c_int, _P_PLAN, _vp, _vp, _vp, _sz, _vp, _P_TRACE]),
@@ -260,6 +263,16 @@ def grouped_gemm_swiglu_noalloc(s: MoeShape, x_perm, w1, w2, plan: Plan, h_saved
     _check("moe_grouped_gemm_swiglu_noalloc",
            _lib.moe_grouped_gemm_swiglu_noalloc(ctypes.byref(s), _ptr(x_perm), _ptr(w1), _ptr(w2),
                                                 ctypes.byref(plan.c), _ptr(h_saved), _ptr(y), _stream(stream)))
+
+
+def grouped_gemm_swiglu_combine(s: MoeShape, x, w1, w2, plan: Plan, h_saved, out, ws, gathered=True, stream=None,
+                                trace=None):
+    """Expert FFN + combine with the gate and the scatter to token order in GEMM2's epilogue
+    (out [T, d]; ws of workspace_bytes(s, MOE_WS_EXPERTS_COMBINE) bytes)."""
+    _check("moe_grouped_gemm_swiglu_combine",
+           _lib.moe_grouped_gemm_swiglu_combine(ctypes.byref(s), _ptr(x), int(bool(gathered)), _ptr(w1), _ptr(w2),
+                                                ctypes.byref(plan.c), _ptr(h_saved), _ptr(out), _ptr(ws), ws.numel(),
+                                                _stream(stream), None if trace is None else ctypes.byref(trace.c)))
 
 
 def quantize_weights_mx(s: MoeShape, w1, w2, ws, stream=None):

@@ -255,6 +255,25 @@ size_t carve_fwd(const moe_shape& s, char* base, FwdWs* w) {
 
 size_t experts_ws(const moe_shape& s) { return carve_fwd(s, nullptr, nullptr); }
 
+// The expert FFN with the combine in GEMM2's epilogue: the expert workspace,
+// then the gated rows in token order [N_max, d] and each row's position [N_max].
+struct CombineWs {
+  FwdWs f;
+  void* yg;
+  int32_t* pos;
+};
+size_t carve_combine(const moe_shape& s, char* base, CombineWs* w) {
+  const size_t fb = al(experts_ws(s));
+  Carver c{base ? base + fb : nullptr};
+  CombineWs q{};
+  if (base) carve_fwd(s, base, &q.f);
+  q.yg = c.take<char>((size_t)max_rows(s) * s.d * esz(s));
+  q.pos = c.take<int32_t>((size_t)max_rows(s) * 4);
+  if (w) *w = q;
+  return fb + c.off;
+}
+size_t combine_ws(const moe_shape& s) { return carve_combine(s, nullptr, nullptr); }
+
 }  // namespace
 
 PlanInternal plan_internal(const moe_shape& s, const moe_plan& p) {
@@ -309,6 +328,7 @@ size_t moe_workspace_bytes(const moe_shape* s, int which) {
     case MOE_WS_ROUTE: return 0;
     case MOE_WS_ROUND: return 0;
     case MOE_WS_EXPERTS: return experts_ws(*s);
+    case MOE_WS_EXPERTS_COMBINE: return combine_ws(*s);
     case MOE_WS_BACKWARD: return carve_bwd(*s, nullptr, nullptr);
     default: return 0;
   }
@@ -428,6 +448,31 @@ moe_status moe_grouped_gemm_swiglu_gather(const moe_shape* s, const void* x, con
                                           const moe_plan* plan, void* h_saved, void* y, void* ws, size_t ws_bytes,
                                           void* stream) {
   return moe_grouped_gemm_swiglu_gather_traced(s, x, w1, w2, plan, h_saved, y, ws, ws_bytes, stream, nullptr);
+}
+
+moe_status moe_grouped_gemm_swiglu_combine(const moe_shape* s, const void* x, int x_gathered, const void* w1,
+                                           const void* w2, const moe_plan* plan, void* h_saved, void* out, void* ws,
+                                           size_t ws_bytes, void* stream, moe_trace* trace) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (s->act != MOE_BF16 || s->gemm != MOE_BF16) return MOE_ENOTSUP;
+  if (x_gathered != 0 && x_gathered != 1) return MOE_EINVAL;
+  if (x_gathered && !gather_ok(*s)) return MOE_ENOTSUP;
+  if (!aligned(x) || !aligned(w1) || !aligned(w2) || !aligned(h_saved) || !aligned(out)) return MOE_EINVAL;
+  if ((st = check_plan(*s, plan)) != MOE_OK) return st;
+  if (!aligned(ws) || ws_bytes < combine_ws(*s)) return MOE_EWORKSPACE;
+  if (!trace_ok(trace)) return MOE_EINVAL;
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  PlanInternal pi = plan_internal(*s, *plan);
+  CombineWs w;
+  carve_combine(*s, reinterpret_cast<char*>(ws), &w);
+  const int32_t* gather = x_gathered ? plan->token_of_row : nullptr;
+  Seq seq(hs, trace);
+  seq("up_swiglu", [&] { return gemm_up_swiglu(*s, *plan, pi, x, gather, w1, h_saved, w.f.act, hs); });
+  seq("row_positions", [&] { return launch_row_positions(*s, *plan, w.pos, hs); });
+  seq("down_gate_scatter", [&] { return gemm_down_gate_scatter(*s, *plan, pi, w.f.act, w2, w.pos, w.yg, hs); });
+  seq("segment_sum", [&] { return launch_segment_sum(*s, w.yg, *plan, out, hs); });
+  return seq.status();
 }
 
 moe_status moe_quantize_weights_mx(const moe_shape* s, const void* w1, const void* w2, void* ws, size_t ws_bytes,

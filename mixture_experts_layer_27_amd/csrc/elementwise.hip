@@ -43,8 +43,10 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(const char* __restric
 // One wave per token: each lane owns CL 16-byte column chunks per pass and
 // issues the loads of up to RU rows before adding them (in ascending row order),
 // so RU * CL row vectors are in flight per lane.  The rows are read once:
-// non-temporal loads.
-template <typename T, int RU>
+// non-temporal loads.  SEG: y holds the gated rows in token order already (row
+// q of y = the q-th entry of tok_rows, gate applied), so t sums rows
+// tok_ptr[t] .. tok_ptr[t+1]-1 as they are.
+template <typename T, int RU, bool SEG = false>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, const int32_t* __restrict__ tok_ptr,
                                                      const int32_t* __restrict__ tok_rows,
                                                      const float* __restrict__ gate, int T_, int d,
@@ -68,8 +70,13 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, c
       u32x4 v[RU][CL];
 #pragma unroll
       for (int u = 0; u < RU; ++u) {
-        r[u] = p + u < p1 ? tok_rows[p + u] : -1;
-        g[u] = r[u] >= 0 ? gate[r[u]] : 0.0f;
+        if constexpr (SEG) {
+          r[u] = p + u < p1 ? p + u : -1;
+          g[u] = 1.0f;
+        } else {
+          r[u] = p + u < p1 ? tok_rows[p + u] : -1;
+          g[u] = r[u] >= 0 ? gate[r[u]] : 0.0f;
+        }
       }
 #pragma unroll
       for (int u = 0; u < RU; ++u)
@@ -111,6 +118,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ y, c
       stg16(out + (int64_t)t * d + c * EV, o);
     }
   }
+}
+
+// pos[tok_rows[q]] = q for the q < tok_ptr[T] rows in use: where each row of the
+// expert-ordered layout sits in token order (a permutation of [0, N)).
+__global__ __launch_bounds__(256) void row_positions_kernel(const int32_t* __restrict__ tok_rows,
+                                                           const int32_t* __restrict__ tok_ptr, int T_, int64_t n_max,
+                                                           int32_t* __restrict__ pos) {
+  const int64_t n = tok_ptr[T_];
+  for (int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; q < n && q < n_max;
+       q += (int64_t)gridDim.x * blockDim.x)
+    pos[tok_rows[q]] = (int32_t)q;
 }
 
 // Input gradient: dx[t] = sum over the rows r of t (ascending) of dx_perm[r]
@@ -511,6 +529,20 @@ hipError_t launch_combine(const moe_shape& s, const void* y, const moe_plan& p, 
   else
     hipLaunchKernelGGL((combine_kernel<float, 1>), dim3(ceil_div(s.T, 4)), dim3(256), 0, st, (const float*)y,
                        p.tok_ptr, p.tok_rows, p.gate_of_row, s.T, s.d, (float*)out);
+  return hipGetLastError();
+}
+
+hipError_t launch_segment_sum(const moe_shape& s, const void* yg, const moe_plan& p, void* out, hipStream_t st) {
+  if (s.act != MOE_BF16) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((combine_kernel<bf16_t, 1, true>), dim3(ceil_div(s.T, 4)), dim3(256), 0, st,
+                     (const bf16_t*)yg, p.tok_ptr, p.tok_rows, p.gate_of_row, s.T, s.d, (bf16_t*)out);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_positions(const moe_shape& s, const moe_plan& p, int32_t* pos, hipStream_t st) {
+  const int64_t n = max_rows(s);
+  hipLaunchKernelGGL(row_positions_kernel, dim3(grid_for(n, 256)), dim3(256), 0, st, p.tok_rows, p.tok_ptr, s.T, n,
+                     pos);
   return hipGetLastError();
 }
 

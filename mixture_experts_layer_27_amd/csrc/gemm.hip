@@ -176,6 +176,28 @@ hipError_t gemm_down(const moe_shape& s, const moe_plan& p, const PlanInternal& 
   return run<float, 128, 128, 2, 2, true, true, GROUP_M, EPI_ACT>(a, grouped_m_tiles(s, 128) * a.tilesN, st);
 }
 
+// GEMM2 with the combine's first half in its epilogue (bf16): row r of A W2^T is
+// scaled by its gate and stored at row pos[r] of yg (the token-ordered rows of
+// the plan's tok_rows), so the rows a token sums are contiguous.
+hipError_t gemm_down_gate_scatter(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const void* act,
+                                  const void* w2, const int32_t* pos, void* yg, hipStream_t st) {
+  Args a = base_args();
+  a.A = act; a.lda = s.d_ff;
+  a.B = w2; a.ldb = s.d_ff; a.b_estride = (int64_t)s.d * s.d_ff;
+  a.C = yg; a.ldc = s.d; a.c_rows = pos;
+  a.row_gate = p.gate_of_row;
+  a.offsets = p.offsets;
+  a.N = s.d; a.K = s.d_ff; a.E = s.E; a.f = s.d_ff;
+  a.tile_prefix = pi.prefix128; a.tile_expert = pi.tile_e128;
+  if (use_big(a.K)) {
+    const int64_t tiles = grouped_m_tiles(s, 128) * ceil_div(a.N, 512);
+    return use_rows_walk(tiles) ? run_rows_big<true, true, EPI_GATE_SCATTER>(a, tiles, st)
+                                : run_big<true, true, GROUP_M, EPI_GATE_SCATTER>(a, tiles, st);
+  }
+  a.tilesN = ceil_div(a.N, 256);
+  return run_dma<128, 256, 2, 4, true, true, GROUP_M, EPI_GATE_SCATTER, 3>(a, grouped_m_tiles(s, 128) * a.tilesN, st);
+}
+
 // ---------------------------------------------------------------- backward
 
 // dS partial sums per row: one per (column tile, wave column) on the bf16 path,

@@ -463,7 +463,7 @@ MOE_DEV void wave_epilogue(const Args& args, const TileCtx& ctx, f32x16 (&acc)[B
         // consecutive columns, so each store instruction writes whole 128-byte
         // lines (fp32 rows written as two interleaved halves cost ~10% of the
         // weight-gradient time).
-        using OT = typename std::conditional<EPI == EPI_ACT, T, float>::type;
+        using OT = typename std::conditional<EPI == EPI_ACT || EPI == EPI_GATE_SCATTER, T, float>::type;
         constexpr int VW = 16 / (int)sizeof(OT);   // values per 16-byte store
         constexpr int CU = WTN / VW;               // 16-byte units per wave row
         constexpr int IT = 32 * CU / 64;
@@ -545,7 +545,14 @@ MOE_DEV void wave_epilogue(const Args& args, const TileCtx& ctx, f32x16 (&acc)[B
             const uint32_t off = (ok && col < args.N) ? (uint32_t)(rr * args.ldc + col) * (uint32_t)sizeof(OT) : kNoStore;
             __builtin_amdgcn_raw_buffer_store_b128(q, crs, (int)off, 0, BUF_POLICY);
           } else if (ok && col < args.N) {
-            if constexpr (VW == 8) {
+            if constexpr (EPI == EPI_GATE_SCATTER) {
+              // the combine's gate, applied before the row is rounded to the act
+              // dtype; the row goes to its token-order position
+              const float g = args.row_gate[grow];
+#pragma unroll
+              for (int c = 0; c < VW; ++c) v[it][c] *= g;
+              Vec8<OT>::store(C + (int64_t)args.c_rows[grow] * args.ldc + col, v[it]);
+            } else if constexpr (VW == 8) {
               Vec8<OT>::store(C + (int64_t)grow * args.ldc + col, v[it]);
             } else {
               const u32x4 q{__float_as_uint(v[it][0]), __float_as_uint(v[it][1]), __float_as_uint(v[it][2]),

@@ -30,13 +30,15 @@ namespace moe_gemm {
 
 enum { GROUP_M = 0, GROUP_K = 1, GROUP_NONE = 2 };
 enum { EPI_ACT = 0, EPI_F32 = 1, EPI_SWIGLU = 2, EPI_DSWIGLU = 3, EPI_LOGITS = 4,
-       EPI_SWIGLU_MX = 6, EPI_DSWIGLU_MX = 7 };   // *_MX: also emit an MXFP8 copy of A / dH
+       EPI_SWIGLU_MX = 6, EPI_DSWIGLU_MX = 7,   // *_MX: also emit an MXFP8 copy of A / dH
+       EPI_GATE_SCATTER = 8 };   // act dtype: row r scaled by row_gate[r], stored at row c_rows[r]
 
 struct Args {
   const void* A; int64_t lda; int64_t a_estride; const int32_t* a_gather;
   const void* B; int64_t ldb; int64_t b_estride; const int32_t* b_gather;   // b_gather: GROUP_K k rows of B
   int64_t gather_rows;          // rows of the tensor a_gather indexes (bounds of gathered loads)
   void* C; int64_t ldc; int64_t c_estride;
+  const int32_t* c_rows;        // EPI_GATE_SCATTER: output row of each GEMM row
   void* C2; int64_t ldc2;
   float* C3; int64_t ldc3;
   const void* aux; int64_t ld_aux;

@@ -74,6 +74,10 @@ struct WgradChunks {
 hipError_t launch_permute_rows(const moe_shape& s, const void* src, const moe_plan& p, void* dst, hipStream_t st);
 hipError_t launch_combine(const moe_shape& s, const void* y, const moe_plan& p, void* out,
                           hipStream_t st);
+// pos[tok_rows[q]] = q for the plan's rows (the token-order position of each row)
+hipError_t launch_row_positions(const moe_shape& s, const moe_plan& p, int32_t* pos, hipStream_t st);
+// out[t] = sum of rows tok_ptr[t] .. tok_ptr[t+1]-1 of yg, ascending, in fp32 (bf16 act)
+hipError_t launch_segment_sum(const moe_shape& s, const void* yg, const moe_plan& p, void* out, hipStream_t st);
 // dxr: the dense router term dz W_g (fp32 [T,d]) or nullptr (then gathered from W_g)
 hipError_t launch_router_dx(const moe_shape& s, const moe_plan& p, const void* dx_perm, const float* dz,
                             const void* wg, const float* dxr, void* dx, hipStream_t st);
@@ -102,6 +106,9 @@ hipError_t gemm_up_swiglu(const moe_shape& s, const moe_plan& p, const PlanInter
                           const int32_t* gather, const void* w1, void* h, void* a, hipStream_t st);
 hipError_t gemm_down(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const void* a,
                      const void* w2, void* y, hipStream_t st);
+// GEMM2 whose epilogue applies each row's gate and stores it at row pos[r] (bf16 only)
+hipError_t gemm_down_gate_scatter(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const void* act,
+                                  const void* w2, const int32_t* pos, void* yg, hipStream_t st);
 hipError_t gemm_dact(const moe_shape& s, const moe_plan& p, const PlanInternal& pi, const void* do_rows,
                      const int32_t* gather, const void* w2, const void* h, void* dh, void* ga, float* ds_part,
                      hipStream_t st);

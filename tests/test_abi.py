@@ -138,6 +138,26 @@ def test_weight_codes_validation_returns_before_launch(b):
     assert wc(ctypes.byref(mx), None, 0, ctypes.byref(plan), fake, fake, fake, 1 << 30, None, None) == 1
 
 
+def test_combine_entry_validation_returns_before_launch(b):
+    """The combine-in-GEMM2 call refuses fp32 and MXFP8 GEMMs, a bad x_gathered
+    flag and a short workspace on the host (nothing launched)."""
+    fake = ctypes.c_void_p(1 << 20)
+    bf = b.make_shape(64, 128, 8, 2, 128, b.MOE_BF16)
+    f32 = b.make_shape(64, 128, 8, 2, 128, b.MOE_F32)
+    mx = b.make_shape(64, 128, 8, 2, 128, b.MOE_BF16, gemm=b.MOE_MXFP8)
+    assert b.workspace_bytes(bf, b.MOE_WS_EXPERTS_COMBINE) >= (b.workspace_bytes(bf, b.MOE_WS_EXPERTS)
+                                                              + b.max_rows(bf) * (128 * 2 + 4))
+    plan = b.MoePlan()
+    assert b._lib.moe_plan_init(ctypes.byref(bf), fake, 1 << 30, ctypes.byref(plan)) == 0
+    cb = b._lib.moe_grouped_gemm_swiglu_combine
+    args = lambda flag, n: (fake, flag, fake, fake, ctypes.byref(plan), fake, fake, fake, n, None, None)
+    assert cb(ctypes.byref(f32), *args(1, 1 << 30)) == 2
+    assert cb(ctypes.byref(mx), *args(1, 1 << 30)) == 2
+    assert cb(ctypes.byref(bf), *args(3, 1 << 30)) == 1
+    assert cb(ctypes.byref(bf), *args(1, 16)) == 3
+    assert cb(ctypes.byref(bf), None, 1, fake, fake, ctypes.byref(plan), fake, fake, fake, 1 << 30, None, None) == 1
+
+
 def test_ref_stream_validation(b):
     fake = ctypes.c_void_p(1 << 20)
     assert b._lib.moe_ref_stream(fake, fake, 15, 2, None) == 1                 # not a multiple of 16

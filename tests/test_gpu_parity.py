@@ -318,6 +318,33 @@ def test_mx_weight_codes_reused_bitwise(name):
             assert torch.equal(a, b), f"micro-batch {j}: {key}"
 
 
+@pytest.mark.parametrize("name", ["fine_small", "sparse_small", "sparse_round_small", "fine_zipf_small",
+                                  "big_tiles_small", "max_E_k", "one_token", "var_capacity_all",
+                                  "var_all_lb_z_noise"])
+def test_combine_in_gemm2(name):
+    """moe_grouped_gemm_swiglu_combine (gate and scatter to token order in GEMM2's
+    epilogue, then a per-token sum of contiguous rows): out within the bar of the
+    oracle's O, H bitwise that of the separate calls, two calls bitwise equal."""
+    from mixture_experts_layer_27_amd import binding
+    cfg, run, ref = run_case(name)
+    print(f"[parity] combine in GEMM2 case={name}", flush=True)
+    s = run.s
+    ws = binding._aligned_ws(binding.workspace_bytes(s, binding.MOE_WS_EXPERTS_COMBINE))
+    ws.fill_(0x5a)   # nothing may rely on a cleared workspace
+    h, out = torch.empty_like(run.h), torch.empty_like(run.out)
+    outs = []
+    for _ in range(2):
+        binding.grouped_gemm_swiglu_combine(s, run.inp["x"], run.inp["w1"], run.inp["w2"], run.plan, h, out, ws)
+        torch.cuda.synchronize()
+        outs.append(out.clone())
+    assert torch.equal(outs[0], outs[1])
+    N = ref["plan"].N
+    assert torch.equal(h[:N], run.h[:N])
+    check = Checks(cfg)
+    check("O", out.double().cpu().numpy(), ref["O"], env=envelope(cfg, run, ref).O)
+    check.done()
+
+
 def _tied_inputs(cfg, dup):
     """Inputs whose router has duplicated rows (W_g[j] = W_g[i] for (i, j) in dup):
     the logits of i and j are equal bit for bit on both sides, so every token
