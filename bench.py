@@ -44,7 +44,7 @@ PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 (MXFP8) MFMA
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 COPY_BYTES = 256 << 20
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "moe_layer_sparse_e256_dw1_hbm_traffic.md")
 
 
 def parse():
