@@ -277,7 +277,7 @@ def test_fused_gather_bitwise(name):
         assert torch.equal(a, b), key
 
 
-@pytest.mark.parametrize("name", ["fine_mx_small", "sparse_mx_small", "mx_ragged_d"])
+@pytest.mark.parametrize("name", ["fine_mx_small", "sparse_mx_small", "mx_ragged_d", "fine_mx_small:x_perm"])
 def test_mx_weight_codes_reused_bitwise(name):
     """Gradient accumulation with MXFP8: the weight codes written once by
     moe_quantize_weights_mx serve two micro-batches (the second with fewer
@@ -285,6 +285,8 @@ def test_mx_weight_codes_reused_bitwise(name):
     every output equals, bit for bit, the step that quantises the weights
     itself.  One workspace, sized for the larger micro-batch, serves both."""
     from mixture_experts_layer_27_amd import binding, synth
+    name, _, src = name.partition(":")
+    fused = src != "x_perm"
     cfg = CASES[name]
     T1 = max(1, cfg.T - 123)
     print(f"[parity] MXFP8 weight codes reused case={name} micro-batches T={cfg.T},{T1}", flush=True)
@@ -300,12 +302,17 @@ def test_mx_weight_codes_reused_bitwise(name):
     for j, (c, inp) in enumerate(zip(cfgs, inputs)):
         outs = []
         for reuse in (False, True):
-            run = binding.LayerRun(c, inp, fused_gather=True)
+            run = binding.LayerRun(c, inp, fused_gather=fused)
             if reuse:
                 assert binding.workspace_bytes(run.s, binding.MOE_WS_EXPERTS) <= ws.numel()
                 run.ws_fwd = ws
                 run.route()
-                binding.grouped_gemm_swiglu_wcodes(run.s, run.inp["x"], run.plan, run.h, run.y, ws)
+                if fused:
+                    binding.grouped_gemm_swiglu_wcodes(run.s, run.inp["x"], run.plan, run.h, run.y, ws)
+                else:
+                    binding.permute(run.s, run.inp["x"], run.plan, run.x_perm)
+                    binding.grouped_gemm_swiglu_wcodes(run.s, run.x_perm, run.plan, run.h, run.y, ws,
+                                                       gathered=False)
                 binding.unpermute_combine(run.s, run.y, run.plan, run.out)
             else:
                 run.forward()
@@ -320,21 +327,25 @@ def test_mx_weight_codes_reused_bitwise(name):
 
 @pytest.mark.parametrize("name", ["fine_small", "sparse_small", "sparse_round_small", "fine_zipf_small",
                                   "big_tiles_small", "max_E_k", "one_token", "var_capacity_all",
-                                  "var_all_lb_z_noise"])
+                                  "var_all_lb_z_noise", "fine_small:x_perm", "sparse_round_small:x_perm"])
 def test_combine_in_gemm2(name):
     """moe_grouped_gemm_swiglu_combine (gate and scatter to token order in GEMM2's
     epilogue, then a per-token sum of contiguous rows): out within the bar of the
     oracle's O, H bitwise that of the separate calls, two calls bitwise equal."""
     from mixture_experts_layer_27_amd import binding
+    name, _, src = name.partition(":")
     cfg, run, ref = run_case(name)
-    print(f"[parity] combine in GEMM2 case={name}", flush=True)
+    print(f"[parity] combine in GEMM2 case={name} x {'permuted' if src else 'read through the plan'}", flush=True)
     s = run.s
+    gathered = src != "x_perm"
+    x = run.inp["x"] if gathered else run.x_perm   # the forward above permuted x into x_perm
     ws = binding._aligned_ws(binding.workspace_bytes(s, binding.MOE_WS_EXPERTS_COMBINE))
     ws.fill_(0x5a)   # nothing may rely on a cleared workspace
     h, out = torch.empty_like(run.h), torch.empty_like(run.out)
     outs = []
     for _ in range(2):
-        binding.grouped_gemm_swiglu_combine(s, run.inp["x"], run.inp["w1"], run.inp["w2"], run.plan, h, out, ws)
+        binding.grouped_gemm_swiglu_combine(s, x, run.inp["w1"], run.inp["w2"], run.plan, h, out, ws,
+                                            gathered=gathered)
         torch.cuda.synchronize()
         outs.append(out.clone())
     assert torch.equal(outs[0], outs[1])
