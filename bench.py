@@ -649,7 +649,7 @@ def main():
         out["combine_in_gemm2"] = comb
     if not a.no_cpu_baseline:
         torch.cuda.empty_cache()
-        tokens = a.cpu_tokens or min(cfg.T, 4096 if cfg.d * cfg.f * cfg.k > 2 ** 23 else 16384)
+        tokens = a.cpu_tokens or min(cfg.T, 8192 if cfg.d * cfg.f * cfg.k > 2 ** 23 else 16384)
         log(f"cpu oracle on {tokens} tokens")
         out["cpu_baseline"] = cpu_baseline(cfg, g, tokens)
     line = json.dumps(out)
